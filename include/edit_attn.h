@@ -1,0 +1,158 @@
+/*
+ * edit_attn.h -- C ABI of the MI355X (gfx950) EDiT linear compressed
+ * attention layer forward and its MM-EDiT hybrid.
+ *
+ * The operation is defined on the page "EDiT: Efficient Diffusion
+ * Transformers with Linear Compressed Attention" (ICCV 2025 paper notes,
+ * arXiv 2503.16726):
+ *   - section "ConvFusion": Q = ReLU(Linear(X + Conv1x1(LeakyReLU(GN(Conv3x3(X)))))),
+ *     the token sequence laid out as an H x W grid before the convolutions;
+ *   - section "Spatial Compressor": K = ReLU(Conv(Linear(X))), V = Conv(Linear(X)),
+ *     the conv being 3x3 depthwise with stride 2 (four times fewer tokens);
+ *   - section "Linear-attention formula": y_i = Q_i (sum_j K_j^T V_j) / (Q_i sum_j K_j);
+ *   - section "MM-EDiT": the hybrid matrix that keeps linear attention for
+ *     image-image pairs and softmax attention for pairs involving text,
+ *     mixed by eta = N_I / (N_I + N_T).
+ * The output projection that follows the attention is not written on the
+ * page; it is a plain Linear C -> C with bias.
+ *
+ * Conventions shared by every entry point
+ *   Layout   x, y: [B][H*W][C], token n = row * W + col, channels innermost.
+ *            x_txt, y_txt: [B][n_text][C]. Heads split the channels
+ *            contiguously: channel c belongs to head c / head_dim.
+ *            Linear weights are [out][in] row-major (y = x W^T + b).
+ *            w_cf1 is [C/r][3][3][C] (input channels innermost), w_cf2 is
+ *            [C][C/r], dw_k / dw_v are [3][3][C]; every bias is [out].
+ *   Dtype    every tensor, weights and biases included, has the shape's
+ *            dtype. EDIT_BF16 keeps bf16 storage with fp32 accumulation
+ *            (GroupNorm statistics, the K^T V state, softmax and every
+ *            accumulator are fp32); EDIT_F32 is fp32 throughout.
+ *   Memory   every pointer is a device pointer owned by the caller; the
+ *            library allocates nothing and keeps no state between calls.
+ *            Tensor pointers must be 16-byte aligned, the workspace
+ *            256-byte aligned. Outputs must not overlap inputs or the
+ *            workspace.
+ *   Stream   work is enqueued on hip_stream (a hipStream_t passed as
+ *            void*; NULL = the default stream) and the call returns without
+ *            waiting. Errors of the asynchronous work surface at the
+ *            caller's next synchronisation.
+ *   Errors   arguments are checked before anything is enqueued; on any
+ *            error nothing is launched and a status other than EDIT_OK is
+ *            returned. edit_last_error() gives the detail (thread-local).
+ *            No entry point aborts or throws.
+ *   Fixed    GroupNorm eps 1e-5, LeakyReLU slope 0.01, softmax scale
+ *            1/sqrt(head_dim); eps of the linear branch comes with the shape.
+ *   Results  are bit-for-bit reproducible for identical inputs and shape
+ *            (no atomics in any reduction).
+ */
+#ifndef EDIT_ATTN_H
+#define EDIT_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { EDIT_F32 = 0, EDIT_BF16 = 1 } edit_dtype_t;
+
+typedef enum {
+  EDIT_OK = 0,
+  EDIT_ERR_ARG = 1,          /* invalid argument: bad size, null / misaligned / overlapping pointer */
+  EDIT_ERR_UNSUPPORTED = 2,  /* valid, but outside the kernels' limits (see edit_shape_t) */
+  EDIT_ERR_WORKSPACE = 3,    /* workspace smaller than the *_workspace_size query */
+  EDIT_ERR_HIP = 4           /* no usable device, or a launch failed */
+} edit_status_t;
+
+/* Problem statement of one layer call.
+ *   B          batch
+ *   H, W       token grid (N = H*W image tokens)
+ *   C          channels, = heads * head_dim
+ *   reduction  ConvFusion channel reduction r (the 3x3 conv maps C -> C/r)
+ *   gn_groups  GroupNorm groups over the C/r compressed channels
+ *   eps        added to the linear-attention denominator Q_i . z (>= 0)
+ * Kernel limits (EDIT_ERR_UNSUPPORTED otherwise): C, C/r and head_dim are
+ * multiples of 8; head_dim <= 128. */
+typedef struct {
+  int B, H, W, C, heads, head_dim, reduction, gn_groups;
+  float eps;
+  edit_dtype_t dtype;
+} edit_shape_t;
+
+/* Parameters of the image stream (EDiT layer). */
+typedef struct {
+  const void *w_cf1, *b_cf1;       /* ConvFusion 3x3, C -> C/r            */
+  const void *gn_gamma, *gn_beta;  /* GroupNorm affine, [C/r]             */
+  const void *w_cf2, *b_cf2;       /* ConvFusion 1x1, C/r -> C            */
+  const void *w_q, *b_q;           /* query Linear (inside ConvFusion)    */
+  const void *w_k, *b_k;           /* key Linear (Spatial Compressor)     */
+  const void *w_v, *b_v;           /* value Linear (Spatial Compressor)   */
+  const void *dw_k, *db_k;         /* key depthwise 3x3 stride 2          */
+  const void *dw_v, *db_v;         /* value depthwise 3x3 stride 2        */
+  const void *w_o, *b_o;           /* output Linear                       */
+} edit_weights_t;
+
+/* Parameters of the text stream of the hybrid: its own Q/K/V/O Linears. */
+typedef struct {
+  const void *w_q, *b_q, *w_k, *b_k, *w_v, *b_v, *w_o, *b_o;
+} edit_text_weights_t;
+
+/* Bytes of workspace edit_attn_forward needs for this shape; 0 if the shape
+ * is invalid (edit_last_error() says why). */
+size_t edit_attn_workspace_size(const edit_shape_t* shape);
+
+/* EDiT layer forward: y = Out(LinearAttention(Q_CF(x), K_SC(x), V_SC(x))).
+ * x [B][H*W][C] in, y [B][H*W][C] out, workspace of at least
+ * edit_attn_workspace_size(shape) bytes. */
+edit_status_t edit_attn_forward(const edit_shape_t* shape, const edit_weights_t* w,
+                                const void* x, void* y,
+                                void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Bytes of workspace mmedit_hybrid_forward needs; 0 if invalid. */
+size_t mmedit_hybrid_workspace_size(const edit_shape_t* shape, int n_text);
+
+/* MM-EDiT hybrid forward.
+ *   image rows: eta * LinearAttention(Q_I, K'_I, V'_I) + (1 - eta) * softmax(Q_I K_T^T / sqrt(d)) V_T
+ *   text rows:  softmax([Q_T K'_I^T, Q_T K_T^T] / sqrt(d)) [V'_I ; V_T]
+ *   eta = H*W / (H*W + n_text); then the image and the text output Linears.
+ * Q_I, K'_I, V'_I are the EDiT features of x_img; Q_T, K_T, V_T the text
+ * Linears of x_txt. n_text = 0 is legal: x_txt, y_txt, txt may then be NULL
+ * and y_img equals edit_attn_forward's y bit for bit. */
+edit_status_t mmedit_hybrid_forward(const edit_shape_t* shape, int n_text,
+                                    const edit_weights_t* img, const edit_text_weights_t* txt,
+                                    const void* x_img, const void* x_txt,
+                                    void* y_img, void* y_txt,
+                                    void* workspace, size_t ws_bytes, void* hip_stream);
+
+/* Where each intermediate of the last forward with this shape lives in the
+ * workspace (byte offsets; 0 size = not produced for this call). The layout
+ * is a pure function of (shape, n_text). Intermediates, with their dtype T
+ * (the shape's dtype) or f32:
+ *   xc      [B][N][C/r] T      ConvFusion 3x3 output
+ *   gn_stat [B][G][2]   f32    GroupNorm mean and 1/sqrt(var + 1e-5)
+ *   xt      [B][N][C]   T      X + Conv1x1(LeakyReLU(GN(xc)))
+ *   q       [B][N][C]   T      ConvFusion queries (after ReLU)
+ *   kv0     [B][N][2C]  T      key Linear | value Linear, side by side per token
+ *   kc, vc  [B][N'][C]  T      compressed keys (ReLU'd) and values, N' = ceil(H/2)*ceil(W/2)
+ *   S       [B][h][d][d] f32   sum_j K'_j^T V'_j per head
+ *   z       [B][h][d]   f32    sum_j K'_j per head
+ *   y       [B][N][C]   T      linear-attention output (hybrid: before blending)
+ *   qkv_t   [B][N_T][3C] T     text Q | K | V (hybrid only)
+ *   y_img   [B][N][C]   T      blended image rows (hybrid with text only)
+ *   y_txt   [B][N_T][C] T      text rows before the text output Linear (hybrid only) */
+typedef struct {
+  size_t xc, gn_stat, xt, q, kv0, kc, vc, S, z, y, qkv_t, y_img, y_txt;
+  size_t total;
+} edit_ws_layout_t;
+
+edit_status_t edit_attn_workspace_layout(const edit_shape_t* shape, int n_text,
+                                         edit_ws_layout_t* layout);
+
+const char* edit_status_string(edit_status_t status);
+const char* edit_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EDIT_ATTN_H */

@@ -1,0 +1,200 @@
+"""Python binding of libedit_attn.so, the gfx950 EDiT linear compressed
+attention layer and its MM-EDiT hybrid.
+
+The functions carry the C ABI's names (include/edit_attn.h) and only marshal
+arguments: torch tensors become device pointers, the current torch stream
+becomes the hipStream_t. Every step of the layer runs in the library's HIP
+kernels; there is no other code path. If the shared library is missing the
+import of this package fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Mapping, Optional
+
+__all__ = [
+    "EDIT_F32", "EDIT_BF16", "EditError", "IMAGE_WEIGHT_FIELDS", "TEXT_WEIGHT_FIELDS", "LAYOUT_FIELDS",
+    "edit_attn_workspace_size", "edit_attn_forward", "mmedit_hybrid_workspace_size",
+    "mmedit_hybrid_forward", "edit_attn_workspace_layout", "edit_status_string", "edit_last_error",
+    "lib_path", "header_symbols",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_PKG)
+_LIB_PATH = os.path.join(_PKG, "libedit_attn.so")
+
+EDIT_F32, EDIT_BF16 = 0, 1
+_STATUS = {0: "EDIT_OK", 1: "EDIT_ERR_ARG", 2: "EDIT_ERR_UNSUPPORTED", 3: "EDIT_ERR_WORKSPACE", 4: "EDIT_ERR_HIP"}
+
+IMAGE_WEIGHT_FIELDS = ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2", "w_q", "b_q", "w_k", "b_k",
+                       "w_v", "b_v", "dw_k", "db_k", "dw_v", "db_v", "w_o", "b_o")
+TEXT_WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o")
+LAYOUT_FIELDS = ("xc", "gn_stat", "xt", "q", "kv0", "kc", "vc", "S", "z", "y", "qkv_t", "y_img", "y_txt", "total")
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("B", "H", "W", "C", "heads", "head_dim", "reduction", "gn_groups")] + \
+               [("eps", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in IMAGE_WEIGHT_FIELDS]
+
+
+class _TextWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in TEXT_WEIGHT_FIELDS]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in LAYOUT_FIELDS]
+
+
+class EditError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m linear_compressed_attention_amd.build` "
+                          "(the HIP library is the only implementation of this package)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER
+    lib.edit_attn_workspace_size.argtypes = [P(_Shape)]
+    lib.edit_attn_workspace_size.restype = ctypes.c_size_t
+    lib.mmedit_hybrid_workspace_size.argtypes = [P(_Shape), ctypes.c_int]
+    lib.mmedit_hybrid_workspace_size.restype = ctypes.c_size_t
+    lib.edit_attn_forward.argtypes = [P(_Shape), P(_Weights), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]
+    lib.edit_attn_forward.restype = ctypes.c_int
+    lib.mmedit_hybrid_forward.argtypes = [P(_Shape), ctypes.c_int, P(_Weights), P(_TextWeights), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]
+    lib.mmedit_hybrid_forward.restype = ctypes.c_int
+    lib.edit_attn_workspace_layout.argtypes = [P(_Shape), ctypes.c_int, P(_Layout)]
+    lib.edit_attn_workspace_layout.restype = ctypes.c_int
+    lib.edit_status_string.argtypes = [ctypes.c_int]
+    lib.edit_status_string.restype = ctypes.c_char_p
+    lib.edit_last_error.argtypes = []
+    lib.edit_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def header_symbols():
+    """Function names declared in include/edit_attn.h."""
+    import re
+    with open(os.path.join(_ROOT, "include", "edit_attn.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, re.M)))
+
+
+def _get(obj, name):
+    return obj[name] if isinstance(obj, Mapping) else getattr(obj, name)
+
+
+def _shape(s) -> _Shape:
+    dt = _get(s, "dtype")
+    if isinstance(dt, str):
+        dt = {"f32": EDIT_F32, "bf16": EDIT_BF16}[dt]
+    return _Shape(*(int(_get(s, n)) for n in ("B", "H", "W", "C", "heads", "head_dim", "reduction", "gn_groups")),
+                  float(_get(s, "eps")), int(dt))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != 0:
+        raise EditError(status, _lib.edit_last_error().decode())
+
+
+def edit_status_string(status: int) -> str:
+    return _lib.edit_status_string(int(status)).decode()
+
+
+def edit_last_error() -> str:
+    return _lib.edit_last_error().decode()
+
+
+def edit_attn_workspace_size(shape) -> int:
+    """Workspace bytes of edit_attn_forward; raises EditError on a bad shape."""
+    sh = _shape(shape)
+    n = _lib.edit_attn_workspace_size(ctypes.byref(sh))
+    if n == 0:
+        _check(_lib.edit_attn_workspace_layout(ctypes.byref(sh), 0, ctypes.byref(_Layout())))
+    return n
+
+
+def mmedit_hybrid_workspace_size(shape, n_text: int) -> int:
+    sh = _shape(shape)
+    n = _lib.mmedit_hybrid_workspace_size(ctypes.byref(sh), int(n_text))
+    if n == 0:
+        _check(_lib.edit_attn_workspace_layout(ctypes.byref(sh), int(n_text), ctypes.byref(_Layout())))
+    return n
+
+
+def edit_attn_workspace_layout(shape, n_text: int = 0) -> dict:
+    """Byte offsets of the intermediates inside the workspace."""
+    lay = _Layout()
+    _check(_lib.edit_attn_workspace_layout(ctypes.byref(_shape(shape)), int(n_text), ctypes.byref(lay)))
+    return {n: getattr(lay, n) for n in LAYOUT_FIELDS}
+
+
+def _weights(w) -> _Weights:
+    return _Weights(*(_ptr(_get(w, n)) for n in IMAGE_WEIGHT_FIELDS))
+
+
+def _text_weights(w) -> Optional[_TextWeights]:
+    if w is None:
+        return None
+    return _TextWeights(*(_ptr(_get(w, n)) for n in TEXT_WEIGHT_FIELDS))
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def edit_attn_forward(shape, weights, x, y, workspace, stream=None) -> None:
+    """EDiT layer forward on device tensors (enqueued on ``stream``, default:
+    torch's current stream). ``weights`` maps the edit_weights_t field names
+    to tensors; ``workspace`` is a byte tensor of edit_attn_workspace_size."""
+    sh = _shape(shape)
+    w = _weights(weights)
+    _check(_lib.edit_attn_forward(ctypes.byref(sh), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(workspace),
+                                  _nbytes(workspace), _stream(stream)))
+
+
+def mmedit_hybrid_forward(shape, n_text, img_weights, txt_weights, x_img, x_txt, y_img, y_txt, workspace,
+                          stream=None) -> None:
+    """MM-EDiT hybrid forward (image and text rows); see edit_attn.h."""
+    sh = _shape(shape)
+    w = _weights(img_weights)
+    tw = _text_weights(txt_weights)
+    _check(_lib.mmedit_hybrid_forward(ctypes.byref(sh), int(n_text), ctypes.byref(w),
+                                      ctypes.byref(tw) if tw is not None else None, _ptr(x_img), _ptr(x_txt),
+                                      _ptr(y_img), _ptr(y_txt), _ptr(workspace), _nbytes(workspace),
+                                      _stream(stream)))

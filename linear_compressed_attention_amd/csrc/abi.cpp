@@ -1,0 +1,415 @@
+// C ABI of the EDiT layer and the MM-EDiT hybrid: argument checks, workspace
+// layout and the launch sequence. Declared in include/edit_attn.h.
+//
+// Launch sequence of one EDiT layer (page "EDiT: Efficient Diffusion
+// Transformers with Linear Compressed Attention", ICCV 2025 notes):
+//   section "ConvFusion":
+//     1 gemm A_CONV3      xc  = Conv3x3(x) + b_cf1               (C -> C/r)
+//     2 groupnorm stats   per (b, group) mean / rstd -> scale, shift
+//     3 gemm A_GNACT      xt  = x + Conv1x1(LeakyReLU(GN(xc))) + b_cf2
+//     4 gemm relu         q   = ReLU(xt W_q^T + b_q)
+//   section "Spatial Compressor":
+//     5 gemm (2 segments) kv0 = [x W_k^T + b_k | x W_v^T + b_v]
+//     6 dwconv_s2         kc  = ReLU(DW(k0)), vc = DW(v0)
+//   section "Linear-attention formula":
+//     7 kv_state          S = kc^T vc, z = sum kc (per head)
+//     8 linattn_apply     y = q S / (q . z + eps)
+//   output Linear:
+//     9 gemm              out = y W_o^T + b_o
+// The hybrid (section "MM-EDiT") adds the text Q/K/V Linears (one gemm with
+// three segments), image rows eta * y + (1 - eta) * softmax(q K_T^T) V_T,
+// text rows over [kc ; K_T], and the text output Linear.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/edit_attn.h"
+#include "launch.hpp"
+
+using edit::bf16;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+edit_status_t fail(edit_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Geometry {
+  int B, H, W, C, heads, d, r, G, Cr, N, M, Hc, Wc, Nc, nt;
+  int gn_chunks, kv_chunks, DT, DR, DP, DK;
+  size_t es;
+  float eps;
+  edit_dtype_t dtype;
+};
+
+struct Layout {
+  size_t xc, gn_part, gn_stat, gn_scale, gn_shift, xt, q, kv0, kc, vc, kv_part, S, z, st, zp, y;
+  size_t qkv_t, y_img, y_txt, total;
+};
+
+edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
+  if (!s) return fail(EDIT_ERR_ARG, "shape is NULL");
+  if (s->B <= 0 || s->H <= 0 || s->W <= 0 || s->C <= 0 || s->heads <= 0 || s->head_dim <= 0 ||
+      s->reduction <= 0 || s->gn_groups <= 0)
+    return fail(EDIT_ERR_ARG, "every size must be positive (B=%d H=%d W=%d C=%d heads=%d head_dim=%d r=%d G=%d)",
+                s->B, s->H, s->W, s->C, s->heads, s->head_dim, s->reduction, s->gn_groups);
+  if ((long)s->heads * s->head_dim != s->C)
+    return fail(EDIT_ERR_ARG, "C (%d) must equal heads (%d) * head_dim (%d)", s->C, s->heads, s->head_dim);
+  if (s->C % s->reduction != 0)
+    return fail(EDIT_ERR_ARG, "reduction %d does not divide C %d", s->reduction, s->C);
+  const int Cr = s->C / s->reduction;
+  if (Cr % s->gn_groups != 0)
+    return fail(EDIT_ERR_ARG, "gn_groups %d does not divide C/r %d", s->gn_groups, Cr);
+  if (!(s->eps >= 0.0f) || !std::isfinite(s->eps)) return fail(EDIT_ERR_ARG, "eps must be finite and >= 0");
+  if (s->dtype != EDIT_F32 && s->dtype != EDIT_BF16) return fail(EDIT_ERR_ARG, "unknown dtype %d", (int)s->dtype);
+  if (n_text < 0) return fail(EDIT_ERR_ARG, "n_text must be >= 0 (got %d)", n_text);
+  if (s->C % 8 || Cr % 8 || s->head_dim % 8)
+    return fail(EDIT_ERR_UNSUPPORTED, "C (%d), C/r (%d) and head_dim (%d) must be multiples of 8", s->C, Cr,
+                s->head_dim);
+  if (s->head_dim > 128) return fail(EDIT_ERR_UNSUPPORTED, "head_dim %d > 128", s->head_dim);
+  if (Cr > 2048) return fail(EDIT_ERR_UNSUPPORTED, "C/r %d > 2048", Cr);
+  const long N = (long)s->H * s->W, M = N * s->B;
+  if (M * 2L * s->C >= (1L << 31) || (long)s->B * n_text * 3L * s->C >= (1L << 31))
+    return fail(EDIT_ERR_UNSUPPORTED, "tensor too large for 32-bit row indexing");
+  g->B = s->B; g->H = s->H; g->W = s->W; g->C = s->C; g->heads = s->heads; g->d = s->head_dim;
+  g->r = s->reduction; g->G = s->gn_groups; g->Cr = Cr; g->N = (int)N; g->M = (int)M;
+  g->Hc = (s->H + 1) / 2; g->Wc = (s->W + 1) / 2; g->Nc = g->Hc * g->Wc; g->nt = n_text;
+  g->gn_chunks = edit::groupnorm_chunks(g->N);
+  g->kv_chunks = edit::kv_state_chunks(g->Nc);
+  g->DT = (g->d + 15) / 16; g->DR = (g->d + 16) / 16;
+  g->DP = edit::kv_state_dp(g->d); g->DK = edit::kv_state_dk(g->d);
+  g->es = s->dtype == EDIT_BF16 ? 2 : 4;
+  g->eps = s->eps;
+  g->dtype = s->dtype;
+  return EDIT_OK;
+}
+
+Layout make_layout(const Geometry& g) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t M = g.M, es = g.es, BH = (size_t)g.B * g.heads;
+  L.xc = take(M * g.Cr * es);
+  L.gn_part = take((size_t)g.B * g.gn_chunks * g.Cr * 2 * 4);
+  L.gn_stat = take((size_t)g.B * g.G * 2 * 4);
+  L.gn_scale = take((size_t)g.B * g.Cr * 4);
+  L.gn_shift = take((size_t)g.B * g.Cr * 4);
+  L.xt = take(M * g.C * es);
+  L.q = take(M * g.C * es);
+  L.kv0 = take(M * 2 * g.C * es);
+  L.kc = take((size_t)g.B * g.Nc * g.C * es);
+  L.vc = take((size_t)g.B * g.Nc * g.C * es);
+  L.kv_part = take(BH * g.kv_chunks * (16 * g.DR) * (16 * g.DT) * 4);
+  L.S = take(BH * g.d * g.d * 4);
+  L.z = take(BH * g.d * 4);
+  L.st = take(BH * 2 * g.DP * g.DK * es);
+  L.zp = take(BH * g.DK * 4);
+  L.y = take(M * g.C * es);
+  if (g.nt > 0) {
+    L.qkv_t = take((size_t)g.B * g.nt * 3 * g.C * es);
+    L.y_img = take(M * g.C * es);
+    L.y_txt = take((size_t)g.B * g.nt * g.C * es);
+  }
+  L.total = off;
+  return L;
+}
+
+bool misaligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || !na || !nb) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+edit_status_t check_ptr(const void* p, const char* name) {
+  if (!p) return fail(EDIT_ERR_ARG, "%s is NULL", name);
+  if (misaligned(p, 16)) return fail(EDIT_ERR_ARG, "%s is not 16-byte aligned", name);
+  return EDIT_OK;
+}
+
+edit_status_t check_weights(const edit_weights_t* w) {
+  if (!w) return fail(EDIT_ERR_ARG, "weights struct is NULL");
+  const void* p[] = {w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, w->w_q, w->b_q, w->w_k,
+                     w->b_k, w->w_v, w->b_v, w->dw_k, w->db_k, w->dw_v, w->db_v, w->w_o, w->b_o};
+  const char* n[] = {"w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2", "w_q", "b_q", "w_k",
+                     "b_k", "w_v", "b_v", "dw_k", "db_k", "dw_v", "db_v", "w_o", "b_o"};
+  for (int i = 0; i < 18; ++i) {
+    edit_status_t st = check_ptr(p[i], n[i]);
+    if (st != EDIT_OK) return st;
+  }
+  return EDIT_OK;
+}
+
+edit_status_t check_text_weights(const edit_text_weights_t* w) {
+  if (!w) return fail(EDIT_ERR_ARG, "text weights struct is NULL");
+  const void* p[] = {w->w_q, w->b_q, w->w_k, w->b_k, w->w_v, w->b_v, w->w_o, w->b_o};
+  const char* n[] = {"txt.w_q", "txt.b_q", "txt.w_k", "txt.b_k", "txt.w_v", "txt.b_v", "txt.w_o", "txt.b_o"};
+  for (int i = 0; i < 8; ++i) {
+    edit_status_t st = check_ptr(p[i], n[i]);
+    if (st != EDIT_OK) return st;
+  }
+  return EDIT_OK;
+}
+
+// The library carries gfx950 code only; confirm the current device is one.
+edit_status_t check_device() {
+  int dev = -1, count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0)
+    return fail(EDIT_ERR_HIP, "no HIP device available (%s)", hipGetErrorString(e));
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EDIT_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  static thread_local int checked_dev = -1;
+  if (checked_dev == dev) return EDIT_OK;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(EDIT_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(EDIT_ERR_HIP, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+  checked_dev = dev;
+  return EDIT_OK;
+}
+
+#define EDIT_LAUNCH(call)                                                                  \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) return fail(EDIT_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+// The image stream up to the linear-attention output y (steps 1-8).
+template <typename T>
+edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
+                        hipStream_t s) {
+  using namespace edit;
+  auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  GemmArgs<T> a{};
+  // 1. xc = Conv3x3(x) + b_cf1
+  a.M = g.M; a.N = g.Cr; a.K = 9 * g.C; a.A = x; a.lda = g.C; a.H = g.H; a.W = g.W; a.Cin = g.C;
+  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_cf1);
+  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_cf1);
+  a.seg_rows = g.Cr; a.ldb = 9 * g.C; a.C = P(L.xc); a.ldc = g.Cr;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
+  // 2. GroupNorm statistics -> per-channel scale / shift
+  EDIT_LAUNCH(launch_groupnorm_stats<T>(P(L.xc), g.B, g.N, g.Cr, g.G, static_cast<const T*>(w->gn_gamma),
+                                        static_cast<const T*>(w->gn_beta), 1e-5f, F(L.gn_part), g.gn_chunks,
+                                        F(L.gn_stat), F(L.gn_scale), F(L.gn_shift), s));
+  // 3. xt = x + LeakyReLU(GN(xc)) W_cf2^T + b_cf2
+  a = GemmArgs<T>{};
+  a.M = g.M; a.N = g.C; a.K = g.Cr; a.A = P(L.xc); a.lda = g.Cr;
+  a.scale = F(L.gn_scale); a.shift = F(L.gn_shift); a.rows_per_batch = g.N;
+  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_cf2);
+  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_cf2);
+  a.seg_rows = g.C; a.ldb = g.Cr; a.C = P(L.xt); a.ldc = g.C; a.R = x; a.ldr = g.C;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_GNACT, E_BIAS_RES, s));
+  // 4. q = ReLU(xt W_q^T + b_q)
+  a = GemmArgs<T>{};
+  a.M = g.M; a.N = g.C; a.K = g.C; a.A = P(L.xt); a.lda = g.C;
+  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_q);
+  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_q);
+  a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.q); a.ldc = g.C;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS_RELU, s));
+  // 5. kv0 = [x W_k^T + b_k | x W_v^T + b_v]
+  a = GemmArgs<T>{};
+  a.M = g.M; a.N = 2 * g.C; a.K = g.C; a.A = x; a.lda = g.C;
+  a.Bseg[0] = static_cast<const T*>(w->w_k); a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_v);
+  a.bias[0] = static_cast<const T*>(w->b_k); a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_v);
+  a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.kv0); a.ldc = 2 * g.C;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
+  // 6. compressed keys / values
+  EDIT_LAUNCH(launch_dwconv_s2<T>(P(L.kv0), g.B, g.H, g.W, g.C, static_cast<const T*>(w->dw_k),
+                                  static_cast<const T*>(w->db_k), static_cast<const T*>(w->dw_v),
+                                  static_cast<const T*>(w->db_v), P(L.kc), P(L.vc), s));
+  // 7. per-head state
+  EDIT_LAUNCH(launch_kv_state<T>(P(L.kc), P(L.vc), g.B, g.Nc, g.heads, g.d, F(L.kv_part), g.kv_chunks, F(L.S),
+                                 F(L.z), P(L.st), F(L.zp), s));
+  // 8. y = q S / (q . z + eps)
+  EDIT_LAUNCH(launch_linattn_apply<T>(P(L.q), g.C, P(L.st), F(L.zp), g.B, g.N, g.heads, g.d, g.eps, P(L.y), g.C,
+                                      s));
+  return EDIT_OK;
+}
+
+template <typename T>
+edit_status_t out_linear(int M, int C, const void* wo, const void* bo, const T* y, T* out, hipStream_t s) {
+  using namespace edit;
+  GemmArgs<T> a{};
+  a.M = M; a.N = C; a.K = C; a.A = y; a.lda = C;
+  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(wo);
+  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(bo);
+  a.seg_rows = C; a.ldb = C; a.C = out; a.ldc = C;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
+  return EDIT_OK;
+}
+
+template <typename T>
+edit_status_t run_edit(const Geometry& g, const Layout& L, const edit_weights_t* w, const void* x, void* y,
+                       void* ws, hipStream_t s) {
+  char* wsb = static_cast<char*>(ws);
+  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x), wsb, s);
+  if (st != EDIT_OK) return st;
+  return out_linear<T>(g.M, g.C, w->w_o, w->b_o, reinterpret_cast<const T*>(wsb + L.y), static_cast<T*>(y), s);
+}
+
+template <typename T>
+edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_t* w,
+                         const edit_text_weights_t* wt, const void* x_img, const void* x_txt, void* y_img,
+                         void* y_txt, void* ws, hipStream_t s) {
+  using namespace edit;
+  char* wsb = static_cast<char*>(ws);
+  auto P = [&](size_t off) { return reinterpret_cast<T*>(wsb + off); };
+  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x_img), wsb, s);
+  if (st != EDIT_OK) return st;
+  if (g.nt == 0) return out_linear<T>(g.M, g.C, w->w_o, w->b_o, P(L.y), static_cast<T*>(y_img), s);
+
+  const int C = g.C, MT = g.B * g.nt;
+  // Text Q | K | V in one GEMM with three weight segments.
+  GemmArgs<T> a{};
+  a.M = MT; a.N = 3 * C; a.K = C; a.A = static_cast<const T*>(x_txt); a.lda = C;
+  a.Bseg[0] = static_cast<const T*>(wt->w_q); a.Bseg[1] = static_cast<const T*>(wt->w_k);
+  a.Bseg[2] = static_cast<const T*>(wt->w_v);
+  a.bias[0] = static_cast<const T*>(wt->b_q); a.bias[1] = static_cast<const T*>(wt->b_k);
+  a.bias[2] = static_cast<const T*>(wt->b_v);
+  a.seg_rows = C; a.ldb = C; a.C = P(L.qkv_t); a.ldc = 3 * C;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
+
+  const T* qkv = P(L.qkv_t);
+  const float eta = (float)((double)g.N / ((double)g.N + (double)g.nt));
+  // Image rows: eta * y_lin + (1 - eta) * softmax(Q_I K_T^T / sqrt(d)) V_T.
+  SdpaArgs<T> sa{};
+  sa.q = P(L.q); sa.ldq = C; sa.Nq = g.N;
+  sa.k1 = qkv + C; sa.v1 = qkv + 2 * C; sa.ldkv1 = 3 * C; sa.N1 = g.nt;
+  sa.k2 = nullptr; sa.v2 = nullptr; sa.ldkv2 = 0; sa.N2 = 0;
+  sa.B = g.B; sa.heads = g.heads; sa.d = g.d;
+  sa.out = P(L.y_img); sa.ldo = C;
+  sa.blend_src = P(L.y); sa.ldbs = C; sa.alpha = eta; sa.beta = 1.0f - eta;
+  EDIT_LAUNCH(launch_sdpa<T>(sa, s));
+  // Text rows: softmax over [K'_I ; K_T] with values [V'_I ; V_T].
+  SdpaArgs<T> ta{};
+  ta.q = qkv; ta.ldq = 3 * C; ta.Nq = g.nt;
+  ta.k1 = P(L.kc); ta.v1 = P(L.vc); ta.ldkv1 = C; ta.N1 = g.Nc;
+  ta.k2 = qkv + C; ta.v2 = qkv + 2 * C; ta.ldkv2 = 3 * C; ta.N2 = g.nt;
+  ta.B = g.B; ta.heads = g.heads; ta.d = g.d;
+  ta.out = P(L.y_txt); ta.ldo = C;
+  ta.blend_src = nullptr; ta.ldbs = 0; ta.alpha = 0.0f; ta.beta = 1.0f;
+  EDIT_LAUNCH(launch_sdpa<T>(ta, s));
+
+  st = out_linear<T>(g.M, C, w->w_o, w->b_o, P(L.y_img), static_cast<T*>(y_img), s);
+  if (st != EDIT_OK) return st;
+  return out_linear<T>(MT, C, wt->w_o, wt->b_o, P(L.y_txt), static_cast<T*>(y_txt), s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t edit_attn_workspace_size(const edit_shape_t* shape) {
+  Geometry g;
+  if (check_shape(shape, 0, &g) != EDIT_OK) return 0;
+  return make_layout(g).total;
+}
+
+size_t mmedit_hybrid_workspace_size(const edit_shape_t* shape, int n_text) {
+  Geometry g;
+  if (check_shape(shape, n_text, &g) != EDIT_OK) return 0;
+  return make_layout(g).total;
+}
+
+edit_status_t edit_attn_workspace_layout(const edit_shape_t* shape, int n_text, edit_ws_layout_t* out) {
+  Geometry g;
+  edit_status_t st = check_shape(shape, n_text, &g);
+  if (st != EDIT_OK) return st;
+  if (!out) return fail(EDIT_ERR_ARG, "layout is NULL");
+  const Layout L = make_layout(g);
+  out->xc = L.xc; out->gn_stat = L.gn_stat; out->xt = L.xt; out->q = L.q; out->kv0 = L.kv0;
+  out->kc = L.kc; out->vc = L.vc; out->S = L.S; out->z = L.z; out->y = L.y;
+  out->qkv_t = L.qkv_t; out->y_img = L.y_img; out->y_txt = L.y_txt; out->total = L.total;
+  return EDIT_OK;
+}
+
+edit_status_t edit_attn_forward(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
+                                void* workspace, size_t ws_bytes, void* hip_stream) {
+  Geometry g;
+  edit_status_t st = check_shape(shape, 0, &g);
+  if (st != EDIT_OK) return st;
+  if ((st = check_weights(w)) != EDIT_OK) return st;
+  if ((st = check_ptr(x, "x")) != EDIT_OK) return st;
+  if ((st = check_ptr(y, "y")) != EDIT_OK) return st;
+  if (!workspace) return fail(EDIT_ERR_ARG, "workspace is NULL");
+  if (misaligned(workspace, 256)) return fail(EDIT_ERR_ARG, "workspace is not 256-byte aligned");
+  const Layout L = make_layout(g);
+  if (ws_bytes < L.total)
+    return fail(EDIT_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  const size_t act = (size_t)g.M * g.C * g.es;
+  if (overlap(y, act, x, act)) return fail(EDIT_ERR_ARG, "y overlaps x");
+  if (overlap(y, act, workspace, ws_bytes)) return fail(EDIT_ERR_ARG, "y overlaps the workspace");
+  if (overlap(x, act, workspace, ws_bytes)) return fail(EDIT_ERR_ARG, "x overlaps the workspace");
+  if ((st = check_device()) != EDIT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  return g.dtype == EDIT_BF16 ? run_edit<bf16>(g, L, w, x, y, workspace, s)
+                              : run_edit<float>(g, L, w, x, y, workspace, s);
+}
+
+edit_status_t mmedit_hybrid_forward(const edit_shape_t* shape, int n_text, const edit_weights_t* img,
+                                    const edit_text_weights_t* txt, const void* x_img, const void* x_txt,
+                                    void* y_img, void* y_txt, void* workspace, size_t ws_bytes,
+                                    void* hip_stream) {
+  Geometry g;
+  edit_status_t st = check_shape(shape, n_text, &g);
+  if (st != EDIT_OK) return st;
+  if ((st = check_weights(img)) != EDIT_OK) return st;
+  if ((st = check_ptr(x_img, "x_img")) != EDIT_OK) return st;
+  if ((st = check_ptr(y_img, "y_img")) != EDIT_OK) return st;
+  if (n_text > 0) {
+    if ((st = check_text_weights(txt)) != EDIT_OK) return st;
+    if ((st = check_ptr(x_txt, "x_txt")) != EDIT_OK) return st;
+    if ((st = check_ptr(y_txt, "y_txt")) != EDIT_OK) return st;
+  }
+  if (!workspace) return fail(EDIT_ERR_ARG, "workspace is NULL");
+  if (misaligned(workspace, 256)) return fail(EDIT_ERR_ARG, "workspace is not 256-byte aligned");
+  const Layout L = make_layout(g);
+  if (ws_bytes < L.total)
+    return fail(EDIT_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  const size_t ai = (size_t)g.M * g.C * g.es, at = (size_t)g.B * n_text * g.C * g.es;
+  const void* ins[] = {x_img, x_txt, workspace};
+  const size_t ins_n[] = {ai, n_text > 0 ? at : 0, ws_bytes};
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(y_img, ai, ins[i], ins_n[i])) return fail(EDIT_ERR_ARG, "y_img overlaps an input or the workspace");
+    if (n_text > 0 && overlap(y_txt, at, ins[i], ins_n[i]))
+      return fail(EDIT_ERR_ARG, "y_txt overlaps an input or the workspace");
+  }
+  if (n_text > 0 && overlap(y_img, ai, y_txt, at)) return fail(EDIT_ERR_ARG, "y_img overlaps y_txt");
+  if (overlap(x_img, ai, workspace, ws_bytes) || (n_text > 0 && overlap(x_txt, at, workspace, ws_bytes)))
+    return fail(EDIT_ERR_ARG, "an input overlaps the workspace");
+  if ((st = check_device()) != EDIT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  return g.dtype == EDIT_BF16 ? run_hybrid<bf16>(g, L, img, txt, x_img, x_txt, y_img, y_txt, workspace, s)
+                              : run_hybrid<float>(g, L, img, txt, x_img, x_txt, y_img, y_txt, workspace, s);
+}
+
+const char* edit_status_string(edit_status_t status) {
+  switch (status) {
+    case EDIT_OK: return "EDIT_OK";
+    case EDIT_ERR_ARG: return "EDIT_ERR_ARG: invalid argument";
+    case EDIT_ERR_UNSUPPORTED: return "EDIT_ERR_UNSUPPORTED: outside the kernels' limits";
+    case EDIT_ERR_WORKSPACE: return "EDIT_ERR_WORKSPACE: workspace too small";
+    case EDIT_ERR_HIP: return "EDIT_ERR_HIP: HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* edit_last_error(void) { return g_err; }
+
+}  // extern "C"

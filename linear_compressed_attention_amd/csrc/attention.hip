@@ -1,0 +1,468 @@
+// Attention cores on the matrix cores of gfx950.
+//
+// Page "EDiT: Efficient Diffusion Transformers with Linear Compressed
+// Attention" (ICCV 2025 notes):
+//   section "Linear-attention formula": y_i = Q_i (sum_j K_j^T V_j) / (Q_i sum_j K_j),
+//     computed as a per-head state S = K'^T V' (d x d), z = sum_j K'_j
+//     (kv_state_*), then y_i = Q_i S / (Q_i . z + eps) (linattn_apply_*);
+//   section "MM-EDiT": the blocks of the hybrid matrix that involve text keep
+//     scaled dot-product attention (sdpa_kernel), and the image rows blend the
+//     linear and the softmax results with eta = N_I / (N_I + N_T).
+//
+// All three use the 16x16x32 matrix-core step of common.hpp. Head dimension d
+// (a multiple of 8, at most 128) is padded to whole 16-row tiles and 32-deep
+// K steps with zeros; DT = ceil(d / 16) is a template parameter.
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace edit {
+
+constexpr int kKvChunk = 256;   // compressed tokens per state partial
+
+int kv_state_chunks(int Nc) { return (Nc + kKvChunk - 1) / kKvChunk; }
+int kv_state_dp(int d) { return 16 * ((d + 15) / 16); }
+int kv_state_dk(int d) { return 32 * ((d + 31) / 32); }
+
+// ---------------------------------------------------------------------------
+// KV state, partial sums over one chunk of compressed tokens.
+// D[n][k] = sum_j A[n][j] * K'_j[k] with A = [V'^T ; 1]: rows n < d give
+// S^T (S[k][n] = sum_j K'_j[k] V'_j[n]), row d gives z[k]. Tokens are the
+// matrix-core K dimension, so each 32-token slab of K' and V' is written to
+// LDS transposed (channel-major) and read back as 16-byte fragments.
+// partial[b][h][chunk][16*DR][16*DT] (fp32).
+// ---------------------------------------------------------------------------
+template <typename T, int DT, int DR>
+__global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
+                                                               int Nc, int heads, int d, int nchunks,
+                                                               float* __restrict__ partial) {
+  constexpr int PITCH = 40;                 // 32 tokens + pad, in elements (16 B multiple for both types)
+  constexpr int NT = DR * DT;
+  constexpr int TPW = (NT + 3) / 4;
+  __shared__ __attribute__((aligned(16))) T Kt[16 * DT * PITCH];
+  __shared__ __attribute__((aligned(16))) T At[16 * DR * PITCH];
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int C = heads * d;
+  const int j0 = chunk * kKvChunk, j1 = min(Nc, j0 + kKvChunk);
+  const int dc = d / 8;                     // 8-channel chunks per token (head slice)
+
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc_zero(acc[t]);
+
+  // Rows that never receive data stay zero: K' channels d..16*DT-1 and the
+  // rows of A past the ones row.
+  for (int i = tid; i < 16 * DT * PITCH; i += 256) Kt[i] = from_f32<T>(0.0f);
+  for (int i = tid; i < 16 * DR * PITCH; i += 256) At[i] = from_f32<T>(0.0f);
+  __syncthreads();
+
+  typedef typename Frag<T>::type FragT;
+  for (int js = j0; js < j1; js += 32) {
+    // Load 32 tokens x d channels of K' and V' (head h), transposed into LDS.
+    for (int e = tid; e < 2 * 32 * dc; e += 256) {
+      const int which = e / (32 * dc);      // 0: K', 1: V'
+      const int r = e % (32 * dc);
+      const int tok = r / dc, c8 = (r % dc) * 8;
+      const int j = js + tok;
+      float v[8];
+      if (j < j1) {
+        load8((which ? vc : kc) + ((size_t)b * Nc + j) * C + h * d + c8, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+      }
+      T* dst = (which ? At : Kt) + c8 * PITCH + tok;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i * PITCH] = from_f32<T>(v[i]);
+    }
+    if (tid < 32) At[d * PITCH + tid] = from_f32<T>(js + tid < j1 ? 1.0f : 0.0f);
+    __syncthreads();
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tile = wave + 4 * t;
+      if (tile < NT) {
+        const int tr = tile / DT, tc = tile % DT;
+        FragT a, bb;
+        frag_load(a, At + (tr * 16 + fr) * PITCH + fk);
+        frag_load(bb, Kt + (tc * 16 + fr) * PITCH + fk);
+        mma16(acc[t], a, bb);
+      }
+    }
+    __syncthreads();
+  }
+
+  float* out = partial + (((size_t)b * heads + h) * nchunks + chunk) * (16 * DR) * (16 * DT);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tile = wave + 4 * t;
+    if (tile < NT) {
+      const int tr = tile / DT, tc = tile % DT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        out[(tr * 16 + (lane >> 4) * 4 + r) * (16 * DT) + tc * 16 + (lane & 15)] = acc[t][r];
+    }
+  }
+}
+
+// Sum the chunk partials in chunk order and emit S (f32, [d][d] as S[k][n]),
+// z (f32), the apply kernel's operand st[2][DP][DK] (rows n, K = k: S^T,
+// padded with zeros; bf16 keeps a hi and a lo part so hi + lo carries ~16
+// mantissa bits of the fp32 sum) and zp[DK].
+template <typename T>
+__global__ __launch_bounds__(256) void kv_state_finalize_kernel(const float* __restrict__ partial, int heads,
+                                                                int d, int DR, int DT, int nchunks,
+                                                                float* __restrict__ S, float* __restrict__ z,
+                                                                T* __restrict__ st, float* __restrict__ zp) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int DP = 16 * DT, DK = 32 * ((DT + 1) / 2);
+  const int RW = 16 * DR, CW = 16 * DT;
+  const size_t bh = (size_t)b * heads + h;
+  const float* part = partial + bh * nchunks * RW * CW;
+  T* sthi = st + bh * 2 * DP * DK;
+  T* stlo = sthi + DP * DK;
+  for (int e = tid; e < DP * DK; e += 256) {
+    const int n = e / DK, k = e % DK;
+    float v = 0.0f;
+    if (n < d && k < d) {
+      for (int c = 0; c < nchunks; ++c) v += part[(size_t)c * RW * CW + n * CW + k];
+      S[(bh * d + k) * d + n] = v;
+    }
+    const T hi = from_f32<T>(v);
+    sthi[e] = hi;
+    stlo[e] = from_f32<T>(v - to_f32(hi));
+  }
+  for (int k = tid; k < DK; k += 256) {
+    float v = 0.0f;
+    if (k < d) {
+      for (int c = 0; c < nchunks; ++c) v += part[(size_t)c * RW * CW + d * CW + k];
+      z[bh * d + k] = v;
+    }
+    zp[bh * DK + k] = v;
+  }
+}
+
+template <typename T, int DT>
+static hipError_t kv_state_dispatch_dr(const T* kc, const T* vc, int B, int Nc, int heads, int d, float* partial,
+                                       int nchunks, hipStream_t s) {
+  dim3 grid(nchunks, heads, B);
+  if ((d + 16) / 16 == DT)
+    hipLaunchKernelGGL((kv_state_partial_kernel<T, DT, DT>), grid, dim3(256), 0, s, kc, vc, Nc, heads, d,
+                       nchunks, partial);
+  else
+    hipLaunchKernelGGL((kv_state_partial_kernel<T, DT, DT + 1>), grid, dim3(256), 0, s, kc, vc, Nc, heads, d,
+                       nchunks, partial);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_kv_state(const T* kc, const T* vc, int B, int Nc, int heads, int d, float* partial,
+                           int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s) {
+  const int DT = (d + 15) / 16, DR = (d + 16) / 16;
+  hipError_t e;
+  switch (DT) {
+    case 1: e = kv_state_dispatch_dr<T, 1>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
+    case 2: e = kv_state_dispatch_dr<T, 2>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
+    case 3: e = kv_state_dispatch_dr<T, 3>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
+    case 4: e = kv_state_dispatch_dr<T, 4>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
+    case 5: e = kv_state_dispatch_dr<T, 5>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
+    case 6: e = kv_state_dispatch_dr<T, 6>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
+    case 7: e = kv_state_dispatch_dr<T, 7>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
+    case 8: e = kv_state_dispatch_dr<T, 8>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((kv_state_finalize_kernel<T>), dim3(heads, B), dim3(256), 0, s, partial, heads, d, DR, DT,
+                     nchunks, S, z, st, zp);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Apply: y_i = (Q_i S) / (Q_i . z + eps) per head. The wave computes
+// Y^T = S^T Q^T on 16-token tiles: A = st (kept in registers for the whole
+// wave), B = 16 queries read straight from memory as 16-byte fragments.
+// Lane l ends with 4 consecutive output channels of token l % 16 (8-byte
+// store). The denominator is a VALU dot of the lane's query slice with z,
+// summed over the four lanes that share a token.
+// ---------------------------------------------------------------------------
+constexpr int kApplyTilesPerWave = 8;
+
+template <typename T, int DT>
+__global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict__ q, int ldq,
+                                                            const T* __restrict__ st, const float* __restrict__ zp,
+                                                            int N, int heads, int d, float eps,
+                                                            T* __restrict__ y, int ldy) {
+  constexpr int KS = (DT + 1) / 2;
+  constexpr int DP = 16 * DT, DK = 32 * KS;
+  constexpr bool SPLIT = std::is_same<T, bf16>::value;
+  typedef typename Frag<T>::type FragT;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int fr = lane & 15, g = lane >> 4;
+  const size_t bh = (size_t)b * heads + h;
+  const T* sthi = st + bh * 2 * DP * DK;
+  const T* stlo = sthi + DP * DK;
+
+  FragT ahi[DT][KS], alo[DT][KS];
+#pragma unroll
+  for (int tn = 0; tn < DT; ++tn)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      frag_load(ahi[tn][s], sthi + (tn * 16 + fr) * DK + s * 32 + g * 8);
+      if (SPLIT) frag_load(alo[tn][s], stlo + (tn * 16 + fr) * DK + s * 32 + g * 8);
+    }
+  float zr[KS][8];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zr[s][i] = zp[bh * DK + s * 32 + g * 8 + i];
+
+  const int ntiles = (N + 15) / 16;
+  const int tile0 = (blockIdx.x * 4 + wave) * kApplyTilesPerWave;
+  for (int tt = 0; tt < kApplyTilesPerWave; ++tt) {
+    const int tile = tile0 + tt;
+    if (tile >= ntiles) break;
+    const int tok = tile * 16 + fr;
+    const bool tv = tok < N;
+    const T* qrow = q + ((size_t)b * N + (tv ? tok : 0)) * ldq + h * d;
+    FragT bq[KS];
+    float den = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int k = s * 32 + g * 8;
+      if (tv && k < d) {
+        frag_load(bq[s], qrow + k);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) den += to_f32(bq[s][i]) * zr[s][i];
+      } else {
+        frag_zero(bq[s]);
+      }
+    }
+    den += __shfl_xor(den, 16, 64);
+    den += __shfl_xor(den, 32, 64);
+    const float inv = 1.0f / (den + eps);
+    f32x4 acc[DT];
+#pragma unroll
+    for (int tn = 0; tn < DT; ++tn) {
+      acc_zero(acc[tn]);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (SPLIT) mma16(acc[tn], alo[tn][s], bq[s]);
+        mma16(acc[tn], ahi[tn][s], bq[s]);
+      }
+    }
+    if (tv) {
+      T* yrow = y + ((size_t)b * N + tok) * ldy + h * d;
+#pragma unroll
+      for (int tn = 0; tn < DT; ++tn) {
+        const int n = tn * 16 + g * 4;
+        if (n < d) {
+          float o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = acc[tn][r] * inv;
+          store4(yrow + n, o);
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_linattn_apply(const T* q, int ldq, const T* st, const float* zp, int B, int N, int heads,
+                                int d, float eps, T* y, int ldy, hipStream_t s) {
+  const int ntiles = (N + 15) / 16;
+  const int blocks = (ntiles + 4 * kApplyTilesPerWave - 1) / (4 * kApplyTilesPerWave);
+  dim3 grid(blocks, heads, B), block(256);
+  switch ((d + 15) / 16) {
+#define EDIT_APPLY_CASE(DTV)                                                                        \
+  case DTV:                                                                                         \
+    hipLaunchKernelGGL((linattn_apply_kernel<T, DTV>), grid, block, 0, s, q, ldq, st, zp, N, heads, d, \
+                       eps, y, ldy);                                                                \
+    break;
+    EDIT_APPLY_CASE(1) EDIT_APPLY_CASE(2) EDIT_APPLY_CASE(3) EDIT_APPLY_CASE(4)
+    EDIT_APPLY_CASE(5) EDIT_APPLY_CASE(6) EDIT_APPLY_CASE(7) EDIT_APPLY_CASE(8)
+#undef EDIT_APPLY_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Softmax attention over up to two key/value segments (the hybrid's
+// image->text and text->[image;text] blocks), scale 1/sqrt(d), online
+// softmax over 32-key slabs. Each wave owns 16 queries. S^T = K Q^T comes out
+// with lane l holding 8 key scores of query l % 16, which is exactly the B
+// fragment of O^T = V^T P^T when V^T is read with the same key order
+// (keys 4g..4g+3 and 16+4g..16+4g+3 for lane group g), so P never leaves
+// registers.
+// ---------------------------------------------------------------------------
+template <typename T, int DT>
+__global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
+  constexpr int KS = (DT + 1) / 2;
+  constexpr int DK = 32 * KS;
+  constexpr int KPITCH = DK + 8;            // elements; 16 B multiple
+  constexpr int VPITCH = 40;
+  typedef typename Frag<T>::type FragT;
+  __shared__ __attribute__((aligned(16))) T Ks[32 * KPITCH];
+  __shared__ __attribute__((aligned(16))) T Vt[16 * DT * VPITCH];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, g = lane >> 4;
+  const int d = p.d;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)d);   // log2(e) / sqrt(d)
+
+  for (int i = tid; i < 32 * KPITCH; i += 256) Ks[i] = from_f32<T>(0.0f);
+  for (int i = tid; i < 16 * DT * VPITCH; i += 256) Vt[i] = from_f32<T>(0.0f);
+
+  const int qi = blockIdx.x * 64 + wave * 16 + fr;
+  const bool qv = qi < p.Nq;
+  const T* qrow = p.q + ((size_t)b * p.Nq + (qv ? qi : 0)) * p.ldq + h * d;
+  FragT bq[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int k = s * 32 + g * 8;
+    if (qv && k < d) frag_load(bq[s], qrow + k);
+    else frag_zero(bq[s]);
+  }
+  f32x4 acc[DT];
+#pragma unroll
+  for (int tn = 0; tn < DT; ++tn) acc_zero(acc[tn]);
+  float mrun = -INFINITY, lrun = 0.0f;
+  const int dc = d / 8;
+  const int Ntot = p.N1 + p.N2;
+  __syncthreads();
+
+  for (int k0 = 0; k0 < Ntot; k0 += 32) {
+    for (int e = tid; e < 2 * 32 * dc; e += 256) {
+      const int which = e / (32 * dc);
+      const int r = e % (32 * dc);
+      const int key = r / dc, c8 = (r % dc) * 8;
+      const int kk = k0 + key;
+      float v[8];
+      if (kk < Ntot) {
+        const bool first = kk < p.N1;
+        const T* base = first ? (which ? p.v1 : p.k1) : (which ? p.v2 : p.k2);
+        const int ld = first ? p.ldkv1 : p.ldkv2;
+        const int nseg = first ? p.N1 : p.N2;
+        const int j = first ? kk : kk - p.N1;
+        load8(base + ((size_t)b * nseg + j) * ld + h * d + c8, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+      }
+      if (which == 0) {
+        store8(Ks + key * KPITCH + c8, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) Vt[(c8 + i) * VPITCH + key] = from_f32<T>(v[i]);
+      }
+    }
+    __syncthreads();
+
+    // Scores of keys 16*kt + 4g + r for query fr.
+    f32x4 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      acc_zero(sc[kt]);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        FragT ak;
+        frag_load(ak, Ks + (kt * 16 + fr) * KPITCH + s * 32 + g * 8);
+        mma16(sc[kt], ak, bq[s]);
+      }
+    }
+    float pv[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = k0 + kt * 16 + g * 4 + r;
+        const float v = kk < Ntot ? sc[kt][r] * sl2 : -INFINITY;
+        pv[kt * 4 + r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(mrun, tmax);
+    const float corr = exp2f(mrun - mnew);
+    mrun = mnew;
+    float psum = 0.0f;
+    float pf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pf[i] = exp2f(pv[i] - mnew);
+      psum += pf[i];
+    }
+    lrun = lrun * corr + psum;
+    FragT bp;
+    frag_from_f32(bp, pf);
+#pragma unroll
+    for (int tn = 0; tn < DT; ++tn) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[tn][r] *= corr;
+      const T* vrow = Vt + (tn * 16 + fr) * VPITCH;
+      float vv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vv[i] = to_f32(vrow[g * 4 + i]);
+        vv[4 + i] = to_f32(vrow[16 + g * 4 + i]);
+      }
+      FragT av;
+      frag_from_f32(av, vv);
+      mma16(acc[tn], av, bp);
+    }
+    __syncthreads();
+  }
+
+  lrun += __shfl_xor(lrun, 16, 64);
+  lrun += __shfl_xor(lrun, 32, 64);
+  const float inv = 1.0f / lrun;
+  if (qv) {
+    T* orow = p.out + ((size_t)b * p.Nq + qi) * p.ldo + h * d;
+    const T* brow = p.blend_src ? p.blend_src + ((size_t)b * p.Nq + qi) * p.ldbs + h * d : nullptr;
+#pragma unroll
+    for (int tn = 0; tn < DT; ++tn) {
+      const int n = tn * 16 + g * 4;
+      if (n < d) {
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = acc[tn][r] * inv;
+        if (brow) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = p.alpha * to_f32(brow[n + r]) + p.beta * o[r];
+        }
+        store4(orow + n, o);
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s) {
+  if (a.Nq <= 0) return hipSuccess;
+  dim3 grid((a.Nq + 63) / 64, a.heads, a.B), block(256);
+  switch ((a.d + 15) / 16) {
+#define EDIT_SDPA_CASE(DTV) \
+  case DTV: hipLaunchKernelGGL((sdpa_kernel<T, DTV>), grid, block, 0, s, a); break;
+    EDIT_SDPA_CASE(1) EDIT_SDPA_CASE(2) EDIT_SDPA_CASE(3) EDIT_SDPA_CASE(4)
+    EDIT_SDPA_CASE(5) EDIT_SDPA_CASE(6) EDIT_SDPA_CASE(7) EDIT_SDPA_CASE(8)
+#undef EDIT_SDPA_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+#define EDIT_INST(T)                                                                                     \
+  template hipError_t launch_kv_state<T>(const T*, const T*, int, int, int, int, float*, int, float*,   \
+                                         float*, T*, float*, hipStream_t);                              \
+  template hipError_t launch_linattn_apply<T>(const T*, int, const T*, const float*, int, int, int, int, \
+                                              float, T*, int, hipStream_t);                             \
+  template hipError_t launch_sdpa<T>(const SdpaArgs<T>&, hipStream_t);
+EDIT_INST(bf16)
+EDIT_INST(float)
+#undef EDIT_INST
+
+}  // namespace edit

@@ -1,0 +1,91 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace edit {
+
+typedef __bf16 bf16;
+
+// How the GEMM's A operand is produced from memory.
+enum AMode {
+  A_PLAIN = 0,   // A[m][k] = a[m*lda + k]
+  A_CONV3 = 1,   // implicit 3x3 stride-1 pad-1 convolution: k = tap*Cin + cin over an image [B][H][W][Cin]
+  A_GNACT = 2    // A[m][k] = LeakyReLU(a[m*lda + k] * scale[b][k] + shift[b][k]), b = m / rows_per_batch
+};
+// What the epilogue adds before the store.
+enum EMode {
+  E_BIAS = 0,       // C = acc + bias
+  E_BIAS_RELU = 1,  // C = max(acc + bias, 0)
+  E_BIAS_RES = 2    // C = acc + bias + R
+};
+
+// C[M][N] = A[M][K] * B[N][K]^T + epilogue. B and the bias may come in up
+// to three row segments of seg_rows rows each (segment s covers rows
+// s*seg_rows .. (s+1)*seg_rows-1), so [W_k; W_v] or [W_q; W_k; W_v] need no
+// concatenated copy.
+template <typename T>
+struct GemmArgs {
+  int M, N, K;
+  const T* A;
+  int lda;
+  int H, W, Cin;               // A_CONV3 geometry (M = B*H*W, K = 9*Cin)
+  const float* scale;          // A_GNACT: [B][K]
+  const float* shift;          // A_GNACT: [B][K]
+  int rows_per_batch;          // A_GNACT
+  const T* Bseg[3];
+  const T* bias[3];
+  int seg_rows;
+  int ldb;
+  T* C;
+  int ldc;
+  const T* R;                  // E_BIAS_RES
+  int ldr;
+};
+
+template <typename T>
+hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s);
+
+// GroupNorm statistics of x [B][HW][Cg*G]: per (b, group) mean and rstd,
+// and the per-channel affine folded into scale/shift [B][C].
+template <typename T>
+hipError_t launch_groupnorm_stats(const T* x, int B, int HW, int C, int G, const T* gamma,
+                                  const T* beta, float eps, float* partial, int nchunks,
+                                  float* stat, float* scale, float* shift, hipStream_t s);
+int groupnorm_chunks(int HW);
+
+// Depthwise 3x3 stride-2 pad-1 conv of two channel groups side by side in
+// kv0 [B][H][W][2C]: keys (channels 0..C-1, then ReLU) and values (C..2C-1).
+template <typename T>
+hipError_t launch_dwconv_s2(const T* kv0, int B, int H, int W, int C, const T* dwk, const T* dbk,
+                            const T* dwv, const T* dbv, T* kc, T* vc, hipStream_t s);
+
+// Per-head state of the compressed keys/values: S = K'^T V', z = sum K'.
+// Writes f32 S [B][h][d][d], z [B][h][d] and the apply kernel's operand:
+// st [B][h][2][DP][DK] of T (S transposed, split hi/lo for bf16), zp [B][h][DK] f32.
+template <typename T>
+hipError_t launch_kv_state(const T* kc, const T* vc, int B, int Nc, int heads, int d, float* partial,
+                           int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s);
+int kv_state_chunks(int Nc);
+int kv_state_dp(int d);   // padded rows of the state operand
+int kv_state_dk(int d);   // padded K of the state operand
+
+// y[b][n][h*d + j] = (q S)_j / (q . z + eps) per head.
+template <typename T>
+hipError_t launch_linattn_apply(const T* q, int ldq, const T* st, const float* zp, int B, int N,
+                                int heads, int d, float eps, T* y, int ldy, hipStream_t s);
+
+// Softmax attention of queries q over up to two key/value segments, per head,
+// scale 1/sqrt(d). If blend_src is given: out = alpha * blend_src + beta * attn.
+template <typename T>
+struct SdpaArgs {
+  const T* q; int ldq; int Nq;
+  const T* k1; const T* v1; int ldkv1; int N1;
+  const T* k2; const T* v2; int ldkv2; int N2;
+  int B, heads, d;
+  T* out; int ldo;
+  const T* blend_src; int ldbs; float alpha, beta;
+};
+template <typename T>
+hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s);
+
+}  // namespace edit

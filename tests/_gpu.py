@@ -1,0 +1,101 @@
+"""Helpers of the GPU parity tests: move seeded inputs to the device, call
+the library through its binding, and read back outputs and the
+intermediates the workspace layout names (test infrastructure)."""
+import numpy as np
+import torch
+
+import linear_compressed_attention_amd as lca
+
+TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def to_dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(TORCH_DTYPE[dtype])
+
+
+def dev_weights(w, dtype):
+    return {k: to_dev(v, dtype) for k, v in w.items()}
+
+
+def poison(t):
+    """Fill with all-ones bytes (NaN in bf16 and f32) so unwritten elements show."""
+    t.view(torch.uint8).fill_(0xFF)
+
+
+def _view(ws, off, shape, dtype):
+    n = int(np.prod(shape))
+    es = torch.tensor([], dtype=dtype).element_size()
+    return ws[off:off + n * es].view(dtype).view(*shape)
+
+
+def read_intermediates(shape, ws, n_text=0):
+    lay = lca.edit_attn_workspace_layout(shape, n_text)
+    s = shape
+    T = TORCH_DTYPE[s.dtype]
+    f32 = torch.float32
+    B, N, C, h, d = s.B, s.N, s.C, s.heads, s.head_dim
+    out = {
+        "xc": _view(ws, lay["xc"], (B, N, s.Cr), T),
+        "gn_stat": _view(ws, lay["gn_stat"], (B, s.gn_groups, 2), f32),
+        "xt": _view(ws, lay["xt"], (B, N, C), T),
+        "q": _view(ws, lay["q"], (B, N, C), T),
+        "kv0": _view(ws, lay["kv0"], (B, N, 2 * C), T),
+        "kc": _view(ws, lay["kc"], (B, s.Nc, C), T),
+        "vc": _view(ws, lay["vc"], (B, s.Nc, C), T),
+        "S": _view(ws, lay["S"], (B, h, d, d), f32),
+        "z": _view(ws, lay["z"], (B, h, d), f32),
+        "y": _view(ws, lay["y"], (B, N, C), T),
+    }
+    if n_text:
+        out["qkv_t"] = _view(ws, lay["qkv_t"], (B, n_text, 3 * C), T)
+        out["y_img"] = _view(ws, lay["y_img"], (B, N, C), T)
+        out["y_txt"] = _view(ws, lay["y_txt"], (B, n_text, C), T)
+    return {k: v.float().cpu().numpy() for k, v in out.items()}
+
+
+def run_edit(shape, inp, stream=None, with_intermediates=True):
+    x = to_dev(inp["x"], shape.dtype)
+    w = dev_weights(inp["w"], shape.dtype)
+    y = torch.empty_like(x)
+    ws = torch.empty(lca.edit_attn_workspace_size(shape), dtype=torch.uint8, device="cuda")
+    poison(y)
+    poison(ws)
+    lca.edit_attn_forward(shape, w, x, y, ws, stream)
+    torch.cuda.synchronize()
+    res = {"out": y.float().cpu().numpy()}
+    if with_intermediates:
+        res.update(read_intermediates(shape, ws))
+    return res
+
+
+def run_hybrid(shape, inp, n_text, with_intermediates=True):
+    x = to_dev(inp["x"], shape.dtype)
+    w = dev_weights(inp["w"], shape.dtype)
+    xt = to_dev(inp["x_txt"], shape.dtype) if n_text else None
+    wt = dev_weights(inp["w_txt"], shape.dtype) if n_text else None
+    y = torch.empty_like(x)
+    yt = torch.empty_like(xt) if n_text else None
+    ws = torch.empty(lca.mmedit_hybrid_workspace_size(shape, n_text), dtype=torch.uint8, device="cuda")
+    poison(y)
+    poison(ws)
+    if yt is not None:
+        poison(yt)
+    lca.mmedit_hybrid_forward(shape, n_text, w, wt, x, xt, y, yt, ws)
+    torch.cuda.synchronize()
+    res = {"out": y.float().cpu().numpy()}
+    if yt is not None:
+        res["out_txt"] = yt.float().cpu().numpy()
+    if with_intermediates:
+        res.update(read_intermediates(shape, ws, n_text))
+    return res
+
+
+def oracle_views(tr, shape):
+    """The oracle trace in the shapes of read_intermediates."""
+    import numpy as np
+    rstd = 1.0 / np.sqrt(tr["gn_var"] + 1e-5)
+    return {
+        "xc": tr["xc"], "gn_stat": np.stack([tr["gn_mean"], rstd], axis=-1), "xt": tr["xt"], "q": tr["q"],
+        "kv0": np.concatenate([tr["k0"], tr["v0"]], axis=-1), "kc": tr["kc"], "vc": tr["vc"],
+        "S": tr["S"], "z": tr["z"], "out": tr["out"],
+    }

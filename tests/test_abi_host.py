@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (CPU only, no kernel runs): the library
+loads, exports every function include/edit_attn.h declares, sizes its
+workspace, and rejects bad arguments before touching a device."""
+import ctypes
+import subprocess
+
+import pytest
+import torch
+
+import linear_compressed_attention_amd as lca
+from seeded_inputs import CONFIGS, make_shape
+
+
+def test_exports_every_header_symbol():
+    names = lca.header_symbols()
+    assert {"edit_attn_forward", "mmedit_hybrid_forward", "edit_attn_workspace_size",
+            "mmedit_hybrid_workspace_size", "edit_attn_workspace_layout", "edit_status_string",
+            "edit_last_error"} <= set(names)
+    lib = ctypes.CDLL(lca.lib_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", lca.lib_path()], capture_output=True, text=True).stdout
+    for n in names:
+        assert f" T {n}\n" in dyn, n
+
+
+def test_library_has_gfx950_code_object():
+    sec = subprocess.run(["objdump", "-h", lca.lib_path()], capture_output=True, text=True).stdout
+    assert ".hip_fatbin" in sec
+    with open(lca.lib_path(), "rb") as f:
+        assert b"amdgcn-amd-amdhsa--gfx950" in f.read()
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workspace_size_and_layout(name):
+    s = CONFIGS[name]
+    n = lca.mmedit_hybrid_workspace_size(s, s.n_text)
+    lay = lca.edit_attn_workspace_layout(s, s.n_text)
+    assert lay["total"] == n
+    es = 2 if s.dtype == "bf16" else 4
+    assert lay["y"] + s.B * s.N * s.C * es <= n
+    offs = sorted(v for k, v in lay.items() if k != "total" and v)
+    assert all(o % 256 == 0 for o in offs)
+    if s.n_text == 0:
+        assert lca.edit_attn_workspace_size(s) == n
+
+
+BAD = [
+    dict(C=60),                     # C != heads * head_dim
+    dict(reduction=5),              # r does not divide C
+    dict(gn_groups=5),              # G does not divide C/r
+    dict(B=0), dict(H=-1), dict(heads=0),
+]
+
+
+@pytest.mark.parametrize("delta", BAD)
+def test_bad_shapes_rejected(delta):
+    base = dict(B=1, H=8, W=8, C=64, heads=2, head_dim=32, reduction=4, gn_groups=4, eps=1e-6, dtype="bf16")
+    base.update(delta)
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_workspace_size(base)
+    assert e.value.status == 1
+
+
+def test_unsupported_shapes():
+    base = dict(B=1, H=8, W=8, C=160, heads=1, head_dim=160, reduction=4, gn_groups=4, eps=1e-6, dtype="bf16")
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_workspace_size(base)
+    assert e.value.status == 2 and "head_dim" in e.value.detail
+    base = dict(B=1, H=8, W=8, C=36, heads=3, head_dim=12, reduction=4, gn_groups=3, eps=1e-6, dtype="bf16")
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_workspace_size(base)
+    assert e.value.status == 2
+
+
+def _fake_weights(base=0x100000):
+    return {n: base + 0x1000 * i for i, n in enumerate(lca.IMAGE_WEIGHT_FIELDS)}
+
+
+class _FakeWS:
+    """A pointer/size pair standing in for a workspace tensor (never dereferenced)."""
+    def __init__(self, ptr, n):
+        self.ptr, self.n = ptr, n
+
+    def data_ptr(self):
+        return self.ptr
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+SHAPE = make_shape(B=1, H=8, W=8, C=64, heads=2, head_dim=32, reduction=4, gn_groups=4, dtype="bf16")
+
+
+def _call(w=None, x=0x9000000, y=0xA000000, ws=None):
+    ws = ws or _FakeWS(0xB000000, lca.edit_attn_workspace_size(SHAPE))
+    lca.edit_attn_forward(SHAPE, w or _fake_weights(), x, y, ws, stream=0)
+
+
+def test_argument_errors_before_any_launch():
+    w = _fake_weights(); w["w_q"] = None
+    with pytest.raises(lca.EditError) as e:
+        _call(w=w)
+    assert e.value.status == 1 and "w_q" in e.value.detail
+    w = _fake_weights(); w["b_o"] += 8
+    with pytest.raises(lca.EditError) as e:
+        _call(w=w)
+    assert e.value.status == 1 and "aligned" in e.value.detail
+    with pytest.raises(lca.EditError) as e:
+        _call(x=0)
+    assert e.value.status == 1
+    with pytest.raises(lca.EditError) as e:
+        _call(ws=_FakeWS(0xB000000, 100))
+    assert e.value.status == 3
+    with pytest.raises(lca.EditError) as e:
+        _call(ws=_FakeWS(0xB000010, 1 << 30))
+    assert e.value.status == 1 and "256" in e.value.detail
+    with pytest.raises(lca.EditError) as e:
+        _call(y=0x9000000 + 64)
+    assert e.value.status == 1 and "overlap" in e.value.detail
+
+
+def test_hybrid_argument_errors():
+    ws = _FakeWS(0xB000000, lca.mmedit_hybrid_workspace_size(SHAPE, 5))
+    with pytest.raises(lca.EditError) as e:
+        lca.mmedit_hybrid_forward(SHAPE, -1, _fake_weights(), None, 0x9000000, None, 0xA000000, None, ws, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(lca.EditError) as e:
+        lca.mmedit_hybrid_forward(SHAPE, 5, _fake_weights(), None, 0x9000000, 0x9800000, 0xA000000, 0xA800000, ws,
+                                  stream=0)
+    assert e.value.status == 1 and "text weights" in e.value.detail
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")
+def test_no_device_is_reported():
+    with pytest.raises(lca.EditError) as e:
+        _call()
+    assert e.value.status == 4
+
+
+def test_status_strings():
+    assert lca.edit_status_string(0) == "EDIT_OK"
+    assert "WORKSPACE" in lca.edit_status_string(3)

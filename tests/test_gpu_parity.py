@@ -1,0 +1,147 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Every intermediate the workspace layout names (xc, GN statistics, xt, q,
+kv0, kc, vc, S, z, y) and the output are compared element by element with
+the float64 oracle on the same seeded inputs: max |g - o| / max |o| per
+tensor <= 2e-2 for bf16, <= 1e-4 for fp32. Outputs and workspace are filled
+with NaN bytes first, so an element a kernel fails to write shows up.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import edit_oracle as O
+from seeded_inputs import CONFIGS, make_inputs, make_shape
+from tests._metrics import BF16_TOL, F32_TOL, centred_rel_err, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests import _gpu as G
+
+
+def _tol(s):
+    return BF16_TOL if s.dtype == "bf16" else F32_TOL
+
+
+def _announce(tag):
+    print(f"\n[gpu-case] {tag}", flush=True)
+
+
+def check_edit(s, seed=0, gn_affine_random=False, x_std=None, centred=("xt", "q", "kc", "vc")):
+    inp = make_inputs(s, seed=seed, gn_affine_random=gn_affine_random, x_std=x_std)
+    _announce(f"edit {s} seed={seed}")
+    got = G.run_edit(s, inp)
+    tr = {}
+    O.edit_attn_forward(inp["x"], inp["w"], s, tr)
+    ref = G.oracle_views(tr, s)
+    ref["y"] = tr["y"]
+    tol = _tol(s)
+    errs = {}
+    for k, r in ref.items():
+        g = got[k]
+        assert np.isfinite(g).all(), f"{k}: non-finite elements (unwritten or overflow)"
+        errs[k] = max_rel_err(g, r)
+    for k in centred:
+        errs[k + "_centred"] = centred_rel_err(got[k], ref[k])
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"over tolerance {tol}: {bad}"
+    return got, tr
+
+
+SMALL = {
+    "f32_d32_ragged": make_shape(B=2, H=13, W=11, C=128, heads=4, head_dim=32, reduction=4, gn_groups=4,
+                                 dtype="f32", x_std=1.0),
+    "bf16_d64_ragged": make_shape(B=2, H=13, W=11, C=256, heads=4, head_dim=64, reduction=4, gn_groups=8,
+                                  dtype="bf16", x_std=1.0),
+    "bf16_d72_ragged": make_shape(B=1, H=21, W=19, C=288, heads=4, head_dim=72, reduction=4, gn_groups=8,
+                                  dtype="bf16", x_std=1.0),
+    "f32_d72": make_shape(B=1, H=9, W=14, C=288, heads=4, head_dim=72, reduction=4, gn_groups=4,
+                          dtype="f32", x_std=1.0),
+    "bf16_d8": make_shape(B=1, H=10, W=10, C=64, heads=8, head_dim=8, reduction=4, gn_groups=2,
+                          dtype="bf16", x_std=1.0),
+    "bf16_d128": make_shape(B=1, H=12, W=16, C=256, heads=2, head_dim=128, reduction=4, gn_groups=8,
+                            dtype="bf16", x_std=1.0),
+    "f32_1x1": make_shape(B=2, H=1, W=1, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
+                          dtype="f32", x_std=1.0),
+    "f32_1x5": make_shape(B=1, H=1, W=5, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
+                          dtype="f32", x_std=1.0),
+}
+
+
+def test_tiny_config_f32():
+    check_edit(CONFIGS["tiny"])
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_shapes(name):
+    check_edit(SMALL[name], seed=1, gn_affine_random=True)
+
+
+@pytest.mark.parametrize("name", ["pixart1024", "pixart2048", "pixart4096"])
+def test_pixart_full_size(name):
+    check_edit(CONFIGS[name])
+
+
+def check_hybrid(s, n_text, seed=0):
+    inp = make_inputs(s, seed=seed, n_text=n_text)
+    _announce(f"hybrid {s} n_text={n_text} seed={seed}")
+    got = G.run_hybrid(s, inp, n_text)
+    tr = {}
+    out_i, out_t = O.mmedit_hybrid_forward(inp["x"], inp.get("x_txt"), inp["w"], inp.get("w_txt"), s, tr)
+    tol = _tol(s)
+    pairs = {"out": (got["out"], out_i), "q": (got["q"], tr["q"]), "kc": (got["kc"], tr["kc"]),
+             "vc": (got["vc"], tr["vc"]), "y_lin": (got["y"], tr["y_lin"])}
+    if n_text:
+        pairs.update({"out_txt": (got["out_txt"], out_t), "y_img": (got["y_img"], tr["y"]),
+                      "y_txt": (got["y_txt"], tr["y_txt"]),
+                      "qkv_t": (got["qkv_t"], np.concatenate([tr["q_t"], tr["k_t"], tr["v_t"]], -1))})
+    errs = {}
+    for k, (g, r) in pairs.items():
+        assert np.isfinite(g).all(), f"{k}: non-finite elements"
+        errs[k] = max_rel_err(g, r)
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"over tolerance {tol}: {bad}"
+    return got
+
+
+HYB = {
+    "f32_small": make_shape(B=2, H=9, W=7, C=128, heads=2, head_dim=64, reduction=4, gn_groups=4, dtype="f32",
+                            x_std=1.0),
+    "bf16_small": make_shape(B=2, H=12, W=10, C=192, heads=3, head_dim=64, reduction=4, gn_groups=4, dtype="bf16",
+                             x_std=1.0),
+    "bf16_d72": make_shape(B=1, H=8, W=8, C=288, heads=4, head_dim=72, reduction=4, gn_groups=4, dtype="bf16",
+                           x_std=1.0),
+}
+
+
+@pytest.mark.parametrize("name,n_text", [("f32_small", 37), ("bf16_small", 77), ("bf16_d72", 5), ("f32_small", 1)])
+def test_hybrid_small(name, n_text):
+    check_hybrid(HYB[name], n_text, seed=2)
+
+
+def test_hybrid_sd35m_full_size():
+    s = CONFIGS["sd35m_hybrid"]
+    check_hybrid(s, s.n_text)
+
+
+@pytest.mark.parametrize("name", ["f32_small", "bf16_small"])
+def test_hybrid_without_text_equals_edit(name):
+    s = HYB[name]
+    inp = make_inputs(s, seed=3)
+    _announce(f"hybrid n_text=0 vs edit {name}")
+    a = G.run_hybrid(s, inp, 0, with_intermediates=False)["out"]
+    b = G.run_edit(s, inp, with_intermediates=False)["out"]
+    np.testing.assert_array_equal(a, b)
+
+
+def test_bitwise_deterministic():
+    s = SMALL["bf16_d72_ragged"]
+    inp = make_inputs(s, seed=4)
+    _announce("determinism")
+    a = G.run_edit(s, inp)
+    b = G.run_edit(s, inp)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
