@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of one EDiT attention-layer forward on one MI355X.
+
+One step = one edit_attn_forward call (ConvFusion queries, Spatial-Compressor
+keys/values, linear attention, output projection) over one batch of the
+workload's synthetic input, which is resident in HBM before timing starts.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload pixart2048]
+
+Prints one JSON line. `value` is image tokens/s over the K timed steps
+(HIP events on the stream the library launches on, bracketed by device
+synchronisation). `roofline` covers the step with the longest average
+duration: its algorithmic work per launch over its average duration, timed
+live with events the library records between its steps, against MI355X's
+published peak. `cpu_baseline` times the float64 CPU oracle on a bounded
+sample of the same workload on the host's cores.
+"""
+import argparse
+import ctypes
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core (f32: vector/matrix fp32)
+
+STEP_NAMES = ["cf_conv3x3", "gn_stats", "cf_restore", "q_proj", "kv_proj", "sc_dwconv", "kv_state",
+              "linattn_apply", "out_proj"]
+STEP_KERNELS = {  # kernels launched per step (rocprofv3 names start with these)
+    "cf_conv3x3": "gemm_kernel<..., A_CONV3, E_BIAS>", "gn_stats": "gn_partial_kernel + gn_finalize_kernel",
+    "cf_restore": "gemm_kernel<..., A_GNACT, E_BIAS_RES>", "q_proj": "gemm_kernel<..., A_PLAIN, E_BIAS_RELU>",
+    "kv_proj": "gemm_kernel<..., A_PLAIN, E_BIAS>", "sc_dwconv": "dwconv_s2_kernel",
+    "kv_state": "kv_state_partial_kernel + kv_state_finalize_kernel", "linattn_apply": "linattn_apply_kernel",
+    "out_proj": "gemm_kernel<..., A_PLAIN, E_BIAS>",
+}
+
+
+def algorithmic_work(s):
+    """Per-launch algorithmic flops and HBM bytes of each step: every input
+    read once, every output written once, weights included."""
+    es = 2 if s.dtype == "bf16" else 4
+    B, N, C, Cr, h, d = s.B, s.N, s.C, s.Cr, s.heads, s.head_dim
+    M, Mc = B * N, B * s.Nc
+    st = B * h * (d * d + d) * 4
+    return {
+        "cf_conv3x3": (2.0 * M * Cr * 9 * C, es * (M * C + Cr * 9 * C + M * Cr + Cr)),
+        "gn_stats": (3.0 * M * Cr, es * M * Cr),
+        "cf_restore": (2.0 * M * C * Cr, es * (M * Cr + 2 * M * C + C * Cr + C)),
+        "q_proj": (2.0 * M * C * C, es * (2 * M * C + C * C + C)),
+        "kv_proj": (2.0 * M * 2 * C * C, es * (M * C + 2 * M * C + 2 * C * C + 2 * C)),
+        "sc_dwconv": (2.0 * 9 * Mc * 2 * C, es * (2 * M * C + 2 * Mc * C + 2 * 10 * C)),
+        "kv_state": (2.0 * Mc * C * (d + 1), es * 2 * Mc * C + st),
+        "linattn_apply": (2.0 * M * C * (d + 1), es * 2 * M * C + st),
+        "out_proj": (2.0 * M * C * C, es * (2 * M * C + C * C + C)),
+    }
+
+
+STEP_BOUND = {"cf_conv3x3": "mfma", "gn_stats": "hbm", "cf_restore": "hbm", "q_proj": "mfma", "kv_proj": "mfma",
+              "sc_dwconv": "hbm", "kv_state": "hbm", "linattn_apply": "hbm", "out_proj": "mfma"}
+
+
+class HipEvents:
+    """hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def cpu_baseline(shape, inp, runs):
+    """The float64 oracle, as it stands, on the host cores."""
+    from threadpoolctl import threadpool_info
+    from oracle import edit_oracle as O
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        O.edit_attn_forward(inp["x"], inp["w"], shape)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": shape.B * shape.N / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{runs} full float64 layer forwards of the same workload ({shape.B * shape.N} tokens each), "
+                      f"median {med:.2f} s; cores = BLAS threads",
+            "seconds_per_layer": med}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="pixart2048")
+    ap.add_argument("--cpu-runs", type=int, default=3, help="oracle runs for cpu_baseline (0 = skip)")
+    ap.add_argument("--profile-steps", type=int, default=None,
+                    help="timed forwards for the per-step breakdown (default: --steps)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
+              "build: the layer shards by grid bands with one per-head state all-reduce, which is designed "
+              "but not implemented here.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import linear_compressed_attention_amd as lca
+    from seeded_inputs import CONFIGS, make_inputs
+
+    s = CONFIGS[args.workload]
+    assert s.n_text == 0, "bench times the EDiT layer; the hybrid workload is a parity case"
+    inp = make_inputs(s, seed=0)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    x = torch.from_numpy(inp["x"]).to(dev).to(tdt)
+    w = {k: torch.from_numpy(v).to(dev).to(tdt) for k, v in inp["w"].items()}
+    y = torch.empty_like(x)
+    ws = torch.empty(lca.edit_attn_workspace_size(s), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        lca.edit_attn_forward(s, w, x, y, ws, stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(K):
+        lca.edit_attn_forward(s, w, x, y, ws, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / K
+    value = s.B * s.N * K / (ms / 1e3)
+    assert torch.isfinite(y).all().item(), "non-finite output"
+
+    # Per-step durations from events the library records between its steps.
+    P = args.profile_steps or K
+    hev = HipEvents()
+    evs = [hev.create(len(STEP_NAMES) + 1) for _ in range(P)]
+    torch.cuda.synchronize()
+    for e in evs:
+        arr = (ctypes.c_void_p * len(e))(*e)
+        lca.edit_attn_forward_timed(s, w, x, y, ws, arr, stream)
+    torch.cuda.synchronize()
+    per_step = {n: [] for n in STEP_NAMES}
+    for e in evs:
+        for i, n in enumerate(STEP_NAMES):
+            per_step[n].append(hev.elapsed_ms(e[i], e[i + 1]))
+    for e in evs:
+        hev.destroy(e)
+
+    work = algorithmic_work(s)
+    steps = {}
+    for n in STEP_NAMES:
+        us = 1e3 * statistics.mean(per_step[n])
+        fl, by = work[n]
+        if STEP_BOUND[n] == "mfma":
+            ach = fl / (us * 1e-6) / 1e12
+            peak = PEAK_MFMA_TFLOPS[s.dtype]
+            unit = "TFLOP/s"
+        else:
+            ach = by / (us * 1e-6) / 1e9
+            peak = PEAK_HBM_GBS
+            unit = "GB/s"
+        steps[n] = {"us": round(us, 2), "bound": STEP_BOUND[n], "achieved": round(ach, 1), "unit": unit,
+                    "frac": round(ach / peak, 4), "flops": fl, "bytes": by, "kernels": STEP_KERNELS[n]}
+    single = [n for n in STEP_NAMES if "+" not in STEP_KERNELS[n]]
+    dom = max(single, key=lambda n: steps[n]["us"])
+    d = steps[dom]
+    roofline = {"bound": d["bound"], "achieved": d["achieved"],
+                "peak": PEAK_MFMA_TFLOPS[s.dtype] if d["bound"] == "mfma" else PEAK_HBM_GBS,
+                "unit": d["unit"], "frac": d["frac"], "traffic": None, "kernel": dom,
+                "avg_us": d["us"], "work_per_launch": d["flops"] if d["bound"] == "mfma" else d["bytes"]}
+    layer_floor_us = sum(max(work[n][0] / (PEAK_MFMA_TFLOPS[s.dtype] * 1e6), work[n][1] / (PEAK_HBM_GBS * 1e3))
+                         for n in STEP_NAMES)
+
+    cpu = None
+    if args.cpu_runs > 0:
+        cpu = cpu_baseline(s, inp, args.cpu_runs)
+
+    out = {
+        "metric": "image tokens/sec per EDiT attention layer fwd at 16384 tokens; % HBM/MFMA peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": s.dtype, "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        "config": {"workload": f"{args.workload}: EDiT attention layer forward, B={s.B}, {s.H}x{s.W} token grid "
+                               f"({s.N} tokens, {s.Nc} compressed K/V tokens), C={s.C}, {s.heads} heads x "
+                               f"{s.head_dim}, r={s.reduction}, {s.gn_groups} GN groups, {s.dtype}",
+                   "B": s.B, "H": s.H, "W": s.W, "C": s.C, "heads": s.heads, "head_dim": s.head_dim,
+                   "reduction": s.reduction, "gn_groups": s.gn_groups},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "layer_roofline": {"floor_us": round(layer_floor_us, 1), "frac": round(layer_floor_us / (ms_per_step * 1e3), 4)},
+        "steps_breakdown": {n: {k: v for k, v in steps[n].items() if k in ("us", "bound", "achieved", "unit", "frac")}
+                            for n in STEP_NAMES},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

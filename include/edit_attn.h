@@ -148,6 +148,29 @@ typedef struct {
 edit_status_t edit_attn_workspace_layout(const edit_shape_t* shape, int n_text,
                                          edit_ws_layout_t* layout);
 
+/* Steps of one EDiT forward, in launch order (per-step timing). */
+typedef enum {
+  EDIT_STEP_CF_CONV3X3 = 0,  /* ConvFusion 3x3 compressing conv             (1 kernel)  */
+  EDIT_STEP_GN_STATS = 1,    /* GroupNorm statistics                         (2 kernels) */
+  EDIT_STEP_CF_RESTORE = 2,  /* GN + LeakyReLU + 1x1 restore + residual      (1 kernel)  */
+  EDIT_STEP_Q_PROJ = 3,      /* query Linear + ReLU                          (1 kernel)  */
+  EDIT_STEP_KV_PROJ = 4,     /* key and value Linears                        (1 kernel)  */
+  EDIT_STEP_SC_DWCONV = 5,   /* depthwise 3x3 stride 2, ReLU on keys          (1 kernel)  */
+  EDIT_STEP_KV_STATE = 6,    /* S = K'^T V', z = sum K' per head             (2 kernels) */
+  EDIT_STEP_APPLY = 7,       /* y = q S / (q . z + eps)                      (1 kernel)  */
+  EDIT_STEP_OUT_PROJ = 8,    /* output Linear                                (1 kernel)  */
+  EDIT_NUM_STEPS = 9
+} edit_step_t;
+
+/* edit_attn_forward that also records events[i] (a hipEvent_t passed as
+ * void*) on hip_stream just before step i is enqueued, and
+ * events[EDIT_NUM_STEPS] after the last one, so hipEventElapsedTime between
+ * neighbours times each step on the stream that runs it. events must hold
+ * EDIT_NUM_STEPS + 1 created events; results equal edit_attn_forward's. */
+edit_status_t edit_attn_forward_timed(const edit_shape_t* shape, const edit_weights_t* w,
+                                      const void* x, void* y, void* workspace, size_t ws_bytes,
+                                      void* hip_stream, void* const* events);
+
 const char* edit_status_string(edit_status_t status);
 const char* edit_last_error(void);
 

@@ -16,7 +16,7 @@ from typing import Mapping, Optional
 __all__ = [
     "EDIT_F32", "EDIT_BF16", "EditError", "IMAGE_WEIGHT_FIELDS", "TEXT_WEIGHT_FIELDS", "LAYOUT_FIELDS",
     "edit_attn_workspace_size", "edit_attn_forward", "mmedit_hybrid_workspace_size",
-    "mmedit_hybrid_forward", "edit_attn_workspace_layout", "edit_status_string", "edit_last_error",
+    "mmedit_hybrid_forward", "edit_attn_forward_timed", "edit_attn_workspace_layout", "EDIT_NUM_STEPS", "edit_status_string", "edit_last_error",
     "lib_path", "header_symbols",
 ]
 
@@ -25,6 +25,7 @@ _ROOT = os.path.dirname(_PKG)
 _LIB_PATH = os.path.join(_PKG, "libedit_attn.so")
 
 EDIT_F32, EDIT_BF16 = 0, 1
+EDIT_NUM_STEPS = 9
 _STATUS = {0: "EDIT_OK", 1: "EDIT_ERR_ARG", 2: "EDIT_ERR_UNSUPPORTED", 3: "EDIT_ERR_WORKSPACE", 4: "EDIT_ERR_HIP"}
 
 IMAGE_WEIGHT_FIELDS = ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2", "w_q", "b_q", "w_k", "b_k",
@@ -59,7 +60,7 @@ class EditError(RuntimeError):
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m linear_compressed_attention_amd.build` "
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python linear_compressed_attention_amd/build.py` "
                           "(the HIP library is the only implementation of this package)")
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.POINTER
@@ -74,6 +75,9 @@ def _load():
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p]
     lib.mmedit_hybrid_forward.restype = ctypes.c_int
+    lib.edit_attn_forward_timed.argtypes = [P(_Shape), P(_Weights), ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.edit_attn_forward_timed.restype = ctypes.c_int
     lib.edit_attn_workspace_layout.argtypes = [P(_Shape), ctypes.c_int, P(_Layout)]
     lib.edit_attn_workspace_layout.restype = ctypes.c_int
     lib.edit_status_string.argtypes = [ctypes.c_int]
@@ -186,6 +190,17 @@ def edit_attn_forward(shape, weights, x, y, workspace, stream=None) -> None:
     w = _weights(weights)
     _check(_lib.edit_attn_forward(ctypes.byref(sh), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(workspace),
                                   _nbytes(workspace), _stream(stream)))
+
+
+def edit_attn_forward_timed(shape, weights, x, y, workspace, events, stream=None) -> None:
+    """edit_attn_forward that records ``events`` (EDIT_NUM_STEPS + 1 hipEvent_t
+    handles, a ctypes array) before each step and after the last one."""
+    if len(events) != EDIT_NUM_STEPS + 1:
+        raise ValueError(f"need {EDIT_NUM_STEPS + 1} events")
+    sh = _shape(shape)
+    w = _weights(weights)
+    _check(_lib.edit_attn_forward_timed(ctypes.byref(sh), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(workspace),
+                                        _nbytes(workspace), _stream(stream), ctypes.cast(events, ctypes.c_void_p)))
 
 
 def mmedit_hybrid_forward(shape, n_text, img_weights, txt_weights, x_img, x_txt, y_img, y_txt, workspace,

@@ -1,6 +1,6 @@
 """Build libedit_attn.so (gfx950) in place with hipcc.
 
-python -m linear_compressed_attention_amd.build
+python linear_compressed_attention_amd/build.py   (or __graft_entry__.build())
 """
 import os
 import subprocess

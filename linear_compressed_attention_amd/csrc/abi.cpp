@@ -86,7 +86,7 @@ edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
   g->B = s->B; g->H = s->H; g->W = s->W; g->C = s->C; g->heads = s->heads; g->d = s->head_dim;
   g->r = s->reduction; g->G = s->gn_groups; g->Cr = Cr; g->N = (int)N; g->M = (int)M;
   g->Hc = (s->H + 1) / 2; g->Wc = (s->W + 1) / 2; g->Nc = g->Hc * g->Wc; g->nt = n_text;
-  g->gn_chunks = edit::groupnorm_chunks(g->N);
+  g->gn_chunks = edit::groupnorm_chunks(g->N, Cr);
   g->kv_chunks = edit::kv_state_chunks(g->Nc);
   g->DT = (g->d + 15) / 16; g->DR = (g->d + 16) / 16;
   g->DP = edit::kv_state_dp(g->d); g->DK = edit::kv_state_dk(g->d);
@@ -102,7 +102,7 @@ Layout make_layout(const Geometry& g) {
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   const size_t M = g.M, es = g.es, BH = (size_t)g.B * g.heads;
   L.xc = take(M * g.Cr * es);
-  L.gn_part = take((size_t)g.B * g.gn_chunks * g.Cr * 2 * 4);
+  L.gn_part = take((size_t)g.B * g.gn_chunks * g.G * 2 * 4);
   L.gn_stat = take((size_t)g.B * g.G * 2 * 4);
   L.gn_scale = take((size_t)g.B * g.Cr * 4);
   L.gn_shift = take((size_t)g.B * g.Cr * 4);
@@ -189,24 +189,36 @@ edit_status_t check_device() {
     if (e_ != hipSuccess) return fail(EDIT_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
   } while (0)
 
+// Records events[i] on the stream when per-step timing was asked for.
+struct Marks {
+  void* const* ev;
+  hipStream_t s;
+  hipError_t mark(int i) const {
+    return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
+  }
+};
+
 // The image stream up to the linear-attention output y (steps 1-8).
 template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
-                        hipStream_t s) {
+                        hipStream_t s, const Marks& mk) {
   using namespace edit;
   auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   GemmArgs<T> a{};
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_CONV3X3));
   // 1. xc = Conv3x3(x) + b_cf1
   a.M = g.M; a.N = g.Cr; a.K = 9 * g.C; a.A = x; a.lda = g.C; a.H = g.H; a.W = g.W; a.Cin = g.C;
   a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_cf1);
   a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_cf1);
   a.seg_rows = g.Cr; a.ldb = 9 * g.C; a.C = P(L.xc); a.ldc = g.Cr;
   EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_GN_STATS));
   // 2. GroupNorm statistics -> per-channel scale / shift
   EDIT_LAUNCH(launch_groupnorm_stats<T>(P(L.xc), g.B, g.N, g.Cr, g.G, static_cast<const T*>(w->gn_gamma),
                                         static_cast<const T*>(w->gn_beta), 1e-5f, F(L.gn_part), g.gn_chunks,
                                         F(L.gn_stat), F(L.gn_scale), F(L.gn_shift), s));
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_RESTORE));
   // 3. xt = x + LeakyReLU(GN(xc)) W_cf2^T + b_cf2
   a = GemmArgs<T>{};
   a.M = g.M; a.N = g.C; a.K = g.Cr; a.A = P(L.xc); a.lda = g.Cr;
@@ -215,6 +227,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
   a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_cf2);
   a.seg_rows = g.C; a.ldb = g.Cr; a.C = P(L.xt); a.ldc = g.C; a.R = x; a.ldr = g.C;
   EDIT_LAUNCH(launch_gemm<T>(a, A_GNACT, E_BIAS_RES, s));
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_Q_PROJ));
   // 4. q = ReLU(xt W_q^T + b_q)
   a = GemmArgs<T>{};
   a.M = g.M; a.N = g.C; a.K = g.C; a.A = P(L.xt); a.lda = g.C;
@@ -222,6 +235,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
   a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_q);
   a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.q); a.ldc = g.C;
   EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS_RELU, s));
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_PROJ));
   // 5. kv0 = [x W_k^T + b_k | x W_v^T + b_v]
   a = GemmArgs<T>{};
   a.M = g.M; a.N = 2 * g.C; a.K = g.C; a.A = x; a.lda = g.C;
@@ -229,13 +243,16 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
   a.bias[0] = static_cast<const T*>(w->b_k); a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_v);
   a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.kv0); a.ldc = 2 * g.C;
   EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
   // 6. compressed keys / values
   EDIT_LAUNCH(launch_dwconv_s2<T>(P(L.kv0), g.B, g.H, g.W, g.C, static_cast<const T*>(w->dw_k),
                                   static_cast<const T*>(w->db_k), static_cast<const T*>(w->dw_v),
                                   static_cast<const T*>(w->db_v), P(L.kc), P(L.vc), s));
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_STATE));
   // 7. per-head state
   EDIT_LAUNCH(launch_kv_state<T>(P(L.kc), P(L.vc), g.B, g.Nc, g.heads, g.d, F(L.kv_part), g.kv_chunks, F(L.S),
                                  F(L.z), P(L.st), F(L.zp), s));
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_APPLY));
   // 8. y = q S / (q . z + eps)
   EDIT_LAUNCH(launch_linattn_apply<T>(P(L.q), g.C, P(L.st), F(L.zp), g.B, g.N, g.heads, g.d, g.eps, P(L.y), g.C,
                                       s));
@@ -256,11 +273,15 @@ edit_status_t out_linear(int M, int C, const void* wo, const void* bo, const T* 
 
 template <typename T>
 edit_status_t run_edit(const Geometry& g, const Layout& L, const edit_weights_t* w, const void* x, void* y,
-                       void* ws, hipStream_t s) {
+                       void* ws, hipStream_t s, const Marks& mk) {
   char* wsb = static_cast<char*>(ws);
-  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x), wsb, s);
+  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x), wsb, s, mk);
   if (st != EDIT_OK) return st;
-  return out_linear<T>(g.M, g.C, w->w_o, w->b_o, reinterpret_cast<const T*>(wsb + L.y), static_cast<T*>(y), s);
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_OUT_PROJ));
+  st = out_linear<T>(g.M, g.C, w->w_o, w->b_o, reinterpret_cast<const T*>(wsb + L.y), static_cast<T*>(y), s);
+  if (st != EDIT_OK) return st;
+  EDIT_LAUNCH(mk.mark(EDIT_NUM_STEPS));
+  return EDIT_OK;
 }
 
 template <typename T>
@@ -270,7 +291,7 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   using namespace edit;
   char* wsb = static_cast<char*>(ws);
   auto P = [&](size_t off) { return reinterpret_cast<T*>(wsb + off); };
-  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x_img), wsb, s);
+  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x_img), wsb, s, Marks{nullptr, s});
   if (st != EDIT_OK) return st;
   if (g.nt == 0) return out_linear<T>(g.M, g.C, w->w_o, w->b_o, P(L.y), static_cast<T*>(y_img), s);
 
@@ -339,8 +360,8 @@ edit_status_t edit_attn_workspace_layout(const edit_shape_t* shape, int n_text, 
   return EDIT_OK;
 }
 
-edit_status_t edit_attn_forward(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
-                                void* workspace, size_t ws_bytes, void* hip_stream) {
+static edit_status_t forward_impl(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
+                                  void* workspace, size_t ws_bytes, void* hip_stream, void* const* events) {
   Geometry g;
   edit_status_t st = check_shape(shape, 0, &g);
   if (st != EDIT_OK) return st;
@@ -358,8 +379,22 @@ edit_status_t edit_attn_forward(const edit_shape_t* shape, const edit_weights_t*
   if (overlap(x, act, workspace, ws_bytes)) return fail(EDIT_ERR_ARG, "x overlaps the workspace");
   if ((st = check_device()) != EDIT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  return g.dtype == EDIT_BF16 ? run_edit<bf16>(g, L, w, x, y, workspace, s)
-                              : run_edit<float>(g, L, w, x, y, workspace, s);
+  const Marks mk{events, s};
+  return g.dtype == EDIT_BF16 ? run_edit<bf16>(g, L, w, x, y, workspace, s, mk)
+                              : run_edit<float>(g, L, w, x, y, workspace, s, mk);
+}
+
+edit_status_t edit_attn_forward(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
+                                void* workspace, size_t ws_bytes, void* hip_stream) {
+  return forward_impl(shape, w, x, y, workspace, ws_bytes, hip_stream, nullptr);
+}
+
+edit_status_t edit_attn_forward_timed(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
+                                      void* workspace, size_t ws_bytes, void* hip_stream, void* const* events) {
+  if (!events) return fail(EDIT_ERR_ARG, "events is NULL");
+  for (int i = 0; i <= EDIT_NUM_STEPS; ++i)
+    if (!events[i]) return fail(EDIT_ERR_ARG, "events[%d] is NULL", i);
+  return forward_impl(shape, w, x, y, workspace, ws_bytes, hip_stream, events);
 }
 
 edit_status_t mmedit_hybrid_forward(const edit_shape_t* shape, int n_text, const edit_weights_t* img,

@@ -29,24 +29,32 @@ int kv_state_dk(int d) { return 32 * ((d + 31) / 32); }
 // KV state, partial sums over one chunk of compressed tokens.
 // D[n][k] = sum_j A[n][j] * K'_j[k] with A = [V'^T ; 1]: rows n < d give
 // S^T (S[k][n] = sum_j K'_j[k] V'_j[n]), row d gives z[k]. Tokens are the
-// matrix-core K dimension, so each 32-token slab of K' and V' is written to
-// LDS transposed (channel-major) and read back as 16-byte fragments.
+// matrix-core K dimension, so the chunk's K' and V' slices are staged in LDS
+// transposed (channel-major). All loads of a slab are issued before the LDS
+// writes (one wait), and bf16 token pairs are packed into 4-byte writes.
 // partial[b][h][chunk][16*DR][16*DT] (fp32).
 // ---------------------------------------------------------------------------
-template <typename T, int DT, int DR>
+template <typename T> struct KvSlab { static constexpr int n = 256; };
+template <> struct KvSlab<float> { static constexpr int n = 64; };
+
+template <typename T, int DC>
 __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
-                                                               int Nc, int heads, int d, int nchunks,
+                                                               int Nc, int heads, int nchunks,
                                                                float* __restrict__ partial) {
-  constexpr int PITCH = 40;                 // 32 tokens + pad, in elements (16 B multiple for both types)
+  constexpr int d = 8 * DC;
+  constexpr int DT = (d + 15) / 16, DR = (d + 16) / 16;
+  constexpr int SLAB = KvSlab<T>::n;       // tokens staged per pass
+  constexpr int PITCH = SLAB + 8;          // elements; rows stay 16-byte aligned
   constexpr int NT = DR * DT;
   constexpr int TPW = (NT + 3) / 4;
+  constexpr int PAIRS = SLAB / 2;          // token pairs per slab
+  constexpr int NLOAD = (2 * PAIRS * DC + 255) / 256;   // (K or V, pair, 8-channel chunk) per thread
   __shared__ __attribute__((aligned(16))) T Kt[16 * DT * PITCH];
   __shared__ __attribute__((aligned(16))) T At[16 * DR * PITCH];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int C = heads * d;
   const int j0 = chunk * kKvChunk, j1 = min(Nc, j0 + kKvChunk);
-  const int dc = d / 8;                     // 8-channel chunks per token (head slice)
 
   f32x4 acc[TPW];
 #pragma unroll
@@ -59,36 +67,55 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   __syncthreads();
 
   typedef typename Frag<T>::type FragT;
-  for (int js = j0; js < j1; js += 32) {
-    // Load 32 tokens x d channels of K' and V' (head h), transposed into LDS.
-    for (int e = tid; e < 2 * 32 * dc; e += 256) {
-      const int which = e / (32 * dc);      // 0: K', 1: V'
-      const int r = e % (32 * dc);
-      const int tok = r / dc, c8 = (r % dc) * 8;
-      const int j = js + tok;
-      float v[8];
-      if (j < j1) {
-        load8((which ? vc : kc) + ((size_t)b * Nc + j) * C + h * d + c8, v);
-      } else {
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int js = j0; js < j1; js += SLAB) {
+    float v[NLOAD][2][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    for (int l = 0; l < NLOAD; ++l) {
+      const int e = tid + 256 * l;
+      const int which = e / (PAIRS * DC);
+      const int r = e % (PAIRS * DC);
+      const int tok = 2 * (r / DC), c8 = (r % DC) * 8;
+      const T* src = (which ? vc : kc) + ((size_t)b * Nc + js + tok) * C + h * d + c8;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (e < 2 * PAIRS * DC && js + tok + u < j1) {
+          load8(src + (size_t)u * C, v[l][u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[l][u][i] = 0.0f;
+        }
       }
-      T* dst = (which ? At : Kt) + c8 * PITCH + tok;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i * PITCH] = from_f32<T>(v[i]);
     }
-    if (tid < 32) At[d * PITCH + tid] = from_f32<T>(js + tid < j1 ? 1.0f : 0.0f);
-    __syncthreads();
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int tile = wave + 4 * t;
-      if (tile < NT) {
-        const int tr = tile / DT, tc = tile % DT;
-        FragT a, bb;
-        frag_load(a, At + (tr * 16 + fr) * PITCH + fk);
-        frag_load(bb, Kt + (tc * 16 + fr) * PITCH + fk);
-        mma16(acc[t], a, bb);
+    for (int l = 0; l < NLOAD; ++l) {
+      const int e = tid + 256 * l;
+      if (e < 2 * PAIRS * DC) {
+        const int which = e / (PAIRS * DC);
+        const int r = e % (PAIRS * DC);
+        const int tok = 2 * (r / DC), c8 = (r % DC) * 8;
+        T* dst = (which ? At : Kt) + c8 * PITCH + tok;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          dst[i * PITCH] = from_f32<T>(v[l][0][i]);
+          dst[i * PITCH + 1] = from_f32<T>(v[l][1][i]);
+        }
+      }
+    }
+    for (int t = tid; t < SLAB; t += 256) At[d * PITCH + t] = from_f32<T>(js + t < j1 ? 1.0f : 0.0f);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < SLAB / 32; ++ks) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int tile = wave + 4 * t;
+        if (tile < NT) {
+          const int tr = tile / DT, tc = tile % DT;
+          FragT a, bb;
+          frag_load(a, At + (tr * 16 + fr) * PITCH + ks * 32 + fk);
+          frag_load(bb, Kt + (tc * 16 + fr) * PITCH + ks * 32 + fk);
+          mma16(acc[t], a, bb);
+        }
       }
     }
     __syncthreads();
@@ -110,72 +137,65 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
 // Sum the chunk partials in chunk order and emit S (f32, [d][d] as S[k][n]),
 // z (f32), the apply kernel's operand st[2][DP][DK] (rows n, K = k: S^T,
 // padded with zeros; bf16 keeps a hi and a lo part so hi + lo carries ~16
-// mantissa bits of the fp32 sum) and zp[DK].
+// mantissa bits of the fp32 sum) and zp[DK]. One thread per output element.
 template <typename T>
 __global__ __launch_bounds__(256) void kv_state_finalize_kernel(const float* __restrict__ partial, int heads,
                                                                 int d, int DR, int DT, int nchunks,
                                                                 float* __restrict__ S, float* __restrict__ z,
                                                                 T* __restrict__ st, float* __restrict__ zp) {
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int DP = 16 * DT, DK = 32 * ((DT + 1) / 2);
   const int RW = 16 * DR, CW = 16 * DT;
   const size_t bh = (size_t)b * heads + h;
   const float* part = partial + bh * nchunks * RW * CW;
-  T* sthi = st + bh * 2 * DP * DK;
-  T* stlo = sthi + DP * DK;
-  for (int e = tid; e < DP * DK; e += 256) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e < DP * DK) {
     const int n = e / DK, k = e % DK;
     float v = 0.0f;
     if (n < d && k < d) {
-      for (int c = 0; c < nchunks; ++c) v += part[(size_t)c * RW * CW + n * CW + k];
+      const float* p = part + n * CW + k;
+      for (int c = 0; c < nchunks; ++c) v += p[(size_t)c * RW * CW];
       S[(bh * d + k) * d + n] = v;
     }
+    T* sthi = st + bh * 2 * DP * DK;
     const T hi = from_f32<T>(v);
     sthi[e] = hi;
-    stlo[e] = from_f32<T>(v - to_f32(hi));
-  }
-  for (int k = tid; k < DK; k += 256) {
+    sthi[DP * DK + e] = from_f32<T>(v - to_f32(hi));
+  } else if (e < DP * DK + DK) {
+    const int k = e - DP * DK;
     float v = 0.0f;
     if (k < d) {
-      for (int c = 0; c < nchunks; ++c) v += part[(size_t)c * RW * CW + d * CW + k];
+      const float* p = part + d * CW + k;
+      for (int c = 0; c < nchunks; ++c) v += p[(size_t)c * RW * CW];
       z[bh * d + k] = v;
     }
     zp[bh * DK + k] = v;
   }
 }
 
-template <typename T, int DT>
-static hipError_t kv_state_dispatch_dr(const T* kc, const T* vc, int B, int Nc, int heads, int d, float* partial,
-                                       int nchunks, hipStream_t s) {
-  dim3 grid(nchunks, heads, B);
-  if ((d + 16) / 16 == DT)
-    hipLaunchKernelGGL((kv_state_partial_kernel<T, DT, DT>), grid, dim3(256), 0, s, kc, vc, Nc, heads, d,
-                       nchunks, partial);
-  else
-    hipLaunchKernelGGL((kv_state_partial_kernel<T, DT, DT + 1>), grid, dim3(256), 0, s, kc, vc, Nc, heads, d,
-                       nchunks, partial);
-  return hipGetLastError();
-}
-
 template <typename T>
 hipError_t launch_kv_state(const T* kc, const T* vc, int B, int Nc, int heads, int d, float* partial,
                            int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s) {
   const int DT = (d + 15) / 16, DR = (d + 16) / 16;
-  hipError_t e;
-  switch (DT) {
-    case 1: e = kv_state_dispatch_dr<T, 1>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
-    case 2: e = kv_state_dispatch_dr<T, 2>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
-    case 3: e = kv_state_dispatch_dr<T, 3>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
-    case 4: e = kv_state_dispatch_dr<T, 4>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
-    case 5: e = kv_state_dispatch_dr<T, 5>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
-    case 6: e = kv_state_dispatch_dr<T, 6>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
-    case 7: e = kv_state_dispatch_dr<T, 7>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
-    case 8: e = kv_state_dispatch_dr<T, 8>(kc, vc, B, Nc, heads, d, partial, nchunks, s); break;
+  dim3 grid(nchunks, heads, B);
+  switch (d / 8) {
+#define EDIT_KV_CASE(DCV)                                                                              \
+  case DCV:                                                                                            \
+    hipLaunchKernelGGL((kv_state_partial_kernel<T, DCV>), grid, dim3(256), 0, s, kc, vc, Nc, heads,    \
+                       nchunks, partial);                                                              \
+    break;
+    EDIT_KV_CASE(1) EDIT_KV_CASE(2) EDIT_KV_CASE(3) EDIT_KV_CASE(4) EDIT_KV_CASE(5) EDIT_KV_CASE(6)
+    EDIT_KV_CASE(7) EDIT_KV_CASE(8) EDIT_KV_CASE(9) EDIT_KV_CASE(10) EDIT_KV_CASE(11) EDIT_KV_CASE(12)
+    EDIT_KV_CASE(13) EDIT_KV_CASE(14) EDIT_KV_CASE(15) EDIT_KV_CASE(16)
+#undef EDIT_KV_CASE
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((kv_state_finalize_kernel<T>), dim3(heads, B), dim3(256), 0, s, partial, heads, d, DR, DT,
-                     nchunks, S, z, st, zp);
+  const int DP = 16 * DT, DK = 32 * ((DT + 1) / 2);
+  dim3 fgrid((DP * DK + DK + 255) / 256, heads, B);
+  hipLaunchKernelGGL((kv_state_finalize_kernel<T>), fgrid, dim3(256), 0, s, partial, heads, d, DR, DT, nchunks, S,
+                     z, st, zp);
   return hipGetLastError();
 }
 

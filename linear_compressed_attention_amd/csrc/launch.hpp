@@ -45,13 +45,14 @@ struct GemmArgs {
 template <typename T>
 hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s);
 
-// GroupNorm statistics of x [B][HW][Cg*G]: per (b, group) mean and rstd,
-// and the per-channel affine folded into scale/shift [B][C].
+// GroupNorm statistics of x [B][HW][C] (G groups of C/G consecutive
+// channels): per (b, group) mean and rstd, and the per-channel affine folded
+// into scale/shift [B][C]. partial holds [B][nchunks][G][2] floats.
 template <typename T>
 hipError_t launch_groupnorm_stats(const T* x, int B, int HW, int C, int G, const T* gamma,
                                   const T* beta, float eps, float* partial, int nchunks,
                                   float* stat, float* scale, float* shift, hipStream_t s);
-int groupnorm_chunks(int HW);
+int groupnorm_chunks(int HW, int C);
 
 // Depthwise 3x3 stride-2 pad-1 conv of two channel groups side by side in
 // kv0 [B][H][W][2C]: keys (channels 0..C-1, then ReLU) and values (C..2C-1).

@@ -11,69 +11,12 @@
 
 namespace edit {
 
-constexpr int kGnPix = 64;   // pixels per statistics chunk
+constexpr int kGnMaxRows = 16;    // pixels one thread keeps in registers
 
-int groupnorm_chunks(int HW) { return (HW + kGnPix - 1) / kGnPix; }
-
-// One block per (chunk of kGnPix pixels, sample): exact two-pass per-channel
-// mean and sum of squared deviations over the chunk.
-// partial[b][chunk][c] = (mean, M2).
-template <typename T>
-__global__ __launch_bounds__(256) void gn_partial_kernel(const T* __restrict__ x, int HW, int C,
-                                                         float* __restrict__ partial, int nchunks) {
-  __shared__ float red[2048];
-  __shared__ float mean_s[2048];
-  const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int tpr = C / 8;                  // threads per pixel row (C <= 2048)
-  const int rows_par = 256 / tpr;
-  const int p0 = chunk * kGnPix, p1 = min(HW, p0 + kGnPix), cnt = p1 - p0;
-  const int c8 = tid % tpr, rl = tid / tpr;
-  const bool active = rl < rows_par;
-  const T* base = x + (size_t)b * HW * C + c8 * 8;
-
-  float s[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s[i] = 0.0f;
-  if (active)
-    for (int p = p0 + rl; p < p1; p += rows_par) {
-      float v[8];
-      load8(base + (size_t)p * C, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] += v[i];
-    }
-  if (active)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) red[rl * C + c8 * 8 + i] = s[i];
-  __syncthreads();
-  for (int c = tid; c < C; c += 256) {
-    float t = 0.0f;
-    for (int r = 0; r < rows_par; ++r) t += red[r * C + c];
-    mean_s[c] = t / (float)cnt;
-  }
-  __syncthreads();
-  float m[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { s[i] = 0.0f; m[i] = active ? mean_s[c8 * 8 + i] : 0.0f; }
-  if (active)
-    for (int p = p0 + rl; p < p1; p += rows_par) {
-      float v[8];
-      load8(base + (size_t)p * C, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { const float d = v[i] - m[i]; s[i] += d * d; }
-    }
-  __syncthreads();
-  if (active)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) red[rl * C + c8 * 8 + i] = s[i];
-  __syncthreads();
-  float* out = partial + ((size_t)b * nchunks + chunk) * C * 2;
-  for (int c = tid; c < C; c += 256) {
-    float t = 0.0f;
-    for (int r = 0; r < rows_par; ++r) t += red[r * C + c];
-    out[2 * c] = mean_s[c];
-    out[2 * c + 1] = t;
-  }
-}
+// A statistics chunk is as many pixels as the block holds in registers:
+// 256 / (C/8) pixel rows in parallel, kGnMaxRows each.
+static int gn_chunk_px(int C) { return (256 / (C / 8)) * kGnMaxRows; }
+int groupnorm_chunks(int HW, int C) { return (HW + gn_chunk_px(C) - 1) / gn_chunk_px(C); }
 
 struct Welford { float n, mean, m2; };
 
@@ -88,47 +31,133 @@ __device__ __forceinline__ Welford chan_merge(Welford a, Welford b) {
   return r;
 }
 
-// One wave per (group, sample): Chan-merge the chunk partials of the group's
-// channels in a fixed order, then fold gamma/beta into per-channel
-// scale/shift: GN(x) = x * scale + shift.
+// One block per (chunk of kGnPix pixels, sample). The chunk's values stay in
+// registers: exact per-channel mean, then per-channel sum of squared
+// deviations, then the group's channels merged (equal counts):
+//   mean_g = avg_c mean_c,  M2_g = sum_c M2_c + cnt * sum_c (mean_c - mean_g)^2.
+// partial[b][chunk][g] = (mean_g, M2_g) over cnt * C/G values.
 template <typename T>
-__global__ __launch_bounds__(64) void gn_finalize_kernel(const float* __restrict__ partial, int HW, int C,
-                                                         int G, int nchunks, const T* __restrict__ gamma,
+__global__ __launch_bounds__(256) void gn_partial_kernel(const T* __restrict__ x, int HW, int C, int G,
+                                                         int chunk_px, float* __restrict__ partial, int nchunks) {
+  __shared__ float red[2048];
+  __shared__ float mean_s[2048];
+  __shared__ float m2_s[2048];
+  const int chunk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int tpr = C / 8;                  // threads per pixel row (C <= 2048)
+  const int rows_par = 256 / tpr;
+  const int p0 = chunk * chunk_px, p1 = min(HW, p0 + chunk_px), cnt = p1 - p0;
+  const int c8 = tid % tpr, rl = tid / tpr;
+  const bool active = rl < rows_par;
+  const T* base = x + (size_t)b * HW * C + c8 * 8;
+
+  float v[kGnMaxRows][8];
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kGnMaxRows; ++r) {
+    const int p = p0 + rl + r * rows_par;
+    if (active && p < p1) {
+      load8(base + (size_t)p * C, v[r]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[r][i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] += v[r][i];
+  }
+  if (active)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[rl * C + c8 * 8 + i] = s[i];
+  __syncthreads();
+  for (int c = tid; c < C; c += 256) {
+    float t = 0.0f;
+    for (int r = 0; r < rows_par; ++r) t += red[r * C + c];
+    mean_s[c] = t / (float)cnt;
+  }
+  __syncthreads();
+  float m[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { s[i] = 0.0f; m[i] = active ? mean_s[c8 * 8 + i] : 0.0f; }
+#pragma unroll
+  for (int r = 0; r < kGnMaxRows; ++r) {
+    const int p = p0 + rl + r * rows_par;
+    if (active && p < p1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { const float d = v[r][i] - m[i]; s[i] += d * d; }
+    }
+  }
+  if (active)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[rl * C + c8 * 8 + i] = s[i];
+  __syncthreads();
+  for (int c = tid; c < C; c += 256) {
+    float t = 0.0f;
+    for (int r = 0; r < rows_par; ++r) t += red[r * C + c];
+    m2_s[c] = t;
+  }
+  __syncthreads();
+  const int cg = C / G;
+  for (int g = tid; g < G; g += 256) {
+    float mg = 0.0f;
+    for (int c = 0; c < cg; ++c) mg += mean_s[g * cg + c];
+    mg /= (float)cg;
+    float m2 = 0.0f;
+    for (int c = 0; c < cg; ++c) {
+      const float d = mean_s[g * cg + c] - mg;
+      m2 += m2_s[g * cg + c] + (float)cnt * d * d;
+    }
+    float* out = partial + (((size_t)b * nchunks + chunk) * G + g) * 2;
+    out[0] = mg;
+    out[1] = m2;
+  }
+}
+
+// One block per (group, sample): each thread Chan-merges a strided subset
+// of the chunk partials, then a fixed-shape LDS tree merges the 256 results,
+// so the statistics are bit-for-bit reproducible. Folds gamma / beta into
+// per-channel scale / shift: GN(x) = x * scale + shift.
+template <typename T>
+__global__ __launch_bounds__(256) void gn_finalize_kernel(const float* __restrict__ partial, int HW, int C,
+                                                         int G, int chunk_px, int nchunks, const T* __restrict__ gamma,
                                                          const T* __restrict__ beta, float eps,
                                                          float* __restrict__ stat, float* __restrict__ scale,
                                                          float* __restrict__ shift) {
-  const int g = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int cg = C / G, entries = nchunks * cg;
+  __shared__ float sn[256], smean[256], sm2[256];
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int cg = C / G;
   Welford acc = {0.0f, 0.0f, 0.0f};
-  for (int e = lane; e < entries; e += 64) {
-    const int chunk = e / cg, c = g * cg + e % cg;
-    const float* pp = partial + (((size_t)b * nchunks + chunk) * C + c) * 2;
+  for (int ch = tid; ch < nchunks; ch += 256) {
+    const float* pp = partial + (((size_t)b * nchunks + ch) * G + g) * 2;
     Welford w;
-    w.n = (float)min(kGnPix, HW - chunk * kGnPix);
+    w.n = (float)(min(chunk_px, HW - ch * chunk_px) * cg);
     w.mean = pp[0];
     w.m2 = pp[1];
     acc = chan_merge(acc, w);
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    Welford other;
-    other.n = __shfl_xor(acc.n, o, 64);
-    other.mean = __shfl_xor(acc.mean, o, 64);
-    other.m2 = __shfl_xor(acc.m2, o, 64);
-    // Merge in lane order so every lane holds the same bits.
-    acc = (lane & o) ? chan_merge(other, acc) : chan_merge(acc, other);
+  sn[tid] = acc.n; smean[tid] = acc.mean; sm2[tid] = acc.m2;
+  __syncthreads();
+  for (int stride = 128; stride > 0; stride >>= 1) {
+    if (tid < stride) {
+      Welford a = {sn[tid], smean[tid], sm2[tid]};
+      Welford o = {sn[tid + stride], smean[tid + stride], sm2[tid + stride]};
+      a = chan_merge(a, o);
+      sn[tid] = a.n; smean[tid] = a.mean; sm2[tid] = a.m2;
+    }
+    __syncthreads();
   }
-  const float var = acc.m2 / acc.n;
+  const float mean = smean[0];
+  const float var = sm2[0] / sn[0];
   const float rstd = 1.0f / sqrtf(var + eps);
-  if (lane == 0) {
-    stat[((size_t)b * G + g) * 2] = acc.mean;
+  if (tid == 0) {
+    stat[((size_t)b * G + g) * 2] = mean;
     stat[((size_t)b * G + g) * 2 + 1] = rstd;
   }
-  for (int i = lane; i < cg; i += 64) {
+  for (int i = tid; i < cg; i += 256) {
     const int c = g * cg + i;
     const float sc = to_f32(gamma[c]) * rstd;
     scale[(size_t)b * C + c] = sc;
-    shift[(size_t)b * C + c] = to_f32(beta[c]) - acc.mean * sc;
+    shift[(size_t)b * C + c] = to_f32(beta[c]) - mean * sc;
   }
 }
 
@@ -136,10 +165,11 @@ template <typename T>
 hipError_t launch_groupnorm_stats(const T* x, int B, int HW, int C, int G, const T* gamma,
                                   const T* beta, float eps, float* partial, int nchunks,
                                   float* stat, float* scale, float* shift, hipStream_t s) {
-  hipLaunchKernelGGL((gn_partial_kernel<T>), dim3(nchunks, B), dim3(256), 0, s, x, HW, C, partial, nchunks);
+  const int px = gn_chunk_px(C);
+  hipLaunchKernelGGL((gn_partial_kernel<T>), dim3(nchunks, B), dim3(256), 0, s, x, HW, C, G, px, partial, nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gn_finalize_kernel<T>), dim3(G, B), dim3(64), 0, s, partial, HW, C, G, nchunks,
+  hipLaunchKernelGGL((gn_finalize_kernel<T>), dim3(G, B), dim3(256), 0, s, partial, HW, C, G, px, nchunks,
                      gamma, beta, eps, stat, scale, shift);
   return hipGetLastError();
 }

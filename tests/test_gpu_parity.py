@@ -145,3 +145,32 @@ def test_bitwise_deterministic():
     b = G.run_edit(s, inp)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_timed_forward_matches_forward():
+    import ctypes
+    import linear_compressed_attention_amd as lca
+    s = SMALL["bf16_d64_ragged"]
+    inp = make_inputs(s, seed=5)
+    _announce("timed forward")
+    ref = G.run_edit(s, inp, with_intermediates=False)["out"]
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    evs = []
+    for _ in range(lca.EDIT_NUM_STEPS + 1):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    x = G.to_dev(inp["x"], s.dtype)
+    w = G.dev_weights(inp["w"], s.dtype)
+    y = torch.empty_like(x)
+    ws = torch.empty(lca.edit_attn_workspace_size(s), dtype=torch.uint8, device="cuda")
+    lca.edit_attn_forward_timed(s, w, x, y, ws, (ctypes.c_void_p * len(evs))(*evs))
+    torch.cuda.synchronize()
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    for i in range(lca.EDIT_NUM_STEPS):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[i], evs[i + 1]) == 0
+        assert ms.value >= 0.0
+    for e in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
+    np.testing.assert_array_equal(y.float().cpu().numpy(), ref)
