@@ -22,7 +22,8 @@ __all__ = [
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_PKG)
-_LIB_PATH = os.path.join(_PKG, "libedit_attn.so")
+# EDIT_ATTN_LIB may point at another build of the same library (e.g. a tuning variant).
+_LIB_PATH = os.environ.get("EDIT_ATTN_LIB") or os.path.join(_PKG, "libedit_attn.so")
 
 EDIT_F32, EDIT_BF16 = 0, 1
 EDIT_NUM_STEPS = 9

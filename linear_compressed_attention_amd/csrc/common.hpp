@@ -91,6 +91,17 @@ __device__ __forceinline__ void frag_load(f32x8& f, const float* p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) { f[i] = a[i]; f[4 + i] = b[i]; }
 }
+// Fragment from a row whose 8 K values sit at element offset o0 (bf16: one
+// 16-byte chunk) or at o0 and o1 (f32: two 16-byte chunks, 4 values each).
+__device__ __forceinline__ void frag_load2(bf16x8& f, const bf16* row, int o0, int) {
+  f = *reinterpret_cast<const bf16x8*>(row + o0);
+}
+__device__ __forceinline__ void frag_load2(f32x8& f, const float* row, int o0, int o1) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(row + o0);
+  f32x4 b = *reinterpret_cast<const f32x4*>(row + o1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[i] = a[i]; f[4 + i] = b[i]; }
+}
 __device__ __forceinline__ void frag_from_f32(bf16x8& f, const float (&v)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = (bf16)v[i];
@@ -114,6 +125,30 @@ __device__ __forceinline__ void mma16(f32x4& acc, const f32x8& a, const f32x8& b
 }
 
 __device__ __forceinline__ void acc_zero(f32x4& a) { a[0] = a[1] = a[2] = a[3] = 0.0f; }
+
+// D(32x32) += A(32x16) * B(16x32): the wide matrix-core step, which gfx950
+// runs at about twice the flop rate of the 16x16x32 form (2.2 vs 1.2 PF/s
+// measured on MI355X with independent accumulators).
+// Lane l supplies A row (l % 32) and B column (l % 32), each with the 8 K
+// indices 8*(l/32) .. 8*(l/32)+7. D element (row 8*(r/4) + 4*(l/32) + r%4,
+// col l%32) is acc[r]. The f32 form issues eight 32x32x2 steps, step j
+// taking element j of every lane.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[j], b[j], acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_any(f32x4& acc, const bf16x8& a, const bf16x8& b) { mma16(acc, a, b); }
+__device__ __forceinline__ void mma_any(f32x4& acc, const f32x8& a, const f32x8& b) { mma16(acc, a, b); }
+__device__ __forceinline__ void mma_any(f32x16& acc, const bf16x8& a, const bf16x8& b) { mma32(acc, a, b); }
+__device__ __forceinline__ void mma_any(f32x16& acc, const f32x8& a, const f32x8& b) { mma32(acc, a, b); }
+__device__ __forceinline__ void acc_zero(f32x16& a) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = 0.0f;
+}
 
 // Blocks are dealt to the 8 XCDs round-robin (block i runs on XCD i % 8).
 // Renumber so that each XCD receives one contiguous range of logical tiles:
