@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--cpu-runs", type=int, default=3, help="oracle runs for cpu_baseline (0 = skip)")
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="timed forwards for the per-step breakdown (default: --steps)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (outside the timed region) whose HBM counter "
+                         "readings calibrate FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
@@ -204,6 +207,14 @@ def main():
                 "avg_us": d["us"], "work_per_launch": d["flops"] if d["bound"] == "mfma" else d["bytes"]}
     layer_floor_us = sum(max(work[n][0] / (PEAK_MFMA_TFLOPS[s.dtype] * 1e6), work[n][1] / (PEAK_HBM_GBS * 1e3))
                          for n in STEP_NAMES)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if args.cpu_runs > 0:

@@ -122,8 +122,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
   do {                                                                                        \
     const int k = (k0_) + cc * EPC;                                                           \
     const bool kin = k < p.K;                                                                 \
+    int kb = k; /* K index the weights use */                                                 \
     if (AM == A_CONV3) {                                                                      \
-      const int tap = k / p.Cin, cin = k - tap * p.Cin;                                       \
+      /* K tiles run channel slice outer, tap inner (when BK divides Cin), so a   */          \
+      /* slice of the three input rows is reused by all nine taps while cached.   */          \
+      int tap, cin;                                                                           \
+      if (p.Cin % BK == 0) {                                                                  \
+        const int kt_ = (k0_) / BK, nsl = p.Cin / BK;                                         \
+        const int sl = kt_ / 9;                                                               \
+        tap = kt_ - sl * 9;                                                                   \
+        cin = sl * BK + cc * EPC;                                                             \
+        kb = tap * p.Cin + cin;                                                               \
+        if (kt_ >= 9 * nsl) tap = 9;                                                          \
+      } else {                                                                                \
+        tap = k / p.Cin;                                                                      \
+        cin = k - tap * p.Cin;                                                                \
+      }                                                                                       \
       const int dy = tap / 3 - 1, dx = tap % 3 - 1;                                           \
       _Pragma("unroll") for (int j = 0; j < APASS; ++j) {                                     \
         const int yy = ay[j] + dy, xx = ax[j] + dx;                                           \
@@ -139,7 +153,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
     }                                                                                         \
     _Pragma("unroll") for (int j = 0; j < BPASS; ++j) {                                       \
       BOK[j] = bval[j] && kin;                                                                \
-      RB[j] = *reinterpret_cast<const u32x4*>(brow[j] + (BOK[j] ? k : 0));                    \
+      RB[j] = *reinterpret_cast<const u32x4*>(brow[j] + (BOK[j] ? kb : 0));                   \
     }                                                                                         \
   } while (0)
 
