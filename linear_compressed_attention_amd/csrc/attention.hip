@@ -31,24 +31,41 @@ int kv_state_dk(int d) { return 32 * ((d + 31) / 32); }
 // S^T (S[k][n] = sum_j K'_j[k] V'_j[n]), row d gives z[k]. Tokens are the
 // matrix-core K dimension, so the chunk's K' and V' slices are staged in LDS
 // transposed (channel-major). All loads of a slab are issued before the LDS
-// writes (one wait), and bf16 token pairs are packed into 4-byte writes.
+// writes (one wait); each thread writes four tokens of a channel as one word,
+// and neighbouring lanes take neighbouring token quads of the same row.
 // partial[b][h][chunk][16*DR][16*DT] (fp32).
 // ---------------------------------------------------------------------------
 template <typename T> struct KvSlab { static constexpr int n = 256; };
 template <> struct KvSlab<float> { static constexpr int n = 64; };
 
+// Four tokens' values of one channel, written to LDS as one 8-byte (bf16) or
+// 16-byte (f32) word.
+__device__ __forceinline__ void store_quad(bf16* dst, bf16 a, bf16 b, bf16 c, bf16 d) {
+  bf16x4 v;
+  v[0] = a; v[1] = b; v[2] = c; v[3] = d;
+  *reinterpret_cast<bf16x4*>(dst) = v;
+}
+__device__ __forceinline__ void store_quad(float* dst, float a, float b, float c, float d) {
+  f32x4 v;
+  v[0] = a; v[1] = b; v[2] = c; v[3] = d;
+  *reinterpret_cast<f32x4*>(dst) = v;
+}
+
 template <typename T, int DC>
 __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
                                                                int Nc, int heads, int nchunks,
                                                                float* __restrict__ partial) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   constexpr int d = 8 * DC;
   constexpr int DT = (d + 15) / 16, DR = (d + 16) / 16;
   constexpr int SLAB = KvSlab<T>::n;       // tokens staged per pass
   constexpr int PITCH = SLAB + 8;          // elements; rows stay 16-byte aligned
   constexpr int NT = DR * DT;
   constexpr int TPW = (NT + 3) / 4;
-  constexpr int PAIRS = SLAB / 2;          // token pairs per slab
-  constexpr int NLOAD = (2 * PAIRS * DC + 255) / 256;   // (K or V, pair, 8-channel chunk) per thread
+  constexpr int QUADS = SLAB / 4;          // token quads per slab
+  constexpr int ITEMS = 2 * QUADS * DC;    // (K or V, 8-channel chunk, token quad)
+  constexpr int NLOAD = (ITEMS + 255) / 256;
+  constexpr int EPC = Chunk<T>::n;         // elements per 16 bytes
   __shared__ __attribute__((aligned(16))) T Kt[16 * DT * PITCH];
   __shared__ __attribute__((aligned(16))) T At[16 * DR * PITCH];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -69,37 +86,37 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   typedef typename Frag<T>::type FragT;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   for (int js = j0; js < j1; js += SLAB) {
-    float v[NLOAD][2][8];
+    // Item e: token quad (fastest), then 8-channel chunk, then K or V.
+    u32x4v raw[NLOAD][4][8 / EPC];
 #pragma unroll
     for (int l = 0; l < NLOAD; ++l) {
       const int e = tid + 256 * l;
-      const int which = e / (PAIRS * DC);
-      const int r = e % (PAIRS * DC);
-      const int tok = 2 * (r / DC), c8 = (r % DC) * 8;
-      const T* src = (which ? vc : kc) + ((size_t)b * Nc + js + tok) * C + h * d + c8;
+      const int tq = e % QUADS, rest = e / QUADS;
+      const int c8 = (rest % DC) * 8, which = rest / DC;
+      const T* src = (which ? vc : kc) + ((size_t)b * Nc + js + 4 * tq) * C + h * d + c8;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if (e < 2 * PAIRS * DC && js + tok + u < j1) {
-          load8(src + (size_t)u * C, v[l][u]);
-        } else {
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = e < ITEMS && js + 4 * tq + u < j1;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[l][u][i] = 0.0f;
+        for (int w = 0; w < 8 / EPC; ++w) {
+          const u32x4v zero = {0u, 0u, 0u, 0u};
+          raw[l][u][w] = ok ? *reinterpret_cast<const u32x4v*>(src + (size_t)u * C + w * EPC) : zero;
         }
       }
     }
 #pragma unroll
     for (int l = 0; l < NLOAD; ++l) {
       const int e = tid + 256 * l;
-      if (e < 2 * PAIRS * DC) {
-        const int which = e / (PAIRS * DC);
-        const int r = e % (PAIRS * DC);
-        const int tok = 2 * (r / DC), c8 = (r % DC) * 8;
-        T* dst = (which ? At : Kt) + c8 * PITCH + tok;
+      if (e < ITEMS) {
+        const int tq = e % QUADS, rest = e / QUADS;
+        const int c8 = (rest % DC) * 8, which = rest / DC;
+        T* dst = (which ? At : Kt) + c8 * PITCH + 4 * tq;
+        const T* v0 = reinterpret_cast<const T*>(&raw[l][0][0]);
+        const T* v1 = reinterpret_cast<const T*>(&raw[l][1][0]);
+        const T* v2 = reinterpret_cast<const T*>(&raw[l][2][0]);
+        const T* v3 = reinterpret_cast<const T*>(&raw[l][3][0]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          dst[i * PITCH] = from_f32<T>(v[l][0][i]);
-          dst[i * PITCH + 1] = from_f32<T>(v[l][1][i]);
-        }
+        for (int i = 0; i < 8; ++i) store_quad(dst + i * PITCH, v0[i], v1[i], v2[i], v3[i]);
       }
     }
     for (int t = tid; t < SLAB; t += 256) At[d * PITCH + t] = from_f32<T>(js + t < j1 ? 1.0f : 0.0f);
@@ -200,14 +217,16 @@ hipError_t launch_kv_state(const T* kc, const T* vc, int B, int Nc, int heads, i
 }
 
 // ---------------------------------------------------------------------------
-// Apply: y_i = (Q_i S) / (Q_i . z + eps) per head. The wave computes
-// Y^T = S^T Q^T on 16-token tiles: A = st (kept in registers for the whole
-// wave), B = 16 queries read straight from memory as 16-byte fragments.
-// Lane l ends with 4 consecutive output channels of token l % 16 (8-byte
-// store). The denominator is a VALU dot of the lane's query slice with z,
-// summed over the four lanes that share a token.
+// Apply: y_i = (Q_i S) / (Q_i . z + eps) per head. A block owns one head and
+// kApplyTokens tokens; it stages the head's operand st (S^T, hi and lo parts)
+// and z in LDS once, and each wave keeps the fragments in registers while it
+// walks 16-token tiles: Y^T = S^T Q^T with B = 16 queries read straight from
+// memory as 16-byte fragments (the next tile's are requested before the
+// current tile's matrix work). Lane l ends with 4 consecutive output channels
+// of token l % 16 (8-byte store). The denominator is a VALU dot of the lane's
+// query slice with z, summed over the four lanes that share a token.
 // ---------------------------------------------------------------------------
-constexpr int kApplyTilesPerWave = 8;
+constexpr int kApplyTokens = 512;   // tokens per block (32 tiles, 8 per wave)
 
 template <typename T, int DT>
 __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict__ q, int ldq,
@@ -216,50 +235,70 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
                                                             T* __restrict__ y, int ldy) {
   constexpr int KS = (DT + 1) / 2;
   constexpr int DP = 16 * DT, DK = 32 * KS;
+  constexpr int PITCH = DK + 8;                      // 16 rows of one fragment read hit distinct banks
   constexpr bool SPLIT = std::is_same<T, bf16>::value;
+  constexpr int NPART = SPLIT ? 2 : 1;
+  constexpr int TPW = kApplyTokens / 16 / 4;         // tiles per wave
   typedef typename Frag<T>::type FragT;
+  __shared__ __attribute__((aligned(16))) T sst[NPART * DP * PITCH];
+  __shared__ float szp[DK];
   const int h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
   const size_t bh = (size_t)b * heads + h;
-  const T* sthi = st + bh * 2 * DP * DK;
-  const T* stlo = sthi + DP * DK;
+  const T* gst = st + bh * 2 * DP * DK;
+
+  // Stage the operand: NPART x DP rows of DK elements, 8 elements per thread step.
+  for (int e = tid; e < NPART * DP * (DK / 8); e += 256) {
+    const int part = e / (DP * (DK / 8));
+    const int r = e % (DP * (DK / 8));
+    const int row = r / (DK / 8), c8 = (r % (DK / 8)) * 8;
+    float v[8];
+    load8(gst + (size_t)part * DP * DK + row * DK + c8, v);
+    store8(sst + (part * DP + row) * PITCH + c8, v);
+  }
+  for (int k = tid; k < DK; k += 256) szp[k] = zp[bh * DK + k];
+  __syncthreads();
 
   FragT ahi[DT][KS], alo[DT][KS];
 #pragma unroll
   for (int tn = 0; tn < DT; ++tn)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      frag_load(ahi[tn][s], sthi + (tn * 16 + fr) * DK + s * 32 + g * 8);
-      if (SPLIT) frag_load(alo[tn][s], stlo + (tn * 16 + fr) * DK + s * 32 + g * 8);
+      frag_load(ahi[tn][s], sst + (tn * 16 + fr) * PITCH + s * 32 + g * 8);
+      if (SPLIT) frag_load(alo[tn][s], sst + (DP + tn * 16 + fr) * PITCH + s * 32 + g * 8);
     }
   float zr[KS][8];
 #pragma unroll
   for (int s = 0; s < KS; ++s)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) zr[s][i] = zp[bh * DK + s * 32 + g * 8 + i];
+    for (int i = 0; i < 8; ++i) zr[s][i] = szp[s * 32 + g * 8 + i];
 
-  const int ntiles = (N + 15) / 16;
-  const int tile0 = (blockIdx.x * 4 + wave) * kApplyTilesPerWave;
-  for (int tt = 0; tt < kApplyTilesPerWave; ++tt) {
-    const int tile = tile0 + tt;
-    if (tile >= ntiles) break;
+  const int tile0 = (blockIdx.x * 4 + wave) * TPW;
+  FragT bq[2][KS];
+  auto load_q = [&](FragT (&dst)[KS], int tile) {
     const int tok = tile * 16 + fr;
     const bool tv = tok < N;
     const T* qrow = q + ((size_t)b * N + (tv ? tok : 0)) * ldq + h * d;
-    FragT bq[KS];
-    float den = 0.0f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int k = s * 32 + g * 8;
-      if (tv && k < d) {
-        frag_load(bq[s], qrow + k);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) den += to_f32(bq[s][i]) * zr[s][i];
-      } else {
-        frag_zero(bq[s]);
-      }
+      if (tv && k < d) frag_load(dst[s], qrow + k);
+      else frag_zero(dst[s]);
     }
+  };
+  load_q(bq[0], tile0);
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tile = tile0 + tt;
+    const int c = tt & 1;
+    if (tt + 1 < TPW) load_q(bq[c ^ 1], tile + 1);
+    const int tok = tile * 16 + fr;
+    float den = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) den += to_f32(bq[c][s][i]) * zr[s][i];
     den += __shfl_xor(den, 16, 64);
     den += __shfl_xor(den, 32, 64);
     const float inv = 1.0f / (den + eps);
@@ -269,11 +308,11 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
       acc_zero(acc[tn]);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        if (SPLIT) mma16(acc[tn], alo[tn][s], bq[s]);
-        mma16(acc[tn], ahi[tn][s], bq[s]);
+        if (SPLIT) mma16(acc[tn], alo[tn][s], bq[c][s]);
+        mma16(acc[tn], ahi[tn][s], bq[c][s]);
       }
     }
-    if (tv) {
+    if (tok < N) {
       T* yrow = y + ((size_t)b * N + tok) * ldy + h * d;
 #pragma unroll
       for (int tn = 0; tn < DT; ++tn) {
@@ -292,8 +331,7 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
 template <typename T>
 hipError_t launch_linattn_apply(const T* q, int ldq, const T* st, const float* zp, int B, int N, int heads,
                                 int d, float eps, T* y, int ldy, hipStream_t s) {
-  const int ntiles = (N + 15) / 16;
-  const int blocks = (ntiles + 4 * kApplyTilesPerWave - 1) / (4 * kApplyTilesPerWave);
+  const int blocks = (N + kApplyTokens - 1) / kApplyTokens;
   dim3 grid(blocks, heads, B), block(256);
   switch ((d + 15) / 16) {
 #define EDIT_APPLY_CASE(DTV)                                                                        \
