@@ -17,8 +17,12 @@ sample of the same workload on the host's cores.
 """
 import argparse
 import ctypes
+import dataclasses
+import glob
+import hashlib
 import json
 import os
+import platform
 import statistics
 import sys
 import time
@@ -60,6 +64,52 @@ def algorithmic_work(s):
     }
 
 
+def kernel_source_hash():
+    """sha256 over the library's kernel and launch sources. HBM counters taken
+    for one version of the kernels describe that version only."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "linear_compressed_attention_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, step):
+    """HBM bytes per launch of `step` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (already scaled by the copy calibration), or None when
+    there is none or the kernels have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"edit_layer_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    src = kernel_source_hash()
+    with open(path) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) == 4 and f[0] == "traffic" and f[1] == step and f[3] == src:
+                return float(f[2])
+    return None
+
+
+def pct(v, q):
+    v = sorted(v)
+    i = q * (len(v) - 1)
+    lo = int(i)
+    hi = min(lo + 1, len(v) - 1)
+    return v[lo] + (v[hi] - v[lo]) * (i - lo)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 STEP_BOUND = {"cf_conv3x3": "mfma", "gn_stats": "hbm", "cf_restore": "hbm", "q_proj": "mfma", "kv_proj": "mfma",
               "sc_dwconv": "hbm", "kv_state": "hbm", "linattn_apply": "hbm", "out_proj": "mfma"}
 
@@ -95,21 +145,29 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def cpu_baseline(shape, inp, runs):
-    """The float64 oracle, as it stands, on the host cores."""
+def cpu_baseline(shape, inp, min_runs, budget_s):
+    """The float64 oracle, as it stands, on the host cores: at least
+    `min_runs` full layer forwards of the same workload, more while the total
+    stays under `budget_s` seconds."""
     from threadpoolctl import threadpool_info
     from oracle import edit_oracle as O
     times = []
-    for _ in range(runs):
+    while len(times) < min_runs or (sum(times) + statistics.median(times) < budget_s and len(times) < 50):
         t0 = time.perf_counter()
-        O.edit_attn_forward(inp["x"], inp["w"], shape)
+        if shape.n_text:
+            O.mmedit_hybrid_forward(inp["x"], inp["x_txt"], inp["w"], inp["w_txt"], shape)
+        else:
+            O.edit_attn_forward(inp["x"], inp["w"], shape)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": shape.B * shape.N / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{runs} full float64 layer forwards of the same workload ({shape.B * shape.N} tokens each), "
+    what = "MM-EDiT hybrid" if shape.n_text else "EDiT layer"
+    return {"value": round(shape.B * shape.N / med, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} full float64 {what} forwards of the same workload "
+                      f"({shape.B * shape.N} image tokens each, {sum(times):.1f} s of CPU work), "
                       f"median {med:.2f} s; cores = BLAS threads",
-            "seconds_per_layer": med}
+            "seconds_per_layer": round(med, 3), "affinity_cores": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model()}
 
 
 def main():
@@ -118,7 +176,11 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="pixart2048")
-    ap.add_argument("--cpu-runs", type=int, default=3, help="oracle runs for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-runs", type=int, default=3, help="minimum oracle runs for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="further oracle runs while their total stays under this many seconds")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="forwards timed with a 512 MiB buffer written before each (0 = skip)")
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="timed forwards for the per-step breakdown (default: --steps)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -138,43 +200,82 @@ def main():
     from seeded_inputs import CONFIGS, make_inputs
 
     s = CONFIGS[args.workload]
-    assert s.n_text == 0, "bench times the EDiT layer; the hybrid workload is a parity case"
+    hybrid = s.n_text > 0
     inp = make_inputs(s, seed=0)
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     x = torch.from_numpy(inp["x"]).to(dev).to(tdt)
     w = {k: torch.from_numpy(v).to(dev).to(tdt) for k, v in inp["w"].items()}
     y = torch.empty_like(x)
-    ws = torch.empty(lca.edit_attn_workspace_size(s), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    if hybrid:
+        xt = torch.from_numpy(inp["x_txt"]).to(dev).to(tdt)
+        wt = {k: torch.from_numpy(v).to(dev).to(tdt) for k, v in inp["w_txt"].items()}
+        yt = torch.empty_like(xt)
+        ws = torch.empty(lca.mmedit_hybrid_workspace_size(s, s.n_text), dtype=torch.uint8, device=dev)
+
+        def step():
+            lca.mmedit_hybrid_forward(s, s.n_text, w, wt, x, xt, y, yt, ws, stream)
+    else:
+        ws = torch.empty(lca.edit_attn_workspace_size(s), dtype=torch.uint8, device=dev)
+
+        def step():
+            lca.edit_attn_forward(s, w, x, y, ws, stream)
 
     for _ in range(args.warmup):
-        lca.edit_attn_forward(s, w, x, y, ws, stream)
+        step()
     torch.cuda.synchronize()
 
+    # Timed region: K forwards, an event before each and after the last.
     K = args.steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evk = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(K):
-        lca.edit_attn_forward(s, w, x, y, ws, stream)
-    ev1.record(stream)
+    evk[0].record(stream)
+    for i in range(K):
+        step()
+        evk[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1)
+    ms = evk[0].elapsed_time(evk[K])
+    per_iter = [evk[i].elapsed_time(evk[i + 1]) for i in range(K)]
     ms_per_step = ms / K
     value = s.B * s.N * K / (ms / 1e3)
     assert torch.isfinite(y).all().item(), "non-finite output"
+
+    # Cold variant: 512 MiB written between forwards so that no intermediate
+    # of the previous forward is still in the 256 MB last-level cache.
+    cold = None
+    if args.cold_steps > 0:
+        junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cms = []
+        for i in range(args.cold_steps):
+            junk.fill_(i & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            b.synchronize()
+            cms.append(a.elapsed_time(b))
+        del junk
+        cold = {"steps": args.cold_steps, "ms_median": round(statistics.median(cms), 5),
+                "tokens_per_s": round(s.B * s.N / (statistics.median(cms) / 1e3), 1)}
 
     # Per-step durations from events the library records between its steps.
     P = args.profile_steps or K
     hev = HipEvents()
     evs = [hev.create(len(STEP_NAMES) + 1) for _ in range(P)]
     torch.cuda.synchronize()
+    # The hybrid's image path runs these same kernels on the same image shape.
+    s_img = dataclasses.replace(s, n_text=0) if hybrid else s
+    ws_img = torch.empty(lca.edit_attn_workspace_size(s_img), dtype=torch.uint8, device=dev) if hybrid else ws
+    # A bounded spin kernel first, so that every timed forward is already
+    # queued when the GPU reaches it: the step intervals then hold no host
+    # launch latency.
+    torch.cuda._sleep(50_000_000)
     for e in evs:
         arr = (ctypes.c_void_p * len(e))(*e)
-        lca.edit_attn_forward_timed(s, w, x, y, ws, arr, stream)
+        lca.edit_attn_forward_timed(s_img, w, x, y, ws_img, arr, stream)
     torch.cuda.synchronize()
     per_step = {n: [] for n in STEP_NAMES}
     for e in evs:
@@ -203,36 +304,59 @@ def main():
     d = steps[dom]
     roofline = {"bound": d["bound"], "achieved": d["achieved"],
                 "peak": PEAK_MFMA_TFLOPS[s.dtype] if d["bound"] == "mfma" else PEAK_HBM_GBS,
-                "unit": d["unit"], "frac": d["frac"], "traffic": None, "kernel": dom,
+                "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(args.workload, dom), "kernel": dom,
                 "avg_us": d["us"], "work_per_launch": d["flops"] if d["bound"] == "mfma" else d["bytes"]}
     layer_floor_us = sum(max(work[n][0] / (PEAK_MFMA_TFLOPS[s.dtype] * 1e6), work[n][1] / (PEAK_HBM_GBS * 1e3))
                          for n in STEP_NAMES)
 
-    if args.copy_calibration:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    # A plain device-to-device copy: the achievable HBM rate beside the
+    # published peak, and (under rocprofv3 --pmc) the HBM counter calibration.
+    nb = 512 << 20
+    src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3 if args.copy_calibration else 10
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nb * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    roofline["achievable_hbm_GBs"] = round(copy_gbs, 1)
+    if d["bound"] == "hbm":
+        roofline["frac_of_achievable"] = round(d["achieved"] / copy_gbs, 4)
 
     cpu = None
     if args.cpu_runs > 0:
-        cpu = cpu_baseline(s, inp, args.cpu_runs)
+        cpu = cpu_baseline(s, inp, args.cpu_runs, args.cpu_budget)
 
+    if hybrid:
+        metric = "image tokens/sec per MM-EDiT hybrid attention layer fwd (text rows included in the time)"
+        wl = (f"{args.workload}: MM-EDiT hybrid attention layer forward, B={s.B}, {s.H}x{s.W} image grid "
+              f"({s.N} image tokens, {s.Nc} compressed) + {s.n_text} text tokens, C={s.C}, {s.heads} heads x "
+              f"{s.head_dim}, r={s.reduction}, {s.gn_groups} GN groups, {s.dtype}")
+    else:
+        metric = "image tokens/sec per EDiT attention layer fwd at 16384 tokens; % HBM/MFMA peak"
+        wl = (f"{args.workload}: EDiT attention layer forward, B={s.B}, {s.H}x{s.W} token grid "
+              f"({s.N} tokens, {s.Nc} compressed K/V tokens), C={s.C}, {s.heads} heads x "
+              f"{s.head_dim}, r={s.reduction}, {s.gn_groups} GN groups, {s.dtype}")
     out = {
-        "metric": "image tokens/sec per EDiT attention layer fwd at 16384 tokens; % HBM/MFMA peak",
+        "metric": metric,
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": s.dtype, "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
-        "config": {"workload": f"{args.workload}: EDiT attention layer forward, B={s.B}, {s.H}x{s.W} token grid "
-                               f"({s.N} tokens, {s.Nc} compressed K/V tokens), C={s.C}, {s.heads} heads x "
-                               f"{s.head_dim}, r={s.reduction}, {s.gn_groups} GN groups, {s.dtype}",
-                   "B": s.B, "H": s.H, "W": s.W, "C": s.C, "heads": s.heads, "head_dim": s.head_dim,
-                   "reduction": s.reduction, "gn_groups": s.gn_groups},
+        "config": {"workload": wl, "B": s.B, "H": s.H, "W": s.W, "C": s.C, "heads": s.heads,
+                   "head_dim": s.head_dim, "reduction": s.reduction, "gn_groups": s.gn_groups,
+                   **({"n_text": s.n_text} if hybrid else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "layer_roofline": {"floor_us": round(layer_floor_us, 1), "frac": round(layer_floor_us / (ms_per_step * 1e3), 4)},
+        "ms_per_step_p10_p50_p90": [round(pct(per_iter, q), 5) for q in (0.1, 0.5, 0.9)],
+        "cold": cold,
+        "layer_roofline": {"floor_us": round(layer_floor_us, 1),
+                           "frac": round(layer_floor_us / (ms_per_step * 1e3), 4),
+                           **({"covers": "image path only"} if hybrid else {})},
         "steps_breakdown": {n: {k: v for k, v in steps[n].items() if k in ("us", "bound", "achieved", "unit", "frac")}
                             for n in STEP_NAMES},
         "wall_s_timed_region": round(wall, 4),

@@ -345,6 +345,10 @@ static hipError_t launch_tiles(const GemmArgs<T>& a, AMode am, EMode em, hipStre
 template <typename T>
 hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if constexpr (std::is_same<T, bf16>::value) {
+    const hipError_t e = launch_gemm_dma(a, am, em, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   switch (EDIT_GEMM_FORCE) {
     case 1: return launch_tiles<T, 128, 96, 2, 2, 2, 1, 0, 16>(a, am, em, s);
     case 2: return launch_tiles<T, 128, 96, 2, 2, 1, 1, 0, 16>(a, am, em, s);

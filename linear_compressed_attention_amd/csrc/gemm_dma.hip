@@ -1,0 +1,364 @@
+// MFMA GEMM for gfx950 with direct global-to-LDS tile loads:
+// C[M][N] = A[M][K] * B[N][K]^T (+ bias, optional ReLU), bf16 in and out,
+// fp32 accumulation. A is either plain rows or an implicit 3x3 stride-1
+// pad-1 convolution over a channels-last image.
+//
+// Serves the dense steps of the EDiT layer ("EDiT: Efficient Diffusion
+// Transformers with Linear Compressed Attention" notes): the ConvFusion 3x3
+// compressing conv (section "ConvFusion"), the query, key and value Linears
+// (sections "ConvFusion" and "Spatial Compressor"), the output Linear and
+// the hybrid's text Linears (section "MM-EDiT").
+//
+// Design (one 4-wave block per CU, 144 KB of LDS):
+//  - Tiles move from HBM/L2 straight into LDS with buffer_load ... lds (16
+//    bytes per lane, no register round trip), through a ring of three stages
+//    held in three distinct LDS arrays, so that the compiler can tell which
+//    stage a fragment read touches and waits only for that stage's loads.
+//    Two K steps are in flight while a third is multiplied.
+//  - Out-of-range rows, and the zero padding of the convolution, read at an
+//    offset beyond the buffer resource: the hardware returns zeros, so the
+//    loads never branch.
+//  - An LDS row is 128 bytes (64 bf16 of K); chunk c of row r sits at
+//    position c ^ ((r >> 1) & 7). A DMA instruction fills 8 whole rows, so
+//    each lane fetches the chunk that belongs at its fixed LDS position.
+//  - 32x32x16 matrix-core steps with the weights as the first operand: an
+//    accumulator then holds 4 consecutive output channels of one token, which
+//    the epilogue writes to LDS as one 8-byte word before 16-byte row stores.
+//  - One barrier per K step, placed before the last quarter of the step's
+//    matrix work: by then every wave holds that quarter's fragments in
+//    registers, so the stage can be refilled while the quarter runs.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace edit {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+constexpr uint32_t kOob = 0x80000000u;   // beyond every resource used here: loads return zero
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // Raw buffer (stride 0); dword 3 selects 32-bit data, the gfx9 default.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Wait until at most VM of this wave's vector-memory loads are outstanding and
+// all of its LDS reads are done, then barrier the block. The empty asm
+// statements keep the compiler from moving memory accesses across.
+template <int VM>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));   // vmcnt(VM) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <typename P>
+__device__ __forceinline__ P pick_seg(const P (&a)[3], int i) {
+  return i == 0 ? a[0] : (i == 1 ? a[1] : a[2]);
+}
+
+}  // namespace
+
+template <int BM, int BN, int WM, int WN, int AM, int EM>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p) {
+  // The body uses gfx950-only types (buffer resources), which the host pass
+  // cannot instantiate; it only needs the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int WTM = BM / WM, WTN = BN / WN;     // tokens x channels per wave
+  constexpr int TI = WTM / 32, CJ = WTN / 32;     // 32 x 32 blocks per wave
+  constexpr int NA = BM / (8 * NW), NB = BN / (8 * NW);   // DMA instructions per wave per stage
+  constexpr int NPER = NA + NB;
+  constexpr int STAGE = (BM + BN) * 128;          // bytes per stage
+  constexpr int CP = BN + 8;                      // epilogue staging pitch (elements)
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
+  static_assert(BM % 16 == 0, "B rows keep the swizzle phase of their LDS row");
+  static_assert(3 * STAGE <= 160 * 1024, "LDS");
+  static_assert(WTM * CP * 2 <= STAGE, "epilogue staging");
+  static_assert(2 * NPER < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) char S0[STAGE];
+  __shared__ __attribute__((aligned(16))) char S1[STAGE];
+  __shared__ __attribute__((aligned(16))) char S2[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  const int seg = n0 / p.seg_rows, nseg0 = n0 - seg * p.seg_rows;   // BN divides seg_rows
+
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, (uint32_t)((size_t)p.M * p.lda * 2));
+  const int seg_n = min(p.seg_rows, p.N - seg * p.seg_rows);
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(pick_seg(p.Bseg, seg), (uint32_t)((size_t)seg_n * p.ldb * 2));
+
+  // Per-lane DMA source offsets. Lane l fills chunk (l & 7) of row (l >> 3)
+  // of an 8-row group; it fetches the logical chunk stored there.
+  const int lr = lane >> 3, pc = lane & 7;
+  uint32_t aoff[NA], boff[NB];
+  uint32_t amask[AM == A_CONV3 ? NA : 1];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const int r = 8 * (a * NW + wave) + lr;
+    const int c = pc ^ ((r >> 1) & 7);
+    const int m = m0 + r;
+    aoff[a] = m < p.M ? (uint32_t)m * (uint32_t)p.lda * 2u + (uint32_t)c * 16u : kOob;
+    if (AM == A_CONV3) {
+      // Taps (ky, kx) whose input pixel (y + ky - 1, x + kx - 1) lies inside the image.
+      uint32_t mk = 0;
+      if (m < p.M) {
+        const int q = m % (p.H * p.W), y = q / p.W, x = q % p.W;
+#pragma unroll
+        for (int t = 0; t < 9; ++t) {
+          const int yy = y + t / 3 - 1, xx = x + t % 3 - 1;
+          if (yy >= 0 && yy < p.H && xx >= 0 && xx < p.W) mk |= 1u << t;
+        }
+      }
+      amask[a] = mk;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int r = 8 * (b * NW + wave) + lr;
+    const int c = pc ^ ((r >> 1) & 7);
+    const int n = n0 + r;
+    boff[b] = n < p.N ? (uint32_t)(nseg0 + r) * (uint32_t)p.ldb * 2u + (uint32_t)c * 16u : kOob;
+  }
+
+  const int nk = AM == A_CONV3 ? 9 * (p.Cin / 64) : p.K / 64;
+
+  // Issue the loads of K step kt into stage S. Plain A: row offsets plus a
+  // uniform K offset. Convolution: K step kt is channel slice kt / 9 of tap
+  // kt % 9; the tap shifts the pixel, which may leave the image.
+#define EDIT_DMA(S, kt_)                                                                          \
+  do {                                                                                            \
+    const int kd_ = (kt_);                                                                         \
+    uint32_t sa, sb;                                                                              \
+    int tap = 0, tapoff = 0;                                                                      \
+    if (AM == A_CONV3) {                                                                          \
+      const int sl = kd_ / 9;                                                                      \
+      tap = kd_ - 9 * sl;                                                                          \
+      tapoff = ((tap / 3 - 1) * p.W + (tap % 3 - 1)) * p.Cin * 2;                                 \
+      sa = (uint32_t)sl * 128u;                                                                   \
+      sb = (uint32_t)(tap * p.Cin + sl * 64) * 2u;                                                \
+    } else {                                                                                      \
+      sa = sb = (uint32_t)kd_ * 128u;                                                              \
+    }                                                                                             \
+    _Pragma("unroll") for (int a = 0; a < NA; ++a) {                                              \
+      uint32_t v = aoff[a];                                                                       \
+      if (AM == A_CONV3) v = ((amask[a] >> tap) & 1u) ? v + (uint32_t)tapoff : kOob;               \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr)((S) + 1024 * (a * NW + wave)), 16, v, \
+                                               sa, 0, 0);                                         \
+    }                                                                                             \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr)((S) + BM * 128 + 1024 * (b * NW + wave)), \
+                                               16, boff[b], sb, 0, 0);                            \
+  } while (0)
+
+  // Fragment addressing: lane l reads row (l & 31) of a 32-row block, logical
+  // chunk 2s + (l >> 5) for sub-step s (16 K values each).
+  const int fr = lane & 31, fh = lane >> 5;
+  int fo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) fo[s] = fr * 128 + (((2 * s + fh) ^ ((fr >> 1) & 7)) << 4);
+  const int xrow = (wm * WTM) * 128;          // this wave's token rows (A region)
+  const int wrow = (BM + wn * WTN) * 128;     // this wave's channel rows (B region)
+
+  f32x16 acc[TI][CJ];
+#pragma unroll
+  for (int t = 0; t < TI; ++t)
+#pragma unroll
+    for (int c = 0; c < CJ; ++c) acc_zero(acc[t][c]);
+  bf16x8 xf[2][TI], wf[2][CJ];
+
+#define EDIT_READ(S, s_, buf_)                                                                    \
+  do {                                                                                            \
+    _Pragma("unroll") for (int t = 0; t < TI; ++t)                                                \
+      xf[buf_][t] = *reinterpret_cast<const bf16x8*>((S) + xrow + t * 4096 + fo[s_]);             \
+    _Pragma("unroll") for (int c = 0; c < CJ; ++c)                                                \
+      wf[buf_][c] = *reinterpret_cast<const bf16x8*>((S) + wrow + c * 4096 + fo[s_]);             \
+  } while (0)
+#define EDIT_MMA(buf_)                                                                            \
+  do {                                                                                            \
+    _Pragma("unroll") for (int t = 0; t < TI; ++t)                                                \
+      _Pragma("unroll") for (int c = 0; c < CJ; ++c)                                              \
+        acc[t][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[buf_][c], xf[buf_][t], acc[t][c], 0, 0, 0); \
+  } while (0)
+
+  // Instruction order inside a sub-step, pinned for the scheduler: each
+  // matrix-core step is followed by one fragment read for the next sub-step
+  // (and, after the barrier, by two of the refill loads), so LDS latency and
+  // load issue hide behind the matrix work.
+  constexpr int NM = TI * CJ, NR = TI + CJ;
+#define EDIT_PIN_SUBSTEP(NV)                                                                      \
+  do {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < NM; ++i) {                                              \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                          \
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
+      if (2 * i < (NV)) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);                         \
+    }                                                                                             \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+  } while (0)
+  // Matrix work of sub-step fragments in set cur_ while the fragments of
+  // sub-step s_ of stage S are read into set nxt_.
+#define EDIT_SUBSTEP(S, s_, nxt_, cur_)                                                           \
+  do {                                                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    EDIT_READ(S, s_, nxt_);                                                                       \
+    EDIT_MMA(cur_);                                                                               \
+    EDIT_PIN_SUBSTEP(0);                                                                          \
+  } while (0)
+
+  // One K step on stage SC (holding step kk); SN holds step kk + 1. On entry
+  // the fragments of sub-step 0 are in set 0. The steady-state form issues
+  // its loads unconditionally, so the loop body is one basic block and the
+  // compiler keeps track of which stage each outstanding load fills.
+#define EDIT_KSTEP_HEAD(SC)                                                                       \
+  EDIT_SUBSTEP(SC, 1, 1, 0);                                                                      \
+  EDIT_SUBSTEP(SC, 2, 0, 1);                                                                      \
+  EDIT_SUBSTEP(SC, 3, 1, 0);
+#define EDIT_KSTEP_FULL(SC, SN, kk)                                                               \
+  do {                                                                                            \
+    EDIT_KSTEP_HEAD(SC)                                                                           \
+    /* step kk+1 landed (only step kk+2's loads may be in flight) and every */                   \
+    /* wave is done reading SC: refill SC with step kk+3.                    */                   \
+    stage_barrier<NPER>();                                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    EDIT_READ(SN, 0, 0);                                                                          \
+    EDIT_DMA(SC, (kk) + 3);                                                                       \
+    EDIT_MMA(1);                                                                                  \
+    EDIT_PIN_SUBSTEP(NPER);                                                                       \
+  } while (0)
+#define EDIT_KSTEP_TAIL(SC, SN, kk)                                                               \
+  do {                                                                                            \
+    EDIT_KSTEP_HEAD(SC)                                                                           \
+    if ((kk) + 2 < nk) stage_barrier<NPER>(); else stage_barrier<0>();                            \
+    if ((kk) + 3 < nk) EDIT_DMA(SC, (kk) + 3);                                                    \
+    if ((kk) + 1 < nk) EDIT_READ(SN, 0, 0);                                                       \
+    EDIT_MMA(1);                                                                                  \
+  } while (0)
+
+  EDIT_DMA(S0, 0);
+  if (nk > 1) EDIT_DMA(S1, 1);
+  if (nk > 2) EDIT_DMA(S2, 2);
+  if (nk > 2) stage_barrier<2 * NPER>();
+  else if (nk > 1) stage_barrier<NPER>();
+  else stage_barrier<0>();
+  EDIT_READ(S0, 0, 0);
+  // Whole rounds of three steps while every step refills its stage, then the
+  // at most five steps left.
+  int kt = 0;
+  for (; kt + 5 < nk; kt += 3) {
+    EDIT_KSTEP_FULL(S0, S1, kt);
+    EDIT_KSTEP_FULL(S1, S2, kt + 1);
+    EDIT_KSTEP_FULL(S2, S0, kt + 2);
+  }
+  EDIT_KSTEP_TAIL(S0, S1, kt);
+  if (kt + 1 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 1);
+  if (kt + 2 < nk) EDIT_KSTEP_TAIL(S2, S0, kt + 2);
+  if (kt + 3 < nk) EDIT_KSTEP_TAIL(S0, S1, kt + 3);
+  if (kt + 4 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 4);
+#undef EDIT_KSTEP_HEAD
+#undef EDIT_KSTEP_FULL
+#undef EDIT_KSTEP_TAIL
+#undef EDIT_SUBSTEP
+#undef EDIT_PIN_SUBSTEP
+#undef EDIT_MMA
+#undef EDIT_READ
+#undef EDIT_DMA
+
+  // Epilogue, one wave row at a time: bias (+ ReLU) in registers, 8-byte
+  // words of 4 channels into LDS, then 16-byte row stores.
+  stage_barrier<0>();
+  bf16* Cs = reinterpret_cast<bf16*>(S0);
+  const bf16* bias = pick_seg(p.bias, seg) + nseg0;
+#pragma unroll 1
+  for (int eg = 0; eg < WM; ++eg) {
+    if (wm == eg) {
+#pragma unroll
+      for (int c = 0; c < CJ; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int nl = wn * WTN + c * 32 + 8 * g + 4 * fh;
+          float bv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (n0 + nl < p.N) {
+            const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(bias + nl);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[i] = (float)b4[i];
+          }
+#pragma unroll
+          for (int t = 0; t < TI; ++t) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[i] = acc[t][c][4 * g + i] + bv[i];
+              if (EM == E_BIAS_RELU) v[i] = v[i] > 0.0f ? v[i] : 0.0f;
+            }
+            store4(Cs + (t * 32 + fr) * CP + nl, v);
+          }
+        }
+    }
+    stage_barrier<0>();
+    constexpr int CPR = BN / 8;
+    for (int idx = tid; idx < WTM * CPR; idx += NT) {
+      const int row = idx / CPR, cg = idx - row * CPR;
+      const int m = m0 + eg * WTM + row, n = n0 + cg * 8;
+      if (m < p.M && n < p.N)
+        *reinterpret_cast<bf16x8*>(p.C + (size_t)m * p.ldc + n) =
+            *reinterpret_cast<const bf16x8*>(Cs + row * CP + cg * 8);
+    }
+    stage_barrier<0>();
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+namespace {
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, AMode am, EMode em, hipStream_t s) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  dim3 grid(tiles), block(64 * WM * WN);
+  if (am == A_PLAIN && em == E_BIAS)
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_PLAIN, E_BIAS>), grid, block, 0, s, a);
+  else if (am == A_PLAIN && em == E_BIAS_RELU)
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_PLAIN, E_BIAS_RELU>), grid, block, 0, s, a);
+  else if (am == A_CONV3 && em == E_BIAS)
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_CONV3, E_BIAS>), grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#ifndef EDIT_DMA_FORCE
+#define EDIT_DMA_FORCE 0
+#endif
+
+// Returns hipErrorNotSupported (nothing launched) when the shape is outside
+// what the kernel handles; the caller then uses the register-staged GEMM.
+hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStream_t s) {
+  if (EDIT_DMA_FORCE < 0) return hipErrorNotSupported;
+  if (am == A_GNACT || em == E_BIAS_RES) return hipErrorNotSupported;
+  // Measured on MI355X (random bf16 data, 16384 tokens): the three-stage
+  // ring pays off on the long K of the 3x3 conv (162 K steps: 132 us against
+  // 227 us for the register-staged kernel), while at K = 1152 (18 steps) the
+  // per-tile fill and epilogue dominate and the register-staged kernel with
+  // several blocks per CU is as fast or faster (63 us against 65-73 us for
+  // the C x C projection). Plain-A GEMMs therefore take this kernel only on
+  // request.
+  if (am == A_PLAIN && EDIT_DMA_FORCE != 1) return hipErrorNotSupported;
+  if (a.K % 64 != 0 || a.N % 8 != 0 || a.ldb % 8 != 0 || a.lda % 8 != 0 || a.ldc % 8 != 0)
+    return hipErrorNotSupported;
+  if (am == A_CONV3 && (a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin)) return hipErrorNotSupported;
+  // Buffer offsets are 32-bit and must stay below the out-of-range marker.
+  if ((size_t)a.M * a.lda * 2 >= kOob) return hipErrorNotSupported;
+  if ((size_t)(a.N < a.seg_rows ? a.N : a.seg_rows) * a.ldb * 2 >= kOob) return hipErrorNotSupported;
+  if (a.N % 128 == 0 && a.seg_rows % 128 == 0 && EDIT_DMA_FORCE != 2)
+    return launch_dma_tiles<256, 128, 2, 2>(a, am, em, s);
+  if (a.N % 96 == 0 && a.seg_rows % 96 == 0) return launch_dma_tiles<256, 96, 4, 1>(a, am, em, s);
+  return hipErrorNotSupported;
+}
+
+}  // namespace edit

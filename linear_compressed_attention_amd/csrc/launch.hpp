@@ -45,6 +45,11 @@ struct GemmArgs {
 template <typename T>
 hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s);
 
+// The bf16 GEMM with direct global-to-LDS loads (plain or 3x3-conv A, bias or
+// bias + ReLU epilogue). Returns hipErrorNotSupported, launching nothing, for
+// shapes it does not cover.
+hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStream_t s);
+
 // GroupNorm statistics of x [B][HW][C] (G groups of C/G consecutive
 // channels): per (b, group) mean and rstd, and the per-channel affine folded
 // into scale/shift [B][C]. partial holds [B][nchunks][G][2] floats.

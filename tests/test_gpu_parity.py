@@ -63,6 +63,13 @@ SMALL = {
                           dtype="bf16", x_std=1.0),
     "bf16_d128": make_shape(B=1, H=12, W=16, C=256, heads=2, head_dim=128, reduction=4, gn_groups=8,
                             dtype="bf16", x_std=1.0),
+    # bf16 shapes whose GEMMs take the direct-to-LDS kernel at ragged token
+    # counts: 256 x 96 conv tiles (C/r = 96) with 6 K steps per projection,
+    # and 256 x 128 conv tiles (C/r = 128) with 72 conv K steps.
+    "bf16_d96_conv96": make_shape(B=2, H=13, W=11, C=384, heads=4, head_dim=96, reduction=4, gn_groups=8,
+                                  dtype="bf16", x_std=1.0),
+    "bf16_d128_conv128": make_shape(B=1, H=9, W=7, C=512, heads=4, head_dim=128, reduction=4, gn_groups=8,
+                                    dtype="bf16", x_std=1.0),
     "f32_1x1": make_shape(B=2, H=1, W=1, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
                           dtype="f32", x_std=1.0),
     "f32_1x5": make_shape(B=1, H=1, W=5, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
