@@ -78,10 +78,16 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   for (int t = 0; t < TPW; ++t) acc_zero(acc[t]);
 
   // Rows that never receive data stay zero: K' channels d..16*DT-1 and the
-  // rows of A past the ones row.
-  for (int i = tid; i < 16 * DT * PITCH; i += 256) Kt[i] = from_f32<T>(0.0f);
-  for (int i = tid; i < 16 * DR * PITCH; i += 256) At[i] = from_f32<T>(0.0f);
-  __syncthreads();
+  // rows of A past the ones row. Only those rows are cleared (16-byte
+  // stores), after the first slab's loads are on their way.
+  auto clear_pad_rows = [&]() {
+    const u32x4v zero = {0u, 0u, 0u, 0u};
+    constexpr int W16 = PITCH * (int)sizeof(T) / 16;   // 16-byte words per row
+    for (int i = tid; i < (16 * DT - d) * W16; i += 256)
+      reinterpret_cast<u32x4v*>(Kt + d * PITCH)[i] = zero;
+    for (int i = tid; i < (16 * DR - d - 1) * W16; i += 256)
+      reinterpret_cast<u32x4v*>(At + (d + 1) * PITCH)[i] = zero;
+  };
 
   typedef typename Frag<T>::type FragT;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
@@ -104,6 +110,7 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
         }
       }
     }
+    if (js == j0) clear_pad_rows();
 #pragma unroll
     for (int l = 0; l < NLOAD; ++l) {
       const int e = tid + 256 * l;

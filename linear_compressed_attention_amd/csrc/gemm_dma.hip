@@ -62,21 +62,19 @@ __device__ __forceinline__ P pick_seg(const P (&a)[3], int i) {
 }  // namespace
 
 template <int BM, int BN, int WM, int WN, int AM, int EM>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p) {
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p, int ntiles) {
   // The body uses gfx950-only types (buffer resources), which the host pass
   // cannot instantiate; it only needs the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;     // tokens x channels per wave
   constexpr int TI = WTM / 32, CJ = WTN / 32;     // 32 x 32 blocks per wave
   constexpr int NA = BM / (8 * NW), NB = BN / (8 * NW);   // DMA instructions per wave per stage
   constexpr int NPER = NA + NB;
   constexpr int STAGE = (BM + BN) * 128;          // bytes per stage
-  constexpr int CP = BN + 8;                      // epilogue staging pitch (elements)
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
   static_assert(BM % 16 == 0, "B rows keep the swizzle phase of their LDS row");
   static_assert(3 * STAGE <= 160 * 1024, "LDS");
-  static_assert(WTM * CP * 2 <= STAGE, "epilogue staging");
   static_assert(2 * NPER < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char S0[STAGE];
   __shared__ __attribute__((aligned(16))) char S1[STAGE];
@@ -85,77 +83,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = (p.N + BN - 1) / BN;
-  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
-  const int seg = n0 / p.seg_rows, nseg0 = n0 - seg * p.seg_rows;   // BN divides seg_rows
-
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, (uint32_t)((size_t)p.M * p.lda * 2));
-  const int seg_n = min(p.seg_rows, p.N - seg * p.seg_rows);
-  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(pick_seg(p.Bseg, seg), (uint32_t)((size_t)seg_n * p.ldb * 2));
-
-  // Per-lane DMA source offsets. Lane l fills chunk (l & 7) of row (l >> 3)
-  // of an 8-row group; it fetches the logical chunk stored there.
-  const int lr = lane >> 3, pc = lane & 7;
-  uint32_t aoff[NA], boff[NB];
-  uint32_t amask[AM == A_CONV3 ? NA : 1];
-#pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    const int r = 8 * (a * NW + wave) + lr;
-    const int c = pc ^ ((r >> 1) & 7);
-    const int m = m0 + r;
-    aoff[a] = m < p.M ? (uint32_t)m * (uint32_t)p.lda * 2u + (uint32_t)c * 16u : kOob;
-    if (AM == A_CONV3) {
-      // Taps (ky, kx) whose input pixel (y + ky - 1, x + kx - 1) lies inside the image.
-      uint32_t mk = 0;
-      if (m < p.M) {
-        const int q = m % (p.H * p.W), y = q / p.W, x = q % p.W;
-#pragma unroll
-        for (int t = 0; t < 9; ++t) {
-          const int yy = y + t / 3 - 1, xx = x + t % 3 - 1;
-          if (yy >= 0 && yy < p.H && xx >= 0 && xx < p.W) mk |= 1u << t;
-        }
-      }
-      amask[a] = mk;
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int r = 8 * (b * NW + wave) + lr;
-    const int c = pc ^ ((r >> 1) & 7);
-    const int n = n0 + r;
-    boff[b] = n < p.N ? (uint32_t)(nseg0 + r) * (uint32_t)p.ldb * 2u + (uint32_t)c * 16u : kOob;
-  }
-
   const int nk = AM == A_CONV3 ? 9 * (p.Cin / 64) : p.K / 64;
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, (uint32_t)((size_t)p.M * p.lda * 2));
 
-  // Issue the loads of K step kt into stage S. Plain A: row offsets plus a
-  // uniform K offset. Convolution: K step kt is channel slice kt / 9 of tap
-  // kt % 9; the tap shifts the pixel, which may leave the image.
-#define EDIT_DMA(S, kt_)                                                                          \
-  do {                                                                                            \
-    const int kd_ = (kt_);                                                                         \
-    uint32_t sa, sb;                                                                              \
-    int tap = 0, tapoff = 0;                                                                      \
-    if (AM == A_CONV3) {                                                                          \
-      const int sl = kd_ / 9;                                                                      \
-      tap = kd_ - 9 * sl;                                                                          \
-      tapoff = ((tap / 3 - 1) * p.W + (tap % 3 - 1)) * p.Cin * 2;                                 \
-      sa = (uint32_t)sl * 128u;                                                                   \
-      sb = (uint32_t)(tap * p.Cin + sl * 64) * 2u;                                                \
-    } else {                                                                                      \
-      sa = sb = (uint32_t)kd_ * 128u;                                                              \
-    }                                                                                             \
-    _Pragma("unroll") for (int a = 0; a < NA; ++a) {                                              \
-      uint32_t v = aoff[a];                                                                       \
-      if (AM == A_CONV3) v = ((amask[a] >> tap) & 1u) ? v + (uint32_t)tapoff : kOob;               \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr)((S) + 1024 * (a * NW + wave)), 16, v, \
-                                               sa, 0, 0);                                         \
-    }                                                                                             \
-    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr)((S) + BM * 128 + 1024 * (b * NW + wave)), \
-                                               16, boff[b], sb, 0, 0);                            \
-  } while (0)
-
+  // Lane l fills chunk (l & 7) of row (l >> 3) of an 8-row DMA group and
+  // fetches the logical chunk stored there.
+  const int lr = lane >> 3, pc = lane & 7;
   // Fragment addressing: lane l reads row (l & 31) of a 32-row block, logical
   // chunk 2s + (l >> 5) for sub-step s (16 K values each).
   const int fr = lane & 31, fh = lane >> 5;
@@ -165,12 +98,86 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
   const int xrow = (wm * WTM) * 128;          // this wave's token rows (A region)
   const int wrow = (BM + wn * WTN) * 128;     // this wave's channel rows (B region)
 
+  // Per-tile state. The block walks tiles bid, bid + G, ... (G = grid size, a
+  // multiple of 8 when there is more than one round), renumbered so that each
+  // XCD takes a contiguous range and its CUs work on neighbouring tiles.
+  int m0, n0, nseg0;
+  __amdgpu_buffer_rsrc_t rsB;
+  const bf16* bias;
+  uint32_t aoff[NA], boff[NB];
+  uint32_t amask[AM == A_CONV3 ? NA : 1];
+#define EDIT_SET_TILE(tl_)                                                                        \
+  do {                                                                                            \
+    const int tile_ = xcd_swizzle((tl_), ntiles);                                                 \
+    m0 = (tile_ / tiles_n) * BM;                                                                  \
+    n0 = (tile_ % tiles_n) * BN;                                                                  \
+    const int seg_ = n0 / p.seg_rows;   /* BN divides seg_rows */                                 \
+    nseg0 = n0 - seg_ * p.seg_rows;                                                               \
+    const int seg_n_ = min(p.seg_rows, p.N - seg_ * p.seg_rows);                                  \
+    rsB = make_rsrc(pick_seg(p.Bseg, seg_), (uint32_t)((size_t)seg_n_ * p.ldb * 2));              \
+    bias = pick_seg(p.bias, seg_) + nseg0;                                                        \
+    _Pragma("unroll") for (int a = 0; a < NA; ++a) {                                              \
+      const int r = 8 * (a * NW + wave) + lr;                                                     \
+      const int c = pc ^ ((r >> 1) & 7);                                                          \
+      const int m = m0 + r;                                                                       \
+      aoff[a] = m < p.M ? (uint32_t)m * (uint32_t)p.lda * 2u + (uint32_t)c * 16u : kOob;          \
+      if (AM == A_CONV3) {                                                                        \
+        /* taps (ky, kx) whose input pixel (y + ky - 1, x + kx - 1) is inside the image */       \
+        uint32_t mk = 0;                                                                          \
+        if (m < p.M) {                                                                            \
+          const int q = m % (p.H * p.W), y = q / p.W, x = q % p.W;                                \
+          _Pragma("unroll") for (int t = 0; t < 9; ++t) {                                         \
+            const int yy = y + t / 3 - 1, xx = x + t % 3 - 1;                                     \
+            if (yy >= 0 && yy < p.H && xx >= 0 && xx < p.W) mk |= 1u << t;                        \
+          }                                                                                       \
+        }                                                                                         \
+        amask[AM == A_CONV3 ? a : 0] = mk;                                                        \
+      }                                                                                           \
+    }                                                                                             \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                              \
+      const int r = 8 * (b * NW + wave) + lr;                                                     \
+      const int c = pc ^ ((r >> 1) & 7);                                                          \
+      boff[b] = n0 + r < p.N ? (uint32_t)(nseg0 + r) * (uint32_t)p.ldb * 2u + (uint32_t)c * 16u : kOob; \
+    }                                                                                             \
+  } while (0)
+
+  // Issue the loads of K step kt into stage S. Plain A: row offsets plus a
+  // uniform K offset. Convolution: K step kt is channel slice kt / 9 of tap
+  // kt % 9; the tap shifts the pixel, which may leave the image.
+#define EDIT_DMA(S, kt_)                                                                          \
+  do {                                                                                            \
+    const int kd_ = (kt_);                                                                        \
+    uint32_t sa, sb;                                                                              \
+    int tap = 0, tapoff = 0;                                                                      \
+    if (AM == A_CONV3) {                                                                          \
+      const int sl = kd_ / 9;                                                                     \
+      tap = kd_ - 9 * sl;                                                                         \
+      tapoff = ((tap / 3 - 1) * p.W + (tap % 3 - 1)) * p.Cin * 2;                                 \
+      sa = (uint32_t)sl * 128u;                                                                   \
+      sb = (uint32_t)(tap * p.Cin + sl * 64) * 2u;                                                \
+    } else {                                                                                      \
+      sa = sb = (uint32_t)kd_ * 128u;                                                             \
+    }                                                                                             \
+    _Pragma("unroll") for (int a = 0; a < NA; ++a) {                                              \
+      uint32_t v = aoff[a];                                                                       \
+      if (AM == A_CONV3) v = ((amask[AM == A_CONV3 ? a : 0] >> tap) & 1u) ? v + (uint32_t)tapoff : kOob; \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr)((S) + 1024 * (a * NW + wave)), 16, v, \
+                                               sa, 0, 0);                                         \
+    }                                                                                             \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr)((S) + BM * 128 + 1024 * (b * NW + wave)), \
+                                               16, boff[b], sb, 0, 0);                            \
+  } while (0)
+#define EDIT_PREFETCH3()                                                                          \
+  do {                                                                                            \
+    EDIT_DMA(S0, 0);                                                                              \
+    if (nk > 1) EDIT_DMA(S1, 1);                                                                  \
+    if (nk > 2) EDIT_DMA(S2, 2);                                                                  \
+  } while (0)
+
   f32x16 acc[TI][CJ];
-#pragma unroll
-  for (int t = 0; t < TI; ++t)
-#pragma unroll
-    for (int c = 0; c < CJ; ++c) acc_zero(acc[t][c]);
   bf16x8 xf[2][TI], wf[2][CJ];
+  bf16x4 bv[CJ][4];   // the tile's bias, fetched before the next tile's loads are queued
 
 #define EDIT_READ(S, s_, buf_)                                                                    \
   do {                                                                                            \
@@ -200,8 +207,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
     }                                                                                             \
     __builtin_amdgcn_sched_barrier(0);                                                            \
   } while (0)
-  // Matrix work of sub-step fragments in set cur_ while the fragments of
-  // sub-step s_ of stage S are read into set nxt_.
+  // Matrix work on the fragments in set cur_ while the fragments of sub-step
+  // s_ of stage S are read into set nxt_.
 #define EDIT_SUBSTEP(S, s_, nxt_, cur_)                                                           \
   do {                                                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                            \
@@ -239,26 +246,75 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
     EDIT_MMA(1);                                                                                  \
   } while (0)
 
-  EDIT_DMA(S0, 0);
-  if (nk > 1) EDIT_DMA(S1, 1);
-  if (nk > 2) EDIT_DMA(S2, 2);
-  if (nk > 2) stage_barrier<2 * NPER>();
-  else if (nk > 1) stage_barrier<NPER>();
-  else stage_barrier<0>();
-  EDIT_READ(S0, 0, 0);
-  // Whole rounds of three steps while every step refills its stage, then the
-  // at most five steps left.
-  int kt = 0;
-  for (; kt + 5 < nk; kt += 3) {
-    EDIT_KSTEP_FULL(S0, S1, kt);
-    EDIT_KSTEP_FULL(S1, S2, kt + 1);
-    EDIT_KSTEP_FULL(S2, S0, kt + 2);
+  int tl = blockIdx.x;
+  EDIT_SET_TILE(tl);
+  EDIT_PREFETCH3();
+  for (;;) {
+    // The tile's bias, requested before anything else is queued behind it.
+#pragma unroll
+    for (int c = 0; c < CJ; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nl = wn * WTN + c * 32 + 8 * g + 4 * fh;
+        bv[c][g] = n0 + nl < p.N ? *reinterpret_cast<const bf16x4*>(bias + nl) : bf16x4{};
+      }
+#pragma unroll
+    for (int t = 0; t < TI; ++t)
+#pragma unroll
+      for (int c = 0; c < CJ; ++c) acc_zero(acc[t][c]);
+
+    // Step 0 landed. Loads complete in issue order; the previous tile's
+    // stores, issued after this tile's loads, may still be outstanding.
+    if (nk > 2) stage_barrier<2 * NPER>();
+    else stage_barrier<0>();
+    EDIT_READ(S0, 0, 0);
+    // Whole rounds of three steps while every step refills its stage, then
+    // the at most five steps left.
+    int kt = 0;
+    for (; kt + 5 < nk; kt += 3) {
+      EDIT_KSTEP_FULL(S0, S1, kt);
+      EDIT_KSTEP_FULL(S1, S2, kt + 1);
+      EDIT_KSTEP_FULL(S2, S0, kt + 2);
+    }
+    EDIT_KSTEP_TAIL(S0, S1, kt);
+    if (kt + 1 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 1);
+    if (kt + 2 < nk) EDIT_KSTEP_TAIL(S2, S0, kt + 2);
+    if (kt + 3 < nk) EDIT_KSTEP_TAIL(S0, S1, kt + 3);
+    if (kt + 4 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 4);
+
+    // The last step's barrier came after every wave's last LDS read: the
+    // stages are free. Queue the next tile's first three steps, then write
+    // this tile from registers while they are in flight.
+    const int em0 = m0, en0 = n0;
+    const int next = tl + (int)gridDim.x;
+    if (next < ntiles) {
+      EDIT_SET_TILE(next);
+      EDIT_PREFETCH3();
+    }
+    // Epilogue: bias (+ ReLU); each accumulator quad is 4 consecutive output
+    // channels of one token, written as one 8-byte store.
+#pragma unroll
+    for (int t = 0; t < TI; ++t) {
+      const int m = em0 + wm * WTM + t * 32 + fr;
+#pragma unroll
+      for (int c = 0; c < CJ; ++c)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = en0 + wn * WTN + c * 32 + 8 * g + 4 * fh;
+          if (m < p.M && n < p.N) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[i] = acc[t][c][4 * g + i] + (float)bv[c][g][i];
+              if (EM == E_BIAS_RELU) v[i] = v[i] > 0.0f ? v[i] : 0.0f;
+            }
+            store4(p.C + (size_t)m * p.ldc + n, v);
+          }
+        }
+    }
+    if (next >= ntiles) break;
+    tl = next;
   }
-  EDIT_KSTEP_TAIL(S0, S1, kt);
-  if (kt + 1 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 1);
-  if (kt + 2 < nk) EDIT_KSTEP_TAIL(S2, S0, kt + 2);
-  if (kt + 3 < nk) EDIT_KSTEP_TAIL(S0, S1, kt + 3);
-  if (kt + 4 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 4);
 #undef EDIT_KSTEP_HEAD
 #undef EDIT_KSTEP_FULL
 #undef EDIT_KSTEP_TAIL
@@ -266,50 +322,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
 #undef EDIT_PIN_SUBSTEP
 #undef EDIT_MMA
 #undef EDIT_READ
+#undef EDIT_PREFETCH3
 #undef EDIT_DMA
-
-  // Epilogue, one wave row at a time: bias (+ ReLU) in registers, 8-byte
-  // words of 4 channels into LDS, then 16-byte row stores.
-  stage_barrier<0>();
-  bf16* Cs = reinterpret_cast<bf16*>(S0);
-  const bf16* bias = pick_seg(p.bias, seg) + nseg0;
-#pragma unroll 1
-  for (int eg = 0; eg < WM; ++eg) {
-    if (wm == eg) {
-#pragma unroll
-      for (int c = 0; c < CJ; ++c)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int nl = wn * WTN + c * 32 + 8 * g + 4 * fh;
-          float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (n0 + nl < p.N) {
-            const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(bias + nl);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bv[i] = (float)b4[i];
-          }
-#pragma unroll
-          for (int t = 0; t < TI; ++t) {
-            float v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              v[i] = acc[t][c][4 * g + i] + bv[i];
-              if (EM == E_BIAS_RELU) v[i] = v[i] > 0.0f ? v[i] : 0.0f;
-            }
-            store4(Cs + (t * 32 + fr) * CP + nl, v);
-          }
-        }
-    }
-    stage_barrier<0>();
-    constexpr int CPR = BN / 8;
-    for (int idx = tid; idx < WTM * CPR; idx += NT) {
-      const int row = idx / CPR, cg = idx - row * CPR;
-      const int m = m0 + eg * WTM + row, n = n0 + cg * 8;
-      if (m < p.M && n < p.N)
-        *reinterpret_cast<bf16x8*>(p.C + (size_t)m * p.ldc + n) =
-            *reinterpret_cast<const bf16x8*>(Cs + row * CP + cg * 8);
-    }
-    stage_barrier<0>();
-  }
+#undef EDIT_SET_TILE
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -317,14 +332,23 @@ namespace {
 
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, AMode am, EMode em, hipStream_t s) {
-  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  dim3 grid(tiles), block(64 * WM * WN);
+  // One block per CU (the kernel holds 3 x (BM + BN) x 128 bytes of LDS); with
+  // more tiles than CUs each block walks several tiles, and the grid stays a
+  // multiple of 8 so that every XCD keeps its own contiguous tile range.
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
+  const int ntiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int g8 = cus / 8 * 8;
+  const int blocks = ntiles <= g8 ? ntiles : g8;
+  dim3 grid(blocks), block(64 * WM * WN);
   if (am == A_PLAIN && em == E_BIAS)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_PLAIN, E_BIAS>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_PLAIN, E_BIAS>), grid, block, 0, s, a, ntiles);
   else if (am == A_PLAIN && em == E_BIAS_RELU)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_PLAIN, E_BIAS_RELU>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_PLAIN, E_BIAS_RELU>), grid, block, 0, s, a, ntiles);
   else if (am == A_CONV3 && em == E_BIAS)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_CONV3, E_BIAS>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_CONV3, E_BIAS>), grid, block, 0, s, a, ntiles);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
