@@ -14,7 +14,7 @@ matrix and the eta approximation under it).
 
 Every step is written from its definition, in the order the page composes
 them, with numpy's matmul as the only library primitive. Where the page
-leaves a detail open, the reading taken is named at the function (R1..R16);
+leaves a detail open, the reading taken is named at the function (R1..R16, R23);
 the same readings are listed in the design notes of the repository.
 
 Pins (what checks this code against something other than itself) live in
@@ -289,7 +289,35 @@ def hybrid_eta(n_img, n_txt):
     return n_img / (n_img + n_txt)
 
 
-def mmedit_hybrid_forward(x_img, x_txt, w, wt, shape, trace=None):
+def linear_attention_denominator(q, z, heads, eps):
+    """Q_i . z + eps per token and head: the normaliser of the linear block
+    (section "Linear-attention formula"; R11). Returns [B, N, heads]."""
+    Q = split_heads(q, heads)
+    return (Q * z[:, :, None, :]).sum(axis=-1).transpose(0, 2, 1) + eps
+
+
+def hybrid_image_rows_exact(q_i, S, z, k_t, v_t, heads, eps):
+    """Image rows of the hybrid with eta^Lin computed instead of approximated.
+
+    Section "MM-EDiT": the hybrid matrix weights the linear block A^Lin by
+    eta^Lin and the image->text softmax block by 1 - eta^Lin; the page replaces
+    eta^Lin by the token ratio to avoid a custom kernel. Computed exactly, the
+    two blocks share one normaliser (R23):
+        y_i = (Q_i S + sum_t exp(s_it) V_t) / (Q_i . z + eps + sum_t exp(s_it)),
+        s_it = Q_i . K_t / sqrt(d),
+    which is eta_i A^Lin_i + (1 - eta_i) A_i with
+    eta_i = (Q_i . z + eps) / (Q_i . z + eps + sum_t exp(s_it)).
+    q_i [B, N, C]; S [B, h, d, d]; z [B, h, d]; k_t, v_t [B, N_T, C]."""
+    Q = split_heads(q_i, heads)
+    Kt, Vt = split_heads(k_t, heads), split_heads(v_t, heads)
+    d = Q.shape[-1]
+    e = np.exp(Q @ np.swapaxes(Kt, 2, 3) / np.sqrt(d))     # [B, h, N, N_T]
+    num = Q @ S + e @ Vt
+    den = (Q * z[:, :, None, :]).sum(axis=-1) + eps + e.sum(axis=-1)
+    return merge_heads(num / den[..., None])
+
+
+def mmedit_hybrid_forward(x_img, x_txt, w, wt, shape, trace=None, eta="ratio"):
     """The MM-EDiT hybrid attention layer (section "MM-EDiT").
 
     Image rows:  eta * A^Lin(Q_I, K'_I, V'_I) + (1 - eta) * A(Q_I, K_T, V_T)
@@ -298,7 +326,11 @@ def mmedit_hybrid_forward(x_img, x_txt, w, wt, shape, trace=None):
     then separate image and text output projections (R12, R16).
     Q_I, K'_I, V'_I are the EDiT features of the image stream (R14); the
     text stream has its own Linear Q/K/V/O and no convolutions (R16).
+    eta="ratio" takes the page's token-count ratio for eta^Lin (R13);
+    eta="exact" computes it per row (hybrid_image_rows_exact, R23).
     Returns (out_img [B, N, C], out_txt [B, N_T, C])."""
+    if eta not in ("ratio", "exact"):
+        raise ValueError(f"eta must be 'ratio' or 'exact', not {eta!r}")
     H, W, heads = shape.H, shape.W, shape.heads
     x_img = _f64(x_img)
     n_img = H * W
@@ -317,13 +349,17 @@ def mmedit_hybrid_forward(x_img, x_txt, w, wt, shape, trace=None):
         q_t = linear(x_txt, wt["w_q"], wt["b_q"])
         k_t = linear(x_txt, wt["w_k"], wt["b_k"])
         v_t = linear(x_txt, wt["w_v"], wt["b_v"])
-        eta = hybrid_eta(n_img, n_txt)
-        y_img = eta * y_lin + (1.0 - eta) * sdpa(q_i, k_t, v_t, heads)
+        if eta == "exact":
+            y_img = hybrid_image_rows_exact(q_i, S, z, k_t, v_t, heads, shape.eps)
+        else:
+            e_r = hybrid_eta(n_img, n_txt)
+            y_img = e_r * y_lin + (1.0 - e_r) * sdpa(q_i, k_t, v_t, heads)
         y_txt = sdpa(q_t, np.concatenate([kc, k_t], axis=1),
                      np.concatenate([vc, v_t], axis=1), heads)
         out_txt = linear(y_txt, wt["w_o"], wt["b_o"])
     out_img = linear(y_img, w["w_o"], w["b_o"])
     if trace is not None:
         trace.update(S=S, z=z, y_lin=y_lin, y=y_img, y_txt=y_txt, q_t=q_t,
-                     k_t=k_t, v_t=v_t, out=out_img, out_txt=out_txt)
+                     k_t=k_t, v_t=v_t, out=out_img, out_txt=out_txt,
+                     lin_den=linear_attention_denominator(q_i, z, heads, shape.eps))
     return out_img, out_txt

@@ -12,6 +12,8 @@ notes evaluate on; no dataset or trained weight is involved):
 * ``pixart1024``    bf16, 2 x 64x64,   C=1152, 16 heads x 72, r=4, 32 groups.
 * ``pixart2048``    bf16, 1 x 128x128, same channels (16384 tokens).
 * ``pixart4096``    bf16, 1 x 256x256, same channels (65536 tokens).
+* ``pixart8192``    bf16, 1 x 512x512, same channels (262144 tokens): the
+                    largest resolution of the notes' latency table.
 * ``sd35m_hybrid``  bf16, 2 x 64x64 image grid + 333 text tokens, C=1536,
                     24 heads x 64, r=4, 32 groups.
 
@@ -83,6 +85,8 @@ CONFIGS: Dict[str, LayerShape] = {
     "pixart2048": LayerShape(B=1, H=128, W=128, C=1152, heads=16, head_dim=72,
                              reduction=4, gn_groups=32, eps=1e-6, dtype="bf16"),
     "pixart4096": LayerShape(B=1, H=256, W=256, C=1152, heads=16, head_dim=72,
+                             reduction=4, gn_groups=32, eps=1e-6, dtype="bf16"),
+    "pixart8192": LayerShape(B=1, H=512, W=512, C=1152, heads=16, head_dim=72,
                              reduction=4, gn_groups=32, eps=1e-6, dtype="bf16"),
     "sd35m_hybrid": LayerShape(B=2, H=64, W=64, C=1536, heads=24, head_dim=64,
                                reduction=4, gn_groups=32, eps=1e-6, dtype="bf16",

@@ -86,7 +86,7 @@ def test_small_shapes(name):
     check_edit(SMALL[name], seed=1, gn_affine_random=True)
 
 
-@pytest.mark.parametrize("name", ["pixart1024", "pixart2048", "pixart4096"])
+@pytest.mark.parametrize("name", ["pixart1024", "pixart2048", "pixart4096", "pixart8192"])
 def test_pixart_full_size(name):
     check_edit(CONFIGS[name])
 

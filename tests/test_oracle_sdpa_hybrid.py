@@ -111,3 +111,113 @@ def test_hybrid_rows_by_definition():
             sc = np.exp(qt[b, 2, sl] @ keys.T / math.sqrt(d))
             np.testing.assert_allclose(tr["y_txt"][b, 2, sl], (sc[:, None] * vals).sum(0) / sc.sum(), rtol=1e-12)
     np.testing.assert_allclose(out_t, tr["y_txt"] @ wt["w_o"].T.astype(float) + wt["b_o"], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# The hybrid's image rows with eta^Lin computed exactly (joint normaliser).
+# ---------------------------------------------------------------------------
+
+def _exact_rows_by_loops(q, kc, vc, kt, vt, heads, eps):
+    """Every weight written out: image key j weighs Q_i . K'_j (the linear
+    kernel, no S or z), text key t weighs exp(Q_i . K_t / sqrt(d)); one
+    normaliser over both, plus eps (pure Python floats)."""
+    B, N, C = q.shape
+    d = C // heads
+    out = np.zeros_like(q)
+    for b in range(B):
+        for h in range(heads):
+            sl = slice(h * d, (h + 1) * d)
+            for i in range(N):
+                num = [0.0] * d
+                den = eps
+                for j in range(kc.shape[1]):
+                    wgt = sum(float(q[b, i, h * d + c]) * float(kc[b, j, h * d + c]) for c in range(d))
+                    den += wgt
+                    for c in range(d):
+                        num[c] += wgt * float(vc[b, j, h * d + c])
+                for t in range(kt.shape[1]):
+                    s = sum(float(q[b, i, h * d + c]) * float(kt[b, t, h * d + c]) for c in range(d))
+                    wgt = math.exp(s / math.sqrt(d))
+                    den += wgt
+                    for c in range(d):
+                        num[c] += wgt * float(vt[b, t, h * d + c])
+                out[b, i, sl] = [u / den for u in num]
+    return out
+
+
+def _feats(rng, B, N, Nc, NT, C):
+    q = np.abs(rng.standard_normal((B, N, C)))          # ReLU'd queries
+    kc = np.abs(rng.standard_normal((B, Nc, C)))        # ReLU'd compressed keys
+    vc = rng.standard_normal((B, Nc, C))
+    kt = rng.standard_normal((B, NT, C))
+    vt = rng.standard_normal((B, NT, C))
+    return q, kc, vc, kt, vt
+
+
+def test_exact_rows_vs_explicit_weights():
+    rng = np.random.default_rng(3)
+    B, heads, d, N, Nc, NT, eps = 2, 2, 4, 5, 6, 3, 1e-6
+    q, kc, vc, kt, vt = _feats(rng, B, N, Nc, NT, heads * d)
+    S, z = O.kv_state(kc, vc, heads)
+    got = O.hybrid_image_rows_exact(q, S, z, kt, vt, heads, eps)
+    ref = _exact_rows_by_loops(q, kc, vc, kt, vt, heads, eps)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_exact_rows_are_the_hybrid_matrix_with_row_eta():
+    """eta_i A^Lin + (1 - eta_i) A with the page's two blocks computed by the
+    oracle's own linear attention and softmax attention, eta_i from the
+    explicit weight masses."""
+    rng = np.random.default_rng(4)
+    B, heads, d, N, Nc, NT, eps = 1, 3, 8, 7, 9, 4, 1e-6
+    q, kc, vc, kt, vt = _feats(rng, B, N, Nc, NT, heads * d)
+    S, z = O.kv_state(kc, vc, heads)
+    lin = O.linear_attention_apply(q, S, z, heads, eps)
+    soft = O.sdpa(q, kt, vt, heads)
+    got = O.hybrid_image_rows_exact(q, S, z, kt, vt, heads, eps)
+    Q, Kc, Kt = O.split_heads(q, heads), O.split_heads(kc, heads), O.split_heads(kt, heads)
+    lin_mass = (Q @ np.swapaxes(Kc, 2, 3)).sum(-1) + eps                 # [B, h, N]
+    soft_mass = np.exp(Q @ np.swapaxes(Kt, 2, 3) / math.sqrt(d)).sum(-1)
+    eta = O.merge_heads(np.repeat((lin_mass / (lin_mass + soft_mass))[..., None], d, axis=-1))
+    np.testing.assert_allclose(got, eta * lin + (1 - eta) * soft, rtol=1e-12, atol=1e-14)
+    den = O.linear_attention_denominator(q, z, heads, eps)
+    np.testing.assert_allclose(den, lin_mass.transpose(0, 2, 1), rtol=1e-13)
+
+
+def test_exact_rows_closed_forms():
+    rng = np.random.default_rng(5)
+    B, heads, d, N, Nc, NT = 1, 2, 4, 4, 5, 3
+    q, kc, vc, kt, vt = _feats(rng, B, N, Nc, NT, heads * d)
+    # Every value the same vector v: a convex combination returns v, up to the
+    # eps share of the normaliser, which has the closed form below.
+    v = rng.standard_normal(heads * d)
+    vc[:] = v
+    vt[:] = v
+    S, z = O.kv_state(kc, vc, heads)
+    eps = 0.25
+    got = O.hybrid_image_rows_exact(q, S, z, kt, vt, heads, eps)
+    den = O.linear_attention_denominator(q, z, heads, eps)                       # [B, N, h]
+    Q, Kt = O.split_heads(q, heads), O.split_heads(kt, heads)
+    soft = np.exp(Q @ np.swapaxes(Kt, 2, 3) / math.sqrt(d)).sum(-1).transpose(0, 2, 1)
+    frac = (den - eps + soft) / (den + soft)                                      # [B, N, h]
+    np.testing.assert_allclose(got, np.repeat(frac, d, axis=-1) * v, rtol=1e-13)
+    # No text keys: the linear attention itself.
+    got0 = O.hybrid_image_rows_exact(q, S, z, kt[:, :0], vt[:, :0], heads, 1e-6)
+    np.testing.assert_allclose(got0, O.linear_attention_apply(q, S, z, heads, 1e-6), rtol=1e-14)
+
+
+def test_exact_hybrid_layer_reduces_and_differs():
+    s = make_shape(B=1, H=6, W=5, C=32, heads=2, head_dim=16, reduction=4, gn_groups=2, n_text=3, x_std=1.0)
+    inp = make_inputs(s, seed=2)
+    tr_r, tr_e = {}, {}
+    o_r, t_r = O.mmedit_hybrid_forward(inp["x"], inp["x_txt"], inp["w"], inp["w_txt"], s, tr_r)
+    o_e, t_e = O.mmedit_hybrid_forward(inp["x"], inp["x_txt"], inp["w"], inp["w_txt"], s, tr_e, eta="exact")
+    # Text rows are exact in both modes.
+    np.testing.assert_array_equal(t_r, t_e)
+    # The image rows differ (the ratio is an approximation) ...
+    assert np.abs(o_r - o_e).max() > 1e-6
+    # ... and with no text both modes are the plain EDiT layer.
+    s0 = make_shape(B=1, H=6, W=5, C=32, heads=2, head_dim=16, reduction=4, gn_groups=2, x_std=1.0)
+    inp0 = make_inputs(s0, seed=2)
+    e0, _ = O.mmedit_hybrid_forward(inp0["x"], None, inp0["w"], None, s0, eta="exact")
+    np.testing.assert_array_equal(e0, O.edit_attn_forward(inp0["x"], inp0["w"], s0))
