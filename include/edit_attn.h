@@ -124,6 +124,25 @@ edit_status_t mmedit_hybrid_forward(const edit_shape_t* shape, int n_text,
                                     void* y_img, void* y_txt,
                                     void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* MM-EDiT hybrid forward with eta computed exactly per image row and head
+ * instead of the token ratio: the notes' hybrid matrix weights the linear
+ * block by eta^Lin and the image->text softmax block by 1 - eta^Lin, and
+ * approximate eta^Lin by N_I / (N_I + N_T) to avoid a custom kernel ("EDiT"
+ * notes, section "MM-EDiT", the hybrid matrix and the remark under it).
+ * Computed exactly, both blocks share one normaliser:
+ *   image row i: (q_i S + sum_t exp(s_it) V_t) / (q_i . z + eps + sum_t exp(s_it)),
+ *   s_it = q_i . K_t / sqrt(d),
+ * i.e. eta_i = (q_i . z + eps) / (q_i . z + eps + sum_t exp(s_it)). Text rows
+ * and everything else as mmedit_hybrid_forward; same arguments, layout and
+ * workspace size (mmedit_hybrid_workspace_size). exp(s) is taken in fp32:
+ * scores above ~88 (never reached by unit-scale features) overflow to the
+ * softmax block alone. n_text = 0 gives edit_attn_forward's y bit for bit. */
+edit_status_t mmedit_hybrid_exact_forward(const edit_shape_t* shape, int n_text,
+                                          const edit_weights_t* img, const edit_text_weights_t* txt,
+                                          const void* x_img, const void* x_txt,
+                                          void* y_img, void* y_txt,
+                                          void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Where each intermediate of the last forward with this shape lives in the
  * workspace (byte offsets; 0 size = not produced for this call). The layout
  * is a pure function of (shape, n_text). Intermediates, with their dtype T
@@ -139,9 +158,10 @@ edit_status_t mmedit_hybrid_forward(const edit_shape_t* shape, int n_text,
  *   y       [B][N][C]   T      linear-attention output (hybrid: before blending)
  *   qkv_t   [B][N_T][3C] T     text Q | K | V (hybrid only)
  *   y_img   [B][N][C]   T      blended image rows (hybrid with text only)
- *   y_txt   [B][N_T][C] T      text rows before the text output Linear (hybrid only) */
+ *   y_txt   [B][N_T][C] T      text rows before the text output Linear (hybrid only)
+ *   lin_den [B][N][h]   f32    q . z + eps per token and head (exact-eta hybrid only) */
 typedef struct {
-  size_t xc, gn_stat, xt, q, kv0, kc, vc, S, z, y, qkv_t, y_img, y_txt;
+  size_t xc, gn_stat, xt, q, kv0, kc, vc, S, z, y, qkv_t, y_img, y_txt, lin_den;
   size_t total;
 } edit_ws_layout_t;
 

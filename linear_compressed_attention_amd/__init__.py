@@ -16,7 +16,7 @@ from typing import Mapping, Optional
 __all__ = [
     "EDIT_F32", "EDIT_BF16", "EditError", "IMAGE_WEIGHT_FIELDS", "TEXT_WEIGHT_FIELDS", "LAYOUT_FIELDS",
     "edit_attn_workspace_size", "edit_attn_forward", "mmedit_hybrid_workspace_size",
-    "mmedit_hybrid_forward", "edit_attn_forward_timed", "edit_attn_workspace_layout", "EDIT_NUM_STEPS", "edit_status_string", "edit_last_error",
+    "mmedit_hybrid_forward", "mmedit_hybrid_exact_forward", "edit_attn_forward_timed", "edit_attn_workspace_layout", "EDIT_NUM_STEPS", "edit_status_string", "edit_last_error",
     "lib_path", "header_symbols",
 ]
 
@@ -32,7 +32,8 @@ _STATUS = {0: "EDIT_OK", 1: "EDIT_ERR_ARG", 2: "EDIT_ERR_UNSUPPORTED", 3: "EDIT_
 IMAGE_WEIGHT_FIELDS = ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2", "w_q", "b_q", "w_k", "b_k",
                        "w_v", "b_v", "dw_k", "db_k", "dw_v", "db_v", "w_o", "b_o")
 TEXT_WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o")
-LAYOUT_FIELDS = ("xc", "gn_stat", "xt", "q", "kv0", "kc", "vc", "S", "z", "y", "qkv_t", "y_img", "y_txt", "total")
+LAYOUT_FIELDS = ("xc", "gn_stat", "xt", "q", "kv0", "kc", "vc", "S", "z", "y", "qkv_t", "y_img", "y_txt", "lin_den",
+                 "total")
 
 
 class _Shape(ctypes.Structure):
@@ -76,6 +77,8 @@ def _load():
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p]
     lib.mmedit_hybrid_forward.restype = ctypes.c_int
+    lib.mmedit_hybrid_exact_forward.argtypes = lib.mmedit_hybrid_forward.argtypes
+    lib.mmedit_hybrid_exact_forward.restype = ctypes.c_int
     lib.edit_attn_forward_timed.argtypes = [P(_Shape), P(_Weights), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     lib.edit_attn_forward_timed.restype = ctypes.c_int
@@ -204,13 +207,24 @@ def edit_attn_forward_timed(shape, weights, x, y, workspace, events, stream=None
                                         _nbytes(workspace), _stream(stream), ctypes.cast(events, ctypes.c_void_p)))
 
 
-def mmedit_hybrid_forward(shape, n_text, img_weights, txt_weights, x_img, x_txt, y_img, y_txt, workspace,
-                          stream=None) -> None:
-    """MM-EDiT hybrid forward (image and text rows); see edit_attn.h."""
+def _hybrid(fn, shape, n_text, img_weights, txt_weights, x_img, x_txt, y_img, y_txt, workspace, stream):
     sh = _shape(shape)
     w = _weights(img_weights)
     tw = _text_weights(txt_weights)
-    _check(_lib.mmedit_hybrid_forward(ctypes.byref(sh), int(n_text), ctypes.byref(w),
-                                      ctypes.byref(tw) if tw is not None else None, _ptr(x_img), _ptr(x_txt),
-                                      _ptr(y_img), _ptr(y_txt), _ptr(workspace), _nbytes(workspace),
-                                      _stream(stream)))
+    _check(fn(ctypes.byref(sh), int(n_text), ctypes.byref(w), ctypes.byref(tw) if tw is not None else None,
+              _ptr(x_img), _ptr(x_txt), _ptr(y_img), _ptr(y_txt), _ptr(workspace), _nbytes(workspace),
+              _stream(stream)))
+
+
+def mmedit_hybrid_forward(shape, n_text, img_weights, txt_weights, x_img, x_txt, y_img, y_txt, workspace,
+                          stream=None) -> None:
+    """MM-EDiT hybrid forward (image and text rows), eta = token ratio; see edit_attn.h."""
+    _hybrid(_lib.mmedit_hybrid_forward, shape, n_text, img_weights, txt_weights, x_img, x_txt, y_img, y_txt,
+            workspace, stream)
+
+
+def mmedit_hybrid_exact_forward(shape, n_text, img_weights, txt_weights, x_img, x_txt, y_img, y_txt, workspace,
+                                stream=None) -> None:
+    """MM-EDiT hybrid forward with eta computed exactly per image row and head; see edit_attn.h."""
+    _hybrid(_lib.mmedit_hybrid_exact_forward, shape, n_text, img_weights, txt_weights, x_img, x_txt, y_img,
+            y_txt, workspace, stream)

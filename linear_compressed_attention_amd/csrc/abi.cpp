@@ -56,7 +56,7 @@ struct Geometry {
 
 struct Layout {
   size_t xc, gn_part, gn_stat, gn_scale, gn_shift, xt, q, kv0, kc, vc, kv_part, S, z, st, zp, y;
-  size_t qkv_t, y_img, y_txt, total;
+  size_t qkv_t, y_img, y_txt, lin_den, total;
 };
 
 edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
@@ -121,6 +121,7 @@ Layout make_layout(const Geometry& g) {
     L.qkv_t = take((size_t)g.B * g.nt * 3 * g.C * es);
     L.y_img = take(M * g.C * es);
     L.y_txt = take((size_t)g.B * g.nt * g.C * es);
+    L.lin_den = take((size_t)g.B * g.N * g.heads * 4);
   }
   L.total = off;
   return L;
@@ -201,7 +202,7 @@ struct Marks {
 // The image stream up to the linear-attention output y (steps 1-8).
 template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
-                        hipStream_t s, const Marks& mk) {
+                        hipStream_t s, const Marks& mk, float* lin_den = nullptr) {
   using namespace edit;
   auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
@@ -255,7 +256,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
   EDIT_LAUNCH(mk.mark(EDIT_STEP_APPLY));
   // 8. y = q S / (q . z + eps)
   EDIT_LAUNCH(launch_linattn_apply<T>(P(L.q), g.C, P(L.st), F(L.zp), g.B, g.N, g.heads, g.d, g.eps, P(L.y), g.C,
-                                      s));
+                                      lin_den, s));
   return EDIT_OK;
 }
 
@@ -287,11 +288,12 @@ edit_status_t run_edit(const Geometry& g, const Layout& L, const edit_weights_t*
 template <typename T>
 edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_t* w,
                          const edit_text_weights_t* wt, const void* x_img, const void* x_txt, void* y_img,
-                         void* y_txt, void* ws, hipStream_t s) {
+                         void* y_txt, void* ws, hipStream_t s, bool exact_eta) {
   using namespace edit;
   char* wsb = static_cast<char*>(ws);
   auto P = [&](size_t off) { return reinterpret_cast<T*>(wsb + off); };
-  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x_img), wsb, s, Marks{nullptr, s});
+  float* lin_den = exact_eta && g.nt > 0 ? reinterpret_cast<float*>(wsb + L.lin_den) : nullptr;
+  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x_img), wsb, s, Marks{nullptr, s}, lin_den);
   if (st != EDIT_OK) return st;
   if (g.nt == 0) return out_linear<T>(g.M, g.C, w->w_o, w->b_o, P(L.y), static_cast<T*>(y_img), s);
 
@@ -308,14 +310,15 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
 
   const T* qkv = P(L.qkv_t);
   const float eta = (float)((double)g.N / ((double)g.N + (double)g.nt));
-  // Image rows: eta * y_lin + (1 - eta) * softmax(Q_I K_T^T / sqrt(d)) V_T.
+  // Image rows: eta * y_lin + (1 - eta) * softmax(Q_I K_T^T / sqrt(d)) V_T, with eta the token ratio
+  // or, exactly, (q.z + eps) / (q.z + eps + sum_t exp(s_t)) per row and head.
   SdpaArgs<T> sa{};
   sa.q = P(L.q); sa.ldq = C; sa.Nq = g.N;
   sa.k1 = qkv + C; sa.v1 = qkv + 2 * C; sa.ldkv1 = 3 * C; sa.N1 = g.nt;
   sa.k2 = nullptr; sa.v2 = nullptr; sa.ldkv2 = 0; sa.N2 = 0;
   sa.B = g.B; sa.heads = g.heads; sa.d = g.d;
   sa.out = P(L.y_img); sa.ldo = C;
-  sa.blend_src = P(L.y); sa.ldbs = C; sa.alpha = eta; sa.beta = 1.0f - eta;
+  sa.blend_src = P(L.y); sa.ldbs = C; sa.alpha = eta; sa.beta = 1.0f - eta; sa.lin_den = lin_den;
   EDIT_LAUNCH(launch_sdpa<T>(sa, s));
   // Text rows: softmax over [K'_I ; K_T] with values [V'_I ; V_T].
   SdpaArgs<T> ta{};
@@ -324,7 +327,7 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   ta.k2 = qkv + C; ta.v2 = qkv + 2 * C; ta.ldkv2 = 3 * C; ta.N2 = g.nt;
   ta.B = g.B; ta.heads = g.heads; ta.d = g.d;
   ta.out = P(L.y_txt); ta.ldo = C;
-  ta.blend_src = nullptr; ta.ldbs = 0; ta.alpha = 0.0f; ta.beta = 1.0f;
+  ta.blend_src = nullptr; ta.ldbs = 0; ta.alpha = 0.0f; ta.beta = 1.0f; ta.lin_den = nullptr;
   EDIT_LAUNCH(launch_sdpa<T>(ta, s));
 
   st = out_linear<T>(g.M, C, w->w_o, w->b_o, P(L.y_img), static_cast<T*>(y_img), s);
@@ -356,7 +359,8 @@ edit_status_t edit_attn_workspace_layout(const edit_shape_t* shape, int n_text, 
   const Layout L = make_layout(g);
   out->xc = L.xc; out->gn_stat = L.gn_stat; out->xt = L.xt; out->q = L.q; out->kv0 = L.kv0;
   out->kc = L.kc; out->vc = L.vc; out->S = L.S; out->z = L.z; out->y = L.y;
-  out->qkv_t = L.qkv_t; out->y_img = L.y_img; out->y_txt = L.y_txt; out->total = L.total;
+  out->qkv_t = L.qkv_t; out->y_img = L.y_img; out->y_txt = L.y_txt; out->lin_den = L.lin_den;
+  out->total = L.total;
   return EDIT_OK;
 }
 
@@ -397,10 +401,10 @@ edit_status_t edit_attn_forward_timed(const edit_shape_t* shape, const edit_weig
   return forward_impl(shape, w, x, y, workspace, ws_bytes, hip_stream, events);
 }
 
-edit_status_t mmedit_hybrid_forward(const edit_shape_t* shape, int n_text, const edit_weights_t* img,
-                                    const edit_text_weights_t* txt, const void* x_img, const void* x_txt,
-                                    void* y_img, void* y_txt, void* workspace, size_t ws_bytes,
-                                    void* hip_stream) {
+static edit_status_t hybrid_impl(const edit_shape_t* shape, int n_text, const edit_weights_t* img,
+                                 const edit_text_weights_t* txt, const void* x_img, const void* x_txt,
+                                 void* y_img, void* y_txt, void* workspace, size_t ws_bytes, void* hip_stream,
+                                 bool exact_eta) {
   Geometry g;
   edit_status_t st = check_shape(shape, n_text, &g);
   if (st != EDIT_OK) return st;
@@ -430,8 +434,23 @@ edit_status_t mmedit_hybrid_forward(const edit_shape_t* shape, int n_text, const
     return fail(EDIT_ERR_ARG, "an input overlaps the workspace");
   if ((st = check_device()) != EDIT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  return g.dtype == EDIT_BF16 ? run_hybrid<bf16>(g, L, img, txt, x_img, x_txt, y_img, y_txt, workspace, s)
-                              : run_hybrid<float>(g, L, img, txt, x_img, x_txt, y_img, y_txt, workspace, s);
+  return g.dtype == EDIT_BF16
+             ? run_hybrid<bf16>(g, L, img, txt, x_img, x_txt, y_img, y_txt, workspace, s, exact_eta)
+             : run_hybrid<float>(g, L, img, txt, x_img, x_txt, y_img, y_txt, workspace, s, exact_eta);
+}
+
+edit_status_t mmedit_hybrid_forward(const edit_shape_t* shape, int n_text, const edit_weights_t* img,
+                                    const edit_text_weights_t* txt, const void* x_img, const void* x_txt,
+                                    void* y_img, void* y_txt, void* workspace, size_t ws_bytes,
+                                    void* hip_stream) {
+  return hybrid_impl(shape, n_text, img, txt, x_img, x_txt, y_img, y_txt, workspace, ws_bytes, hip_stream, false);
+}
+
+edit_status_t mmedit_hybrid_exact_forward(const edit_shape_t* shape, int n_text, const edit_weights_t* img,
+                                          const edit_text_weights_t* txt, const void* x_img, const void* x_txt,
+                                          void* y_img, void* y_txt, void* workspace, size_t ws_bytes,
+                                          void* hip_stream) {
+  return hybrid_impl(shape, n_text, img, txt, x_img, x_txt, y_img, y_txt, workspace, ws_bytes, hip_stream, true);
 }
 
 const char* edit_status_string(edit_status_t status) {

@@ -239,7 +239,8 @@ template <typename T, int DT>
 __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict__ q, int ldq,
                                                             const T* __restrict__ st, const float* __restrict__ zp,
                                                             int N, int heads, int d, float eps,
-                                                            T* __restrict__ y, int ldy) {
+                                                            T* __restrict__ y, int ldy,
+                                                            float* __restrict__ den_out) {
   constexpr int KS = (DT + 1) / 2;
   constexpr int DP = 16 * DT, DK = 32 * KS;
   constexpr int PITCH = DK + 8;                      // 16 rows of one fragment read hit distinct banks
@@ -309,6 +310,8 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
     den += __shfl_xor(den, 16, 64);
     den += __shfl_xor(den, 32, 64);
     const float inv = 1.0f / (den + eps);
+    // The normaliser q . z + eps, kept for the hybrid's exact eta.
+    if (den_out && g == 0 && tok < N) den_out[((size_t)b * N + tok) * heads + h] = den + eps;
     f32x4 acc[DT];
 #pragma unroll
     for (int tn = 0; tn < DT; ++tn) {
@@ -337,14 +340,14 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
 
 template <typename T>
 hipError_t launch_linattn_apply(const T* q, int ldq, const T* st, const float* zp, int B, int N, int heads,
-                                int d, float eps, T* y, int ldy, hipStream_t s) {
+                                int d, float eps, T* y, int ldy, float* den_out, hipStream_t s) {
   const int blocks = (N + kApplyTokens - 1) / kApplyTokens;
   dim3 grid(blocks, heads, B), block(256);
   switch ((d + 15) / 16) {
 #define EDIT_APPLY_CASE(DTV)                                                                        \
   case DTV:                                                                                         \
     hipLaunchKernelGGL((linattn_apply_kernel<T, DTV>), grid, block, 0, s, q, ldq, st, zp, N, heads, d, \
-                       eps, y, ldy);                                                                \
+                       eps, y, ldy, den_out);                                                       \
     break;
     EDIT_APPLY_CASE(1) EDIT_APPLY_CASE(2) EDIT_APPLY_CASE(3) EDIT_APPLY_CASE(4)
     EDIT_APPLY_CASE(5) EDIT_APPLY_CASE(6) EDIT_APPLY_CASE(7) EDIT_APPLY_CASE(8)
@@ -488,6 +491,15 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   if (qv) {
     T* orow = p.out + ((size_t)b * p.Nq + qi) * p.ldo + h * d;
     const T* brow = p.blend_src ? p.blend_src + ((size_t)b * p.Nq + qi) * p.ldbs + h * d : nullptr;
+    float alpha = p.alpha, beta = p.beta;
+    if (brow && p.lin_den) {
+      // Exact eta: the linear block's mass q . z + eps against the softmax
+      // block's sum_t exp(s_t) = 2^mrun * lrun (scores are kept in log2 units).
+      const float lin = p.lin_den[((size_t)b * p.Nq + qi) * p.heads + h];
+      const float soft = exp2f(mrun) * lrun;
+      alpha = lin / (lin + soft);
+      beta = 1.0f - alpha;
+    }
 #pragma unroll
     for (int tn = 0; tn < DT; ++tn) {
       const int n = tn * 16 + g * 4;
@@ -497,7 +509,7 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
         for (int r = 0; r < 4; ++r) o[r] = acc[tn][r] * inv;
         if (brow) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = p.alpha * to_f32(brow[n + r]) + p.beta * o[r];
+          for (int r = 0; r < 4; ++r) o[r] = alpha * to_f32(brow[n + r]) + beta * o[r];
         }
         store4(orow + n, o);
       }
@@ -524,7 +536,7 @@ hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s) {
   template hipError_t launch_kv_state<T>(const T*, const T*, int, int, int, int, float*, int, float*,   \
                                          float*, T*, float*, hipStream_t);                              \
   template hipError_t launch_linattn_apply<T>(const T*, int, const T*, const float*, int, int, int, int, \
-                                              float, T*, int, hipStream_t);                             \
+                                              float, T*, int, float*, hipStream_t);                     \
   template hipError_t launch_sdpa<T>(const SdpaArgs<T>&, hipStream_t);
 EDIT_INST(bf16)
 EDIT_INST(float)

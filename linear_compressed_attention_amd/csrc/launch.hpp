@@ -75,10 +75,11 @@ int kv_state_chunks(int Nc);
 int kv_state_dp(int d);   // padded rows of the state operand
 int kv_state_dk(int d);   // padded K of the state operand
 
-// y[b][n][h*d + j] = (q S)_j / (q . z + eps) per head.
+// y[b][n][h*d + j] = (q S)_j / (q . z + eps) per head. If den_out is given it
+// receives q . z + eps as [B][N][heads] floats.
 template <typename T>
 hipError_t launch_linattn_apply(const T* q, int ldq, const T* st, const float* zp, int B, int N,
-                                int heads, int d, float eps, T* y, int ldy, hipStream_t s);
+                                int heads, int d, float eps, T* y, int ldy, float* den_out, hipStream_t s);
 
 // Softmax attention of queries q over up to two key/value segments, per head,
 // scale 1/sqrt(d). If blend_src is given: out = alpha * blend_src + beta * attn.
@@ -90,6 +91,9 @@ struct SdpaArgs {
   int B, heads, d;
   T* out; int ldo;
   const T* blend_src; int ldbs; float alpha, beta;
+  // If set (with blend_src): alpha = L / (L + sum_t exp(s_t)) per query and
+  // head, L = lin_den[b][query][head], beta = 1 - alpha.
+  const float* lin_den;
 };
 template <typename T>
 hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s);

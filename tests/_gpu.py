@@ -68,7 +68,7 @@ def run_edit(shape, inp, stream=None, with_intermediates=True):
     return res
 
 
-def run_hybrid(shape, inp, n_text, with_intermediates=True):
+def run_hybrid(shape, inp, n_text, with_intermediates=True, exact=False):
     x = to_dev(inp["x"], shape.dtype)
     w = dev_weights(inp["w"], shape.dtype)
     xt = to_dev(inp["x_txt"], shape.dtype) if n_text else None
@@ -80,13 +80,18 @@ def run_hybrid(shape, inp, n_text, with_intermediates=True):
     poison(ws)
     if yt is not None:
         poison(yt)
-    lca.mmedit_hybrid_forward(shape, n_text, w, wt, x, xt, y, yt, ws)
+    fwd = lca.mmedit_hybrid_exact_forward if exact else lca.mmedit_hybrid_forward
+    fwd(shape, n_text, w, wt, x, xt, y, yt, ws)
     torch.cuda.synchronize()
     res = {"out": y.float().cpu().numpy()}
     if yt is not None:
         res["out_txt"] = yt.float().cpu().numpy()
     if with_intermediates:
         res.update(read_intermediates(shape, ws, n_text))
+        if exact and n_text:
+            lay = lca.edit_attn_workspace_layout(shape, n_text)
+            res["lin_den"] = _view(ws, lay["lin_den"], (shape.B, shape.N, shape.heads),
+                                   torch.float32).cpu().numpy()
     return res
 
 

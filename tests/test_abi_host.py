@@ -13,7 +13,7 @@ from seeded_inputs import CONFIGS, make_shape
 
 def test_exports_every_header_symbol():
     names = lca.header_symbols()
-    assert {"edit_attn_forward", "mmedit_hybrid_forward", "edit_attn_workspace_size",
+    assert {"edit_attn_forward", "mmedit_hybrid_forward", "mmedit_hybrid_exact_forward", "edit_attn_workspace_size",
             "mmedit_hybrid_workspace_size", "edit_attn_workspace_layout", "edit_status_string",
             "edit_last_error"} <= set(names)
     lib = ctypes.CDLL(lca.lib_path())
@@ -123,15 +123,27 @@ def test_argument_errors_before_any_launch():
     assert e.value.status == 1 and "overlap" in e.value.detail
 
 
-def test_hybrid_argument_errors():
+@pytest.mark.parametrize("fwd", ["mmedit_hybrid_forward", "mmedit_hybrid_exact_forward"])
+def test_hybrid_argument_errors(fwd):
+    f = getattr(lca, fwd)
     ws = _FakeWS(0xB000000, lca.mmedit_hybrid_workspace_size(SHAPE, 5))
     with pytest.raises(lca.EditError) as e:
-        lca.mmedit_hybrid_forward(SHAPE, -1, _fake_weights(), None, 0x9000000, None, 0xA000000, None, ws, stream=0)
+        f(SHAPE, -1, _fake_weights(), None, 0x9000000, None, 0xA000000, None, ws, stream=0)
     assert e.value.status == 1
     with pytest.raises(lca.EditError) as e:
-        lca.mmedit_hybrid_forward(SHAPE, 5, _fake_weights(), None, 0x9000000, 0x9800000, 0xA000000, 0xA800000, ws,
-                                  stream=0)
+        f(SHAPE, 5, _fake_weights(), None, 0x9000000, 0x9800000, 0xA000000, 0xA800000, ws, stream=0)
     assert e.value.status == 1 and "text weights" in e.value.detail
+    small = _FakeWS(0xB000000, lca.mmedit_hybrid_workspace_size(SHAPE, 5) - 256)
+    with pytest.raises(lca.EditError) as e:
+        f(SHAPE, 5, _fake_weights(), {n: 0x200000 + 0x1000 * i for i, n in enumerate(lca.TEXT_WEIGHT_FIELDS)},
+          0x9000000, 0x9800000, 0xA000000, 0xA800000, small, stream=0)
+    assert e.value.status == 3
+
+
+def test_exact_eta_layout_has_the_normaliser():
+    lay = lca.edit_attn_workspace_layout(SHAPE, 5)
+    assert lay["lin_den"] > 0 and lay["lin_den"] % 256 == 0
+    assert lca.edit_attn_workspace_layout(SHAPE, 0)["lin_den"] == 0
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")

@@ -91,12 +91,13 @@ def test_pixart_full_size(name):
     check_edit(CONFIGS[name])
 
 
-def check_hybrid(s, n_text, seed=0):
+def check_hybrid(s, n_text, seed=0, exact=False):
     inp = make_inputs(s, seed=seed, n_text=n_text)
-    _announce(f"hybrid {s} n_text={n_text} seed={seed}")
-    got = G.run_hybrid(s, inp, n_text)
+    _announce(f"hybrid {s} n_text={n_text} seed={seed} exact_eta={exact}")
+    got = G.run_hybrid(s, inp, n_text, exact=exact)
     tr = {}
-    out_i, out_t = O.mmedit_hybrid_forward(inp["x"], inp.get("x_txt"), inp["w"], inp.get("w_txt"), s, tr)
+    out_i, out_t = O.mmedit_hybrid_forward(inp["x"], inp.get("x_txt"), inp["w"], inp.get("w_txt"), s, tr,
+                                           eta="exact" if exact else "ratio")
     tol = _tol(s)
     pairs = {"out": (got["out"], out_i), "q": (got["q"], tr["q"]), "kc": (got["kc"], tr["kc"]),
              "vc": (got["vc"], tr["vc"]), "y_lin": (got["y"], tr["y_lin"])}
@@ -104,6 +105,8 @@ def check_hybrid(s, n_text, seed=0):
         pairs.update({"out_txt": (got["out_txt"], out_t), "y_img": (got["y_img"], tr["y"]),
                       "y_txt": (got["y_txt"], tr["y_txt"]),
                       "qkv_t": (got["qkv_t"], np.concatenate([tr["q_t"], tr["k_t"], tr["v_t"]], -1))})
+        if exact:
+            pairs["lin_den"] = (got["lin_den"], tr["lin_den"])
     errs = {}
     for k, (g, r) in pairs.items():
         assert np.isfinite(g).all(), f"{k}: non-finite elements"
@@ -132,6 +135,26 @@ def test_hybrid_small(name, n_text):
 def test_hybrid_sd35m_full_size():
     s = CONFIGS["sd35m_hybrid"]
     check_hybrid(s, s.n_text)
+
+
+@pytest.mark.parametrize("name,n_text", [("f32_small", 37), ("bf16_small", 77), ("bf16_d72", 5)])
+def test_hybrid_exact_eta_small(name, n_text):
+    check_hybrid(HYB[name], n_text, seed=6, exact=True)
+
+
+def test_hybrid_exact_eta_sd35m_full_size():
+    s = CONFIGS["sd35m_hybrid"]
+    check_hybrid(s, s.n_text, exact=True)
+
+
+@pytest.mark.parametrize("name", ["f32_small", "bf16_small"])
+def test_hybrid_exact_eta_without_text_equals_edit(name):
+    s = HYB[name]
+    inp = make_inputs(s, seed=3)
+    _announce(f"exact-eta hybrid n_text=0 vs edit {name}")
+    a = G.run_hybrid(s, inp, 0, with_intermediates=False, exact=True)["out"]
+    b = G.run_edit(s, inp, with_intermediates=False)["out"]
+    np.testing.assert_array_equal(a, b)
 
 
 @pytest.mark.parametrize("name", ["f32_small", "bf16_small"])
