@@ -9,12 +9,14 @@ Source: the page "EDiT: Efficient Diffusion Transformers with Linear
 Compressed Attention" (ICCV 2025 paper notes, arXiv 2503.16726), cited below
 by its sections: "ConvFusion" (the Q^EDiT equation), "Spatial Compressor"
 (the K^EDiT / V^EDiT equations and the depthwise stride-2 remark),
-"Linear-attention formula" (the y_i equation) and "MM-EDiT" (the A^Hybrid
-matrix and the eta approximation under it).
+"Linear-attention formula" (the y_i equation), "MM-EDiT" (the A^Hybrid
+matrix and the eta approximation under it) and "Ablation: Query/Key/Value
+processing" (the table of Q/K/V variants).
 
 Every step is written from its definition, in the order the page composes
 them, with numpy's matmul as the only library primitive. Where the page
-leaves a detail open, the reading taken is named at the function (R1..R16, R23);
+leaves a detail open, the reading taken is named at the function (R1..R16,
+R23..R26);
 the same readings are listed in the design notes of the repository.
 
 Pins (what checks this code against something other than itself) live in
@@ -258,6 +260,61 @@ def edit_attn_forward(x, w, shape, trace=None):
     out = linear(y, w["w_o"], w["b_o"])
     if trace is not None:
         trace.update(S=S, z=z, y=y, out=out)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Ablation variants of the query / key / value processing
+# ----------------------------------------------------------------------------
+
+QUERY_MODES = ("convfusion", "linear")
+KV_MODES = ("compressed", "full", "key_convfusion")
+
+
+def edit_attn_variant_forward(x, w, shape, query="convfusion", kv="compressed", w_kcf=None, trace=None):
+    """The EDiT layer with the query and key/value processing of the notes'
+    ablation table (section "Ablation: Query/Key/Value processing", whose rows
+    are (Q, K, V) = (CF, SC, SC), (CF, CF, -), (-, SC, SC) and (CF, -, -)).
+
+    query="convfusion": Q = ReLU(Linear_Q(X + ConvFusion(X)))  (the layer's Q)
+    query="linear":     Q = ReLU(Linear_Q(X))                   (R24)
+    kv="compressed":    K' = ReLU(DW(Linear_K X)), V' = DW(Linear_V X)  (SC, SC)
+    kv="full":          K = ReLU(Linear_K X), V = Linear_V X over all N tokens  (-, -; R25)
+    kv="key_convfusion": K = ReLU(Linear_K(X + ConvFusion_K(X))) with the key
+                        branch's own ConvFusion parameters ``w_kcf`` (w_cf1,
+                        b_cf1, gn_gamma, gn_beta, w_cf2, b_cf2), V = Linear_V X
+                        (CF, -; R26)
+    The linear attention, its eps and the output projection are the layer's.
+    ``trace`` receives q, k, v (the keys and values the sums run over), S, z,
+    y, out, and for the key branch xc_k / xt_k."""
+    if query not in QUERY_MODES or kv not in KV_MODES:
+        raise ValueError(f"unknown variant ({query!r}, {kv!r})")
+    H, W, heads, G = shape.H, shape.W, shape.heads, shape.gn_groups
+    x = _f64(x)
+    if query == "convfusion":
+        q = convfusion_query(x, H, W, w, G, trace)
+    else:
+        q = relu(linear(x, w["w_q"], w["b_q"]))
+    if kv == "compressed":
+        k, v = spatial_compressor_kv(x, H, W, w, trace)
+    elif kv == "full":
+        k = relu(linear(x, w["w_k"], w["b_k"]))
+        v = linear(x, w["w_v"], w["b_v"])
+    else:
+        if w_kcf is None:
+            raise ValueError("kv='key_convfusion' needs the key ConvFusion parameters")
+        wk = dict(w_kcf)
+        wk["w_q"], wk["b_q"] = w["w_k"], w["b_k"]
+        tk = {} if trace is not None else None
+        k = convfusion_query(x, H, W, wk, G, tk)
+        v = linear(x, w["w_v"], w["b_v"])
+        if trace is not None:
+            trace.update(xc_k=tk["xc"], xt_k=tk["xt"])
+    S, z = kv_state(k, v, heads)
+    y = linear_attention_apply(q, S, z, heads, shape.eps)
+    out = linear(y, w["w_o"], w["b_o"])
+    if trace is not None:
+        trace.update(q=q, k=k, v=v, S=S, z=z, y=y, out=out)
     return out
 
 

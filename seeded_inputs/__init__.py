@@ -24,7 +24,8 @@ Values of a bf16 workload are rounded to bf16 (round to nearest even) once,
 here, and returned as float32 arrays that hold bf16-exact values.
 
 Draw order is fixed: x, then the image weights in the order of
-``IMAGE_WEIGHT_NAMES``, then (hybrid only) x_txt and ``TEXT_WEIGHT_NAMES``.
+``IMAGE_WEIGHT_NAMES``, then (hybrid only) x_txt and ``TEXT_WEIGHT_NAMES``,
+then (key-ConvFusion ablation only) ``KEY_CONVFUSION_NAMES``.
 """
 from __future__ import annotations
 
@@ -34,7 +35,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = [
-    "LayerShape", "CONFIGS", "IMAGE_WEIGHT_NAMES", "TEXT_WEIGHT_NAMES",
+    "LayerShape", "CONFIGS", "IMAGE_WEIGHT_NAMES", "TEXT_WEIGHT_NAMES", "KEY_CONVFUSION_NAMES",
     "image_weight_shapes", "text_weight_shapes", "round_to_bf16",
     "make_inputs", "make_shape",
 ]
@@ -147,13 +148,21 @@ def _draw(rng: np.random.Generator, shape, std: float, mean: float = 0.0) -> np.
     return (rng.standard_normal(shape, dtype=np.float64) * std + mean).astype(np.float32)
 
 
+KEY_CONVFUSION_NAMES = ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2")
+
+
 def make_inputs(s: LayerShape, seed: int = 0, gn_affine_random: bool = False,
-                x_std: Optional[float] = None, n_text: Optional[int] = None) -> dict:
+                x_std: Optional[float] = None, n_text: Optional[int] = None,
+                key_convfusion: bool = False) -> dict:
     """Draw one workload's inputs.
 
     Returns ``{"x": [B, N, C], "w": {...}}`` and, when the layer has text
-    tokens, ``"x_txt": [B, N_T, C]`` and ``"w_txt": {...}``. All arrays are
-    float32 (bf16-exact for a bf16 workload) and C-contiguous.
+    tokens, ``"x_txt": [B, N_T, C]`` and ``"w_txt": {...}``. With
+    ``key_convfusion`` also ``"w_kcf"``: a second set of ConvFusion
+    parameters (``KEY_CONVFUSION_NAMES``, shapes as the image weights of the
+    same names) for the ablation variant that passes the keys through
+    ConvFusion, drawn last. All arrays are float32 (bf16-exact for a bf16
+    workload) and C-contiguous.
     """
     rng = np.random.default_rng(seed)
     xs = s.x_std if x_std is None else x_std
@@ -175,4 +184,16 @@ def make_inputs(s: LayerShape, seed: int = 0, gn_affine_random: bool = False,
         out["x_txt"] = rnd(_draw(rng, (s.B, nt, s.C), 1.0))
         out["w_txt"] = {name: rnd(_draw(rng, shp, s.w_std))
                         for name, shp in text_weight_shapes(s).items()}
+    if key_convfusion:
+        shapes = image_weight_shapes(s)
+        wk = {}
+        for name in KEY_CONVFUSION_NAMES:
+            if name == "gn_gamma":
+                wk[name] = _draw(rng, shapes[name], 0.1, 1.0) if gn_affine_random else np.ones(shapes[name], np.float32)
+            elif name == "gn_beta":
+                wk[name] = _draw(rng, shapes[name], 0.1) if gn_affine_random else np.zeros(shapes[name], np.float32)
+            else:
+                wk[name] = _draw(rng, shapes[name], s.w_std)
+            wk[name] = rnd(wk[name])
+        out["w_kcf"] = wk
     return out
