@@ -159,14 +159,59 @@ edit_status_t mmedit_hybrid_exact_forward(const edit_shape_t* shape, int n_text,
  *   qkv_t   [B][N_T][3C] T     text Q | K | V (hybrid only)
  *   y_img   [B][N][C]   T      blended image rows (hybrid with text only)
  *   y_txt   [B][N_T][C] T      text rows before the text output Linear (hybrid only)
- *   lin_den [B][N][h]   f32    q . z + eps per token and head (exact-eta hybrid only) */
+ *   lin_den [B][N][h]   f32    q . z + eps per token and head (exact-eta hybrid only)
+ *   xc_k, gn_stat_k, xt_k      the key branch's ConvFusion (EDIT_KV_KEY_CONVFUSION only)
+ * For the ablation variants (edit_attn_variant_forward): q holds the variant's
+ * queries; with uncompressed keys kv0 holds ReLU(key Linear) | value Linear
+ * and the sums S, z run over all N tokens; kc, vc (and xc, gn_stat, xt with
+ * a plain query) are not produced. */
 typedef struct {
   size_t xc, gn_stat, xt, q, kv0, kc, vc, S, z, y, qkv_t, y_img, y_txt, lin_den;
+  size_t xc_k, gn_stat_k, xt_k;
   size_t total;
 } edit_ws_layout_t;
 
 edit_status_t edit_attn_workspace_layout(const edit_shape_t* shape, int n_text,
                                          edit_ws_layout_t* layout);
+
+/* Ablation variants of the query and key/value processing ("EDiT" notes,
+ * section "Ablation: Query/Key/Value processing": the table of rows
+ * (Q, K, V) = (CF, SC, SC), (CF, CF, -), (-, SC, SC), (CF, -, -)):
+ *   query EDIT_QUERY_CONVFUSION  Q = ReLU(Linear_Q(X + ConvFusion(X)))   (CF)
+ *         EDIT_QUERY_LINEAR      Q = ReLU(Linear_Q(X))                   (-)
+ *   kv    EDIT_KV_COMPRESSED     K' = ReLU(DW(Linear_K X)), V' = DW(Linear_V X)   (SC, SC)
+ *         EDIT_KV_FULL           K = ReLU(Linear_K X), V = Linear_V X over all N  (-, -)
+ *         EDIT_KV_KEY_CONVFUSION K = ReLU(Linear_K(X + ConvFusion_K(X))) with the
+ *                                key branch's own ConvFusion parameters, V = Linear_V X  (CF, -)
+ * The table's rows are {CONVFUSION, COMPRESSED} (the layer itself),
+ * {CONVFUSION, KEY_CONVFUSION}, {LINEAR, COMPRESSED} and {CONVFUSION, FULL}. */
+typedef enum { EDIT_QUERY_CONVFUSION = 0, EDIT_QUERY_LINEAR = 1 } edit_query_mode_t;
+typedef enum { EDIT_KV_COMPRESSED = 0, EDIT_KV_FULL = 1, EDIT_KV_KEY_CONVFUSION = 2 } edit_kv_mode_t;
+typedef struct {
+  edit_query_mode_t query;
+  edit_kv_mode_t kv;
+} edit_variant_t;
+
+/* The key branch's ConvFusion parameters (shapes as the image stream's
+ * w_cf1, b_cf1, gn_gamma, gn_beta, w_cf2, b_cf2). */
+typedef struct {
+  const void *w_cf1, *b_cf1, *gn_gamma, *gn_beta, *w_cf2, *b_cf2;
+} edit_convfusion_weights_t;
+
+/* Workspace bytes and layout of a variant; 0 / an error for an invalid one. */
+size_t edit_attn_variant_workspace_size(const edit_shape_t* shape, const edit_variant_t* variant);
+edit_status_t edit_attn_variant_workspace_layout(const edit_shape_t* shape, const edit_variant_t* variant,
+                                                 edit_ws_layout_t* layout);
+
+/* EDiT layer forward in an ablation variant. Arguments as edit_attn_forward;
+ * weights the variant does not read may be NULL (the ConvFusion set with a
+ * plain query, the depthwise set with uncompressed keys); key_cf is read (and
+ * must be valid) only for EDIT_KV_KEY_CONVFUSION. {CONVFUSION, COMPRESSED}
+ * gives edit_attn_forward's y bit for bit. */
+edit_status_t edit_attn_variant_forward(const edit_shape_t* shape, const edit_variant_t* variant,
+                                        const edit_weights_t* w, const edit_convfusion_weights_t* key_cf,
+                                        const void* x, void* y,
+                                        void* workspace, size_t ws_bytes, void* hip_stream);
 
 /* Steps of one EDiT forward, in launch order (per-step timing). */
 typedef enum {

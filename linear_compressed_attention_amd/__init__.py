@@ -17,7 +17,8 @@ __all__ = [
     "EDIT_F32", "EDIT_BF16", "EditError", "IMAGE_WEIGHT_FIELDS", "TEXT_WEIGHT_FIELDS", "LAYOUT_FIELDS",
     "edit_attn_workspace_size", "edit_attn_forward", "mmedit_hybrid_workspace_size",
     "mmedit_hybrid_forward", "mmedit_hybrid_exact_forward", "edit_attn_forward_timed", "edit_attn_workspace_layout", "EDIT_NUM_STEPS", "edit_status_string", "edit_last_error",
-    "lib_path", "header_symbols",
+    "lib_path", "header_symbols", "QUERY_MODES", "KV_MODES", "KEY_CONVFUSION_FIELDS",
+    "edit_attn_variant_workspace_size", "edit_attn_variant_workspace_layout", "edit_attn_variant_forward",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +34,10 @@ IMAGE_WEIGHT_FIELDS = ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2"
                        "w_v", "b_v", "dw_k", "db_k", "dw_v", "db_v", "w_o", "b_o")
 TEXT_WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o")
 LAYOUT_FIELDS = ("xc", "gn_stat", "xt", "q", "kv0", "kc", "vc", "S", "z", "y", "qkv_t", "y_img", "y_txt", "lin_den",
-                 "total")
+                 "xc_k", "gn_stat_k", "xt_k", "total")
+QUERY_MODES = {"convfusion": 0, "linear": 1}                      # edit_query_mode_t
+KV_MODES = {"compressed": 0, "full": 1, "key_convfusion": 2}      # edit_kv_mode_t
+KEY_CONVFUSION_FIELDS = ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2")
 
 
 class _Shape(ctypes.Structure):
@@ -51,6 +55,14 @@ class _TextWeights(ctypes.Structure):
 
 class _Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in LAYOUT_FIELDS]
+
+
+class _Variant(ctypes.Structure):
+    _fields_ = [("query", ctypes.c_int), ("kv", ctypes.c_int)]
+
+
+class _ConvFusionWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in KEY_CONVFUSION_FIELDS]
 
 
 class EditError(RuntimeError):
@@ -79,6 +91,14 @@ def _load():
     lib.mmedit_hybrid_forward.restype = ctypes.c_int
     lib.mmedit_hybrid_exact_forward.argtypes = lib.mmedit_hybrid_forward.argtypes
     lib.mmedit_hybrid_exact_forward.restype = ctypes.c_int
+    lib.edit_attn_variant_workspace_size.argtypes = [P(_Shape), P(_Variant)]
+    lib.edit_attn_variant_workspace_size.restype = ctypes.c_size_t
+    lib.edit_attn_variant_workspace_layout.argtypes = [P(_Shape), P(_Variant), P(_Layout)]
+    lib.edit_attn_variant_workspace_layout.restype = ctypes.c_int
+    lib.edit_attn_variant_forward.argtypes = [P(_Shape), P(_Variant), P(_Weights), P(_ConvFusionWeights),
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                              ctypes.c_void_p]
+    lib.edit_attn_variant_forward.restype = ctypes.c_int
     lib.edit_attn_forward_timed.argtypes = [P(_Shape), P(_Weights), ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     lib.edit_attn_forward_timed.restype = ctypes.c_int
@@ -228,3 +248,45 @@ def mmedit_hybrid_exact_forward(shape, n_text, img_weights, txt_weights, x_img, 
     """MM-EDiT hybrid forward with eta computed exactly per image row and head; see edit_attn.h."""
     _hybrid(_lib.mmedit_hybrid_exact_forward, shape, n_text, img_weights, txt_weights, x_img, x_txt, y_img,
             y_txt, workspace, stream)
+
+
+def _variant(query, kv) -> _Variant:
+    q = QUERY_MODES[query] if isinstance(query, str) else int(query)
+    k = KV_MODES[kv] if isinstance(kv, str) else int(kv)
+    return _Variant(q, k)
+
+
+def _opt(w, n):
+    """A weight the variant may not read: absent keys pass NULL."""
+    if isinstance(w, Mapping):
+        return _ptr(w.get(n))
+    return _ptr(getattr(w, n, None))
+
+
+def edit_attn_variant_workspace_size(shape, query, kv) -> int:
+    """Workspace bytes of edit_attn_variant_forward; raises EditError on a bad shape or variant."""
+    sh, v = _shape(shape), _variant(query, kv)
+    n = _lib.edit_attn_variant_workspace_size(ctypes.byref(sh), ctypes.byref(v))
+    if n == 0:
+        _check(_lib.edit_attn_variant_workspace_layout(ctypes.byref(sh), ctypes.byref(v), ctypes.byref(_Layout())))
+    return n
+
+
+def edit_attn_variant_workspace_layout(shape, query, kv) -> dict:
+    lay = _Layout()
+    _check(_lib.edit_attn_variant_workspace_layout(ctypes.byref(_shape(shape)), ctypes.byref(_variant(query, kv)),
+                                                   ctypes.byref(lay)))
+    return {n: getattr(lay, n) for n in LAYOUT_FIELDS}
+
+
+def edit_attn_variant_forward(shape, query, kv, weights, key_cf, x, y, workspace, stream=None) -> None:
+    """EDiT layer forward in an ablation variant (query "convfusion" | "linear",
+    kv "compressed" | "full" | "key_convfusion"); see edit_attn.h. Weights the
+    variant does not read may be absent; ``key_cf`` maps KEY_CONVFUSION_FIELDS
+    to tensors (key_convfusion only, else None)."""
+    sh, v = _shape(shape), _variant(query, kv)
+    w = _Weights(*(_opt(weights, n) for n in IMAGE_WEIGHT_FIELDS))
+    kcf = None if key_cf is None else _ConvFusionWeights(*(_opt(key_cf, n) for n in KEY_CONVFUSION_FIELDS))
+    _check(_lib.edit_attn_variant_forward(ctypes.byref(sh), ctypes.byref(v), ctypes.byref(w),
+                                          ctypes.byref(kcf) if kcf is not None else None, _ptr(x), _ptr(y),
+                                          _ptr(workspace), _nbytes(workspace), _stream(stream)))

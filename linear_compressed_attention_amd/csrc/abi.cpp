@@ -48,6 +48,8 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Geometry {
   int B, H, W, C, heads, d, r, G, Cr, N, M, Hc, Wc, Nc, nt;
+  int qmode, kvmode;   // edit_query_mode_t, edit_kv_mode_t (the layer itself: 0, 0)
+  int Nkv;             // tokens the per-head sums run over (Nc, or N for uncompressed keys)
   int gn_chunks, kv_chunks, DT, DR, DP, DK;
   size_t es;
   float eps;
@@ -56,7 +58,9 @@ struct Geometry {
 
 struct Layout {
   size_t xc, gn_part, gn_stat, gn_scale, gn_shift, xt, q, kv0, kc, vc, kv_part, S, z, st, zp, y;
-  size_t qkv_t, y_img, y_txt, lin_den, total;
+  size_t qkv_t, y_img, y_txt, lin_den;
+  size_t xc_k, gn_part_k, gn_stat_k, gn_scale_k, gn_shift_k, xt_k;   // key ConvFusion branch
+  size_t total;
 };
 
 edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
@@ -86,8 +90,9 @@ edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
   g->B = s->B; g->H = s->H; g->W = s->W; g->C = s->C; g->heads = s->heads; g->d = s->head_dim;
   g->r = s->reduction; g->G = s->gn_groups; g->Cr = Cr; g->N = (int)N; g->M = (int)M;
   g->Hc = (s->H + 1) / 2; g->Wc = (s->W + 1) / 2; g->Nc = g->Hc * g->Wc; g->nt = n_text;
+  g->qmode = EDIT_QUERY_CONVFUSION; g->kvmode = EDIT_KV_COMPRESSED; g->Nkv = g->Nc;
   g->gn_chunks = edit::groupnorm_chunks(g->N, Cr);
-  g->kv_chunks = edit::kv_state_chunks(g->Nc);
+  g->kv_chunks = edit::kv_state_chunks(g->Nkv);
   g->DT = (g->d + 15) / 16; g->DR = (g->d + 16) / 16;
   g->DP = edit::kv_state_dp(g->d); g->DK = edit::kv_state_dk(g->d);
   g->es = s->dtype == EDIT_BF16 ? 2 : 4;
@@ -96,21 +101,47 @@ edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
   return EDIT_OK;
 }
 
+// The query / key-value processing of the ablation variants.
+edit_status_t apply_variant(const edit_variant_t* v, Geometry* g) {
+  if (!v) return fail(EDIT_ERR_ARG, "variant is NULL");
+  if (v->query != EDIT_QUERY_CONVFUSION && v->query != EDIT_QUERY_LINEAR)
+    return fail(EDIT_ERR_ARG, "unknown query mode %d", (int)v->query);
+  if (v->kv != EDIT_KV_COMPRESSED && v->kv != EDIT_KV_FULL && v->kv != EDIT_KV_KEY_CONVFUSION)
+    return fail(EDIT_ERR_ARG, "unknown key/value mode %d", (int)v->kv);
+  g->qmode = v->query;
+  g->kvmode = v->kv;
+  g->Nkv = v->kv == EDIT_KV_COMPRESSED ? g->Nc : g->N;
+  g->kv_chunks = edit::kv_state_chunks(g->Nkv);
+  return EDIT_OK;
+}
+
 Layout make_layout(const Geometry& g) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   const size_t M = g.M, es = g.es, BH = (size_t)g.B * g.heads;
-  L.xc = take(M * g.Cr * es);
-  L.gn_part = take((size_t)g.B * g.gn_chunks * g.G * 2 * 4);
-  L.gn_stat = take((size_t)g.B * g.G * 2 * 4);
-  L.gn_scale = take((size_t)g.B * g.Cr * 4);
-  L.gn_shift = take((size_t)g.B * g.Cr * 4);
-  L.xt = take(M * g.C * es);
+  if (g.qmode == EDIT_QUERY_CONVFUSION) {
+    L.xc = take(M * g.Cr * es);
+    L.gn_part = take((size_t)g.B * g.gn_chunks * g.G * 2 * 4);
+    L.gn_stat = take((size_t)g.B * g.G * 2 * 4);
+    L.gn_scale = take((size_t)g.B * g.Cr * 4);
+    L.gn_shift = take((size_t)g.B * g.Cr * 4);
+    L.xt = take(M * g.C * es);
+  }
   L.q = take(M * g.C * es);
   L.kv0 = take(M * 2 * g.C * es);
-  L.kc = take((size_t)g.B * g.Nc * g.C * es);
-  L.vc = take((size_t)g.B * g.Nc * g.C * es);
+  if (g.kvmode == EDIT_KV_COMPRESSED) {
+    L.kc = take((size_t)g.B * g.Nc * g.C * es);
+    L.vc = take((size_t)g.B * g.Nc * g.C * es);
+  }
+  if (g.kvmode == EDIT_KV_KEY_CONVFUSION) {
+    L.xc_k = take(M * g.Cr * es);
+    L.gn_part_k = take((size_t)g.B * g.gn_chunks * g.G * 2 * 4);
+    L.gn_stat_k = take((size_t)g.B * g.G * 2 * 4);
+    L.gn_scale_k = take((size_t)g.B * g.Cr * 4);
+    L.gn_shift_k = take((size_t)g.B * g.Cr * 4);
+    L.xt_k = take(M * g.C * es);
+  }
   L.kv_part = take(BH * g.kv_chunks * (16 * g.DR) * (16 * g.DT) * 4);
   L.S = take(BH * g.d * g.d * 4);
   L.z = take(BH * g.d * 4);
@@ -141,13 +172,28 @@ edit_status_t check_ptr(const void* p, const char* name) {
   return EDIT_OK;
 }
 
-edit_status_t check_weights(const edit_weights_t* w) {
+// The parameters a geometry's variant reads: the ConvFusion set only with a
+// ConvFusion query, the depthwise set only with compressed keys and values.
+edit_status_t check_weights(const edit_weights_t* w, const Geometry& g) {
   if (!w) return fail(EDIT_ERR_ARG, "weights struct is NULL");
-  const void* p[] = {w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, w->w_q, w->b_q, w->w_k,
-                     w->b_k, w->w_v, w->b_v, w->dw_k, w->db_k, w->dw_v, w->db_v, w->w_o, w->b_o};
-  const char* n[] = {"w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2", "w_q", "b_q", "w_k",
-                     "b_k", "w_v", "b_v", "dw_k", "db_k", "dw_v", "db_v", "w_o", "b_o"};
+  const void* p[] = {w->w_q, w->b_q, w->w_k, w->b_k, w->w_v, w->b_v, w->w_o, w->b_o, w->w_cf1, w->b_cf1,
+                     w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, w->dw_k, w->db_k, w->dw_v, w->db_v};
+  const char* n[] = {"w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o", "w_cf1", "b_cf1",
+                     "gn_gamma", "gn_beta", "w_cf2", "b_cf2", "dw_k", "db_k", "dw_v", "db_v"};
   for (int i = 0; i < 18; ++i) {
+    if (i >= 8 && i < 14 && g.qmode != EDIT_QUERY_CONVFUSION) continue;
+    if (i >= 14 && g.kvmode != EDIT_KV_COMPRESSED) continue;
+    edit_status_t st = check_ptr(p[i], n[i]);
+    if (st != EDIT_OK) return st;
+  }
+  return EDIT_OK;
+}
+
+edit_status_t check_convfusion_weights(const edit_convfusion_weights_t* w) {
+  if (!w) return fail(EDIT_ERR_ARG, "key ConvFusion weights struct is NULL");
+  const void* p[] = {w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2};
+  const char* n[] = {"key.w_cf1", "key.b_cf1", "key.gn_gamma", "key.gn_beta", "key.w_cf2", "key.b_cf2"};
+  for (int i = 0; i < 6; ++i) {
     edit_status_t st = check_ptr(p[i], n[i]);
     if (st != EDIT_OK) return st;
   }
@@ -199,59 +245,107 @@ struct Marks {
   }
 };
 
-// The image stream up to the linear-attention output y (steps 1-8).
+// ConvFusion of x up to the restored stream: xt = x + Conv1x1(LeakyReLU(GN(Conv3x3(x)))).
+template <typename T>
+edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const void* b_cf1, const void* gamma,
+                         const void* beta, const void* w_cf2, const void* b_cf2, T* xc, float* gn_part,
+                         float* gn_stat, float* gn_scale, float* gn_shift, T* xt, hipStream_t s, const Marks& mk) {
+  using namespace edit;
+  GemmArgs<T> a{};
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_CONV3X3));
+  // xc = Conv3x3(x) + b_cf1
+  a.M = g.M; a.N = g.Cr; a.K = 9 * g.C; a.A = x; a.lda = g.C; a.H = g.H; a.W = g.W; a.Cin = g.C;
+  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w_cf1);
+  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(b_cf1);
+  a.seg_rows = g.Cr; a.ldb = 9 * g.C; a.C = xc; a.ldc = g.Cr;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_GN_STATS));
+  // GroupNorm statistics -> per-channel scale / shift
+  EDIT_LAUNCH(launch_groupnorm_stats<T>(xc, g.B, g.N, g.Cr, g.G, static_cast<const T*>(gamma),
+                                        static_cast<const T*>(beta), 1e-5f, gn_part, g.gn_chunks, gn_stat,
+                                        gn_scale, gn_shift, s));
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_RESTORE));
+  // xt = x + LeakyReLU(GN(xc)) W_cf2^T + b_cf2
+  a = GemmArgs<T>{};
+  a.M = g.M; a.N = g.C; a.K = g.Cr; a.A = xc; a.lda = g.Cr;
+  a.scale = gn_scale; a.shift = gn_shift; a.rows_per_batch = g.N;
+  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w_cf2);
+  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(b_cf2);
+  a.seg_rows = g.C; a.ldb = g.Cr; a.C = xt; a.ldc = g.C; a.R = x; a.ldr = g.C;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_GNACT, E_BIAS_RES, s));
+  return EDIT_OK;
+}
+
+// out[m][0..C) = epilogue(a[m] W^T + b) with row stride ldc.
+template <typename T>
+edit_status_t linear_cc(const Geometry& g, const T* a_in, const void* w, const void* b, T* out, int ldc, bool relu,
+                        hipStream_t s) {
+  using namespace edit;
+  GemmArgs<T> a{};
+  a.M = g.M; a.N = g.C; a.K = g.C; a.A = a_in; a.lda = g.C;
+  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w);
+  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(b);
+  a.seg_rows = g.C; a.ldb = g.C; a.C = out; a.ldc = ldc;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, relu ? E_BIAS_RELU : E_BIAS, s));
+  return EDIT_OK;
+}
+
+// The image stream up to the linear-attention output y (steps 1-8 of the
+// layer; the ablation variants swap the query or the key/value processing).
 template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
-                        hipStream_t s, const Marks& mk, float* lin_den = nullptr) {
+                        hipStream_t s, const Marks& mk, float* lin_den = nullptr,
+                        const edit_convfusion_weights_t* kcf = nullptr) {
   using namespace edit;
   auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  GemmArgs<T> a{};
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_CONV3X3));
-  // 1. xc = Conv3x3(x) + b_cf1
-  a.M = g.M; a.N = g.Cr; a.K = 9 * g.C; a.A = x; a.lda = g.C; a.H = g.H; a.W = g.W; a.Cin = g.C;
-  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_cf1);
-  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_cf1);
-  a.seg_rows = g.Cr; a.ldb = 9 * g.C; a.C = P(L.xc); a.ldc = g.Cr;
-  EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_GN_STATS));
-  // 2. GroupNorm statistics -> per-channel scale / shift
-  EDIT_LAUNCH(launch_groupnorm_stats<T>(P(L.xc), g.B, g.N, g.Cr, g.G, static_cast<const T*>(w->gn_gamma),
-                                        static_cast<const T*>(w->gn_beta), 1e-5f, F(L.gn_part), g.gn_chunks,
-                                        F(L.gn_stat), F(L.gn_scale), F(L.gn_shift), s));
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_RESTORE));
-  // 3. xt = x + LeakyReLU(GN(xc)) W_cf2^T + b_cf2
-  a = GemmArgs<T>{};
-  a.M = g.M; a.N = g.C; a.K = g.Cr; a.A = P(L.xc); a.lda = g.Cr;
-  a.scale = F(L.gn_scale); a.shift = F(L.gn_shift); a.rows_per_batch = g.N;
-  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_cf2);
-  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_cf2);
-  a.seg_rows = g.C; a.ldb = g.Cr; a.C = P(L.xt); a.ldc = g.C; a.R = x; a.ldr = g.C;
-  EDIT_LAUNCH(launch_gemm<T>(a, A_GNACT, E_BIAS_RES, s));
+  edit_status_t st;
+  // 1-4. queries: q = ReLU(xt W_q^T + b_q), xt = x + ConvFusion(x) (or x itself)
+  const T* qin = x;
+  if (g.qmode == EDIT_QUERY_CONVFUSION) {
+    st = convfusion<T>(g, x, w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, P(L.xc),
+                       F(L.gn_part), F(L.gn_stat), F(L.gn_scale), F(L.gn_shift), P(L.xt), s, mk);
+    if (st != EDIT_OK) return st;
+    qin = P(L.xt);
+  }
   EDIT_LAUNCH(mk.mark(EDIT_STEP_Q_PROJ));
-  // 4. q = ReLU(xt W_q^T + b_q)
-  a = GemmArgs<T>{};
-  a.M = g.M; a.N = g.C; a.K = g.C; a.A = P(L.xt); a.lda = g.C;
-  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_q);
-  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_q);
-  a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.q); a.ldc = g.C;
-  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS_RELU, s));
+  if ((st = linear_cc<T>(g, qin, w->w_q, w->b_q, P(L.q), g.C, true, s)) != EDIT_OK) return st;
   EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_PROJ));
-  // 5. kv0 = [x W_k^T + b_k | x W_v^T + b_v]
-  a = GemmArgs<T>{};
-  a.M = g.M; a.N = 2 * g.C; a.K = g.C; a.A = x; a.lda = g.C;
-  a.Bseg[0] = static_cast<const T*>(w->w_k); a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_v);
-  a.bias[0] = static_cast<const T*>(w->b_k); a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_v);
-  a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.kv0); a.ldc = 2 * g.C;
-  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
-  // 6. compressed keys / values
-  EDIT_LAUNCH(launch_dwconv_s2<T>(P(L.kv0), g.B, g.H, g.W, g.C, static_cast<const T*>(w->dw_k),
-                                  static_cast<const T*>(w->db_k), static_cast<const T*>(w->dw_v),
-                                  static_cast<const T*>(w->db_v), P(L.kc), P(L.vc), s));
+  const T *kk, *vv;
+  int ldkv;
+  if (g.kvmode == EDIT_KV_COMPRESSED) {
+    // 5. kv0 = [x W_k^T + b_k | x W_v^T + b_v]
+    GemmArgs<T> a{};
+    a.M = g.M; a.N = 2 * g.C; a.K = g.C; a.A = x; a.lda = g.C;
+    a.Bseg[0] = static_cast<const T*>(w->w_k); a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_v);
+    a.bias[0] = static_cast<const T*>(w->b_k); a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_v);
+    a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.kv0); a.ldc = 2 * g.C;
+    EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
+    EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
+    // 6. compressed keys / values
+    EDIT_LAUNCH(launch_dwconv_s2<T>(P(L.kv0), g.B, g.H, g.W, g.C, static_cast<const T*>(w->dw_k),
+                                    static_cast<const T*>(w->db_k), static_cast<const T*>(w->dw_v),
+                                    static_cast<const T*>(w->db_v), P(L.kc), P(L.vc), s));
+    kk = P(L.kc); vv = P(L.vc); ldkv = g.C;
+  } else {
+    // Uncompressed keys and values side by side in kv0: K = ReLU(kin W_k^T + b_k), V = x W_v^T + b_v,
+    // with kin = x or, for ConvFusion keys, x + ConvFusion_K(x).
+    const T* kin = x;
+    if (g.kvmode == EDIT_KV_KEY_CONVFUSION) {
+      st = convfusion<T>(g, x, kcf->w_cf1, kcf->b_cf1, kcf->gn_gamma, kcf->gn_beta, kcf->w_cf2, kcf->b_cf2,
+                         P(L.xc_k), F(L.gn_part_k), F(L.gn_stat_k), F(L.gn_scale_k), F(L.gn_shift_k), P(L.xt_k), s,
+                         Marks{nullptr, s});
+      if (st != EDIT_OK) return st;
+      kin = P(L.xt_k);
+    }
+    if ((st = linear_cc<T>(g, kin, w->w_k, w->b_k, P(L.kv0), 2 * g.C, true, s)) != EDIT_OK) return st;
+    if ((st = linear_cc<T>(g, x, w->w_v, w->b_v, P(L.kv0) + g.C, 2 * g.C, false, s)) != EDIT_OK) return st;
+    EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
+    kk = P(L.kv0); vv = P(L.kv0) + g.C; ldkv = 2 * g.C;
+  }
   EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_STATE));
   // 7. per-head state
-  EDIT_LAUNCH(launch_kv_state<T>(P(L.kc), P(L.vc), g.B, g.Nc, g.heads, g.d, F(L.kv_part), g.kv_chunks, F(L.S),
+  EDIT_LAUNCH(launch_kv_state<T>(kk, vv, ldkv, g.B, g.Nkv, g.heads, g.d, F(L.kv_part), g.kv_chunks, F(L.S),
                                  F(L.z), P(L.st), F(L.zp), s));
   EDIT_LAUNCH(mk.mark(EDIT_STEP_APPLY));
   // 8. y = q S / (q . z + eps)
@@ -274,9 +368,9 @@ edit_status_t out_linear(int M, int C, const void* wo, const void* bo, const T* 
 
 template <typename T>
 edit_status_t run_edit(const Geometry& g, const Layout& L, const edit_weights_t* w, const void* x, void* y,
-                       void* ws, hipStream_t s, const Marks& mk) {
+                       void* ws, hipStream_t s, const Marks& mk, const edit_convfusion_weights_t* kcf = nullptr) {
   char* wsb = static_cast<char*>(ws);
-  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x), wsb, s, mk);
+  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x), wsb, s, mk, nullptr, kcf);
   if (st != EDIT_OK) return st;
   EDIT_LAUNCH(mk.mark(EDIT_STEP_OUT_PROJ));
   st = out_linear<T>(g.M, g.C, w->w_o, w->b_o, reinterpret_cast<const T*>(wsb + L.y), static_cast<T*>(y), s);
@@ -351,25 +445,50 @@ size_t mmedit_hybrid_workspace_size(const edit_shape_t* shape, int n_text) {
   return make_layout(g).total;
 }
 
+static void export_layout(const Layout& L, edit_ws_layout_t* out) {
+  out->xc = L.xc; out->gn_stat = L.gn_stat; out->xt = L.xt; out->q = L.q; out->kv0 = L.kv0;
+  out->kc = L.kc; out->vc = L.vc; out->S = L.S; out->z = L.z; out->y = L.y;
+  out->qkv_t = L.qkv_t; out->y_img = L.y_img; out->y_txt = L.y_txt; out->lin_den = L.lin_den;
+  out->xc_k = L.xc_k; out->gn_stat_k = L.gn_stat_k; out->xt_k = L.xt_k;
+  out->total = L.total;
+}
+
 edit_status_t edit_attn_workspace_layout(const edit_shape_t* shape, int n_text, edit_ws_layout_t* out) {
   Geometry g;
   edit_status_t st = check_shape(shape, n_text, &g);
   if (st != EDIT_OK) return st;
   if (!out) return fail(EDIT_ERR_ARG, "layout is NULL");
-  const Layout L = make_layout(g);
-  out->xc = L.xc; out->gn_stat = L.gn_stat; out->xt = L.xt; out->q = L.q; out->kv0 = L.kv0;
-  out->kc = L.kc; out->vc = L.vc; out->S = L.S; out->z = L.z; out->y = L.y;
-  out->qkv_t = L.qkv_t; out->y_img = L.y_img; out->y_txt = L.y_txt; out->lin_den = L.lin_den;
-  out->total = L.total;
+  export_layout(make_layout(g), out);
+  return EDIT_OK;
+}
+
+size_t edit_attn_variant_workspace_size(const edit_shape_t* shape, const edit_variant_t* variant) {
+  Geometry g;
+  if (check_shape(shape, 0, &g) != EDIT_OK || apply_variant(variant, &g) != EDIT_OK) return 0;
+  return make_layout(g).total;
+}
+
+edit_status_t edit_attn_variant_workspace_layout(const edit_shape_t* shape, const edit_variant_t* variant,
+                                                 edit_ws_layout_t* out) {
+  Geometry g;
+  edit_status_t st = check_shape(shape, 0, &g);
+  if (st != EDIT_OK) return st;
+  if ((st = apply_variant(variant, &g)) != EDIT_OK) return st;
+  if (!out) return fail(EDIT_ERR_ARG, "layout is NULL");
+  export_layout(make_layout(g), out);
   return EDIT_OK;
 }
 
 static edit_status_t forward_impl(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
-                                  void* workspace, size_t ws_bytes, void* hip_stream, void* const* events) {
+                                  void* workspace, size_t ws_bytes, void* hip_stream, void* const* events,
+                                  const edit_variant_t* variant = nullptr,
+                                  const edit_convfusion_weights_t* kcf = nullptr) {
   Geometry g;
   edit_status_t st = check_shape(shape, 0, &g);
   if (st != EDIT_OK) return st;
-  if ((st = check_weights(w)) != EDIT_OK) return st;
+  if (variant && (st = apply_variant(variant, &g)) != EDIT_OK) return st;
+  if ((st = check_weights(w, g)) != EDIT_OK) return st;
+  if (g.kvmode == EDIT_KV_KEY_CONVFUSION && (st = check_convfusion_weights(kcf)) != EDIT_OK) return st;
   if ((st = check_ptr(x, "x")) != EDIT_OK) return st;
   if ((st = check_ptr(y, "y")) != EDIT_OK) return st;
   if (!workspace) return fail(EDIT_ERR_ARG, "workspace is NULL");
@@ -384,13 +503,21 @@ static edit_status_t forward_impl(const edit_shape_t* shape, const edit_weights_
   if ((st = check_device()) != EDIT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const Marks mk{events, s};
-  return g.dtype == EDIT_BF16 ? run_edit<bf16>(g, L, w, x, y, workspace, s, mk)
-                              : run_edit<float>(g, L, w, x, y, workspace, s, mk);
+  return g.dtype == EDIT_BF16 ? run_edit<bf16>(g, L, w, x, y, workspace, s, mk, kcf)
+                              : run_edit<float>(g, L, w, x, y, workspace, s, mk, kcf);
 }
 
 edit_status_t edit_attn_forward(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
                                 void* workspace, size_t ws_bytes, void* hip_stream) {
   return forward_impl(shape, w, x, y, workspace, ws_bytes, hip_stream, nullptr);
+}
+
+edit_status_t edit_attn_variant_forward(const edit_shape_t* shape, const edit_variant_t* variant,
+                                        const edit_weights_t* w, const edit_convfusion_weights_t* key_cf,
+                                        const void* x, void* y, void* workspace, size_t ws_bytes,
+                                        void* hip_stream) {
+  if (!variant) return fail(EDIT_ERR_ARG, "variant is NULL");
+  return forward_impl(shape, w, x, y, workspace, ws_bytes, hip_stream, nullptr, variant, key_cf);
 }
 
 edit_status_t edit_attn_forward_timed(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
@@ -408,7 +535,7 @@ static edit_status_t hybrid_impl(const edit_shape_t* shape, int n_text, const ed
   Geometry g;
   edit_status_t st = check_shape(shape, n_text, &g);
   if (st != EDIT_OK) return st;
-  if ((st = check_weights(img)) != EDIT_OK) return st;
+  if ((st = check_weights(img, g)) != EDIT_OK) return st;
   if ((st = check_ptr(x_img, "x_img")) != EDIT_OK) return st;
   if ((st = check_ptr(y_img, "y_img")) != EDIT_OK) return st;
   if (n_text > 0) {

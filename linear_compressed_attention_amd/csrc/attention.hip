@@ -53,7 +53,7 @@ __device__ __forceinline__ void store_quad(float* dst, float a, float b, float c
 
 template <typename T, int DC>
 __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
-                                                               int Nc, int heads, int nchunks,
+                                                               int ld, int Nc, int heads, int nchunks,
                                                                float* __restrict__ partial) {
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   constexpr int d = 8 * DC;
@@ -70,7 +70,6 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   __shared__ __attribute__((aligned(16))) T At[16 * DR * PITCH];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int C = heads * d;
   const int j0 = chunk * kKvChunk, j1 = min(Nc, j0 + kKvChunk);
 
   f32x4 acc[TPW];
@@ -99,14 +98,14 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
       const int e = tid + 256 * l;
       const int tq = e % QUADS, rest = e / QUADS;
       const int c8 = (rest % DC) * 8, which = rest / DC;
-      const T* src = (which ? vc : kc) + ((size_t)b * Nc + js + 4 * tq) * C + h * d + c8;
+      const T* src = (which ? vc : kc) + ((size_t)b * Nc + js + 4 * tq) * ld + h * d + c8;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bool ok = e < ITEMS && js + 4 * tq + u < j1;
 #pragma unroll
         for (int w = 0; w < 8 / EPC; ++w) {
           const u32x4v zero = {0u, 0u, 0u, 0u};
-          raw[l][u][w] = ok ? *reinterpret_cast<const u32x4v*>(src + (size_t)u * C + w * EPC) : zero;
+          raw[l][u][w] = ok ? *reinterpret_cast<const u32x4v*>(src + (size_t)u * ld + w * EPC) : zero;
         }
       }
     }
@@ -198,14 +197,14 @@ __global__ __launch_bounds__(256) void kv_state_finalize_kernel(const float* __r
 }
 
 template <typename T>
-hipError_t launch_kv_state(const T* kc, const T* vc, int B, int Nc, int heads, int d, float* partial,
+hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int heads, int d, float* partial,
                            int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s) {
   const int DT = (d + 15) / 16, DR = (d + 16) / 16;
   dim3 grid(nchunks, heads, B);
   switch (d / 8) {
 #define EDIT_KV_CASE(DCV)                                                                              \
   case DCV:                                                                                            \
-    hipLaunchKernelGGL((kv_state_partial_kernel<T, DCV>), grid, dim3(256), 0, s, kc, vc, Nc, heads,    \
+    hipLaunchKernelGGL((kv_state_partial_kernel<T, DCV>), grid, dim3(256), 0, s, kc, vc, ld, Nc, heads, \
                        nchunks, partial);                                                              \
     break;
     EDIT_KV_CASE(1) EDIT_KV_CASE(2) EDIT_KV_CASE(3) EDIT_KV_CASE(4) EDIT_KV_CASE(5) EDIT_KV_CASE(6)
@@ -533,7 +532,7 @@ hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s) {
 }
 
 #define EDIT_INST(T)                                                                                     \
-  template hipError_t launch_kv_state<T>(const T*, const T*, int, int, int, int, float*, int, float*,   \
+  template hipError_t launch_kv_state<T>(const T*, const T*, int, int, int, int, int, float*, int, float*, \
                                          float*, T*, float*, hipStream_t);                              \
   template hipError_t launch_linattn_apply<T>(const T*, int, const T*, const float*, int, int, int, int, \
                                               float, T*, int, float*, hipStream_t);                     \

@@ -66,10 +66,11 @@ hipError_t launch_dwconv_s2(const T* kv0, int B, int H, int W, int C, const T* d
                             const T* dwv, const T* dbv, T* kc, T* vc, hipStream_t s);
 
 // Per-head state of the compressed keys/values: S = K'^T V', z = sum K'.
+// kc and vc rows (tokens) are ld elements apart.
 // Writes f32 S [B][h][d][d], z [B][h][d] and the apply kernel's operand:
 // st [B][h][2][DP][DK] of T (S transposed, split hi/lo for bf16), zp [B][h][DK] f32.
 template <typename T>
-hipError_t launch_kv_state(const T* kc, const T* vc, int B, int Nc, int heads, int d, float* partial,
+hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int heads, int d, float* partial,
                            int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s);
 int kv_state_chunks(int Nc);
 int kv_state_dp(int d);   // padded rows of the state operand

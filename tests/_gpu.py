@@ -104,3 +104,39 @@ def oracle_views(tr, shape):
         "kv0": np.concatenate([tr["k0"], tr["v0"]], axis=-1), "kc": tr["kc"], "vc": tr["vc"],
         "S": tr["S"], "z": tr["z"], "out": tr["out"],
     }
+
+
+def run_variant(shape, inp, query, kv):
+    """edit_attn_variant_forward; returns the output and the variant's intermediates."""
+    x = to_dev(inp["x"], shape.dtype)
+    w = dev_weights(inp["w"], shape.dtype)
+    if query == "linear":
+        for n in ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2"):
+            w.pop(n)
+    if kv != "compressed":
+        for n in ("dw_k", "db_k", "dw_v", "db_v"):
+            w.pop(n)
+    kcf = dev_weights(inp["w_kcf"], shape.dtype) if kv == "key_convfusion" else None
+    y = torch.empty_like(x)
+    ws = torch.empty(lca.edit_attn_variant_workspace_size(shape, query, kv), dtype=torch.uint8, device="cuda")
+    poison(y)
+    poison(ws)
+    lca.edit_attn_variant_forward(shape, query, kv, w, kcf, x, y, ws)
+    torch.cuda.synchronize()
+    lay = lca.edit_attn_variant_workspace_layout(shape, query, kv)
+    s = shape
+    T, f32 = TORCH_DTYPE[s.dtype], torch.float32
+    B, N, C, h, d = s.B, s.N, s.C, s.heads, s.head_dim
+    got = {"out": y, "q": _view(ws, lay["q"], (B, N, C), T), "S": _view(ws, lay["S"], (B, h, d, d), f32),
+           "z": _view(ws, lay["z"], (B, h, d), f32), "y": _view(ws, lay["y"], (B, N, C), T)}
+    if kv == "compressed":
+        got["kc"] = _view(ws, lay["kc"], (B, s.Nc, C), T)
+        got["vc"] = _view(ws, lay["vc"], (B, s.Nc, C), T)
+    else:
+        kv0 = _view(ws, lay["kv0"], (B, N, 2 * C), T)
+        got["k"], got["v"] = kv0[..., :C], kv0[..., C:]
+    if kv == "key_convfusion":
+        got["xt_k"] = _view(ws, lay["xt_k"], (B, N, C), T)
+    if query == "convfusion":
+        got["xt"] = _view(ws, lay["xt"], (B, N, C), T)
+    return {k: v.float().cpu().numpy() for k, v in got.items()}

@@ -156,3 +156,51 @@ def test_no_device_is_reported():
 def test_status_strings():
     assert lca.edit_status_string(0) == "EDIT_OK"
     assert "WORKSPACE" in lca.edit_status_string(3)
+
+
+@pytest.mark.parametrize("query,kv", [("convfusion", "compressed"), ("convfusion", "full"),
+                                      ("convfusion", "key_convfusion"), ("linear", "compressed"),
+                                      ("linear", "full")])
+def test_variant_layouts(query, kv):
+    s = CONFIGS["pixart1024"]
+    lay = lca.edit_attn_variant_workspace_layout(s, query, kv)
+    assert lay["total"] == lca.edit_attn_variant_workspace_size(s, query, kv)
+    assert (lay["xt"] > 0) == (query == "convfusion")
+    assert (lay["kc"] > 0) == (kv == "compressed")
+    assert (lay["xt_k"] > 0) == (kv == "key_convfusion")
+    assert all(v % 256 == 0 for v in lay.values())
+    if (query, kv) == ("convfusion", "compressed"):
+        assert lay == lca.edit_attn_workspace_layout(s, 0)
+
+
+def test_variant_argument_errors():
+    ws = _FakeWS(0xB000000, lca.edit_attn_variant_workspace_size(SHAPE, "convfusion", "key_convfusion"))
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_variant_forward(SHAPE, 7, "compressed", _fake_weights(), None, 0x9000000, 0xA000000, ws,
+                                      stream=0)
+    assert e.value.status == 1 and "query mode" in e.value.detail
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_variant_forward(SHAPE, "convfusion", 5, _fake_weights(), None, 0x9000000, 0xA000000, ws,
+                                      stream=0)
+    assert e.value.status == 1 and "key/value mode" in e.value.detail
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_variant_forward(SHAPE, "convfusion", "key_convfusion", _fake_weights(), None, 0x9000000,
+                                      0xA000000, ws, stream=0)
+    assert e.value.status == 1 and "key ConvFusion" in e.value.detail
+    w = _fake_weights()
+    w["w_cf1"] = None
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_variant_forward(SHAPE, "convfusion", "full", w, None, 0x9000000, 0xA000000, ws, stream=0)
+    assert e.value.status == 1 and "w_cf1" in e.value.detail
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")
+def test_variant_unread_weights_may_be_null():
+    """A plain query reads no ConvFusion parameters and uncompressed keys no
+    depthwise ones: the arguments pass, and only the missing device is reported."""
+    w = {n: p for n, p in _fake_weights().items()
+         if n not in ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2", "dw_k", "db_k", "dw_v", "db_v")}
+    ws = _FakeWS(0xB000000, lca.edit_attn_variant_workspace_size(SHAPE, "linear", "full"))
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_variant_forward(SHAPE, "linear", "full", w, None, 0x9000000, 0xA000000, ws, stream=0)
+    assert e.value.status == 4

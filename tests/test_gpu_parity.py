@@ -204,3 +204,60 @@ def test_timed_forward_matches_forward():
     for e in evs:
         hip.hipEventDestroy(ctypes.c_void_p(e))
     np.testing.assert_array_equal(y.float().cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------
+# Ablation variants of the query / key-value processing
+# ---------------------------------------------------------------------------
+
+VARIANTS = [("convfusion", "key_convfusion"), ("linear", "compressed"), ("convfusion", "full"),
+            ("linear", "full"), ("linear", "key_convfusion")]
+
+
+def check_variant(s, query, kv, seed=0):
+    inp = make_inputs(s, seed=seed, gn_affine_random=True, key_convfusion=(kv == "key_convfusion"))
+    _announce(f"variant ({query}, {kv}) {s} seed={seed}")
+    got = G.run_variant(s, inp, query, kv)
+    tr = {}
+    out = O.edit_attn_variant_forward(inp["x"], inp["w"], s, query, kv, inp.get("w_kcf"), trace=tr)
+    ref = {"out": out, "q": tr["q"], "S": tr["S"], "z": tr["z"], "y": tr["y"]}
+    if kv == "compressed":
+        ref.update(kc=tr["kc"], vc=tr["vc"])
+    else:
+        ref.update(k=tr["k"], v=tr["v"])
+    if kv == "key_convfusion":
+        ref["xt_k"] = tr["xt_k"]
+    if query == "convfusion":
+        ref["xt"] = tr["xt"]
+    tol = _tol(s)
+    errs = {}
+    for k, r in ref.items():
+        assert np.isfinite(got[k]).all(), f"{k}: non-finite elements"
+        errs[k] = max_rel_err(got[k], r)
+    for k in ("q", "k", "kc", "xt_k"):
+        if k in ref:
+            errs[k + "_centred"] = centred_rel_err(got[k], ref[k])
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"over tolerance {tol}: {bad}"
+
+
+@pytest.mark.parametrize("query,kv", VARIANTS)
+@pytest.mark.parametrize("name", ["f32_d32_ragged", "bf16_d96_conv96"])
+def test_variants_small(name, query, kv):
+    check_variant(SMALL[name], query, kv, seed=8)
+
+
+@pytest.mark.parametrize("query,kv", [("convfusion", "key_convfusion"), ("linear", "compressed"),
+                                      ("convfusion", "full")])
+def test_variants_pixart1024(query, kv):
+    check_variant(CONFIGS["pixart1024"], query, kv)
+
+
+def test_variant_main_row_equals_layer():
+    s = SMALL["bf16_d64_ragged"]
+    inp = make_inputs(s, seed=9)
+    _announce("variant (convfusion, compressed) vs edit")
+    a = G.run_variant(s, inp, "convfusion", "compressed")["out"]
+    b = G.run_edit(s, inp, with_intermediates=False)["out"]
+    np.testing.assert_array_equal(a, b)
