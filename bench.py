@@ -145,7 +145,7 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def cpu_baseline(shape, inp, min_runs, budget_s):
+def cpu_baseline(shape, inp, min_runs, budget_s, eta="ratio", query="convfusion", kv="compressed"):
     """The float64 oracle, as it stands, on the host cores: at least
     `min_runs` full layer forwards of the same workload, more while the total
     stays under `budget_s` seconds."""
@@ -155,7 +155,9 @@ def cpu_baseline(shape, inp, min_runs, budget_s):
     while len(times) < min_runs or (sum(times) + statistics.median(times) < budget_s and len(times) < 50):
         t0 = time.perf_counter()
         if shape.n_text:
-            O.mmedit_hybrid_forward(inp["x"], inp["x_txt"], inp["w"], inp["w_txt"], shape)
+            O.mmedit_hybrid_forward(inp["x"], inp["x_txt"], inp["w"], inp["w_txt"], shape, eta=eta)
+        elif (query, kv) != ("convfusion", "compressed"):
+            O.edit_attn_variant_forward(inp["x"], inp["w"], shape, query, kv, inp.get("w_kcf"))
         else:
             O.edit_attn_forward(inp["x"], inp["w"], shape)
         times.append(time.perf_counter() - t0)
@@ -186,6 +188,12 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (outside the timed region) whose HBM counter "
                          "readings calibrate FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--exact-eta", action="store_true",
+                    help="hybrid workloads: time mmedit_hybrid_exact_forward (eta per row) instead of the ratio")
+    ap.add_argument("--query", default="convfusion", choices=["convfusion", "linear"],
+                    help="ablation variant: query processing (EDiT workloads)")
+    ap.add_argument("--kv", default="compressed", choices=["compressed", "full", "key_convfusion"],
+                    help="ablation variant: key/value processing (EDiT workloads)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
@@ -201,7 +209,14 @@ def main():
 
     s = CONFIGS[args.workload]
     hybrid = s.n_text > 0
-    inp = make_inputs(s, seed=0)
+    variant = (args.query, args.kv) != ("convfusion", "compressed")
+    if hybrid and variant:
+        print("the ablation variants apply to the EDiT layer, not the hybrid", file=sys.stderr)
+        sys.exit(2)
+    if args.exact_eta and not hybrid:
+        print("--exact-eta applies to the hybrid workloads", file=sys.stderr)
+        sys.exit(2)
+    inp = make_inputs(s, seed=0, key_convfusion=args.kv == "key_convfusion")
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     x = torch.from_numpy(inp["x"]).to(dev).to(tdt)
@@ -214,8 +229,18 @@ def main():
         yt = torch.empty_like(xt)
         ws = torch.empty(lca.mmedit_hybrid_workspace_size(s, s.n_text), dtype=torch.uint8, device=dev)
 
+        hfwd = lca.mmedit_hybrid_exact_forward if args.exact_eta else lca.mmedit_hybrid_forward
+
         def step():
-            lca.mmedit_hybrid_forward(s, s.n_text, w, wt, x, xt, y, yt, ws, stream)
+            hfwd(s, s.n_text, w, wt, x, xt, y, yt, ws, stream)
+    elif variant:
+        kcf = ({k: torch.from_numpy(v).to(dev).to(tdt) for k, v in inp["w_kcf"].items()}
+               if args.kv == "key_convfusion" else None)
+        ws = torch.empty(lca.edit_attn_variant_workspace_size(s, args.query, args.kv), dtype=torch.uint8,
+                         device=dev)
+
+        def step():
+            lca.edit_attn_variant_forward(s, args.query, args.kv, w, kcf, x, y, ws, stream)
     else:
         ws = torch.empty(lca.edit_attn_workspace_size(s), dtype=torch.uint8, device=dev)
 
@@ -268,7 +293,8 @@ def main():
     torch.cuda.synchronize()
     # The hybrid's image path runs these same kernels on the same image shape.
     s_img = dataclasses.replace(s, n_text=0) if hybrid else s
-    ws_img = torch.empty(lca.edit_attn_workspace_size(s_img), dtype=torch.uint8, device=dev) if hybrid else ws
+    ws_img = (torch.empty(lca.edit_attn_workspace_size(s_img), dtype=torch.uint8, device=dev)
+              if hybrid or variant else ws)
     # A bounded spin kernel first, so that every timed forward is already
     # queued when the GPU reaches it: the step intervals then hold no host
     # launch latency.
@@ -330,18 +356,23 @@ def main():
 
     cpu = None
     if args.cpu_runs > 0:
-        cpu = cpu_baseline(s, inp, args.cpu_runs, args.cpu_budget)
+        cpu = cpu_baseline(s, inp, args.cpu_runs, args.cpu_budget, eta="exact" if args.exact_eta else "ratio",
+                           query=args.query, kv=args.kv)
 
     if hybrid:
         metric = "image tokens/sec per MM-EDiT hybrid attention layer fwd (text rows included in the time)"
         wl = (f"{args.workload}: MM-EDiT hybrid attention layer forward, B={s.B}, {s.H}x{s.W} image grid "
               f"({s.N} image tokens, {s.Nc} compressed) + {s.n_text} text tokens, C={s.C}, {s.heads} heads x "
               f"{s.head_dim}, r={s.reduction}, {s.gn_groups} GN groups, {s.dtype}")
+        if args.exact_eta:
+            wl += ", eta computed per image row (exact)"
     else:
         metric = "image tokens/sec per EDiT attention layer fwd at 16384 tokens; % HBM/MFMA peak"
         wl = (f"{args.workload}: EDiT attention layer forward, B={s.B}, {s.H}x{s.W} token grid "
               f"({s.N} tokens, {s.Nc} compressed K/V tokens), C={s.C}, {s.heads} heads x "
               f"{s.head_dim}, r={s.reduction}, {s.gn_groups} GN groups, {s.dtype}")
+        if variant:
+            wl += f", ablation variant query={args.query} kv={args.kv}"
     out = {
         "metric": metric,
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -349,14 +380,18 @@ def main():
         "dtype": s.dtype, "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
         "config": {"workload": wl, "B": s.B, "H": s.H, "W": s.W, "C": s.C, "heads": s.heads,
                    "head_dim": s.head_dim, "reduction": s.reduction, "gn_groups": s.gn_groups,
-                   **({"n_text": s.n_text} if hybrid else {})},
+                   **({"n_text": s.n_text} if hybrid else {}),
+                   **({"eta": "exact"} if args.exact_eta else {}),
+                   **({"query": args.query, "kv": args.kv} if variant else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ms_per_step_p10_p50_p90": [round(pct(per_iter, q), 5) for q in (0.1, 0.5, 0.9)],
         "cold": cold,
         "layer_roofline": {"floor_us": round(layer_floor_us, 1),
                            "frac": round(layer_floor_us / (ms_per_step * 1e3), 4),
-                           **({"covers": "image path only"} if hybrid else {})},
+                           **({"covers": "image path only"} if hybrid else {}),
+                           **({"covers": "the layer's own steps (breakdown taken on the layer, not the variant)"}
+                              if variant else {})},
         "steps_breakdown": {n: {k: v for k, v in steps[n].items() if k in ("us", "bound", "achieved", "unit", "frac")}
                             for n in STEP_NAMES},
         "wall_s_timed_region": round(wall, 4),
