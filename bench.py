@@ -37,7 +37,7 @@ STEP_NAMES = ["cf_conv3x3", "gn_stats", "cf_restore", "q_proj", "kv_proj", "sc_d
               "linattn_apply", "out_proj"]
 STEP_KERNELS = {  # kernels launched per step (rocprofv3 names start with these)
     "cf_conv3x3": "gemm_kernel<..., A_CONV3, E_BIAS>", "gn_stats": "gn_partial_kernel + gn_finalize_kernel",
-    "cf_restore": "gemm_kernel<..., A_GNACT, E_BIAS_RES>", "q_proj": "gemm_kernel<..., A_PLAIN, E_BIAS_RELU>",
+    "cf_restore": "gn_apply_kernel + gemm_dma_kernel<..., A_PLAIN, E_BIAS_RES>", "q_proj": "gemm_kernel<..., A_PLAIN, E_BIAS_RELU>",
     "kv_proj": "gemm_kernel<..., A_PLAIN, E_BIAS>", "sc_dwconv": "dwconv_s2_kernel",
     "kv_state": "kv_state_partial_kernel + kv_state_finalize_kernel", "linattn_apply": "linattn_apply_kernel",
     "out_proj": "gemm_kernel<..., A_PLAIN, E_BIAS>",

@@ -149,6 +149,7 @@ edit_status_t mmedit_hybrid_exact_forward(const edit_shape_t* shape, int n_text,
  * (the shape's dtype) or f32:
  *   xc      [B][N][C/r] T      ConvFusion 3x3 output
  *   gn_stat [B][G][2]   f32    GroupNorm mean and 1/sqrt(var + 1e-5)
+ *   cf_act  [B][N][C/r] T      LeakyReLU(GN(xc)), the input of the 1x1 restore
  *   xt      [B][N][C]   T      X + Conv1x1(LeakyReLU(GN(xc)))
  *   q       [B][N][C]   T      ConvFusion queries (after ReLU)
  *   kv0     [B][N][2C]  T      key Linear | value Linear, side by side per token
@@ -166,7 +167,7 @@ edit_status_t mmedit_hybrid_exact_forward(const edit_shape_t* shape, int n_text,
  * and the sums S, z run over all N tokens; kc, vc (and xc, gn_stat, xt with
  * a plain query) are not produced. */
 typedef struct {
-  size_t xc, gn_stat, xt, q, kv0, kc, vc, S, z, y, qkv_t, y_img, y_txt, lin_den;
+  size_t xc, gn_stat, cf_act, xt, q, kv0, kc, vc, S, z, y, qkv_t, y_img, y_txt, lin_den;
   size_t xc_k, gn_stat_k, xt_k;
   size_t total;
 } edit_ws_layout_t;
@@ -217,7 +218,7 @@ edit_status_t edit_attn_variant_forward(const edit_shape_t* shape, const edit_va
 typedef enum {
   EDIT_STEP_CF_CONV3X3 = 0,  /* ConvFusion 3x3 compressing conv             (1 kernel)  */
   EDIT_STEP_GN_STATS = 1,    /* GroupNorm statistics                         (2 kernels) */
-  EDIT_STEP_CF_RESTORE = 2,  /* GN + LeakyReLU + 1x1 restore + residual      (1 kernel)  */
+  EDIT_STEP_CF_RESTORE = 2,  /* GN + LeakyReLU, then 1x1 restore + residual  (2 kernels) */
   EDIT_STEP_Q_PROJ = 3,      /* query Linear + ReLU                          (1 kernel)  */
   EDIT_STEP_KV_PROJ = 4,     /* key and value Linears                        (1 kernel)  */
   EDIT_STEP_SC_DWCONV = 5,   /* depthwise 3x3 stride 2, ReLU on keys          (1 kernel)  */

@@ -6,7 +6,7 @@
 //   section "ConvFusion":
 //     1 gemm A_CONV3      xc  = Conv3x3(x) + b_cf1               (C -> C/r)
 //     2 groupnorm stats   per (b, group) mean / rstd -> scale, shift
-//     3 gemm A_GNACT      xt  = x + Conv1x1(LeakyReLU(GN(xc))) + b_cf2
+//     3 gn apply, gemm    act = LeakyReLU(GN(xc)); xt = x + act W_cf2^T + b_cf2
 //     4 gemm relu         q   = ReLU(xt W_q^T + b_q)
 //   section "Spatial Compressor":
 //     5 gemm (2 segments) kv0 = [x W_k^T + b_k | x W_v^T + b_v]
@@ -57,9 +57,9 @@ struct Geometry {
 };
 
 struct Layout {
-  size_t xc, gn_part, gn_stat, gn_scale, gn_shift, xt, q, kv0, kc, vc, kv_part, S, z, st, zp, y;
+  size_t xc, gn_part, gn_stat, gn_scale, gn_shift, cf_act, xt, q, kv0, kc, vc, kv_part, S, z, st, zp, y;
   size_t qkv_t, y_img, y_txt, lin_den;
-  size_t xc_k, gn_part_k, gn_stat_k, gn_scale_k, gn_shift_k, xt_k;   // key ConvFusion branch
+  size_t xc_k, gn_part_k, gn_stat_k, gn_scale_k, gn_shift_k, cf_act_k, xt_k;   // key ConvFusion branch
   size_t total;
 };
 
@@ -126,6 +126,7 @@ Layout make_layout(const Geometry& g) {
     L.gn_stat = take((size_t)g.B * g.G * 2 * 4);
     L.gn_scale = take((size_t)g.B * g.Cr * 4);
     L.gn_shift = take((size_t)g.B * g.Cr * 4);
+    L.cf_act = take(M * g.Cr * es);
     L.xt = take(M * g.C * es);
   }
   L.q = take(M * g.C * es);
@@ -140,6 +141,7 @@ Layout make_layout(const Geometry& g) {
     L.gn_stat_k = take((size_t)g.B * g.G * 2 * 4);
     L.gn_scale_k = take((size_t)g.B * g.Cr * 4);
     L.gn_shift_k = take((size_t)g.B * g.Cr * 4);
+    L.cf_act_k = take(M * g.Cr * es);
     L.xt_k = take(M * g.C * es);
   }
   L.kv_part = take(BH * g.kv_chunks * (16 * g.DR) * (16 * g.DT) * 4);
@@ -249,7 +251,8 @@ struct Marks {
 template <typename T>
 edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const void* b_cf1, const void* gamma,
                          const void* beta, const void* w_cf2, const void* b_cf2, T* xc, float* gn_part,
-                         float* gn_stat, float* gn_scale, float* gn_shift, T* xt, hipStream_t s, const Marks& mk) {
+                         float* gn_stat, float* gn_scale, float* gn_shift, T* act, T* xt, hipStream_t s,
+                         const Marks& mk) {
   using namespace edit;
   GemmArgs<T> a{};
   EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_CONV3X3));
@@ -265,14 +268,14 @@ edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const
                                         static_cast<const T*>(beta), 1e-5f, gn_part, g.gn_chunks, gn_stat,
                                         gn_scale, gn_shift, s));
   EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_RESTORE));
-  // xt = x + LeakyReLU(GN(xc)) W_cf2^T + b_cf2
+  // act = LeakyReLU(GN(xc)); xt = x + act W_cf2^T + b_cf2
+  EDIT_LAUNCH(launch_groupnorm_apply<T>(xc, g.B, g.N, g.Cr, gn_scale, gn_shift, act, s));
   a = GemmArgs<T>{};
-  a.M = g.M; a.N = g.C; a.K = g.Cr; a.A = xc; a.lda = g.Cr;
-  a.scale = gn_scale; a.shift = gn_shift; a.rows_per_batch = g.N;
+  a.M = g.M; a.N = g.C; a.K = g.Cr; a.A = act; a.lda = g.Cr;
   a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w_cf2);
   a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(b_cf2);
   a.seg_rows = g.C; a.ldb = g.Cr; a.C = xt; a.ldc = g.C; a.R = x; a.ldr = g.C;
-  EDIT_LAUNCH(launch_gemm<T>(a, A_GNACT, E_BIAS_RES, s));
+  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS_RES, s));
   return EDIT_OK;
 }
 
@@ -304,7 +307,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
   const T* qin = x;
   if (g.qmode == EDIT_QUERY_CONVFUSION) {
     st = convfusion<T>(g, x, w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, P(L.xc),
-                       F(L.gn_part), F(L.gn_stat), F(L.gn_scale), F(L.gn_shift), P(L.xt), s, mk);
+                       F(L.gn_part), F(L.gn_stat), F(L.gn_scale), F(L.gn_shift), P(L.cf_act), P(L.xt), s, mk);
     if (st != EDIT_OK) return st;
     qin = P(L.xt);
   }
@@ -333,8 +336,8 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     const T* kin = x;
     if (g.kvmode == EDIT_KV_KEY_CONVFUSION) {
       st = convfusion<T>(g, x, kcf->w_cf1, kcf->b_cf1, kcf->gn_gamma, kcf->gn_beta, kcf->w_cf2, kcf->b_cf2,
-                         P(L.xc_k), F(L.gn_part_k), F(L.gn_stat_k), F(L.gn_scale_k), F(L.gn_shift_k), P(L.xt_k), s,
-                         Marks{nullptr, s});
+                         P(L.xc_k), F(L.gn_part_k), F(L.gn_stat_k), F(L.gn_scale_k), F(L.gn_shift_k), P(L.cf_act_k),
+                         P(L.xt_k), s, Marks{nullptr, s});
       if (st != EDIT_OK) return st;
       kin = P(L.xt_k);
     }
@@ -446,7 +449,7 @@ size_t mmedit_hybrid_workspace_size(const edit_shape_t* shape, int n_text) {
 }
 
 static void export_layout(const Layout& L, edit_ws_layout_t* out) {
-  out->xc = L.xc; out->gn_stat = L.gn_stat; out->xt = L.xt; out->q = L.q; out->kv0 = L.kv0;
+  out->xc = L.xc; out->gn_stat = L.gn_stat; out->cf_act = L.cf_act; out->xt = L.xt; out->q = L.q; out->kv0 = L.kv0;
   out->kc = L.kc; out->vc = L.vc; out->S = L.S; out->z = L.z; out->y = L.y;
   out->qkv_t = L.qkv_t; out->y_img = L.y_img; out->y_txt = L.y_txt; out->lin_den = L.lin_den;
   out->xc_k = L.xc_k; out->gn_stat_k = L.gn_stat_k; out->xt_k = L.xt_k;

@@ -332,6 +332,7 @@ static hipError_t launch_tiles(const GemmArgs<T>& a, AMode am, EMode em, hipStre
   }
   EDIT_GEMM_CASE(A_PLAIN, E_BIAS)
   EDIT_GEMM_CASE(A_PLAIN, E_BIAS_RELU)
+  EDIT_GEMM_CASE(A_PLAIN, E_BIAS_RES)
   EDIT_GEMM_CASE(A_CONV3, E_BIAS)
   EDIT_GEMM_CASE(A_GNACT, E_BIAS_RES)
 #undef EDIT_GEMM_CASE

@@ -1,7 +1,7 @@
 // MFMA GEMM for gfx950 with direct global-to-LDS tile loads:
 // C[M][N] = A[M][K] * B[N][K]^T (+ bias, optional ReLU), bf16 in and out,
-// fp32 accumulation. A is either plain rows or an implicit 3x3 stride-1
-// pad-1 convolution over a channels-last image.
+// fp32 accumulation, optional residual. A is either plain rows or an implicit
+// 3x3 stride-1 pad-1 convolution over a channels-last image.
 //
 // Serves the dense steps of the EDiT layer ("EDiT: Efficient Diffusion
 // Transformers with Linear Compressed Attention" notes): the ConvFusion 3x3
@@ -83,12 +83,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = (p.N + BN - 1) / BN;
-  const int nk = AM == A_CONV3 ? 9 * (p.Cin / 64) : p.K / 64;
+  const int nk = AM == A_CONV3 ? 9 * (p.Cin / 64) : (p.K + 63) / 64;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, (uint32_t)((size_t)p.M * p.lda * 2));
 
   // Lane l fills chunk (l & 7) of row (l >> 3) of an 8-row DMA group and
   // fetches the logical chunk stored there.
   const int lr = lane >> 3, pc = lane & 7;
+  // The logical chunk a lane fetches, for 8-row groups of even and odd index
+  // (row r = 8g + lr is stored with phase (r >> 1) & 7 = (4g + lr / 2) & 7).
+  const int cl0 = pc ^ (lr >> 1), cl1 = pc ^ (4 + (lr >> 1));
   // Fragment addressing: lane l reads row (l & 31) of a 32-row block, logical
   // chunk 2s + (l >> 5) for sub-step s (16 K values each).
   const int fr = lane & 31, fh = lane >> 5;
@@ -158,15 +161,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
     } else {                                                                                      \
       sa = sb = (uint32_t)kd_ * 128u;                                                             \
     }                                                                                             \
+    /* K tail: chunks at or past K read zeros (A and B), so they add nothing */                  \
+    const bool ktail_ = AM != A_CONV3 && kd_ * 64 + 64 > p.K;                                     \
+    const int klim_ = p.K - kd_ * 64;                                                             \
     _Pragma("unroll") for (int a = 0; a < NA; ++a) {                                              \
       uint32_t v = aoff[a];                                                                       \
       if (AM == A_CONV3) v = ((amask[AM == A_CONV3 ? a : 0] >> tap) & 1u) ? v + (uint32_t)tapoff : kOob; \
+      if (ktail_ && 8 * (((a * NW + wave) & 1) ? cl1 : cl0) >= klim_) v = kOob;                  \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr)((S) + 1024 * (a * NW + wave)), 16, v, \
                                                sa, 0, 0);                                         \
     }                                                                                             \
-    _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                              \
+      uint32_t v = boff[b];                                                                       \
+      if (ktail_ && 8 * (((b * NW + wave) & 1) ? cl1 : cl0) >= klim_) v = kOob;                  \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_ptr)((S) + BM * 128 + 1024 * (b * NW + wave)), \
-                                               16, boff[b], sb, 0, 0);                            \
+                                               16, v, sb, 0, 0);                                  \
+    }                                                                                             \
   } while (0)
 #define EDIT_PREFETCH3()                                                                          \
   do {                                                                                            \
@@ -179,7 +189,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
   bf16x8 xf[2][TI], wf[2][CJ];
   bf16x4 bv[CJ][4];   // the tile's bias, fetched before the next tile's loads are queued
 
-#define EDIT_READ(S, s_, buf_)                                                                    \
+#define EDIT_READ(S, s_, buf_)                                                               \
   do {                                                                                            \
     _Pragma("unroll") for (int t = 0; t < TI; ++t)                                                \
       xf[buf_][t] = *reinterpret_cast<const bf16x8*>((S) + xrow + t * 4096 + fo[s_]);             \
@@ -287,30 +297,92 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
     // this tile from registers while they are in flight.
     const int em0 = m0, en0 = n0;
     const int next = tl + (int)gridDim.x;
+    // Residual rows (E_BIAS_RES), requested before the next tile's loads so
+    // that waiting for them does not wait for those.
+    uint4 rv[EM == E_BIAS_RES ? TI : 1][EM == E_BIAS_RES ? CJ : 1][2];
+    if (EM == E_BIAS_RES) {
+#pragma unroll
+      for (int t = 0; t < TI; ++t) {
+        const int m = em0 + wm * WTM + t * 32 + fr;
+#pragma unroll
+        for (int c = 0; c < CJ; ++c)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int n = en0 + wn * WTN + c * 32 + 8 * (fh ? 2 * j + 1 : 2 * j);
+            rv[EM == E_BIAS_RES ? t : 0][EM == E_BIAS_RES ? c : 0][j] =
+                m < p.M && n < p.N ? *reinterpret_cast<const uint4*>(p.R + (size_t)m * p.ldr + n)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+          }
+      }
+    }
     if (next < ntiles) {
       EDIT_SET_TILE(next);
       EDIT_PREFETCH3();
     }
-    // Epilogue: bias (+ ReLU); each accumulator quad is 4 consecutive output
-    // channels of one token, written as one 8-byte store.
+    // Epilogue: bias (+ ReLU, or + residual). Accumulator quad g of lane l
+    // holds channels 8g + 4(l >> 5) .. +3 of token l & 31; lanes l and l ^ 32
+    // swap the halves of g = 2j + 1 (lower lane) and g = 2j (upper lane), so
+    // that each lane writes 8 consecutive channels of its token with one
+    // 16-byte store: 16 stores per tile per lane, which the next tile's first
+    // wait can leave in flight. With a residual the swap moves fp32 values,
+    // so that bias, product and residual are rounded to bf16 once.
 #pragma unroll
     for (int t = 0; t < TI; ++t) {
       const int m = em0 + wm * WTM + t * 32 + fr;
 #pragma unroll
-      for (int c = 0; c < CJ; ++c)
+      for (int c = 0; c < CJ; ++c) {
+        float f[4][4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = en0 + wn * WTN + c * 32 + 8 * g + 4 * fh;
-          if (m < p.M && n < p.N) {
-            float v[4];
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[g][i] = acc[t][c][4 * g + i] + (float)bv[c][g][i];
+            if (EM == E_BIAS_RELU) f[g][i] = f[g][i] > 0.0f ? f[g][i] : 0.0f;
+          }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int ge = 2 * j, go = 2 * j + 1;
+          const int gsel = fh ? go : ge;
+          const int n = en0 + wn * WTN + c * 32 + 8 * gsel;
+          uint32_t w[4];
+          if (EM == E_BIAS_RES) {
+            float o[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              v[i] = acc[t][c][4 * g + i] + (float)bv[c][g][i];
-              if (EM == E_BIAS_RELU) v[i] = v[i] > 0.0f ? v[i] : 0.0f;
+              const float snd = fh ? f[ge][i] : f[go][i];
+              const float rcv = __shfl_xor(snd, 32, 64);
+              o[i] = fh ? rcv : f[ge][i];
+              o[4 + i] = fh ? f[go][i] : rcv;
             }
-            store4(p.C + (size_t)m * p.ldc + n, v);
+            const bf16* r8 = reinterpret_cast<const bf16*>(&rv[EM == E_BIAS_RES ? t : 0][EM == E_BIAS_RES ? c : 0][j]);
+            bf16x8 ob;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ob[i] = (bf16)(o[i] + (float)r8[i]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(&ob)[i];
+          } else {
+            uint32_t pk[2][2];   // bf16 pairs of quads ge, go
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              bf16x4 b4;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) b4[i] = (bf16)f[h ? go : ge][i];
+              pk[h][0] = reinterpret_cast<const uint32_t*>(&b4)[0];
+              pk[h][1] = reinterpret_cast<const uint32_t*>(&b4)[1];
+            }
+            const uint32_t s0 = fh ? pk[0][0] : pk[1][0];
+            const uint32_t s1 = fh ? pk[0][1] : pk[1][1];
+            const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32, 64);
+            const uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32, 64);
+            w[0] = fh ? r0 : pk[0][0];
+            w[1] = fh ? r1 : pk[0][1];
+            w[2] = fh ? pk[1][0] : r0;
+            w[3] = fh ? pk[1][1] : r1;
           }
+          if (m < p.M && n < p.N)
+            *reinterpret_cast<uint4*>(p.C + (size_t)m * p.ldc + n) = make_uint4(w[0], w[1], w[2], w[3]);
         }
+      }
     }
     if (next >= ntiles) break;
     tl = next;
@@ -330,8 +402,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
 
 namespace {
 
-template <int BM, int BN, int WM, int WN>
-hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, AMode am, EMode em, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, int AM, int EM>
+hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, hipStream_t s) {
   // One block per CU (the kernel holds 3 x (BM + BN) x 128 bytes of LDS); with
   // more tiles than CUs each block walks several tiles, and the grid stays a
   // multiple of 8 so that every XCD keeps its own contiguous tile range.
@@ -342,15 +414,7 @@ hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, AMode am, EMode em, hipStre
   const int ntiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int g8 = cus / 8 * 8;
   const int blocks = ntiles <= g8 ? ntiles : g8;
-  dim3 grid(blocks), block(64 * WM * WN);
-  if (am == A_PLAIN && em == E_BIAS)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_PLAIN, E_BIAS>), grid, block, 0, s, a, ntiles);
-  else if (am == A_PLAIN && em == E_BIAS_RELU)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_PLAIN, E_BIAS_RELU>), grid, block, 0, s, a, ntiles);
-  else if (am == A_CONV3 && em == E_BIAS)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, A_CONV3, E_BIAS>), grid, block, 0, s, a, ntiles);
-  else
-    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, AM, EM>), dim3(blocks), dim3(64 * WM * WN), 0, s, a, ntiles);
   return hipGetLastError();
 }
 
@@ -364,24 +428,36 @@ hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, AMode am, EMode em, hipStre
 // what the kernel handles; the caller then uses the register-staged GEMM.
 hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStream_t s) {
   if (EDIT_DMA_FORCE < 0) return hipErrorNotSupported;
-  if (am == A_GNACT || em == E_BIAS_RES) return hipErrorNotSupported;
-  // Measured on MI355X (random bf16 data, 16384 tokens): the three-stage
-  // ring pays off on the long K of the 3x3 conv (162 K steps: 132 us against
-  // 227 us for the register-staged kernel), while at K = 1152 (18 steps) the
-  // per-tile fill and epilogue dominate and the register-staged kernel with
-  // several blocks per CU is as fast or faster (63 us against 65-73 us for
-  // the C x C projection). Plain-A GEMMs therefore take this kernel only on
-  // request.
-  if (am == A_PLAIN && EDIT_DMA_FORCE != 1) return hipErrorNotSupported;
-  if (a.K % 64 != 0 || a.N % 8 != 0 || a.ldb % 8 != 0 || a.lda % 8 != 0 || a.ldc % 8 != 0)
+  if (a.K % 8 != 0 || a.N % 8 != 0 || a.ldb % 8 != 0 || a.lda % 8 != 0 || a.ldc % 8 != 0)
     return hipErrorNotSupported;
-  if (am == A_CONV3 && (a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin)) return hipErrorNotSupported;
   // Buffer offsets are 32-bit and must stay below the out-of-range marker.
   if ((size_t)a.M * a.lda * 2 >= kOob) return hipErrorNotSupported;
   if ((size_t)(a.N < a.seg_rows ? a.N : a.seg_rows) * a.ldb * 2 >= kOob) return hipErrorNotSupported;
-  if (a.N % 128 == 0 && a.seg_rows % 128 == 0 && EDIT_DMA_FORCE != 2)
-    return launch_dma_tiles<256, 128, 2, 2>(a, am, em, s);
-  if (a.N % 96 == 0 && a.seg_rows % 96 == 0) return launch_dma_tiles<256, 96, 4, 1>(a, am, em, s);
+  const bool n96 = a.N % 96 == 0 && a.seg_rows % 96 == 0, n128 = a.N % 128 == 0 && a.seg_rows % 128 == 0,
+             n192 = a.N % 192 == 0 && a.seg_rows % 192 == 0;
+  // Measured on MI355X (random bf16 data, 16384 tokens):
+  //  - the 3x3 conv (162 K steps): 119 us against 227 us for the register-staged kernel;
+  //  - plain-A projections at K = 1152: 61-64 us against 63 us register-staged, so those stay there
+  //    unless asked for.
+  if (am == A_CONV3 && em == E_BIAS) {
+    if (a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin) return hipErrorNotSupported;
+    if (n96) return launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_BIAS>(a, s);
+    if (n128) return launch_dma_tiles<256, 128, 2, 2, A_CONV3, E_BIAS>(a, s);
+    return hipErrorNotSupported;
+  }
+  if (am == A_PLAIN && em == E_BIAS_RES) {
+    // The ConvFusion restore (K = C/r, a few K steps, HBM-bound): 36 us at
+    // 16384 x 1152 x 288 against 55 us for the register-staged kernel with
+    // the GroupNorm producer fused.
+    if (a.ldr % 8 != 0) return hipErrorNotSupported;
+    if (n192) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS_RES>(a, s);
+    if (n128) return launch_dma_tiles<256, 128, 2, 2, A_PLAIN, E_BIAS_RES>(a, s);
+    return hipErrorNotSupported;
+  }
+  if (am == A_PLAIN && EDIT_DMA_FORCE == 1 && n128) {
+    if (em == E_BIAS) return launch_dma_tiles<256, 128, 2, 2, A_PLAIN, E_BIAS>(a, s);
+    if (em == E_BIAS_RELU) return launch_dma_tiles<256, 128, 2, 2, A_PLAIN, E_BIAS_RELU>(a, s);
+  }
   return hipErrorNotSupported;
 }
 

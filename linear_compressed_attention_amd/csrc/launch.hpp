@@ -59,6 +59,11 @@ hipError_t launch_groupnorm_stats(const T* x, int B, int HW, int C, int G, const
                                   float* stat, float* scale, float* shift, hipStream_t s);
 int groupnorm_chunks(int HW, int C);
 
+// a = LeakyReLU(x * scale[b] + shift[b], 0.01) elementwise over x [B][HW][C].
+template <typename T>
+hipError_t launch_groupnorm_apply(const T* x, int B, int HW, int C, const float* scale, const float* shift, T* a,
+                                  hipStream_t s);
+
 // Depthwise 3x3 stride-2 pad-1 conv of two channel groups side by side in
 // kv0 [B][H][W][2C]: keys (channels 0..C-1, then ReLU) and values (C..2C-1).
 template <typename T>

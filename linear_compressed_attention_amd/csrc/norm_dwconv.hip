@@ -177,6 +177,43 @@ hipError_t launch_groupnorm_stats(const T* x, int B, int HW, int C, int G, const
 }
 
 // ---------------------------------------------------------------------------
+// a = LeakyReLU(x * scale[b][c] + shift[b][c], 0.01): GroupNorm with its
+// affine folded into scale / shift, then the ConvFusion activation (section
+// "ConvFusion"), once per element, 8 channels per thread (16-byte accesses).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void gn_apply_kernel(const T* __restrict__ x, int HW, int C, size_t n8,
+                                                       const float* __restrict__ scale,
+                                                       const float* __restrict__ shift, T* __restrict__ a) {
+  const size_t i = (size_t)xcd_swizzle(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const size_t e = i * 8;                      // first element (C is a multiple of 8)
+  const size_t row = e / C;
+  const int c = (int)(e - row * C);
+  const int b = (int)(row / HW);
+  float v[8], sc[8], sh[8];
+  load8(x + e, v);
+  load8(scale + (size_t)b * C + c, sc);
+  load8(shift + (size_t)b * C + c, sh);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float t = v[k] * sc[k] + sh[k];
+    v[k] = t >= 0.0f ? t : 0.01f * t;
+  }
+  store8(a + e, v);
+}
+
+template <typename T>
+hipError_t launch_groupnorm_apply(const T* x, int B, int HW, int C, const float* scale, const float* shift, T* a,
+                                  hipStream_t s) {
+  const size_t n8 = (size_t)B * HW * C / 8;
+  if (n8 == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n8 + 255) / 256);
+  hipLaunchKernelGGL((gn_apply_kernel<T>), dim3(blocks), dim3(256), 0, s, x, HW, C, n8, scale, shift, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Depthwise 3x3, stride 2, zero pad 1 over kv0 [B][H][W][2C]: output pixel
 // (y', x') of channel c reads input (2y'+ky-1, 2x'+kx-1). One thread makes
 // 8 consecutive channels of one output pixel; consecutive threads walk the
@@ -240,6 +277,8 @@ hipError_t launch_dwconv_s2(const T* kv0, int B, int H, int W, int C, const T* d
 }
 
 #define EDIT_INST(T)                                                                                    \
+  template hipError_t launch_groupnorm_apply<T>(const T*, int, int, int, const float*, const float*, T*,  \
+                                                hipStream_t);                                           \
   template hipError_t launch_groupnorm_stats<T>(const T*, int, int, int, int, const T*, const T*, float, \
                                                 float*, int, float*, float*, float*, hipStream_t);      \
   template hipError_t launch_dwconv_s2<T>(const T*, int, int, int, int, const T*, const T*, const T*,    \

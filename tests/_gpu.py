@@ -37,6 +37,7 @@ def read_intermediates(shape, ws, n_text=0):
     out = {
         "xc": _view(ws, lay["xc"], (B, N, s.Cr), T),
         "gn_stat": _view(ws, lay["gn_stat"], (B, s.gn_groups, 2), f32),
+        "cf_act": _view(ws, lay["cf_act"], (B, N, s.Cr), T),
         "xt": _view(ws, lay["xt"], (B, N, C), T),
         "q": _view(ws, lay["q"], (B, N, C), T),
         "kv0": _view(ws, lay["kv0"], (B, N, 2 * C), T),
@@ -100,7 +101,8 @@ def oracle_views(tr, shape):
     import numpy as np
     rstd = 1.0 / np.sqrt(tr["gn_var"] + 1e-5)
     return {
-        "xc": tr["xc"], "gn_stat": np.stack([tr["gn_mean"], rstd], axis=-1), "xt": tr["xt"], "q": tr["q"],
+        "xc": tr["xc"], "gn_stat": np.stack([tr["gn_mean"], rstd], axis=-1), "cf_act": tr["cf_act"],
+        "xt": tr["xt"], "q": tr["q"],
         "kv0": np.concatenate([tr["k0"], tr["v0"]], axis=-1), "kc": tr["kc"], "vc": tr["vc"],
         "S": tr["S"], "z": tr["z"], "out": tr["out"],
     }

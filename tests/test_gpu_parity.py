@@ -70,6 +70,13 @@ SMALL = {
                                   dtype="bf16", x_std=1.0),
     "bf16_d128_conv128": make_shape(B=1, H=9, W=7, C=512, heads=4, head_dim=128, reduction=4, gn_groups=8,
                                     dtype="bf16", x_std=1.0),
+    # Token counts per sample that are multiples of 128, so the GroupNorm
+    # restore also runs on the direct-to-LDS kernel: K = C/r = 96 (one and a
+    # half K steps) and K = 288 (four and a half, the PixArt width).
+    "bf16_gnrestore_k96": make_shape(B=2, H=16, W=8, C=384, heads=4, head_dim=96, reduction=4, gn_groups=8,
+                                     dtype="bf16", x_std=1.0),
+    "bf16_gnrestore_k288": make_shape(B=1, H=16, W=16, C=1152, heads=16, head_dim=72, reduction=4, gn_groups=32,
+                                      dtype="bf16", x_std=1.0),
     "f32_1x1": make_shape(B=2, H=1, W=1, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
                           dtype="f32", x_std=1.0),
     "f32_1x5": make_shape(B=1, H=1, W=5, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
