@@ -282,7 +282,11 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
     for (int i = 0; i < 8; ++i) zr[s][i] = szp[s * 32 + g * 8 + i];
 
   const int tile0 = (blockIdx.x * 4 + wave) * TPW;
-  FragT bq[2][KS];
+  // Query fragments run PD tiles ahead of the matrix work (a ring of PD
+  // register sets, about 48 registers), so PD - 1 memory latencies overlap.
+  constexpr int QREG = KS * (int)sizeof(FragT) / 4;
+  constexpr int PD = 48 / QREG < 2 ? 2 : (48 / QREG > TPW ? TPW : 48 / QREG);
+  FragT bq[PD][KS];
   auto load_q = [&](FragT (&dst)[KS], int tile) {
     const int tok = tile * 16 + fr;
     const bool tv = tok < N;
@@ -294,12 +298,13 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
       else frag_zero(dst[s]);
     }
   };
-  load_q(bq[0], tile0);
+#pragma unroll
+  for (int tt = 0; tt < PD - 1; ++tt) load_q(bq[tt], tile0 + tt);
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int tile = tile0 + tt;
-    const int c = tt & 1;
-    if (tt + 1 < TPW) load_q(bq[c ^ 1], tile + 1);
+    const int c = tt % PD;
+    if (tt + PD - 1 < TPW) load_q(bq[(tt + PD - 1) % PD], tile + PD - 1);
     const int tok = tile * 16 + fr;
     float den = 0.0f;
 #pragma unroll

@@ -22,8 +22,9 @@
 //    position c ^ ((r >> 1) & 7). A DMA instruction fills 8 whole rows, so
 //    each lane fetches the chunk that belongs at its fixed LDS position.
 //  - 32x32x16 matrix-core steps with the weights as the first operand: an
-//    accumulator then holds 4 consecutive output channels of one token, which
-//    the epilogue writes to LDS as one 8-byte word before 16-byte row stores.
+//    accumulator then holds 4 consecutive output channels of one token. The
+//    epilogue pairs the quads of lanes l and l ^ 32 (v_permlane32_swap) so
+//    that every lane stores 8 consecutive channels with one 16-byte write.
 //  - One barrier per K step, placed before the last quarter of the step's
 //    matrix work: by then every wave holds that quarter's fragments in
 //    registers, so the stage can be refilled while the quarter runs.
@@ -52,6 +53,13 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));   // vmcnt(VM) expcnt(7) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// The value lane l ^ 32 holds: one v_permlane32_swap exchanges the two
+// halves of the wave (no LDS crossbar round trip).
+__device__ __forceinline__ uint32_t from_other_half(uint32_t v, bool upper) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return upper ? pr[0] : pr[1];
 }
 
 template <typename P>
@@ -350,7 +358,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float snd = fh ? f[ge][i] : f[go][i];
-              const float rcv = __shfl_xor(snd, 32, 64);
+              const float rcv = __uint_as_float(from_other_half(__float_as_uint(snd), fh));
               o[i] = fh ? rcv : f[ge][i];
               o[4 + i] = fh ? f[go][i] : rcv;
             }
@@ -372,8 +380,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
             }
             const uint32_t s0 = fh ? pk[0][0] : pk[1][0];
             const uint32_t s1 = fh ? pk[0][1] : pk[1][1];
-            const uint32_t r0 = (uint32_t)__shfl_xor((int)s0, 32, 64);
-            const uint32_t r1 = (uint32_t)__shfl_xor((int)s1, 32, 64);
+            const uint32_t r0 = from_other_half(s0, fh);
+            const uint32_t r1 = from_other_half(s1, fh);
             w[0] = fh ? r0 : pk[0][0];
             w[1] = fh ? r1 : pk[0][1];
             w[2] = fh ? pk[1][0] : r0;
@@ -437,8 +445,8 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
              n192 = a.N % 192 == 0 && a.seg_rows % 192 == 0;
   // Measured on MI355X (random bf16 data, 16384 tokens):
   //  - the 3x3 conv (162 K steps): 119 us against 227 us for the register-staged kernel;
-  //  - plain-A projections at K = 1152: 61-64 us against 63 us register-staged, so those stay there
-  //    unless asked for.
+  //  - plain-A projections, 16384 x 1152 x 1152: 52 us with 128 x 192 tiles (768 tiles, three per
+  //    CU) against 63 us register-staged; 16384 x 2304 x 1152: 105 us, as register-staged.
   if (am == A_CONV3 && em == E_BIAS) {
     if (a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin) return hipErrorNotSupported;
     if (n96) return launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_BIAS>(a, s);
@@ -453,6 +461,10 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
     if (n192) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS_RES>(a, s);
     if (n128) return launch_dma_tiles<256, 128, 2, 2, A_PLAIN, E_BIAS_RES>(a, s);
     return hipErrorNotSupported;
+  }
+  if (am == A_PLAIN && n192) {
+    if (em == E_BIAS) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS>(a, s);
+    if (em == E_BIAS_RELU) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS_RELU>(a, s);
   }
   if (am == A_PLAIN && EDIT_DMA_FORCE == 1 && n128) {
     if (em == E_BIAS) return launch_dma_tiles<256, 128, 2, 2, A_PLAIN, E_BIAS>(a, s);
