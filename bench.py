@@ -33,14 +33,16 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core (f32: vector/matrix fp32)
 
-STEP_NAMES = ["cf_conv3x3", "gn_stats", "cf_restore", "q_proj", "kv_proj", "sc_dwconv", "kv_state",
+STEP_NAMES = ["cf_conv3x3", "gn_stats", "cf_act", "q_proj", "kv_proj", "sc_dwconv", "kv_state",
               "linattn_apply", "out_proj"]
-STEP_KERNELS = {  # kernels launched per step (rocprofv3 names start with these)
-    "cf_conv3x3": "gemm_kernel<..., A_CONV3, E_BIAS>", "gn_stats": "gn_partial_kernel + gn_finalize_kernel",
-    "cf_restore": "gn_apply_kernel + gemm_dma_kernel<..., A_PLAIN, E_BIAS_RES>", "q_proj": "gemm_kernel<..., A_PLAIN, E_BIAS_RELU>",
-    "kv_proj": "gemm_kernel<..., A_PLAIN, E_BIAS>", "sc_dwconv": "dwconv_s2_kernel",
+STEP_KERNELS = {  # kernels launched per step at bf16 (rocprofv3 names start with these)
+    "cf_conv3x3": "gemm_dma_kernel<256, 96, 4, 1, A_CONV3, E_BIAS>",
+    "gn_stats": "gn_partial_kernel + gn_finalize_kernel",
+    "cf_act": "gn_apply_kernel + restore_fold_mfma_kernel",
+    "q_proj": "gemm_dma_kernel<128, 192, 2, 2, A_CAT2, E_BIAS_RELU>",
+    "kv_proj": "gemm_dma_kernel<128, 192, 2, 2, A_PLAIN, E_BIAS>", "sc_dwconv": "dwconv_s2_kernel",
     "kv_state": "kv_state_partial_kernel + kv_state_finalize_kernel", "linattn_apply": "linattn_apply_kernel",
-    "out_proj": "gemm_kernel<..., A_PLAIN, E_BIAS>",
+    "out_proj": "gemm_dma_kernel<128, 192, 2, 2, A_PLAIN, E_BIAS>",
 }
 
 
@@ -54,8 +56,11 @@ def algorithmic_work(s):
     return {
         "cf_conv3x3": (2.0 * M * Cr * 9 * C, es * (M * C + Cr * 9 * C + M * Cr + Cr)),
         "gn_stats": (3.0 * M * Cr, es * M * Cr),
-        "cf_restore": (2.0 * M * C * Cr, es * (M * Cr + 2 * M * C + C * Cr + C)),
-        "q_proj": (2.0 * M * C * C, es * (2 * M * C + C * C + C)),
+        # GN + LeakyReLU over xc; the fold [W_q | W_q W_cf2], b_q + W_q b_cf2
+        "cf_act": (3.0 * M * Cr + 2.0 * C * C * Cr,
+                   es * (2 * M * Cr + C * C + C * Cr + 2 * C + C * (C + Cr) + C)),
+        # ReLU([X | act] [W_q | W_q W_cf2]^T + b)
+        "q_proj": (2.0 * M * C * (C + Cr), es * (M * C + M * Cr + M * C + C * (C + Cr) + C)),
         "kv_proj": (2.0 * M * 2 * C * C, es * (M * C + 2 * M * C + 2 * C * C + 2 * C)),
         "sc_dwconv": (2.0 * 9 * Mc * 2 * C, es * (2 * M * C + 2 * Mc * C + 2 * 10 * C)),
         "kv_state": (2.0 * Mc * C * (d + 1), es * 2 * Mc * C + st),
@@ -110,7 +115,7 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
-STEP_BOUND = {"cf_conv3x3": "mfma", "gn_stats": "hbm", "cf_restore": "hbm", "q_proj": "mfma", "kv_proj": "mfma",
+STEP_BOUND = {"cf_conv3x3": "mfma", "gn_stats": "hbm", "cf_act": "hbm", "q_proj": "mfma", "kv_proj": "mfma",
               "sc_dwconv": "hbm", "kv_state": "hbm", "linattn_apply": "hbm", "out_proj": "mfma"}
 
 

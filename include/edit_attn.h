@@ -150,7 +150,10 @@ edit_status_t mmedit_hybrid_exact_forward(const edit_shape_t* shape, int n_text,
  *   xc      [B][N][C/r] T      ConvFusion 3x3 output
  *   gn_stat [B][G][2]   f32    GroupNorm mean and 1/sqrt(var + 1e-5)
  *   cf_act  [B][N][C/r] T      LeakyReLU(GN(xc)), the input of the 1x1 restore
- *   xt      [B][N][C]   T      X + Conv1x1(LeakyReLU(GN(xc)))
+ *   q_fold_w [C][C+C/r] T      [W_q | W_q W_cf2]: the 1x1 restore folded into the query
+ *   q_fold_b [C]        T      b_q + W_q b_cf2   Linear, so q = ReLU([X | cf_act] q_fold_w^T + q_fold_b)
+ *                              equals ReLU(Linear_Q(X + Conv1x1(cf_act))); the restored
+ *                              stream itself is never stored
  *   q       [B][N][C]   T      ConvFusion queries (after ReLU)
  *   kv0     [B][N][2C]  T      key Linear | value Linear, side by side per token
  *   kc, vc  [B][N'][C]  T      compressed keys (ReLU'd) and values, N' = ceil(H/2)*ceil(W/2)
@@ -161,14 +164,16 @@ edit_status_t mmedit_hybrid_exact_forward(const edit_shape_t* shape, int n_text,
  *   y_img   [B][N][C]   T      blended image rows (hybrid with text only)
  *   y_txt   [B][N_T][C] T      text rows before the text output Linear (hybrid only)
  *   lin_den [B][N][h]   f32    q . z + eps per token and head (exact-eta hybrid only)
- *   xc_k, gn_stat_k, xt_k      the key branch's ConvFusion (EDIT_KV_KEY_CONVFUSION only)
+ *   xc_k, gn_stat_k, cf_act_k, k_fold_w, k_fold_b
+ *                              the key branch's ConvFusion, its restore folded into
+ *                              W_k (EDIT_KV_KEY_CONVFUSION only)
  * For the ablation variants (edit_attn_variant_forward): q holds the variant's
  * queries; with uncompressed keys kv0 holds ReLU(key Linear) | value Linear
- * and the sums S, z run over all N tokens; kc, vc (and xc, gn_stat, xt with
- * a plain query) are not produced. */
+ * and the sums S, z run over all N tokens; kc, vc (and xc, gn_stat, cf_act,
+ * q_fold_w, q_fold_b with a plain query) are not produced. */
 typedef struct {
-  size_t xc, gn_stat, cf_act, xt, q, kv0, kc, vc, S, z, y, qkv_t, y_img, y_txt, lin_den;
-  size_t xc_k, gn_stat_k, xt_k;
+  size_t xc, gn_stat, cf_act, q_fold_w, q_fold_b, q, kv0, kc, vc, S, z, y, qkv_t, y_img, y_txt, lin_den;
+  size_t xc_k, gn_stat_k, cf_act_k, k_fold_w, k_fold_b;
   size_t total;
 } edit_ws_layout_t;
 
@@ -218,8 +223,8 @@ edit_status_t edit_attn_variant_forward(const edit_shape_t* shape, const edit_va
 typedef enum {
   EDIT_STEP_CF_CONV3X3 = 0,  /* ConvFusion 3x3 compressing conv             (1 kernel)  */
   EDIT_STEP_GN_STATS = 1,    /* GroupNorm statistics                         (2 kernels) */
-  EDIT_STEP_CF_RESTORE = 2,  /* GN + LeakyReLU, then 1x1 restore + residual  (2 kernels) */
-  EDIT_STEP_Q_PROJ = 3,      /* query Linear + ReLU                          (1 kernel)  */
+  EDIT_STEP_CF_ACT = 2,      /* GN + LeakyReLU; 1x1 restore folded into W_q (2 kernels) */
+  EDIT_STEP_Q_PROJ = 3,      /* query Linear over [X | act] + ReLU           (1 kernel)  */
   EDIT_STEP_KV_PROJ = 4,     /* key and value Linears                        (1 kernel)  */
   EDIT_STEP_SC_DWCONV = 5,   /* depthwise 3x3 stride 2, ReLU on keys          (1 kernel)  */
   EDIT_STEP_KV_STATE = 6,    /* S = K'^T V', z = sum K' per head             (2 kernels) */

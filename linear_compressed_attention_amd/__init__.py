@@ -33,8 +33,8 @@ _STATUS = {0: "EDIT_OK", 1: "EDIT_ERR_ARG", 2: "EDIT_ERR_UNSUPPORTED", 3: "EDIT_
 IMAGE_WEIGHT_FIELDS = ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2", "w_q", "b_q", "w_k", "b_k",
                        "w_v", "b_v", "dw_k", "db_k", "dw_v", "db_v", "w_o", "b_o")
 TEXT_WEIGHT_FIELDS = ("w_q", "b_q", "w_k", "b_k", "w_v", "b_v", "w_o", "b_o")
-LAYOUT_FIELDS = ("xc", "gn_stat", "cf_act", "xt", "q", "kv0", "kc", "vc", "S", "z", "y", "qkv_t", "y_img", "y_txt", "lin_den",
-                 "xc_k", "gn_stat_k", "xt_k", "total")
+LAYOUT_FIELDS = ("xc", "gn_stat", "cf_act", "q_fold_w", "q_fold_b", "q", "kv0", "kc", "vc", "S", "z", "y", "qkv_t",
+                 "y_img", "y_txt", "lin_den", "xc_k", "gn_stat_k", "cf_act_k", "k_fold_w", "k_fold_b", "total")
 QUERY_MODES = {"convfusion": 0, "linear": 1}                      # edit_query_mode_t
 KV_MODES = {"compressed": 0, "full": 1, "key_convfusion": 2}      # edit_kv_mode_t
 KEY_CONVFUSION_FIELDS = ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2")

@@ -6,8 +6,10 @@
 //   section "ConvFusion":
 //     1 gemm A_CONV3      xc  = Conv3x3(x) + b_cf1               (C -> C/r)
 //     2 groupnorm stats   per (b, group) mean / rstd -> scale, shift
-//     3 gn apply, gemm    act = LeakyReLU(GN(xc)); xt = x + act W_cf2^T + b_cf2
-//     4 gemm relu         q   = ReLU(xt W_q^T + b_q)
+//     3 gn apply, fold    act = LeakyReLU(GN(xc)); wcat = [W_q | W_q W_cf2],
+//                         bcat = b_q + W_q b_cf2 (the 1x1 restore folded into W_q)
+//     4 gemm A_CAT2 relu  q   = ReLU([x | act] wcat^T + bcat)
+//                             = ReLU((x + act W_cf2^T + b_cf2) W_q^T + b_q)
 //   section "Spatial Compressor":
 //     5 gemm (2 segments) kv0 = [x W_k^T + b_k | x W_v^T + b_v]
 //     6 dwconv_s2         kc  = ReLU(DW(k0)), vc = DW(v0)
@@ -26,6 +28,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/edit_attn.h"
 #include "launch.hpp"
@@ -57,9 +60,10 @@ struct Geometry {
 };
 
 struct Layout {
-  size_t xc, gn_part, gn_stat, gn_scale, gn_shift, cf_act, xt, q, kv0, kc, vc, kv_part, S, z, st, zp, y;
+  size_t xc, gn_part, gn_stat, gn_scale, gn_shift, cf_act, q_fold_w, q_fold_b, q, kv0, kc, vc, kv_part, S, z, st,
+      zp, y;
   size_t qkv_t, y_img, y_txt, lin_den;
-  size_t xc_k, gn_part_k, gn_stat_k, gn_scale_k, gn_shift_k, cf_act_k, xt_k;   // key ConvFusion branch
+  size_t xc_k, gn_part_k, gn_stat_k, gn_scale_k, gn_shift_k, cf_act_k, k_fold_w, k_fold_b;   // key ConvFusion branch
   size_t total;
 };
 
@@ -127,7 +131,8 @@ Layout make_layout(const Geometry& g) {
     L.gn_scale = take((size_t)g.B * g.Cr * 4);
     L.gn_shift = take((size_t)g.B * g.Cr * 4);
     L.cf_act = take(M * g.Cr * es);
-    L.xt = take(M * g.C * es);
+    L.q_fold_w = take((size_t)g.C * (g.C + g.Cr) * es);
+    L.q_fold_b = take((size_t)g.C * es);
   }
   L.q = take(M * g.C * es);
   L.kv0 = take(M * 2 * g.C * es);
@@ -142,7 +147,8 @@ Layout make_layout(const Geometry& g) {
     L.gn_scale_k = take((size_t)g.B * g.Cr * 4);
     L.gn_shift_k = take((size_t)g.B * g.Cr * 4);
     L.cf_act_k = take(M * g.Cr * es);
-    L.xt_k = take(M * g.C * es);
+    L.k_fold_w = take((size_t)g.C * (g.C + g.Cr) * es);
+    L.k_fold_b = take((size_t)g.C * es);
   }
   L.kv_part = take(BH * g.kv_chunks * (16 * g.DR) * (16 * g.DT) * 4);
   L.S = take(BH * g.d * g.d * 4);
@@ -247,12 +253,15 @@ struct Marks {
   }
 };
 
-// ConvFusion of x up to the restored stream: xt = x + Conv1x1(LeakyReLU(GN(Conv3x3(x)))).
+// ConvFusion of x up to the restore: act = LeakyReLU(GN(Conv3x3(x))). The 1x1
+// restore is folded into the Linear (w_lin, b_lin) that reads the restored
+// stream x + act W_cf2^T + b_cf2: wcat = [w_lin | w_lin W_cf2],
+// bcat = b_lin + w_lin b_cf2, for one GEMM over [x | act] (cat_linear).
 template <typename T>
 edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const void* b_cf1, const void* gamma,
-                         const void* beta, const void* w_cf2, const void* b_cf2, T* xc, float* gn_part,
-                         float* gn_stat, float* gn_scale, float* gn_shift, T* act, T* xt, hipStream_t s,
-                         const Marks& mk) {
+                         const void* beta, const void* w_cf2, const void* b_cf2, const void* w_lin,
+                         const void* b_lin, T* xc, float* gn_part, float* gn_stat, float* gn_scale, float* gn_shift,
+                         T* act, T* wcat, T* bcat, hipStream_t s, const Marks& mk) {
   using namespace edit;
   GemmArgs<T> a{};
   EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_CONV3X3));
@@ -267,24 +276,38 @@ edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const
   EDIT_LAUNCH(launch_groupnorm_stats<T>(xc, g.B, g.N, g.Cr, g.G, static_cast<const T*>(gamma),
                                         static_cast<const T*>(beta), 1e-5f, gn_part, g.gn_chunks, gn_stat,
                                         gn_scale, gn_shift, s));
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_RESTORE));
-  // act = LeakyReLU(GN(xc)); xt = x + act W_cf2^T + b_cf2
+  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_ACT));
+  // act = LeakyReLU(GN(xc)); the restore folded into the Linear's weights
   EDIT_LAUNCH(launch_groupnorm_apply<T>(xc, g.B, g.N, g.Cr, gn_scale, gn_shift, act, s));
-  a = GemmArgs<T>{};
-  a.M = g.M; a.N = g.C; a.K = g.Cr; a.A = act; a.lda = g.Cr;
-  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w_cf2);
-  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(b_cf2);
-  a.seg_rows = g.C; a.ldb = g.Cr; a.C = xt; a.ldc = g.C; a.R = x; a.ldr = g.C;
-  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS_RES, s));
+  EDIT_LAUNCH(launch_restore_fold<T>(static_cast<const T*>(w_lin), static_cast<const T*>(b_lin),
+                                     static_cast<const T*>(w_cf2), static_cast<const T*>(b_cf2), g.C, g.Cr, wcat,
+                                     bcat, s));
+  return EDIT_OK;
+}
+
+// out = [x | act] wcat^T + bcat (+ ReLU), row stride ldc: the Linear of the
+// restored stream x + ConvFusion(x) with the restore folded in.
+template <typename T>
+edit_status_t cat_linear(const Geometry& g, const T* x, const T* act, const T* wcat, const T* bcat, T* out, int ldc,
+                         bool spread, hipStream_t s) {
+  using namespace edit;
+  GemmArgs<T> a{};
+  a.spread = spread;
+  a.M = g.M; a.N = g.C; a.K = g.C + g.Cr; a.A = x; a.lda = g.C; a.A2 = act; a.lda2 = g.Cr; a.K1 = g.C;
+  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = wcat;
+  a.bias[0] = a.bias[1] = a.bias[2] = bcat;
+  a.seg_rows = g.C; a.ldb = g.C + g.Cr; a.C = out; a.ldc = ldc;
+  EDIT_LAUNCH(launch_gemm<T>(a, A_CAT2, E_BIAS_RELU, s));
   return EDIT_OK;
 }
 
 // out[m][0..C) = epilogue(a[m] W^T + b) with row stride ldc.
 template <typename T>
 edit_status_t linear_cc(const Geometry& g, const T* a_in, const void* w, const void* b, T* out, int ldc, bool relu,
-                        hipStream_t s) {
+                        bool spread, hipStream_t s) {
   using namespace edit;
   GemmArgs<T> a{};
+  a.spread = spread;
   a.M = g.M; a.N = g.C; a.K = g.C; a.A = a_in; a.lda = g.C;
   a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w);
   a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(b);
@@ -293,8 +316,40 @@ edit_status_t linear_cc(const Geometry& g, const T* a_in, const void* w, const v
   return EDIT_OK;
 }
 
+// A second stream per device for the key/value branch, and the events that
+// fork it from the caller's stream and join it back. Created on first use,
+// kept for the life of the process; g_side_mu serialises the enqueue of a
+// fork .. join section, so that concurrent callers do not interleave records
+// of the shared events.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+SideStream g_side[64];
+
+edit_status_t side_stream(SideStream** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) return fail(EDIT_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess)
+      return fail(EDIT_ERR_HIP, "creating the key/value stream failed: %s", hipGetErrorString(e));
+  }
+  *out = &ss;
+  return EDIT_OK;
+}
+
 // The image stream up to the linear-attention output y (steps 1-8 of the
 // layer; the ablation variants swap the query or the key/value processing).
+// The query branch (steps 1-4) and the key/value branch (steps 5-7) only
+// meet at step 8. Without per-step events the key/value branch runs on a
+// second stream, so its kernels take the CUs the query branch leaves idle
+// (the 3x3 conv has C/r / 96 x M / 256 tiles, 192 at 16384 tokens, fewer
+// than the CUs); with them every step runs in order on the caller's stream.
 template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
                         hipStream_t s, const Marks& mk, float* lin_den = nullptr,
@@ -302,54 +357,86 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
   using namespace edit;
   auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  edit_status_t st;
-  // 1-4. queries: q = ReLU(xt W_q^T + b_q), xt = x + ConvFusion(x) (or x itself)
-  const T* qin = x;
-  if (g.qmode == EDIT_QUERY_CONVFUSION) {
-    st = convfusion<T>(g, x, w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, P(L.xc),
-                       F(L.gn_part), F(L.gn_stat), F(L.gn_scale), F(L.gn_shift), P(L.cf_act), P(L.xt), s, mk);
-    if (st != EDIT_OK) return st;
-    qin = P(L.xt);
-  }
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_Q_PROJ));
-  if ((st = linear_cc<T>(g, qin, w->w_q, w->b_q, P(L.q), g.C, true, s)) != EDIT_OK) return st;
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_PROJ));
-  const T *kk, *vv;
-  int ldkv;
-  if (g.kvmode == EDIT_KV_COMPRESSED) {
-    // 5. kv0 = [x W_k^T + b_k | x W_v^T + b_v]
-    GemmArgs<T> a{};
-    a.M = g.M; a.N = 2 * g.C; a.K = g.C; a.A = x; a.lda = g.C;
-    a.Bseg[0] = static_cast<const T*>(w->w_k); a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_v);
-    a.bias[0] = static_cast<const T*>(w->b_k); a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_v);
-    a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.kv0); a.ldc = 2 * g.C;
-    EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
-    EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
-    // 6. compressed keys / values
-    EDIT_LAUNCH(launch_dwconv_s2<T>(P(L.kv0), g.B, g.H, g.W, g.C, static_cast<const T*>(w->dw_k),
-                                    static_cast<const T*>(w->db_k), static_cast<const T*>(w->dw_v),
-                                    static_cast<const T*>(w->db_v), P(L.kc), P(L.vc), s));
-    kk = P(L.kc); vv = P(L.vc); ldkv = g.C;
-  } else {
-    // Uncompressed keys and values side by side in kv0: K = ReLU(kin W_k^T + b_k), V = x W_v^T + b_v,
-    // with kin = x or, for ConvFusion keys, x + ConvFusion_K(x).
-    const T* kin = x;
-    if (g.kvmode == EDIT_KV_KEY_CONVFUSION) {
-      st = convfusion<T>(g, x, kcf->w_cf1, kcf->b_cf1, kcf->gn_gamma, kcf->gn_beta, kcf->w_cf2, kcf->b_cf2,
-                         P(L.xc_k), F(L.gn_part_k), F(L.gn_stat_k), F(L.gn_scale_k), F(L.gn_shift_k), P(L.cf_act_k),
-                         P(L.xt_k), s, Marks{nullptr, s});
+  const bool fork = mk.ev == nullptr;
+
+  // 1-4. queries: q = ReLU((x + ConvFusion(x)) W_q^T + b_q), or ReLU(x W_q^T + b_q)
+  auto query_branch = [&](hipStream_t qs) -> edit_status_t {
+    edit_status_t st;
+    if (g.qmode == EDIT_QUERY_CONVFUSION) {
+      st = convfusion<T>(g, x, w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, w->w_q, w->b_q,
+                         P(L.xc), F(L.gn_part), F(L.gn_stat), F(L.gn_scale), F(L.gn_shift), P(L.cf_act),
+                         P(L.q_fold_w), P(L.q_fold_b), qs, mk);
       if (st != EDIT_OK) return st;
-      kin = P(L.xt_k);
+      EDIT_LAUNCH(mk.mark(EDIT_STEP_Q_PROJ));
+      return cat_linear<T>(g, x, P(L.cf_act), P(L.q_fold_w), P(L.q_fold_b), P(L.q), g.C, fork, qs);
     }
-    if ((st = linear_cc<T>(g, kin, w->w_k, w->b_k, P(L.kv0), 2 * g.C, true, s)) != EDIT_OK) return st;
-    if ((st = linear_cc<T>(g, x, w->w_v, w->b_v, P(L.kv0) + g.C, 2 * g.C, false, s)) != EDIT_OK) return st;
-    EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
-    kk = P(L.kv0); vv = P(L.kv0) + g.C; ldkv = 2 * g.C;
+    EDIT_LAUNCH(mk.mark(EDIT_STEP_Q_PROJ));
+    return linear_cc<T>(g, x, w->w_q, w->b_q, P(L.q), g.C, true, fork, qs);
+  };
+  // 5-7. keys, values and the per-head state S, z
+  auto kv_branch = [&](hipStream_t ks) -> edit_status_t {
+    edit_status_t st;
+    EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_PROJ));
+    const T *kk, *vv;
+    int ldkv;
+    if (g.kvmode == EDIT_KV_COMPRESSED) {
+      // 5. kv0 = [x W_k^T + b_k | x W_v^T + b_v]
+      GemmArgs<T> a{};
+      a.M = g.M; a.N = 2 * g.C; a.K = g.C; a.A = x; a.lda = g.C;
+      a.Bseg[0] = static_cast<const T*>(w->w_k); a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w->w_v);
+      a.bias[0] = static_cast<const T*>(w->b_k); a.bias[1] = a.bias[2] = static_cast<const T*>(w->b_v);
+      a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.kv0); a.ldc = 2 * g.C; a.spread = fork;
+      EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, ks));
+      EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
+      // 6. compressed keys / values
+      EDIT_LAUNCH(launch_dwconv_s2<T>(P(L.kv0), g.B, g.H, g.W, g.C, static_cast<const T*>(w->dw_k),
+                                      static_cast<const T*>(w->db_k), static_cast<const T*>(w->dw_v),
+                                      static_cast<const T*>(w->db_v), P(L.kc), P(L.vc), ks));
+      kk = P(L.kc); vv = P(L.vc); ldkv = g.C;
+    } else {
+      // Uncompressed keys and values side by side in kv0: K = ReLU(kin W_k^T + b_k), V = x W_v^T + b_v,
+      // with kin = x or, for ConvFusion keys, x + ConvFusion_K(x) (its restore folded into W_k).
+      if (g.kvmode == EDIT_KV_KEY_CONVFUSION) {
+        st = convfusion<T>(g, x, kcf->w_cf1, kcf->b_cf1, kcf->gn_gamma, kcf->gn_beta, kcf->w_cf2, kcf->b_cf2,
+                           w->w_k, w->b_k, P(L.xc_k), F(L.gn_part_k), F(L.gn_stat_k), F(L.gn_scale_k),
+                           F(L.gn_shift_k), P(L.cf_act_k), P(L.k_fold_w), P(L.k_fold_b), ks, Marks{nullptr, ks});
+        if (st != EDIT_OK) return st;
+        st = cat_linear<T>(g, x, P(L.cf_act_k), P(L.k_fold_w), P(L.k_fold_b), P(L.kv0), 2 * g.C, fork, ks);
+      } else {
+        st = linear_cc<T>(g, x, w->w_k, w->b_k, P(L.kv0), 2 * g.C, true, fork, ks);
+      }
+      if (st != EDIT_OK) return st;
+      if ((st = linear_cc<T>(g, x, w->w_v, w->b_v, P(L.kv0) + g.C, 2 * g.C, false, fork, ks)) != EDIT_OK) return st;
+      EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
+      kk = P(L.kv0); vv = P(L.kv0) + g.C; ldkv = 2 * g.C;
+    }
+    EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_STATE));
+    // 7. per-head state
+    EDIT_LAUNCH(launch_kv_state<T>(kk, vv, ldkv, g.B, g.Nkv, g.heads, g.d, F(L.kv_part), g.kv_chunks, F(L.S),
+                                   F(L.z), P(L.st), F(L.zp), ks));
+    return EDIT_OK;
+  };
+
+  edit_status_t st;
+  if (!fork) {
+    if ((st = query_branch(s)) != EDIT_OK) return st;
+    if ((st = kv_branch(s)) != EDIT_OK) return st;
+  } else {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* side;
+    if ((st = side_stream(&side)) != EDIT_OK) return st;
+    EDIT_LAUNCH(hipEventRecord(side->fork, s));
+    EDIT_LAUNCH(hipStreamWaitEvent(side->s, side->fork, 0));
+    // The longer (query) branch is queued first, so its conv takes its CUs first.
+    st = query_branch(s);
+    const edit_status_t st2 = st == EDIT_OK ? kv_branch(side->s) : st;
+    // Join even after a failed launch, so the caller's stream never runs ahead of queued side work.
+    const hipError_t e1 = hipEventRecord(side->join, side->s);
+    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(s, side->join, 0) : e1;
+    if (st != EDIT_OK) return st;
+    if (st2 != EDIT_OK) return st2;
+    if (e2 != hipSuccess) return fail(EDIT_ERR_HIP, "joining the key/value stream failed: %s", hipGetErrorString(e2));
   }
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_STATE));
-  // 7. per-head state
-  EDIT_LAUNCH(launch_kv_state<T>(kk, vv, ldkv, g.B, g.Nkv, g.heads, g.d, F(L.kv_part), g.kv_chunks, F(L.S),
-                                 F(L.z), P(L.st), F(L.zp), s));
   EDIT_LAUNCH(mk.mark(EDIT_STEP_APPLY));
   // 8. y = q S / (q . z + eps)
   EDIT_LAUNCH(launch_linattn_apply<T>(P(L.q), g.C, P(L.st), F(L.zp), g.B, g.N, g.heads, g.d, g.eps, P(L.y), g.C,
@@ -449,10 +536,12 @@ size_t mmedit_hybrid_workspace_size(const edit_shape_t* shape, int n_text) {
 }
 
 static void export_layout(const Layout& L, edit_ws_layout_t* out) {
-  out->xc = L.xc; out->gn_stat = L.gn_stat; out->cf_act = L.cf_act; out->xt = L.xt; out->q = L.q; out->kv0 = L.kv0;
+  out->xc = L.xc; out->gn_stat = L.gn_stat; out->cf_act = L.cf_act; out->q_fold_w = L.q_fold_w;
+  out->q_fold_b = L.q_fold_b; out->q = L.q; out->kv0 = L.kv0;
   out->kc = L.kc; out->vc = L.vc; out->S = L.S; out->z = L.z; out->y = L.y;
   out->qkv_t = L.qkv_t; out->y_img = L.y_img; out->y_txt = L.y_txt; out->lin_den = L.lin_den;
-  out->xc_k = L.xc_k; out->gn_stat_k = L.gn_stat_k; out->xt_k = L.xt_k;
+  out->xc_k = L.xc_k; out->gn_stat_k = L.gn_stat_k; out->cf_act_k = L.cf_act_k; out->k_fold_w = L.k_fold_w;
+  out->k_fold_b = L.k_fold_b;
   out->total = L.total;
 }
 

@@ -1,13 +1,14 @@
 // MFMA GEMM for gfx950: C[M][N] = A[M][K] * B[N][K]^T with fused A-operand
-// producers (plain rows, implicit 3x3 convolution, GroupNorm + LeakyReLU)
-// and fused epilogues (bias, ReLU, residual).
+// producers (plain rows, implicit 3x3 convolution, two row sources side by
+// side) and fused epilogues (bias, ReLU).
 //
 // Serves the dense steps of the EDiT layer ("EDiT: Efficient Diffusion
 // Transformers with Linear Compressed Attention" notes): the ConvFusion 3x3
-// compressing conv and its 1x1 restore with the residual (section
-// "ConvFusion"), the query, key and value Linears (sections "ConvFusion" and
-// "Spatial Compressor"), the output Linear and the hybrid's text Linears
-// (section "MM-EDiT").
+// compressing conv, the query Linear over [X | act] with the 1x1 restore
+// folded into its weights (section "ConvFusion"), the key and value Linears
+// (section "Spatial Compressor"), the output Linear and the hybrid's text
+// Linears (section "MM-EDiT"). Used for fp32 and for bf16 shapes outside the
+// direct-to-LDS kernel's range.
 //
 // Tiling: 256 threads = 4 waves in a WM x WN grid; a block tile BM x BN,
 // K in steps of 128 bytes per row (64 bf16 / 32 f32). Tiles pass through
@@ -75,7 +76,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
 
   // Per-row state of the A producer.
   const T* arow[APASS];
-  int ay[APASS], ax[APASS], ab[APASS];
+  const T* arow2[AM == A_CAT2 ? APASS : 1];
+  int ay[APASS], ax[APASS];
   bool aval[APASS];
 #pragma unroll
   for (int j = 0; j < APASS; ++j) {
@@ -84,17 +86,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
     aval[j] = (BM % RPP == 0 || r < BM) && m < p.M;
     const int mm = aval[j] ? m : 0;
     arow[j] = p.A + (size_t)mm * p.lda;
+    if (AM == A_CAT2) arow2[AM == A_CAT2 ? j : 0] = p.A2 + (size_t)mm * p.lda2;
     if (AM == A_CONV3) {
       const int hw = p.H * p.W;
       const int q = mm % hw;
       ay[j] = q / p.W;
       ax[j] = q % p.W;
-      ab[j] = 0;
-    } else if (AM == A_GNACT) {
-      ab[j] = mm / p.rows_per_batch;
-      ay[j] = ax[j] = 0;
     } else {
-      ay[j] = ax[j] = ab[j] = 0;
+      ay[j] = ax[j] = 0;
     }
   }
   const T* brow[BPASS];
@@ -146,9 +145,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
         RA[j] = *reinterpret_cast<const u32x4*>(src);                                         \
       }                                                                                       \
     } else {                                                                                  \
+      /* A_CAT2: a 16-byte chunk lies in one source (K1 is a multiple of 8) */                \
+      const bool sec = AM == A_CAT2 && k >= p.K1;                                             \
       _Pragma("unroll") for (int j = 0; j < APASS; ++j) {                                     \
         AOK[j] = aval[j] && kin;                                                              \
-        RA[j] = *reinterpret_cast<const u32x4*>(arow[j] + (AOK[j] ? k : 0));                  \
+        const T* src = sec ? arow2[AM == A_CAT2 ? j : 0] + (AOK[j] ? k - p.K1 : 0)             \
+                           : arow[j] + (AOK[j] ? k : 0);                                      \
+        RA[j] = *reinterpret_cast<const u32x4*>(src);                                         \
       }                                                                                       \
     }                                                                                         \
     _Pragma("unroll") for (int j = 0; j < BPASS; ++j) {                                       \
@@ -164,21 +167,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
     _Pragma("unroll") for (int j = 0; j < APASS; ++j) {                                       \
       const int r = rr + RPP * j;                                                             \
       if (BM % RPP != 0 && r >= BM) continue;                                                 \
-      u32x4 v = AOK[j] ? RA[j] : zero4;                                                       \
-      if (AM == A_GNACT && AOK[j]) {                                                          \
-        const int k = (k0_) + cc * EPC;                                                       \
-        const T* e = reinterpret_cast<const T*>(&v);                                          \
-        T o[EPC];                                                                             \
-        const float* sc = p.scale + (size_t)ab[j] * p.K + k;                                  \
-        const float* sh = p.shift + (size_t)ab[j] * p.K + k;                                  \
-        _Pragma("unroll") for (int i = 0; i < EPC; ++i) {                                     \
-          float t = to_f32(e[i]) * sc[i] + sh[i];                                             \
-          t = t >= 0.0f ? t : 0.01f * t;                                                      \
-          o[i] = from_f32<T>(t);                                                              \
-        }                                                                                     \
-        v = *reinterpret_cast<const u32x4*>(o);                                               \
-      }                                                                                       \
-      *reinterpret_cast<u32x4*>(a_ + r * ROW + ccs * EPC) = v;                                \
+      *reinterpret_cast<u32x4*>(a_ + r * ROW + ccs * EPC) = AOK[j] ? RA[j] : zero4;           \
     }                                                                                         \
     _Pragma("unroll") for (int j = 0; j < BPASS; ++j) {                                       \
       const int r = rr + RPP * j;                                                             \
@@ -278,7 +267,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
 #undef EDIT_STORE_TILES
 
   // Epilogue, KG wave-rows at a time: accumulators -> LDS (fp32) ->
-  // bias / ReLU / residual -> 16-byte row stores.
+  // bias / ReLU -> 16-byte row stores.
   float* Cs = reinterpret_cast<float*>(smem);
   constexpr int CPR = BN / 8;   // 8-column groups per row
 #pragma unroll 1
@@ -309,11 +298,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
       if (EM == E_BIAS_RELU) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = v[i] > 0.0f ? v[i] : 0.0f;
-      } else if (EM == E_BIAS_RES) {
-        float rv[8];
-        load8(p.R + (size_t)m * p.ldr + n, rv);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] += rv[i];
       }
       store8(p.C + (size_t)m * p.ldc + n, v);
     }
@@ -332,9 +316,8 @@ static hipError_t launch_tiles(const GemmArgs<T>& a, AMode am, EMode em, hipStre
   }
   EDIT_GEMM_CASE(A_PLAIN, E_BIAS)
   EDIT_GEMM_CASE(A_PLAIN, E_BIAS_RELU)
-  EDIT_GEMM_CASE(A_PLAIN, E_BIAS_RES)
   EDIT_GEMM_CASE(A_CONV3, E_BIAS)
-  EDIT_GEMM_CASE(A_GNACT, E_BIAS_RES)
+  EDIT_GEMM_CASE(A_CAT2, E_BIAS_RELU)
 #undef EDIT_GEMM_CASE
   return hipErrorInvalidValue;
 }
@@ -360,7 +343,7 @@ hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s) 
   // Tile choice (measured on MI355X at the 16384-token shapes; the loop is
   // bound by LDS traffic and latency, not by the matrix cores, so the
   // 16x16x32 step with its smaller fragments measures slightly ahead):
-  //  - N a multiple of 128 (the C x C and 2C x C projections, the 1x1 restore):
+  //  - N a multiple of 128 (the C x C and 2C x C projections):
   //    128 x 128 tiles, one LDS stage, 2 x 2 waves of 64 x 64;
   //  - otherwise (the C/r-wide 3x3 conv, 96 | N): 128 x 96 tiles, two stages,
   //    2 x 2 waves of 64 x 48 on the 16x16x32 step (48 does not split into

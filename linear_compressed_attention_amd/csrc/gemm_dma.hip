@@ -1,20 +1,29 @@
 // MFMA GEMM for gfx950 with direct global-to-LDS tile loads:
 // C[M][N] = A[M][K] * B[N][K]^T (+ bias, optional ReLU), bf16 in and out,
-// fp32 accumulation, optional residual. A is either plain rows or an implicit
-// 3x3 stride-1 pad-1 convolution over a channels-last image.
+// fp32 accumulation. A is plain rows, two row sources side by side along K,
+// or an implicit 3x3 stride-1 pad-1 convolution over a channels-last image.
 //
 // Serves the dense steps of the EDiT layer ("EDiT: Efficient Diffusion
 // Transformers with Linear Compressed Attention" notes): the ConvFusion 3x3
-// compressing conv (section "ConvFusion"), the query, key and value Linears
-// (sections "ConvFusion" and "Spatial Compressor"), the output Linear and
-// the hybrid's text Linears (section "MM-EDiT").
+// compressing conv, the query Linear over [X | act] with the 1x1 restore
+// folded into its weights (section "ConvFusion"), the key and value Linears
+// (section "Spatial Compressor"), the output Linear and the hybrid's text
+// Linears (section "MM-EDiT").
 //
-// Design (one 4-wave block per CU, 144 KB of LDS):
+// Design (4-wave blocks):
 //  - Tiles move from HBM/L2 straight into LDS with buffer_load ... lds (16
-//    bytes per lane, no register round trip), through a ring of three stages
-//    held in three distinct LDS arrays, so that the compiler can tell which
-//    stage a fragment read touches and waits only for that stage's loads.
-//    Two K steps are in flight while a third is multiplied.
+//    bytes per lane, no register round trip), through a ring of ST stages
+//    held in distinct LDS arrays, so that the compiler can tell which stage
+//    a fragment read touches and waits only for that stage's loads.
+//  - ST = 3 (one block per CU, up to 160 KB): two K steps are in flight
+//    while a third is multiplied; the block walks several tiles and queues
+//    the next tile's first steps before it writes the current one.
+//  - ST = 2 (two blocks per CU, at most 80 KB each, one block per tile):
+//    one K step is in flight while the other is multiplied, and the CU's
+//    second block covers the wait, the prologue and the epilogue, so every
+//    SIMD runs two waves. Measured on MI355X with 128 x 192 tiles: 46 us
+//    against 53 us (three stages, persistent) at 16384 x 1152 x 1152,
+//    91 against 110 us at 16384 x 2304 x 1152.
 //  - Out-of-range rows, and the zero padding of the convolution, read at an
 //    offset beyond the buffer resource: the hardware returns zeros, so the
 //    loads never branch.
@@ -69,8 +78,8 @@ __device__ __forceinline__ P pick_seg(const P (&a)[3], int i) {
 
 }  // namespace
 
-template <int BM, int BN, int WM, int WN, int AM, int EM>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p, int ntiles) {
+template <int BM, int BN, int WM, int WN, int AM, int EM, int ST>
+__global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel(GemmArgs<bf16> p, int ntiles) {
   // The body uses gfx950-only types (buffer resources), which the host pass
   // cannot instantiate; it only needs the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -82,17 +91,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
   constexpr int STAGE = (BM + BN) * 128;          // bytes per stage
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
   static_assert(BM % 16 == 0, "B rows keep the swizzle phase of their LDS row");
-  static_assert(3 * STAGE <= 160 * 1024, "LDS");
+  static_assert(ST * STAGE <= (ST == 2 ? 80 : 160) * 1024, "LDS");
   static_assert(2 * NPER < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char S0[STAGE];
   __shared__ __attribute__((aligned(16))) char S1[STAGE];
-  __shared__ __attribute__((aligned(16))) char S2[STAGE];
+  __shared__ __attribute__((aligned(16))) char S2[ST == 3 ? STAGE : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int nk = AM == A_CONV3 ? 9 * (p.Cin / 64) : (p.K + 63) / 64;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, (uint32_t)((size_t)p.M * p.lda * 2));
+  // A_CAT2: K steps 0 .. nk1-1 read A, the rest read A2 (K1 is a multiple of 64).
+  const __amdgpu_buffer_rsrc_t rsA2 = make_rsrc(AM == A_CAT2 ? p.A2 : p.A,
+                                                (uint32_t)((size_t)p.M * (AM == A_CAT2 ? p.lda2 : p.lda) * 2));
+  const int nk1 = AM == A_CAT2 ? p.K1 / 64 : nk;
 
   // Lane l fills chunk (l & 7) of row (l >> 3) of an 8-row DMA group and
   // fetches the logical chunk stored there.
@@ -116,6 +129,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
   __amdgpu_buffer_rsrc_t rsB;
   const bf16* bias;
   uint32_t aoff[NA], boff[NB];
+  uint32_t aoff2[AM == A_CAT2 ? NA : 1];
   uint32_t amask[AM == A_CONV3 ? NA : 1];
 #define EDIT_SET_TILE(tl_)                                                                        \
   do {                                                                                            \
@@ -132,6 +146,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
       const int c = pc ^ ((r >> 1) & 7);                                                          \
       const int m = m0 + r;                                                                       \
       aoff[a] = m < p.M ? (uint32_t)m * (uint32_t)p.lda * 2u + (uint32_t)c * 16u : kOob;          \
+      if (AM == A_CAT2)                                                                           \
+        aoff2[AM == A_CAT2 ? a : 0] = m < p.M ? (uint32_t)m * (uint32_t)p.lda2 * 2u + (uint32_t)c * 16u : kOob; \
       if (AM == A_CONV3) {                                                                        \
         /* taps (ky, kx) whose input pixel (y + ky - 1, x + kx - 1) is inside the image */       \
         uint32_t mk = 0;                                                                          \
@@ -169,14 +185,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
     } else {                                                                                      \
       sa = sb = (uint32_t)kd_ * 128u;                                                             \
     }                                                                                             \
+    /* A_CAT2: a uniform choice of source (scalar selects, no branch) */                         \
+    const bool sec_ = AM == A_CAT2 && kd_ >= nk1;                                                 \
+    const __amdgpu_buffer_rsrc_t rsa_ = sec_ ? rsA2 : rsA;                                        \
+    if (AM == A_CAT2) sa = (uint32_t)(sec_ ? kd_ - nk1 : kd_) * 128u;                             \
     /* K tail: chunks at or past K read zeros (A and B), so they add nothing */                  \
     const bool ktail_ = AM != A_CONV3 && kd_ * 64 + 64 > p.K;                                     \
     const int klim_ = p.K - kd_ * 64;                                                             \
     _Pragma("unroll") for (int a = 0; a < NA; ++a) {                                              \
       uint32_t v = aoff[a];                                                                       \
       if (AM == A_CONV3) v = ((amask[AM == A_CONV3 ? a : 0] >> tap) & 1u) ? v + (uint32_t)tapoff : kOob; \
+      if (AM == A_CAT2 && sec_) v = aoff2[AM == A_CAT2 ? a : 0];                                  \
       if (ktail_ && 8 * (((a * NW + wave) & 1) ? cl1 : cl0) >= klim_) v = kOob;                  \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_ptr)((S) + 1024 * (a * NW + wave)), 16, v, \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa_, (lds_ptr)((S) + 1024 * (a * NW + wave)), 16, v, \
                                                sa, 0, 0);                                         \
     }                                                                                             \
     _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                              \
@@ -190,7 +211,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
   do {                                                                                            \
     EDIT_DMA(S0, 0);                                                                              \
     if (nk > 1) EDIT_DMA(S1, 1);                                                                  \
-    if (nk > 2) EDIT_DMA(S2, 2);                                                                  \
+    if (ST == 3 && nk > 2) EDIT_DMA(S2, 2);                                                       \
   } while (0)
 
   f32x16 acc[TI][CJ];
@@ -264,6 +285,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
     EDIT_MMA(1);                                                                                  \
   } while (0)
 
+#define EDIT_KSTEP_FULL2(SC, SN, kk)                                                              \
+  do {                                                                                            \
+    EDIT_KSTEP_HEAD(SC)                                                                           \
+    stage_barrier<0>();                                                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    EDIT_READ(SN, 0, 0);                                                                          \
+    EDIT_DMA(SC, (kk) + 2);                                                                       \
+    EDIT_MMA(1);                                                                                  \
+    EDIT_PIN_SUBSTEP(NPER);                                                                       \
+  } while (0)
+#define EDIT_KSTEP_TAIL2(SC, SN, kk)                                                              \
+  do {                                                                                            \
+    EDIT_KSTEP_HEAD(SC)                                                                           \
+    stage_barrier<0>();                                                                           \
+    if ((kk) + 2 < nk) EDIT_DMA(SC, (kk) + 2);                                                    \
+    if ((kk) + 1 < nk) EDIT_READ(SN, 0, 0);                                                       \
+    EDIT_MMA(1);                                                                                  \
+  } while (0)
+
   int tl = blockIdx.x;
   EDIT_SET_TILE(tl);
   EDIT_PREFETCH3();
@@ -283,57 +323,51 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
 
     // Step 0 landed. Loads complete in issue order; the previous tile's
     // stores, issued after this tile's loads, may still be outstanding.
-    if (nk > 2) stage_barrier<2 * NPER>();
-    else stage_barrier<0>();
-    EDIT_READ(S0, 0, 0);
-    // Whole rounds of three steps while every step refills its stage, then
-    // the at most five steps left.
-    int kt = 0;
-    for (; kt + 5 < nk; kt += 3) {
-      EDIT_KSTEP_FULL(S0, S1, kt);
-      EDIT_KSTEP_FULL(S1, S2, kt + 1);
-      EDIT_KSTEP_FULL(S2, S0, kt + 2);
+    if (ST == 3) {
+      if (nk > 2) stage_barrier<2 * NPER>();
+      else stage_barrier<0>();
+    } else {
+      if (nk > 1) stage_barrier<NPER>();
+      else stage_barrier<0>();
     }
-    EDIT_KSTEP_TAIL(S0, S1, kt);
-    if (kt + 1 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 1);
-    if (kt + 2 < nk) EDIT_KSTEP_TAIL(S2, S0, kt + 2);
-    if (kt + 3 < nk) EDIT_KSTEP_TAIL(S0, S1, kt + 3);
-    if (kt + 4 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 4);
+    EDIT_READ(S0, 0, 0);
+    int kt = 0;
+    if (ST == 3) {
+      // Whole rounds of three steps while every step refills its stage, then
+      // the at most five steps left.
+      for (; kt + 5 < nk; kt += 3) {
+        EDIT_KSTEP_FULL(S0, S1, kt);
+        EDIT_KSTEP_FULL(S1, S2, kt + 1);
+        EDIT_KSTEP_FULL(S2, S0, kt + 2);
+      }
+      EDIT_KSTEP_TAIL(S0, S1, kt);
+      if (kt + 1 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 1);
+      if (kt + 2 < nk) EDIT_KSTEP_TAIL(S2, S0, kt + 2);
+      if (kt + 3 < nk) EDIT_KSTEP_TAIL(S0, S1, kt + 3);
+      if (kt + 4 < nk) EDIT_KSTEP_TAIL(S1, S2, kt + 4);
+    } else {
+      for (; kt + 3 < nk; kt += 2) {
+        EDIT_KSTEP_FULL2(S0, S1, kt);
+        EDIT_KSTEP_FULL2(S1, S0, kt + 1);
+      }
+      EDIT_KSTEP_TAIL2(S0, S1, kt);
+      if (kt + 1 < nk) EDIT_KSTEP_TAIL2(S1, S0, kt + 1);
+      if (kt + 2 < nk) EDIT_KSTEP_TAIL2(S0, S1, kt + 2);
+    }
 
     // The last step's barrier came after every wave's last LDS read: the
     // stages are free. Queue the next tile's first three steps, then write
     // this tile from registers while they are in flight.
     const int em0 = m0, en0 = n0;
     const int next = tl + (int)gridDim.x;
-    // Residual rows (E_BIAS_RES), requested before the next tile's loads so
-    // that waiting for them does not wait for those.
-    uint4 rv[EM == E_BIAS_RES ? TI : 1][EM == E_BIAS_RES ? CJ : 1][2];
-    if (EM == E_BIAS_RES) {
-#pragma unroll
-      for (int t = 0; t < TI; ++t) {
-        const int m = em0 + wm * WTM + t * 32 + fr;
-#pragma unroll
-        for (int c = 0; c < CJ; ++c)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int n = en0 + wn * WTN + c * 32 + 8 * (fh ? 2 * j + 1 : 2 * j);
-            rv[EM == E_BIAS_RES ? t : 0][EM == E_BIAS_RES ? c : 0][j] =
-                m < p.M && n < p.N ? *reinterpret_cast<const uint4*>(p.R + (size_t)m * p.ldr + n)
-                                   : make_uint4(0u, 0u, 0u, 0u);
-          }
-      }
-    }
     if (next < ntiles) {
       EDIT_SET_TILE(next);
       EDIT_PREFETCH3();
     }
-    // Epilogue: bias (+ ReLU, or + residual). Accumulator quad g of lane l
-    // holds channels 8g + 4(l >> 5) .. +3 of token l & 31; lanes l and l ^ 32
-    // swap the halves of g = 2j + 1 (lower lane) and g = 2j (upper lane), so
-    // that each lane writes 8 consecutive channels of its token with one
-    // 16-byte store: 16 stores per tile per lane, which the next tile's first
-    // wait can leave in flight. With a residual the swap moves fp32 values,
-    // so that bias, product and residual are rounded to bf16 once.
+    // Epilogue: bias (+ ReLU). Accumulator quad g of lane l holds channels
+    // 8g + 4(l >> 5) .. +3 of token l & 31; lanes l and l ^ 32 swap the
+    // halves of g = 2j + 1 (lower lane) and g = 2j (upper lane), so that each
+    // lane writes 8 consecutive channels of its token with one 16-byte store.
 #pragma unroll
     for (int t = 0; t < TI; ++t) {
       const int m = em0 + wm * WTM + t * 32 + fr;
@@ -353,22 +387,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
           const int gsel = fh ? go : ge;
           const int n = en0 + wn * WTN + c * 32 + 8 * gsel;
           uint32_t w[4];
-          if (EM == E_BIAS_RES) {
-            float o[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float snd = fh ? f[ge][i] : f[go][i];
-              const float rcv = __uint_as_float(from_other_half(__float_as_uint(snd), fh));
-              o[i] = fh ? rcv : f[ge][i];
-              o[4 + i] = fh ? f[go][i] : rcv;
-            }
-            const bf16* r8 = reinterpret_cast<const bf16*>(&rv[EM == E_BIAS_RES ? t : 0][EM == E_BIAS_RES ? c : 0][j]);
-            bf16x8 ob;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ob[i] = (bf16)(o[i] + (float)r8[i]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(&ob)[i];
-          } else {
+          {
             uint32_t pk[2][2];   // bf16 pairs of quads ge, go
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -398,6 +417,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
 #undef EDIT_KSTEP_HEAD
 #undef EDIT_KSTEP_FULL
 #undef EDIT_KSTEP_TAIL
+#undef EDIT_KSTEP_FULL2
+#undef EDIT_KSTEP_TAIL2
 #undef EDIT_SUBSTEP
 #undef EDIT_PIN_SUBSTEP
 #undef EDIT_MMA
@@ -410,19 +431,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(GemmArgs<bf16> p
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int AM, int EM>
+template <int BM, int BN, int WM, int WN, int AM, int EM, int ST = 3>
 hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, hipStream_t s) {
-  // One block per CU (the kernel holds 3 x (BM + BN) x 128 bytes of LDS); with
+  // Three stages: one block per CU (3 x (BM + BN) x 128 bytes of LDS); with
   // more tiles than CUs each block walks several tiles, and the grid stays a
   // multiple of 8 so that every XCD keeps its own contiguous tile range.
+  // Spread: one block per tile instead (the loop then ends after one tile),
+  // so that CUs that another stream's kernels leave free take tiles as they
+  // come; measured 3-6% slower than persistent blocks on an idle chip.
+  // Two stages: always one block per tile, two resident per CU.
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidDevice;
   const int ntiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int g8 = cus / 8 * 8;
-  const int blocks = ntiles <= g8 ? ntiles : g8;
-  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, AM, EM>), dim3(blocks), dim3(64 * WM * WN), 0, s, a, ntiles);
+  const int blocks = ST == 2 || ntiles <= g8 || a.spread ? ntiles : g8;
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, AM, EM, ST>), dim3(blocks), dim3(64 * WM * WN), 0, s, a, ntiles);
   return hipGetLastError();
 }
 
@@ -445,26 +470,24 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
              n192 = a.N % 192 == 0 && a.seg_rows % 192 == 0;
   // Measured on MI355X (random bf16 data, 16384 tokens):
   //  - the 3x3 conv (162 K steps): 119 us against 227 us for the register-staged kernel;
-  //  - plain-A projections, 16384 x 1152 x 1152: 52 us with 128 x 192 tiles (768 tiles, three per
-  //    CU) against 63 us register-staged; 16384 x 2304 x 1152: 105 us, as register-staged.
+  //  - plain-A projections with 128 x 192 tiles, two stages, two blocks per CU: 46 us at
+  //    16384 x 1152 x 1152 and 91 us at 16384 x 2304 x 1152 against 63 and 105 us register-staged.
   if (am == A_CONV3 && em == E_BIAS) {
     if (a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin) return hipErrorNotSupported;
     if (n96) return launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_BIAS>(a, s);
     if (n128) return launch_dma_tiles<256, 128, 2, 2, A_CONV3, E_BIAS>(a, s);
     return hipErrorNotSupported;
   }
-  if (am == A_PLAIN && em == E_BIAS_RES) {
-    // The ConvFusion restore (K = C/r, a few K steps, HBM-bound): 36 us at
-    // 16384 x 1152 x 288 against 55 us for the register-staged kernel with
-    // the GroupNorm producer fused.
-    if (a.ldr % 8 != 0) return hipErrorNotSupported;
-    if (n192) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS_RES>(a, s);
-    if (n128) return launch_dma_tiles<256, 128, 2, 2, A_PLAIN, E_BIAS_RES>(a, s);
+  if (am == A_CAT2) {
+    // The query Linear over [X | act] with the restore folded in (K = C + C/r).
+    if (a.K1 % 64 != 0 || a.K1 >= a.K || a.lda2 % 8 != 0 || (size_t)a.M * a.lda2 * 2 >= kOob)
+      return hipErrorNotSupported;
+    if (n192 && em == E_BIAS_RELU) return launch_dma_tiles<128, 192, 2, 2, A_CAT2, E_BIAS_RELU, 2>(a, s);
     return hipErrorNotSupported;
   }
   if (am == A_PLAIN && n192) {
-    if (em == E_BIAS) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS>(a, s);
-    if (em == E_BIAS_RELU) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS_RELU>(a, s);
+    if (em == E_BIAS) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS, 2>(a, s);
+    if (em == E_BIAS_RELU) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS_RELU, 2>(a, s);
   }
   if (am == A_PLAIN && EDIT_DMA_FORCE == 1 && n128) {
     if (em == E_BIAS) return launch_dma_tiles<256, 128, 2, 2, A_PLAIN, E_BIAS>(a, s);

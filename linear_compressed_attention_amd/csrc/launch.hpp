@@ -10,13 +10,12 @@ typedef __bf16 bf16;
 enum AMode {
   A_PLAIN = 0,   // A[m][k] = a[m*lda + k]
   A_CONV3 = 1,   // implicit 3x3 stride-1 pad-1 convolution: k = tap*Cin + cin over an image [B][H][W][Cin]
-  A_GNACT = 2    // A[m][k] = LeakyReLU(a[m*lda + k] * scale[b][k] + shift[b][k]), b = m / rows_per_batch
+  A_CAT2 = 2     // two row sources side by side: A[m][k] = a[m*lda + k] for k < K1, else a2[m*lda2 + k - K1]
 };
 // What the epilogue adds before the store.
 enum EMode {
   E_BIAS = 0,       // C = acc + bias
-  E_BIAS_RELU = 1,  // C = max(acc + bias, 0)
-  E_BIAS_RES = 2    // C = acc + bias + R
+  E_BIAS_RELU = 1   // C = max(acc + bias, 0)
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T + epilogue. B and the bias may come in up
@@ -29,17 +28,17 @@ struct GemmArgs {
   const T* A;
   int lda;
   int H, W, Cin;               // A_CONV3 geometry (M = B*H*W, K = 9*Cin)
-  const float* scale;          // A_GNACT: [B][K]
-  const float* shift;          // A_GNACT: [B][K]
-  int rows_per_batch;          // A_GNACT
+  const T* A2;                 // A_CAT2: second source, columns K1 .. K-1
+  int lda2;
+  int K1;
   const T* Bseg[3];
   const T* bias[3];
   int seg_rows;
   int ldb;
   T* C;
   int ldc;
-  const T* R;                  // E_BIAS_RES
-  int ldr;
+  int spread;                  // 1: one block per tile, so that the hardware hands tiles to CUs as
+                               // they free up (for GEMMs that share the chip with another stream)
 };
 
 template <typename T>
@@ -58,6 +57,13 @@ hipError_t launch_groupnorm_stats(const T* x, int B, int HW, int C, int G, const
                                   const T* beta, float eps, float* partial, int nchunks,
                                   float* stat, float* scale, float* shift, hipStream_t s);
 int groupnorm_chunks(int HW, int C);
+
+// The ConvFusion 1x1 restore (W2 [C][Cr], b2 [C]) folded into a Linear
+// (W [C][C], b [C]) that reads X + act W2^T + b2: wcat [C][C + Cr] = [W | W W2],
+// bcat [C] = b + W b2, for an A_CAT2 GEMM over [X | act].
+template <typename T>
+hipError_t launch_restore_fold(const T* W, const T* b, const T* W2, const T* b2, int C, int Cr, T* wcat, T* bcat,
+                               hipStream_t s);
 
 // a = LeakyReLU(x * scale[b] + shift[b], 0.01) elementwise over x [B][HW][C].
 template <typename T>

@@ -309,7 +309,7 @@ def edit_attn_variant_forward(x, w, shape, query="convfusion", kv="compressed", 
         k = convfusion_query(x, H, W, wk, G, tk)
         v = linear(x, w["w_v"], w["b_v"])
         if trace is not None:
-            trace.update(xc_k=tk["xc"], xt_k=tk["xt"])
+            trace.update(xc_k=tk["xc"], cf_act_k=tk["cf_act"], xt_k=tk["xt"])
     S, z = kv_state(k, v, heads)
     y = linear_attention_apply(q, S, z, heads, shape.eps)
     out = linear(y, w["w_o"], w["b_o"])

@@ -38,7 +38,8 @@ def read_intermediates(shape, ws, n_text=0):
         "xc": _view(ws, lay["xc"], (B, N, s.Cr), T),
         "gn_stat": _view(ws, lay["gn_stat"], (B, s.gn_groups, 2), f32),
         "cf_act": _view(ws, lay["cf_act"], (B, N, s.Cr), T),
-        "xt": _view(ws, lay["xt"], (B, N, C), T),
+        "q_fold_w": _view(ws, lay["q_fold_w"], (C, C + s.Cr), T),
+        "q_fold_b": _view(ws, lay["q_fold_b"], (C,), T),
         "q": _view(ws, lay["q"], (B, N, C), T),
         "kv0": _view(ws, lay["kv0"], (B, N, 2 * C), T),
         "kc": _view(ws, lay["kc"], (B, s.Nc, C), T),
@@ -96,13 +97,22 @@ def run_hybrid(shape, inp, n_text, with_intermediates=True, exact=False):
     return res
 
 
+def restore_fold(w_lin, b_lin, w_cf2, b_cf2):
+    """[W | W W_cf2] and b + W b_cf2 in float64 from the weights (the 1x1
+    restore folded into the Linear that reads x + Conv1x1(act))."""
+    import numpy as np
+    W, W2 = np.asarray(w_lin, np.float64), np.asarray(w_cf2, np.float64)
+    return (np.concatenate([W, W @ W2], axis=1),
+            np.asarray(b_lin, np.float64) + W @ np.asarray(b_cf2, np.float64))
+
+
 def oracle_views(tr, shape):
     """The oracle trace in the shapes of read_intermediates."""
     import numpy as np
     rstd = 1.0 / np.sqrt(tr["gn_var"] + 1e-5)
     return {
         "xc": tr["xc"], "gn_stat": np.stack([tr["gn_mean"], rstd], axis=-1), "cf_act": tr["cf_act"],
-        "xt": tr["xt"], "q": tr["q"],
+        "q": tr["q"],
         "kv0": np.concatenate([tr["k0"], tr["v0"]], axis=-1), "kc": tr["kc"], "vc": tr["vc"],
         "S": tr["S"], "z": tr["z"], "out": tr["out"],
     }
@@ -138,7 +148,11 @@ def run_variant(shape, inp, query, kv):
         kv0 = _view(ws, lay["kv0"], (B, N, 2 * C), T)
         got["k"], got["v"] = kv0[..., :C], kv0[..., C:]
     if kv == "key_convfusion":
-        got["xt_k"] = _view(ws, lay["xt_k"], (B, N, C), T)
+        got["cf_act_k"] = _view(ws, lay["cf_act_k"], (B, N, s.Cr), T)
+        got["k_fold_w"] = _view(ws, lay["k_fold_w"], (C, C + s.Cr), T)
+        got["k_fold_b"] = _view(ws, lay["k_fold_b"], (C,), T)
     if query == "convfusion":
-        got["xt"] = _view(ws, lay["xt"], (B, N, C), T)
+        got["cf_act"] = _view(ws, lay["cf_act"], (B, N, s.Cr), T)
+        got["q_fold_w"] = _view(ws, lay["q_fold_w"], (C, C + s.Cr), T)
+        got["q_fold_b"] = _view(ws, lay["q_fold_b"], (C,), T)
     return {k: v.float().cpu().numpy() for k, v in got.items()}

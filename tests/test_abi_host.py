@@ -165,9 +165,9 @@ def test_variant_layouts(query, kv):
     s = CONFIGS["pixart1024"]
     lay = lca.edit_attn_variant_workspace_layout(s, query, kv)
     assert lay["total"] == lca.edit_attn_variant_workspace_size(s, query, kv)
-    assert (lay["xt"] > 0) == (query == "convfusion")
+    assert (lay["q_fold_w"] > 0) == (query == "convfusion")
     assert (lay["kc"] > 0) == (kv == "compressed")
-    assert (lay["xt_k"] > 0) == (kv == "key_convfusion")
+    assert (lay["k_fold_w"] > 0) == (kv == "key_convfusion")
     assert all(v % 256 == 0 for v in lay.values())
     if (query, kv) == ("convfusion", "compressed"):
         assert lay == lca.edit_attn_workspace_layout(s, 0)

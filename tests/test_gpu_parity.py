@@ -1,6 +1,6 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
-Every intermediate the workspace layout names (xc, GN statistics, xt, q,
+Every intermediate the workspace layout names (xc, GN statistics, cf_act, the folded query weights, q,
 kv0, kc, vc, S, z, y) and the output are compared element by element with
 the float64 oracle on the same seeded inputs: max |g - o| / max |o| per
 tensor <= 2e-2 for bf16, <= 1e-4 for fp32. Outputs and workspace are filled
@@ -28,7 +28,7 @@ def _announce(tag):
     print(f"\n[gpu-case] {tag}", flush=True)
 
 
-def check_edit(s, seed=0, gn_affine_random=False, x_std=None, centred=("xt", "q", "kc", "vc")):
+def check_edit(s, seed=0, gn_affine_random=False, x_std=None, centred=("q", "kc", "vc")):
     inp = make_inputs(s, seed=seed, gn_affine_random=gn_affine_random, x_std=x_std)
     _announce(f"edit {s} seed={seed}")
     got = G.run_edit(s, inp)
@@ -36,6 +36,8 @@ def check_edit(s, seed=0, gn_affine_random=False, x_std=None, centred=("xt", "q"
     O.edit_attn_forward(inp["x"], inp["w"], s, tr)
     ref = G.oracle_views(tr, s)
     ref["y"] = tr["y"]
+    ref["q_fold_w"], ref["q_fold_b"] = G.restore_fold(inp["w"]["w_q"], inp["w"]["b_q"], inp["w"]["w_cf2"],
+                                                      inp["w"]["b_cf2"])
     tol = _tol(s)
     errs = {}
     for k, r in ref.items():
@@ -233,15 +235,19 @@ def check_variant(s, query, kv, seed=0):
     else:
         ref.update(k=tr["k"], v=tr["v"])
     if kv == "key_convfusion":
-        ref["xt_k"] = tr["xt_k"]
+        ref["cf_act_k"] = tr["cf_act_k"]
+        ref["k_fold_w"], ref["k_fold_b"] = G.restore_fold(inp["w"]["w_k"], inp["w"]["b_k"], inp["w_kcf"]["w_cf2"],
+                                                          inp["w_kcf"]["b_cf2"])
     if query == "convfusion":
-        ref["xt"] = tr["xt"]
+        ref["cf_act"] = tr["cf_act"]
+        ref["q_fold_w"], ref["q_fold_b"] = G.restore_fold(inp["w"]["w_q"], inp["w"]["b_q"], inp["w"]["w_cf2"],
+                                                          inp["w"]["b_cf2"])
     tol = _tol(s)
     errs = {}
     for k, r in ref.items():
         assert np.isfinite(got[k]).all(), f"{k}: non-finite elements"
         errs[k] = max_rel_err(got[k], r)
-    for k in ("q", "k", "kc", "xt_k"):
+    for k in ("q", "k", "kc"):
         if k in ref:
             errs[k + "_centred"] = centred_rel_err(got[k], ref[k])
     print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
