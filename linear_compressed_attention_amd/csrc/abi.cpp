@@ -257,31 +257,40 @@ struct Marks {
 // restore is folded into the Linear (w_lin, b_lin) that reads the restored
 // stream x + act W_cf2^T + b_cf2: wcat = [w_lin | w_lin W_cf2],
 // bcat = b_lin + w_lin b_cf2, for one GEMM over [x | act] (cat_linear).
+// parts selects the 3x3 conv, the GroupNorm + LeakyReLU, and the fold (which
+// reads weights only, so it may run on another stream).
+enum { CF_CONV = 1, CF_NORM = 2, CF_FOLD = 4, CF_ALL = 7 };
 template <typename T>
 edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const void* b_cf1, const void* gamma,
                          const void* beta, const void* w_cf2, const void* b_cf2, const void* w_lin,
                          const void* b_lin, T* xc, float* gn_part, float* gn_stat, float* gn_scale, float* gn_shift,
-                         T* act, T* wcat, T* bcat, hipStream_t s, const Marks& mk) {
+                         T* act, T* wcat, T* bcat, hipStream_t s, const Marks& mk, int parts = CF_ALL) {
   using namespace edit;
-  GemmArgs<T> a{};
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_CONV3X3));
-  // xc = Conv3x3(x) + b_cf1
-  a.M = g.M; a.N = g.Cr; a.K = 9 * g.C; a.A = x; a.lda = g.C; a.H = g.H; a.W = g.W; a.Cin = g.C;
-  a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w_cf1);
-  a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(b_cf1);
-  a.seg_rows = g.Cr; a.ldb = 9 * g.C; a.C = xc; a.ldc = g.Cr;
-  EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_GN_STATS));
-  // GroupNorm statistics -> per-channel scale / shift
-  EDIT_LAUNCH(launch_groupnorm_stats<T>(xc, g.B, g.N, g.Cr, g.G, static_cast<const T*>(gamma),
-                                        static_cast<const T*>(beta), 1e-5f, gn_part, g.gn_chunks, gn_stat,
-                                        gn_scale, gn_shift, s));
-  EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_ACT));
-  // act = LeakyReLU(GN(xc)); the restore folded into the Linear's weights
-  EDIT_LAUNCH(launch_groupnorm_apply<T>(xc, g.B, g.N, g.Cr, gn_scale, gn_shift, act, s));
-  EDIT_LAUNCH(launch_restore_fold<T>(static_cast<const T*>(w_lin), static_cast<const T*>(b_lin),
-                                     static_cast<const T*>(w_cf2), static_cast<const T*>(b_cf2), g.C, g.Cr, wcat,
-                                     bcat, s));
+  if (parts & CF_CONV) {
+    // xc = Conv3x3(x) + b_cf1
+    EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_CONV3X3));
+    GemmArgs<T> a{};
+    a.M = g.M; a.N = g.Cr; a.K = 9 * g.C; a.A = x; a.lda = g.C; a.H = g.H; a.W = g.W; a.Cin = g.C;
+    a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w_cf1);
+    a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(b_cf1);
+    a.seg_rows = g.Cr; a.ldb = 9 * g.C; a.C = xc; a.ldc = g.Cr;
+    EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
+  }
+  if (parts & CF_NORM) {
+    // GroupNorm statistics -> per-channel scale / shift; act = LeakyReLU(GN(xc))
+    EDIT_LAUNCH(mk.mark(EDIT_STEP_GN_STATS));
+    EDIT_LAUNCH(launch_groupnorm_stats<T>(xc, g.B, g.N, g.Cr, g.G, static_cast<const T*>(gamma),
+                                          static_cast<const T*>(beta), 1e-5f, gn_part, g.gn_chunks, gn_stat,
+                                          gn_scale, gn_shift, s));
+    EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_ACT));
+    EDIT_LAUNCH(launch_groupnorm_apply<T>(xc, g.B, g.N, g.Cr, gn_scale, gn_shift, act, s));
+  }
+  if (parts & CF_FOLD) {
+    // the restore folded into the Linear's weights
+    EDIT_LAUNCH(launch_restore_fold<T>(static_cast<const T*>(w_lin), static_cast<const T*>(b_lin),
+                                       static_cast<const T*>(w_cf2), static_cast<const T*>(b_cf2), g.C, g.Cr, wcat,
+                                       bcat, s));
+  }
   return EDIT_OK;
 }
 
@@ -334,9 +343,11 @@ edit_status_t side_stream(SideStream** out) {
   if (e != hipSuccess || dev < 0 || dev >= 64) return fail(EDIT_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
   SideStream& ss = g_side[dev];
   if (!ss.s) {
+    // Both streams run on this device: a device-scope release is enough.
+    const unsigned fl = hipEventDisableTiming | hipEventReleaseToDevice;
     if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess)
+        (e = hipEventCreateWithFlags(&ss.fork, fl)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ss.join, fl)) != hipSuccess)
       return fail(EDIT_ERR_HIP, "creating the key/value stream failed: %s", hipGetErrorString(e));
   }
   *out = &ss;
@@ -350,6 +361,8 @@ edit_status_t side_stream(SideStream** out) {
 // second stream, so its kernels take the CUs the query branch leaves idle
 // (the 3x3 conv has C/r / 96 x M / 256 tiles, 192 at 16384 tokens, fewer
 // than the CUs); with them every step runs in order on the caller's stream.
+// Each cross-stream event costs 5-10 us on MI355X, so there are only the
+// fork and the join.
 template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
                         hipStream_t s, const Marks& mk, float* lin_den = nullptr,
@@ -359,18 +372,17 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   const bool fork = mk.ev == nullptr;
 
-  // 1-4. queries: q = ReLU((x + ConvFusion(x)) W_q^T + b_q), or ReLU(x W_q^T + b_q)
-  auto query_branch = [&](hipStream_t qs) -> edit_status_t {
-    edit_status_t st;
-    if (g.qmode == EDIT_QUERY_CONVFUSION) {
-      st = convfusion<T>(g, x, w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, w->w_q, w->b_q,
+  // 1-4. queries: q = ReLU((x + ConvFusion(x)) W_q^T + b_q), or ReLU(x W_q^T + b_q).
+  // parts: which ConvFusion parts to queue; q_proj waits for `folded` on qs when it is given.
+  const bool cf = g.qmode == EDIT_QUERY_CONVFUSION;
+  auto q_convfusion = [&](hipStream_t qs, int parts) -> edit_status_t {
+    return convfusion<T>(g, x, w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, w->w_q, w->b_q,
                          P(L.xc), F(L.gn_part), F(L.gn_stat), F(L.gn_scale), F(L.gn_shift), P(L.cf_act),
-                         P(L.q_fold_w), P(L.q_fold_b), qs, mk);
-      if (st != EDIT_OK) return st;
-      EDIT_LAUNCH(mk.mark(EDIT_STEP_Q_PROJ));
-      return cat_linear<T>(g, x, P(L.cf_act), P(L.q_fold_w), P(L.q_fold_b), P(L.q), g.C, fork, qs);
-    }
+                         P(L.q_fold_w), P(L.q_fold_b), qs, mk, parts);
+  };
+  auto q_proj = [&](hipStream_t qs) -> edit_status_t {
     EDIT_LAUNCH(mk.mark(EDIT_STEP_Q_PROJ));
+    if (cf) return cat_linear<T>(g, x, P(L.cf_act), P(L.q_fold_w), P(L.q_fold_b), P(L.q), g.C, fork, qs);
     return linear_cc<T>(g, x, w->w_q, w->b_q, P(L.q), g.C, true, fork, qs);
   };
   // 5-7. keys, values and the per-head state S, z
@@ -419,7 +431,8 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
 
   edit_status_t st;
   if (!fork) {
-    if ((st = query_branch(s)) != EDIT_OK) return st;
+    if (cf && (st = q_convfusion(s, CF_ALL)) != EDIT_OK) return st;
+    if ((st = q_proj(s)) != EDIT_OK) return st;
     if ((st = kv_branch(s)) != EDIT_OK) return st;
   } else {
     std::lock_guard<std::mutex> lock(g_side_mu);
@@ -427,14 +440,16 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     if ((st = side_stream(&side)) != EDIT_OK) return st;
     EDIT_LAUNCH(hipEventRecord(side->fork, s));
     EDIT_LAUNCH(hipStreamWaitEvent(side->s, side->fork, 0));
-    // The longer (query) branch is queued first, so its conv takes its CUs first.
-    st = query_branch(s);
-    const edit_status_t st2 = st == EDIT_OK ? kv_branch(side->s) : st;
+    // The query branch is the longer chain and is queued first, so its conv
+    // takes its CUs before the key/value GEMM's blocks fill the rest. (Any
+    // kernel queued ahead of the conv lets those blocks take every CU first.)
+    st = cf ? q_convfusion(s, CF_ALL) : EDIT_OK;
+    if (st == EDIT_OK) st = q_proj(s);
+    if (st == EDIT_OK) st = kv_branch(side->s);
     // Join even after a failed launch, so the caller's stream never runs ahead of queued side work.
     const hipError_t e1 = hipEventRecord(side->join, side->s);
     const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(s, side->join, 0) : e1;
     if (st != EDIT_OK) return st;
-    if (st2 != EDIT_OK) return st2;
     if (e2 != hipSuccess) return fail(EDIT_ERR_HIP, "joining the key/value stream failed: %s", hipGetErrorString(e2));
   }
   EDIT_LAUNCH(mk.mark(EDIT_STEP_APPLY));

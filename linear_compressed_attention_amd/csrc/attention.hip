@@ -31,8 +31,9 @@ int kv_state_dk(int d) { return 32 * ((d + 31) / 32); }
 // S^T (S[k][n] = sum_j K'_j[k] V'_j[n]), row d gives z[k]. Tokens are the
 // matrix-core K dimension, so the chunk's K' and V' slices are staged in LDS
 // transposed (channel-major). All loads of a slab are issued before the LDS
-// writes (one wait); each thread writes four tokens of a channel as one word,
-// and neighbouring lanes take neighbouring token quads of the same row.
+// writes (one wait); neighbouring lanes load neighbouring 16-byte channel
+// chunks of the same tokens (each token's head slice is one contiguous read),
+// and each thread writes four tokens of a channel as one LDS word.
 // partial[b][h][chunk][16*DR][16*DT] (fp32).
 // ---------------------------------------------------------------------------
 template <typename T> struct KvSlab { static constexpr int n = 256; };
@@ -91,13 +92,13 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   typedef typename Frag<T>::type FragT;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
   for (int js = j0; js < j1; js += SLAB) {
-    // Item e: token quad (fastest), then 8-channel chunk, then K or V.
+    // Item e: 8-channel chunk (fastest), then token quad, then K or V.
     u32x4v raw[NLOAD][4][8 / EPC];
 #pragma unroll
     for (int l = 0; l < NLOAD; ++l) {
       const int e = tid + 256 * l;
-      const int tq = e % QUADS, rest = e / QUADS;
-      const int c8 = (rest % DC) * 8, which = rest / DC;
+      const int c8 = (e % DC) * 8, rest = e / DC;
+      const int tq = rest % QUADS, which = rest / QUADS;
       const T* src = (which ? vc : kc) + ((size_t)b * Nc + js + 4 * tq) * ld + h * d + c8;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -114,8 +115,8 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
     for (int l = 0; l < NLOAD; ++l) {
       const int e = tid + 256 * l;
       if (e < ITEMS) {
-        const int tq = e % QUADS, rest = e / QUADS;
-        const int c8 = (rest % DC) * 8, which = rest / DC;
+        const int c8 = (e % DC) * 8, rest = e / DC;
+        const int tq = rest % QUADS, which = rest / QUADS;
         T* dst = (which ? At : Kt) + c8 * PITCH + 4 * tq;
         const T* v0 = reinterpret_cast<const T*>(&raw[l][0][0]);
         const T* v1 = reinterpret_cast<const T*>(&raw[l][1][0]);
@@ -177,6 +178,7 @@ __global__ __launch_bounds__(256) void kv_state_finalize_kernel(const float* __r
     float v = 0.0f;
     if (n < d && k < d) {
       const float* p = part + n * CW + k;
+#pragma unroll 8
       for (int c = 0; c < nchunks; ++c) v += p[(size_t)c * RW * CW];
       S[(bh * d + k) * d + n] = v;
     }
@@ -189,6 +191,7 @@ __global__ __launch_bounds__(256) void kv_state_finalize_kernel(const float* __r
     float v = 0.0f;
     if (k < d) {
       const float* p = part + d * CW + k;
+#pragma unroll 8
       for (int c = 0; c < nchunks; ++c) v += p[(size_t)c * RW * CW];
       z[bh * d + k] = v;
     }
