@@ -242,6 +242,40 @@ edit_status_t edit_attn_forward_timed(const edit_shape_t* shape, const edit_weig
                                       const void* x, void* y, void* workspace, size_t ws_bytes,
                                       void* hip_stream, void* const* events);
 
+/* Gradients of the image-stream parameters: one output per edit_weights_t
+ * member, same shape and dtype. */
+typedef struct {
+  void *w_cf1, *b_cf1, *gn_gamma, *gn_beta, *w_cf2, *b_cf2, *w_q, *b_q, *w_k, *b_k, *w_v, *b_v;
+  void *dw_k, *db_k, *dw_v, *db_v, *w_o, *b_o;
+} edit_grads_t;
+
+/* Bytes of scratch edit_attn_backward needs for this shape (beyond the
+ * forward's workspace); 0 if the shape is invalid. */
+size_t edit_attn_backward_workspace_size(const edit_shape_t* shape);
+
+/* EDiT layer backward: the gradients of sum(dy * y) with respect to x and to
+ * every parameter, y = edit_attn_forward(x, w). It is the chain rule through
+ * the forward steps (the page trains the layer by distillation, section
+ * "Distillation", which needs them): the output Linear, the linear-attention
+ * formula (dQ, dS, dz, then dK', dV' through S = sum K'^T V' and z = sum K'),
+ * the depthwise stride-2 convs and their ReLU, the key / value Linears, and
+ * ConvFusion (the query Linear with the 1x1 restore folded in, LeakyReLU,
+ * GroupNorm, the 3x3 conv).
+ *   fwd_workspace  the workspace of an edit_attn_forward call with the same
+ *                  shape, weights and x, not modified since (its
+ *                  intermediates are read, never written); fwd_ws_bytes its size
+ *   dy             [B][H*W][C], gradient of the layer output
+ *   dx             [B][H*W][C] out; grads: every member an output
+ *   workspace      scratch of edit_attn_backward_workspace_size(shape) bytes
+ * Parameter gradients are sums over the batch and the tokens, accumulated in
+ * fp32 in a fixed order and rounded once to the dtype; outputs are
+ * overwritten, not accumulated into. */
+edit_status_t edit_attn_backward(const edit_shape_t* shape, const edit_weights_t* w,
+                                 const void* x, const void* dy,
+                                 const void* fwd_workspace, size_t fwd_ws_bytes,
+                                 void* dx, const edit_grads_t* grads,
+                                 void* workspace, size_t ws_bytes, void* hip_stream);
+
 const char* edit_status_string(edit_status_t status);
 const char* edit_last_error(void);
 

@@ -19,6 +19,7 @@ __all__ = [
     "mmedit_hybrid_forward", "mmedit_hybrid_exact_forward", "edit_attn_forward_timed", "edit_attn_workspace_layout", "EDIT_NUM_STEPS", "edit_status_string", "edit_last_error",
     "lib_path", "header_symbols", "QUERY_MODES", "KV_MODES", "KEY_CONVFUSION_FIELDS",
     "edit_attn_variant_workspace_size", "edit_attn_variant_workspace_layout", "edit_attn_variant_forward",
+    "edit_attn_backward_workspace_size", "edit_attn_backward",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -46,6 +47,10 @@ class _Shape(ctypes.Structure):
 
 
 class _Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in IMAGE_WEIGHT_FIELDS]
+
+
+class _Grads(ctypes.Structure):          # edit_grads_t: one output per weight, same order
     _fields_ = [(n, ctypes.c_void_p) for n in IMAGE_WEIGHT_FIELDS]
 
 
@@ -104,6 +109,12 @@ def _load():
     lib.edit_attn_forward_timed.restype = ctypes.c_int
     lib.edit_attn_workspace_layout.argtypes = [P(_Shape), ctypes.c_int, P(_Layout)]
     lib.edit_attn_workspace_layout.restype = ctypes.c_int
+    lib.edit_attn_backward_workspace_size.argtypes = [P(_Shape)]
+    lib.edit_attn_backward_workspace_size.restype = ctypes.c_size_t
+    lib.edit_attn_backward.argtypes = [P(_Shape), P(_Weights), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p, P(_Grads), ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+    lib.edit_attn_backward.restype = ctypes.c_int
     lib.edit_status_string.argtypes = [ctypes.c_int]
     lib.edit_status_string.restype = ctypes.c_char_p
     lib.edit_last_error.argtypes = []
@@ -214,6 +225,27 @@ def edit_attn_forward(shape, weights, x, y, workspace, stream=None) -> None:
     w = _weights(weights)
     _check(_lib.edit_attn_forward(ctypes.byref(sh), ctypes.byref(w), _ptr(x), _ptr(y), _ptr(workspace),
                                   _nbytes(workspace), _stream(stream)))
+
+
+def edit_attn_backward_workspace_size(shape) -> int:
+    """Scratch bytes edit_attn_backward needs beyond the forward's workspace."""
+    return int(_lib.edit_attn_backward_workspace_size(ctypes.byref(_shape(shape))))
+
+
+def edit_attn_backward(shape, weights, x, dy, fwd_workspace, dx, grads, workspace, stream=None) -> None:
+    """EDiT layer backward on device tensors: dx and the parameter gradients
+    of sum(dy * y), reading the intermediates a preceding edit_attn_forward
+    left in ``fwd_workspace`` (same shape, weights and x). ``grads`` maps the
+    edit_weights_t field names to output tensors."""
+    sh = _shape(shape)
+    w = _weights(weights)
+    missing = [n for n in IMAGE_WEIGHT_FIELDS if n not in grads]
+    if missing:
+        raise ValueError(f"grads lacks {missing}")
+    g = _Grads(**{n: _ptr(grads[n]) for n in IMAGE_WEIGHT_FIELDS})
+    _check(_lib.edit_attn_backward(ctypes.byref(sh), ctypes.byref(w), _ptr(x), _ptr(dy), _ptr(fwd_workspace),
+                                   _nbytes(fwd_workspace), _ptr(dx), ctypes.byref(g), _ptr(workspace),
+                                   _nbytes(workspace), _stream(stream)))
 
 
 def edit_attn_forward_timed(shape, weights, x, y, workspace, events, stream=None) -> None:

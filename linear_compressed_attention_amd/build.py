@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libedit_attn.so")
-SOURCES = ["gemm.hip", "gemm_dma.hip", "fold.hip", "norm_dwconv.hip", "attention.hip", "abi.cpp"]
+SOURCES = ["gemm.hip", "gemm_dma.hip", "fold.hip", "norm_dwconv.hip", "attention.hip", "backward.hip", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

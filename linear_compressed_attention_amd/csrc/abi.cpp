@@ -534,6 +534,206 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   return out_linear<T>(MT, C, wt->w_o, wt->b_o, P(L.y_txt), static_cast<T*>(y_txt), s);
 }
 
+// ---------------------------------------------------------------------------
+// Backward (the chain rule through the forward steps; see edit_attn_backward
+// in the header). Scratch layout, byte offsets into the backward workspace.
+// Tensors contracted over tokens (the weight gradients) are transposed to
+// [channels][tokens] rows of Mp = M rounded up to 8 elements, so that the
+// GEMM reads both operands K-contiguous; those products are cut into K slices
+// (split-K) written as fp32 partials and added in slice order.
+// ---------------------------------------------------------------------------
+struct BwdLayout {
+  size_t zeros, w_oT, wqT, wkvT, wflip, dy, g, cvec, dq_pre, dS, dz, st, zp, kvpart, dkv, dk0v0, dXq, dXkv, dXc;
+  size_t dact, dxc, doutT, yT, xT, dqT, actT, dkvT, dxcT, skpart, dWx, dWa, dbq32, colpart, dwpart, gnpart, m12;
+  size_t total;
+  int Mp;
+};
+
+struct SplitK {
+  int S, kchunk;
+};
+
+// K slices for a [rows][cols] weight gradient over M tokens: about 512 output
+// tiles of 128 x 128 in flight, slices of at least 64 tokens.
+SplitK splitk(int rows, int cols, int M) {
+  const long tiles = ((long)(rows + 127) / 128) * ((cols + 127) / 128);
+  long S = (512 + tiles - 1) / tiles;
+  if (S > 32) S = 32;
+  if (S < 1) S = 1;
+  long kchunk = ((M + S - 1) / S + 63) / 64 * 64;
+  if (kchunk < 64) kchunk = 64;
+  SplitK r;
+  r.kchunk = (int)kchunk;
+  r.S = (int)((M + kchunk - 1) / kchunk);
+  return r;
+}
+
+BwdLayout make_bwd_layout(const Geometry& g) {
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t M = g.M, Mc = (size_t)g.B * g.Nc, C = g.C, Cr = g.Cr, es = g.es, BH = (size_t)g.B * g.heads;
+  L.Mp = (int)((M + 7) / 8 * 8);
+  const size_t Mp = L.Mp;
+  L.zeros = take(2 * C * es);
+  L.w_oT = take(C * C * es);
+  L.wqT = take((C + Cr) * C * es);
+  L.wkvT = take(C * 2 * C * es);
+  L.wflip = take(C * 9 * Cr * es);
+  L.dy = take(M * C * es);
+  L.g = take(M * C * es);
+  L.cvec = take(M * g.heads * 4);
+  L.dq_pre = take(M * C * es);
+  L.dS = take(BH * g.d * g.d * 4);
+  L.dz = take(BH * g.d * 4);
+  L.st = take(BH * 2 * g.DP * g.DK * es);
+  L.zp = take(BH * g.DK * 4);
+  L.kvpart = take(BH * edit::kv_state_chunks(g.N) * (16 * g.DR) * (16 * g.DT) * 4);
+  L.dkv = take(Mc * 2 * C * es);
+  L.dk0v0 = take(M * 2 * C * es);
+  L.dXq = take(M * C * es);
+  L.dXkv = take(M * C * es);
+  L.dXc = take(M * C * es);
+  L.dact = take(M * Cr * es);
+  L.dxc = take(M * Cr * es);
+  L.doutT = take(C * Mp * es);
+  L.yT = take(C * Mp * es);
+  L.xT = take(C * Mp * es);
+  L.dqT = take(C * Mp * es);
+  L.actT = take(Cr * Mp * es);
+  L.dkvT = take(2 * C * Mp * es);
+  L.dxcT = take(Cr * Mp * es);
+  size_t sk = 0;
+  const int shapes[4][2] = {{g.C, g.C}, {2 * g.C, g.C}, {g.C, g.Cr}, {g.Cr, g.C}};
+  for (auto& sh : shapes) {
+    const SplitK k = splitk(sh[0], sh[1], g.M);
+    const size_t b = (size_t)k.S * sh[0] * sh[1] * 4;
+    if (b > sk) sk = b;
+  }
+  L.skpart = take(sk);
+  L.dWx = take(C * C * 4);
+  L.dWa = take(C * Cr * 4);
+  L.dbq32 = take(C * 4);
+  L.colpart = take((size_t)edit::colsum_chunks(g.M) * 2 * C * 4);
+  L.dwpart = take((size_t)edit::dw_bwd_chunks(g.B, g.H, g.W) * 10 * 2 * C * 4);
+  L.gnpart = take((size_t)g.B * edit::gn_bwd_chunks(g.N) * Cr * 2 * 4);
+  L.m12 = take((size_t)g.B * g.G * 2 * 4);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& L, const edit_weights_t* w,
+                           const T* x, const T* dout, const char* fws, T* dx, const edit_grads_t* gr, char* ws,
+                           hipStream_t s) {
+  using namespace edit;
+  auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
+  auto Q = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  auto FP = [&](size_t off) { return reinterpret_cast<const T*>(fws + off); };
+  auto FF = [&](size_t off) { return reinterpret_cast<const float*>(fws + off); };
+  auto W = [](const void* p) { return static_cast<const T*>(p); };
+  auto G = [](void* p) { return static_cast<T*>(p); };
+  const int M = g.M, C = g.C, Cr = g.Cr, Mp = L.Mp;
+  const T* zeros = P(L.zeros);
+
+  // C[M'][N'] = A B^T + 0 (bf16 / fp32 out), both operands K-contiguous.
+  auto gemm = [&](int Mr, int Nr, int K, const T* A, int lda, const T* B, int ldb, T* out, int ldc) -> edit_status_t {
+    GemmArgs<T> a{};
+    a.M = Mr; a.N = Nr; a.K = K; a.A = A; a.lda = lda;
+    a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = B;
+    a.bias[0] = a.bias[1] = a.bias[2] = zeros;
+    a.seg_rows = Nr; a.ldb = ldb; a.C = out; a.ldc = ldc;
+    EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
+    return EDIT_OK;
+  };
+  // out[r][c] = sum_m At[r][m] Bt[c][m] over the M tokens (transposed operands, row stride Mp).
+  auto wgrad = [&](int rows, int cols, const T* At, const T* Bt, auto* out, int ldo) -> edit_status_t {
+    const SplitK k = splitk(rows, cols, M);
+    GemmArgs<T> a{};
+    a.M = rows; a.N = cols; a.K = M; a.A = At; a.lda = Mp;
+    a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = Bt;
+    a.bias[0] = a.bias[1] = a.bias[2] = zeros;
+    a.seg_rows = cols; a.ldb = Mp; a.ldc = cols;
+    a.Cf = Q(L.skpart); a.split_stride = (long long)rows * cols; a.kchunk = k.kchunk;
+    EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_F32, s));
+    EDIT_LAUNCH(launch_splitk_reduce(Q(L.skpart), k.S, (long long)rows * cols, rows, cols, out, ldo, s));
+    return EDIT_OK;
+  };
+  edit_status_t st;
+
+  // weights arranged as the GEMMs' B operands
+  EDIT_LAUNCH(launch_zero<T>(P(L.zeros), 2L * C, s));
+  EDIT_LAUNCH(launch_transpose<T>(W(w->w_o), C, C, C, P(L.w_oT), C, s));
+  EDIT_LAUNCH(launch_transpose<T>(FP(F.q_fold_w), C, C + Cr, C + Cr, P(L.wqT), C, s));
+  EDIT_LAUNCH(launch_transpose<T>(W(w->w_k), C, C, C, P(L.wkvT), 2 * C, s));
+  EDIT_LAUNCH(launch_transpose<T>(W(w->w_v), C, C, C, P(L.wkvT) + C, 2 * C, s));
+  EDIT_LAUNCH(launch_conv_weight_flip<T>(W(w->w_cf1), Cr, C, P(L.wflip), s));
+  EDIT_LAUNCH(launch_transpose<T>(x, M, C, C, P(L.xT), Mp, s, Mp));
+
+  // output Linear: dy = dout W_o, dW_o = dout^T y, db_o = sum dout
+  if ((st = gemm(M, C, C, dout, C, P(L.w_oT), C, P(L.dy), C)) != EDIT_OK) return st;
+  EDIT_LAUNCH(launch_colsum<T>(dout, M, C, C, Q(L.colpart), G(gr->b_o), s));
+  EDIT_LAUNCH(launch_transpose<T>(dout, M, C, C, P(L.doutT), Mp, s, Mp));
+  EDIT_LAUNCH(launch_transpose<T>(FP(F.y), M, C, C, P(L.yT), Mp, s, Mp));
+  if ((st = wgrad(C, C, P(L.doutT), P(L.yT), G(gr->w_o), C)) != EDIT_OK) return st;
+
+  // linear attention: g, c, dq_pre; dS = sum q^T g and dz = sum c q (the state kernel with per-token weights c)
+  EDIT_LAUNCH(launch_attn_bwd_q<T>(P(L.dy), FP(F.q), FF(F.S), FF(F.z), g.B, g.N, g.heads, g.d, g.eps, P(L.g),
+                                   Q(L.cvec), P(L.dq_pre), s));
+  EDIT_LAUNCH(launch_kv_state<T>(FP(F.q), P(L.g), C, g.B, g.N, g.heads, g.d, Q(L.kvpart), kv_state_chunks(g.N),
+                                 Q(L.dS), Q(L.dz), P(L.st), Q(L.zp), s, Q(L.cvec)));
+  // dK' (through the keys' ReLU), dV'
+  EDIT_LAUNCH(launch_kv_bwd<T>(FP(F.kc), FP(F.vc), Q(L.dS), Q(L.dz), g.B, g.Nc, g.heads, g.d, P(L.dkv), s));
+
+  // Spatial Compressor: depthwise convs, then the key / value Linears
+  EDIT_LAUNCH(launch_dw_bwd_input<T>(P(L.dkv), g.B, g.H, g.W, C, W(w->dw_k), W(w->dw_v), P(L.dk0v0), s));
+  EDIT_LAUNCH(launch_dw_bwd_weight<T>(P(L.dkv), FP(F.kv0), g.B, g.H, g.W, C, Q(L.dwpart), G(gr->dw_k), G(gr->db_k),
+                                      G(gr->dw_v), G(gr->db_v), s));
+  if ((st = gemm(M, C, 2 * C, P(L.dk0v0), 2 * C, P(L.wkvT), 2 * C, P(L.dXkv), C)) != EDIT_OK) return st;
+  EDIT_LAUNCH(launch_colsum<T>(P(L.dk0v0), M, C, 2 * C, Q(L.colpart), G(gr->b_k), s));
+  EDIT_LAUNCH(launch_colsum<T>(P(L.dk0v0) + C, M, C, 2 * C, Q(L.colpart), G(gr->b_v), s));
+  EDIT_LAUNCH(launch_transpose<T>(P(L.dk0v0), M, 2 * C, 2 * C, P(L.dkvT), Mp, s, Mp));
+  if ((st = wgrad(C, C, P(L.dkvT), P(L.xT), G(gr->w_k), C)) != EDIT_OK) return st;
+  if ((st = wgrad(C, C, P(L.dkvT) + (size_t)C * Mp, P(L.xT), G(gr->w_v), C)) != EDIT_OK) return st;
+
+  // query Linear over [x | act] with the restore folded in (W' = [W_q | W_q W_cf2], b' = b_q + W_q b_cf2):
+  // dx += dq_pre W_q, dact = dq_pre W_q W_cf2, dW' = dq_pre^T [x | act], then
+  // dW_q = dW'_x + dW'_act W_cf2^T + db_q b_cf2^T, dW_cf2 = W_q^T dW'_act, db_q = sum dq_pre,
+  // db_cf2 = W_q^T db_q
+  if ((st = gemm(M, C, C, P(L.dq_pre), C, P(L.wqT), C, P(L.dXq), C)) != EDIT_OK) return st;
+  if ((st = gemm(M, Cr, C, P(L.dq_pre), C, P(L.wqT) + (size_t)C * C, C, P(L.dact), Cr)) != EDIT_OK) return st;
+  EDIT_LAUNCH(launch_colsum<T>(P(L.dq_pre), M, C, C, Q(L.colpart), G(gr->b_q), s, Q(L.dbq32)));
+  EDIT_LAUNCH(launch_transpose<T>(P(L.dq_pre), M, C, C, P(L.dqT), Mp, s, Mp));
+  EDIT_LAUNCH(launch_transpose<T>(FP(F.cf_act), M, Cr, Cr, P(L.actT), Mp, s, Mp));
+  if ((st = wgrad(C, C, P(L.dqT), P(L.xT), Q(L.dWx), C)) != EDIT_OK) return st;
+  if ((st = wgrad(C, Cr, P(L.dqT), P(L.actT), Q(L.dWa), Cr)) != EDIT_OK) return st;
+  EDIT_LAUNCH((launch_small_matmul<float, T, T>(C, C, Cr, Q(L.dWa), Cr, 1, W(w->w_cf2), 1, Cr, Q(L.dWx), C,
+                                                G(gr->w_q), C, s, Q(L.dbq32), W(w->b_cf2))));
+  EDIT_LAUNCH((launch_small_matmul<T, float, T>(C, Cr, C, W(w->w_q), 1, C, Q(L.dWa), Cr, 1, nullptr, 0,
+                                                G(gr->w_cf2), Cr, s)));
+  EDIT_LAUNCH((launch_small_matmul<T, float, T>(C, 1, C, W(w->w_q), 1, C, Q(L.dbq32), 1, 0, nullptr, 0,
+                                                G(gr->b_cf2), 1, s)));
+
+  // LeakyReLU + GroupNorm, then the 3x3 conv: dx += conv(dxc, mirrored taps), dW_cf1 per tap
+  EDIT_LAUNCH(launch_gn_bwd<T>(P(L.dact), FP(F.cf_act), FP(F.xc), FF(F.gn_stat), W(w->gn_gamma), g.B, g.N, Cr, g.G,
+                               Q(L.gnpart), Q(L.m12), G(gr->gn_gamma), G(gr->gn_beta), P(L.dxc), s));
+  EDIT_LAUNCH(launch_colsum<T>(P(L.dxc), M, Cr, Cr, Q(L.colpart), G(gr->b_cf1), s));
+  {
+    GemmArgs<T> a{};
+    a.M = M; a.N = C; a.K = 9 * Cr; a.A = P(L.dxc); a.lda = Cr; a.H = g.H; a.W = g.W; a.Cin = Cr;
+    a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = P(L.wflip);
+    a.bias[0] = a.bias[1] = a.bias[2] = zeros;
+    a.seg_rows = C; a.ldb = 9 * Cr; a.C = P(L.dXc); a.ldc = C;
+    EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
+  }
+  for (int t = 0; t < 9; ++t) {
+    EDIT_LAUNCH(launch_shift_transpose<T>(P(L.dxc), g.B, g.H, g.W, Cr, P(L.dxcT), Mp, t / 3, t % 3, s));
+    if ((st = wgrad(Cr, C, P(L.dxcT), P(L.xT), G(gr->w_cf1) + (size_t)t * C, 9 * C)) != EDIT_OK) return st;
+  }
+  EDIT_LAUNCH(launch_sum3<T>(P(L.dXq), P(L.dXkv), P(L.dXc), (long)M * C, dx, s));
+  return EDIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -633,6 +833,59 @@ edit_status_t edit_attn_forward_timed(const edit_shape_t* shape, const edit_weig
   for (int i = 0; i <= EDIT_NUM_STEPS; ++i)
     if (!events[i]) return fail(EDIT_ERR_ARG, "events[%d] is NULL", i);
   return forward_impl(shape, w, x, y, workspace, ws_bytes, hip_stream, events);
+}
+
+size_t edit_attn_backward_workspace_size(const edit_shape_t* shape) {
+  Geometry g;
+  if (check_shape(shape, 0, &g) != EDIT_OK) return 0;
+  return make_bwd_layout(g).total;
+}
+
+edit_status_t edit_attn_backward(const edit_shape_t* shape, const edit_weights_t* w, const void* x, const void* dy,
+                                 const void* fwd_workspace, size_t fwd_ws_bytes, void* dx, const edit_grads_t* grads,
+                                 void* workspace, size_t ws_bytes, void* hip_stream) {
+  Geometry g;
+  edit_status_t st = check_shape(shape, 0, &g);
+  if (st != EDIT_OK) return st;
+  if ((st = check_weights(w, g)) != EDIT_OK) return st;
+  if ((st = check_ptr(x, "x")) != EDIT_OK) return st;
+  if ((st = check_ptr(dy, "dy")) != EDIT_OK) return st;
+  if ((st = check_ptr(dx, "dx")) != EDIT_OK) return st;
+  if (!grads) return fail(EDIT_ERR_ARG, "grads struct is NULL");
+  {
+    const void* p[] = {grads->w_cf1, grads->b_cf1, grads->gn_gamma, grads->gn_beta, grads->w_cf2, grads->b_cf2,
+                       grads->w_q, grads->b_q, grads->w_k, grads->b_k, grads->w_v, grads->b_v,
+                       grads->dw_k, grads->db_k, grads->dw_v, grads->db_v, grads->w_o, grads->b_o};
+    const char* n[] = {"grads.w_cf1", "grads.b_cf1", "grads.gn_gamma", "grads.gn_beta", "grads.w_cf2",
+                       "grads.b_cf2", "grads.w_q", "grads.b_q", "grads.w_k", "grads.b_k", "grads.w_v", "grads.b_v",
+                       "grads.dw_k", "grads.db_k", "grads.dw_v", "grads.db_v", "grads.w_o", "grads.b_o"};
+    for (int i = 0; i < 18; ++i)
+      if ((st = check_ptr(p[i], n[i])) != EDIT_OK) return st;
+  }
+  if (!fwd_workspace) return fail(EDIT_ERR_ARG, "forward workspace is NULL");
+  if (misaligned(fwd_workspace, 256)) return fail(EDIT_ERR_ARG, "forward workspace is not 256-byte aligned");
+  const Layout F = make_layout(g);
+  if (fwd_ws_bytes < F.total)
+    return fail(EDIT_ERR_WORKSPACE, "forward workspace has %zu bytes, needs %zu", fwd_ws_bytes, F.total);
+  if (!workspace) return fail(EDIT_ERR_ARG, "workspace is NULL");
+  if (misaligned(workspace, 256)) return fail(EDIT_ERR_ARG, "workspace is not 256-byte aligned");
+  const BwdLayout L = make_bwd_layout(g);
+  if (ws_bytes < L.total) return fail(EDIT_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  const size_t act = (size_t)g.M * g.C * g.es;
+  if (overlap(dx, act, x, act) || overlap(dx, act, dy, act)) return fail(EDIT_ERR_ARG, "dx overlaps x or dy");
+  if (overlap(dx, act, workspace, ws_bytes) || overlap(dx, act, fwd_workspace, fwd_ws_bytes))
+    return fail(EDIT_ERR_ARG, "dx overlaps a workspace");
+  if (overlap(workspace, ws_bytes, fwd_workspace, fwd_ws_bytes))
+    return fail(EDIT_ERR_ARG, "the two workspaces overlap");
+  if ((st = check_device()) != EDIT_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const char* fws = static_cast<const char*>(fwd_workspace);
+  char* wsb = static_cast<char*>(workspace);
+  return g.dtype == EDIT_BF16
+             ? run_backward<bf16>(g, F, L, w, static_cast<const bf16*>(x), static_cast<const bf16*>(dy), fws,
+                                  static_cast<bf16*>(dx), grads, wsb, s)
+             : run_backward<float>(g, F, L, w, static_cast<const float*>(x), static_cast<const float*>(dy), fws,
+                                   static_cast<float*>(dx), grads, wsb, s);
 }
 
 static edit_status_t hybrid_impl(const edit_shape_t* shape, int n_text, const edit_weights_t* img,

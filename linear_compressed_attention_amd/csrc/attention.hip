@@ -27,8 +27,12 @@ int kv_state_dk(int d) { return 32 * ((d + 31) / 32); }
 
 // ---------------------------------------------------------------------------
 // KV state, partial sums over one chunk of compressed tokens.
-// D[n][k] = sum_j A[n][j] * K'_j[k] with A = [V'^T ; 1]: rows n < d give
-// S^T (S[k][n] = sum_j K'_j[k] V'_j[n]), row d gives z[k]. Tokens are the
+// D[n][k] = sum_j A[n][j] * K'_j[k] with A = [V'^T ; w_hi ; w_lo]: rows n < d
+// give S^T (S[k][n] = sum_j K'_j[k] V'_j[n]), rows d and d + 1 give
+// z[k] = sum_j w_j K'_j[k] with w = 1 (the layer), or per-token weights
+// w[b][j][h] (the backward's dz = sum_j c_j q_j, the same kernel forming
+// dS = sum_j q_j^T g_j), split into w_hi = T(w) and w_lo = T(w - w_hi) so
+// that a bf16 operand carries ~16 mantissa bits of w. Tokens are the
 // matrix-core K dimension, so the chunk's K' and V' slices are staged in LDS
 // transposed (channel-major). All loads of a slab are issued before the LDS
 // writes (one wait); neighbouring lanes load neighbouring 16-byte channel
@@ -55,6 +59,7 @@ __device__ __forceinline__ void store_quad(float* dst, float a, float b, float c
 template <typename T, int DC>
 __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
                                                                int ld, int Nc, int heads, int nchunks,
+                                                               const float* __restrict__ wrow,
                                                                float* __restrict__ partial) {
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   constexpr int d = 8 * DC;
@@ -78,15 +83,15 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   for (int t = 0; t < TPW; ++t) acc_zero(acc[t]);
 
   // Rows that never receive data stay zero: K' channels d..16*DT-1 and the
-  // rows of A past the ones row. Only those rows are cleared (16-byte
+  // rows of A past the two weight rows. Only those rows are cleared (16-byte
   // stores), after the first slab's loads are on their way.
   auto clear_pad_rows = [&]() {
     const u32x4v zero = {0u, 0u, 0u, 0u};
     constexpr int W16 = PITCH * (int)sizeof(T) / 16;   // 16-byte words per row
     for (int i = tid; i < (16 * DT - d) * W16; i += 256)
       reinterpret_cast<u32x4v*>(Kt + d * PITCH)[i] = zero;
-    for (int i = tid; i < (16 * DR - d - 1) * W16; i += 256)
-      reinterpret_cast<u32x4v*>(At + (d + 1) * PITCH)[i] = zero;
+    for (int i = tid; i < (16 * DR - d - 2) * W16; i += 256)
+      reinterpret_cast<u32x4v*>(At + (d + 2) * PITCH)[i] = zero;
   };
 
   typedef typename Frag<T>::type FragT;
@@ -126,7 +131,12 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
         for (int i = 0; i < 8; ++i) store_quad(dst + i * PITCH, v0[i], v1[i], v2[i], v3[i]);
       }
     }
-    for (int t = tid; t < SLAB; t += 256) At[d * PITCH + t] = from_f32<T>(js + t < j1 ? 1.0f : 0.0f);
+    for (int t = tid; t < SLAB; t += 256) {
+      const float wv = js + t < j1 ? (wrow ? wrow[((size_t)b * Nc + js + t) * heads + h] : 1.0f) : 0.0f;
+      const T hi = from_f32<T>(wv);
+      At[d * PITCH + t] = hi;
+      At[(d + 1) * PITCH + t] = from_f32<T>(wv - to_f32(hi));
+    }
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < SLAB / 32; ++ks) {
@@ -190,9 +200,9 @@ __global__ __launch_bounds__(256) void kv_state_finalize_kernel(const float* __r
     const int k = e - DP * DK;
     float v = 0.0f;
     if (k < d) {
-      const float* p = part + d * CW + k;
+      const float* p = part + d * CW + k;   // rows d (w_hi) and d + 1 (w_lo)
 #pragma unroll 8
-      for (int c = 0; c < nchunks; ++c) v += p[(size_t)c * RW * CW];
+      for (int c = 0; c < nchunks; ++c) v += p[(size_t)c * RW * CW] + p[(size_t)c * RW * CW + CW];
       z[bh * d + k] = v;
     }
     zp[bh * DK + k] = v;
@@ -201,14 +211,14 @@ __global__ __launch_bounds__(256) void kv_state_finalize_kernel(const float* __r
 
 template <typename T>
 hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int heads, int d, float* partial,
-                           int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s) {
+                           int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s, const float* wrow) {
   const int DT = (d + 15) / 16, DR = (d + 16) / 16;
   dim3 grid(nchunks, heads, B);
   switch (d / 8) {
 #define EDIT_KV_CASE(DCV)                                                                              \
   case DCV:                                                                                            \
     hipLaunchKernelGGL((kv_state_partial_kernel<T, DCV>), grid, dim3(256), 0, s, kc, vc, ld, Nc, heads, \
-                       nchunks, partial);                                                              \
+                       nchunks, wrow, partial);                                                        \
     break;
     EDIT_KV_CASE(1) EDIT_KV_CASE(2) EDIT_KV_CASE(3) EDIT_KV_CASE(4) EDIT_KV_CASE(5) EDIT_KV_CASE(6)
     EDIT_KV_CASE(7) EDIT_KV_CASE(8) EDIT_KV_CASE(9) EDIT_KV_CASE(10) EDIT_KV_CASE(11) EDIT_KV_CASE(12)
@@ -541,7 +551,7 @@ hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s) {
 
 #define EDIT_INST(T)                                                                                     \
   template hipError_t launch_kv_state<T>(const T*, const T*, int, int, int, int, int, float*, int, float*, \
-                                         float*, T*, float*, hipStream_t);                              \
+                                         float*, T*, float*, hipStream_t, const float*);                              \
   template hipError_t launch_linattn_apply<T>(const T*, int, const T*, const float*, int, int, int, int, \
                                               float, T*, int, float*, hipStream_t);                     \
   template hipError_t launch_sdpa<T>(const SdpaArgs<T>&, hipStream_t);

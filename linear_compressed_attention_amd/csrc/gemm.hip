@@ -68,6 +68,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int NB = (p.N + BN - 1) / BN;
+  // Split-K (E_F32): grid row s multiplies K columns [s * kchunk, s * kchunk + Kc).
+  const int kbase = EM == E_F32 && p.kchunk ? (int)blockIdx.y * p.kchunk : 0;
+  const int Kc = EM == E_F32 && p.kchunk ? min(p.kchunk, p.K - kbase) : p.K;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
   const int m0 = (tile / NB) * BM, n0 = (tile % NB) * BN;
   const int cc = tid & 7;              // 16 B chunk column this thread loads
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
     const int m = m0 + r;
     aval[j] = (BM % RPP == 0 || r < BM) && m < p.M;
     const int mm = aval[j] ? m : 0;
-    arow[j] = p.A + (size_t)mm * p.lda;
+    arow[j] = p.A + (size_t)mm * p.lda + kbase;
     if (AM == A_CAT2) arow2[AM == A_CAT2 ? j : 0] = p.A2 + (size_t)mm * p.lda2;
     if (AM == A_CONV3) {
       const int hw = p.H * p.W;
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
     const int n = n0 + r;
     bval[j] = (BN % RPP == 0 || r < BN) && n < p.N;
     const int nn = bval[j] ? n : 0;
-    brow[j] = pick3(p.Bseg, nn / p.seg_rows) + (size_t)(nn % p.seg_rows) * p.ldb;
+    brow[j] = pick3(p.Bseg, nn / p.seg_rows) + (size_t)(nn % p.seg_rows) * p.ldb + kbase;
   }
 
   // Two register sets for prefetched global tiles (ra0/rb0, ra1/rb1): with
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
 #define EDIT_LOAD_TILES(RA, RB, AOK, BOK, k0_)                                                \
   do {                                                                                        \
     const int k = (k0_) + cc * EPC;                                                           \
-    const bool kin = k < p.K;                                                                 \
+    const bool kin = k < Kc;                                                                  \
     int kb = k; /* K index the weights use */                                                 \
     if (AM == A_CONV3) {                                                                      \
       /* K tiles run channel slice outer, tap inner (when BK divides Cin), so a   */          \
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
     }
   };
 
-  const int nk = (p.K + BK - 1) / BK;
+  const int nk = (Kc + BK - 1) / BK;
   if (PF == 1) {
     EDIT_LOAD_TILES(ra0, rb0, aok0, bok0, 0);
     EDIT_STORE_TILES(ra0, rb0, aok0, bok0, 0, 0);
@@ -291,6 +294,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = Cs[row * CROW + cg * 8 + i];
+      if (EM == E_F32) {
+        store8(p.Cf + (size_t)blockIdx.y * p.split_stride + (size_t)m * p.ldc + n, v);
+        continue;
+      }
       float bv[8];
       load8(pick3(p.bias, n / p.seg_rows) + n % p.seg_rows, bv);
 #pragma unroll
@@ -308,7 +315,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
 template <typename T, int BM, int BN, int WM, int WN, int STAGES = 2, int PF = 1, int SB = 0, int MM = 32>
 static hipError_t launch_tiles(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  dim3 grid(tiles), block(64 * WM * WN);
+  const int splits = em == E_F32 && a.kchunk ? (a.K + a.kchunk - 1) / a.kchunk : 1;
+  dim3 grid(tiles, splits), block(64 * WM * WN);
 #define EDIT_GEMM_CASE(AMV, EMV)                                                               \
   if (am == AMV && em == EMV) {                                                               \
     hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, AMV, EMV, STAGES, PF, SB, MM>), grid, block, 0, s, a);     \
@@ -318,6 +326,7 @@ static hipError_t launch_tiles(const GemmArgs<T>& a, AMode am, EMode em, hipStre
   EDIT_GEMM_CASE(A_PLAIN, E_BIAS_RELU)
   EDIT_GEMM_CASE(A_CONV3, E_BIAS)
   EDIT_GEMM_CASE(A_CAT2, E_BIAS_RELU)
+  EDIT_GEMM_CASE(A_PLAIN, E_F32)
 #undef EDIT_GEMM_CASE
   return hipErrorInvalidValue;
 }

@@ -15,7 +15,8 @@ enum AMode {
 // What the epilogue adds before the store.
 enum EMode {
   E_BIAS = 0,       // C = acc + bias
-  E_BIAS_RELU = 1   // C = max(acc + bias, 0)
+  E_BIAS_RELU = 1,  // C = max(acc + bias, 0)
+  E_F32 = 2         // Cf[split][m][n] = acc (fp32, no bias): one K slice of a split-K product
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T + epilogue. B and the bias may come in up
@@ -39,6 +40,11 @@ struct GemmArgs {
   int ldc;
   int spread;                  // 1: one block per tile, so that the hardware hands tiles to CUs as
                                // they free up (for GEMMs that share the chip with another stream)
+  // E_F32 (register-staged kernel): K is cut into slices of kchunk (a multiple of 64), one per
+  // grid row; slice s writes Cf + s * split_stride with row stride ldc.
+  float* Cf;
+  long long split_stride;
+  int kchunk;
 };
 
 template <typename T>
@@ -80,10 +86,67 @@ hipError_t launch_dwconv_s2(const T* kv0, int B, int H, int W, int C, const T* d
 // kc and vc rows (tokens) are ld elements apart.
 // Writes f32 S [B][h][d][d], z [B][h][d] and the apply kernel's operand:
 // st [B][h][2][DP][DK] of T (S transposed, split hi/lo for bf16), zp [B][h][DK] f32.
+// wrow (optional, [B][Nc][heads] f32) weights each token's term of z.
 template <typename T>
 hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int heads, int d, float* partial,
-                           int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s);
+                           int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s,
+                           const float* wrow = nullptr);
 int kv_state_chunks(int Nc);
+
+// ---- backward (backward.hip) ----
+// out[c][r] = in[r][c] (row strides ldi, ldo).
+// Output columns rows .. rows_pad - 1 are written as zeros.
+template <typename T>
+hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, int ldo, hipStream_t s,
+                            int rows_pad = 0);
+// out[c][m'] = in[m' - off][c] for the 3x3 conv's tap (ky, kx), zero where
+// that tap does not connect the two pixels (and in the padding up to ldo);
+// in is [B*H*W][cols], out [cols][ldo].
+template <typename T>
+hipError_t launch_shift_transpose(const T* in, int B, int H, int W, int cols, T* out, int ldo, int ky, int kx,
+                                  hipStream_t s);
+// out[c] = sum_r in[r][c] in a fixed order (partial: colsum_chunks(rows) x cols floats); out32 optional.
+int colsum_chunks(int rows);
+template <typename T>
+hipError_t launch_colsum(const T* in, int rows, int cols, int ld, float* partial, T* out, hipStream_t s,
+                         float* out32 = nullptr);
+template <typename T>
+hipError_t launch_zero(T* p, long n, hipStream_t s);
+// out[r][c] = sum_s part[s * stride + r * cols + c].
+template <typename O>
+hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int rows, int cols, O* out, int ldo,
+                                hipStream_t s);
+// Linear-attention backward, query side: g = dy / den, c = -(dy . y) / den, dq_pre = (g S^T + c z) where q > 0.
+template <typename T>
+hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const float* z, int B, int N, int heads, int d,
+                             float eps, T* g, float* c, T* dq_pre, hipStream_t s);
+// dkv [B][Nc][2C] = [ (V' dS^T + dz) where K' > 0 | K' dS ].
+template <typename T>
+hipError_t launch_kv_bwd(const T* kc, const T* vc, const float* dS, const float* dz, int B, int Nc, int heads,
+                         int d, T* dkv, hipStream_t s);
+// Depthwise 3x3 stride-2 backward over 2C channels: input gradient, and weight / bias gradients.
+template <typename T>
+hipError_t launch_dw_bwd_input(const T* dout, int B, int H, int W, int C, const T* dwk, const T* dwv, T* din,
+                               hipStream_t s);
+int dw_bwd_chunks(int B, int H, int W);
+template <typename T>
+hipError_t launch_dw_bwd_weight(const T* dout, const T* in, int B, int H, int W, int C, float* partial, T* dwk,
+                                T* dbk, T* dwv, T* dbv, hipStream_t s);
+// GroupNorm + LeakyReLU backward: dgamma, dbeta and dxc from dact (partial: B x gn_bwd_chunks(N) x C x 2 floats).
+int gn_bwd_chunks(int N);
+template <typename T>
+hipError_t launch_gn_bwd(const T* dact, const T* act, const T* xc, const float* stat, const T* gamma, int B, int N,
+                         int C, int G, float* partial, float* m12, T* dgamma, T* dbeta, T* dxc, hipStream_t s);
+// wflip[ci][t * Co + co] = w[co][8 - t][ci].
+template <typename T>
+hipError_t launch_conv_weight_flip(const T* w, int Co, int Ci, T* wflip, hipStream_t s);
+// out[i][j] = add[i][j] + ru[i] rv[j] + sum_k A[i * ars + k * acs] B[k * brs + j * bcs] (add, ru optional).
+template <typename TA, typename TB, typename TO>
+hipError_t launch_small_matmul(int M, int N, int K, const TA* A, long ars, long acs, const TB* Bm, long brs, long bcs,
+                               const float* add, int ldadd, TO* out, int ldo, hipStream_t s,
+                               const float* ru = nullptr, const TB* rv = nullptr);
+template <typename T>
+hipError_t launch_sum3(const T* a, const T* b, const T* c, long n, T* out, hipStream_t s);
 int kv_state_dp(int d);   // padded rows of the state operand
 int kv_state_dk(int d);   // padded K of the state operand
 

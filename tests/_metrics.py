@@ -26,3 +26,17 @@ def centred_rel_err(got, ref, token_axis=-2):
     ref = np.asarray(ref, dtype=np.float64)
     return max_rel_err(got - got.mean(axis=token_axis, keepdims=True),
                        ref - ref.mean(axis=token_axis, keepdims=True))
+
+
+def norm_rel_err(got, ref):
+    """||g - o|| / ||o|| (Frobenius) over one tensor: the gate for bf16
+    gradients that pass a ReLU mask, where a pre-activation within bf16
+    rounding of zero may fall on the other side of the kink than in float64
+    and move one element by a whole upstream value."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    n = np.linalg.norm(ref)
+    if n == 0:
+        return float(np.linalg.norm(got))
+    return float(np.linalg.norm(got - ref) / n)

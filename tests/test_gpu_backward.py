@@ -1,0 +1,126 @@
+"""GPU parity of the layer backward (edit_attn_backward) against the
+float64 oracle backward, through the C ABI.
+
+A forward fills the workspace, the backward reads it; dx and all 18
+parameter gradients are compared with oracle.edit_backward on the same
+seeded inputs and upstream gradient. Outputs and scratch are NaN-filled
+first.
+
+The backward passes three kinks (the queries' ReLU, the keys' ReLU, the
+LeakyReLU after GroupNorm). Where a pre-activation lies within the GPU
+forward's rounding of zero, the GPU and the float64 oracle can fall on
+opposite sides, and that gradient element moves by a whole upstream value.
+With a fraction f of such elements the error of every gradient behind the
+kink grows like sqrt(f): about 2-6% in bf16 (f ~ 1e-3), and a few 1e-4 in fp32
+at the PixArt-1024 shape (about five of its 9.4 M query pre-activations lie
+within fp32 rounding of zero), whatever the kernels do. The gates:
+- fp32, small ragged shapes (no ambiguous decision expected): max |g - o| /
+  max |o| <= 1e-4 for every tensor;
+- the gradients no kink reaches (SMOOTH: the output Linear, the value Linear
+  and the value depthwise conv; dV' = K' dS passes no mask): max-relative
+  <= 1e-4 (fp32) and <= 2e-2 (bf16) at every shape;
+- the gradients behind a kink, at the larger shapes: normwise
+  ||g - o|| / ||o|| <= 1e-3 (fp32) and <= 1e-1 (bf16).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import edit_backward as OB
+from seeded_inputs import CONFIGS, make_inputs, make_shape
+from seeded_inputs import round_to_bf16
+from tests._metrics import BF16_TOL, F32_TOL, max_rel_err, norm_rel_err
+
+SMOOTH = ("w_o", "b_o", "w_v", "b_v", "dw_v", "db_v")   # reached by no kink
+KINK_NORMWISE = {"f32": 1e-3, "bf16": 1e-1}
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import linear_compressed_attention_amd as lca
+    from tests import _gpu as G
+
+
+SHAPES = {
+    "f32_ragged": make_shape(B=2, H=13, W=11, C=128, heads=4, head_dim=32, reduction=4, gn_groups=4,
+                             dtype="f32", x_std=1.0),
+    "f32_d72": make_shape(B=1, H=9, W=14, C=288, heads=4, head_dim=72, reduction=4, gn_groups=4,
+                          dtype="f32", x_std=1.0),
+    "bf16_ragged_c384": make_shape(B=2, H=13, W=11, C=384, heads=4, head_dim=96, reduction=4, gn_groups=8,
+                                   dtype="bf16", x_std=1.0),
+    "bf16_c1152": make_shape(B=1, H=16, W=16, C=1152, heads=16, head_dim=72, reduction=4, gn_groups=32,
+                             dtype="bf16", x_std=1.0),
+}
+F32_PIXART1024 = make_shape(B=2, H=64, W=64, C=1152, heads=16, head_dim=72, reduction=4, gn_groups=32,
+                            dtype="f32", x_std=1.0)
+
+
+def run_backward(s, inp, dout):
+    x = G.to_dev(inp["x"], s.dtype)
+    w = G.dev_weights(inp["w"], s.dtype)
+    y = torch.empty_like(x)
+    fws = torch.empty(lca.edit_attn_workspace_size(s), dtype=torch.uint8, device="cuda")
+    G.poison(fws)
+    lca.edit_attn_forward(s, w, x, y, fws)
+    dy = G.to_dev(dout, s.dtype)
+    dx = torch.empty_like(x)
+    grads = {n: torch.empty_like(t) for n, t in w.items()}
+    ws = torch.empty(lca.edit_attn_backward_workspace_size(s), dtype=torch.uint8, device="cuda")
+    for t in [dx, ws] + list(grads.values()):
+        G.poison(t)
+    lca.edit_attn_backward(s, w, x, dy, fws, dx, grads, ws)
+    torch.cuda.synchronize()
+    out = {"x": dx.float().cpu().numpy()}
+    out.update({n: t.float().cpu().numpy() for n, t in grads.items()})
+    return out
+
+
+def check_backward(s, seed=0, strict=False):
+    """strict: every tensor max-relative (shapes too small for an ambiguous kink decision)."""
+    inp = make_inputs(s, seed=seed, gn_affine_random=True)
+    rng = np.random.default_rng(500 + seed)
+    dout = rng.standard_normal((s.B, s.N, s.C)).astype(np.float32)
+    if s.dtype == "bf16":
+        dout = round_to_bf16(dout)
+    print(f"\n[gpu-case] backward {s} seed={seed}", flush=True)
+    got = run_backward(s, inp, dout)
+    dx, grads = OB.edit_attn_backward(inp["x"], inp["w"], s, dout)
+    ref = {"x": dx, **grads}
+    errs, bad = {}, {}
+    for k, r in ref.items():
+        g = got[k]
+        assert g.shape == r.shape, (k, g.shape, r.shape)
+        assert np.isfinite(g).all(), f"{k}: non-finite elements (unwritten or overflow)"
+        if strict or k in SMOOTH:
+            e, tol = max_rel_err(g, r), (F32_TOL if s.dtype == "f32" else BF16_TOL)
+        else:
+            e, tol = norm_rel_err(g, r), KINK_NORMWISE[s.dtype]
+        errs[k] = e
+        if not e <= tol:
+            bad[k] = e
+    print({k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    assert not bad, f"over tolerance: {bad}"
+    return errs
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_backward_small(name):
+    check_backward(SHAPES[name], seed=1, strict=SHAPES[name].dtype == "f32")
+
+
+def test_backward_deterministic():
+    s = SHAPES["bf16_ragged_c384"]
+    inp = make_inputs(s, seed=4)
+    dout = np.random.default_rng(4).standard_normal((s.B, s.N, s.C)).astype(np.float32)
+    a = run_backward(s, inp, dout)
+    b = run_backward(s, inp, dout)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_f32_pixart1024_shape():
+    check_backward(F32_PIXART1024)
+
+
+def test_backward_pixart1024():
+    check_backward(CONFIGS["pixart1024"])
