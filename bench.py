@@ -177,6 +177,104 @@ def cpu_baseline(shape, inp, min_runs, budget_s, eta="ratio", query="convfusion"
             "cpu_model": cpu_model()}
 
 
+def backward_work(s):
+    """Algorithmic flops of one edit_attn_backward call: the GEMM-shaped
+    products (input and weight gradients of every Linear and of the 3x3 conv,
+    the folded query weights' two small products) and the linear-attention
+    core (t = S dy twice per query, dS and dz over the tokens, dK' and dV')."""
+    B, N, C, Cr, h, d = s.B, s.N, s.C, s.Cr, s.heads, s.head_dim
+    M, Mc = B * N, B * s.Nc
+    gemm = (2.0 * M * C * C * 2          # dy = dout W_o, dW_o
+            + 4.0 * M * C * C * 2        # dx from [dk0 | dv0], dW_k and dW_v
+            + 2.0 * M * C * C + 2.0 * M * C * Cr     # dx and dact from dq_pre
+            + 2.0 * M * C * C + 2.0 * M * C * Cr     # dW' over [x | act]
+            + 2.0 * M * C * 9 * Cr * 2   # conv input gradient, dW_cf1
+            + 2.0 * 2 * C * C * Cr)      # dW_q's and dW_cf2's small products
+    core = 2.0 * M * C * d * 2 + 2.0 * M * C * (d + 2) + 2.0 * 2 * Mc * C * d
+    return gemm + core
+
+
+def bench_backward(args, s, inp):
+    """Times edit_attn_backward (after one forward fills its workspace) and
+    prints the JSON line; the oracle backward is timed beside it."""
+    import numpy as np
+    import torch
+
+    import linear_compressed_attention_amd as lca
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    x = torch.from_numpy(inp["x"]).to(dev).to(tdt)
+    w = {k: torch.from_numpy(v).to(dev).to(tdt) for k, v in inp["w"].items()}
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    fws = torch.empty(lca.edit_attn_workspace_size(s), dtype=torch.uint8, device=dev)
+    lca.edit_attn_forward(s, w, x, y, fws, stream)
+    rng = np.random.default_rng(1)
+    dout_np = rng.standard_normal((s.B, s.N, s.C)).astype(np.float32)
+    dy = torch.from_numpy(dout_np).to(dev).to(tdt)
+    dx = torch.empty_like(x)
+    grads = {k: torch.empty_like(v) for k, v in w.items()}
+    bws = torch.empty(lca.edit_attn_backward_workspace_size(s), dtype=torch.uint8, device=dev)
+
+    def step():
+        lca.edit_attn_backward(s, w, x, dy, fws, dx, grads, bws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    wall0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(K):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev[0].elapsed_time(ev[K])
+    per_iter = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
+    assert torch.isfinite(dx).all().item(), "non-finite dx"
+    flops = backward_work(s)
+    ach = flops / (ms / K * 1e-3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[s.dtype]
+    cpu = None
+    if args.cpu_runs > 0:
+        from threadpoolctl import threadpool_info
+        from oracle import edit_backward as OB
+        times = []
+        while len(times) < args.cpu_runs or (sum(times) + statistics.median(times) < args.cpu_budget
+                                             and len(times) < 20):
+            t0 = time.perf_counter()
+            OB.edit_attn_backward(inp["x"], inp["w"], s, dout_np)
+            times.append(time.perf_counter() - t0)
+        med = statistics.median(times)
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        cpu = {"value": round(s.B * s.N / med, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(times)} full float64 layer backwards (forward recomputed inside, as the oracle "
+                         f"does) of the same workload, median {med:.2f} s; cores = BLAS threads",
+               "cpu_model": cpu_model()}
+    wl = (f"{args.workload}: EDiT attention layer backward (dx and the 18 parameter gradients from the "
+          f"forward's workspace), B={s.B}, {s.H}x{s.W} token grid ({s.N} tokens), C={s.C}, {s.heads} heads x "
+          f"{s.head_dim}, r={s.reduction}, {s.gn_groups} GN groups, {s.dtype}")
+    out = {
+        "metric": "image tokens/sec per EDiT attention layer backward",
+        "value": round(s.B * s.N * K / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms / K, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": s.dtype,
+        "data": "synthetic (seeded N(0,1) activations and upstream gradient, N(0,0.02^2) weights)",
+        "config": {"workload": wl, "B": s.B, "H": s.H, "W": s.W, "C": s.C, "heads": s.heads,
+                   "head_dim": s.head_dim, "reduction": s.reduction, "gn_groups": s.gn_groups, "pass": "backward"},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(ach / peak, 4), "traffic": None,
+                     "kernel": "edit_attn_backward, all launches (algorithmic flops over the call's time)",
+                     "work_per_launch": flops},
+        "cpu_baseline": cpu,
+        "ms_per_step_p10_p50_p90": [round(pct(per_iter, q), 5) for q in (0.1, 0.5, 0.9)],
+        "wall_s_timed_region": round(wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +297,8 @@ def main():
                     help="ablation variant: query processing (EDiT workloads)")
     ap.add_argument("--kv", default="compressed", choices=["compressed", "full", "key_convfusion"],
                     help="ablation variant: key/value processing (EDiT workloads)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the layer backward (edit_attn_backward) instead of the forward")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); multi-GPU runs are not part of this "
@@ -222,6 +322,12 @@ def main():
         print("--exact-eta applies to the hybrid workloads", file=sys.stderr)
         sys.exit(2)
     inp = make_inputs(s, seed=0, key_convfusion=args.kv == "key_convfusion")
+    if args.backward:
+        if hybrid or variant or args.exact_eta:
+            print("--backward applies to the EDiT layer itself", file=sys.stderr)
+            sys.exit(2)
+        bench_backward(args, s, inp)
+        return
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     x = torch.from_numpy(inp["x"]).to(dev).to(tdt)
