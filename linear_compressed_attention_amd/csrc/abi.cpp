@@ -698,8 +698,7 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
 
   // query Linear over [x | act] with the restore folded in (W' = [W_q | W_q W_cf2], b' = b_q + W_q b_cf2):
   // dx += dq_pre W_q, dact = dq_pre W_q W_cf2, dW' = dq_pre^T [x | act], then
-  // dW_q = dW'_x + dW'_act W_cf2^T + db_q b_cf2^T, dW_cf2 = W_q^T dW'_act, db_q = sum dq_pre,
-  // db_cf2 = W_q^T db_q
+  // dW_q = dW'_x + dW'_act W_cf2^T + db_q b_cf2^T, db_q = sum dq_pre
   if ((st = gemm(M, C, C, P(L.dq_pre), C, P(L.wqT), C, P(L.dXq), C)) != EDIT_OK) return st;
   if ((st = gemm(M, Cr, C, P(L.dq_pre), C, P(L.wqT) + (size_t)C * C, C, P(L.dact), Cr)) != EDIT_OK) return st;
   EDIT_LAUNCH(launch_colsum<T>(P(L.dq_pre), M, C, C, Q(L.colpart), G(gr->b_q), s, Q(L.dbq32)));
@@ -709,10 +708,10 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   if ((st = wgrad(C, Cr, P(L.dqT), P(L.actT), Q(L.dWa), Cr)) != EDIT_OK) return st;
   EDIT_LAUNCH((launch_small_matmul<float, T, T>(C, C, Cr, Q(L.dWa), Cr, 1, W(w->w_cf2), 1, Cr, Q(L.dWx), C,
                                                 G(gr->w_q), C, s, Q(L.dbq32), W(w->b_cf2))));
-  EDIT_LAUNCH((launch_small_matmul<T, float, T>(C, Cr, C, W(w->w_q), 1, C, Q(L.dWa), Cr, 1, nullptr, 0,
-                                                G(gr->w_cf2), Cr, s)));
-  EDIT_LAUNCH((launch_small_matmul<T, float, T>(C, 1, C, W(w->w_q), 1, C, Q(L.dbq32), 1, 0, nullptr, 0,
-                                                G(gr->b_cf2), 1, s)));
+  // the restore's 1x1 conv: dxt = dq_pre W_q (= dXq), dW_cf2 = dxt^T act, db_cf2 = sum dxt
+  EDIT_LAUNCH(launch_transpose<T>(P(L.dXq), M, C, C, P(L.dqT), Mp, s, Mp));
+  if ((st = wgrad(C, Cr, P(L.dqT), P(L.actT), G(gr->w_cf2), Cr)) != EDIT_OK) return st;
+  EDIT_LAUNCH(launch_colsum<T>(P(L.dXq), M, C, C, Q(L.colpart), G(gr->b_cf2), s));
 
   // LeakyReLU + GroupNorm, then the 3x3 conv: dx += conv(dxc, mirrored taps), dW_cf1 per tap
   EDIT_LAUNCH(launch_gn_bwd<T>(P(L.dact), FP(F.cf_act), FP(F.xc), FF(F.gn_stat), W(w->gn_gamma), g.B, g.N, Cr, g.G,

@@ -26,29 +26,45 @@ template <typename T, bool SHIFT>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int rows, int rows_pad, int cols,
                                                         int ldi, T* __restrict__ out, int ldo, int H, int W, int ky,
                                                         int kx) {
+  // 64 x 64 tile; every global access is 16 bytes (EPC elements): a load
+  // takes EPC consecutive columns of one row, a store EPC consecutive rows
+  // of one column. cols, ldi, ldo and rows_pad are multiples of EPC.
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int VPR = 64 / EPC;                 // 16-byte vectors per 64-element tile row
+  typedef uint32_t u32x4t __attribute__((ext_vector_type(4)));
   __shared__ float tile[64][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    float v = 0.0f;
+  for (int v = threadIdx.x; v < 64 * VPR; v += 256) {
+    const int i = v / VPR, cv = v % VPR;
+    const int r = r0 + i, c = c0 + cv * EPC;
+    T e[EPC];
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) e[k] = from_f32<T>(0.0f);
     if (r < rows && c < cols) {
+      size_t src = (size_t)r;
+      bool ok = true;
       if (SHIFT) {
-        // r is the destination token m'; the source token is m = m' - off,
-        // valid when its pixel (y, x) has (y + ky - 1, x + kx - 1) = pixel(m').
+        // r is the destination token m'; the source token m = m' - off is
+        // valid when its pixel (y, x) reads pixel(m') through tap (ky, kx).
         const int hw = H * W, b = r / hw, q = r - b * hw, y1 = q / W, x1 = q - (q / W) * W;
         const int y = y1 - (ky - 1), x = x1 - (kx - 1);
-        if (y >= 0 && y < H && x >= 0 && x < W) v = to_f32(in[((size_t)b * hw + (size_t)y * W + x) * ldi + c]);
-      } else {
-        v = to_f32(in[(size_t)r * ldi + c]);
+        ok = y >= 0 && y < H && x >= 0 && x < W;
+        src = (size_t)b * hw + (size_t)y * W + x;
       }
+      if (ok) *reinterpret_cast<u32x4t*>(e) = *reinterpret_cast<const u32x4t*>(in + src * ldi + c);
     }
-    tile[i][tx] = v;
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) tile[i][cv * EPC + k] = to_f32(e[k]);
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows_pad) out[(size_t)c * ldo + r] = from_f32<T>(tile[tx][i]);
+  for (int v = threadIdx.x; v < 64 * VPR; v += 256) {
+    const int i = v / VPR, rv = v % VPR;          // column c0 + i, rows r0 + rv*EPC ..
+    const int c = c0 + i, r = r0 + rv * EPC;
+    if (c >= cols || r >= rows_pad) continue;
+    T e[EPC];
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) e[k] = from_f32<T>(tile[rv * EPC + k][i]);
+    *reinterpret_cast<u32x4t*>(out + (size_t)c * ldo + r) = *reinterpret_cast<const u32x4t*>(e);
   }
 }
 
@@ -57,6 +73,8 @@ hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, in
                             int rows_pad) {
   if (rows_pad < rows) rows_pad = rows;
   if (rows <= 0 || cols <= 0) return hipSuccess;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  if (cols % EPC || ldi % EPC || ldo % EPC || rows_pad % EPC) return hipErrorInvalidValue;
   dim3 grid((cols + 63) / 64, (rows_pad + 63) / 64);
   hipLaunchKernelGGL((transpose_kernel<T, false>), grid, dim3(256), 0, s, in, rows, rows_pad, cols, ldi, out, ldo, 1,
                      1, 1, 1);
@@ -68,6 +86,8 @@ hipError_t launch_shift_transpose(const T* in, int B, int H, int W, int cols, T*
                                   hipStream_t s) {
   const int rows = B * H * W;
   if (rows <= 0 || cols <= 0) return hipSuccess;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  if (cols % EPC || ldo % EPC || ldo < rows) return hipErrorInvalidValue;
   dim3 grid((cols + 63) / 64, (ldo + 63) / 64);
   hipLaunchKernelGGL((transpose_kernel<T, true>), grid, dim3(256), 0, s, in, rows, ldo, cols, cols, out, ldo, H, W,
                      ky, kx);
@@ -75,8 +95,10 @@ hipError_t launch_shift_transpose(const T* in, int B, int H, int W, int cols, T*
 }
 
 // ---------------------------------------------------------------------------
-// Column sums (bias gradients): out[c] = sum_r in[r][c], rows summed in
-// chunks of 256 (partial[chunk][c]), then the chunks in order.
+// Column sums (bias gradients): out[c] = sum_r in[r][c]. A block sums 256
+// rows of 256 columns: 32 lanes of 8 columns (16-byte loads) x 8 row lanes,
+// the row lanes added through LDS (partial[chunk][c]); then the chunks in
+// order. cols and ld are multiples of 8.
 // ---------------------------------------------------------------------------
 constexpr int kColChunk = 256;
 int colsum_chunks(int rows) { return (rows + kColChunk - 1) / kColChunk; }
@@ -84,12 +106,32 @@ int colsum_chunks(int rows) { return (rows + kColChunk - 1) / kColChunk; }
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict__ in, int rows, int cols, int ld,
                                                              float* __restrict__ partial) {
-  const int c = blockIdx.x * 256 + threadIdx.x, ch = blockIdx.y;
-  if (c >= cols) return;
-  const int r0 = ch * kColChunk, r1 = min(rows, r0 + kColChunk);
-  float s = 0.0f;
-  for (int r = r0; r < r1; ++r) s += to_f32(in[(size_t)r * ld + c]);
-  partial[(size_t)ch * cols + c] = s;
+  __shared__ float red[8][256];
+  const int cg = threadIdx.x & 31, rl = threadIdx.x >> 5, ch = blockIdx.y;
+  const int c0 = (blockIdx.x * 32 + cg) * 8;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  if (c0 < cols) {
+    const int r1 = min(rows, (ch + 1) * kColChunk);
+#pragma unroll 8
+    for (int r = ch * kColChunk + rl; r < r1; r += 8) {
+      float v[8];
+      load8(in + (size_t)r * ld + c0, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[rl][cg * 8 + i] = acc[i];
+  __syncthreads();
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < cols) {
+    float t = 0.0f;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) t += red[l][threadIdx.x];
+    partial[(size_t)ch * cols + c] = t;
+  }
 }
 
 // Writes out[c] (T) and, when given, out32[c] (the same sum in f32).
@@ -166,85 +208,84 @@ hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int 
 //   dq = t / den + c z, then the outer ReLU of the queries: dq_pre = dq where q > 0.
 // dy . y is formed from q, S and dy in fp32 rather than from the stored y:
 // the two terms of dq nearly cancel (y does not change when q is scaled), so
-// y's rounding would be amplified. One thread per token (128 per block, one
-// head): S is staged transposed in LDS (ST[n][a] = S[a][n], so eight outputs
-// read one 32-byte row segment), the token's dy in a padded LDS row; d is a
-// runtime value. t is formed twice (once for dy . y, once for dq). g (T) and
-// c (f32) are kept for the state gradient dS = sum q^T g, dz = sum c q.
+// y's rounding would be amplified. One thread per token (256 per block, one
+// head); the token's dy in registers, S row-major in LDS (a row of S is read
+// as broadcast 16-byte words); t is formed twice, eight outputs at a time
+// (once for dy . y, once for dq). g (T) and c (f32) are kept for the state
+// gradient dS = sum q^T g, dz = sum c q.
 // ---------------------------------------------------------------------------
-constexpr int kBwdTok = 128;
+constexpr int kBwdTok = 256;
 
-__host__ __device__ inline size_t head_bwd_lds(int d) { return ((size_t)d * d + d + (size_t)kBwdTok * (d + 1)) * 4; }
+// acc[i] += sum_n r[n] M[(a0 + i) * d + n], i < 8 (M row-major in LDS).
+template <int d>
+__device__ __forceinline__ void rows8_dot(const float* M, int a0, const float (&r)[d], float (&acc)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float* row = M + (a0 + i) * d;
+    float s = 0.0f;
+#pragma unroll
+    for (int n = 0; n < d; n += 4) {
+      const f32x4 m = *reinterpret_cast<const f32x4*>(row + n);
+      s += r[n] * m[0] + r[n + 1] * m[1] + r[n + 2] * m[2] + r[n + 3] * m[3];
+    }
+    acc[i] += s;
+  }
+}
 
-template <typename T>
+template <typename T, int DC>
 __global__ __launch_bounds__(kBwdTok) void attn_bwd_q_kernel(const T* __restrict__ dy, const T* __restrict__ q,
                                                              const float* __restrict__ S,
-                                                             const float* __restrict__ z, int N, int heads, int d,
+                                                             const float* __restrict__ z, int N, int heads,
                                                              float eps, T* __restrict__ g_out,
                                                              float* __restrict__ c_out, T* __restrict__ dq_pre) {
-  extern __shared__ __attribute__((aligned(16))) float sm[];
-  float* ST = sm;              // [d][d]
-  float* zs = ST + d * d;      // [d]
-  float* ds = zs + d;          // [kBwdTok][d + 1]
-  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, dp = d + 1;
+  constexpr int d = 8 * DC;
+  __shared__ __attribute__((aligned(16))) float Ss[d * d];
+  __shared__ float zs[d];
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int C = heads * d;
   const size_t bh = (size_t)b * heads + h;
-  for (int i = tid; i < d * d; i += kBwdTok) {
-    const int a = i / d, n = i - a * d;
-    ST[n * d + a] = S[bh * d * d + i];
-  }
+  for (int i = tid; i < d * d; i += kBwdTok) Ss[i] = S[bh * d * d + i];
   for (int i = tid; i < d; i += kBwdTok) zs[i] = z[bh * d + i];
   __syncthreads();
   const int tok = blockIdx.x * kBwdTok + tid;
   if (tok >= N) return;
   const size_t row = ((size_t)b * N + tok) * C + (size_t)h * d;
-  float* dr = ds + tid * dp;
+  float dv[d];
   float den = eps;
-  for (int c8 = 0; c8 < d; c8 += 8) {
-    float qv[8], dv[8];
-    load8(q + row + c8, qv);
-    load8(dy + row + c8, dv);
+#pragma unroll
+  for (int c8 = 0; c8 < DC; ++c8) {
+    float qv[8], v[8];
+    load8(q + row + 8 * c8, qv);
+    load8(dy + row + 8 * c8, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      den += qv[i] * zs[c8 + i];
-      dr[c8 + i] = dv[i];
+      den += qv[i] * zs[8 * c8 + i];
+      dv[8 * c8 + i] = v[i];
     }
   }
   const float inv = 1.0f / den;
-  // t[a0 .. a0+7] = sum_n dy[n] S[a][n]
-  auto t8 = [&](int a0, float (&t)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) t[i] = 0.0f;
-    for (int n = 0; n < d; ++n) {
-      const float dn = dr[n];
-      const f32x4 s0 = *reinterpret_cast<const f32x4*>(ST + n * d + a0);
-      const f32x4 s1 = *reinterpret_cast<const f32x4*>(ST + n * d + a0 + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        t[i] += dn * s0[i];
-        t[4 + i] += dn * s1[i];
-      }
-    }
-  };
   float qt = 0.0f;
+#pragma unroll 1
   for (int a0 = 0; a0 < d; a0 += 8) {
-    float t[8], qv[8];
-    t8(a0, t);
+    float t[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qv[8];
+    rows8_dot<d>(Ss, a0, dv, t);
     load8(q + row + a0, qv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) qt += qv[i] * t[i];
   }
   const float c = -qt * inv * inv;
   c_out[((size_t)b * N + tok) * heads + h] = c;
-  for (int c8 = 0; c8 < d; c8 += 8) {
+#pragma unroll
+  for (int c8 = 0; c8 < DC; ++c8) {
     float go[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) go[i] = dr[c8 + i] * inv;
-    store8(g_out + row + c8, go);
+    for (int i = 0; i < 8; ++i) go[i] = dv[8 * c8 + i] * inv;
+    store8(g_out + row + 8 * c8, go);
   }
+#pragma unroll 1
   for (int a0 = 0; a0 < d; a0 += 8) {
-    float t[8], qv[8], o[8];
-    t8(a0, t);
+    float t[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qv[8], o[8];
+    rows8_dot<d>(Ss, a0, dv, t);
     load8(q + row + a0, qv);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -258,13 +299,19 @@ __global__ __launch_bounds__(kBwdTok) void attn_bwd_q_kernel(const T* __restrict
 template <typename T>
 hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const float* z, int B, int N, int heads, int d,
                              float eps, T* g, float* c, T* dq_pre, hipStream_t s) {
-  const size_t lds = head_bwd_lds(d);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bwd_q_kernel<T>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   dim3 grid((N + kBwdTok - 1) / kBwdTok, heads, B);
-  hipLaunchKernelGGL((attn_bwd_q_kernel<T>), grid, dim3(kBwdTok), lds, s, dy, q, S, z, N, heads, d, eps, g, c,
-                     dq_pre);
+  switch (d / 8) {
+#define EDIT_BQ_CASE(DCV)                                                                                       \
+  case DCV:                                                                                                     \
+    hipLaunchKernelGGL((attn_bwd_q_kernel<T, DCV>), grid, dim3(kBwdTok), 0, s, dy, q, S, z, N, heads, eps, g, c, \
+                       dq_pre);                                                                                 \
+    break;
+    EDIT_BQ_CASE(1) EDIT_BQ_CASE(2) EDIT_BQ_CASE(3) EDIT_BQ_CASE(4) EDIT_BQ_CASE(5) EDIT_BQ_CASE(6)
+    EDIT_BQ_CASE(7) EDIT_BQ_CASE(8) EDIT_BQ_CASE(9) EDIT_BQ_CASE(10) EDIT_BQ_CASE(11) EDIT_BQ_CASE(12)
+    EDIT_BQ_CASE(13) EDIT_BQ_CASE(14) EDIT_BQ_CASE(15) EDIT_BQ_CASE(16)
+#undef EDIT_BQ_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -274,100 +321,83 @@ hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const floa
 //   dK'_j = V'_j dS^T + dz, then the keys' ReLU (where K'_j > 0),
 //   dV'_j = K'_j dS.
 // Writes dkv [B][Nc][2C]: the keys' gradient before their ReLU | the values'.
-// Same layout as the query side: the matrix in LDS in the orientation that
-// gives eight outputs one row segment (dS^T for the keys, dS for the values),
-// the token's row in a padded LDS row.
+// One thread per token, its V' and K' rows in registers; dS and dS^T
+// row-major in LDS, eight outputs at a time.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int DC>
 __global__ __launch_bounds__(kBwdTok) void kv_bwd_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
                                                          const float* __restrict__ dS, const float* __restrict__ dz,
-                                                         int Nc, int heads, int d, T* __restrict__ dkv) {
-  extern __shared__ __attribute__((aligned(16))) float sm[];
-  float* Mx = sm;              // [d][d]
-  float* zs = Mx + d * d;      // [d]
-  float* ts = zs + d;          // [kBwdTok][d + 1]
-  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x, dp = d + 1;
+                                                         int Nc, int heads, T* __restrict__ dkv) {
+  constexpr int d = 8 * DC;
+  __shared__ __attribute__((aligned(16))) float Ss[d * d];    // dS[a][n]
+  __shared__ __attribute__((aligned(16))) float St[d * d];    // dS^T: St[n][a] = dS[a][n]
+  __shared__ float zs[d];
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int C = heads * d;
   const size_t bh = (size_t)b * heads + h;
-  const int tok = blockIdx.x * kBwdTok + tid;
-  const bool valid = tok < Nc;
-  const size_t row = ((size_t)b * Nc + (valid ? tok : 0)) * C + (size_t)h * d;
-  T* out = dkv + ((size_t)b * Nc + (valid ? tok : 0)) * 2 * C + (size_t)h * d;
-  float* tr = ts + tid * dp;
-
-  // keys: Mx[n][a] = dS[a][n]
   for (int i = tid; i < d * d; i += kBwdTok) {
+    const float v = dS[bh * d * d + i];
     const int a = i / d, n = i - a * d;
-    Mx[n * d + a] = dS[bh * d * d + i];
+    Ss[i] = v;
+    St[n * d + a] = v;
   }
   for (int i = tid; i < d; i += kBwdTok) zs[i] = dz[bh * d + i];
-  if (valid)
-    for (int c8 = 0; c8 < d; c8 += 8) {
-      float v[8];
-      load8(vc + row + c8, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) tr[c8 + i] = v[i];
-    }
   __syncthreads();
-  if (valid)
-    for (int a0 = 0; a0 < d; a0 += 8) {
-      float acc[8], kv[8];
+  const int tok = blockIdx.x * kBwdTok + tid;
+  if (tok >= Nc) return;
+  const size_t row = ((size_t)b * Nc + tok) * C + (size_t)h * d;
+  T* out = dkv + ((size_t)b * Nc + tok) * 2 * C + (size_t)h * d;
+  float r[d];
+  // keys: dK'[a] = sum_n dS[a][n] V'[n] + dz[a], masked by K' > 0
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = zs[a0 + i];
-      for (int n = 0; n < d; ++n) {
-        const float vn = tr[n];
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(Mx + n * d + a0);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(Mx + n * d + a0 + 4);
+  for (int c8 = 0; c8 < DC; ++c8) {
+    float v[8];
+    load8(vc + row + 8 * c8, v);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i] += vn * s0[i];
-          acc[4 + i] += vn * s1[i];
-        }
-      }
-      load8(kc + row + a0, kv);
+    for (int i = 0; i < 8; ++i) r[8 * c8 + i] = v[i];
+  }
+#pragma unroll 1
+  for (int a0 = 0; a0 < d; a0 += 8) {
+    float acc[8], kv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = kv[i] > 0.0f ? acc[i] : 0.0f;
-      store8(out + a0, acc);
-    }
-  __syncthreads();
-  // values: Mx[m][a] = dS[m][a]
-  for (int i = tid; i < d * d; i += kBwdTok) Mx[i] = dS[bh * d * d + i];
-  if (valid)
-    for (int c8 = 0; c8 < d; c8 += 8) {
-      float k[8];
-      load8(kc + row + c8, k);
+    for (int i = 0; i < 8; ++i) acc[i] = zs[a0 + i];
+    rows8_dot<d>(Ss, a0, r, acc);
+    load8(kc + row + a0, kv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) tr[c8 + i] = k[i];
-    }
-  __syncthreads();
-  if (valid)
-    for (int a0 = 0; a0 < d; a0 += 8) {
-      float acc[8];
+    for (int i = 0; i < 8; ++i) acc[i] = kv[i] > 0.0f ? acc[i] : 0.0f;
+    store8(out + a0, acc);
+  }
+  // values: dV'[n] = sum_m K'[m] dS[m][n] = (dS^T K')[n]
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-      for (int m = 0; m < d; ++m) {
-        const float km = tr[m];
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(Mx + m * d + a0);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(Mx + m * d + a0 + 4);
+  for (int c8 = 0; c8 < DC; ++c8) {
+    float k[8];
+    load8(kc + row + 8 * c8, k);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i] += km * s0[i];
-          acc[4 + i] += km * s1[i];
-        }
-      }
-      store8(out + C + a0, acc);
-    }
+    for (int i = 0; i < 8; ++i) r[8 * c8 + i] = k[i];
+  }
+#pragma unroll 1
+  for (int n0 = 0; n0 < d; n0 += 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    rows8_dot<d>(St, n0, r, acc);
+    store8(out + C + n0, acc);
+  }
 }
 
 template <typename T>
 hipError_t launch_kv_bwd(const T* kc, const T* vc, const float* dS, const float* dz, int B, int Nc, int heads,
                          int d, T* dkv, hipStream_t s) {
-  const size_t lds = head_bwd_lds(d);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&kv_bwd_kernel<T>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   dim3 grid((Nc + kBwdTok - 1) / kBwdTok, heads, B);
-  hipLaunchKernelGGL((kv_bwd_kernel<T>), grid, dim3(kBwdTok), lds, s, kc, vc, dS, dz, Nc, heads, d, dkv);
+  switch (d / 8) {
+#define EDIT_BKV_CASE(DCV)                                                                                  \
+  case DCV:                                                                                                 \
+    hipLaunchKernelGGL((kv_bwd_kernel<T, DCV>), grid, dim3(kBwdTok), 0, s, kc, vc, dS, dz, Nc, heads, dkv); \
+    break;
+    EDIT_BKV_CASE(1) EDIT_BKV_CASE(2) EDIT_BKV_CASE(3) EDIT_BKV_CASE(4) EDIT_BKV_CASE(5) EDIT_BKV_CASE(6)
+    EDIT_BKV_CASE(7) EDIT_BKV_CASE(8) EDIT_BKV_CASE(9) EDIT_BKV_CASE(10) EDIT_BKV_CASE(11) EDIT_BKV_CASE(12)
+    EDIT_BKV_CASE(13) EDIT_BKV_CASE(14) EDIT_BKV_CASE(15) EDIT_BKV_CASE(16)
+#undef EDIT_BKV_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -538,72 +568,131 @@ hipError_t launch_dw_bwd_weight(const T* dout, const T* in, int B, int H, int W,
 // finalize adds the chunks in order (per sample) and forms dgamma, dbeta
 // (summed over samples) and m1, m2 per (sample, group).
 // ---------------------------------------------------------------------------
-constexpr int kGnbRows = 64;
+constexpr int kGnbRows = 128;
 int gn_bwd_chunks(int N) { return (N + kGnbRows - 1) / kGnbRows; }
 
+// One block per (128-token chunk, 256 channels, sample): 32 lanes of 8
+// channels x 8 row lanes, the row lanes added through LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void gn_bwd_partial_kernel(const T* __restrict__ dact, const T* __restrict__ act,
                                                              const T* __restrict__ xc, const float* __restrict__ stat,
                                                              int N, int C, int G, float* __restrict__ partial) {
-  const int c = blockIdx.y * 256 + threadIdx.x, chunk = blockIdx.x, b = blockIdx.z;
-  if (c >= C) return;
-  const int cg = C / G, g = c / cg;
-  const float mean = stat[((size_t)b * G + g) * 2], rstd = stat[((size_t)b * G + g) * 2 + 1];
-  const int n0 = chunk * kGnbRows, n1 = min(N, n0 + kGnbRows);
-  float s1 = 0.0f, s2 = 0.0f;
-  for (int n = n0; n < n1; ++n) {
-    const size_t i = ((size_t)b * N + n) * C + c;
-    const float a = to_f32(act[i]), da0 = to_f32(dact[i]);
-    const float da = a >= 0.0f ? da0 : 0.01f * da0;
-    s1 += da;
-    s2 += da * (to_f32(xc[i]) - mean) * rstd;
+  __shared__ float red[2][8][256];
+  const int cg = threadIdx.x & 31, rl = threadIdx.x >> 5;
+  const int chunk = blockIdx.x, b = blockIdx.z;
+  const int c0 = (blockIdx.y * 32 + cg) * 8;
+  float s1[8], s2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s1[i] = s2[i] = 0.0f;
+  if (c0 < C) {
+    const int cpg = C / G;
+    float mean[8], rstd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int g = (c0 + i) / cpg;
+      mean[i] = stat[((size_t)b * G + g) * 2];
+      rstd[i] = stat[((size_t)b * G + g) * 2 + 1];
+    }
+    const int n1 = min(N, (chunk + 1) * kGnbRows);
+    for (int n = chunk * kGnbRows + rl; n < n1; n += 8) {
+      const size_t i0 = ((size_t)b * N + n) * C + c0;
+      float a[8], da[8], x[8];
+      load8(act + i0, a);
+      load8(dact + i0, da);
+      load8(xc + i0, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float dd = a[i] >= 0.0f ? da[i] : 0.01f * da[i];
+        s1[i] += dd;
+        s2[i] += dd * (x[i] - mean[i]) * rstd[i];
+      }
+    }
   }
-  const int nch = gridDim.x;
-  float* out = partial + (((size_t)b * nch + chunk) * C + c) * 2;
-  out[0] = s1;
-  out[1] = s2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    red[0][rl][cg * 8 + i] = s1[i];
+    red[1][rl][cg * 8 + i] = s2[i];
+  }
+  __syncthreads();
+  const int c = blockIdx.y * 256 + threadIdx.x;
+  if (c < C) {
+    float t1 = 0.0f, t2 = 0.0f;
+#pragma unroll
+    for (int l = 0; l < 8; ++l) {
+      t1 += red[0][l][threadIdx.x];
+      t2 += red[1][l][threadIdx.x];
+    }
+    float* out = partial + (((size_t)b * gridDim.x + chunk) * C + c) * 2;
+    out[0] = t1;
+    out[1] = t2;
+  }
 }
 
-// One block per (sample, group), one thread per channel of the group; block
-// (0, g) also writes dgamma, dbeta of its channels (summed over samples).
+// One block per (group, sample): threads (channel of the group, chunk lane)
+// sum strided chunks, then each channel's lanes in order; per (sample,
+// group) m1, m2; block (g, 0) also writes dgamma, dbeta of its channels,
+// summed over the samples in order.
 template <typename T>
 __global__ __launch_bounds__(256) void gn_bwd_finalize_kernel(const float* __restrict__ partial, int nchunks, int B,
                                                               int N, int C, int G, const T* __restrict__ gamma,
                                                               float* __restrict__ m12, T* __restrict__ dgamma,
                                                               T* __restrict__ dbeta) {
-  __shared__ float r1[256], r2[256];
+  __shared__ float r1[256], r2[256], t1s[256], t2s[256];
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int cg = C / G;
-  float s1 = 0.0f, s2 = 0.0f;
+  const int cg = C / G, lanes = 256 / cg;
+  const int ci = tid % cg, lane = tid / cg;
+  auto chunk_sums = [&](int bb, float& a1, float& a2) {
+    a1 = a2 = 0.0f;
+    if (lane < lanes)
+      for (int ch = lane; ch < nchunks; ch += lanes) {
+        const float* p = partial + (((size_t)bb * nchunks + ch) * C + g * cg + ci) * 2;
+        a1 += p[0];
+        a2 += p[1];
+      }
+  };
+  float a1, a2;
+  chunk_sums(b, a1, a2);
+  r1[tid] = a1;
+  r2[tid] = a2;
+  __syncthreads();
+  float s1 = 0.0f, s2 = 0.0f;     // per channel ci (threads tid < cg)
+  if (tid < cg)
+    for (int l = 0; l < lanes; ++l) {
+      s1 += r1[l * cg + tid];
+      s2 += r2[l * cg + tid];
+    }
+  __syncthreads();
   if (tid < cg) {
-    const int c = g * cg + tid;
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const float* p = partial + (((size_t)b * nchunks + ch) * C + c) * 2;
-      s1 += p[0];
-      s2 += p[1];
-    }
-    const float gm = to_f32(gamma[c]);
-    r1[tid] = gm * s1;
-    r2[tid] = gm * s2;
-    if (b == 0) {
-      float t1 = 0.0f, t2 = 0.0f;
-      for (int bb = 0; bb < B; ++bb)
-        for (int ch = 0; ch < nchunks; ++ch) {
-          const float* p = partial + (((size_t)bb * nchunks + ch) * C + c) * 2;
-          t1 += p[0];
-          t2 += p[1];
-        }
-      dbeta[c] = from_f32<T>(t1);
-      dgamma[c] = from_f32<T>(t2);
-    }
+    const float gm = to_f32(gamma[g * cg + tid]);
+    t1s[tid] = gm * s1;
+    t2s[tid] = gm * s2;
   }
   __syncthreads();
   if (tid == 0) {
-    float a1 = 0.0f, a2 = 0.0f;
-    for (int i = 0; i < cg; ++i) { a1 += r1[i]; a2 += r2[i]; }
+    float q1 = 0.0f, q2 = 0.0f;
+    for (int i = 0; i < cg; ++i) { q1 += t1s[i]; q2 += t2s[i]; }
     const float inv = 1.0f / ((float)N * (float)cg);
-    m12[((size_t)b * G + g) * 2] = a1 * inv;
-    m12[((size_t)b * G + g) * 2 + 1] = a2 * inv;
+    m12[((size_t)b * G + g) * 2] = q1 * inv;
+    m12[((size_t)b * G + g) * 2 + 1] = q2 * inv;
+  }
+  if (b != 0) return;
+  // dgamma, dbeta over the samples, in sample order
+  float d1 = s1, d2 = s2;
+  for (int bb = 1; bb < B; ++bb) {
+    __syncthreads();
+    chunk_sums(bb, a1, a2);
+    r1[tid] = a1;
+    r2[tid] = a2;
+    __syncthreads();
+    if (tid < cg)
+      for (int l = 0; l < lanes; ++l) {
+        d1 += r1[l * cg + tid];
+        d2 += r2[l * cg + tid];
+      }
+  }
+  if (tid < cg) {
+    dbeta[g * cg + tid] = from_f32<T>(d1);
+    dgamma[g * cg + tid] = from_f32<T>(d2);
   }
 }
 
@@ -629,7 +718,7 @@ __global__ __launch_bounds__(256) void gn_bwd_apply_kernel(const T* __restrict__
 template <typename T>
 hipError_t launch_gn_bwd(const T* dact, const T* act, const T* xc, const float* stat, const T* gamma, int B, int N,
                          int C, int G, float* partial, float* m12, T* dgamma, T* dbeta, T* dxc, hipStream_t s) {
-  if (C / G > 256) return hipErrorInvalidValue;
+  if (C / G > 256 || C % 8 != 0) return hipErrorInvalidValue;
   const int nch = gn_bwd_chunks(N);
   hipLaunchKernelGGL((gn_bwd_partial_kernel<T>), dim3(nch, (C + 255) / 256, B), dim3(256), 0, s, dact, act, xc, stat,
                      N, C, G, partial);
@@ -783,9 +872,6 @@ EDIT_INST(float)
 template hipError_t launch_small_matmul<float, bf16, bf16>(int, int, int, const float*, long, long, const bf16*, long,
                                                            long, const float*, int, bf16*, int, hipStream_t,
                                                            const float*, const bf16*);
-template hipError_t launch_small_matmul<bf16, float, bf16>(int, int, int, const bf16*, long, long, const float*, long,
-                                                           long, const float*, int, bf16*, int, hipStream_t,
-                                                           const float*, const float*);
 template hipError_t launch_small_matmul<float, float, float>(int, int, int, const float*, long, long, const float*,
                                                              long, long, const float*, int, float*, int, hipStream_t,
                                                              const float*, const float*);
