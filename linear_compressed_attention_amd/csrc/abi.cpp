@@ -544,7 +544,7 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
 // ---------------------------------------------------------------------------
 struct BwdLayout {
   size_t zeros, w_oT, wqT, wkvT, wflip, dy, g, cvec, dq_pre, dS, dz, st, zp, kvpart, dkv, dk0v0, dXq, dXkv, dXc;
-  size_t dact, dxc, doutT, yT, xT, dqT, actT, dkvT, dxcT, skpart, dWx, dWa, dbq32, colpart, dwpart, gnpart, m12;
+  size_t dact, dxc, doutT, yT, xT, dqT, actT, dkvT, dxcT9, skpart, dWx, dWa, dbq32, dwpart, gnpart, m12;
   size_t total;
   int Mp;
 };
@@ -553,10 +553,13 @@ struct SplitK {
   int S, kchunk;
 };
 
-// K slices for a [rows][cols] weight gradient over M tokens: about 512 output
-// tiles of 128 x 128 in flight, slices of at least 64 tokens.
-SplitK splitk(int rows, int cols, int M) {
-  const long tiles = ((long)(rows + 127) / 128) * ((cols + 127) / 128);
+// K slices for a [rows][cols] weight gradient over M tokens: about 512 blocks
+// (two per CU) in flight, slices a multiple of 64 tokens. The output tile is
+// the one the GEMM will pick: bf16 128 x 192 (cols a multiple of 192) or
+// 128 x 96 (of 96) on the DMA kernel, else 128 x 128.
+SplitK splitk(int rows, int cols, int M, bool bf) {
+  const int bn = bf && cols % 192 == 0 ? 192 : (bf && cols % 96 == 0 ? 96 : 128);
+  const long tiles = ((long)(rows + 127) / 128) * ((cols + bn - 1) / bn);
   long S = (512 + tiles - 1) / tiles;
   if (S > 32) S = 32;
   if (S < 1) S = 1;
@@ -602,11 +605,11 @@ BwdLayout make_bwd_layout(const Geometry& g) {
   L.dqT = take(C * Mp * es);
   L.actT = take(Cr * Mp * es);
   L.dkvT = take(2 * C * Mp * es);
-  L.dxcT = take(Cr * Mp * es);
+  L.dxcT9 = take(9 * Cr * Mp * es);
   size_t sk = 0;
-  const int shapes[4][2] = {{g.C, g.C}, {2 * g.C, g.C}, {g.C, g.Cr}, {g.Cr, g.C}};
+  const int shapes[3][2] = {{g.C, g.C}, {g.C, g.Cr}, {9 * g.Cr, g.C}};
   for (auto& sh : shapes) {
-    const SplitK k = splitk(sh[0], sh[1], g.M);
+    const SplitK k = splitk(sh[0], sh[1], L.Mp, g.es == 2);
     const size_t b = (size_t)k.S * sh[0] * sh[1] * 4;
     if (b > sk) sk = b;
   }
@@ -614,7 +617,6 @@ BwdLayout make_bwd_layout(const Geometry& g) {
   L.dWx = take(C * C * 4);
   L.dWa = take(C * Cr * 4);
   L.dbq32 = take(C * 4);
-  L.colpart = take((size_t)edit::colsum_chunks(g.M) * 2 * C * 4);
   L.dwpart = take((size_t)edit::dw_bwd_chunks(g.B, g.H, g.W) * 10 * 2 * C * 4);
   L.gnpart = take((size_t)g.B * edit::gn_bwd_chunks(g.N) * Cr * 2 * 4);
   L.m12 = take((size_t)g.B * g.G * 2 * 4);
@@ -646,17 +648,19 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
     EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
     return EDIT_OK;
   };
-  // out[r][c] = sum_m At[r][m] Bt[c][m] over the M tokens (transposed operands, row stride Mp).
-  auto wgrad = [&](int rows, int cols, const T* At, const T* Bt, auto* out, int ldo) -> edit_status_t {
-    const SplitK k = splitk(rows, cols, M);
+  // out[r][c] = sum_m At[r][m] Bt[c][m] over the tokens (transposed operands, row stride Mp, zero
+  // padding past M); rows in groups of rpg interleave in the output row (see launch_splitk_reduce).
+  auto wgrad = [&](int rows, int cols, const T* At, const T* Bt, auto* out, int ldo, int rpg = 0,
+                   int gstride = 0) -> edit_status_t {
+    const SplitK k = splitk(rows, cols, Mp, sizeof(T) == 2);
     GemmArgs<T> a{};
-    a.M = rows; a.N = cols; a.K = M; a.A = At; a.lda = Mp;
+    a.M = rows; a.N = cols; a.K = Mp; a.A = At; a.lda = Mp;
     a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = Bt;
     a.bias[0] = a.bias[1] = a.bias[2] = zeros;
     a.seg_rows = cols; a.ldb = Mp; a.ldc = cols;
     a.Cf = Q(L.skpart); a.split_stride = (long long)rows * cols; a.kchunk = k.kchunk;
     EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_F32, s));
-    EDIT_LAUNCH(launch_splitk_reduce(Q(L.skpart), k.S, (long long)rows * cols, rows, cols, out, ldo, s));
+    EDIT_LAUNCH(launch_splitk_reduce(Q(L.skpart), k.S, (long long)rows * cols, rows, cols, out, ldo, s, rpg, gstride));
     return EDIT_OK;
   };
   edit_status_t st;
@@ -667,13 +671,15 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   EDIT_LAUNCH(launch_transpose<T>(FP(F.q_fold_w), C, C + Cr, C + Cr, P(L.wqT), C, s));
   EDIT_LAUNCH(launch_transpose<T>(W(w->w_k), C, C, C, P(L.wkvT), 2 * C, s));
   EDIT_LAUNCH(launch_transpose<T>(W(w->w_v), C, C, C, P(L.wkvT) + C, 2 * C, s));
-  EDIT_LAUNCH(launch_conv_weight_flip<T>(W(w->w_cf1), Cr, C, P(L.wflip), s));
+  // the 3x3 conv's input gradient is a 3x3 conv of dxc with the taps mirrored and the channel roles
+  // swapped: wflip[ci][t * Cr + co] = w_cf1[co][8 - t][ci], one transpose per tap
+  EDIT_LAUNCH(launch_transpose<T>(W(w->w_cf1) + 8 * C, Cr, C, 9 * C, P(L.wflip), 9 * Cr, s, Cr, 9, -(long)C, Cr));
   EDIT_LAUNCH(launch_transpose<T>(x, M, C, C, P(L.xT), Mp, s, Mp));
 
   // output Linear: dy = dout W_o, dW_o = dout^T y, db_o = sum dout
   if ((st = gemm(M, C, C, dout, C, P(L.w_oT), C, P(L.dy), C)) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_colsum<T>(dout, M, C, C, Q(L.colpart), G(gr->b_o), s));
   EDIT_LAUNCH(launch_transpose<T>(dout, M, C, C, P(L.doutT), Mp, s, Mp));
+  EDIT_LAUNCH(launch_rowsum<T>(P(L.doutT), C, Mp, Mp, G(gr->b_o), s));
   EDIT_LAUNCH(launch_transpose<T>(FP(F.y), M, C, C, P(L.yT), Mp, s, Mp));
   if ((st = wgrad(C, C, P(L.doutT), P(L.yT), G(gr->w_o), C)) != EDIT_OK) return st;
 
@@ -690,9 +696,9 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   EDIT_LAUNCH(launch_dw_bwd_weight<T>(P(L.dkv), FP(F.kv0), g.B, g.H, g.W, C, Q(L.dwpart), G(gr->dw_k), G(gr->db_k),
                                       G(gr->dw_v), G(gr->db_v), s));
   if ((st = gemm(M, C, 2 * C, P(L.dk0v0), 2 * C, P(L.wkvT), 2 * C, P(L.dXkv), C)) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_colsum<T>(P(L.dk0v0), M, C, 2 * C, Q(L.colpart), G(gr->b_k), s));
-  EDIT_LAUNCH(launch_colsum<T>(P(L.dk0v0) + C, M, C, 2 * C, Q(L.colpart), G(gr->b_v), s));
   EDIT_LAUNCH(launch_transpose<T>(P(L.dk0v0), M, 2 * C, 2 * C, P(L.dkvT), Mp, s, Mp));
+  EDIT_LAUNCH(launch_rowsum<T>(P(L.dkvT), C, Mp, Mp, G(gr->b_k), s));
+  EDIT_LAUNCH(launch_rowsum<T>(P(L.dkvT) + (size_t)C * Mp, C, Mp, Mp, G(gr->b_v), s));
   if ((st = wgrad(C, C, P(L.dkvT), P(L.xT), G(gr->w_k), C)) != EDIT_OK) return st;
   if ((st = wgrad(C, C, P(L.dkvT) + (size_t)C * Mp, P(L.xT), G(gr->w_v), C)) != EDIT_OK) return st;
 
@@ -701,8 +707,8 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   // dW_q = dW'_x + dW'_act W_cf2^T + db_q b_cf2^T, db_q = sum dq_pre
   if ((st = gemm(M, C, C, P(L.dq_pre), C, P(L.wqT), C, P(L.dXq), C)) != EDIT_OK) return st;
   if ((st = gemm(M, Cr, C, P(L.dq_pre), C, P(L.wqT) + (size_t)C * C, C, P(L.dact), Cr)) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_colsum<T>(P(L.dq_pre), M, C, C, Q(L.colpart), G(gr->b_q), s, Q(L.dbq32)));
   EDIT_LAUNCH(launch_transpose<T>(P(L.dq_pre), M, C, C, P(L.dqT), Mp, s, Mp));
+  EDIT_LAUNCH(launch_rowsum<T>(P(L.dqT), C, Mp, Mp, G(gr->b_q), s, Q(L.dbq32)));
   EDIT_LAUNCH(launch_transpose<T>(FP(F.cf_act), M, Cr, Cr, P(L.actT), Mp, s, Mp));
   if ((st = wgrad(C, C, P(L.dqT), P(L.xT), Q(L.dWx), C)) != EDIT_OK) return st;
   if ((st = wgrad(C, Cr, P(L.dqT), P(L.actT), Q(L.dWa), Cr)) != EDIT_OK) return st;
@@ -711,12 +717,11 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   // the restore's 1x1 conv: dxt = dq_pre W_q (= dXq), dW_cf2 = dxt^T act, db_cf2 = sum dxt
   EDIT_LAUNCH(launch_transpose<T>(P(L.dXq), M, C, C, P(L.dqT), Mp, s, Mp));
   if ((st = wgrad(C, Cr, P(L.dqT), P(L.actT), G(gr->w_cf2), Cr)) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_colsum<T>(P(L.dXq), M, C, C, Q(L.colpart), G(gr->b_cf2), s));
+  EDIT_LAUNCH(launch_rowsum<T>(P(L.dqT), C, Mp, Mp, G(gr->b_cf2), s));
 
   // LeakyReLU + GroupNorm, then the 3x3 conv: dx += conv(dxc, mirrored taps), dW_cf1 per tap
   EDIT_LAUNCH(launch_gn_bwd<T>(P(L.dact), FP(F.cf_act), FP(F.xc), FF(F.gn_stat), W(w->gn_gamma), g.B, g.N, Cr, g.G,
                                Q(L.gnpart), Q(L.m12), G(gr->gn_gamma), G(gr->gn_beta), P(L.dxc), s));
-  EDIT_LAUNCH(launch_colsum<T>(P(L.dxc), M, Cr, Cr, Q(L.colpart), G(gr->b_cf1), s));
   {
     GemmArgs<T> a{};
     a.M = M; a.N = C; a.K = 9 * Cr; a.A = P(L.dxc); a.lda = Cr; a.H = g.H; a.W = g.W; a.Cin = Cr;
@@ -725,10 +730,11 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
     a.seg_rows = C; a.ldb = 9 * Cr; a.C = P(L.dXc); a.ldc = C;
     EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
   }
-  for (int t = 0; t < 9; ++t) {
-    EDIT_LAUNCH(launch_shift_transpose<T>(P(L.dxc), g.B, g.H, g.W, Cr, P(L.dxcT), Mp, t / 3, t % 3, s));
-    if ((st = wgrad(Cr, C, P(L.dxcT), P(L.xT), G(gr->w_cf1) + (size_t)t * C, 9 * C)) != EDIT_OK) return st;
-  }
+  // dW_cf1[co][t][ci] = sum_m dxc[m + off_t][co] x[m][ci]: the nine shifted copies of dxc stacked as
+  // [9 Cr][tokens], one product whose row t * Cr + co lands at w_cf1 + co * 9C + t * C
+  EDIT_LAUNCH(launch_shift_transpose9<T>(P(L.dxc), g.B, g.H, g.W, Cr, P(L.dxcT9), Mp, s));
+  EDIT_LAUNCH(launch_rowsum<T>(P(L.dxcT9) + (size_t)4 * Cr * Mp, Cr, Mp, Mp, G(gr->b_cf1), s));   // centre tap
+  if ((st = wgrad(9 * Cr, C, P(L.dxcT9), P(L.xT), G(gr->w_cf1), 9 * C, Cr, C)) != EDIT_OK) return st;
   EDIT_LAUNCH(launch_sum3<T>(P(L.dXq), P(L.dXkv), P(L.dXc), (long)M * C, dx, s));
   return EDIT_OK;
 }

@@ -8,6 +8,7 @@
 // products run on the GEMM kernels (with transposed operands where the
 // contraction is over tokens). Every reduction sums in a fixed order, so
 // gradients are bit-for-bit reproducible.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -16,16 +17,17 @@
 namespace edit {
 
 // ---------------------------------------------------------------------------
-// Transpose: out[c][r] = in[r][c] through a 64 x 65 LDS tile. With a shift
-// (the 3x3 conv's tap (ky, kx)): out[c][m] = in[m - off][c] where the pixel
-// of m - off lies inside its image and reads m through that tap, else 0;
-// off = (ky - 1) W + (kx - 1). Rows are tokens b*H*W + y*W + x. Output
+// Transpose: out[c][r] = in[r][c] through a 64 x 65 LDS tile, batched over
+// blockIdx.z (in + z * zin, out + z * zout). With a shift, z is the 3x3
+// conv's tap (ky, kx) = (z / 3, z % 3): out[c][m] = in[m - off][c] where the
+// pixel of m - off lies inside its image and reads m through that tap, else
+// 0; off = (ky - 1) W + (kx - 1). Rows are tokens b*H*W + y*W + x. Output
 // columns rows .. rows_pad - 1 (the row padding of out) are written as zeros.
 // ---------------------------------------------------------------------------
 template <typename T, bool SHIFT>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int rows, int rows_pad, int cols,
-                                                        int ldi, T* __restrict__ out, int ldo, int H, int W, int ky,
-                                                        int kx) {
+                                                        int ldi, T* __restrict__ out, int ldo, int H, int W,
+                                                        long zin, long zout) {
   // 64 x 64 tile; every global access is 16 bytes (EPC elements): a load
   // takes EPC consecutive columns of one row, a store EPC consecutive rows
   // of one column. cols, ldi, ldo and rows_pad are multiples of EPC.
@@ -34,6 +36,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
   typedef uint32_t u32x4t __attribute__((ext_vector_type(4)));
   __shared__ float tile[64][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  in += (long)blockIdx.z * zin;
+  out += (long)blockIdx.z * zout;
+  const int ky = SHIFT ? (int)blockIdx.z / 3 : 1, kx = SHIFT ? (int)blockIdx.z % 3 : 1;
   for (int v = threadIdx.x; v < 64 * VPR; v += 256) {
     const int i = v / VPR, cv = v % VPR;
     const int r = r0 + i, c = c0 + cv * EPC;
@@ -70,94 +75,65 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
 
 template <typename T>
 hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, int ldo, hipStream_t s,
-                            int rows_pad) {
+                            int rows_pad, int batch, long zin, long zout) {
   if (rows_pad < rows) rows_pad = rows;
-  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
   constexpr int EPC = 16 / (int)sizeof(T);
-  if (cols % EPC || ldi % EPC || ldo % EPC || rows_pad % EPC) return hipErrorInvalidValue;
-  dim3 grid((cols + 63) / 64, (rows_pad + 63) / 64);
+  if (cols % EPC || ldi % EPC || ldo % EPC || rows_pad % EPC || zin % EPC || zout % EPC)
+    return hipErrorInvalidValue;
+  dim3 grid((cols + 63) / 64, (rows_pad + 63) / 64, batch);
   hipLaunchKernelGGL((transpose_kernel<T, false>), grid, dim3(256), 0, s, in, rows, rows_pad, cols, ldi, out, ldo, 1,
-                     1, 1, 1);
+                     1, zin, zout);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_shift_transpose(const T* in, int B, int H, int W, int cols, T* out, int ldo, int ky, int kx,
-                                  hipStream_t s) {
+hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, T* out, int ldo, hipStream_t s) {
   const int rows = B * H * W;
   if (rows <= 0 || cols <= 0) return hipSuccess;
   constexpr int EPC = 16 / (int)sizeof(T);
   if (cols % EPC || ldo % EPC || ldo < rows) return hipErrorInvalidValue;
-  dim3 grid((cols + 63) / 64, (ldo + 63) / 64);
+  dim3 grid((cols + 63) / 64, (ldo + 63) / 64, 9);
   hipLaunchKernelGGL((transpose_kernel<T, true>), grid, dim3(256), 0, s, in, rows, ldo, cols, cols, out, ldo, H, W,
-                     ky, kx);
+                     0L, (long)cols * ldo);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Column sums (bias gradients): out[c] = sum_r in[r][c]. A block sums 256
-// rows of 256 columns: 32 lanes of 8 columns (16-byte loads) x 8 row lanes,
-// the row lanes added through LDS (partial[chunk][c]); then the chunks in
-// order. cols and ld are multiples of 8.
+// Row sums (bias gradients): out[r] = sum_m in[r][m] over a transposed
+// [channels][tokens] buffer (the bias gradient is the sum over tokens of the
+// output gradient, whose transpose the weight gradient needs anyway). One
+// wave per row: lanes take 8 tokens at a time (16-byte loads), then a
+// butterfly; a fixed order. len and ld are multiples of 8 (the token padding
+// holds zeros).
 // ---------------------------------------------------------------------------
-constexpr int kColChunk = 256;
-int colsum_chunks(int rows) { return (rows + kColChunk - 1) / kColChunk; }
-
 template <typename T>
-__global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict__ in, int rows, int cols, int ld,
-                                                             float* __restrict__ partial) {
-  __shared__ float red[8][256];
-  const int cg = threadIdx.x & 31, rl = threadIdx.x >> 5, ch = blockIdx.y;
-  const int c0 = (blockIdx.x * 32 + cg) * 8;
-  float acc[8];
+__global__ __launch_bounds__(256) void rowsum_kernel(const T* __restrict__ in, int rows, int len, int ld,
+                                                     T* __restrict__ out, float* __restrict__ out32) {
+  const int r = blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const T* p = in + (size_t)r * ld;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 4
+  for (int i = lane * 8; i < len; i += 512) {
+    float v[8];
+    load8(p + i, v);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  if (c0 < cols) {
-    const int r1 = min(rows, (ch + 1) * kColChunk);
-#pragma unroll 8
-    for (int r = ch * kColChunk + rl; r < r1; r += 8) {
-      float v[8];
-      load8(in + (size_t)r * ld + c0, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
+    for (int k = 0; k < 8; ++k) acc[k] += v[k];
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) red[rl][cg * 8 + i] = acc[i];
-  __syncthreads();
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c < cols) {
-    float t = 0.0f;
-#pragma unroll
-    for (int l = 0; l < 8; ++l) t += red[l][threadIdx.x];
-    partial[(size_t)ch * cols + c] = t;
+  float t = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  t = wave_sum(t);
+  if (lane == 0) {
+    out[r] = from_f32<T>(t);
+    if (out32) out32[r] = t;
   }
 }
 
-// Writes out[c] (T) and, when given, out32[c] (the same sum in f32).
 template <typename T>
-__global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __restrict__ partial, int nchunks,
-                                                              int cols, T* __restrict__ out,
-                                                              float* __restrict__ out32) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= cols) return;
-  float s = 0.0f;
-  for (int ch = 0; ch < nchunks; ++ch) s += partial[(size_t)ch * cols + c];
-  out[c] = from_f32<T>(s);
-  if (out32) out32[c] = s;
-}
-
-template <typename T>
-hipError_t launch_colsum(const T* in, int rows, int cols, int ld, float* partial, T* out, hipStream_t s,
-                         float* out32) {
-  if (cols <= 0) return hipSuccess;
-  const int nch = colsum_chunks(rows);
-  hipLaunchKernelGGL((colsum_partial_kernel<T>), dim3((cols + 255) / 256, nch), dim3(256), 0, s, in, rows, cols, ld,
-                     partial);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((colsum_finalize_kernel<T>), dim3((cols + 255) / 256), dim3(256), 0, s, partial, nch, cols, out,
-                     out32);
+hipError_t launch_rowsum(const T* in, int rows, int len, int ld, T* out, hipStream_t s, float* out32) {
+  if (rows <= 0) return hipSuccess;
+  if (len % 8 || ld % 8 || len > ld) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((rowsum_kernel<T>), dim3((rows + 3) / 4), dim3(256), 0, s, in, rows, len, ld, out, out32);
   return hipGetLastError();
 }
 
@@ -176,28 +152,118 @@ hipError_t launch_zero(T* p, long n, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K reduction: out[r][c] = sum_s part[s][r][c] (ld cols), s in order.
+// Split-K reduction: sum_s part[s][r][c] (row stride cols), s in order, to
+// out[(r % rpg) * ldo + (r / rpg) * gstride + c]: rows come in groups of rpg
+// (the 3x3 conv's taps, each a [C/r][C] block) that interleave in the
+// output row. Four columns per thread.
 // ---------------------------------------------------------------------------
 template <typename O>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S,
                                                             long long stride, int rows, int cols,
-                                                            O* __restrict__ out, int ldo) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+                                                            O* __restrict__ out, int ldo, int rpg, int gstride) {
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= (long long)rows * cols) return;
   const int r = (int)(i / cols), c = (int)(i - (long long)r * cols);
-  float v = 0.0f;
-  for (int s = 0; s < S; ++s) v += part[(size_t)s * stride + i];
-  out[(size_t)r * ldo + c] = from_f32<O>(v);
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
+  for (int s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4*>(part + (size_t)s * stride + i);
+  const float o[4] = {v[0], v[1], v[2], v[3]};
+  store4(out + (size_t)(r % rpg) * ldo + (size_t)(r / rpg) * gstride + c, o);
 }
 
 template <typename O>
 hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int rows, int cols, O* out, int ldo,
-                                hipStream_t s) {
+                                hipStream_t s, int rpg, int gstride) {
   const long long n = (long long)rows * cols;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((splitk_reduce_kernel<O>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, S, stride,
-                     rows, cols, out, ldo);
+  if (rpg <= 0) rpg = rows;
+  if (cols % 4 || ldo % 4 || gstride % 4 || stride % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((splitk_reduce_kernel<O>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, part, S,
+                     stride, rows, cols, out, ldo, rpg, gstride);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-head products on the matrix cores. A head's d x d state matrix M sits
+// in LDS as the A operand of the 32x32x16 step (rows padded to RT*32, K to
+// KS*16 with zeros); for bf16 it is held as two bf16 matrices hi + lo
+// (hi = bf16(M), lo = bf16(M - hi)), so M times a bf16 token row is formed to
+// about fp32 accuracy; for f32 the f32 step takes M itself. A wave takes 32
+// tokens as the B operand's columns (lane l: token l % 32, 8 K values from
+// 8*(l/32)), and the accumulator holds the product transposed: element r of
+// lane l is row 8*(r/4) + 4*(l/32) + r%4 (a channel of the head) of column
+// l % 32 (a token). Per-token dot products over the head's channels add
+// each half-wave's 16 rows per tile and then the two halves (lanes l, l^32).
+// ---------------------------------------------------------------------------
+template <typename T, int KS>
+struct HeadMat {
+  static constexpr int RT = (KS + 1) / 2;                 // 32-row tiles
+  static constexpr int KP = KS * 16 + 16 / (int)sizeof(T);  // padded LDS row (16-byte multiple)
+  static constexpr int NC = sizeof(T) == 2 ? 2 : 1;       // bf16: hi + lo copies
+};
+
+__device__ __forceinline__ bf16x8 frag_ld(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 frag_ld(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
+  return r;
+}
+template <typename F> __device__ __forceinline__ F frag_zero() {
+  F r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = 0;
+  return r;
+}
+__device__ __forceinline__ void load4(const bf16* p, float (&v)[4]) {
+  const bf16x4 t = *reinterpret_cast<const bf16x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = (float)t[i];
+}
+__device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
+  const f32x4 t = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = t[i];
+}
+// M (fp32, element (i, k) at src[i * rs + k * cs], d x d) into the LDS operand.
+// dst holds NC copies of [RT * 32][KP].
+template <typename T, int KS>
+__device__ __forceinline__ void head_mat_fill(T* dst, const float* __restrict__ src, int rs, int cs, int d) {
+  using HM = HeadMat<T, KS>;
+  constexpr int CP = HM::RT * 32 * HM::KP;
+  for (int i = threadIdx.x; i < HM::RT * 32 * KS * 16; i += blockDim.x) {
+    const int row = i / (KS * 16), k = i - row * (KS * 16);
+    const float v = row < d && k < d ? src[row * rs + k * cs] : 0.0f;
+    if constexpr (HM::NC == 2) {
+      const bf16 hi = (bf16)v;
+      dst[row * HM::KP + k] = hi;
+      dst[CP + row * HM::KP + k] = (bf16)(v - (float)hi);
+    } else {
+      dst[row * HM::KP + k] = v;
+    }
+  }
+}
+
+// acc[rt] = M[rt-th 32 rows] x B for the wave's 32 tokens.
+template <typename T, int KS, int RT>
+__device__ __forceinline__ void head_mat_apply(const T* A, const typename Frag<T>::type (&bf)[KS],
+                                               f32x16 (&acc)[RT], int lane) {
+  using HM = HeadMat<T, KS>;
+  constexpr int CP = HM::RT * 32 * HM::KP;
+  const int col = lane & 31, kh = 8 * (lane >> 5);
+#pragma unroll
+  for (int rt = 0; rt < HM::RT; ++rt) acc_zero(acc[rt]);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < HM::RT; ++rt)
+#pragma unroll
+      for (int c = 0; c < HM::NC; ++c) mma32(acc[rt], frag_ld(A + c * CP + (rt * 32 + col) * HM::KP + ks * 16 + kh), bf[ks]);
+}
+
+// The wave's 32-token tiles: tiles_per_wave consecutive tiles from tile0.
+__device__ __forceinline__ int head_tile0(int tiles_per_wave) {
+  return (blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * tiles_per_wave;
 }
 
 // ---------------------------------------------------------------------------
@@ -206,112 +272,118 @@ hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int 
 //   den = q . z + eps, t = S dy (t[a] = sum_n S[a][n] dy[n]),
 //   dy . y = q . t / den, c = -(dy . y) / den, g = dy / den,
 //   dq = t / den + c z, then the outer ReLU of the queries: dq_pre = dq where q > 0.
-// dy . y is formed from q, S and dy in fp32 rather than from the stored y:
-// the two terms of dq nearly cancel (y does not change when q is scaled), so
-// y's rounding would be amplified. One thread per token (256 per block, one
-// head); the token's dy in registers, S row-major in LDS (a row of S is read
-// as broadcast 16-byte words); t is formed twice, eight outputs at a time
-// (once for dy . y, once for dq). g (T) and c (f32) are kept for the state
-// gradient dS = sum q^T g, dz = sum c q.
+// dy . y is formed from q and t rather than from the stored y: the two
+// terms of dq nearly cancel (y does not change when q is scaled), so y's
+// rounding would be amplified. g (T) and c (f32) are kept for the state
+// gradient dS = sum q^T g, dz = sum c q. Block: 4 waves of one (sample,
+// head); t^T = S dy^T on the matrix cores.
 // ---------------------------------------------------------------------------
-constexpr int kBwdTok = 256;
-
-// acc[i] += sum_n r[n] M[(a0 + i) * d + n], i < 8 (M row-major in LDS).
-template <int d>
-__device__ __forceinline__ void rows8_dot(const float* M, int a0, const float (&r)[d], float (&acc)[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float* row = M + (a0 + i) * d;
-    float s = 0.0f;
-#pragma unroll
-    for (int n = 0; n < d; n += 4) {
-      const f32x4 m = *reinterpret_cast<const f32x4*>(row + n);
-      s += r[n] * m[0] + r[n + 1] * m[1] + r[n + 2] * m[2] + r[n + 3] * m[3];
-    }
-    acc[i] += s;
-  }
-}
-
-template <typename T, int DC>
-__global__ __launch_bounds__(kBwdTok) void attn_bwd_q_kernel(const T* __restrict__ dy, const T* __restrict__ q,
-                                                             const float* __restrict__ S,
-                                                             const float* __restrict__ z, int N, int heads,
-                                                             float eps, T* __restrict__ g_out,
-                                                             float* __restrict__ c_out, T* __restrict__ dq_pre) {
-  constexpr int d = 8 * DC;
-  __shared__ __attribute__((aligned(16))) float Ss[d * d];
-  __shared__ float zs[d];
-  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int C = heads * d;
+template <typename T, int KS>
+__global__ __launch_bounds__(256) void attn_bwd_q_kernel(const T* __restrict__ dy, const T* __restrict__ q,
+                                                         const float* __restrict__ S,
+                                                         const float* __restrict__ z, int N, int heads, int d,
+                                                         float eps, int tiles_per_wave, T* __restrict__ g_out,
+                                                         float* __restrict__ c_out, T* __restrict__ dq_pre) {
+  using HM = HeadMat<T, KS>;
+  using F = typename Frag<T>::type;
+  __shared__ __attribute__((aligned(16))) T As[HM::NC * HM::RT * 32 * HM::KP];
+  __shared__ float zs[HM::RT * 32];
+  const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
+  const int C = heads * d, col = lane & 31, half = lane >> 5;
   const size_t bh = (size_t)b * heads + h;
-  for (int i = tid; i < d * d; i += kBwdTok) Ss[i] = S[bh * d * d + i];
-  for (int i = tid; i < d; i += kBwdTok) zs[i] = z[bh * d + i];
+  head_mat_fill<T, KS>(As, S + bh * d * d, d, 1, d);
+  for (int i = threadIdx.x; i < HM::RT * 32; i += blockDim.x) zs[i] = i < d ? z[bh * d + i] : 0.0f;
   __syncthreads();
-  const int tok = blockIdx.x * kBwdTok + tid;
-  if (tok >= N) return;
-  const size_t row = ((size_t)b * N + tok) * C + (size_t)h * d;
-  float dv[d];
-  float den = eps;
+  const int t0 = head_tile0(tiles_per_wave);
+  for (int t = 0; t < tiles_per_wave; ++t) {
+    const int tok0 = (t0 + t) * 32;
+    if (tok0 >= N) break;
+    const int tok = tok0 + col;
+    const bool valid = tok < N;
+    const size_t row = ((size_t)b * N + (valid ? tok : 0)) * C + (size_t)h * d;
+    F bf[KS];
 #pragma unroll
-  for (int c8 = 0; c8 < DC; ++c8) {
-    float qv[8], v[8];
-    load8(q + row + 8 * c8, qv);
-    load8(dy + row + 8 * c8, v);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      den += qv[i] * zs[8 * c8 + i];
-      dv[8 * c8 + i] = v[i];
+    for (int ks = 0; ks < KS; ++ks) {
+      const int k = ks * 16 + 8 * half;
+      bf[ks] = valid && k < d ? frag_ld(dy + row + k) : frag_zero<F>();
     }
-  }
-  const float inv = 1.0f / den;
-  float qt = 0.0f;
-#pragma unroll 1
-  for (int a0 = 0; a0 < d; a0 += 8) {
-    float t[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qv[8];
-    rows8_dot<d>(Ss, a0, dv, t);
-    load8(q + row + a0, qv);
+    f32x16 acc[HM::RT];
+    head_mat_apply<T, KS, HM::RT>(As, bf, acc, lane);
+    float qv[HM::RT][16];
+    float den = 0.0f, qt = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) qt += qv[i] * t[i];
-  }
-  const float c = -qt * inv * inv;
-  c_out[((size_t)b * N + tok) * heads + h] = c;
+    for (int rt = 0; rt < HM::RT; ++rt)
 #pragma unroll
-  for (int c8 = 0; c8 < DC; ++c8) {
-    float go[8];
+      for (int g = 0; g < 4; ++g) {
+        const int a0 = rt * 32 + 8 * g + 4 * half;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (valid && a0 < d) load4(q + row + a0, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) go[i] = dv[8 * c8 + i] * inv;
-    store8(g_out + row + 8 * c8, go);
-  }
-#pragma unroll 1
-  for (int a0 = 0; a0 < d; a0 += 8) {
-    float t[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qv[8], o[8];
-    rows8_dot<d>(Ss, a0, dv, t);
-    load8(q + row + a0, qv);
+        for (int i = 0; i < 4; ++i) {
+          qv[rt][4 * g + i] = v[i];
+          den += v[i] * zs[a0 + i];
+          qt += v[i] * acc[rt][4 * g + i];
+        }
+      }
+    den += __shfl_xor(den, 32, kWave) + eps;
+    qt += __shfl_xor(qt, 32, kWave);
+    const float inv = 1.0f / den;
+    const float c = -qt * inv * inv;
+    if (!valid) continue;
+    if (half == 0) c_out[((size_t)b * N + tok) * heads + h] = c;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float v = t[i] * inv + c * zs[a0 + i];
-      o[i] = qv[i] > 0.0f ? v : 0.0f;
+    for (int rt = 0; rt < HM::RT; ++rt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int a0 = rt * 32 + 8 * g + 4 * half;
+        if (a0 >= d) continue;
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = acc[rt][4 * g + i] * inv + c * zs[a0 + i];
+          o[i] = qv[rt][4 * g + i] > 0.0f ? v : 0.0f;
+        }
+        store4(dq_pre + row + a0, o);
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int k = ks * 16 + 8 * half;
+      if (k >= d) continue;
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = (float)bf[ks][i] * inv;
+      store8(g_out + row + k, o);
     }
-    store8(dq_pre + row + a0, o);
   }
 }
+
+// Tiles per wave so that about 1024 blocks cover the (sample, head) pairs.
+static int head_tiles_per_wave(int B, int heads, int ntok) {
+  const int tiles = (ntok + 31) / 32;
+  const int pairs = B * heads;
+  const int blocks_per_pair = std::max(1, 1024 / std::max(1, pairs));
+  return std::max(1, (tiles + 4 * blocks_per_pair - 1) / (4 * blocks_per_pair));
+}
+
+#define EDIT_KS_SWITCH(KSV_MACRO)                                                                          \
+  switch ((d + 15) / 16) {                                                                                 \
+    KSV_MACRO(1) KSV_MACRO(2) KSV_MACRO(3) KSV_MACRO(4) KSV_MACRO(5) KSV_MACRO(6) KSV_MACRO(7) KSV_MACRO(8) \
+    default: return hipErrorInvalidValue;                                                                  \
+  }
 
 template <typename T>
 hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const float* z, int B, int N, int heads, int d,
                              float eps, T* g, float* c, T* dq_pre, hipStream_t s) {
-  dim3 grid((N + kBwdTok - 1) / kBwdTok, heads, B);
-  switch (d / 8) {
-#define EDIT_BQ_CASE(DCV)                                                                                       \
-  case DCV:                                                                                                     \
-    hipLaunchKernelGGL((attn_bwd_q_kernel<T, DCV>), grid, dim3(kBwdTok), 0, s, dy, q, S, z, N, heads, eps, g, c, \
-                       dq_pre);                                                                                 \
+  if (d % 8 || d > 128 || N <= 0) return N <= 0 ? hipSuccess : hipErrorInvalidValue;
+  const int tpw = head_tiles_per_wave(B, heads, N);
+  dim3 grid(((N + 31) / 32 + 4 * tpw - 1) / (4 * tpw), heads, B);
+#define EDIT_BQ_CASE(KSV)                                                                                       \
+  case KSV:                                                                                                     \
+    hipLaunchKernelGGL((attn_bwd_q_kernel<T, KSV>), grid, dim3(256), 0, s, dy, q, S, z, N, heads, d, eps, tpw, g, \
+                       c, dq_pre);                                                                              \
     break;
-    EDIT_BQ_CASE(1) EDIT_BQ_CASE(2) EDIT_BQ_CASE(3) EDIT_BQ_CASE(4) EDIT_BQ_CASE(5) EDIT_BQ_CASE(6)
-    EDIT_BQ_CASE(7) EDIT_BQ_CASE(8) EDIT_BQ_CASE(9) EDIT_BQ_CASE(10) EDIT_BQ_CASE(11) EDIT_BQ_CASE(12)
-    EDIT_BQ_CASE(13) EDIT_BQ_CASE(14) EDIT_BQ_CASE(15) EDIT_BQ_CASE(16)
+  EDIT_KS_SWITCH(EDIT_BQ_CASE)
 #undef EDIT_BQ_CASE
-    default: return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 
@@ -321,85 +393,95 @@ hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const floa
 //   dK'_j = V'_j dS^T + dz, then the keys' ReLU (where K'_j > 0),
 //   dV'_j = K'_j dS.
 // Writes dkv [B][Nc][2C]: the keys' gradient before their ReLU | the values'.
-// One thread per token, its V' and K' rows in registers; dS and dS^T
-// row-major in LDS, eight outputs at a time.
+// On the matrix cores: dK'^T = dS V'^T (A operand dS) and dV'^T = dS^T K'^T
+// (A operand dS^T), 32 compressed tokens per wave.
 // ---------------------------------------------------------------------------
-template <typename T, int DC>
-__global__ __launch_bounds__(kBwdTok) void kv_bwd_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
-                                                         const float* __restrict__ dS, const float* __restrict__ dz,
-                                                         int Nc, int heads, T* __restrict__ dkv) {
-  constexpr int d = 8 * DC;
-  __shared__ __attribute__((aligned(16))) float Ss[d * d];    // dS[a][n]
-  __shared__ __attribute__((aligned(16))) float St[d * d];    // dS^T: St[n][a] = dS[a][n]
-  __shared__ float zs[d];
-  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-  const int C = heads * d;
+template <typename T, int KS>
+__global__ __launch_bounds__(256) void kv_bwd_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
+                                                     const float* __restrict__ dS, const float* __restrict__ dz,
+                                                     int Nc, int heads, int d, int tiles_per_wave,
+                                                     T* __restrict__ dkv) {
+  using HM = HeadMat<T, KS>;
+  using F = typename Frag<T>::type;
+  __shared__ __attribute__((aligned(16))) T A1[HM::NC * HM::RT * 32 * HM::KP];   // dS
+  __shared__ __attribute__((aligned(16))) T A2[HM::NC * HM::RT * 32 * HM::KP];   // dS^T
+  __shared__ float zs[HM::RT * 32];
+  const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
+  const int C = heads * d, col = lane & 31, half = lane >> 5;
   const size_t bh = (size_t)b * heads + h;
-  for (int i = tid; i < d * d; i += kBwdTok) {
-    const float v = dS[bh * d * d + i];
-    const int a = i / d, n = i - a * d;
-    Ss[i] = v;
-    St[n * d + a] = v;
-  }
-  for (int i = tid; i < d; i += kBwdTok) zs[i] = dz[bh * d + i];
+  head_mat_fill<T, KS>(A1, dS + bh * d * d, d, 1, d);
+  head_mat_fill<T, KS>(A2, dS + bh * d * d, 1, d, d);
+  for (int i = threadIdx.x; i < HM::RT * 32; i += blockDim.x) zs[i] = i < d ? dz[bh * d + i] : 0.0f;
   __syncthreads();
-  const int tok = blockIdx.x * kBwdTok + tid;
-  if (tok >= Nc) return;
-  const size_t row = ((size_t)b * Nc + tok) * C + (size_t)h * d;
-  T* out = dkv + ((size_t)b * Nc + tok) * 2 * C + (size_t)h * d;
-  float r[d];
-  // keys: dK'[a] = sum_n dS[a][n] V'[n] + dz[a], masked by K' > 0
+  const int t0 = head_tile0(tiles_per_wave);
+  for (int t = 0; t < tiles_per_wave; ++t) {
+    const int tok0 = (t0 + t) * 32;
+    if (tok0 >= Nc) break;
+    const int tok = tok0 + col;
+    const bool valid = tok < Nc;
+    const size_t row = ((size_t)b * Nc + (valid ? tok : 0)) * C + (size_t)h * d;
+    T* out = dkv + ((size_t)b * Nc + (valid ? tok : 0)) * 2 * C + (size_t)h * d;
+    F bf[KS];
+    f32x16 acc[HM::RT];
+    // keys: dK'^T = dS V'^T, + dz, masked by K' > 0
 #pragma unroll
-  for (int c8 = 0; c8 < DC; ++c8) {
-    float v[8];
-    load8(vc + row + 8 * c8, v);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int k = ks * 16 + 8 * half;
+      bf[ks] = valid && k < d ? frag_ld(vc + row + k) : frag_zero<F>();
+    }
+    head_mat_apply<T, KS, HM::RT>(A1, bf, acc, lane);
+    if (valid) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[8 * c8 + i] = v[i];
-  }
-#pragma unroll 1
-  for (int a0 = 0; a0 < d; a0 += 8) {
-    float acc[8], kv[8];
+      for (int rt = 0; rt < HM::RT; ++rt)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = zs[a0 + i];
-    rows8_dot<d>(Ss, a0, r, acc);
-    load8(kc + row + a0, kv);
+        for (int g = 0; g < 4; ++g) {
+          const int a0 = rt * 32 + 8 * g + 4 * half;
+          if (a0 >= d) continue;
+          float kv[4], o[4];
+          load4(kc + row + a0, kv);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = kv[i] > 0.0f ? acc[i] : 0.0f;
-    store8(out + a0, acc);
-  }
-  // values: dV'[n] = sum_m K'[m] dS[m][n] = (dS^T K')[n]
+          for (int i = 0; i < 4; ++i) o[i] = kv[i] > 0.0f ? acc[rt][4 * g + i] + zs[a0 + i] : 0.0f;
+          store4(out + a0, o);
+        }
+    }
+    // values: dV'^T = dS^T K'^T
 #pragma unroll
-  for (int c8 = 0; c8 < DC; ++c8) {
-    float k[8];
-    load8(kc + row + 8 * c8, k);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int k = ks * 16 + 8 * half;
+      bf[ks] = valid && k < d ? frag_ld(kc + row + k) : frag_zero<F>();
+    }
+    head_mat_apply<T, KS, HM::RT>(A2, bf, acc, lane);
+    if (valid) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[8 * c8 + i] = k[i];
-  }
-#pragma unroll 1
-  for (int n0 = 0; n0 < d; n0 += 8) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    rows8_dot<d>(St, n0, r, acc);
-    store8(out + C + n0, acc);
+      for (int rt = 0; rt < HM::RT; ++rt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n0 = rt * 32 + 8 * g + 4 * half;
+          if (n0 >= d) continue;
+          float o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = acc[rt][4 * g + i];
+          store4(out + C + n0, o);
+        }
+    }
   }
 }
 
 template <typename T>
 hipError_t launch_kv_bwd(const T* kc, const T* vc, const float* dS, const float* dz, int B, int Nc, int heads,
                          int d, T* dkv, hipStream_t s) {
-  dim3 grid((Nc + kBwdTok - 1) / kBwdTok, heads, B);
-  switch (d / 8) {
-#define EDIT_BKV_CASE(DCV)                                                                                  \
-  case DCV:                                                                                                 \
-    hipLaunchKernelGGL((kv_bwd_kernel<T, DCV>), grid, dim3(kBwdTok), 0, s, kc, vc, dS, dz, Nc, heads, dkv); \
+  if (d % 8 || d > 128 || Nc <= 0) return Nc <= 0 ? hipSuccess : hipErrorInvalidValue;
+  const int tpw = head_tiles_per_wave(B, heads, Nc);
+  dim3 grid(((Nc + 31) / 32 + 4 * tpw - 1) / (4 * tpw), heads, B);
+#define EDIT_BKV_CASE(KSV)                                                                                        \
+  case KSV:                                                                                                       \
+    hipLaunchKernelGGL((kv_bwd_kernel<T, KSV>), grid, dim3(256), 0, s, kc, vc, dS, dz, Nc, heads, d, tpw, dkv); \
     break;
-    EDIT_BKV_CASE(1) EDIT_BKV_CASE(2) EDIT_BKV_CASE(3) EDIT_BKV_CASE(4) EDIT_BKV_CASE(5) EDIT_BKV_CASE(6)
-    EDIT_BKV_CASE(7) EDIT_BKV_CASE(8) EDIT_BKV_CASE(9) EDIT_BKV_CASE(10) EDIT_BKV_CASE(11) EDIT_BKV_CASE(12)
-    EDIT_BKV_CASE(13) EDIT_BKV_CASE(14) EDIT_BKV_CASE(15) EDIT_BKV_CASE(16)
+  EDIT_KS_SWITCH(EDIT_BKV_CASE)
 #undef EDIT_BKV_CASE
-    default: return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
+#undef EDIT_KS_SWITCH
 
 // ---------------------------------------------------------------------------
 // Depthwise 3x3 stride-2 backward (section "Spatial Compressor"), over the
@@ -734,31 +816,6 @@ hipError_t launch_gn_bwd(const T* dact, const T* act, const T* xc, const float* 
 }
 
 // ---------------------------------------------------------------------------
-// Weight rearrangements for the input-gradient GEMMs (C = A B^T needs B as
-// [N][K]): the 3x3 conv's input gradient is a 3x3 conv of dxc with the taps
-// mirrored and the channel roles swapped,
-//   wflip[ci][t * Co + co] = w[co][8 - t][ci]   (w is [Co][3][3][Ci]).
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void conv_weight_flip_kernel(const T* __restrict__ w, int Co, int Ci,
-                                                               T* __restrict__ wflip) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  const long total = (long)Ci * 9 * Co;
-  if (i >= total) return;
-  const int ci = (int)(i / (9 * Co)), rest = (int)(i - (long)ci * 9 * Co);
-  const int t = rest / Co, co = rest - t * Co;
-  wflip[i] = w[((size_t)co * 9 + (8 - t)) * Ci + ci];
-}
-
-template <typename T>
-hipError_t launch_conv_weight_flip(const T* w, int Co, int Ci, T* wflip, hipStream_t s) {
-  const long total = (long)Ci * 9 * Co;
-  hipLaunchKernelGGL((conv_weight_flip_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w, Co, Ci,
-                     wflip);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // Small fp32 products for the folded query weights' gradients:
 //   out[i][j] = (add ? add[i][j] : 0) + (ru ? ru[i] rv[j] : 0) + sum_k A(i, k) B(k, j),
 // A(i, k) = A[i * ars + k * acs], B(k, j) = B[k * brs + j * bcs] (any strides,
@@ -850,11 +907,12 @@ hipError_t launch_sum3(const T* a, const T* b, const T* c, long n, T* out, hipSt
 }
 
 #define EDIT_INST(T)                                                                                               \
-  template hipError_t launch_transpose<T>(const T*, int, int, int, T*, int, hipStream_t, int);                     \
-  template hipError_t launch_shift_transpose<T>(const T*, int, int, int, int, T*, int, int, int, hipStream_t);     \
-  template hipError_t launch_colsum<T>(const T*, int, int, int, float*, T*, hipStream_t, float*);                  \
+  template hipError_t launch_transpose<T>(const T*, int, int, int, T*, int, hipStream_t, int, int, long, long);   \
+  template hipError_t launch_shift_transpose9<T>(const T*, int, int, int, int, T*, int, hipStream_t);              \
+  template hipError_t launch_rowsum<T>(const T*, int, int, int, T*, hipStream_t, float*);                         \
   template hipError_t launch_zero<T>(T*, long, hipStream_t);                                                       \
-  template hipError_t launch_splitk_reduce<T>(const float*, int, long long, int, int, T*, int, hipStream_t);       \
+  template hipError_t launch_splitk_reduce<T>(const float*, int, long long, int, int, T*, int, hipStream_t, int,  \
+                                              int);                                                               \
   template hipError_t launch_attn_bwd_q<T>(const T*, const T*, const float*, const float*, int, int, int, int,     \
                                            float, T*, float*, T*, hipStream_t);                                    \
   template hipError_t launch_kv_bwd<T>(const T*, const T*, const float*, const float*, int, int, int, int, T*,     \
@@ -864,7 +922,6 @@ hipError_t launch_sum3(const T* a, const T* b, const T* c, long n, T* out, hipSt
                                               hipStream_t);                                                        \
   template hipError_t launch_gn_bwd<T>(const T*, const T*, const T*, const float*, const T*, int, int, int, int,   \
                                        float*, float*, T*, T*, T*, hipStream_t);                                   \
-  template hipError_t launch_conv_weight_flip<T>(const T*, int, int, T*, hipStream_t);                             \
   template hipError_t launch_sum3<T>(const T*, const T*, const T*, long, T*, hipStream_t);
 EDIT_INST(bf16)
 EDIT_INST(float)

@@ -100,7 +100,11 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_n = (p.N + BN - 1) / BN;
-  const int nk = AM == A_CONV3 ? 9 * (p.Cin / 64) : (p.K + 63) / 64;
+  const int tiles_mn = ((p.M + BM - 1) / BM) * tiles_n;
+  // K steps of the current tile; E_F32 (split K): tile index = split * tiles_mn
+  // + output tile, the split covering K range [kb, kb + ktot).
+  int nk = AM == A_CONV3 ? 9 * (p.Cin / 64) : (p.K + 63) / 64;
+  int ktot = p.K, split = 0;
   const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, (uint32_t)((size_t)p.M * p.lda * 2));
   // A_CAT2: K steps 0 .. nk1-1 read A, the rest read A2 (K1 is a multiple of 64).
   const __amdgpu_buffer_rsrc_t rsA2 = make_rsrc(AM == A_CAT2 ? p.A2 : p.A,
@@ -133,7 +137,15 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
   uint32_t amask[AM == A_CONV3 ? NA : 1];
 #define EDIT_SET_TILE(tl_)                                                                        \
   do {                                                                                            \
-    const int tile_ = xcd_swizzle((tl_), ntiles);                                                 \
+    int tile_ = xcd_swizzle((tl_), ntiles);                                                       \
+    uint32_t kb_ = 0;                                                                             \
+    if (EM == E_F32) {                                                                            \
+      split = tile_ / tiles_mn;                                                                   \
+      tile_ -= split * tiles_mn;                                                                  \
+      kb_ = (uint32_t)split * (uint32_t)p.kchunk;                                                 \
+      ktot = min(p.kchunk, p.K - (int)kb_);                                                       \
+      nk = (ktot + 63) / 64;                                                                      \
+    }                                                                                             \
     m0 = (tile_ / tiles_n) * BM;                                                                  \
     n0 = (tile_ % tiles_n) * BN;                                                                  \
     const int seg_ = n0 / p.seg_rows;   /* BN divides seg_rows */                                 \
@@ -145,7 +157,7 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
       const int r = 8 * (a * NW + wave) + lr;                                                     \
       const int c = pc ^ ((r >> 1) & 7);                                                          \
       const int m = m0 + r;                                                                       \
-      aoff[a] = m < p.M ? (uint32_t)m * (uint32_t)p.lda * 2u + (uint32_t)c * 16u : kOob;          \
+      aoff[a] = m < p.M ? (uint32_t)m * (uint32_t)p.lda * 2u + (uint32_t)c * 16u + 2u * kb_ : kOob; \
       if (AM == A_CAT2)                                                                           \
         aoff2[AM == A_CAT2 ? a : 0] = m < p.M ? (uint32_t)m * (uint32_t)p.lda2 * 2u + (uint32_t)c * 16u : kOob; \
       if (AM == A_CONV3) {                                                                        \
@@ -164,7 +176,7 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
     _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                              \
       const int r = 8 * (b * NW + wave) + lr;                                                     \
       const int c = pc ^ ((r >> 1) & 7);                                                          \
-      boff[b] = n0 + r < p.N ? (uint32_t)(nseg0 + r) * (uint32_t)p.ldb * 2u + (uint32_t)c * 16u : kOob; \
+      boff[b] = n0 + r < p.N ? (uint32_t)(nseg0 + r) * (uint32_t)p.ldb * 2u + (uint32_t)c * 16u + 2u * kb_ : kOob; \
     }                                                                                             \
   } while (0)
 
@@ -190,8 +202,8 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
     const __amdgpu_buffer_rsrc_t rsa_ = sec_ ? rsA2 : rsA;                                        \
     if (AM == A_CAT2) sa = (uint32_t)(sec_ ? kd_ - nk1 : kd_) * 128u;                             \
     /* K tail: chunks at or past K read zeros (A and B), so they add nothing */                  \
-    const bool ktail_ = AM != A_CONV3 && kd_ * 64 + 64 > p.K;                                     \
-    const int klim_ = p.K - kd_ * 64;                                                             \
+    const bool ktail_ = AM != A_CONV3 && kd_ * 64 + 64 > ktot;                                    \
+    const int klim_ = ktot - kd_ * 64;                                                            \
     _Pragma("unroll") for (int a = 0; a < NA; ++a) {                                              \
       uint32_t v = aoff[a];                                                                       \
       if (AM == A_CONV3) v = ((amask[AM == A_CONV3 ? a : 0] >> tap) & 1u) ? v + (uint32_t)tapoff : kOob; \
@@ -309,13 +321,15 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
   EDIT_PREFETCH3();
   for (;;) {
     // The tile's bias, requested before anything else is queued behind it.
+    if (EM != E_F32) {
 #pragma unroll
-    for (int c = 0; c < CJ; ++c)
+      for (int c = 0; c < CJ; ++c)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int nl = wn * WTN + c * 32 + 8 * g + 4 * fh;
-        bv[c][g] = n0 + nl < p.N ? *reinterpret_cast<const bf16x4*>(bias + nl) : bf16x4{};
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int nl = wn * WTN + c * 32 + 8 * g + 4 * fh;
+          bv[c][g] = n0 + nl < p.N ? *reinterpret_cast<const bf16x4*>(bias + nl) : bf16x4{};
+        }
+    }
 #pragma unroll
     for (int t = 0; t < TI; ++t)
 #pragma unroll
@@ -358,11 +372,32 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
     // The last step's barrier came after every wave's last LDS read: the
     // stages are free. Queue the next tile's first three steps, then write
     // this tile from registers while they are in flight.
-    const int em0 = m0, en0 = n0;
+    const int em0 = m0, en0 = n0, esplit = split;
     const int next = tl + (int)gridDim.x;
     if (next < ntiles) {
       EDIT_SET_TILE(next);
       EDIT_PREFETCH3();
+    }
+    if (EM == E_F32) {
+      // Split-K partial sums in fp32: quad g of lane l is 4 consecutive
+      // columns 8g + 4(l >> 5) .. +3 of row l & 31, one 16-byte store.
+      float* outp = p.Cf + (size_t)esplit * (size_t)p.split_stride;
+#pragma unroll
+      for (int t = 0; t < TI; ++t) {
+        const int m = em0 + wm * WTM + t * 32 + fr;
+#pragma unroll
+        for (int c = 0; c < CJ; ++c)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = en0 + wn * WTN + c * 32 + 8 * g + 4 * fh;
+            if (m < p.M && n < p.N)
+              *reinterpret_cast<f32x4*>(outp + (size_t)m * p.ldc + n) =
+                  f32x4{acc[t][c][4 * g], acc[t][c][4 * g + 1], acc[t][c][4 * g + 2], acc[t][c][4 * g + 3]};
+          }
+      }
+      if (next >= ntiles) break;
+      tl = next;
+      continue;
     }
     // Epilogue: bias (+ ReLU). Accumulator quad g of lane l holds channels
     // 8g + 4(l >> 5) .. +3 of token l & 31; lanes l and l ^ 32 swap the
@@ -444,7 +479,8 @@ hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, hipStream_t s) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidDevice;
-  const int ntiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  int ntiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  if (EM == E_F32) ntiles *= (a.K + a.kchunk - 1) / a.kchunk;
   const int g8 = cus / 8 * 8;
   const int blocks = ST == 2 || ntiles <= g8 || a.spread ? ntiles : g8;
   hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, AM, EM, ST>), dim3(blocks), dim3(64 * WM * WN), 0, s, a, ntiles);
@@ -483,6 +519,13 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
     if (a.K1 % 64 != 0 || a.K1 >= a.K || a.lda2 % 8 != 0 || (size_t)a.M * a.lda2 * 2 >= kOob)
       return hipErrorNotSupported;
     if (n192 && em == E_BIAS_RELU) return launch_dma_tiles<128, 192, 2, 2, A_CAT2, E_BIAS_RELU, 2>(a, s);
+    return hipErrorNotSupported;
+  }
+  if (am == A_PLAIN && em == E_F32) {
+    // Split-K weight gradients (K = tokens): every split is a multiple of 64.
+    if (a.kchunk <= 0 || a.kchunk % 64 != 0 || a.ldc % 4 != 0) return hipErrorNotSupported;
+    if (n192) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_F32, 2>(a, s);
+    if (n96) return launch_dma_tiles<128, 96, 4, 1, A_PLAIN, E_F32, 2>(a, s);
     return hipErrorNotSupported;
   }
   if (am == A_PLAIN && n192) {

@@ -40,8 +40,9 @@ struct GemmArgs {
   int ldc;
   int spread;                  // 1: one block per tile, so that the hardware hands tiles to CUs as
                                // they free up (for GEMMs that share the chip with another stream)
-  // E_F32 (register-staged kernel): K is cut into slices of kchunk (a multiple of 64), one per
-  // grid row; slice s writes Cf + s * split_stride with row stride ldc.
+  // E_F32: K is cut into slices of kchunk (a multiple of 64); slice s writes Cf + s * split_stride
+  // with row stride ldc (register-staged kernel: one grid row per slice; DMA kernel: tile index
+  // = slice * output tiles + output tile).
   float* Cf;
   long long split_stride;
   int kchunk;
@@ -94,28 +95,25 @@ hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int 
 int kv_state_chunks(int Nc);
 
 // ---- backward (backward.hip) ----
-// out[c][r] = in[r][c] (row strides ldi, ldo).
+// out[c][r] = in[r][c] (row strides ldi, ldo), for z < batch at in + z * zin, out + z * zout.
 // Output columns rows .. rows_pad - 1 are written as zeros.
 template <typename T>
 hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, int ldo, hipStream_t s,
-                            int rows_pad = 0);
-// out[c][m'] = in[m' - off][c] for the 3x3 conv's tap (ky, kx), zero where
-// that tap does not connect the two pixels (and in the padding up to ldo);
-// in is [B*H*W][cols], out [cols][ldo].
+                            int rows_pad = 0, int batch = 1, long zin = 0, long zout = 0);
+// For every tap t = 3 ky + kx of the 3x3 conv: out[t][c][m'] = in[m' - off][c],
+// zero where that tap does not connect the two pixels (and in the padding up
+// to ldo); in is [B*H*W][cols], out [9][cols][ldo].
 template <typename T>
-hipError_t launch_shift_transpose(const T* in, int B, int H, int W, int cols, T* out, int ldo, int ky, int kx,
-                                  hipStream_t s);
-// out[c] = sum_r in[r][c] in a fixed order (partial: colsum_chunks(rows) x cols floats); out32 optional.
-int colsum_chunks(int rows);
+hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, T* out, int ldo, hipStream_t s);
+// out[r] = sum_m in[r][m] for m < len (a transposed [channels][tokens] buffer), fixed order; out32 optional.
 template <typename T>
-hipError_t launch_colsum(const T* in, int rows, int cols, int ld, float* partial, T* out, hipStream_t s,
-                         float* out32 = nullptr);
+hipError_t launch_rowsum(const T* in, int rows, int len, int ld, T* out, hipStream_t s, float* out32 = nullptr);
 template <typename T>
 hipError_t launch_zero(T* p, long n, hipStream_t s);
-// out[r][c] = sum_s part[s * stride + r * cols + c].
+// out[(r % rpg) * ldo + (r / rpg) * gstride + c] = sum_s part[s * stride + r * cols + c] (rpg 0: rows).
 template <typename O>
 hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int rows, int cols, O* out, int ldo,
-                                hipStream_t s);
+                                hipStream_t s, int rpg = 0, int gstride = 0);
 // Linear-attention backward, query side: g = dy / den, c = -(dy . y) / den, dq_pre = (g S^T + c z) where q > 0.
 template <typename T>
 hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const float* z, int B, int N, int heads, int d,
@@ -137,9 +135,6 @@ int gn_bwd_chunks(int N);
 template <typename T>
 hipError_t launch_gn_bwd(const T* dact, const T* act, const T* xc, const float* stat, const T* gamma, int B, int N,
                          int C, int G, float* partial, float* m12, T* dgamma, T* dbeta, T* dxc, hipStream_t s);
-// wflip[ci][t * Co + co] = w[co][8 - t][ci].
-template <typename T>
-hipError_t launch_conv_weight_flip(const T* w, int Co, int Ci, T* wflip, hipStream_t s);
 // out[i][j] = add[i][j] + ru[i] rv[j] + sum_k A[i * ars + k * acs] B[k * brs + j * bcs] (add, ru optional).
 template <typename TA, typename TB, typename TO>
 hipError_t launch_small_matmul(int M, int N, int K, const TA* A, long ars, long acs, const TB* Bm, long brs, long bcs,
