@@ -543,10 +543,10 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
 // (split-K) written as fp32 partials and added in slice order.
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-  size_t zeros, w_oT, wqT, wkvT, wflip, dy, g, cvec, dq_pre, dS, dz, st, zp, kvpart, dkv, dk0v0, dXq, dXkv, dXc;
+  size_t zeros, w_oT, wqT, wkvT, wflip, dy, g, cvec, dq_pre, dS, dz, st, zp, kvpart, dkv, dk0v0, dXq, dXkv;
   size_t dact, dxc, doutT, yT, xT, dqT, actT, dkvT, dxcT9, skpart, dWx, dWa, dbq32, dwpart, gnpart, m12;
   size_t total;
-  int Mp;
+  int Mp, Crp;   // tokens rounded up to 8; C/r rounded up to 64 (the conv input gradient's channel stride)
 };
 
 struct SplitK {
@@ -577,16 +577,18 @@ BwdLayout make_bwd_layout(const Geometry& g) {
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   const size_t M = g.M, Mc = (size_t)g.B * g.Nc, C = g.C, Cr = g.Cr, es = g.es, BH = (size_t)g.B * g.heads;
   L.Mp = (int)((M + 7) / 8 * 8);
-  const size_t Mp = L.Mp;
+  L.Crp = (int)((Cr + 63) / 64 * 64);
+  const size_t Mp = L.Mp, Crp = L.Crp;
   L.zeros = take(2 * C * es);
   L.w_oT = take(C * C * es);
   L.wqT = take((C + Cr) * C * es);
   L.wkvT = take(C * 2 * C * es);
-  L.wflip = take(C * 9 * Cr * es);
+  L.wflip = take(C * 9 * Crp * es);
   L.dy = take(M * C * es);
   L.g = take(M * C * es);
   L.cvec = take(M * g.heads * 4);
   L.dq_pre = take(M * C * es);
+  L.dXq = take(M * C * es);   // transposed together with dq_pre (one batched launch)
   L.dS = take(BH * g.d * g.d * 4);
   L.dz = take(BH * g.d * 4);
   L.st = take(BH * 2 * g.DP * g.DK * es);
@@ -594,20 +596,18 @@ BwdLayout make_bwd_layout(const Geometry& g) {
   L.kvpart = take(BH * edit::kv_state_chunks(g.N) * (16 * g.DR) * (16 * g.DT) * 4);
   L.dkv = take(Mc * 2 * C * es);
   L.dk0v0 = take(M * 2 * C * es);
-  L.dXq = take(M * C * es);
   L.dXkv = take(M * C * es);
-  L.dXc = take(M * C * es);
   L.dact = take(M * Cr * es);
-  L.dxc = take(M * Cr * es);
+  L.dxc = take(M * Crp * es);
   L.doutT = take(C * Mp * es);
   L.yT = take(C * Mp * es);
   L.xT = take(C * Mp * es);
-  L.dqT = take(C * Mp * es);
+  L.dqT = take(2 * C * Mp * es);
   L.actT = take(Cr * Mp * es);
   L.dkvT = take(2 * C * Mp * es);
   L.dxcT9 = take(9 * Cr * Mp * es);
   size_t sk = 0;
-  const int shapes[3][2] = {{g.C, g.C}, {g.C, g.Cr}, {9 * g.Cr, g.C}};
+  const int shapes[4][2] = {{g.C, g.C}, {2 * g.C, g.C}, {2 * g.C, g.Cr}, {9 * g.Cr, g.C}};
   for (auto& sh : shapes) {
     const SplitK k = splitk(sh[0], sh[1], L.Mp, g.es == 2);
     const size_t b = (size_t)k.S * sh[0] * sh[1] * 4;
@@ -635,23 +635,25 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   auto FF = [&](size_t off) { return reinterpret_cast<const float*>(fws + off); };
   auto W = [](const void* p) { return static_cast<const T*>(p); };
   auto G = [](void* p) { return static_cast<T*>(p); };
-  const int M = g.M, C = g.C, Cr = g.Cr, Mp = L.Mp;
+  const int M = g.M, C = g.C, Cr = g.Cr, Mp = L.Mp, Crp = L.Crp;
   const T* zeros = P(L.zeros);
 
-  // C[M'][N'] = A B^T + 0 (bf16 / fp32 out), both operands K-contiguous.
-  auto gemm = [&](int Mr, int Nr, int K, const T* A, int lda, const T* B, int ldb, T* out, int ldc) -> edit_status_t {
+  // C[M'][N'] = A B^T (+ R), both operands K-contiguous.
+  auto gemm = [&](int Mr, int Nr, int K, const T* A, int lda, const T* B, int ldb, T* out, int ldc,
+                  const T* R = nullptr) -> edit_status_t {
     GemmArgs<T> a{};
     a.M = Mr; a.N = Nr; a.K = K; a.A = A; a.lda = lda;
     a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = B;
     a.bias[0] = a.bias[1] = a.bias[2] = zeros;
-    a.seg_rows = Nr; a.ldb = ldb; a.C = out; a.ldc = ldc;
+    a.seg_rows = Nr; a.ldb = ldb; a.C = out; a.ldc = ldc; a.R = R; a.ldr = ldc;
     EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
     return EDIT_OK;
   };
-  // out[r][c] = sum_m At[r][m] Bt[c][m] over the tokens (transposed operands, row stride Mp, zero
-  // padding past M); rows in groups of rpg interleave in the output row (see launch_splitk_reduce).
-  auto wgrad = [&](int rows, int cols, const T* At, const T* Bt, auto* out, int ldo, int rpg = 0,
-                   int gstride = 0) -> edit_status_t {
+  // P[r][c] = sum_m At[r][m] Bt[c][m] over the tokens (transposed operands, row stride Mp, zero
+  // padding past M) as split-K fp32 partials; wsum then adds the slices of rows [r0, r0 + n) into out
+  // (rows in groups of rpg interleave in the output row, see launch_splitk_reduce).
+  int wrows = 0, wcols = 0, wS = 0;
+  auto wprod = [&](int rows, int cols, const T* At, const T* Bt) -> edit_status_t {
     const SplitK k = splitk(rows, cols, Mp, sizeof(T) == 2);
     GemmArgs<T> a{};
     a.M = rows; a.N = cols; a.K = Mp; a.A = At; a.lda = Mp;
@@ -660,8 +662,18 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
     a.seg_rows = cols; a.ldb = Mp; a.ldc = cols;
     a.Cf = Q(L.skpart); a.split_stride = (long long)rows * cols; a.kchunk = k.kchunk;
     EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_F32, s));
-    EDIT_LAUNCH(launch_splitk_reduce(Q(L.skpart), k.S, (long long)rows * cols, rows, cols, out, ldo, s, rpg, gstride));
+    wrows = rows; wcols = cols; wS = k.S;
     return EDIT_OK;
+  };
+  auto wsum = [&](int r0, int n, auto* out, int ldo, int rpg = 0, int gstride = 0) -> edit_status_t {
+    EDIT_LAUNCH(launch_splitk_reduce(Q(L.skpart) + (size_t)r0 * wcols, wS, (long long)wrows * wcols, n, wcols, out,
+                                     ldo, s, rpg, gstride));
+    return EDIT_OK;
+  };
+  auto wgrad = [&](int rows, int cols, const T* At, const T* Bt, auto* out, int ldo, int rpg = 0,
+                   int gstride = 0) -> edit_status_t {
+    edit_status_t e = wprod(rows, cols, At, Bt);
+    return e != EDIT_OK ? e : wsum(0, rows, out, ldo, rpg, gstride);
   };
   edit_status_t st;
 
@@ -673,7 +685,8 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   EDIT_LAUNCH(launch_transpose<T>(W(w->w_v), C, C, C, P(L.wkvT) + C, 2 * C, s));
   // the 3x3 conv's input gradient is a 3x3 conv of dxc with the taps mirrored and the channel roles
   // swapped: wflip[ci][t * Cr + co] = w_cf1[co][8 - t][ci], one transpose per tap
-  EDIT_LAUNCH(launch_transpose<T>(W(w->w_cf1) + 8 * C, Cr, C, 9 * C, P(L.wflip), 9 * Cr, s, Cr, 9, -(long)C, Cr));
+  // (channel slots Cr .. Crp - 1 of every tap zero)
+  EDIT_LAUNCH(launch_transpose<T>(W(w->w_cf1) + 8 * C, Cr, C, 9 * C, P(L.wflip), 9 * Crp, s, Crp, 9, -(long)C, Crp));
   EDIT_LAUNCH(launch_transpose<T>(x, M, C, C, P(L.xT), Mp, s, Mp));
 
   // output Linear: dy = dout W_o, dW_o = dout^T y, db_o = sum dout
@@ -686,6 +699,10 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   // linear attention: g, c, dq_pre; dS = sum q^T g and dz = sum c q (the state kernel with per-token weights c)
   EDIT_LAUNCH(launch_attn_bwd_q<T>(P(L.dy), FP(F.q), FF(F.S), FF(F.z), g.B, g.N, g.heads, g.d, g.eps, P(L.g),
                                    Q(L.cvec), P(L.dq_pre), s));
+  // query Linear over [x | act] with the restore folded in (W' = [W_q | W_q W_cf2], b' = b_q + W_q b_cf2):
+  // dXq = dq_pre W_q (the restored stream's gradient dxt, which also reaches x), dact = dq_pre W_q W_cf2
+  if ((st = gemm(M, C, C, P(L.dq_pre), C, P(L.wqT), C, P(L.dXq), C)) != EDIT_OK) return st;
+  if ((st = gemm(M, Cr, C, P(L.dq_pre), C, P(L.wqT) + (size_t)C * C, C, P(L.dact), Cr)) != EDIT_OK) return st;
   EDIT_LAUNCH(launch_kv_state<T>(FP(F.q), P(L.g), C, g.B, g.N, g.heads, g.d, Q(L.kvpart), kv_state_chunks(g.N),
                                  Q(L.dS), Q(L.dz), P(L.st), Q(L.zp), s, Q(L.cvec)));
   // dK' (through the keys' ReLU), dV'
@@ -695,47 +712,49 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   EDIT_LAUNCH(launch_dw_bwd_input<T>(P(L.dkv), g.B, g.H, g.W, C, W(w->dw_k), W(w->dw_v), P(L.dk0v0), s));
   EDIT_LAUNCH(launch_dw_bwd_weight<T>(P(L.dkv), FP(F.kv0), g.B, g.H, g.W, C, Q(L.dwpart), G(gr->dw_k), G(gr->db_k),
                                       G(gr->dw_v), G(gr->db_v), s));
-  if ((st = gemm(M, C, 2 * C, P(L.dk0v0), 2 * C, P(L.wkvT), 2 * C, P(L.dXkv), C)) != EDIT_OK) return st;
+  // dXkv = [dk0 | dv0] [W_k; W_v] + dXq (the two input-gradient terms so far)
+  if ((st = gemm(M, C, 2 * C, P(L.dk0v0), 2 * C, P(L.wkvT), 2 * C, P(L.dXkv), C, P(L.dXq))) != EDIT_OK) return st;
   EDIT_LAUNCH(launch_transpose<T>(P(L.dk0v0), M, 2 * C, 2 * C, P(L.dkvT), Mp, s, Mp));
   EDIT_LAUNCH(launch_rowsum<T>(P(L.dkvT), C, Mp, Mp, G(gr->b_k), s));
   EDIT_LAUNCH(launch_rowsum<T>(P(L.dkvT) + (size_t)C * Mp, C, Mp, Mp, G(gr->b_v), s));
-  if ((st = wgrad(C, C, P(L.dkvT), P(L.xT), G(gr->w_k), C)) != EDIT_OK) return st;
-  if ((st = wgrad(C, C, P(L.dkvT) + (size_t)C * Mp, P(L.xT), G(gr->w_v), C)) != EDIT_OK) return st;
+  // dW_k and dW_v: one product over [dk0 | dv0]^T
+  if ((st = wprod(2 * C, C, P(L.dkvT), P(L.xT))) != EDIT_OK) return st;
+  if ((st = wsum(0, C, G(gr->w_k), C)) != EDIT_OK) return st;
+  if ((st = wsum(C, C, G(gr->w_v), C)) != EDIT_OK) return st;
 
-  // query Linear over [x | act] with the restore folded in (W' = [W_q | W_q W_cf2], b' = b_q + W_q b_cf2):
-  // dx += dq_pre W_q, dact = dq_pre W_q W_cf2, dW' = dq_pre^T [x | act], then
+  // the query Linear's weights: dW' = dq_pre^T [x | act], then
   // dW_q = dW'_x + dW'_act W_cf2^T + db_q b_cf2^T, db_q = sum dq_pre
-  if ((st = gemm(M, C, C, P(L.dq_pre), C, P(L.wqT), C, P(L.dXq), C)) != EDIT_OK) return st;
-  if ((st = gemm(M, Cr, C, P(L.dq_pre), C, P(L.wqT) + (size_t)C * C, C, P(L.dact), Cr)) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_transpose<T>(P(L.dq_pre), M, C, C, P(L.dqT), Mp, s, Mp));
+  // and the restore's 1x1 conv: dxt = dq_pre W_q (= dXq), dW_cf2 = dxt^T act, db_cf2 = sum dxt.
+  // dqT = [dq_pre | dxt]^T (one batched transpose over the two buffers).
+  EDIT_LAUNCH(launch_transpose<T>(P(L.dq_pre), M, C, C, P(L.dqT), Mp, s, Mp, 2, (long)((L.dXq - L.dq_pre) / sizeof(T)),
+                                  (long)C * Mp));
   EDIT_LAUNCH(launch_rowsum<T>(P(L.dqT), C, Mp, Mp, G(gr->b_q), s, Q(L.dbq32)));
+  EDIT_LAUNCH(launch_rowsum<T>(P(L.dqT) + (size_t)C * Mp, C, Mp, Mp, G(gr->b_cf2), s));
   EDIT_LAUNCH(launch_transpose<T>(FP(F.cf_act), M, Cr, Cr, P(L.actT), Mp, s, Mp));
   if ((st = wgrad(C, C, P(L.dqT), P(L.xT), Q(L.dWx), C)) != EDIT_OK) return st;
-  if ((st = wgrad(C, Cr, P(L.dqT), P(L.actT), Q(L.dWa), Cr)) != EDIT_OK) return st;
-  EDIT_LAUNCH((launch_small_matmul<float, T, T>(C, C, Cr, Q(L.dWa), Cr, 1, W(w->w_cf2), 1, Cr, Q(L.dWx), C,
-                                                G(gr->w_q), C, s, Q(L.dbq32), W(w->b_cf2))));
-  // the restore's 1x1 conv: dxt = dq_pre W_q (= dXq), dW_cf2 = dxt^T act, db_cf2 = sum dxt
-  EDIT_LAUNCH(launch_transpose<T>(P(L.dXq), M, C, C, P(L.dqT), Mp, s, Mp));
-  if ((st = wgrad(C, Cr, P(L.dqT), P(L.actT), G(gr->w_cf2), Cr)) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_rowsum<T>(P(L.dqT), C, Mp, Mp, G(gr->b_cf2), s));
+  if ((st = wprod(2 * C, Cr, P(L.dqT), P(L.actT))) != EDIT_OK) return st;   // [dW'_act | dW_cf2]
+  if ((st = wsum(0, C, Q(L.dWa), Cr)) != EDIT_OK) return st;
+  if ((st = wsum(C, C, G(gr->w_cf2), Cr)) != EDIT_OK) return st;
+  EDIT_LAUNCH((launch_small_nt<T, T>(C, C, Cr, Q(L.dWa), Cr, W(w->w_cf2), Cr, Q(L.dWx), C, G(gr->w_q), C, s,
+                                     Q(L.dbq32), W(w->b_cf2))));
 
   // LeakyReLU + GroupNorm, then the 3x3 conv: dx += conv(dxc, mirrored taps), dW_cf1 per tap
   EDIT_LAUNCH(launch_gn_bwd<T>(P(L.dact), FP(F.cf_act), FP(F.xc), FF(F.gn_stat), W(w->gn_gamma), g.B, g.N, Cr, g.G,
-                               Q(L.gnpart), Q(L.m12), G(gr->gn_gamma), G(gr->gn_beta), P(L.dxc), s));
+                               Q(L.gnpart), Q(L.m12), G(gr->gn_gamma), G(gr->gn_beta), P(L.dxc), Crp, s));
   {
     GemmArgs<T> a{};
-    a.M = M; a.N = C; a.K = 9 * Cr; a.A = P(L.dxc); a.lda = Cr; a.H = g.H; a.W = g.W; a.Cin = Cr;
+    // dx = conv(dxc, mirrored taps) + dXkv; dxc's channels padded to Crp (zeros) for 64-wide K steps
+    a.M = M; a.N = C; a.K = 9 * Crp; a.A = P(L.dxc); a.lda = Crp; a.H = g.H; a.W = g.W; a.Cin = Crp;
     a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = P(L.wflip);
     a.bias[0] = a.bias[1] = a.bias[2] = zeros;
-    a.seg_rows = C; a.ldb = 9 * Cr; a.C = P(L.dXc); a.ldc = C;
+    a.seg_rows = C; a.ldb = 9 * Crp; a.C = dx; a.ldc = C; a.R = P(L.dXkv); a.ldr = C;
     EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
   }
   // dW_cf1[co][t][ci] = sum_m dxc[m + off_t][co] x[m][ci]: the nine shifted copies of dxc stacked as
   // [9 Cr][tokens], one product whose row t * Cr + co lands at w_cf1 + co * 9C + t * C
-  EDIT_LAUNCH(launch_shift_transpose9<T>(P(L.dxc), g.B, g.H, g.W, Cr, P(L.dxcT9), Mp, s));
+  EDIT_LAUNCH(launch_shift_transpose9<T>(P(L.dxc), g.B, g.H, g.W, Cr, Crp, P(L.dxcT9), Mp, s));
   EDIT_LAUNCH(launch_rowsum<T>(P(L.dxcT9) + (size_t)4 * Cr * Mp, Cr, Mp, Mp, G(gr->b_cf1), s));   // centre tap
   if ((st = wgrad(9 * Cr, C, P(L.dxcT9), P(L.xT), G(gr->w_cf1), 9 * C, Cr, C)) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_sum3<T>(P(L.dXq), P(L.dXkv), P(L.dXc), (long)M * C, dx, s));
   return EDIT_OK;
 }
 

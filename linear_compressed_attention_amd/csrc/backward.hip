@@ -88,13 +88,14 @@ hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, in
 }
 
 template <typename T>
-hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, T* out, int ldo, hipStream_t s) {
+hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, int ldi, T* out, int ldo,
+                                   hipStream_t s) {
   const int rows = B * H * W;
   if (rows <= 0 || cols <= 0) return hipSuccess;
   constexpr int EPC = 16 / (int)sizeof(T);
-  if (cols % EPC || ldo % EPC || ldo < rows) return hipErrorInvalidValue;
+  if (cols % EPC || ldi % EPC || ldo % EPC || ldo < rows) return hipErrorInvalidValue;
   dim3 grid((cols + 63) / 64, (ldo + 63) / 64, 9);
-  hipLaunchKernelGGL((transpose_kernel<T, true>), grid, dim3(256), 0, s, in, rows, ldo, cols, cols, out, ldo, H, W,
+  hipLaunchKernelGGL((transpose_kernel<T, true>), grid, dim3(256), 0, s, in, rows, ldo, cols, ldi, out, ldo, H, W,
                      0L, (long)cols * ldo);
   return hipGetLastError();
 }
@@ -225,21 +226,33 @@ __device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = t[i];
 }
-// M (fp32, element (i, k) at src[i * rs + k * cs], d x d) into the LDS operand.
-// dst holds NC copies of [RT * 32][KP].
-template <typename T, int KS>
-__device__ __forceinline__ void head_mat_fill(T* dst, const float* __restrict__ src, int rs, int cs, int d) {
+// M (fp32, d x d, row-major at src) into the LDS operand, or its transpose
+// (TR): dst row i, column k holds M[i][k] (TR: M[k][i]). 16-byte loads along
+// src's rows; dst holds NC copies of [RT * 32][KP].
+template <typename T, int KS, bool TR>
+__device__ __forceinline__ void head_mat_fill(T* dst, const float* __restrict__ src, int d) {
   using HM = HeadMat<T, KS>;
   constexpr int CP = HM::RT * 32 * HM::KP;
-  for (int i = threadIdx.x; i < HM::RT * 32 * KS * 16; i += blockDim.x) {
-    const int row = i / (KS * 16), k = i - row * (KS * 16);
-    const float v = row < d && k < d ? src[row * rs + k * cs] : 0.0f;
-    if constexpr (HM::NC == 2) {
-      const bf16 hi = (bf16)v;
-      dst[row * HM::KP + k] = hi;
-      dst[CP + row * HM::KP + k] = (bf16)(v - (float)hi);
-    } else {
-      dst[row * HM::KP + k] = v;
+  constexpr int RW = HM::RT * 32;                  // rows of the operand
+  constexpr int QW = (KS * 16) / 4;                // 4-element groups along K
+  // Source element groups: (i, k0..k0+3) of M. Not transposed: i = operand
+  // row, k = operand column; transposed: the operand's row is k.
+  constexpr int NI = TR ? KS * 16 : RW, NQ = TR ? RW / 4 : QW;
+#pragma unroll 4
+  for (int e = threadIdx.x; e < NI * NQ; e += blockDim.x) {
+    const int i = e / NQ, k0 = (e - i * NQ) * 4;
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (i < d && k0 < d) v = *reinterpret_cast<const f32x4*>(src + (size_t)i * d + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = TR ? k0 + j : i, col = TR ? i : k0 + j;
+      if constexpr (HM::NC == 2) {
+        const bf16 hi = (bf16)v[j];
+        dst[row * HM::KP + col] = hi;
+        dst[CP + row * HM::KP + col] = (bf16)(v[j] - (float)hi);
+      } else {
+        dst[row * HM::KP + col] = v[j];
+      }
     }
   }
 }
@@ -291,7 +304,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(const T* __restrict__ d
   const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
   const int C = heads * d, col = lane & 31, half = lane >> 5;
   const size_t bh = (size_t)b * heads + h;
-  head_mat_fill<T, KS>(As, S + bh * d * d, d, 1, d);
+  head_mat_fill<T, KS, false>(As, S + bh * d * d, d);
   for (int i = threadIdx.x; i < HM::RT * 32; i += blockDim.x) zs[i] = i < d ? z[bh * d + i] : 0.0f;
   __syncthreads();
   const int t0 = head_tile0(tiles_per_wave);
@@ -357,11 +370,12 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(const T* __restrict__ d
   }
 }
 
-// Tiles per wave so that about 1024 blocks cover the (sample, head) pairs.
+// Tiles per wave: one (so that a wave's loads never queue behind its own
+// earlier stores) until the grid would pass about 4096 blocks.
 static int head_tiles_per_wave(int B, int heads, int ntok) {
   const int tiles = (ntok + 31) / 32;
   const int pairs = B * heads;
-  const int blocks_per_pair = std::max(1, 1024 / std::max(1, pairs));
+  const int blocks_per_pair = std::max(1, 4096 / std::max(1, pairs));
   return std::max(1, (tiles + 4 * blocks_per_pair - 1) / (4 * blocks_per_pair));
 }
 
@@ -409,8 +423,8 @@ __global__ __launch_bounds__(256) void kv_bwd_kernel(const T* __restrict__ kc, c
   const int h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
   const int C = heads * d, col = lane & 31, half = lane >> 5;
   const size_t bh = (size_t)b * heads + h;
-  head_mat_fill<T, KS>(A1, dS + bh * d * d, d, 1, d);
-  head_mat_fill<T, KS>(A2, dS + bh * d * d, 1, d, d);
+  head_mat_fill<T, KS, false>(A1, dS + bh * d * d, d);
+  head_mat_fill<T, KS, true>(A2, dS + bh * d * d, d);
   for (int i = threadIdx.x; i < HM::RT * 32; i += blockDim.x) zs[i] = i < d ? dz[bh * d + i] : 0.0f;
   __syncthreads();
   const int t0 = head_tile0(tiles_per_wave);
@@ -421,15 +435,29 @@ __global__ __launch_bounds__(256) void kv_bwd_kernel(const T* __restrict__ kc, c
     const bool valid = tok < Nc;
     const size_t row = ((size_t)b * Nc + (valid ? tok : 0)) * C + (size_t)h * d;
     T* out = dkv + ((size_t)b * Nc + (valid ? tok : 0)) * 2 * C + (size_t)h * d;
-    F bf[KS];
-    f32x16 acc[HM::RT];
-    // keys: dK'^T = dS V'^T, + dz, masked by K' > 0
+    // Every load of the tile (V', K' as operands, K' for the ReLU mask) is
+    // issued before its first store: a load queued behind a store waits for it.
+    F bv[KS], bk[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int k = ks * 16 + 8 * half;
-      bf[ks] = valid && k < d ? frag_ld(vc + row + k) : frag_zero<F>();
+      bv[ks] = valid && k < d ? frag_ld(vc + row + k) : frag_zero<F>();
+      bk[ks] = valid && k < d ? frag_ld(kc + row + k) : frag_zero<F>();
     }
-    head_mat_apply<T, KS, HM::RT>(A1, bf, acc, lane);
+    float kv[HM::RT][16];
+#pragma unroll
+    for (int rt = 0; rt < HM::RT; ++rt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int a0 = rt * 32 + 8 * g + 4 * half;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (valid && a0 < d) load4(kc + row + a0, v);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kv[rt][4 * g + i] = v[i];
+      }
+    f32x16 acc[HM::RT];
+    // keys: dK'^T = dS V'^T, + dz, masked by K' > 0
+    head_mat_apply<T, KS, HM::RT>(A1, bv, acc, lane);
     if (valid) {
 #pragma unroll
       for (int rt = 0; rt < HM::RT; ++rt)
@@ -437,20 +465,14 @@ __global__ __launch_bounds__(256) void kv_bwd_kernel(const T* __restrict__ kc, c
         for (int g = 0; g < 4; ++g) {
           const int a0 = rt * 32 + 8 * g + 4 * half;
           if (a0 >= d) continue;
-          float kv[4], o[4];
-          load4(kc + row + a0, kv);
+          float o[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = kv[i] > 0.0f ? acc[rt][4 * g + i] + zs[a0 + i] : 0.0f;
+          for (int i = 0; i < 4; ++i) o[i] = kv[rt][4 * g + i] > 0.0f ? acc[rt][4 * g + i] + zs[a0 + i] : 0.0f;
           store4(out + a0, o);
         }
     }
     // values: dV'^T = dS^T K'^T
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int k = ks * 16 + 8 * half;
-      bf[ks] = valid && k < d ? frag_ld(kc + row + k) : frag_zero<F>();
-    }
-    head_mat_apply<T, KS, HM::RT>(A2, bf, acc, lane);
+    head_mat_apply<T, KS, HM::RT>(A2, bk, acc, lane);
     if (valid) {
 #pragma unroll
       for (int rt = 0; rt < HM::RT; ++rt)
@@ -542,7 +564,7 @@ hipError_t launch_dw_bwd_input(const T* dout, int B, int H, int W, int C, const 
 // each thread keeps 10 x 8 sums, the 8 lanes are added through LDS, and the
 // chunk's partial goes to partial[chunk][10][2C]; the chunks are then added
 // in order.
-constexpr int kDwPix = 128;   // output pixels per partial
+constexpr int kDwPix = 32;    // output pixels per partial
 
 template <typename T>
 __global__ __launch_bounds__(256) void dw_bwd_weight_partial_kernel(const T* __restrict__ dout,
@@ -613,6 +635,7 @@ __global__ __launch_bounds__(256) void dw_bwd_weight_finalize_kernel(const float
   if (i >= 10 * 2 * C) return;
   const int t = i / (2 * C), c2 = i - t * 2 * C;
   float s = 0.0f;
+#pragma unroll 8
   for (int ch = 0; ch < nchunks; ++ch) s += partial[(size_t)ch * 10 * 2 * C + i];
   const bool k = c2 < C;
   const int c = k ? c2 : c2 - C;
@@ -778,29 +801,44 @@ __global__ __launch_bounds__(256) void gn_bwd_finalize_kernel(const float* __res
   }
 }
 
+// dxc[m][c] (row stride ldo; channels C .. ldo - 1 written as zeros), eight
+// channels per thread.
 template <typename T>
 __global__ __launch_bounds__(256) void gn_bwd_apply_kernel(const T* __restrict__ dact, const T* __restrict__ act,
                                                            const T* __restrict__ xc, const float* __restrict__ stat,
                                                            const float* __restrict__ m12,
-                                                           const T* __restrict__ gamma, int N, int C, int G,
-                                                           long total, T* __restrict__ dxc) {
+                                                           const T* __restrict__ gamma, int N, int C, int G, long rows,
+                                                           int ldo, T* __restrict__ dxc) {
+  const int cpr = ldo / 8;
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const int c = (int)(i % C);
-  const int b = (int)(i / ((long)N * C));
-  const int g = c / (C / G);
-  const float mean = stat[((size_t)b * G + g) * 2], rstd = stat[((size_t)b * G + g) * 2 + 1];
-  const float m1 = m12[((size_t)b * G + g) * 2], m2 = m12[((size_t)b * G + g) * 2 + 1];
-  const float a = to_f32(act[i]), da0 = to_f32(dact[i]);
-  const float da = a >= 0.0f ? da0 : 0.01f * da0;
-  const float xn = (to_f32(xc[i]) - mean) * rstd;
-  dxc[i] = from_f32<T>(rstd * (to_f32(gamma[c]) * da - m1 - xn * m2));
+  if (i >= rows * cpr) return;
+  const long m = i / cpr;
+  const int c0 = (int)(i - m * cpr) * 8;
+  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (c0 < C) {
+    const int b = (int)(m / N), cpg = C / G;
+    float a[8], da[8], x[8];
+    load8(act + m * C + c0, a);
+    load8(dact + m * C + c0, da);
+    load8(xc + m * C + c0, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int g = (c0 + k) / cpg;
+      const float mean = stat[((size_t)b * G + g) * 2], rstd = stat[((size_t)b * G + g) * 2 + 1];
+      const float m1 = m12[((size_t)b * G + g) * 2], m2 = m12[((size_t)b * G + g) * 2 + 1];
+      const float d = a[k] >= 0.0f ? da[k] : 0.01f * da[k];
+      const float xn = (x[k] - mean) * rstd;
+      o[k] = rstd * (to_f32(gamma[c0 + k]) * d - m1 - xn * m2);
+    }
+  }
+  store8(dxc + m * ldo + c0, o);
 }
 
 template <typename T>
 hipError_t launch_gn_bwd(const T* dact, const T* act, const T* xc, const float* stat, const T* gamma, int B, int N,
-                         int C, int G, float* partial, float* m12, T* dgamma, T* dbeta, T* dxc, hipStream_t s) {
-  if (C / G > 256 || C % 8 != 0) return hipErrorInvalidValue;
+                         int C, int G, float* partial, float* m12, T* dgamma, T* dbeta, T* dxc, int lddxc,
+                         hipStream_t s) {
+  if (C / G > 256 || C % 8 != 0 || lddxc < C || lddxc % 8 != 0) return hipErrorInvalidValue;
   const int nch = gn_bwd_chunks(N);
   hipLaunchKernelGGL((gn_bwd_partial_kernel<T>), dim3(nch, (C + 255) / 256, B), dim3(256), 0, s, dact, act, xc, stat,
                      N, C, G, partial);
@@ -809,49 +847,55 @@ hipError_t launch_gn_bwd(const T* dact, const T* act, const T* xc, const float* 
   hipLaunchKernelGGL((gn_bwd_finalize_kernel<T>), dim3(G, B), dim3(256), 0, s, partial, nch, B, N, C, G, gamma, m12,
                      dgamma, dbeta);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const long total = (long)B * N * C;
+  const long rows = (long)B * N, total = rows * (lddxc / 8);
   hipLaunchKernelGGL((gn_bwd_apply_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, dact, act, xc,
-                     stat, m12, gamma, N, C, G, total, dxc);
+                     stat, m12, gamma, N, C, G, rows, lddxc, dxc);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Small fp32 products for the folded query weights' gradients:
-//   out[i][j] = (add ? add[i][j] : 0) + (ru ? ru[i] rv[j] : 0) + sum_k A(i, k) B(k, j),
-// A(i, k) = A[i * ars + k * acs], B(k, j) = B[k * brs + j * bcs] (any strides,
-// so either operand may be read transposed). 64 x 64 output tiles, 16 x 16
-// threads with 4 x 4 outputs each, K in steps of 16 through LDS.
+// Small fp32 product for the folded query weights' gradient:
+//   out[i][j] = add[i][j] + ru[i] rv[j] + sum_k A[i][k] B[j][k]
+// (A fp32 [M][lda], B [N][ldb], both K-contiguous). 64 x 64 output tiles,
+// 16 x 16 threads with 4 x 4 outputs each; K in chunks of 64 through LDS,
+// stored K-major so that a thread reads its 4 rows (columns) as one float4.
 // ---------------------------------------------------------------------------
-template <typename TA, typename TB, typename TO>
-__global__ __launch_bounds__(256) void small_matmul_kernel(int M, int N, int K, const TA* __restrict__ A, long ars,
-                                                           long acs, const TB* __restrict__ Bm, long brs, long bcs,
-                                                           const float* __restrict__ add, int ldadd,
-                                                           const float* __restrict__ ru, const TB* __restrict__ rv,
-                                                           TO* __restrict__ out, int ldo) {
-  __shared__ float As[16][64 + 1];
-  __shared__ float Bs[16][64 + 1];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+constexpr int kSmKc = 64;
+
+template <typename TB, typename TO>
+__global__ __launch_bounds__(256) void small_nt_kernel(int M, int N, int K, const float* __restrict__ A, int lda,
+                                                       const TB* __restrict__ Bm, int ldb,
+                                                       const float* __restrict__ add, int ldadd,
+                                                       const float* __restrict__ ru, const TB* __restrict__ rv,
+                                                       TO* __restrict__ out, int ldo) {
+  __shared__ __attribute__((aligned(16))) float As[kSmKc][64 + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[kSmKc][64 + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  float acc[4][4];
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += kSmKc) {
+    // A: 64 rows x 16 float4 along K; B: 64 rows x 8 groups of 8 along K.
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+    for (int e = tid; e < 64 * 16; e += 256) {
+      const int r = e >> 4, k = k0 + (e & 15) * 4;
+      f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (i0 + r < M && k < K) v = *reinterpret_cast<const f32x4*>(A + (size_t)(i0 + r) * lda + k);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0f;
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int e = threadIdx.x; e < 16 * 64; e += 256) {
-      const int kk = e >> 6, r = e & 63;
-      const int i = i0 + r, j = j0 + r, k = k0 + kk;
-      As[kk][r] = i < M && k < K ? to_f32(A[i * ars + k * acs]) : 0.0f;
-      Bs[kk][r] = j < N && k < K ? to_f32(Bm[k * brs + j * bcs]) : 0.0f;
+      for (int q = 0; q < 4; ++q) As[(e & 15) * 4 + q][r] = v[q];
+    }
+#pragma unroll
+    for (int e = tid; e < 64 * 8; e += 256) {
+      const int r = e >> 3, k = k0 + (e & 7) * 8;
+      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (j0 + r < N && k < K) load8(Bm + (size_t)(j0 + r) * ldb + k, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) Bs[(e & 7) * 8 + q][r] = v[q];
     }
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[kk][ty * 4 + a];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[kk][tx * 4 + c];
+#pragma unroll 8
+    for (int kk = 0; kk < kSmKc; ++kk) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&As[kk][ty * 4]);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bs[kk][tx * 4]);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -859,56 +903,42 @@ __global__ __launch_bounds__(256) void small_matmul_kernel(int M, int N, int K, 
     }
     __syncthreads();
   }
+  // Every load of the epilogue before its first store (a load queued behind
+  // a store waits for it).
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int i = i0 + ty * 4 + a, j = j0 + tx * 4 + c;
       if (i < M && j < N) {
-        float v = acc[a][c] + (add ? add[(size_t)i * ldadd + j] : 0.0f);
-        if (ru) v += ru[i] * to_f32(rv[j]);
-        out[(size_t)i * ldo + j] = from_f32<TO>(v);
+        if (add) acc[a][c] += add[(size_t)i * ldadd + j];
+        if (ru) acc[a][c] += ru[i] * to_f32(rv[j]);
       }
+    }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = i0 + ty * 4 + a, j = j0 + tx * 4 + c;
+      if (i < M && j < N) out[(size_t)i * ldo + j] = from_f32<TO>(acc[a][c]);
     }
 }
 
-template <typename TA, typename TB, typename TO>
-hipError_t launch_small_matmul(int M, int N, int K, const TA* A, long ars, long acs, const TB* Bm, long brs, long bcs,
-                               const float* add, int ldadd, TO* out, int ldo, hipStream_t s, const float* ru,
-                               const TB* rv) {
+template <typename TB, typename TO>
+hipError_t launch_small_nt(int M, int N, int K, const float* A, int lda, const TB* Bm, int ldb, const float* add,
+                           int ldadd, TO* out, int ldo, hipStream_t s, const float* ru, const TB* rv) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (K % 8 || lda % 4 || ldb % 8) return hipErrorInvalidValue;
   dim3 grid((N + 63) / 64, (M + 63) / 64);
-  hipLaunchKernelGGL((small_matmul_kernel<TA, TB, TO>), grid, dim3(256), 0, s, M, N, K, A, ars, acs, Bm, brs, bcs,
-                     add, ldadd, ru, rv, out, ldo);
+  hipLaunchKernelGGL((small_nt_kernel<TB, TO>), grid, dim3(256), 0, s, M, N, K, A, lda, Bm, ldb, add, ldadd, ru, rv,
+                     out, ldo);
   return hipGetLastError();
 }
 
-// dx = a + b + c (T inputs, fp32 sum, one rounding).
-template <typename T>
-__global__ __launch_bounds__(256) void sum3_kernel(const T* __restrict__ a, const T* __restrict__ b,
-                                                   const T* __restrict__ c, long n8, T* __restrict__ out) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  float va[8], vb[8], vc[8];
-  load8(a + 8 * i, va);
-  load8(b + 8 * i, vb);
-  load8(c + 8 * i, vc);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) va[k] += vb[k] + vc[k];
-  store8(out + 8 * i, va);
-}
-
-template <typename T>
-hipError_t launch_sum3(const T* a, const T* b, const T* c, long n, T* out, hipStream_t s) {
-  const long n8 = n / 8;
-  if (n8 <= 0) return hipSuccess;
-  hipLaunchKernelGGL((sum3_kernel<T>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a, b, c, n8, out);
-  return hipGetLastError();
-}
 
 #define EDIT_INST(T)                                                                                               \
   template hipError_t launch_transpose<T>(const T*, int, int, int, T*, int, hipStream_t, int, int, long, long);   \
-  template hipError_t launch_shift_transpose9<T>(const T*, int, int, int, int, T*, int, hipStream_t);              \
+  template hipError_t launch_shift_transpose9<T>(const T*, int, int, int, int, int, T*, int, hipStream_t);         \
   template hipError_t launch_rowsum<T>(const T*, int, int, int, T*, hipStream_t, float*);                         \
   template hipError_t launch_zero<T>(T*, long, hipStream_t);                                                       \
   template hipError_t launch_splitk_reduce<T>(const float*, int, long long, int, int, T*, int, hipStream_t, int,  \
@@ -921,16 +951,13 @@ hipError_t launch_sum3(const T* a, const T* b, const T* c, long n, T* out, hipSt
   template hipError_t launch_dw_bwd_weight<T>(const T*, const T*, int, int, int, int, float*, T*, T*, T*, T*,      \
                                               hipStream_t);                                                        \
   template hipError_t launch_gn_bwd<T>(const T*, const T*, const T*, const float*, const T*, int, int, int, int,   \
-                                       float*, float*, T*, T*, T*, hipStream_t);                                   \
-  template hipError_t launch_sum3<T>(const T*, const T*, const T*, long, T*, hipStream_t);
+                                       float*, float*, T*, T*, T*, int, hipStream_t);
 EDIT_INST(bf16)
 EDIT_INST(float)
 #undef EDIT_INST
-template hipError_t launch_small_matmul<float, bf16, bf16>(int, int, int, const float*, long, long, const bf16*, long,
-                                                           long, const float*, int, bf16*, int, hipStream_t,
-                                                           const float*, const bf16*);
-template hipError_t launch_small_matmul<float, float, float>(int, int, int, const float*, long, long, const float*,
-                                                             long, long, const float*, int, float*, int, hipStream_t,
-                                                             const float*, const float*);
+template hipError_t launch_small_nt<bf16, bf16>(int, int, int, const float*, int, const bf16*, int, const float*, int,
+                                               bf16*, int, hipStream_t, const float*, const bf16*);
+template hipError_t launch_small_nt<float, float>(int, int, int, const float*, int, const float*, int, const float*,
+                                                  int, float*, int, hipStream_t, const float*, const float*);
 
 }  // namespace edit

@@ -302,6 +302,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs<T> p) {
       load8(pick3(p.bias, n / p.seg_rows) + n % p.seg_rows, bv);
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] += bv[i];
+      if (EM == E_RES) {
+        load8(p.R + (size_t)m * p.ldr + n, bv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] += bv[i];
+      }
       if (EM == E_BIAS_RELU) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = v[i] > 0.0f ? v[i] : 0.0f;
@@ -327,6 +332,8 @@ static hipError_t launch_tiles(const GemmArgs<T>& a, AMode am, EMode em, hipStre
   EDIT_GEMM_CASE(A_CONV3, E_BIAS)
   EDIT_GEMM_CASE(A_CAT2, E_BIAS_RELU)
   EDIT_GEMM_CASE(A_PLAIN, E_F32)
+  EDIT_GEMM_CASE(A_PLAIN, E_RES)
+  EDIT_GEMM_CASE(A_CONV3, E_RES)
 #undef EDIT_GEMM_CASE
   return hipErrorInvalidValue;
 }
@@ -338,6 +345,10 @@ static hipError_t launch_tiles(const GemmArgs<T>& a, AMode am, EMode em, hipStre
 template <typename T>
 hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.R != nullptr) {
+    if (em != E_BIAS) return hipErrorInvalidValue;
+    em = E_RES;
+  }
   if constexpr (std::is_same<T, bf16>::value) {
     const hipError_t e = launch_gemm_dma(a, am, em, s);
     if (e != hipErrorNotSupported) return e;

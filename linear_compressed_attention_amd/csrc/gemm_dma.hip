@@ -406,6 +406,21 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
 #pragma unroll
     for (int t = 0; t < TI; ++t) {
       const int m = em0 + wm * WTM + t * 32 + fr;
+      // The residual's quads for this row block, all requested before any
+      // store of the block (a load behind a store to possibly the same
+      // memory would wait for it).
+      bf16x4 rr[EM == E_RES ? CJ : 1][4];
+      if (EM == E_RES) {
+#pragma unroll
+        for (int c = 0; c < CJ; ++c)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = en0 + wn * WTN + c * 32 + 8 * g + 4 * fh;
+            rr[EM == E_RES ? c : 0][g] = m < p.M && n < p.N
+                                              ? *reinterpret_cast<const bf16x4*>(p.R + (size_t)m * p.ldr + n)
+                                              : bf16x4{};
+          }
+      }
 #pragma unroll
       for (int c = 0; c < CJ; ++c) {
         float f[4][4];
@@ -416,6 +431,13 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
             f[g][i] = acc[t][c][4 * g + i] + (float)bv[c][g][i];
             if (EM == E_BIAS_RELU) f[g][i] = f[g][i] > 0.0f ? f[g][i] : 0.0f;
           }
+        if (EM == E_RES) {
+          // residual: quad g holds channels 8g + 4(l >> 5) .. +3 of token m
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[g][i] += (float)rr[EM == E_RES ? c : 0][g][i];
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int ge = 2 * j, go = 2 * j + 1;
@@ -497,6 +519,7 @@ hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, hipStream_t s) {
 // what the kernel handles; the caller then uses the register-staged GEMM.
 hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStream_t s) {
   if (EDIT_DMA_FORCE < 0) return hipErrorNotSupported;
+  if (em == E_RES && a.ldr % 4 != 0) return hipErrorNotSupported;
   if (a.K % 8 != 0 || a.N % 8 != 0 || a.ldb % 8 != 0 || a.lda % 8 != 0 || a.ldc % 8 != 0)
     return hipErrorNotSupported;
   // Buffer offsets are 32-bit and must stay below the out-of-range marker.
@@ -508,8 +531,9 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
   //  - the 3x3 conv (162 K steps): 119 us against 227 us for the register-staged kernel;
   //  - plain-A projections with 128 x 192 tiles, two stages, two blocks per CU: 46 us at
   //    16384 x 1152 x 1152 and 91 us at 16384 x 2304 x 1152 against 63 and 105 us register-staged.
-  if (am == A_CONV3 && em == E_BIAS) {
+  if (am == A_CONV3 && (em == E_BIAS || em == E_RES)) {
     if (a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin) return hipErrorNotSupported;
+    if (em == E_RES) return n96 ? launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_RES>(a, s) : hipErrorNotSupported;
     if (n96) return launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_BIAS>(a, s);
     if (n128) return launch_dma_tiles<256, 128, 2, 2, A_CONV3, E_BIAS>(a, s);
     return hipErrorNotSupported;
@@ -528,7 +552,9 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
     if (n96) return launch_dma_tiles<128, 96, 4, 1, A_PLAIN, E_F32, 2>(a, s);
     return hipErrorNotSupported;
   }
+  if (am == A_PLAIN && !n192 && n96 && em == E_BIAS) return launch_dma_tiles<128, 96, 4, 1, A_PLAIN, E_BIAS, 2>(a, s);
   if (am == A_PLAIN && n192) {
+    if (em == E_RES) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_RES, 2>(a, s);
     if (em == E_BIAS) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS, 2>(a, s);
     if (em == E_BIAS_RELU) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS_RELU, 2>(a, s);
   }

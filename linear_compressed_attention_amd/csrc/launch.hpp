@@ -16,7 +16,8 @@ enum AMode {
 enum EMode {
   E_BIAS = 0,       // C = acc + bias
   E_BIAS_RELU = 1,  // C = max(acc + bias, 0)
-  E_F32 = 2         // Cf[split][m][n] = acc (fp32, no bias): one K slice of a split-K product
+  E_F32 = 2,        // Cf[split][m][n] = acc (fp32, no bias): one K slice of a split-K product
+  E_RES = 3         // C = acc + bias + R (launch_gemm picks it for E_BIAS when GemmArgs::R is set)
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T + epilogue. B and the bias may come in up
@@ -46,6 +47,9 @@ struct GemmArgs {
   float* Cf;
   long long split_stride;
   int kchunk;
+  // E_BIAS with R set (run as E_RES): C = A B^T + bias + R (R [M][ldr], the same type as C).
+  const T* R;
+  int ldr;
 };
 
 template <typename T>
@@ -102,9 +106,10 @@ hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, in
                             int rows_pad = 0, int batch = 1, long zin = 0, long zout = 0);
 // For every tap t = 3 ky + kx of the 3x3 conv: out[t][c][m'] = in[m' - off][c],
 // zero where that tap does not connect the two pixels (and in the padding up
-// to ldo); in is [B*H*W][cols], out [9][cols][ldo].
+// to ldo); in is [B*H*W][ldi], out [9][cols][ldo].
 template <typename T>
-hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, T* out, int ldo, hipStream_t s);
+hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, int ldi, T* out, int ldo,
+                                   hipStream_t s);
 // out[r] = sum_m in[r][m] for m < len (a transposed [channels][tokens] buffer), fixed order; out32 optional.
 template <typename T>
 hipError_t launch_rowsum(const T* in, int rows, int len, int ld, T* out, hipStream_t s, float* out32 = nullptr);
@@ -134,14 +139,13 @@ hipError_t launch_dw_bwd_weight(const T* dout, const T* in, int B, int H, int W,
 int gn_bwd_chunks(int N);
 template <typename T>
 hipError_t launch_gn_bwd(const T* dact, const T* act, const T* xc, const float* stat, const T* gamma, int B, int N,
-                         int C, int G, float* partial, float* m12, T* dgamma, T* dbeta, T* dxc, hipStream_t s);
-// out[i][j] = add[i][j] + ru[i] rv[j] + sum_k A[i * ars + k * acs] B[k * brs + j * bcs] (add, ru optional).
-template <typename TA, typename TB, typename TO>
-hipError_t launch_small_matmul(int M, int N, int K, const TA* A, long ars, long acs, const TB* Bm, long brs, long bcs,
-                               const float* add, int ldadd, TO* out, int ldo, hipStream_t s,
-                               const float* ru = nullptr, const TB* rv = nullptr);
-template <typename T>
-hipError_t launch_sum3(const T* a, const T* b, const T* c, long n, T* out, hipStream_t s);
+                         int C, int G, float* partial, float* m12, T* dgamma, T* dbeta, T* dxc, int lddxc,
+                         hipStream_t s);
+// out[i][j] = add[i][j] + ru[i] rv[j] + sum_k A[i][k] B[j][k] (A fp32 [M][lda], B [N][ldb]; add, ru optional).
+template <typename TB, typename TO>
+hipError_t launch_small_nt(int M, int N, int K, const float* A, int lda, const TB* Bm, int ldb, const float* add,
+                           int ldadd, TO* out, int ldo, hipStream_t s, const float* ru = nullptr,
+                           const TB* rv = nullptr);
 int kv_state_dp(int d);   // padded rows of the state operand
 int kv_state_dk(int d);   // padded K of the state operand
 
