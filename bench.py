@@ -36,14 +36,22 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core (f32: ve
 STEP_NAMES = ["cf_conv3x3", "gn_stats", "cf_act", "q_proj", "kv_proj", "sc_dwconv", "kv_state",
               "linattn_apply", "out_proj"]
 STEP_KERNELS = {  # kernels launched per step at bf16 (rocprofv3 names start with these)
-    "cf_conv3x3": "gemm_dma_kernel<256, 96, 4, 1, A_CONV3, E_BIAS>",
-    "gn_stats": "gn_partial_kernel + gn_finalize_kernel",
-    "cf_act": "gn_apply_kernel + restore_fold_mfma_kernel",
+    "cf_conv3x3": "gemm_dma_kernel<256, 96, 4, 1, A_CONV3, E_BIAS_GN> (with the GroupNorm partials and the restore fold)",
+    "gn_stats": "gn_finalize_channels_kernel",
+    "cf_act": "gn_apply_kernel",
     "q_proj": "gemm_dma_kernel<128, 192, 2, 2, A_CAT2, E_BIAS_RELU>",
     "kv_proj": "gemm_dma_kernel<128, 192, 2, 2, A_PLAIN, E_BIAS>", "sc_dwconv": "dwconv_s2_kernel",
     "kv_state": "kv_state_partial_kernel + kv_state_finalize_kernel", "linattn_apply": "linattn_apply_kernel",
     "out_proj": "gemm_dma_kernel<128, 192, 2, 2, A_PLAIN, E_BIAS>",
 }
+
+
+def stats_in_conv(s):
+    """Whether the bf16 conv's epilogue computes the GroupNorm partial
+    statistics (and its launch the restore fold): the library does so when
+    the conv runs on the direct-load kernel and its 256-row tiles never
+    straddle two samples."""
+    return s.dtype == "bf16" and s.N % 256 == 0 and s.C % 64 == 0 and s.Cr % 96 == 0
 
 
 def algorithmic_work(s):
@@ -53,12 +61,23 @@ def algorithmic_work(s):
     B, N, C, Cr, h, d = s.B, s.N, s.C, s.Cr, s.heads, s.head_dim
     M, Mc = B * N, B * s.Nc
     st = B * h * (d * d + d) * 4
+    conv = (2.0 * M * Cr * 9 * C, es * (M * C + Cr * 9 * C + M * Cr + Cr))
+    stats = (3.0 * M * Cr, es * M * Cr)
+    act = (3.0 * M * Cr, es * 2 * M * Cr)
+    # the fold [W_q | W_q W_cf2], b_q + W_q b_cf2
+    fold = (2.0 * C * C * Cr, es * (C * C + C * Cr + 2 * C + C * (C + Cr) + C))
+    if stats_in_conv(s):
+        # the statistics leave the conv in registers; the gn_stats step merges the per-(tile, channel)
+        # partials (M / 256 x C/r x 2 floats); the fold runs in the conv's launch
+        conv = (conv[0] + stats[0] + fold[0], conv[1] + fold[1] + 8 * (M // 256) * Cr)
+        stats = (3.0 * (M // 256) * Cr, 8 * (M // 256) * Cr)
+    else:
+        act = (act[0] + fold[0], act[1] + fold[1])
     return {
-        "cf_conv3x3": (2.0 * M * Cr * 9 * C, es * (M * C + Cr * 9 * C + M * Cr + Cr)),
-        "gn_stats": (3.0 * M * Cr, es * M * Cr),
-        # GN + LeakyReLU over xc; the fold [W_q | W_q W_cf2], b_q + W_q b_cf2
-        "cf_act": (3.0 * M * Cr + 2.0 * C * C * Cr,
-                   es * (2 * M * Cr + C * C + C * Cr + 2 * C + C * (C + Cr) + C)),
+        "cf_conv3x3": conv,
+        "gn_stats": stats,
+        # GN + LeakyReLU over xc (and the fold, when the conv's launch does not take it)
+        "cf_act": act,
         # ReLU([X | act] [W_q | W_q W_cf2]^T + b)
         "q_proj": (2.0 * M * C * (C + Cr), es * (M * C + M * Cr + M * C + C * (C + Cr) + C)),
         "kv_proj": (2.0 * M * 2 * C * C, es * (M * C + 2 * M * C + 2 * C * C + 2 * C)),

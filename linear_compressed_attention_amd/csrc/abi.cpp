@@ -119,6 +119,20 @@ edit_status_t apply_variant(const edit_variant_t* v, Geometry* g) {
   return EDIT_OK;
 }
 
+// The bf16 conv computes the GroupNorm partial statistics in its epilogue when its 256-row tiles never
+// straddle two samples (H*W a multiple of 256) and it runs on the direct-load kernel (C a multiple of 64,
+// C/r of 96); otherwise a separate pass over xc does.
+constexpr int kGnTileRows = 256;
+bool gn_in_conv(const Geometry& g) {
+  return g.es == 2 && g.N % kGnTileRows == 0 && g.C % 64 == 0 && g.Cr % 96 == 0 &&
+         (size_t)g.M * g.C * 2 < 0x80000000ull && (size_t)g.Cr * 9 * g.C * 2 < 0x80000000ull;
+}
+size_t gn_part_bytes(const Geometry& g) {
+  const size_t sep = (size_t)g.B * g.gn_chunks * g.G * 2 * 4;
+  const size_t fused = gn_in_conv(g) ? (size_t)g.M / kGnTileRows * g.Cr * 2 * 4 : 0;
+  return sep > fused ? sep : fused;
+}
+
 Layout make_layout(const Geometry& g) {
   Layout L{};
   size_t off = 0;
@@ -126,7 +140,7 @@ Layout make_layout(const Geometry& g) {
   const size_t M = g.M, es = g.es, BH = (size_t)g.B * g.heads;
   if (g.qmode == EDIT_QUERY_CONVFUSION) {
     L.xc = take(M * g.Cr * es);
-    L.gn_part = take((size_t)g.B * g.gn_chunks * g.G * 2 * 4);
+    L.gn_part = take(gn_part_bytes(g));
     L.gn_stat = take((size_t)g.B * g.G * 2 * 4);
     L.gn_scale = take((size_t)g.B * g.Cr * 4);
     L.gn_shift = take((size_t)g.B * g.Cr * 4);
@@ -142,7 +156,7 @@ Layout make_layout(const Geometry& g) {
   }
   if (g.kvmode == EDIT_KV_KEY_CONVFUSION) {
     L.xc_k = take(M * g.Cr * es);
-    L.gn_part_k = take((size_t)g.B * g.gn_chunks * g.G * 2 * 4);
+    L.gn_part_k = take(gn_part_bytes(g));
     L.gn_stat_k = take((size_t)g.B * g.G * 2 * 4);
     L.gn_scale_k = take((size_t)g.B * g.Cr * 4);
     L.gn_shift_k = take((size_t)g.B * g.Cr * 4);
@@ -266,6 +280,9 @@ edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const
                          const void* b_lin, T* xc, float* gn_part, float* gn_stat, float* gn_scale, float* gn_shift,
                          T* act, T* wcat, T* bcat, hipStream_t s, const Marks& mk, int parts = CF_ALL) {
   using namespace edit;
+  // bf16: the restore fold goes with the conv's launch (see GemmArgs::fold)
+  const bool fold_with_conv = (parts & CF_CONV) && (parts & CF_FOLD) && std::is_same<T, bf16>::value &&
+                              g.C % 64 == 0 && g.Cr % 32 == 0;
   if (parts & CF_CONV) {
     // xc = Conv3x3(x) + b_cf1
     EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_CONV3X3));
@@ -274,18 +291,34 @@ edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const
     a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(w_cf1);
     a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(b_cf1);
     a.seg_rows = g.Cr; a.ldb = 9 * g.C; a.C = xc; a.ldc = g.Cr;
-    EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
+    if constexpr (std::is_same<T, bf16>::value) {
+      if (fold_with_conv)
+        a.fold = FoldArgs{static_cast<const bf16*>(w_lin), static_cast<const bf16*>(b_lin),
+                          static_cast<const bf16*>(w_cf2), static_cast<const bf16*>(b_cf2), wcat, bcat, g.C, g.Cr};
+    }
+    if (gn_in_conv(g)) {
+      a.gnp = gn_part; a.gn_rows = kGnTileRows;
+      EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS_GN, s));
+    } else {
+      EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
+    }
   }
   if (parts & CF_NORM) {
     // GroupNorm statistics -> per-channel scale / shift; act = LeakyReLU(GN(xc))
     EDIT_LAUNCH(mk.mark(EDIT_STEP_GN_STATS));
-    EDIT_LAUNCH(launch_groupnorm_stats<T>(xc, g.B, g.N, g.Cr, g.G, static_cast<const T*>(gamma),
-                                          static_cast<const T*>(beta), 1e-5f, gn_part, g.gn_chunks, gn_stat,
-                                          gn_scale, gn_shift, s));
+    if (gn_in_conv(g)) {
+      EDIT_LAUNCH(launch_groupnorm_finalize_channels<T>(gn_part, g.B, g.N, g.Cr, g.G, kGnTileRows,
+                                                        static_cast<const T*>(gamma), static_cast<const T*>(beta),
+                                                        1e-5f, gn_stat, gn_scale, gn_shift, s));
+    } else {
+      EDIT_LAUNCH(launch_groupnorm_stats<T>(xc, g.B, g.N, g.Cr, g.G, static_cast<const T*>(gamma),
+                                            static_cast<const T*>(beta), 1e-5f, gn_part, g.gn_chunks, gn_stat,
+                                            gn_scale, gn_shift, s));
+    }
     EDIT_LAUNCH(mk.mark(EDIT_STEP_CF_ACT));
     EDIT_LAUNCH(launch_groupnorm_apply<T>(xc, g.B, g.N, g.Cr, gn_scale, gn_shift, act, s));
   }
-  if (parts & CF_FOLD) {
+  if ((parts & CF_FOLD) && !fold_with_conv) {
     // the restore folded into the Linear's weights
     EDIT_LAUNCH(launch_restore_fold<T>(static_cast<const T*>(w_lin), static_cast<const T*>(b_lin),
                                        static_cast<const T*>(w_cf2), static_cast<const T*>(b_cf2), g.C, g.Cr, wcat,

@@ -345,9 +345,30 @@ static hipError_t launch_tiles(const GemmArgs<T>& a, AMode am, EMode em, hipStre
 template <typename T>
 hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.fold.W != nullptr) {
+    // the restore fold requested with the conv: on the direct-load kernel (fused there when it can be),
+    // else the register-staged conv, then the fold's own kernel
+    if (am != A_CONV3) return hipErrorInvalidValue;
+    if constexpr (std::is_same<T, bf16>::value) {
+      const hipError_t e = launch_gemm_dma(a, am, em, s);
+      if (e != hipErrorNotSupported) return e;
+      GemmArgs<T> b = a;
+      b.fold = FoldArgs{};
+      const hipError_t e2 = launch_gemm<T>(b, am, em, s);
+      if (e2 != hipSuccess) return e2;
+      const FoldArgs& f = a.fold;
+      return launch_restore_fold<bf16>(f.W, f.b, f.W2, f.b2, f.C, f.Cr, f.wcat, f.bcat, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.R != nullptr) {
     if (em != E_BIAS) return hipErrorInvalidValue;
     em = E_RES;
+  }
+  if (em == E_BIAS_GN) {
+    // only the direct-load conv has the statistics epilogue
+    if constexpr (std::is_same<T, bf16>::value) return launch_gemm_dma(a, am, em, s);
+    return hipErrorNotSupported;
   }
   if constexpr (std::is_same<T, bf16>::value) {
     const hipError_t e = launch_gemm_dma(a, am, em, s);

@@ -96,9 +96,25 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
   __shared__ __attribute__((aligned(16))) char S0[STAGE];
   __shared__ __attribute__((aligned(16))) char S1[STAGE];
   __shared__ __attribute__((aligned(16))) char S2[ST == 3 ? STAGE : 16];
+  // E_BIAS_GN: per-wave column sums, then the tile's column means.
+  static_assert(EM != E_BIAS_GN || WN == 1, "the statistics epilogue has every wave on all BN columns");
+  __shared__ float gnred[EM == E_BIAS_GN ? WM * BN : 1];
+  __shared__ float gnmean[EM == E_BIAS_GN ? BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
+  // The last fold_blocks blocks of a conv launch compute the restore fold
+  // (fold.hpp) on CUs the conv's tiles leave idle; their LDS holds the
+  // fold's partial tiles instead of stages.
+  const int nblk = (int)gridDim.x - (AM == A_CONV3 ? p.fold_blocks : 0);
+  if (AM == A_CONV3 && (int)blockIdx.x >= nblk) {
+    float(*red)[32][33] = reinterpret_cast<float(*)[32][33]>(S0);
+    const int fb = (int)blockIdx.x - nblk, steps = p.fold.C / 64;
+    if (steps % 6 == 0) fold_blocks<6>(p.fold, fb, p.fold_blocks, red);
+    else if (steps % 2 == 0) fold_blocks<2>(p.fold, fb, p.fold_blocks, red);
+    else fold_blocks<1>(p.fold, fb, p.fold_blocks, red);
+    return;
+  }
   const int tiles_n = (p.N + BN - 1) / BN;
   const int tiles_mn = ((p.M + BM - 1) / BM) * tiles_n;
   // K steps of the current tile; E_F32 (split K): tile index = split * tiles_mn
@@ -373,7 +389,7 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
     // stages are free. Queue the next tile's first three steps, then write
     // this tile from registers while they are in flight.
     const int em0 = m0, en0 = n0, esplit = split;
-    const int next = tl + (int)gridDim.x;
+    const int next = tl + nblk;
     if (next < ntiles) {
       EDIT_SET_TILE(next);
       EDIT_PREFETCH3();
@@ -398,6 +414,72 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
       if (next >= ntiles) break;
       tl = next;
       continue;
+    }
+    if (EM == E_BIAS_GN) {
+      // GroupNorm partial statistics of the tile as stored (bf16), per column over its BM rows:
+      // the exact mean, then the sum of squared deviations from it. Element k of accumulator (t, c)
+      // is column c*32 + 8(k/4) + 4(l>>5) + k%4 of row t*32 + (l & 31). Each lane first adds its TI
+      // rows for all its CJ*16 columns; the 32 lanes of a half-wave then add level by level (every
+      // level a batch of independent steps: four row-local DPP moves, then the swap of 16-lane
+      // rows), and the waves' sums meet in LDS. A fixed order throughout.
+      constexpr int NV = CJ * 16;
+      float sm[NV];
+      auto stored = [&](int t, int c, int k) -> float {
+        return (float)(bf16)(acc[t][c][k] + (float)bv[c][k >> 2][k & 3]);
+      };
+#pragma unroll
+      for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int c = 0; c < CJ; ++c)
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const float mu = pass ? gnmean[c * 32 + 8 * (k >> 2) + 4 * fh + (k & 3)] : 0.0f;
+            float v = 0.0f;
+#pragma unroll
+            for (int t = 0; t < TI; ++t) {
+              const float d = stored(t, c, k) - mu;
+              v += pass ? d * d : d;
+            }
+            sm[c * 16 + k] = v;
+          }
+        // lane i += lane i^1, i^2 (quad perms), then 7-i within 8, then 15-i within 16 (mirrors)
+#define EDIT_DPP_LEVEL(CTRL)                                                                          \
+        _Pragma("unroll") for (int j = 0; j < NV; ++j)                                                 \
+          sm[j] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                              \
+              0, __builtin_bit_cast(int, sm[j]), (CTRL), 0xF, 0xF, false));
+        EDIT_DPP_LEVEL(0xB1)
+        EDIT_DPP_LEVEL(0x4E)
+        EDIT_DPP_LEVEL(0x141)
+        EDIT_DPP_LEVEL(0x140)
+#undef EDIT_DPP_LEVEL
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          // the other 16-lane row of this half-wave (rows 0 <-> 1, 2 <-> 3)
+          const uint32_t u = __builtin_bit_cast(uint32_t, sm[j]);
+          const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+          sm[j] += __builtin_bit_cast(float, (lane & 16) ? pr[0] : pr[1]);
+        }
+        if (fr == 0) {
+#pragma unroll
+          for (int c = 0; c < CJ; ++c)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) gnred[wm * BN + c * 32 + 8 * (k >> 2) + 4 * fh + (k & 3)] = sm[c * 16 + k];
+        }
+        stage_barrier<63>();   // LDS only: the next tile's loads stay in flight
+        if (tid < BN) {
+          float v = 0.0f;
+#pragma unroll
+          for (int w = 0; w < WM; ++w) v += gnred[w * BN + tid];
+          if (pass == 0) {
+            gnmean[tid] = v / (float)BM;
+          } else if (en0 + tid < p.N) {
+            float* o = p.gnp + ((size_t)(em0 / BM) * p.N + en0 + tid) * 2;
+            o[0] = gnmean[tid];
+            o[1] = v;
+          }
+        }
+        stage_barrier<63>();
+      }
     }
     // Epilogue: bias (+ ReLU). Accumulator quad g of lane l holds channels
     // 8g + 4(l >> 5) .. +3 of token l & 31; lanes l and l ^ 32 swap the
@@ -505,14 +587,27 @@ hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, hipStream_t s) {
   if (EM == E_F32) ntiles *= (a.K + a.kchunk - 1) / a.kchunk;
   const int g8 = cus / 8 * 8;
   const int blocks = ST == 2 || ntiles <= g8 || a.spread ? ntiles : g8;
-  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, AM, EM, ST>), dim3(blocks), dim3(64 * WM * WN), 0, s, a, ntiles);
-  return hipGetLastError();
+  GemmArgs<bf16> b = a;
+  b.fold_blocks = 0;
+  // The fold rides along when the conv leaves at least 16 CUs idle; otherwise it runs after.
+  const bool fold_here = AM == A_CONV3 && a.fold.W != nullptr && a.fold.C % 64 == 0 && a.fold.Cr % 32 == 0 &&
+                         blocks + 16 <= cus;
+  if (fold_here) b.fold_blocks = cus - blocks;
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, WM, WN, AM, EM, ST>), dim3(blocks + b.fold_blocks), dim3(64 * WM * WN), 0,
+                     s, b, ntiles);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || AM != A_CONV3 || a.fold.W == nullptr || fold_here) return e;
+  const FoldArgs& f = a.fold;
+  return launch_restore_fold<bf16>(f.W, f.b, f.W2, f.b2, f.C, f.Cr, f.wcat, f.bcat, s);
 }
 
 }  // namespace
 
 #ifndef EDIT_DMA_FORCE
 #define EDIT_DMA_FORCE 0
+#endif
+#ifndef EDIT_CONV_TILE
+#define EDIT_CONV_TILE 0
 #endif
 
 // Returns hipErrorNotSupported (nothing launched) when the shape is outside
@@ -531,9 +626,17 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
   //  - the 3x3 conv (162 K steps): 119 us against 227 us for the register-staged kernel;
   //  - plain-A projections with 128 x 192 tiles, two stages, two blocks per CU: 46 us at
   //    16384 x 1152 x 1152 and 91 us at 16384 x 2304 x 1152 against 63 and 105 us register-staged.
-  if (am == A_CONV3 && (em == E_BIAS || em == E_RES)) {
+  if (am == A_CONV3 && (em == E_BIAS || em == E_RES || em == E_BIAS_GN)) {
     if (a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin) return hipErrorNotSupported;
     if (em == E_RES) return n96 ? launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_RES>(a, s) : hipErrorNotSupported;
+    if (em == E_BIAS_GN) {
+      // every 256-row tile full (its rows are one sample's when H*W is a multiple of 256)
+      if (!n96 || a.M % 256 != 0 || a.gn_rows != 256 || a.gnp == nullptr) return hipErrorNotSupported;
+      return launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_BIAS_GN>(a, s);
+    }
+#if EDIT_CONV_TILE == 1
+    if (n96) return launch_dma_tiles<128, 96, 4, 1, A_CONV3, E_BIAS, 2>(a, s);
+#endif
     if (n96) return launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_BIAS>(a, s);
     if (n128) return launch_dma_tiles<256, 128, 2, 2, A_CONV3, E_BIAS>(a, s);
     return hipErrorNotSupported;

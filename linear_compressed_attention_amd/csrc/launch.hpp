@@ -2,6 +2,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include "fold.hpp"
+
 namespace edit {
 
 typedef __bf16 bf16;
@@ -17,7 +19,8 @@ enum EMode {
   E_BIAS = 0,       // C = acc + bias
   E_BIAS_RELU = 1,  // C = max(acc + bias, 0)
   E_F32 = 2,        // Cf[split][m][n] = acc (fp32, no bias): one K slice of a split-K product
-  E_RES = 3         // C = acc + bias + R (launch_gemm picks it for E_BIAS when GemmArgs::R is set)
+  E_RES = 3,        // C = acc + bias + R (launch_gemm picks it for E_BIAS when GemmArgs::R is set)
+  E_BIAS_GN = 4     // C = acc + bias, and GroupNorm partial statistics of the stored tile into gnp
 };
 
 // C[M][N] = A[M][K] * B[N][K]^T + epilogue. B and the bias may come in up
@@ -50,6 +53,14 @@ struct GemmArgs {
   // E_BIAS with R set (run as E_RES): C = A B^T + bias + R (R [M][ldr], the same type as C).
   const T* R;
   int ldr;
+  // E_BIAS_GN (the direct-load conv only): per output tile of gn_rows rows and every column n,
+  // gnp[(m0 / gn_rows) * N + n] = (mean, sum of squared deviations) of the stored values.
+  float* gnp;
+  int gn_rows;
+  // bf16 A_CONV3 with fold.W set: the restore fold (fold.hpp) is also computed, by extra blocks of the
+  // conv's launch where its tiles leave CUs idle, else by the fold's own kernel after it.
+  FoldArgs fold;
+  int fold_blocks;             // set by the launcher
 };
 
 template <typename T>
@@ -68,6 +79,12 @@ hipError_t launch_groupnorm_stats(const T* x, int B, int HW, int C, int G, const
                                   const T* beta, float eps, float* partial, int nchunks,
                                   float* stat, float* scale, float* shift, hipStream_t s);
 int groupnorm_chunks(int HW, int C);
+// GroupNorm statistics from per-(tile, channel) partials (mean, M2) of tiles of `rows` rows
+// (partial [B * HW / rows][C][2]; HW a multiple of rows): stat, scale and shift as launch_groupnorm_stats.
+template <typename T>
+hipError_t launch_groupnorm_finalize_channels(const float* partial, int B, int HW, int C, int G, int rows,
+                                              const T* gamma, const T* beta, float eps, float* stat, float* scale,
+                                              float* shift, hipStream_t s);
 
 // The ConvFusion 1x1 restore (W2 [C][Cr], b2 [C]) folded into a Linear
 // (W [C][C], b [C]) that reads X + act W2^T + b2: wcat [C][C + Cr] = [W | W W2],

@@ -176,6 +176,65 @@ hipError_t launch_groupnorm_stats(const T* x, int B, int HW, int C, int G, const
   return hipGetLastError();
 }
 
+// Statistics from the conv epilogue's partials: one (mean, M2) per tile of
+// `rows` rows and channel. One block per (group, sample) Chan-merges the
+// (tile, channel) items of its sample and group, each thread a strided
+// subset, then the same fixed LDS tree as above; scale / shift as above.
+template <typename T>
+__global__ __launch_bounds__(256) void gn_finalize_channels_kernel(const float* __restrict__ partial, int HW, int C,
+                                                                   int G, int rows, const T* __restrict__ gamma,
+                                                                   const T* __restrict__ beta, float eps,
+                                                                   float* __restrict__ stat, float* __restrict__ scale,
+                                                                   float* __restrict__ shift) {
+  __shared__ float sn[256], smean[256], sm2[256];
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int cg = C / G, tps = HW / rows;
+  Welford acc = {0.0f, 0.0f, 0.0f};
+  for (int it = tid; it < tps * cg; it += 256) {
+    const int tile = b * tps + it / cg, c = g * cg + it % cg;
+    const float* pp = partial + ((size_t)tile * C + c) * 2;
+    Welford w;
+    w.n = (float)rows;
+    w.mean = pp[0];
+    w.m2 = pp[1];
+    acc = chan_merge(acc, w);
+  }
+  sn[tid] = acc.n; smean[tid] = acc.mean; sm2[tid] = acc.m2;
+  __syncthreads();
+  for (int stride = 128; stride > 0; stride >>= 1) {
+    if (tid < stride) {
+      Welford a = {sn[tid], smean[tid], sm2[tid]};
+      Welford o = {sn[tid + stride], smean[tid + stride], sm2[tid + stride]};
+      a = chan_merge(a, o);
+      sn[tid] = a.n; smean[tid] = a.mean; sm2[tid] = a.m2;
+    }
+    __syncthreads();
+  }
+  const float mean = smean[0];
+  const float var = sm2[0] / sn[0];
+  const float rstd = 1.0f / sqrtf(var + eps);
+  if (tid == 0) {
+    stat[((size_t)b * G + g) * 2] = mean;
+    stat[((size_t)b * G + g) * 2 + 1] = rstd;
+  }
+  for (int i = tid; i < cg; i += 256) {
+    const int c = g * cg + i;
+    const float sc = to_f32(gamma[c]) * rstd;
+    scale[(size_t)b * C + c] = sc;
+    shift[(size_t)b * C + c] = to_f32(beta[c]) - mean * sc;
+  }
+}
+
+template <typename T>
+hipError_t launch_groupnorm_finalize_channels(const float* partial, int B, int HW, int C, int G, int rows,
+                                              const T* gamma, const T* beta, float eps, float* stat, float* scale,
+                                              float* shift, hipStream_t s) {
+  if (rows <= 0 || HW % rows != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gn_finalize_channels_kernel<T>), dim3(G, B), dim3(256), 0, s, partial, HW, C, G, rows, gamma,
+                     beta, eps, stat, scale, shift);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // a = LeakyReLU(x * scale[b][c] + shift[b][c], 0.01): GroupNorm with its
 // affine folded into scale / shift, then the ConvFusion activation (section
@@ -281,6 +340,9 @@ hipError_t launch_dwconv_s2(const T* kv0, int B, int H, int W, int C, const T* d
                                                 hipStream_t);                                           \
   template hipError_t launch_groupnorm_stats<T>(const T*, int, int, int, int, const T*, const T*, float, \
                                                 float*, int, float*, float*, float*, hipStream_t);      \
+  template hipError_t launch_groupnorm_finalize_channels<T>(const float*, int, int, int, int, int,        \
+                                                            const T*, const T*, float, float*, float*,   \
+                                                            float*, hipStream_t);                        \
   template hipError_t launch_dwconv_s2<T>(const T*, int, int, int, int, const T*, const T*, const T*,    \
                                           const T*, T*, T*, hipStream_t);
 EDIT_INST(bf16)
