@@ -43,6 +43,13 @@ int kv_state_dk(int d) { return 32 * ((d + 31) / 32); }
 template <typename T> struct KvSlab { static constexpr int n = 256; };
 template <> struct KvSlab<float> { static constexpr int n = 64; };
 
+// Column (token) position of element (row, col) of a staged channel-major
+// tile: 8-element chunks are XOR-swizzled by row / 8, so that the transposed
+// stores, which hit rows 8 apart, fall in different LDS banks (a 528-byte
+// row pitch is a multiple of 128 bytes: unswizzled, every lane of such a
+// store hit the same bank). Rows need a multiple of 64 columns.
+__device__ __forceinline__ int kv_col(int row, int col) { return (((col >> 3) ^ ((row >> 3) & 7)) << 3) | (col & 7); }
+
 // Four tokens' values of one channel, written to LDS as one 8-byte (bf16) or
 // 16-byte (f32) word.
 __device__ __forceinline__ void store_quad(bf16* dst, bf16 a, bf16 b, bf16 c, bf16 d) {
@@ -72,6 +79,7 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   constexpr int ITEMS = 2 * QUADS * DC;    // (K or V, 8-channel chunk, token quad)
   constexpr int NLOAD = (ITEMS + 255) / 256;
   constexpr int EPC = Chunk<T>::n;         // elements per 16 bytes
+  static_assert(SLAB % 64 == 0, "kv_col swizzles within groups of 8 chunks of 8 columns");
   __shared__ __attribute__((aligned(16))) T Kt[16 * DT * PITCH];
   __shared__ __attribute__((aligned(16))) T At[16 * DR * PITCH];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -122,20 +130,23 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
       if (e < ITEMS) {
         const int c8 = (e % DC) * 8, rest = e / DC;
         const int tq = rest % QUADS, which = rest / QUADS;
-        T* dst = (which ? At : Kt) + c8 * PITCH + 4 * tq;
+        T* dst = which ? At : Kt;
         const T* v0 = reinterpret_cast<const T*>(&raw[l][0][0]);
         const T* v1 = reinterpret_cast<const T*>(&raw[l][1][0]);
         const T* v2 = reinterpret_cast<const T*>(&raw[l][2][0]);
         const T* v3 = reinterpret_cast<const T*>(&raw[l][3][0]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) store_quad(dst + i * PITCH, v0[i], v1[i], v2[i], v3[i]);
+        for (int i = 0; i < 8; ++i) {
+          const int row = c8 + i;
+          store_quad(dst + row * PITCH + kv_col(row, 4 * tq), v0[i], v1[i], v2[i], v3[i]);
+        }
       }
     }
     for (int t = tid; t < SLAB; t += 256) {
       const float wv = js + t < j1 ? (wrow ? wrow[((size_t)b * Nc + js + t) * heads + h] : 1.0f) : 0.0f;
       const T hi = from_f32<T>(wv);
-      At[d * PITCH + t] = hi;
-      At[(d + 1) * PITCH + t] = from_f32<T>(wv - to_f32(hi));
+      At[d * PITCH + kv_col(d, t)] = hi;
+      At[(d + 1) * PITCH + kv_col(d + 1, t)] = from_f32<T>(wv - to_f32(hi));
     }
     __syncthreads();
 #pragma unroll
@@ -146,8 +157,9 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
         if (tile < NT) {
           const int tr = tile / DT, tc = tile % DT;
           FragT a, bb;
-          frag_load(a, At + (tr * 16 + fr) * PITCH + ks * 32 + fk);
-          frag_load(bb, Kt + (tc * 16 + fr) * PITCH + ks * 32 + fk);
+          const int ra = tr * 16 + fr, rk = tc * 16 + fr;
+          frag_load(a, At + ra * PITCH + kv_col(ra, ks * 32 + fk));
+          frag_load(bb, Kt + rk * PITCH + kv_col(rk, ks * 32 + fk));
           mma16(acc[t], a, bb);
         }
       }

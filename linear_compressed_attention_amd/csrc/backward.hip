@@ -227,32 +227,43 @@ __device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
   for (int i = 0; i < 4; ++i) v[i] = t[i];
 }
 // M (fp32, d x d, row-major at src) into the LDS operand, or its transpose
-// (TR): dst row i, column k holds M[i][k] (TR: M[k][i]). 16-byte loads along
-// src's rows; dst holds NC copies of [RT * 32][KP].
+// (TR): dst row i, column k holds M[i][k] (TR: M[k][i]); dst holds NC copies
+// of [RT * 32][KP]. A thread writes 4 consecutive columns of one row as one
+// vector per copy (neighbouring threads: neighbouring columns).
+__device__ __forceinline__ void store4_lds(bf16* p, const float (&v)[4]) { store4(p, v); }
+__device__ __forceinline__ void store4_lds(float* p, const float (&v)[4]) { store4(p, v); }
+
 template <typename T, int KS, bool TR>
 __device__ __forceinline__ void head_mat_fill(T* dst, const float* __restrict__ src, int d) {
   using HM = HeadMat<T, KS>;
   constexpr int CP = HM::RT * 32 * HM::KP;
   constexpr int RW = HM::RT * 32;                  // rows of the operand
-  constexpr int QW = (KS * 16) / 4;                // 4-element groups along K
-  // Source element groups: (i, k0..k0+3) of M. Not transposed: i = operand
-  // row, k = operand column; transposed: the operand's row is k.
-  constexpr int NI = TR ? KS * 16 : RW, NQ = TR ? RW / 4 : QW;
+  constexpr int NQ = (KS * 16) / 4;                // 4-column groups per row
 #pragma unroll 4
-  for (int e = threadIdx.x; e < NI * NQ; e += blockDim.x) {
-    const int i = e / NQ, k0 = (e - i * NQ) * 4;
-    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (i < d && k0 < d) v = *reinterpret_cast<const f32x4*>(src + (size_t)i * d + k0);
+  for (int e = threadIdx.x; e < RW * NQ; e += blockDim.x) {
+    const int row = e / NQ, c0 = (e - row * NQ) * 4;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (row < d && c0 < d) {
+      if constexpr (TR) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = TR ? k0 + j : i, col = TR ? i : k0 + j;
-      if constexpr (HM::NC == 2) {
-        const bf16 hi = (bf16)v[j];
-        dst[row * HM::KP + col] = hi;
-        dst[CP + row * HM::KP + col] = (bf16)(v[j] - (float)hi);
+        for (int j = 0; j < 4; ++j) v[j] = src[(size_t)(c0 + j) * d + row];
       } else {
-        dst[row * HM::KP + col] = v[j];
+        const f32x4 q = *reinterpret_cast<const f32x4*>(src + (size_t)row * d + c0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = q[j];
       }
+    }
+    if constexpr (HM::NC == 2) {
+      float hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hi[j] = (float)(bf16)v[j];
+        lo[j] = v[j] - hi[j];
+      }
+      store4_lds(dst + row * HM::KP + c0, hi);
+      store4_lds(dst + CP + row * HM::KP + c0, lo);
+    } else {
+      store4_lds(dst + row * HM::KP + c0, v);
     }
   }
 }
