@@ -50,6 +50,15 @@ SHAPES = {
                                    dtype="bf16", x_std=1.0),
     "bf16_c1152": make_shape(B=1, H=16, W=16, C=1152, heads=16, head_dim=72, reduction=4, gn_groups=32,
                              dtype="bf16", x_std=1.0),
+    # the per-head kernels' extremes: one 16-wide K step (d = 8) and eight (d = 128), and an even count (d = 64)
+    "f32_d8": make_shape(B=1, H=10, W=9, C=64, heads=8, head_dim=8, reduction=4, gn_groups=2, dtype="f32",
+                         x_std=1.0),
+    "f32_d64": make_shape(B=2, H=7, W=10, C=192, heads=3, head_dim=64, reduction=4, gn_groups=4, dtype="f32",
+                          x_std=1.0),
+    "f32_d128": make_shape(B=1, H=12, W=9, C=256, heads=2, head_dim=128, reduction=4, gn_groups=8, dtype="f32",
+                           x_std=1.0),
+    "bf16_d128": make_shape(B=1, H=12, W=10, C=256, heads=2, head_dim=128, reduction=4, gn_groups=8,
+                            dtype="bf16", x_std=1.0),
 }
 F32_PIXART1024 = make_shape(B=2, H=64, W=64, C=1152, heads=16, head_dim=72, reduction=4, gn_groups=32,
                             dtype="f32", x_std=1.0)
