@@ -302,20 +302,22 @@ __global__ __launch_bounds__(256) void dwconv_s2_kernel(const T* __restrict__ kv
   float acc[8];
   load8(bias + ch, acc);
   const T* img = kv0 + (size_t)b * H * W * 2 * C + ch2;
+  // Every tap's load is issued (at a clamped, in-image position) before any
+  // is used; a tap outside the image then contributes zero.
+  float v[9][8], wv[9][8];
 #pragma unroll
-  for (int ky = 0; ky < 3; ++ky) {
-    const int yy = 2 * yo + ky - 1;
-    if (yy < 0 || yy >= H) continue;
+  for (int t = 0; t < 9; ++t) {
+    const int yy = 2 * yo + t / 3 - 1, xx = 2 * xo + t % 3 - 1;
+    const int yc = min(max(yy, 0), H - 1), xcl = min(max(xx, 0), W - 1);
+    load8(img + ((size_t)yc * W + xcl) * 2 * C, v[t]);
+    load8(w + t * C + ch, wv[t]);
+  }
 #pragma unroll
-    for (int kx = 0; kx < 3; ++kx) {
-      const int xx = 2 * xo + kx - 1;
-      if (xx < 0 || xx >= W) continue;
-      float v[8], wv[8];
-      load8(img + ((size_t)yy * W + xx) * 2 * C, v);
-      load8(w + (ky * 3 + kx) * C + ch, wv);
+  for (int t = 0; t < 9; ++t) {
+    const int yy = 2 * yo + t / 3 - 1, xx = 2 * xo + t % 3 - 1;
+    const bool in = yy >= 0 && yy < H && xx >= 0 && xx < W;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += wv[i] * v[i];
-    }
+    for (int i = 0; i < 8; ++i) acc[i] += in ? wv[t][i] * v[t][i] : 0.0f;
   }
   if (is_k) {
 #pragma unroll
