@@ -85,13 +85,29 @@ __device__ __forceinline__ void fold_tile(const FoldArgs& f, int tile, float (*r
   __syncthreads();   // red is free for the next tile
 }
 
-// [W | .] part of wcat: 16-byte chunks, chunk idx of every stride-th from first.
+// [W | .] part of wcat: 16-byte chunks, chunk idx of every stride-th from
+// first; eight loads are in flight before their stores.
 __device__ __forceinline__ void fold_copy(const FoldArgs& f, int first, int stride) {
-  const int ldw = f.C + f.Cr, cpr = f.C / 8;
-  for (int idx = first; idx < f.C * cpr; idx += stride) {
-    const int r = idx / cpr, c8 = idx - r * cpr;
-    *reinterpret_cast<bf16x8*>(f.wcat + (size_t)r * ldw + 8 * c8) =
-        *reinterpret_cast<const bf16x8*>(f.W + (size_t)r * f.C + 8 * c8);
+  constexpr int U = 8;
+  const int ldw = f.C + f.Cr, cpr = f.C / 8, total = f.C * cpr;
+  for (int base = first; base < total; base += U * stride) {
+    bf16x8 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * stride;
+      if (idx < total) {
+        const int r = idx / cpr, c8 = idx - r * cpr;
+        v[u] = *reinterpret_cast<const bf16x8*>(f.W + (size_t)r * f.C + 8 * c8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * stride;
+      if (idx < total) {
+        const int r = idx / cpr, c8 = idx - r * cpr;
+        *reinterpret_cast<bf16x8*>(f.wcat + (size_t)r * ldw + 8 * c8) = v[u];
+      }
+    }
   }
 }
 

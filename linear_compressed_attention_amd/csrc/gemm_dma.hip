@@ -78,8 +78,14 @@ __device__ __forceinline__ P pick_seg(const P (&a)[3], int i) {
 
 }  // namespace
 
+// Blocks resident per CU: two-stage 4-wave blocks pair up; 8-wave blocks and
+// three-stage blocks run alone (still two waves per SIMD for 8 waves).
+template <int NW, int ST>
+constexpr int dma_blocks_per_cu() { return ST == 2 && NW <= 4 ? 2 : 1; }
+
 template <int BM, int BN, int WM, int WN, int AM, int EM, int ST>
-__global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel(GemmArgs<bf16> p, int ntiles) {
+__global__ __launch_bounds__(64 * WM * WN, (dma_blocks_per_cu<WM * WN, ST>())) void gemm_dma_kernel(GemmArgs<bf16> p,
+                                                                                                     int ntiles) {
   // The body uses gfx950-only types (buffer resources), which the host pass
   // cannot instantiate; it only needs the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
   constexpr int STAGE = (BM + BN) * 128;          // bytes per stage
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile");
   static_assert(BM % 16 == 0, "B rows keep the swizzle phase of their LDS row");
-  static_assert(ST * STAGE <= (ST == 2 ? 80 : 160) * 1024, "LDS");
+  static_assert(ST * STAGE <= 160 * 1024 / dma_blocks_per_cu<NW, ST>(), "LDS");
   static_assert(2 * NPER < 64, "vmcnt range");
   __shared__ __attribute__((aligned(16))) char S0[STAGE];
   __shared__ __attribute__((aligned(16))) char S1[STAGE];
@@ -110,7 +116,8 @@ __global__ __launch_bounds__(64 * WM * WN, ST == 2 ? 2 : 1) void gemm_dma_kernel
   if (AM == A_CONV3 && (int)blockIdx.x >= nblk) {
     float(*red)[32][33] = reinterpret_cast<float(*)[32][33]>(S0);
     const int fb = (int)blockIdx.x - nblk, steps = p.fold.C / 64;
-    if (steps % 6 == 0) fold_blocks<6>(p.fold, fb, p.fold_blocks, red);
+    if (steps % 18 == 0) fold_blocks<18>(p.fold, fb, p.fold_blocks, red);
+    else if (steps % 6 == 0) fold_blocks<6>(p.fold, fb, p.fold_blocks, red);
     else if (steps % 2 == 0) fold_blocks<2>(p.fold, fb, p.fold_blocks, red);
     else fold_blocks<1>(p.fold, fb, p.fold_blocks, red);
     return;
@@ -578,7 +585,9 @@ hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, hipStream_t s) {
   // Spread: one block per tile instead (the loop then ends after one tile),
   // so that CUs that another stream's kernels leave free take tiles as they
   // come; measured 3-6% slower than persistent blocks on an idle chip.
-  // Two stages: always one block per tile, two resident per CU.
+  // Two stages with 4-wave blocks: always one block per tile, two resident
+  // per CU. Two stages with 8-wave blocks: one block per CU, persistent like
+  // three stages (the next tile's two steps are queued before the epilogue).
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -586,7 +595,8 @@ hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, hipStream_t s) {
   int ntiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (EM == E_F32) ntiles *= (a.K + a.kchunk - 1) / a.kchunk;
   const int g8 = cus / 8 * 8;
-  const int blocks = ST == 2 || ntiles <= g8 || a.spread ? ntiles : g8;
+  const bool paired = dma_blocks_per_cu<WM * WN, ST>() == 2;
+  const int blocks = paired || ntiles <= g8 || a.spread ? ntiles : g8;
   GemmArgs<bf16> b = a;
   b.fold_blocks = 0;
   // The fold rides along when the conv leaves at least 16 CUs idle; otherwise it runs after.
