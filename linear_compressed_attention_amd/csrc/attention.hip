@@ -82,7 +82,10 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   static_assert(SLAB % 64 == 0, "kv_col swizzles within groups of 8 chunks of 8 columns");
   __shared__ __attribute__((aligned(16))) T Kt[16 * DT * PITCH];
   __shared__ __attribute__((aligned(16))) T At[16 * DR * PITCH];
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // (sample, chunk, head) order, head fastest, contiguous per XCD: the heads
+  // of one chunk share its token rows' cache lines in one L2.
+  const int lb = xcd_swizzle((int)blockIdx.x, (int)gridDim.x);
+  const int h = lb % heads, chunk = (lb / heads) % nchunks, b = lb / heads / nchunks;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = chunk * kKvChunk, j1 = min(Nc, j0 + kKvChunk);
 
@@ -225,7 +228,8 @@ template <typename T>
 hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int heads, int d, float* partial,
                            int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s, const float* wrow) {
   const int DT = (d + 15) / 16, DR = (d + 16) / 16;
-  dim3 grid(nchunks, heads, B);
+  if ((long long)nchunks * heads * B >= (1LL << 31)) return hipErrorInvalidValue;
+  dim3 grid(nchunks * heads * B);
   switch (d / 8) {
 #define EDIT_KV_CASE(DCV)                                                                              \
   case DCV:                                                                                            \
@@ -274,7 +278,13 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
   typedef typename Frag<T>::type FragT;
   __shared__ __attribute__((aligned(16))) T sst[NPART * DP * PITCH];
   __shared__ float szp[DK];
-  const int h = blockIdx.y, b = blockIdx.z;
+  // Blocks in (sample, token range, head) order, head fastest, each XCD
+  // taking a contiguous range: the heads of one token range run together on
+  // one XCD, whose L2 then merges their partial-line reads of q and writes
+  // of y (a head's slice of a token row is d elements, not whole lines).
+  const int ntb = (N + kApplyTokens - 1) / kApplyTokens;
+  const int lb = xcd_swizzle((int)blockIdx.x, (int)gridDim.x);
+  const int h = lb % heads, tb = (lb / heads) % ntb, b = lb / heads / ntb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
   const size_t bh = (size_t)b * heads + h;
@@ -306,7 +316,7 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
 #pragma unroll
     for (int i = 0; i < 8; ++i) zr[s][i] = szp[s * 32 + g * 8 + i];
 
-  const int tile0 = (blockIdx.x * 4 + wave) * TPW;
+  const int tile0 = (tb * 4 + wave) * TPW;
   // Query fragments run PD tiles ahead of the matrix work (a ring of PD
   // register sets, about 48 registers), so PD - 1 memory latencies overlap.
   constexpr int QREG = KS * (int)sizeof(FragT) / 4;
@@ -371,7 +381,8 @@ template <typename T>
 hipError_t launch_linattn_apply(const T* q, int ldq, const T* st, const float* zp, int B, int N, int heads,
                                 int d, float eps, T* y, int ldy, float* den_out, hipStream_t s) {
   const int blocks = (N + kApplyTokens - 1) / kApplyTokens;
-  dim3 grid(blocks, heads, B), block(256);
+  if ((long long)blocks * heads * B >= (1LL << 31)) return hipErrorInvalidValue;
+  dim3 grid(blocks * heads * B), block(256);
   switch ((d + 15) / 16) {
 #define EDIT_APPLY_CASE(DTV)                                                                        \
   case DTV:                                                                                         \
