@@ -36,7 +36,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core (f32: ve
 STEP_NAMES = ["cf_conv3x3", "gn_stats", "cf_act", "q_proj", "kv_proj", "sc_dwconv", "kv_state",
               "linattn_apply", "out_proj"]
 STEP_KERNELS = {  # kernels launched per step at bf16 (rocprofv3 names start with these)
-    "cf_conv3x3": "gemm_dma_kernel<256, 96, 4, 1, A_CONV3, E_BIAS_GN> (with the GroupNorm partials and the restore fold)",
+    "cf_conv3x3": "gemm_dma_kernel<256 or 128, 96, 4, 1, A_CONV3, E_BIAS_GN> (with the GroupNorm partials and the restore fold)",
     "gn_stats": "gn_finalize_channels_kernel",
     "cf_act": "gn_apply_kernel",
     "q_proj": "gemm_dma_kernel<128, 192, 2, 2, A_CAT2, E_BIAS_RELU>",
@@ -46,12 +46,19 @@ STEP_KERNELS = {  # kernels launched per step at bf16 (rocprofv3 names start wit
 }
 
 
+def gn_tile_rows(s):
+    """Rows per statistics tile of the conv's epilogue: 256, or 128 where
+    256-row tiles would fill fewer than half of the 256 CUs (the library's
+    rule)."""
+    return 128 if (s.B * s.N // 256) * (s.Cr // 96) < 128 and s.N % 128 == 0 else 256
+
+
 def stats_in_conv(s):
     """Whether the bf16 conv's epilogue computes the GroupNorm partial
     statistics (and its launch the restore fold): the library does so when
-    the conv runs on the direct-load kernel and its 256-row tiles never
+    the conv runs on the direct-load kernel and its row tiles never
     straddle two samples."""
-    return s.dtype == "bf16" and s.N % 256 == 0 and s.C % 64 == 0 and s.Cr % 96 == 0
+    return s.dtype == "bf16" and s.N % gn_tile_rows(s) == 0 and s.C % 64 == 0 and s.Cr % 96 == 0
 
 
 def algorithmic_work(s):
@@ -68,9 +75,10 @@ def algorithmic_work(s):
     fold = (2.0 * C * C * Cr, es * (C * C + C * Cr + 2 * C + C * (C + Cr) + C))
     if stats_in_conv(s):
         # the statistics leave the conv in registers; the gn_stats step merges the per-(tile, channel)
-        # partials (M / 256 x C/r x 2 floats); the fold runs in the conv's launch
-        conv = (conv[0] + stats[0] + fold[0], conv[1] + fold[1] + 8 * (M // 256) * Cr)
-        stats = (3.0 * (M // 256) * Cr, 8 * (M // 256) * Cr)
+        # partials (M / rows x C/r x 2 floats); the fold runs in the conv's launch
+        tiles = M // gn_tile_rows(s)
+        conv = (conv[0] + stats[0] + fold[0], conv[1] + fold[1] + 8 * tiles * Cr)
+        stats = (3.0 * tiles * Cr, 8 * tiles * Cr)
     else:
         act = (act[0] + fold[0], act[1] + fold[1])
     return {

@@ -119,17 +119,21 @@ edit_status_t apply_variant(const edit_variant_t* v, Geometry* g) {
   return EDIT_OK;
 }
 
-// The bf16 conv computes the GroupNorm partial statistics in its epilogue when its 256-row tiles never
-// straddle two samples (H*W a multiple of 256) and it runs on the direct-load kernel (C a multiple of 64,
-// C/r of 96); otherwise a separate pass over xc does.
-constexpr int kGnTileRows = 256;
+// The bf16 conv computes the GroupNorm partial statistics in its epilogue when its row tiles never
+// straddle two samples (H*W a multiple of the tile height) and it runs on the direct-load kernel (C a
+// multiple of 64, C/r of 96); otherwise a separate pass over xc does. Tiles are 256 rows, or 128 where
+// 256-row tiles (x C/r / 96 column tiles) would fill fewer than half of an MI355X's 256 CUs.
+int gn_tile_rows(const Geometry& g) {
+  const long tiles256 = (long)(g.M / 256) * (g.Cr / 96);
+  return tiles256 < 128 && g.N % 128 == 0 ? 128 : 256;
+}
 bool gn_in_conv(const Geometry& g) {
-  return g.es == 2 && g.N % kGnTileRows == 0 && g.C % 64 == 0 && g.Cr % 96 == 0 &&
+  return g.es == 2 && g.N % gn_tile_rows(g) == 0 && g.C % 64 == 0 && g.Cr % 96 == 0 &&
          (size_t)g.M * g.C * 2 < 0x80000000ull && (size_t)g.Cr * 9 * g.C * 2 < 0x80000000ull;
 }
 size_t gn_part_bytes(const Geometry& g) {
   const size_t sep = (size_t)g.B * g.gn_chunks * g.G * 2 * 4;
-  const size_t fused = gn_in_conv(g) ? (size_t)g.M / kGnTileRows * g.Cr * 2 * 4 : 0;
+  const size_t fused = gn_in_conv(g) ? (size_t)g.M / gn_tile_rows(g) * g.Cr * 2 * 4 : 0;
   return sep > fused ? sep : fused;
 }
 
@@ -297,7 +301,7 @@ edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const
                           static_cast<const bf16*>(w_cf2), static_cast<const bf16*>(b_cf2), wcat, bcat, g.C, g.Cr};
     }
     if (gn_in_conv(g)) {
-      a.gnp = gn_part; a.gn_rows = kGnTileRows;
+      a.gnp = gn_part; a.gn_rows = gn_tile_rows(g);
       EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS_GN, s));
     } else {
       EDIT_LAUNCH(launch_gemm<T>(a, A_CONV3, E_BIAS, s));
@@ -307,7 +311,7 @@ edit_status_t convfusion(const Geometry& g, const T* x, const void* w_cf1, const
     // GroupNorm statistics -> per-channel scale / shift; act = LeakyReLU(GN(xc))
     EDIT_LAUNCH(mk.mark(EDIT_STEP_GN_STATS));
     if (gn_in_conv(g)) {
-      EDIT_LAUNCH(launch_groupnorm_finalize_channels<T>(gn_part, g.B, g.N, g.Cr, g.G, kGnTileRows,
+      EDIT_LAUNCH(launch_groupnorm_finalize_channels<T>(gn_part, g.B, g.N, g.Cr, g.G, gn_tile_rows(g),
                                                         static_cast<const T*>(gamma), static_cast<const T*>(beta),
                                                         1e-5f, gn_stat, gn_scale, gn_shift, s));
     } else {

@@ -640,8 +640,11 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
     if (a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin) return hipErrorNotSupported;
     if (em == E_RES) return n96 ? launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_RES>(a, s) : hipErrorNotSupported;
     if (em == E_BIAS_GN) {
-      // every 256-row tile full (its rows are one sample's when H*W is a multiple of 256)
-      if (!n96 || a.M % 256 != 0 || a.gn_rows != 256 || a.gnp == nullptr) return hipErrorNotSupported;
+      // every tile full and within one sample (H*W a multiple of the tile height gn_rows); 128-row tiles
+      // run two stages, two blocks per CU
+      if (!n96 || a.gnp == nullptr || (a.gn_rows != 256 && a.gn_rows != 128) || a.M % a.gn_rows != 0)
+        return hipErrorNotSupported;
+      if (a.gn_rows == 128) return launch_dma_tiles<128, 96, 4, 1, A_CONV3, E_BIAS_GN, 2>(a, s);
       return launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_BIAS_GN>(a, s);
     }
 #if EDIT_CONV_TILE == 1
