@@ -40,8 +40,11 @@ int kv_state_dk(int d) { return 32 * ((d + 31) / 32); }
 // and each thread writes four tokens of a channel as one LDS word.
 // partial[b][h][chunk][16*DR][16*DT] (fp32).
 // ---------------------------------------------------------------------------
-template <typename T> struct KvSlab { static constexpr int n = 256; };
-template <> struct KvSlab<float> { static constexpr int n = 64; };
+// Tokens staged per pass: a whole 256-token chunk in bf16 (84 KB of LDS at
+// d = 72, one block per CU), half of it where a launch has several rounds
+// of blocks (three blocks per CU then overlap one another's loads).
+template <typename T, bool HALF> struct KvSlab { static constexpr int n = HALF ? 128 : 256; };
+template <bool HALF> struct KvSlab<float, HALF> { static constexpr int n = 64; };
 
 // Column (token) position of element (row, col) of a staged channel-major
 // tile: 8-element chunks are XOR-swizzled by row / 8, so that the transposed
@@ -63,7 +66,7 @@ __device__ __forceinline__ void store_quad(float* dst, float a, float b, float c
   *reinterpret_cast<f32x4*>(dst) = v;
 }
 
-template <typename T, int DC>
+template <typename T, int DC, bool HALF>
 __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
                                                                int ld, int Nc, int heads, int nchunks,
                                                                const float* __restrict__ wrow,
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   constexpr int d = 8 * DC;
   constexpr int DT = (d + 15) / 16, DR = (d + 16) / 16;
-  constexpr int SLAB = KvSlab<T>::n;       // tokens staged per pass
+  constexpr int SLAB = KvSlab<T, HALF>::n;   // tokens staged per pass
   constexpr int PITCH = SLAB + 8;          // elements; rows stay 16-byte aligned
   constexpr int NT = DR * DT;
   constexpr int TPW = (NT + 3) / 4;
@@ -230,11 +233,17 @@ hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int 
   const int DT = (d + 15) / 16, DR = (d + 16) / 16;
   if ((long long)nchunks * heads * B >= (1LL << 31)) return hipErrorInvalidValue;
   dim3 grid(nchunks * heads * B);
+  // more blocks than one round on an MI355X (256 CUs): half slabs
+  const bool half = (long long)nchunks * heads * B > 256;
   switch (d / 8) {
 #define EDIT_KV_CASE(DCV)                                                                              \
   case DCV:                                                                                            \
-    hipLaunchKernelGGL((kv_state_partial_kernel<T, DCV>), grid, dim3(256), 0, s, kc, vc, ld, Nc, heads, \
-                       nchunks, wrow, partial);                                                        \
+    if (half)                                                                                          \
+      hipLaunchKernelGGL((kv_state_partial_kernel<T, DCV, true>), grid, dim3(256), 0, s, kc, vc, ld, Nc, \
+                         heads, nchunks, wrow, partial);                                               \
+    else                                                                                               \
+      hipLaunchKernelGGL((kv_state_partial_kernel<T, DCV, false>), grid, dim3(256), 0, s, kc, vc, ld, Nc, \
+                         heads, nchunks, wrow, partial);                                               \
     break;
     EDIT_KV_CASE(1) EDIT_KV_CASE(2) EDIT_KV_CASE(3) EDIT_KV_CASE(4) EDIT_KV_CASE(5) EDIT_KV_CASE(6)
     EDIT_KV_CASE(7) EDIT_KV_CASE(8) EDIT_KV_CASE(9) EDIT_KV_CASE(10) EDIT_KV_CASE(11) EDIT_KV_CASE(12)
