@@ -541,21 +541,33 @@ __global__ __launch_bounds__(256) void dw_bwd_input_kernel(const T* __restrict__
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  // yy = y + 1 - ky must be even: ky in {0, 2} for odd y, {1} for even y
+  // (likewise kx). The up to four taps' loads are all issued (at clamped
+  // addresses) before any is used; a tap that does not reach an output
+  // pixel adds nothing. Taps are still added in (ky, kx) order.
+  const int kys[2] = {(y & 1) ? 0 : 1, 2}, kxs[2] = {(x & 1) ? 0 : 1, 2};
+  float g[2][2][8], wv[2][2][8];
+  bool live[2][2];
 #pragma unroll
-  for (int ky = 0; ky < 3; ++ky) {
-    const int yy = y + 1 - ky;                 // = 2 y'
-    if (yy < 0 || (yy & 1) || (yy >> 1) >= Hc) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int kx = 0; kx < 3; ++kx) {
-      const int xx = x + 1 - kx;
-      if (xx < 0 || (xx & 1) || (xx >> 1) >= Wc) continue;
-      float g[8], wv[8];
-      load8(dout + (((size_t)b * Hc + (yy >> 1)) * Wc + (xx >> 1)) * 2 * C + ch2, g);
-      load8(w + (ky * 3 + kx) * C + ch, wv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += g[i] * wv[i];
+    for (int j = 0; j < 2; ++j) {
+      const int ky = kys[i], kx = kxs[j];
+      const int yy = y + 1 - ky, xx = x + 1 - kx;
+      live[i][j] = (i == 0 || (y & 1)) && (j == 0 || (x & 1)) && yy >= 0 && (yy >> 1) < Hc && xx >= 0 &&
+                   (xx >> 1) < Wc;
+      const int yc = min(max(yy >> 1, 0), Hc - 1), xc = min(max(xx >> 1, 0), Wc - 1);
+      load8(dout + (((size_t)b * Hc + yc) * Wc + xc) * 2 * C + ch2, g[i][j]);
+      load8(w + (ky * 3 + kx) * C + ch, wv[i][j]);
     }
-  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (live[i][j]) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += g[i][j][k] * wv[i][j][k];
+      }
   store8(din + (size_t)pix * 2 * C + ch2, acc);
 }
 
@@ -597,22 +609,23 @@ __global__ __launch_bounds__(256) void dw_bwd_weight_partial_kernel(const T* __r
   if (active) {
     for (int p = p0 + pl; p < min(Pc, p0 + kDwPix); p += 8) {
       const int xo = p % Wc, yo = (p / Wc) % Hc, b = p / (Wc * Hc);
-      float g[8];
+      // the output gradient and all nine taps' inputs requested (clamped
+      // in-image addresses) before any is used; taps outside add nothing
+      float g[8], v[9][8];
       load8(dout + (size_t)p * 2 * C + ch2, g);
+#pragma unroll
+      for (int t = 0; t < 9; ++t) {
+        const int yc = min(max(2 * yo + t / 3 - 1, 0), H - 1), xc = min(max(2 * xo + t % 3 - 1, 0), W - 1);
+        load8(in + (((size_t)b * H + yc) * W + xc) * 2 * C + ch2, v[t]);
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[9][i] += g[i];
 #pragma unroll
-      for (int ky = 0; ky < 3; ++ky) {
-        const int yy = 2 * yo + ky - 1;
-        if (yy < 0 || yy >= H) continue;
+      for (int t = 0; t < 9; ++t) {
+        const int yy = 2 * yo + t / 3 - 1, xx = 2 * xo + t % 3 - 1;
+        if (yy >= 0 && yy < H && xx >= 0 && xx < W) {
 #pragma unroll
-        for (int kx = 0; kx < 3; ++kx) {
-          const int xx = 2 * xo + kx - 1;
-          if (xx < 0 || xx >= W) continue;
-          float v[8];
-          load8(in + (((size_t)b * H + yy) * W + xx) * 2 * C + ch2, v);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[ky * 3 + kx][i] += g[i] * v[i];
+          for (int i = 0; i < 8; ++i) acc[t][i] += g[i] * v[t][i];
         }
       }
     }
