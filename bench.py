@@ -146,6 +146,24 @@ STEP_BOUND = {"cf_conv3x3": "mfma", "gn_stats": "hbm", "cf_act": "hbm", "q_proj"
               "sc_dwconv": "hbm", "kv_state": "hbm", "linattn_apply": "hbm", "out_proj": "mfma"}
 
 
+def device_info():
+    """The device measured: name, architecture, CU count and peak clock from
+    the HIP runtime, and the peaks they imply (dense bf16 MFMA 4096 and fp32
+    vector 256 flop/clk/CU on CDNA4) beside the published ones the
+    rooflines use."""
+    p = torch.cuda.get_device_properties(0)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    khz = ctypes.c_int(0)
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) != 0:   # hipDeviceAttributeClockRate (kHz)
+        khz.value = 0
+    cus, ghz = p.multi_processor_count, khz.value / 1e6
+    return {"name": p.name, "arch": p.gcnArchName, "cus": cus, "max_clock_mhz": round(khz.value / 1e3),
+            "derived_peak_bf16_mfma_tflops": round(cus * 4096 * ghz / 1e3, 1),
+            "derived_peak_fp32_vector_tflops": round(cus * 256 * ghz / 1e3, 1),
+            "published_peak_bf16_mfma_tflops": PEAK_MFMA_TFLOPS["bf16"], "published_peak_hbm_gbs": PEAK_HBM_GBS}
+
+
 class HipEvents:
     """hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
 
@@ -287,7 +305,7 @@ def bench_backward(args, s, inp):
         "metric": "image tokens/sec per EDiT attention layer backward",
         "value": round(s.B * s.N * K / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms / K, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": s.dtype,
+        "vs_baseline": None, "dtype": s.dtype, "device": device_info(),
         "data": "synthetic (seeded N(0,1) activations and upstream gradient, N(0,0.02^2) weights)",
         "config": {"workload": wl, "B": s.B, "H": s.H, "W": s.W, "C": s.C, "heads": s.heads,
                    "head_dim": s.head_dim, "reduction": s.reduction, "gn_groups": s.gn_groups, "pass": "backward"},
@@ -516,6 +534,7 @@ def main():
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": s.dtype, "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        "device": device_info(),
         "config": {"workload": wl, "B": s.B, "H": s.H, "W": s.W, "C": s.C, "heads": s.heads,
                    "head_dim": s.head_dim, "reduction": s.reduction, "gn_groups": s.gn_groups,
                    **({"n_text": s.n_text} if hybrid else {}),
