@@ -151,6 +151,8 @@ def device_info():
     the HIP runtime, and the peaks they imply (dense bf16 MFMA 4096 and fp32
     vector 256 flop/clk/CU on CDNA4) beside the published ones the
     rooflines use."""
+    import torch
+
     p = torch.cuda.get_device_properties(0)
     hip = ctypes.CDLL("libamdhip64.so.7")
     hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
