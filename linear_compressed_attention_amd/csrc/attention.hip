@@ -415,6 +415,12 @@ hipError_t launch_linattn_apply(const T* q, int ldq, const T* st, const float* z
 // (keys 4g..4g+3 and 16+4g..16+4g+3 for lane group g), so P never leaves
 // registers.
 // ---------------------------------------------------------------------------
+// Position of key k in row `row` (a channel) of the transposed value slab:
+// groups of 4 keys are XOR-swizzled by row / 8, so that the staging writes
+// (8 channels of one key per thread, 8 rows apart across a wave's lanes) and
+// the fragment reads (4 keys of 16 rows) fall in distinct LDS banks.
+__device__ __forceinline__ int vt_key(int row, int k) { return ((((k >> 2) ^ (row >> 3)) & 7) << 2) | (k & 3); }
+
 template <typename T, int DT>
 __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   constexpr int KS = (DT + 1) / 2;
@@ -451,87 +457,124 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   const int Ntot = p.N1 + p.N2;
   __syncthreads();
 
-  for (int k0 = 0; k0 < Ntot; k0 += 32) {
-    for (int e = tid; e < 2 * 32 * dc; e += 256) {
-      const int which = e / (32 * dc);
-      const int r = e % (32 * dc);
-      const int key = r / dc, c8 = (r % dc) * 8;
-      const int kk = k0 + key;
-      float v[8];
-      if (kk < Ntot) {
+  // Key/value slabs of 32 keys. A thread's share of a slab (item e: K or V,
+  // key, 8-channel chunk) is loaded into registers PF slabs ahead, so that
+  // PF slabs' loads are in flight while one is staged in LDS and used; the
+  // loop is unrolled by PF so that every ring slot is a compile-time index.
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  constexpr int EPC = 16 / (int)sizeof(T);         // elements per 16 bytes
+  constexpr int NIT = (DT + 1) / 2;                // items per thread (2 x 32 keys x d/8 chunks <= 256 NIT)
+  constexpr int PF = sizeof(T) == 2 ? 4 : 2;       // slabs in flight
+  const int nitems = 2 * 32 * dc;
+  const int nslab = (Ntot + 31) / 32;
+  u32x4v raw[PF][NIT][8 / EPC];
+  auto issue = [&](u32x4v (&dst)[NIT][8 / EPC], int k0) {
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+      const int e = tid + 256 * u;
+      const int which = e / (32 * dc), r = e % (32 * dc);
+      const int kk = k0 + r / dc, c8 = (r % dc) * 8;
+      const u32x4v zero = {0u, 0u, 0u, 0u};
+      if (e < nitems && kk < Ntot) {
         const bool first = kk < p.N1;
         const T* base = first ? (which ? p.v1 : p.k1) : (which ? p.v2 : p.k2);
         const int ld = first ? p.ldkv1 : p.ldkv2;
         const int nseg = first ? p.N1 : p.N2;
         const int j = first ? kk : kk - p.N1;
-        load8(base + ((size_t)b * nseg + j) * ld + h * d + c8, v);
+        const T* src = base + ((size_t)b * nseg + j) * ld + h * d + c8;
+#pragma unroll
+        for (int w = 0; w < 8 / EPC; ++w) dst[u][w] = *reinterpret_cast<const u32x4v*>(src + w * EPC);
       } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-      }
-      if (which == 0) {
-        store8(Ks + key * KPITCH + c8, v);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) Vt[(c8 + i) * VPITCH + key] = from_f32<T>(v[i]);
+        for (int w = 0; w < 8 / EPC; ++w) dst[u][w] = zero;
       }
     }
-    __syncthreads();
+  };
+  auto stage = [&](const u32x4v (&src)[NIT][8 / EPC]) {
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+      const int e = tid + 256 * u;
+      if (e < nitems) {
+        const int which = e / (32 * dc), r = e % (32 * dc);
+        const int key = r / dc, c8 = (r % dc) * 8;
+        if (which == 0) {
+#pragma unroll
+          for (int w = 0; w < 8 / EPC; ++w) *reinterpret_cast<u32x4v*>(Ks + key * KPITCH + c8 + w * EPC) = src[u][w];
+        } else {
+          const T* v = reinterpret_cast<const T*>(&src[u][0]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) Vt[(c8 + i) * VPITCH + vt_key(c8 + i, key)] = v[i];
+        }
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < PF - 1; ++i)
+    if (i < nslab) issue(raw[i], 32 * i);
 
-    // Scores of keys 16*kt + 4g + r for query fr.
-    f32x4 sc[2];
+  for (int js0 = 0; js0 < nslab; js0 += PF) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      acc_zero(sc[kt]);
+    for (int u = 0; u < PF; ++u) {
+      const int js = js0 + u;
+      if (js >= nslab) break;
+      const int k0 = 32 * js;
+      if (js + PF - 1 < nslab) issue(raw[(u + PF - 1) % PF], 32 * (js + PF - 1));
+      stage(raw[u]);
+      __syncthreads();
+      // Scores of keys 16*kt + 4g + r for query fr.
+      f32x4 sc[2];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        FragT ak;
-        frag_load(ak, Ks + (kt * 16 + fr) * KPITCH + s * 32 + g * 8);
-        mma16(sc[kt], ak, bq[s]);
+      for (int kt = 0; kt < 2; ++kt) {
+        acc_zero(sc[kt]);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          FragT ak;
+          frag_load(ak, Ks + (kt * 16 + fr) * KPITCH + s * 32 + g * 8);
+          mma16(sc[kt], ak, bq[s]);
+        }
       }
-    }
-    float pv[8];
-    float tmax = -INFINITY;
+      float pv[8];
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = k0 + kt * 16 + g * 4 + r;
-        const float v = kk < Ntot ? sc[kt][r] * sl2 : -INFINITY;
-        pv[kt * 4 + r] = v;
-        tmax = fmaxf(tmax, v);
+        for (int r = 0; r < 4; ++r) {
+          const int kk = k0 + kt * 16 + g * 4 + r;
+          const float v = kk < Ntot ? sc[kt][r] * sl2 : -INFINITY;
+          pv[kt * 4 + r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun, tmax);
+      const float corr = exp2f(mrun - mnew);
+      mrun = mnew;
+      float psum = 0.0f;
+      float pf[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pf[i] = exp2f(pv[i] - mnew);
+        psum += pf[i];
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float mnew = fmaxf(mrun, tmax);
-    const float corr = exp2f(mrun - mnew);
-    mrun = mnew;
-    float psum = 0.0f;
-    float pf[8];
+      lrun = lrun * corr + psum;
+      FragT bp;
+      frag_from_f32(bp, pf);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pf[i] = exp2f(pv[i] - mnew);
-      psum += pf[i];
-    }
-    lrun = lrun * corr + psum;
-    FragT bp;
-    frag_from_f32(bp, pf);
+      for (int tn = 0; tn < DT; ++tn) {
 #pragma unroll
-    for (int tn = 0; tn < DT; ++tn) {
+        for (int r = 0; r < 4; ++r) acc[tn][r] *= corr;
+        const int row = tn * 16 + fr;
+        const T* vrow = Vt + row * VPITCH;
+        FragT av;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[tn][r] *= corr;
-      const T* vrow = Vt + (tn * 16 + fr) * VPITCH;
-      float vv[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vv[i] = to_f32(vrow[g * 4 + i]);
-        vv[4 + i] = to_f32(vrow[16 + g * 4 + i]);
+        for (int i = 0; i < 4; ++i) {
+          av[i] = vrow[vt_key(row, g * 4) + i];
+          av[4 + i] = vrow[vt_key(row, 16 + g * 4) + i];
+        }
+        mma16(acc[tn], av, bp);
       }
-      FragT av;
-      frag_from_f32(av, vv);
-      mma16(acc[tn], av, bp);
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   lrun += __shfl_xor(lrun, 16, 64);
