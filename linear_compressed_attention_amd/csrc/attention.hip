@@ -468,14 +468,25 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   const int nitems = 2 * 32 * dc;
   const int nslab = (Ntot + 31) / 32;
   u32x4v raw[PF][NIT][8 / EPC];
+  // A thread's items, the same in every slab: K or V, key within the slab,
+  // channel chunk (the divisions by d / 8 done once).
+  int it_key[NIT], it_c8[NIT];
+  bool it_v[NIT], it_ok[NIT];
+#pragma unroll
+  for (int u = 0; u < NIT; ++u) {
+    const int e = tid + 256 * u, r = e % (32 * dc);
+    it_ok[u] = e < nitems;
+    it_v[u] = e >= 32 * dc;
+    it_key[u] = r / dc;
+    it_c8[u] = (r % dc) * 8;
+  }
   auto issue = [&](u32x4v (&dst)[NIT][8 / EPC], int k0) {
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
-      const int e = tid + 256 * u;
-      const int which = e / (32 * dc), r = e % (32 * dc);
-      const int kk = k0 + r / dc, c8 = (r % dc) * 8;
+      const bool which = it_v[u];
+      const int kk = k0 + it_key[u], c8 = it_c8[u];
       const u32x4v zero = {0u, 0u, 0u, 0u};
-      if (e < nitems && kk < Ntot) {
+      if (it_ok[u] && kk < Ntot) {
         const bool first = kk < p.N1;
         const T* base = first ? (which ? p.v1 : p.k1) : (which ? p.v2 : p.k2);
         const int ld = first ? p.ldkv1 : p.ldkv2;
@@ -493,11 +504,9 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   auto stage = [&](const u32x4v (&src)[NIT][8 / EPC]) {
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
-      const int e = tid + 256 * u;
-      if (e < nitems) {
-        const int which = e / (32 * dc), r = e % (32 * dc);
-        const int key = r / dc, c8 = (r % dc) * 8;
-        if (which == 0) {
+      if (it_ok[u]) {
+        const int key = it_key[u], c8 = it_c8[u];
+        if (!it_v[u]) {
 #pragma unroll
           for (int w = 0; w < 8 / EPC; ++w) *reinterpret_cast<u32x4v*>(Ks + key * KPITCH + c8 + w * EPC) = src[u][w];
         } else {
