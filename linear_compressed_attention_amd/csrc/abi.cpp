@@ -62,7 +62,7 @@ struct Geometry {
 struct Layout {
   size_t xc, gn_part, gn_stat, gn_scale, gn_shift, cf_act, q_fold_w, q_fold_b, q, kv0, kc, vc, kv_part, S, z, st,
       zp, y;
-  size_t qkv_t, y_img, y_txt, lin_den;
+  size_t qkv_t, y_img, y_txt, lin_den, sdpa_part;
   size_t xc_k, gn_part_k, gn_stat_k, gn_scale_k, gn_shift_k, cf_act_k, k_fold_w, k_fold_b;   // key ConvFusion branch
   size_t total;
 };
@@ -179,6 +179,10 @@ Layout make_layout(const Geometry& g) {
     L.y_img = take(M * g.C * es);
     L.y_txt = take((size_t)g.B * g.nt * g.C * es);
     L.lin_den = take((size_t)g.B * g.N * g.heads * 4);
+    // the softmax blocks' key-split partials (image rows, then text rows, one buffer)
+    const size_t pi = (size_t)edit::sdpa_splits(g.N, g.nt, g.heads, g.B) * g.B * g.heads * g.N * (g.d + 2) * 4;
+    const size_t pt = (size_t)edit::sdpa_splits(g.nt, g.Nc + g.nt, g.heads, g.B) * g.B * g.heads * g.nt * (g.d + 2) * 4;
+    L.sdpa_part = take(pi > pt ? pi : pt);
   }
   L.total = off;
   return L;
@@ -555,6 +559,8 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   sa.B = g.B; sa.heads = g.heads; sa.d = g.d;
   sa.out = P(L.y_img); sa.ldo = C;
   sa.blend_src = P(L.y); sa.ldbs = C; sa.alpha = eta; sa.beta = 1.0f - eta; sa.lin_den = lin_den;
+  sa.splits = sdpa_splits(g.N, g.nt, g.heads, g.B);
+  sa.part = reinterpret_cast<float*>(wsb + L.sdpa_part);
   EDIT_LAUNCH(launch_sdpa<T>(sa, s));
   // Text rows: softmax over [K'_I ; K_T] with values [V'_I ; V_T].
   SdpaArgs<T> ta{};
@@ -564,6 +570,8 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   ta.B = g.B; ta.heads = g.heads; ta.d = g.d;
   ta.out = P(L.y_txt); ta.ldo = C;
   ta.blend_src = nullptr; ta.ldbs = 0; ta.alpha = 0.0f; ta.beta = 1.0f; ta.lin_den = nullptr;
+  ta.splits = sdpa_splits(g.nt, g.Nc + g.nt, g.heads, g.B);
+  ta.part = reinterpret_cast<float*>(wsb + L.sdpa_part);
   EDIT_LAUNCH(launch_sdpa<T>(ta, s));
 
   st = out_linear<T>(g.M, C, w->w_o, w->b_o, P(L.y_img), static_cast<T*>(y_img), s);

@@ -12,6 +12,7 @@
 // All three use the 16x16x32 matrix-core step of common.hpp. Head dimension d
 // (a multiple of 8, at most 128) is padded to whole 16-row tiles and 32-deep
 // K steps with zeros; DT = ceil(d / 16) is a template parameter.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -439,7 +440,9 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   for (int i = tid; i < 32 * KPITCH; i += 256) Ks[i] = from_f32<T>(0.0f);
   for (int i = tid; i < 16 * DT * VPITCH; i += 256) Vt[i] = from_f32<T>(0.0f);
 
-  const int qi = blockIdx.x * 64 + wave * 16 + fr;
+  // blockIdx.x = split * query blocks + query block; the split takes slabs [jlo, jhi).
+  const int nqb = (p.Nq + 63) / 64, sp = (int)blockIdx.x / nqb, qb = (int)blockIdx.x % nqb;
+  const int qi = qb * 64 + wave * 16 + fr;
   const bool qv = qi < p.Nq;
   const T* qrow = p.q + ((size_t)b * p.Nq + (qv ? qi : 0)) * p.ldq + h * d;
   FragT bq[KS];
@@ -466,7 +469,8 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   constexpr int NIT = (DT + 1) / 2;                // items per thread (2 x 32 keys x d/8 chunks <= 256 NIT)
   constexpr int PF = sizeof(T) == 2 ? 4 : 2;       // slabs in flight
   const int nitems = 2 * 32 * dc;
-  const int nslab = (Ntot + 31) / 32;
+  const int nslab_all = (Ntot + 31) / 32, spl = (nslab_all + p.splits - 1) / p.splits;
+  const int jlo = sp * spl, nslab = max(0, min(nslab_all, jlo + spl) - jlo);
   u32x4v raw[PF][NIT][8 / EPC];
   // A thread's items, the same in every slab: K or V, key within the slab,
   // channel chunk (the divisions by d / 8 done once).
@@ -519,15 +523,15 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   };
 #pragma unroll
   for (int i = 0; i < PF - 1; ++i)
-    if (i < nslab) issue(raw[i], 32 * i);
+    if (i < nslab) issue(raw[i], 32 * (jlo + i));
 
   for (int js0 = 0; js0 < nslab; js0 += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int js = js0 + u;
       if (js >= nslab) break;
-      const int k0 = 32 * js;
-      if (js + PF - 1 < nslab) issue(raw[(u + PF - 1) % PF], 32 * (js + PF - 1));
+      const int k0 = 32 * (jlo + js);
+      if (js + PF - 1 < nslab) issue(raw[(u + PF - 1) % PF], 32 * (jlo + js + PF - 1));
       stage(raw[u]);
       __syncthreads();
       // Scores of keys 16*kt + 4g + r for query fr.
@@ -588,6 +592,25 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
 
   lrun += __shfl_xor(lrun, 16, 64);
   lrun += __shfl_xor(lrun, 32, 64);
+  if (p.splits > 1) {
+    // This split's partial: unnormalised output, running max (log2 units), running sum.
+    if (qv) {
+      float* prow = p.part + ((((size_t)sp * p.B + b) * p.heads + h) * p.Nq + qi) * (d + 2);
+#pragma unroll
+      for (int tn = 0; tn < DT; ++tn) {
+        const int n = tn * 16 + g * 4;
+        if (n < d) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) prow[n + r] = acc[tn][r];
+        }
+      }
+      if (g == 0) {
+        prow[d] = mrun;
+        prow[d + 1] = lrun;
+      }
+    }
+    return;
+  }
   const float inv = 1.0f / lrun;
   if (qv) {
     T* orow = p.out + ((size_t)b * p.Nq + qi) * p.ldo + h * d;
@@ -618,10 +641,62 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   }
 }
 
+// Merge of the key splits, one thread per output element: with M the largest
+// running max, the output is sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+// then the same blend as the one-pass kernel (the exact eta's softmax mass is
+// 2^M times that denominator).
 template <typename T>
-hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s) {
-  if (a.Nq <= 0) return hipSuccess;
-  dim3 grid((a.Nq + 63) / 64, a.heads, a.B), block(256);
+__global__ __launch_bounds__(256) void sdpa_combine_kernel(SdpaArgs<T> p) {
+  const int d = p.d;
+  const long long total = (long long)p.B * p.Nq * p.heads * d;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int n = (int)(idx % d);
+  long long r = idx / d;
+  const int h = (int)(r % p.heads);
+  r /= p.heads;
+  const int qi = (int)(r % p.Nq), b = (int)(r / p.Nq);
+  const size_t sstride = (size_t)p.B * p.heads * p.Nq * (d + 2);
+  const float* base = p.part + (((size_t)b * p.heads + h) * p.Nq + qi) * (d + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, base[s * sstride + d]);
+  float L = 0.0f, O = 0.0f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float* ps = base + s * sstride;
+    const float w = exp2f(ps[d] - M);
+    L += w * ps[d + 1];
+    O += w * ps[n];
+  }
+  float o = O / L;
+  if (p.blend_src) {
+    float alpha = p.alpha, beta = p.beta;
+    if (p.lin_den) {
+      const float lin = p.lin_den[((size_t)b * p.Nq + qi) * p.heads + h];
+      alpha = lin / (lin + exp2f(M) * L);
+      beta = 1.0f - alpha;
+    }
+    o = alpha * to_f32(p.blend_src[((size_t)b * p.Nq + qi) * p.ldbs + h * d + n]) + beta * o;
+  }
+  p.out[((size_t)b * p.Nq + qi) * p.ldo + h * d + n] = from_f32<T>(o);
+}
+
+int sdpa_splits(int Nq, int Nkeys, int heads, int B) {
+  const long long base = (long long)((Nq + 63) / 64) * heads * B;
+  const int nslab = (Nkeys + 31) / 32;
+  if (base <= 0 || nslab <= 0) return 1;
+  long long s = (2048 + base - 1) / base;
+  s = std::min<long long>(s, (nslab + 3) / 4);
+  return (int)std::max<long long>(1, std::min<long long>(s, 32));
+}
+
+template <typename T>
+hipError_t launch_sdpa(const SdpaArgs<T>& a0, hipStream_t s) {
+  if (a0.Nq <= 0) return hipSuccess;
+  SdpaArgs<T> a = a0;
+  if (a.splits < 1 || a.part == nullptr) a.splits = 1;
+  const long long gx = (long long)((a.Nq + 63) / 64) * a.splits;
+  if (gx >= (1LL << 31)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)gx, a.heads, a.B), block(256);
   switch ((a.d + 15) / 16) {
 #define EDIT_SDPA_CASE(DTV) \
   case DTV: hipLaunchKernelGGL((sdpa_kernel<T, DTV>), grid, block, 0, s, a); break;
@@ -630,6 +705,10 @@ hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s) {
 #undef EDIT_SDPA_CASE
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  const long long total = (long long)a.B * a.Nq * a.heads * a.d;
+  hipLaunchKernelGGL((sdpa_combine_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

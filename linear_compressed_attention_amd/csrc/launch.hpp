@@ -185,8 +185,17 @@ struct SdpaArgs {
   // If set (with blend_src): alpha = L / (L + sum_t exp(s_t)) per query and
   // head, L = lin_den[b][query][head], beta = 1 - alpha.
   const float* lin_den;
+  // Key splits (1: one pass over all keys). With splits > 1 each block takes
+  // one split's slabs and writes fp32 partials [split][B][heads][Nq][d + 2]
+  // (unnormalised output, running max, running sum) to part, and a second
+  // kernel merges them in split order, then normalises and blends.
+  int splits;
+  float* part;
 };
 template <typename T>
 hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s);
+// Key splits for Nq queries over Nkeys keys: enough blocks for the chip
+// (about 2048) with at least four 32-key slabs per split, at most 32.
+int sdpa_splits(int Nq, int Nkeys, int heads, int B);
 
 }  // namespace edit

@@ -133,10 +133,20 @@ HYB = {
                              x_std=1.0),
     "bf16_d72": make_shape(B=1, H=8, W=8, C=288, heads=4, head_dim=72, reduction=4, gn_groups=4, dtype="bf16",
                            x_std=1.0),
+    # enough keys that both softmax launches split them across blocks (3 splits for the
+    # image rows over 300 text keys, 5 for the text rows over 256 + 300 keys) and merge
+    "bf16_many_keys": make_shape(B=1, H=32, W=32, C=256, heads=4, head_dim=64, reduction=4, gn_groups=4,
+                                 dtype="bf16", x_std=1.0),
+    "f32_many_keys": make_shape(B=1, H=32, W=32, C=128, heads=2, head_dim=64, reduction=4, gn_groups=4,
+                                dtype="f32", x_std=1.0),
+    # a wider fp32 hybrid: 4096 image tokens, 16 heads
+    "f32_many_queries": make_shape(B=1, H=64, W=64, C=1024, heads=16, head_dim=64, reduction=4, gn_groups=8,
+                                   dtype="f32", x_std=1.0),
 }
 
 
-@pytest.mark.parametrize("name,n_text", [("f32_small", 37), ("bf16_small", 77), ("bf16_d72", 5), ("f32_small", 1)])
+@pytest.mark.parametrize("name,n_text", [("f32_small", 37), ("bf16_small", 77), ("bf16_d72", 5), ("f32_small", 1),
+                                         ("bf16_many_keys", 300), ("f32_many_keys", 300), ("f32_many_queries", 40)])
 def test_hybrid_small(name, n_text):
     check_hybrid(HYB[name], n_text, seed=2)
 
@@ -146,7 +156,8 @@ def test_hybrid_sd35m_full_size():
     check_hybrid(s, s.n_text)
 
 
-@pytest.mark.parametrize("name,n_text", [("f32_small", 37), ("bf16_small", 77), ("bf16_d72", 5)])
+@pytest.mark.parametrize("name,n_text", [("f32_small", 37), ("bf16_small", 77), ("bf16_d72", 5),
+                                         ("bf16_many_keys", 300), ("f32_many_keys", 300)])
 def test_hybrid_exact_eta_small(name, n_text):
     check_hybrid(HYB[name], n_text, seed=6, exact=True)
 
