@@ -28,13 +28,18 @@
  *            (GroupNorm statistics, the K^T V state, softmax and every
  *            accumulator are fp32); EDIT_F32 is fp32 throughout.
  *   Memory   every pointer is a device pointer owned by the caller; the
- *            library allocates nothing and keeps no state between calls.
+ *            library allocates no memory and keeps no data between calls
+ *            (on first use on a device it creates one more stream and two
+ *            events there, kept for the life of the process).
  *            Tensor pointers must be 16-byte aligned, the workspace
  *            256-byte aligned. Outputs must not overlap inputs or the
  *            workspace.
  *   Stream   work is enqueued on hip_stream (a hipStream_t passed as
- *            void*; NULL = the default stream) and the call returns without
- *            waiting. Errors of the asynchronous work surface at the
+ *            void*; NULL = the default stream), which must belong to the
+ *            current HIP device, and the call returns without waiting. The
+ *            forwards fork part of their work onto the library's second
+ *            stream of that device and join it back to hip_stream before
+ *            returning. Errors of the asynchronous work surface at the
  *            caller's next synchronisation.
  *   Errors   arguments are checked before anything is enqueued; on any
  *            error nothing is launched and a status other than EDIT_OK is

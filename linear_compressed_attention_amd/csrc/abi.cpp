@@ -384,12 +384,20 @@ edit_status_t side_stream(SideStream** out) {
   if (e != hipSuccess || dev < 0 || dev >= 64) return fail(EDIT_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
   SideStream& ss = g_side[dev];
   if (!ss.s) {
-    // Both streams run on this device: a device-scope release is enough.
+    // Both streams run on this device: a device-scope release is enough. All
+    // three objects are created before any is kept, so a failure leaves the
+    // slot empty for the next call to retry.
     const unsigned fl = hipEventDisableTiming | hipEventReleaseToDevice;
-    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&ss.fork, fl)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&ss.join, fl)) != hipSuccess)
+    SideStream n;
+    if ((e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&n.fork, fl)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&n.join, fl)) != hipSuccess) {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.s) (void)hipStreamDestroy(n.s);
       return fail(EDIT_ERR_HIP, "creating the key/value stream failed: %s", hipGetErrorString(e));
+    }
+    ss = n;
   }
   *out = &ss;
   return EDIT_OK;
