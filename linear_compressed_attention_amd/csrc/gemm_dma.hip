@@ -429,48 +429,56 @@ __global__ __launch_bounds__(64 * WM * WN, (dma_blocks_per_cu<WM * WN, ST>())) v
       // rows for all its CJ*16 columns; the 32 lanes of a half-wave then add level by level (every
       // level a batch of independent steps: four row-local DPP moves, then the swap of 16-lane
       // rows), and the waves' sums meet in LDS. A fixed order throughout.
-      constexpr int NV = CJ * 16;
-      float sm[NV];
+      // Column blocks per reduction batch: all of them with a CU to itself; one at a time where two
+      // blocks share a CU (their register budget is halved), which changes no sum.
+      constexpr int CG = dma_blocks_per_cu<NW, ST>() == 2 ? 1 : CJ;
+      constexpr int NV = CG * 16;
       auto stored = [&](int t, int c, int k) -> float {
         return (float)(bf16)(acc[t][c][k] + (float)bv[c][k >> 2][k & 3]);
       };
 #pragma unroll
       for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-        for (int c = 0; c < CJ; ++c)
+        for (int c0 = 0; c0 < CJ; c0 += CG) {
+          float sm[NV];
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const float mu = pass ? gnmean[c * 32 + 8 * (k >> 2) + 4 * fh + (k & 3)] : 0.0f;
-            float v = 0.0f;
+          for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
-            for (int t = 0; t < TI; ++t) {
-              const float d = stored(t, c, k) - mu;
-              v += pass ? d * d : d;
+            for (int k = 0; k < 16; ++k) {
+              const int c = c0 + cc;
+              const float mu = pass ? gnmean[c * 32 + 8 * (k >> 2) + 4 * fh + (k & 3)] : 0.0f;
+              float v = 0.0f;
+#pragma unroll
+              for (int t = 0; t < TI; ++t) {
+                const float d = stored(t, c, k) - mu;
+                v += pass ? d * d : d;
+              }
+              sm[cc * 16 + k] = v;
             }
-            sm[c * 16 + k] = v;
-          }
-        // lane i += lane i^1, i^2 (quad perms), then 7-i within 8, then 15-i within 16 (mirrors)
+          // lane i += lane i^1, i^2 (quad perms), then 7-i within 8, then 15-i within 16 (mirrors)
 #define EDIT_DPP_LEVEL(CTRL)                                                                          \
-        _Pragma("unroll") for (int j = 0; j < NV; ++j)                                                 \
-          sm[j] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                              \
-              0, __builtin_bit_cast(int, sm[j]), (CTRL), 0xF, 0xF, false));
-        EDIT_DPP_LEVEL(0xB1)
-        EDIT_DPP_LEVEL(0x4E)
-        EDIT_DPP_LEVEL(0x141)
-        EDIT_DPP_LEVEL(0x140)
+          _Pragma("unroll") for (int j = 0; j < NV; ++j)                                               \
+            sm[j] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                            \
+                0, __builtin_bit_cast(int, sm[j]), (CTRL), 0xF, 0xF, false));
+          EDIT_DPP_LEVEL(0xB1)
+          EDIT_DPP_LEVEL(0x4E)
+          EDIT_DPP_LEVEL(0x141)
+          EDIT_DPP_LEVEL(0x140)
 #undef EDIT_DPP_LEVEL
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          // the other 16-lane row of this half-wave (rows 0 <-> 1, 2 <-> 3)
-          const uint32_t u = __builtin_bit_cast(uint32_t, sm[j]);
-          const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-          sm[j] += __builtin_bit_cast(float, (lane & 16) ? pr[0] : pr[1]);
-        }
-        if (fr == 0) {
+          for (int j = 0; j < NV; ++j) {
+            // the other 16-lane row of this half-wave (rows 0 <-> 1, 2 <-> 3)
+            const uint32_t u = __builtin_bit_cast(uint32_t, sm[j]);
+            const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+            sm[j] += __builtin_bit_cast(float, (lane & 16) ? pr[0] : pr[1]);
+          }
+          if (fr == 0) {
 #pragma unroll
-          for (int c = 0; c < CJ; ++c)
+            for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
-            for (int k = 0; k < 16; ++k) gnred[wm * BN + c * 32 + 8 * (k >> 2) + 4 * fh + (k & 3)] = sm[c * 16 + k];
+              for (int k = 0; k < 16; ++k)
+                gnred[wm * BN + (c0 + cc) * 32 + 8 * (k >> 2) + 4 * fh + (k & 3)] = sm[cc * 16 + k];
+          }
         }
         stage_barrier<63>();   // LDS only: the next tile's loads stay in flight
         if (tid < BN) {
