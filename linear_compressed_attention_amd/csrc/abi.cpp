@@ -597,7 +597,7 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
 // ---------------------------------------------------------------------------
 struct BwdLayout {
   size_t zeros, w_oT, wqT, wkvT, wflip, dy, g, cvec, dq_pre, dS, dz, st, zp, kvpart, dkv, dk0v0, dXq, dXkv;
-  size_t dact, dxc, doutT, yT, xT, dqT, actT, dkvT, dxcT9, skpart, dWx, dWa, dbq32, dwpart, gnpart, m12;
+  size_t dact, dxc, doutT, yT, xT, dqT, actT, dkvT, dxcT9, colsum, skpart, dWx, dWa, dbq32, dwpart, gnpart, m12;
   size_t total;
   int Mp, Crp;   // tokens rounded up to 8; C/r rounded up to 64 (the conv input gradient's channel stride)
 };
@@ -659,6 +659,8 @@ BwdLayout make_bwd_layout(const Geometry& g) {
   L.actT = take(Cr * Mp * es);
   L.dkvT = take(2 * C * Mp * es);
   L.dxcT9 = take(9 * Cr * Mp * es);
+  // the transposes' per-64-token-tile channel sums, for the bias gradients
+  L.colsum = take((2 * C > 9 * Cr ? 2 * C : 9 * Cr) * ((Mp + 63) / 64) * 4);
   size_t sk = 0;
   const int shapes[4][2] = {{g.C, g.C}, {2 * g.C, g.C}, {2 * g.C, g.Cr}, {9 * g.Cr, g.C}};
   for (auto& sh : shapes) {
@@ -690,6 +692,9 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   auto G = [](void* p) { return static_cast<T*>(p); };
   const int M = g.M, C = g.C, Cr = g.Cr, Mp = L.Mp, Crp = L.Crp;
   const T* zeros = P(L.zeros);
+  // bias gradients: the transposes of the output gradients also write per-tile channel sums (nrt tiles)
+  float* cs = Q(L.colsum);
+  const int nrt = (Mp + 63) / 64;
 
   // C[M'][N'] = A B^T (+ R), both operands K-contiguous.
   auto gemm = [&](int Mr, int Nr, int K, const T* A, int lda, const T* B, int ldb, T* out, int ldc,
@@ -744,8 +749,8 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
 
   // output Linear: dy = dout W_o, dW_o = dout^T y, db_o = sum dout
   if ((st = gemm(M, C, C, dout, C, P(L.w_oT), C, P(L.dy), C)) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_transpose<T>(dout, M, C, C, P(L.doutT), Mp, s, Mp));
-  EDIT_LAUNCH(launch_rowsum<T>(P(L.doutT), C, Mp, Mp, G(gr->b_o), s));
+  EDIT_LAUNCH(launch_transpose<T>(dout, M, C, C, P(L.doutT), Mp, s, Mp, 1, 0, 0, cs));
+  EDIT_LAUNCH(launch_colsum_finalize<T>(cs, C, nrt, G(gr->b_o), s));
   EDIT_LAUNCH(launch_transpose<T>(FP(F.y), M, C, C, P(L.yT), Mp, s, Mp));
   if ((st = wgrad(C, C, P(L.doutT), P(L.yT), G(gr->w_o), C)) != EDIT_OK) return st;
 
@@ -767,9 +772,9 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
                                       G(gr->dw_v), G(gr->db_v), s));
   // dXkv = [dk0 | dv0] [W_k; W_v] + dXq (the two input-gradient terms so far)
   if ((st = gemm(M, C, 2 * C, P(L.dk0v0), 2 * C, P(L.wkvT), 2 * C, P(L.dXkv), C, P(L.dXq))) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_transpose<T>(P(L.dk0v0), M, 2 * C, 2 * C, P(L.dkvT), Mp, s, Mp));
-  EDIT_LAUNCH(launch_rowsum<T>(P(L.dkvT), C, Mp, Mp, G(gr->b_k), s));
-  EDIT_LAUNCH(launch_rowsum<T>(P(L.dkvT) + (size_t)C * Mp, C, Mp, Mp, G(gr->b_v), s));
+  EDIT_LAUNCH(launch_transpose<T>(P(L.dk0v0), M, 2 * C, 2 * C, P(L.dkvT), Mp, s, Mp, 1, 0, 0, cs));
+  EDIT_LAUNCH(launch_colsum_finalize<T>(cs, C, nrt, G(gr->b_k), s));
+  EDIT_LAUNCH(launch_colsum_finalize<T>(cs + (size_t)C * nrt, C, nrt, G(gr->b_v), s));
   // dW_k and dW_v: one product over [dk0 | dv0]^T
   if ((st = wprod(2 * C, C, P(L.dkvT), P(L.xT))) != EDIT_OK) return st;
   if ((st = wsum(0, C, G(gr->w_k), C)) != EDIT_OK) return st;
@@ -780,9 +785,9 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   // and the restore's 1x1 conv: dxt = dq_pre W_q (= dXq), dW_cf2 = dxt^T act, db_cf2 = sum dxt.
   // dqT = [dq_pre | dxt]^T (one batched transpose over the two buffers).
   EDIT_LAUNCH(launch_transpose<T>(P(L.dq_pre), M, C, C, P(L.dqT), Mp, s, Mp, 2, (long)((L.dXq - L.dq_pre) / sizeof(T)),
-                                  (long)C * Mp));
-  EDIT_LAUNCH(launch_rowsum<T>(P(L.dqT), C, Mp, Mp, G(gr->b_q), s, Q(L.dbq32)));
-  EDIT_LAUNCH(launch_rowsum<T>(P(L.dqT) + (size_t)C * Mp, C, Mp, Mp, G(gr->b_cf2), s));
+                                  (long)C * Mp, cs));
+  EDIT_LAUNCH(launch_colsum_finalize<T>(cs, C, nrt, G(gr->b_q), s, Q(L.dbq32)));
+  EDIT_LAUNCH(launch_colsum_finalize<T>(cs + (size_t)C * nrt, C, nrt, G(gr->b_cf2), s));
   EDIT_LAUNCH(launch_transpose<T>(FP(F.cf_act), M, Cr, Cr, P(L.actT), Mp, s, Mp));
   if ((st = wgrad(C, C, P(L.dqT), P(L.xT), Q(L.dWx), C)) != EDIT_OK) return st;
   if ((st = wprod(2 * C, Cr, P(L.dqT), P(L.actT))) != EDIT_OK) return st;   // [dW'_act | dW_cf2]
@@ -805,8 +810,8 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   }
   // dW_cf1[co][t][ci] = sum_m dxc[m + off_t][co] x[m][ci]: the nine shifted copies of dxc stacked as
   // [9 Cr][tokens], one product whose row t * Cr + co lands at w_cf1 + co * 9C + t * C
-  EDIT_LAUNCH(launch_shift_transpose9<T>(P(L.dxc), g.B, g.H, g.W, Cr, Crp, P(L.dxcT9), Mp, s));
-  EDIT_LAUNCH(launch_rowsum<T>(P(L.dxcT9) + (size_t)4 * Cr * Mp, Cr, Mp, Mp, G(gr->b_cf1), s));   // centre tap
+  EDIT_LAUNCH(launch_shift_transpose9<T>(P(L.dxc), g.B, g.H, g.W, Cr, Crp, P(L.dxcT9), Mp, s, cs));
+  EDIT_LAUNCH(launch_colsum_finalize<T>(cs + (size_t)4 * Cr * nrt, Cr, nrt, G(gr->b_cf1), s));   // centre tap
   if ((st = wgrad(9 * Cr, C, P(L.dxcT9), P(L.xT), G(gr->w_cf1), 9 * C, Cr, C)) != EDIT_OK) return st;
   return EDIT_OK;
 }

@@ -23,11 +23,15 @@ namespace edit {
 // pixel of m - off lies inside its image and reads m through that tap, else
 // 0; off = (ky - 1) W + (kx - 1). Rows are tokens b*H*W + y*W + x. Output
 // columns rows .. rows_pad - 1 (the row padding of out) are written as zeros.
+// With colsum, each block also writes its tile's column sums over its 64 rows
+// (the transposed tensor's per-tile row sums, in a fixed order) to
+// colsum[(z * cols + c) * gridDim.y + blockIdx.y] (fp32): a bias gradient is
+// then a short sum over them instead of another pass over the tensor.
 // ---------------------------------------------------------------------------
 template <typename T, bool SHIFT>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int rows, int rows_pad, int cols,
                                                         int ldi, T* __restrict__ out, int ldo, int H, int W,
-                                                        long zin, long zout) {
+                                                        long zin, long zout, float* __restrict__ colsum) {
   // 64 x 64 tile; every global access is 16 bytes (EPC elements): a load
   // takes EPC consecutive columns of one row, a store EPC consecutive rows
   // of one column. cols, ldi, ldo and rows_pad are multiples of EPC.
@@ -62,6 +66,19 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
     for (int k = 0; k < EPC; ++k) tile[i][cv * EPC + k] = to_f32(e[k]);
   }
   __syncthreads();
+  if (colsum != nullptr) {
+    // wave q adds rows 16q .. 16q + 15 of every column; the four waves' sums meet in LDS
+    __shared__ float csum[4][64];
+    const int i = threadIdx.x & 63, q = threadIdx.x >> 6;
+    float a = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) a += tile[q * 16 + k][i];
+    csum[q][i] = a;
+    __syncthreads();
+    if (threadIdx.x < 64 && c0 + i < cols)
+      colsum[((long)blockIdx.z * cols + c0 + i) * gridDim.y + blockIdx.y] =
+          (csum[0][i] + csum[1][i]) + (csum[2][i] + csum[3][i]);
+  }
   for (int v = threadIdx.x; v < 64 * VPR; v += 256) {
     const int i = v / VPR, rv = v % VPR;          // column c0 + i, rows r0 + rv*EPC ..
     const int c = c0 + i, r = r0 + rv * EPC;
@@ -75,7 +92,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
 
 template <typename T>
 hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, int ldo, hipStream_t s,
-                            int rows_pad, int batch, long zin, long zout) {
+                            int rows_pad, int batch, long zin, long zout, float* colsum) {
   if (rows_pad < rows) rows_pad = rows;
   if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
   constexpr int EPC = 16 / (int)sizeof(T);
@@ -83,58 +100,48 @@ hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, in
     return hipErrorInvalidValue;
   dim3 grid((cols + 63) / 64, (rows_pad + 63) / 64, batch);
   hipLaunchKernelGGL((transpose_kernel<T, false>), grid, dim3(256), 0, s, in, rows, rows_pad, cols, ldi, out, ldo, 1,
-                     1, zin, zout);
+                     1, zin, zout, colsum);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, int ldi, T* out, int ldo,
-                                   hipStream_t s) {
+                                   hipStream_t s, float* colsum) {
   const int rows = B * H * W;
   if (rows <= 0 || cols <= 0) return hipSuccess;
   constexpr int EPC = 16 / (int)sizeof(T);
   if (cols % EPC || ldi % EPC || ldo % EPC || ldo < rows) return hipErrorInvalidValue;
   dim3 grid((cols + 63) / 64, (ldo + 63) / 64, 9);
   hipLaunchKernelGGL((transpose_kernel<T, true>), grid, dim3(256), 0, s, in, rows, ldo, cols, ldi, out, ldo, H, W,
-                     0L, (long)cols * ldo);
+                     0L, (long)cols * ldo, colsum);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Row sums (bias gradients): out[r] = sum_m in[r][m] over a transposed
-// [channels][tokens] buffer (the bias gradient is the sum over tokens of the
-// output gradient, whose transpose the weight gradient needs anyway). One
-// wave per row: lanes take 8 tokens at a time (16-byte loads), then a
-// butterfly; a fixed order. len and ld are multiples of 8 (the token padding
-// holds zeros).
+// Bias gradients from the transposes' per-tile sums: out[r] = sum over the n
+// row tiles of part[r * n + t], one wave per row, lanes strided over the
+// tiles, then a butterfly; a fixed order. out32 (optional) keeps the fp32 sum.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void rowsum_kernel(const T* __restrict__ in, int rows, int len, int ld,
-                                                     T* __restrict__ out, float* __restrict__ out32) {
+__global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __restrict__ part, int rows, int n,
+                                                              T* __restrict__ out, float* __restrict__ out32) {
   const int r = blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= rows) return;
-  const T* p = in + (size_t)r * ld;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
-  for (int i = lane * 8; i < len; i += 512) {
-    float v[8];
-    load8(p + i, v);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] += v[k];
-  }
-  float t = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-  t = wave_sum(t);
+  const float* p = part + (size_t)r * n;
+  float a = 0.0f;
+  for (int t = lane; t < n; t += 64) a += p[t];
+  a = wave_sum(a);
   if (lane == 0) {
-    out[r] = from_f32<T>(t);
-    if (out32) out32[r] = t;
+    out[r] = from_f32<T>(a);
+    if (out32) out32[r] = a;
   }
 }
 
 template <typename T>
-hipError_t launch_rowsum(const T* in, int rows, int len, int ld, T* out, hipStream_t s, float* out32) {
+hipError_t launch_colsum_finalize(const float* part, int rows, int n, T* out, hipStream_t s, float* out32) {
   if (rows <= 0) return hipSuccess;
-  if (len % 8 || ld % 8 || len > ld) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((rowsum_kernel<T>), dim3((rows + 3) / 4), dim3(256), 0, s, in, rows, len, ld, out, out32);
+  if (n <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((colsum_finalize_kernel<T>), dim3((rows + 3) / 4), dim3(256), 0, s, part, rows, n, out, out32);
   return hipGetLastError();
 }
 
@@ -961,9 +968,10 @@ hipError_t launch_small_nt(int M, int N, int K, const float* A, int lda, const T
 
 
 #define EDIT_INST(T)                                                                                               \
-  template hipError_t launch_transpose<T>(const T*, int, int, int, T*, int, hipStream_t, int, int, long, long);   \
-  template hipError_t launch_shift_transpose9<T>(const T*, int, int, int, int, int, T*, int, hipStream_t);         \
-  template hipError_t launch_rowsum<T>(const T*, int, int, int, T*, hipStream_t, float*);                         \
+  template hipError_t launch_transpose<T>(const T*, int, int, int, T*, int, hipStream_t, int, int, long, long,    \
+                                          float*);                                                               \
+  template hipError_t launch_shift_transpose9<T>(const T*, int, int, int, int, int, T*, int, hipStream_t, float*); \
+  template hipError_t launch_colsum_finalize<T>(const float*, int, int, T*, hipStream_t, float*);                 \
   template hipError_t launch_zero<T>(T*, long, hipStream_t);                                                       \
   template hipError_t launch_splitk_reduce<T>(const float*, int, long long, int, int, T*, int, hipStream_t, int,  \
                                               int);                                                               \

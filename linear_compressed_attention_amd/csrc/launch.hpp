@@ -117,19 +117,22 @@ int kv_state_chunks(int Nc);
 
 // ---- backward (backward.hip) ----
 // out[c][r] = in[r][c] (row strides ldi, ldo), for z < batch at in + z * zin, out + z * zout.
-// Output columns rows .. rows_pad - 1 are written as zeros.
+// Output columns rows .. rows_pad - 1 are written as zeros. colsum (optional,
+// fp32): per 64-row tile t = 0 .. ceil(rows_pad / 64) - 1, the sum of that
+// tile's rows of in, at colsum[(z * cols + c) * tiles + t].
 template <typename T>
 hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, int ldo, hipStream_t s,
-                            int rows_pad = 0, int batch = 1, long zin = 0, long zout = 0);
+                            int rows_pad = 0, int batch = 1, long zin = 0, long zout = 0, float* colsum = nullptr);
 // For every tap t = 3 ky + kx of the 3x3 conv: out[t][c][m'] = in[m' - off][c],
 // zero where that tap does not connect the two pixels (and in the padding up
-// to ldo); in is [B*H*W][ldi], out [9][cols][ldo].
+// to ldo); in is [B*H*W][ldi], out [9][cols][ldo]. colsum as for launch_transpose
+// (tap t as z, ceil(ldo / 64) tiles).
 template <typename T>
 hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, int ldi, T* out, int ldo,
-                                   hipStream_t s);
-// out[r] = sum_m in[r][m] for m < len (a transposed [channels][tokens] buffer), fixed order; out32 optional.
+                                   hipStream_t s, float* colsum = nullptr);
+// out[r] = sum_t part[r * n + t] for t < n (the per-tile sums a transpose wrote), fixed order; out32 optional.
 template <typename T>
-hipError_t launch_rowsum(const T* in, int rows, int len, int ld, T* out, hipStream_t s, float* out32 = nullptr);
+hipError_t launch_colsum_finalize(const float* part, int rows, int n, T* out, hipStream_t s, float* out32 = nullptr);
 template <typename T>
 hipError_t launch_zero(T* p, long n, hipStream_t s);
 // out[(r % rpg) * ldo + (r / rpg) * gstride + c] = sum_s part[s * stride + r * cols + c] (rpg 0: rows).
