@@ -728,6 +728,12 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
                                      ldo, s, rpg, gstride));
     return EDIT_OK;
   };
+  // rows 0 .. n1 - 1 of the product to out1, rows n1 .. n - 1 to out2 (one launch)
+  auto wsum2 = [&](int n, int n1, T* out1, T* out2, int ldo) -> edit_status_t {
+    EDIT_LAUNCH(launch_splitk_reduce(Q(L.skpart), wS, (long long)wrows * wcols, n, wcols, out1, ldo, s, 0, 0, out2,
+                                     n1));
+    return EDIT_OK;
+  };
   auto wgrad = [&](int rows, int cols, const T* At, const T* Bt, auto* out, int ldo, int rpg = 0,
                    int gstride = 0) -> edit_status_t {
     edit_status_t e = wprod(rows, cols, At, Bt);
@@ -773,12 +779,10 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   // dXkv = [dk0 | dv0] [W_k; W_v] + dXq (the two input-gradient terms so far)
   if ((st = gemm(M, C, 2 * C, P(L.dk0v0), 2 * C, P(L.wkvT), 2 * C, P(L.dXkv), C, P(L.dXq))) != EDIT_OK) return st;
   EDIT_LAUNCH(launch_transpose<T>(P(L.dk0v0), M, 2 * C, 2 * C, P(L.dkvT), Mp, s, Mp, 1, 0, 0, cs));
-  EDIT_LAUNCH(launch_colsum_finalize<T>(cs, C, nrt, G(gr->b_k), s));
-  EDIT_LAUNCH(launch_colsum_finalize<T>(cs + (size_t)C * nrt, C, nrt, G(gr->b_v), s));
+  EDIT_LAUNCH(launch_colsum_finalize<T>(cs, 2 * C, nrt, G(gr->b_k), s, nullptr, G(gr->b_v), C));
   // dW_k and dW_v: one product over [dk0 | dv0]^T
   if ((st = wprod(2 * C, C, P(L.dkvT), P(L.xT))) != EDIT_OK) return st;
-  if ((st = wsum(0, C, G(gr->w_k), C)) != EDIT_OK) return st;
-  if ((st = wsum(C, C, G(gr->w_v), C)) != EDIT_OK) return st;
+  if ((st = wsum2(2 * C, C, G(gr->w_k), G(gr->w_v), C)) != EDIT_OK) return st;
 
   // the query Linear's weights: dW' = dq_pre^T [x | act], then
   // dW_q = dW'_x + dW'_act W_cf2^T + db_q b_cf2^T, db_q = sum dq_pre
@@ -786,8 +790,7 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   // dqT = [dq_pre | dxt]^T (one batched transpose over the two buffers).
   EDIT_LAUNCH(launch_transpose<T>(P(L.dq_pre), M, C, C, P(L.dqT), Mp, s, Mp, 2, (long)((L.dXq - L.dq_pre) / sizeof(T)),
                                   (long)C * Mp, cs));
-  EDIT_LAUNCH(launch_colsum_finalize<T>(cs, C, nrt, G(gr->b_q), s, Q(L.dbq32)));
-  EDIT_LAUNCH(launch_colsum_finalize<T>(cs + (size_t)C * nrt, C, nrt, G(gr->b_cf2), s));
+  EDIT_LAUNCH(launch_colsum_finalize<T>(cs, 2 * C, nrt, G(gr->b_q), s, Q(L.dbq32), G(gr->b_cf2), C));
   EDIT_LAUNCH(launch_transpose<T>(FP(F.cf_act), M, Cr, Cr, P(L.actT), Mp, s, Mp));
   if ((st = wgrad(C, C, P(L.dqT), P(L.xT), Q(L.dWx), C)) != EDIT_OK) return st;
   if ((st = wprod(2 * C, Cr, P(L.dqT), P(L.actT))) != EDIT_OK) return st;   // [dW'_act | dW_cf2]

@@ -121,10 +121,12 @@ hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, i
 // Bias gradients from the transposes' per-tile sums: out[r] = sum over the n
 // row tiles of part[r * n + t], one wave per row, lanes strided over the
 // tiles, then a butterfly; a fixed order. out32 (optional) keeps the fp32 sum.
+// Rows from rsplit on go to out2 (row r - rsplit) and have no fp32 copy.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __restrict__ part, int rows, int n,
-                                                              T* __restrict__ out, float* __restrict__ out32) {
+                                                              T* __restrict__ out, float* __restrict__ out32,
+                                                              T* __restrict__ out2, int rsplit) {
   const int r = blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (r >= rows) return;
   const float* p = part + (size_t)r * n;
@@ -132,16 +134,23 @@ __global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* __res
   for (int t = lane; t < n; t += 64) a += p[t];
   a = wave_sum(a);
   if (lane == 0) {
-    out[r] = from_f32<T>(a);
-    if (out32) out32[r] = a;
+    if (r < rsplit) {
+      out[r] = from_f32<T>(a);
+      if (out32) out32[r] = a;
+    } else {
+      out2[r - rsplit] = from_f32<T>(a);
+    }
   }
 }
 
 template <typename T>
-hipError_t launch_colsum_finalize(const float* part, int rows, int n, T* out, hipStream_t s, float* out32) {
+hipError_t launch_colsum_finalize(const float* part, int rows, int n, T* out, hipStream_t s, float* out32, T* out2,
+                                  int rsplit) {
   if (rows <= 0) return hipSuccess;
   if (n <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((colsum_finalize_kernel<T>), dim3((rows + 3) / 4), dim3(256), 0, s, part, rows, n, out, out32);
+  if (out2 == nullptr || rsplit <= 0 || rsplit > rows) rsplit = rows;
+  hipLaunchKernelGGL((colsum_finalize_kernel<T>), dim3((rows + 3) / 4), dim3(256), 0, s, part, rows, n, out, out32,
+                     out2, rsplit);
   return hipGetLastError();
 }
 
@@ -168,25 +177,30 @@ hipError_t launch_zero(T* p, long n, hipStream_t s) {
 template <typename O>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S,
                                                             long long stride, int rows, int cols,
-                                                            O* __restrict__ out, int ldo, int rpg, int gstride) {
+                                                            O* __restrict__ out, int ldo, int rpg, int gstride,
+                                                            O* __restrict__ out2, int rsplit) {
   const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= (long long)rows * cols) return;
   const int r = (int)(i / cols), c = (int)(i - (long long)r * cols);
   f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
   for (int s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4*>(part + (size_t)s * stride + i);
   const float o[4] = {v[0], v[1], v[2], v[3]};
-  store4(out + (size_t)(r % rpg) * ldo + (size_t)(r / rpg) * gstride + c, o);
+  // rows from rsplit on go to the second output
+  O* const dst = r < rsplit ? out : out2;
+  const int rr = r < rsplit ? r : r - rsplit;
+  store4(dst + (size_t)(rr % rpg) * ldo + (size_t)(rr / rpg) * gstride + c, o);
 }
 
 template <typename O>
 hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int rows, int cols, O* out, int ldo,
-                                hipStream_t s, int rpg, int gstride) {
+                                hipStream_t s, int rpg, int gstride, O* out2, int rsplit) {
   const long long n = (long long)rows * cols;
   if (n <= 0) return hipSuccess;
-  if (rpg <= 0) rpg = rows;
+  if (out2 == nullptr || rsplit <= 0 || rsplit > rows) rsplit = rows;
+  if (rpg <= 0) rpg = rsplit;
   if (cols % 4 || ldo % 4 || gstride % 4 || stride % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL((splitk_reduce_kernel<O>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, part, S,
-                     stride, rows, cols, out, ldo, rpg, gstride);
+                     stride, rows, cols, out, ldo, rpg, gstride, out2, rsplit);
   return hipGetLastError();
 }
 
@@ -971,10 +985,10 @@ hipError_t launch_small_nt(int M, int N, int K, const float* A, int lda, const T
   template hipError_t launch_transpose<T>(const T*, int, int, int, T*, int, hipStream_t, int, int, long, long,    \
                                           float*);                                                               \
   template hipError_t launch_shift_transpose9<T>(const T*, int, int, int, int, int, T*, int, hipStream_t, float*); \
-  template hipError_t launch_colsum_finalize<T>(const float*, int, int, T*, hipStream_t, float*);                 \
+  template hipError_t launch_colsum_finalize<T>(const float*, int, int, T*, hipStream_t, float*, T*, int);        \
   template hipError_t launch_zero<T>(T*, long, hipStream_t);                                                       \
   template hipError_t launch_splitk_reduce<T>(const float*, int, long long, int, int, T*, int, hipStream_t, int,  \
-                                              int);                                                               \
+                                              int, T*, int);                                                      \
   template hipError_t launch_attn_bwd_q<T>(const T*, const T*, const float*, const float*, int, int, int, int,     \
                                            float, T*, float*, T*, hipStream_t);                                    \
   template hipError_t launch_kv_bwd<T>(const T*, const T*, const float*, const float*, int, int, int, int, T*,     \

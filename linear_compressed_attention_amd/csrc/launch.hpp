@@ -131,14 +131,17 @@ template <typename T>
 hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, int ldi, T* out, int ldo,
                                    hipStream_t s, float* colsum = nullptr);
 // out[r] = sum_t part[r * n + t] for t < n (the per-tile sums a transpose wrote), fixed order; out32 optional.
+// Rows from rsplit on (when out2 is given) go to out2[r - rsplit], without the fp32 copy.
 template <typename T>
-hipError_t launch_colsum_finalize(const float* part, int rows, int n, T* out, hipStream_t s, float* out32 = nullptr);
+hipError_t launch_colsum_finalize(const float* part, int rows, int n, T* out, hipStream_t s, float* out32 = nullptr,
+                                  T* out2 = nullptr, int rsplit = 0);
 template <typename T>
 hipError_t launch_zero(T* p, long n, hipStream_t s);
 // out[(r % rpg) * ldo + (r / rpg) * gstride + c] = sum_s part[s * stride + r * cols + c] (rpg 0: rows).
+// With out2, rows r >= rsplit go to out2 at row r - rsplit instead (rpg 0: rsplit).
 template <typename O>
 hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int rows, int cols, O* out, int ldo,
-                                hipStream_t s, int rpg = 0, int gstride = 0);
+                                hipStream_t s, int rpg = 0, int gstride = 0, O* out2 = nullptr, int rsplit = 0);
 // Linear-attention backward, query side: g = dy / den, c = -(dy . y) / den, dq_pre = (g S^T + c z) where q > 0.
 template <typename T>
 hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const float* z, int B, int N, int heads, int d,
