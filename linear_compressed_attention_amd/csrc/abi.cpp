@@ -745,8 +745,8 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   EDIT_LAUNCH(launch_zero<T>(P(L.zeros), 2L * C, s));
   EDIT_LAUNCH(launch_transpose<T>(W(w->w_o), C, C, C, P(L.w_oT), C, s));
   EDIT_LAUNCH(launch_transpose<T>(FP(F.q_fold_w), C, C + Cr, C + Cr, P(L.wqT), C, s));
-  EDIT_LAUNCH(launch_transpose<T>(W(w->w_k), C, C, C, P(L.wkvT), 2 * C, s));
-  EDIT_LAUNCH(launch_transpose<T>(W(w->w_v), C, C, C, P(L.wkvT) + C, 2 * C, s));
+  // W_k^T and W_v^T side by side, one launch (z = 1 reads W_v)
+  EDIT_LAUNCH(launch_transpose<T>(W(w->w_k), C, C, C, P(L.wkvT), 2 * C, s, 0, 2, 0, (long)C, nullptr, W(w->w_v)));
   // the 3x3 conv's input gradient is a 3x3 conv of dxc with the taps mirrored and the channel roles
   // swapped: wflip[ci][t * Cr + co] = w_cf1[co][8 - t][ci], one transpose per tap
   // (channel slots Cr .. Crp - 1 of every tap zero)
@@ -794,8 +794,9 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   EDIT_LAUNCH(launch_transpose<T>(FP(F.cf_act), M, Cr, Cr, P(L.actT), Mp, s, Mp));
   if ((st = wgrad(C, C, P(L.dqT), P(L.xT), Q(L.dWx), C)) != EDIT_OK) return st;
   if ((st = wprod(2 * C, Cr, P(L.dqT), P(L.actT))) != EDIT_OK) return st;   // [dW'_act | dW_cf2]
-  if ((st = wsum(0, C, Q(L.dWa), Cr)) != EDIT_OK) return st;
-  if ((st = wsum(C, C, G(gr->w_cf2), Cr)) != EDIT_OK) return st;
+  // dW'_act (fp32, rows 0 .. C - 1) and dW_cf2 (rows C .. 2C - 1), one launch
+  EDIT_LAUNCH(launch_splitk_reduce(Q(L.skpart), wS, (long long)wrows * wcols, 2 * C, wcols, Q(L.dWa), Cr, s, 0, 0,
+                                   G(gr->w_cf2), C));
   EDIT_LAUNCH((launch_small_nt<T, T>(C, C, Cr, Q(L.dWa), Cr, W(w->w_cf2), Cr, Q(L.dWx), C, G(gr->w_q), C, s,
                                      Q(L.dbq32), W(w->b_cf2))));
 

@@ -31,7 +31,8 @@ namespace edit {
 template <typename T, bool SHIFT>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int rows, int rows_pad, int cols,
                                                         int ldi, T* __restrict__ out, int ldo, int H, int W,
-                                                        long zin, long zout, float* __restrict__ colsum) {
+                                                        long zin, long zout, float* __restrict__ colsum,
+                                                        const T* __restrict__ in2) {
   // 64 x 64 tile; every global access is 16 bytes (EPC elements): a load
   // takes EPC consecutive columns of one row, a store EPC consecutive rows
   // of one column. cols, ldi, ldo and rows_pad are multiples of EPC.
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
   typedef uint32_t u32x4t __attribute__((ext_vector_type(4)));
   __shared__ float tile[64][65];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  in += (long)blockIdx.z * zin;
+  in = in2 != nullptr && blockIdx.z == 1 ? in2 : in + (long)blockIdx.z * zin;
   out += (long)blockIdx.z * zout;
   const int ky = SHIFT ? (int)blockIdx.z / 3 : 1, kx = SHIFT ? (int)blockIdx.z % 3 : 1;
   for (int v = threadIdx.x; v < 64 * VPR; v += 256) {
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
 
 template <typename T>
 hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, int ldo, hipStream_t s,
-                            int rows_pad, int batch, long zin, long zout, float* colsum) {
+                            int rows_pad, int batch, long zin, long zout, float* colsum, const T* in2) {
   if (rows_pad < rows) rows_pad = rows;
   if (rows <= 0 || cols <= 0 || batch <= 0) return hipSuccess;
   constexpr int EPC = 16 / (int)sizeof(T);
@@ -100,7 +101,7 @@ hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, in
     return hipErrorInvalidValue;
   dim3 grid((cols + 63) / 64, (rows_pad + 63) / 64, batch);
   hipLaunchKernelGGL((transpose_kernel<T, false>), grid, dim3(256), 0, s, in, rows, rows_pad, cols, ldi, out, ldo, 1,
-                     1, zin, zout, colsum);
+                     1, zin, zout, colsum, in2);
   return hipGetLastError();
 }
 
@@ -113,7 +114,7 @@ hipError_t launch_shift_transpose9(const T* in, int B, int H, int W, int cols, i
   if (cols % EPC || ldi % EPC || ldo % EPC || ldo < rows) return hipErrorInvalidValue;
   dim3 grid((cols + 63) / 64, (ldo + 63) / 64, 9);
   hipLaunchKernelGGL((transpose_kernel<T, true>), grid, dim3(256), 0, s, in, rows, ldo, cols, ldi, out, ldo, H, W,
-                     0L, (long)cols * ldo, colsum);
+                     0L, (long)cols * ldo, colsum, nullptr);
   return hipGetLastError();
 }
 
@@ -174,11 +175,11 @@ hipError_t launch_zero(T* p, long n, hipStream_t s) {
 // (the 3x3 conv's taps, each a [C/r][C] block) that interleave in the
 // output row. Four columns per thread.
 // ---------------------------------------------------------------------------
-template <typename O>
+template <typename O, typename O2>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S,
                                                             long long stride, int rows, int cols,
                                                             O* __restrict__ out, int ldo, int rpg, int gstride,
-                                                            O* __restrict__ out2, int rsplit) {
+                                                            O2* __restrict__ out2, int rsplit) {
   const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= (long long)rows * cols) return;
   const int r = (int)(i / cols), c = (int)(i - (long long)r * cols);
@@ -186,20 +187,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   for (int s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4*>(part + (size_t)s * stride + i);
   const float o[4] = {v[0], v[1], v[2], v[3]};
   // rows from rsplit on go to the second output
-  O* const dst = r < rsplit ? out : out2;
-  const int rr = r < rsplit ? r : r - rsplit;
-  store4(dst + (size_t)(rr % rpg) * ldo + (size_t)(rr / rpg) * gstride + c, o);
+  if (r < rsplit) store4(out + (size_t)(r % rpg) * ldo + (size_t)(r / rpg) * gstride + c, o);
+  else store4(out2 + (size_t)((r - rsplit) % rpg) * ldo + (size_t)((r - rsplit) / rpg) * gstride + c, o);
 }
 
-template <typename O>
+template <typename O, typename O2>
 hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int rows, int cols, O* out, int ldo,
-                                hipStream_t s, int rpg, int gstride, O* out2, int rsplit) {
+                                hipStream_t s, int rpg, int gstride, O2* out2, int rsplit) {
   const long long n = (long long)rows * cols;
   if (n <= 0) return hipSuccess;
   if (out2 == nullptr || rsplit <= 0 || rsplit > rows) rsplit = rows;
   if (rpg <= 0) rpg = rsplit;
   if (cols % 4 || ldo % 4 || gstride % 4 || stride % 4) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((splitk_reduce_kernel<O>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, part, S,
+  hipLaunchKernelGGL((splitk_reduce_kernel<O, O2>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, part, S,
                      stride, rows, cols, out, ldo, rpg, gstride, out2, rsplit);
   return hipGetLastError();
 }
@@ -981,14 +981,18 @@ hipError_t launch_small_nt(int M, int N, int K, const float* A, int lda, const T
 }
 
 
+// fp32 rows to one output, bf16 rows to the other (one launch for two weight gradients)
+template hipError_t launch_splitk_reduce<float, bf16>(const float*, int, long long, int, int, float*, int, hipStream_t,
+                                                      int, int, bf16*, int);
+
 #define EDIT_INST(T)                                                                                               \
   template hipError_t launch_transpose<T>(const T*, int, int, int, T*, int, hipStream_t, int, int, long, long,    \
-                                          float*);                                                               \
+                                          float*, const T*);                                                     \
   template hipError_t launch_shift_transpose9<T>(const T*, int, int, int, int, int, T*, int, hipStream_t, float*); \
   template hipError_t launch_colsum_finalize<T>(const float*, int, int, T*, hipStream_t, float*, T*, int);        \
   template hipError_t launch_zero<T>(T*, long, hipStream_t);                                                       \
-  template hipError_t launch_splitk_reduce<T>(const float*, int, long long, int, int, T*, int, hipStream_t, int,  \
-                                              int, T*, int);                                                      \
+  template hipError_t launch_splitk_reduce<T, T>(const float*, int, long long, int, int, T*, int, hipStream_t,   \
+                                                 int, int, T*, int);                                              \
   template hipError_t launch_attn_bwd_q<T>(const T*, const T*, const float*, const float*, int, int, int, int,     \
                                            float, T*, float*, T*, hipStream_t);                                    \
   template hipError_t launch_kv_bwd<T>(const T*, const T*, const float*, const float*, int, int, int, int, T*,     \

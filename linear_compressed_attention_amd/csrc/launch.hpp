@@ -119,10 +119,12 @@ int kv_state_chunks(int Nc);
 // out[c][r] = in[r][c] (row strides ldi, ldo), for z < batch at in + z * zin, out + z * zout.
 // Output columns rows .. rows_pad - 1 are written as zeros. colsum (optional,
 // fp32): per 64-row tile t = 0 .. ceil(rows_pad / 64) - 1, the sum of that
-// tile's rows of in, at colsum[(z * cols + c) * tiles + t].
+// tile's rows of in, at colsum[(z * cols + c) * tiles + t]. in2 (optional): the input of z = 1
+// instead of in + zin.
 template <typename T>
 hipError_t launch_transpose(const T* in, int rows, int cols, int ldi, T* out, int ldo, hipStream_t s,
-                            int rows_pad = 0, int batch = 1, long zin = 0, long zout = 0, float* colsum = nullptr);
+                            int rows_pad = 0, int batch = 1, long zin = 0, long zout = 0, float* colsum = nullptr,
+                            const T* in2 = nullptr);
 // For every tap t = 3 ky + kx of the 3x3 conv: out[t][c][m'] = in[m' - off][c],
 // zero where that tap does not connect the two pixels (and in the padding up
 // to ldo); in is [B*H*W][ldi], out [9][cols][ldo]. colsum as for launch_transpose
@@ -139,9 +141,9 @@ template <typename T>
 hipError_t launch_zero(T* p, long n, hipStream_t s);
 // out[(r % rpg) * ldo + (r / rpg) * gstride + c] = sum_s part[s * stride + r * cols + c] (rpg 0: rows).
 // With out2, rows r >= rsplit go to out2 at row r - rsplit instead (rpg 0: rsplit).
-template <typename O>
+template <typename O, typename O2 = O>
 hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int rows, int cols, O* out, int ldo,
-                                hipStream_t s, int rpg = 0, int gstride = 0, O* out2 = nullptr, int rsplit = 0);
+                                hipStream_t s, int rpg = 0, int gstride = 0, O2* out2 = nullptr, int rsplit = 0);
 // Linear-attention backward, query side: g = dy / den, c = -(dy . y) / den, dq_pre = (g S^T + c z) where q > 0.
 template <typename T>
 hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const float* z, int B, int N, int heads, int d,
