@@ -261,7 +261,7 @@ size_t edit_attn_backward_workspace_size(const edit_shape_t* shape);
 /* EDiT layer backward: the gradients of sum(dy * y) with respect to x and to
  * every parameter, y = edit_attn_forward(x, w). It is the chain rule through
  * the forward steps (the page trains the layer by distillation, section
- * "Distillation", which needs them): the output Linear, the linear-attention
+ * "训练策略" (training strategy), which needs them): the output Linear, the linear-attention
  * formula (dQ, dS, dz, then dK', dV' through S = sum K'^T V' and z = sum K'),
  * the depthwise stride-2 convs and their ReLU, the key / value Linears, and
  * ConvFusion (the query Linear with the 1x1 restore folded in, LeakyReLU,

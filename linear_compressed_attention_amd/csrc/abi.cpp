@@ -49,6 +49,15 @@ edit_status_t fail(edit_status_t st, const char* fmt, ...) {
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// The bits of an enum field as an int (the C ABI's enums are int-sized).
+template <typename E>
+int enum_int(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 struct Geometry {
   int B, H, W, C, heads, d, r, G, Cr, N, M, Hc, Wc, Nc, nt;
   int qmode, kvmode;   // edit_query_mode_t, edit_kv_mode_t (the layer itself: 0, 0)
@@ -81,7 +90,10 @@ edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
   if (Cr % s->gn_groups != 0)
     return fail(EDIT_ERR_ARG, "gn_groups %d does not divide C/r %d", s->gn_groups, Cr);
   if (!(s->eps >= 0.0f) || !std::isfinite(s->eps)) return fail(EDIT_ERR_ARG, "eps must be finite and >= 0");
-  if (s->dtype != EDIT_F32 && s->dtype != EDIT_BF16) return fail(EDIT_ERR_ARG, "unknown dtype %d", (int)s->dtype);
+  // A C caller may put any int in an enum field: read it as an int, since a C++ load of an enum
+  // value outside the enumerators' range is undefined.
+  const int dt = enum_int(s->dtype);
+  if (dt != EDIT_F32 && dt != EDIT_BF16) return fail(EDIT_ERR_ARG, "unknown dtype %d", dt);
   if (n_text < 0) return fail(EDIT_ERR_ARG, "n_text must be >= 0 (got %d)", n_text);
   if (s->C % 8 || Cr % 8 || s->head_dim % 8)
     return fail(EDIT_ERR_UNSUPPORTED, "C (%d), C/r (%d) and head_dim (%d) must be multiples of 8", s->C, Cr,
@@ -108,13 +120,14 @@ edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
 // The query / key-value processing of the ablation variants.
 edit_status_t apply_variant(const edit_variant_t* v, Geometry* g) {
   if (!v) return fail(EDIT_ERR_ARG, "variant is NULL");
-  if (v->query != EDIT_QUERY_CONVFUSION && v->query != EDIT_QUERY_LINEAR)
-    return fail(EDIT_ERR_ARG, "unknown query mode %d", (int)v->query);
-  if (v->kv != EDIT_KV_COMPRESSED && v->kv != EDIT_KV_FULL && v->kv != EDIT_KV_KEY_CONVFUSION)
-    return fail(EDIT_ERR_ARG, "unknown key/value mode %d", (int)v->kv);
-  g->qmode = v->query;
-  g->kvmode = v->kv;
-  g->Nkv = v->kv == EDIT_KV_COMPRESSED ? g->Nc : g->N;
+  const int qm = enum_int(v->query), kvm = enum_int(v->kv);
+  if (qm != EDIT_QUERY_CONVFUSION && qm != EDIT_QUERY_LINEAR)
+    return fail(EDIT_ERR_ARG, "unknown query mode %d", qm);
+  if (kvm != EDIT_KV_COMPRESSED && kvm != EDIT_KV_FULL && kvm != EDIT_KV_KEY_CONVFUSION)
+    return fail(EDIT_ERR_ARG, "unknown key/value mode %d", kvm);
+  g->qmode = qm;
+  g->kvmode = kvm;
+  g->Nkv = kvm == EDIT_KV_COMPRESSED ? g->Nc : g->N;
   g->kv_chunks = edit::kv_state_chunks(g->Nkv);
   return EDIT_OK;
 }
@@ -217,6 +230,29 @@ edit_status_t check_weights(const edit_weights_t* w, const Geometry& g) {
     if (st != EDIT_OK) return st;
   }
   return EDIT_OK;
+}
+
+// Elements of each edit_weights_t member, in its declaration order.
+void weight_elems(const Geometry& g, size_t (&ne)[18]) {
+  const size_t C = g.C, Cr = g.Cr;
+  const size_t v[18] = {Cr * 9 * C, Cr, Cr, Cr, C * Cr, C, C * C, C, C * C, C, C * C, C, 9 * C, C, 9 * C, C,
+                        C * C, C};
+  for (int i = 0; i < 18; ++i) ne[i] = v[i];
+}
+void weight_ptrs(const edit_weights_t* w, const void* (&p)[18]) {
+  const void* v[18] = {w->w_cf1, w->b_cf1, w->gn_gamma, w->gn_beta, w->w_cf2, w->b_cf2, w->w_q, w->b_q, w->w_k,
+                       w->b_k, w->w_v, w->b_v, w->dw_k, w->db_k, w->dw_v, w->db_v, w->w_o, w->b_o};
+  for (int i = 0; i < 18; ++i) p[i] = v[i];
+}
+// Whether [p, p + bytes) overlaps any parameter the geometry's variant reads.
+bool overlaps_weight(const void* p, size_t bytes, const edit_weights_t* w, const Geometry& g) {
+  size_t ne[18];
+  const void* wp[18];
+  weight_elems(g, ne);
+  weight_ptrs(w, wp);
+  for (int i = 0; i < 18; ++i)
+    if (overlap(p, bytes, wp[i], ne[i] * g.es)) return true;
+  return false;
 }
 
 edit_status_t check_convfusion_weights(const edit_convfusion_weights_t* w) {
@@ -891,6 +927,7 @@ static edit_status_t forward_impl(const edit_shape_t* shape, const edit_weights_
     return fail(EDIT_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
   const size_t act = (size_t)g.M * g.C * g.es;
   if (overlap(y, act, x, act)) return fail(EDIT_ERR_ARG, "y overlaps x");
+  if (overlaps_weight(y, act, w, g)) return fail(EDIT_ERR_ARG, "y overlaps a weight");
   if (overlap(y, act, workspace, ws_bytes)) return fail(EDIT_ERR_ARG, "y overlaps the workspace");
   if (overlap(x, act, workspace, ws_bytes)) return fail(EDIT_ERR_ARG, "x overlaps the workspace");
   if ((st = check_device()) != EDIT_OK) return st;
@@ -947,6 +984,23 @@ edit_status_t edit_attn_backward(const edit_shape_t* shape, const edit_weights_t
                        "grads.dw_k", "grads.db_k", "grads.dw_v", "grads.db_v", "grads.w_o", "grads.b_o"};
     for (int i = 0; i < 18; ++i)
       if ((st = check_ptr(p[i], n[i])) != EDIT_OK) return st;
+    // Every gradient is an output: it may overlap no input (x, dy, a weight), no other output
+    // (dx, another gradient) and neither workspace. Sizes in edit_weights_t / edit_grads_t order.
+    size_t ne[18];
+    weight_elems(g, ne);
+    const size_t act = (size_t)g.M * g.C * g.es;
+    for (int i = 0; i < 18; ++i) {
+      const size_t bi = ne[i] * g.es;
+      if (overlap(p[i], bi, x, act) || overlap(p[i], bi, dy, act) || overlap(p[i], bi, dx, act))
+        return fail(EDIT_ERR_ARG, "%s overlaps x, dy or dx", n[i]);
+      if (overlap(p[i], bi, workspace, ws_bytes) || overlap(p[i], bi, fwd_workspace, fwd_ws_bytes))
+        return fail(EDIT_ERR_ARG, "%s overlaps a workspace", n[i]);
+      if (overlaps_weight(p[i], bi, w, g)) return fail(EDIT_ERR_ARG, "%s overlaps a weight", n[i]);
+      for (int j = 0; j < 18; ++j)
+        if (j != i && overlap(p[i], bi, p[j], ne[j] * g.es))
+          return fail(EDIT_ERR_ARG, "%s overlaps another gradient", n[i]);
+    }
+    if (overlaps_weight(dx, act, w, g)) return fail(EDIT_ERR_ARG, "dx overlaps a weight");
   }
   if (!fwd_workspace) return fail(EDIT_ERR_ARG, "forward workspace is NULL");
   if (misaligned(fwd_workspace, 256)) return fail(EDIT_ERR_ARG, "forward workspace is not 256-byte aligned");
@@ -1003,6 +1057,8 @@ static edit_status_t hybrid_impl(const edit_shape_t* shape, int n_text, const ed
       return fail(EDIT_ERR_ARG, "y_txt overlaps an input or the workspace");
   }
   if (n_text > 0 && overlap(y_img, ai, y_txt, at)) return fail(EDIT_ERR_ARG, "y_img overlaps y_txt");
+  if (overlaps_weight(y_img, ai, img, g) || (n_text > 0 && overlaps_weight(y_txt, at, img, g)))
+    return fail(EDIT_ERR_ARG, "an output overlaps an image-stream weight");
   if (overlap(x_img, ai, workspace, ws_bytes) || (n_text > 0 && overlap(x_txt, at, workspace, ws_bytes)))
     return fail(EDIT_ERR_ARG, "an input overlaps the workspace");
   if ((st = check_device()) != EDIT_OK) return st;

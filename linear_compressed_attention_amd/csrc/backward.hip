@@ -2,7 +2,7 @@
 //
 // Page "EDiT: Efficient Diffusion Transformers with Linear Compressed
 // Attention" (ICCV 2025 notes): the layer is trained by distillation
-// (section "Distillation"), which needs the gradient of every forward step
+// (section "训练策略", training strategy), which needs the gradient of every forward step
 // (sections "ConvFusion", "Spatial Compressor", "Linear-attention formula").
 // Each kernel below is the chain rule of one forward step; the GEMM-shaped
 // products run on the GEMM kernels (with transposed operands where the

@@ -621,17 +621,9 @@ hipError_t launch_dma_tiles(const GemmArgs<bf16>& a, hipStream_t s) {
 
 }  // namespace
 
-#ifndef EDIT_DMA_FORCE
-#define EDIT_DMA_FORCE 0
-#endif
-#ifndef EDIT_CONV_TILE
-#define EDIT_CONV_TILE 0
-#endif
-
 // Returns hipErrorNotSupported (nothing launched) when the shape is outside
 // what the kernel handles; the caller then uses the register-staged GEMM.
 hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStream_t s) {
-  if (EDIT_DMA_FORCE < 0) return hipErrorNotSupported;
   if (em == E_RES && a.ldr % 4 != 0) return hipErrorNotSupported;
   if (a.K % 8 != 0 || a.N % 8 != 0 || a.ldb % 8 != 0 || a.lda % 8 != 0 || a.ldc % 8 != 0)
     return hipErrorNotSupported;
@@ -655,9 +647,6 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
       if (a.gn_rows == 128) return launch_dma_tiles<128, 96, 4, 1, A_CONV3, E_BIAS_GN, 2>(a, s);
       return launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_BIAS_GN>(a, s);
     }
-#if EDIT_CONV_TILE == 1
-    if (n96) return launch_dma_tiles<128, 96, 4, 1, A_CONV3, E_BIAS, 2>(a, s);
-#endif
     if (n96) return launch_dma_tiles<256, 96, 4, 1, A_CONV3, E_BIAS>(a, s);
     if (n128) return launch_dma_tiles<256, 128, 2, 2, A_CONV3, E_BIAS>(a, s);
     return hipErrorNotSupported;
@@ -681,10 +670,6 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
     if (em == E_RES) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_RES, 2>(a, s);
     if (em == E_BIAS) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS, 2>(a, s);
     if (em == E_BIAS_RELU) return launch_dma_tiles<128, 192, 2, 2, A_PLAIN, E_BIAS_RELU, 2>(a, s);
-  }
-  if (am == A_PLAIN && EDIT_DMA_FORCE == 1 && n128) {
-    if (em == E_BIAS) return launch_dma_tiles<256, 128, 2, 2, A_PLAIN, E_BIAS>(a, s);
-    if (em == E_BIAS_RELU) return launch_dma_tiles<256, 128, 2, 2, A_PLAIN, E_BIAS_RELU>(a, s);
   }
   return hipErrorNotSupported;
 }

@@ -204,3 +204,57 @@ def test_variant_unread_weights_may_be_null():
     with pytest.raises(lca.EditError) as e:
         lca.edit_attn_variant_forward(SHAPE, "linear", "full", w, None, 0x9000000, 0xA000000, ws, stream=0)
     assert e.value.status == 4
+
+
+def _fake_grads(base=0x3000000):
+    return {n: base + 0x10000 * i for i, n in enumerate(lca.IMAGE_WEIGHT_FIELDS)}
+
+
+def _bwd_call(grads=None, w=None, x=0x9000000, dy=0x9800000, dx=0xA000000):
+    fws = _FakeWS(0xB000000, lca.edit_attn_workspace_size(SHAPE))
+    ws = _FakeWS(0xC000000, lca.edit_attn_backward_workspace_size(SHAPE))
+    lca.edit_attn_backward(SHAPE, w or _fake_weights(), x, dy, fws, dx, grads or _fake_grads(), ws, stream=0)
+
+
+@pytest.mark.parametrize("case", ["x", "dy", "dx", "weight", "fwd_ws", "ws", "other_grad", "dx_weight"])
+def test_backward_gradient_overlaps_rejected(case):
+    """Each gradient is an output sized from the shape (w_cf1: C/r x 9 x C, a Linear: C x C, ...): one that
+    overlaps an input, another output or a workspace is rejected before anything is launched."""
+    g = _fake_grads()
+    kw = {}
+    if case == "x":
+        g["w_q"] = 0x9000000 + 0x100
+    elif case == "dy":
+        g["b_k"] = 0x9800000
+    elif case == "dx":
+        g["dw_v"] = 0xA000000 + 0x400
+    elif case == "weight":
+        g["w_cf1"] = _fake_weights()["w_o"] + 0x10    # within w_o's C x C bf16 elements
+    elif case == "fwd_ws":
+        g["gn_beta"] = 0xB000000 + 0x200
+    elif case == "ws":
+        g["b_o"] = 0xC000000 + 0x2000
+    elif case == "other_grad":
+        g["b_q"] = g["w_q"] + 64 * 64 * 2 - 16      # the last 16 bytes of w_q's gradient
+    elif case == "dx_weight":
+        kw["dx"] = _fake_weights()["w_k"]
+    with pytest.raises(lca.EditError) as e:
+        _bwd_call(grads=g, **kw)
+    assert e.value.status == 1 and "overlaps" in e.value.detail, e.value.detail
+
+
+def test_backward_gradients_just_apart_pass_the_checks():
+    """Gradients that only touch end to start are accepted (the missing device is what is reported here)."""
+    g = _fake_grads()
+    g["b_q"] = g["w_q"] + 64 * 64 * 2                # right after w_q's gradient
+    if torch.cuda.device_count() > 0:
+        pytest.skip("checks the argument path up to the no-device report")
+    with pytest.raises(lca.EditError) as e:
+        _bwd_call(grads=g)
+    assert e.value.status == 4, e.value.detail
+
+
+def test_forward_output_overlapping_a_weight_rejected():
+    with pytest.raises(lca.EditError) as e:
+        _call(y=_fake_weights()["w_q"])
+    assert e.value.status == 1 and "weight" in e.value.detail

@@ -100,6 +100,14 @@ def test_pixart_full_size(name):
     check_edit(CONFIGS[name])
 
 
+def test_pixart1024_shape_f32():
+    """fp32 mode at the PixArt-1024 layer shape (2 x 64x64 tokens, C = 1152,
+    16 heads x 72): every intermediate and the output within 1e-4."""
+    s = make_shape(B=2, H=64, W=64, C=1152, heads=16, head_dim=72, reduction=4, gn_groups=32, dtype="f32",
+                   x_std=1.0)
+    check_edit(s, seed=0)
+
+
 def check_hybrid(s, n_text, seed=0, exact=False):
     inp = make_inputs(s, seed=seed, n_text=n_text)
     _announce(f"hybrid {s} n_text={n_text} seed={seed} exact_eta={exact}")

@@ -28,20 +28,34 @@ def _inp(s, seed):
     return inp, dout
 
 
-def torch_forward(x, w, s):
+def _kink(out, pre, mask):
+    """out's values with the derivative `mask` (a tensor of slopes) in place
+    of out's own: a straight-through branch choice."""
+    return out if mask is None else out.detach() + (pre - pre.detach()) * mask
+
+
+def torch_forward(x, w, s, masks=None):
     """The layer in float64 torch.nn.functional, channels-first, written
-    independently of the oracle (same readings)."""
+    independently of the oracle (same readings). masks (optional): per kink
+    the slope its derivative takes ("q", "kc": 1 / 0; "act": 1 / 0.01), in
+    the token-major shapes of the oracle's q, kc and cf_act."""
     B, H, W, C, h = s.B, s.H, s.W, s.C, s.heads
     d = C // h
+    m = masks or {}
+    cf = lambda t: None if t is None else t.reshape(B, H, W, -1).permute(0, 3, 1, 2)
     g = x.reshape(B, H, W, C).permute(0, 3, 1, 2)
     xc = F.conv2d(g, w["w_cf1"].permute(0, 3, 1, 2), w["b_cf1"], padding=1)
-    a = F.leaky_relu(F.group_norm(xc, s.gn_groups, w["gn_gamma"], w["gn_beta"], eps=1e-5), 0.01)
+    gn = F.group_norm(xc, s.gn_groups, w["gn_gamma"], w["gn_beta"], eps=1e-5)
+    a = _kink(F.leaky_relu(gn, 0.01), gn, cf(m.get("act")))
     r = F.conv2d(a, w["w_cf2"][:, :, None, None], w["b_cf2"])
     xt = (g + r).permute(0, 2, 3, 1).reshape(B, H * W, C)
-    q = F.relu(F.linear(xt, w["w_q"], w["b_q"]))
+    qp = F.linear(xt, w["w_q"], w["b_q"])
+    q = _kink(F.relu(qp), qp, m.get("q"))
     k0 = F.linear(x, w["w_k"], w["b_k"]).reshape(B, H, W, C).permute(0, 3, 1, 2)
     v0 = F.linear(x, w["w_v"], w["b_v"]).reshape(B, H, W, C).permute(0, 3, 1, 2)
-    kc = F.relu(F.conv2d(k0, w["dw_k"].permute(2, 0, 1)[:, None], w["db_k"], stride=2, padding=1, groups=C))
+    kp = F.conv2d(k0, w["dw_k"].permute(2, 0, 1)[:, None], w["db_k"], stride=2, padding=1, groups=C)
+    mk = m.get("kc")
+    kc = _kink(F.relu(kp), kp, None if mk is None else mk.reshape(B, kp.shape[2], kp.shape[3], C).permute(0, 3, 1, 2))
     vc = F.conv2d(v0, w["dw_v"].permute(2, 0, 1)[:, None], w["db_v"], stride=2, padding=1, groups=C)
     kc = kc.permute(0, 2, 3, 1).reshape(B, -1, h, d)
     vc = vc.permute(0, 2, 3, 1).reshape(B, -1, h, d)
@@ -72,6 +86,47 @@ def test_backward_against_torch_autograd(s, seed):
     for n in OB.PARAM_NAMES:
         assert grads[n].shape == inp["w"][n].shape, n
         close(grads[n], wt[n].grad.numpy(), n)
+
+
+@pytest.mark.parametrize("s,seed", [(S_TINY, 2), (S_MID, 4)])
+def test_backward_with_kink_masks_against_torch_autograd(s, seed):
+    """With masks given, the oracle backward is the gradient of the branch the
+    masks name (R28): torch.autograd through a forward whose ReLU and
+    LeakyReLU keep their values but take the masks' slopes. A fifth of the
+    decisions are flipped against the oracle's own forward, so the masks,
+    not the signs of the float64 forward, must decide."""
+    inp, dout = _inp(s, seed)
+    f = {}
+    O.edit_attn_forward(inp["x"], inp["w"], s, f)
+    rng = np.random.default_rng(2000 + seed)
+    flip = lambda on: on ^ (rng.random(on.shape) < 0.2)
+    masks = {"q": flip(f["q"] > 0), "kc": flip(f["kc"] > 0), "act": flip(f["cf_act"] >= 0)}
+    dx, grads = OB.edit_attn_backward(inp["x"], inp["w"], s, dout, masks=masks)
+    dx0, _ = OB.edit_attn_backward(inp["x"], inp["w"], s, dout)
+    assert np.abs(dx - dx0).max() > 1e-3 * np.abs(dx0).max()       # the flips matter
+    slopes = {"q": torch.from_numpy(masks["q"].astype(np.float64)),
+              "kc": torch.from_numpy(masks["kc"].astype(np.float64)),
+              "act": torch.from_numpy(np.where(masks["act"], 1.0, 0.01))}
+    xt = torch.tensor(inp["x"], dtype=torch.float64, requires_grad=True)
+    wt = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in inp["w"].items()}
+    (torch_forward(xt, wt, s, slopes) * torch.from_numpy(dout)).sum().backward()
+    for name, a, b in [("x", dx, xt.grad.numpy())] + [(n, grads[n], wt[n].grad.numpy()) for n in OB.PARAM_NAMES]:
+        scale = max(np.abs(b).max(), 1e-300)
+        assert np.abs(a - b).max() <= 1e-10 * scale, f"{name}: {np.abs(a - b).max() / scale:.3e}"
+
+
+def test_backward_with_own_masks_is_unchanged():
+    """Masks equal to the oracle's own kink decisions give its unmasked result bit for bit."""
+    s = S_TINY
+    inp, dout = _inp(s, 6)
+    f = {}
+    O.edit_attn_forward(inp["x"], inp["w"], s, f)
+    masks = {"q": f["q"] > 0, "kc": f["kc"] > 0, "act": f["cf_act"] >= 0}
+    dx, g = OB.edit_attn_backward(inp["x"], inp["w"], s, dout, masks=masks)
+    dx0, g0 = OB.edit_attn_backward(inp["x"], inp["w"], s, dout)
+    assert np.array_equal(dx, dx0)
+    for n in OB.PARAM_NAMES:
+        assert np.array_equal(g[n], g0[n]), n
 
 
 def _loss(x, w, s, dout):
