@@ -511,6 +511,10 @@ def main():
     roofline["achievable_hbm_GBs"] = round(copy_gbs, 1)
     if d["bound"] == "hbm":
         roofline["frac_of_achievable"] = round(d["achieved"] / copy_gbs, 4)
+    # every HBM-bound step also against the copy rate this box reached
+    for n in STEP_NAMES:
+        if steps[n]["bound"] == "hbm":
+            steps[n]["frac_of_achievable"] = round(steps[n]["achieved"] / copy_gbs, 4)
 
     cpu = None
     if args.cpu_runs > 0:
@@ -551,7 +555,8 @@ def main():
                            **({"covers": "image path only"} if hybrid else {}),
                            **({"covers": "the layer's own steps (breakdown taken on the layer, not the variant)"}
                               if variant else {})},
-        "steps_breakdown": {n: {k: v for k, v in steps[n].items() if k in ("us", "bound", "achieved", "unit", "frac")}
+        "steps_breakdown": {n: {k: v for k, v in steps[n].items()
+                                if k in ("us", "bound", "achieved", "unit", "frac", "frac_of_achievable")}
                             for n in STEP_NAMES},
         "wall_s_timed_region": round(wall, 4),
     }

@@ -281,6 +281,28 @@ edit_status_t edit_attn_backward(const edit_shape_t* shape, const edit_weights_t
                                  void* dx, const edit_grads_t* grads,
                                  void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* Where the backward's intermediate gradients of the last edit_attn_backward
+ * call with this shape live in its workspace (byte offsets; a pure function
+ * of the shape), for checking the backward step by step. T is the shape's
+ * dtype; chain-rule steps as in edit_attn_backward:
+ *   dy      [B][N][C]    T    gradient of the linear-attention output (dout W_o)
+ *   dq_pre  [B][N][C]    T    gradient of the queries' pre-activation (the ReLU's mask applied)
+ *   dS      [B][h][d][d] f32  gradient of S = sum K'^T V' (same index order as S)
+ *   dz      [B][h][d]    f32  gradient of z = sum K'
+ *   dkv     [B][N'][2C]  f32  gradients of the keys' pre-activation (ReLU's mask applied) | of V'
+ *   dk0v0   [B][N][2C]   T    gradients of the key | value Linears' outputs
+ *   dxq     [B][N][C]    T    gradient of the restored stream x + Conv1x1(act) (= dq_pre W_q)
+ *   dxkv    [B][N][C]    T    dxq + the key and value Linears' input gradients
+ *   dact    [B][N][C/r]  T    gradient of act = LeakyReLU(GN(xc))
+ *   dxc     [B][N][.]    T    gradient of xc, rows of dxc_ld elements (C/r used, the rest zero) */
+typedef struct {
+  size_t dy, dq_pre, dS, dz, dkv, dk0v0, dxq, dxkv, dact, dxc;
+  size_t dxc_ld;   /* elements per dxc row */
+  size_t total;
+} edit_bwd_layout_t;
+
+edit_status_t edit_attn_backward_workspace_layout(const edit_shape_t* shape, edit_bwd_layout_t* layout);
+
 const char* edit_status_string(edit_status_t status);
 const char* edit_last_error(void);
 

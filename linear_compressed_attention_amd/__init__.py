@@ -19,7 +19,8 @@ __all__ = [
     "mmedit_hybrid_forward", "mmedit_hybrid_exact_forward", "edit_attn_forward_timed", "edit_attn_workspace_layout", "EDIT_NUM_STEPS", "edit_status_string", "edit_last_error",
     "lib_path", "header_symbols", "QUERY_MODES", "KV_MODES", "KEY_CONVFUSION_FIELDS",
     "edit_attn_variant_workspace_size", "edit_attn_variant_workspace_layout", "edit_attn_variant_forward",
-    "edit_attn_backward_workspace_size", "edit_attn_backward",
+    "edit_attn_backward_workspace_size", "edit_attn_backward", "edit_attn_backward_workspace_layout",
+    "BWD_LAYOUT_FIELDS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +60,13 @@ class _TextWeights(ctypes.Structure):
 
 class _Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in LAYOUT_FIELDS]
+
+
+BWD_LAYOUT_FIELDS = ("dy", "dq_pre", "dS", "dz", "dkv", "dk0v0", "dxq", "dxkv", "dact", "dxc", "dxc_ld", "total")
+
+
+class _BwdLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in BWD_LAYOUT_FIELDS]
 
 
 class _Variant(ctypes.Structure):
@@ -114,6 +122,8 @@ def _load():
                                        ctypes.c_size_t, ctypes.c_void_p, P(_Grads), ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]
     lib.edit_attn_backward.restype = ctypes.c_int
+    lib.edit_attn_backward_workspace_layout.argtypes = [P(_Shape), P(_BwdLayout)]
+    lib.edit_attn_backward_workspace_layout.restype = ctypes.c_int
     lib.edit_status_string.argtypes = [ctypes.c_int]
     lib.edit_status_string.restype = ctypes.c_char_p
     lib.edit_last_error.argtypes = []
@@ -229,6 +239,14 @@ def edit_attn_forward(shape, weights, x, y, workspace, stream=None) -> None:
 def edit_attn_backward_workspace_size(shape) -> int:
     """Scratch bytes edit_attn_backward needs beyond the forward's workspace."""
     return int(_lib.edit_attn_backward_workspace_size(ctypes.byref(_shape(shape))))
+
+
+def edit_attn_backward_workspace_layout(shape) -> dict:
+    """Byte offsets of the backward's intermediate gradients in its workspace
+    (and dxc_ld, the dxc row length in elements)."""
+    lay = _BwdLayout()
+    _check(_lib.edit_attn_backward_workspace_layout(ctypes.byref(_shape(shape)), ctypes.byref(lay)))
+    return {n: int(getattr(lay, n)) for n in BWD_LAYOUT_FIELDS}
 
 
 def edit_attn_backward(shape, weights, x, dy, fwd_workspace, dx, grads, workspace, stream=None) -> None:

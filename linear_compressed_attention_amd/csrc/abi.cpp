@@ -683,7 +683,7 @@ BwdLayout make_bwd_layout(const Geometry& g) {
   L.st = take(BH * 2 * g.DP * g.DK * es);
   L.zp = take(BH * g.DK * 4);
   L.kvpart = take(BH * edit::kv_state_chunks(g.N) * (16 * g.DR) * (16 * g.DT) * 4);
-  L.dkv = take(Mc * 2 * C * es);
+  L.dkv = take(Mc * 2 * C * 4);   // fp32: its sums over tokens cancel (see kv_bwd_kernel)
   L.dk0v0 = take(M * 2 * C * es);
   L.dXkv = take(M * C * es);
   L.dact = take(M * Cr * es);
@@ -708,7 +708,7 @@ BwdLayout make_bwd_layout(const Geometry& g) {
   L.dWx = take(C * C * 4);
   L.dWa = take(C * Cr * 4);
   L.dbq32 = take(C * 4);
-  L.dwpart = take((size_t)edit::dw_bwd_chunks(g.B, g.H, g.W) * 10 * 2 * C * 4);
+  L.dwpart = take((size_t)edit::dw_bwd_chunks(g.B, g.H, g.W) * 11 * 2 * C * 4);
   L.gnpart = take((size_t)g.B * edit::gn_bwd_chunks(g.N) * Cr * 2 * 4);
   L.m12 = take((size_t)g.B * g.G * 2 * 4);
   L.total = off;
@@ -806,16 +806,16 @@ edit_status_t run_backward(const Geometry& g, const Layout& F, const BwdLayout& 
   EDIT_LAUNCH(launch_kv_state<T>(FP(F.q), P(L.g), C, g.B, g.N, g.heads, g.d, Q(L.kvpart), kv_state_chunks(g.N),
                                  Q(L.dS), Q(L.dz), P(L.st), Q(L.zp), s, Q(L.cvec)));
   // dK' (through the keys' ReLU), dV'
-  EDIT_LAUNCH(launch_kv_bwd<T>(FP(F.kc), FP(F.vc), Q(L.dS), Q(L.dz), g.B, g.Nc, g.heads, g.d, P(L.dkv), s));
+  EDIT_LAUNCH(launch_kv_bwd<T>(FP(F.kc), FP(F.vc), Q(L.dS), Q(L.dz), g.B, g.Nc, g.heads, g.d, Q(L.dkv), s));
 
   // Spatial Compressor: depthwise convs, then the key / value Linears
-  EDIT_LAUNCH(launch_dw_bwd_input<T>(P(L.dkv), g.B, g.H, g.W, C, W(w->dw_k), W(w->dw_v), P(L.dk0v0), s));
-  EDIT_LAUNCH(launch_dw_bwd_weight<T>(P(L.dkv), FP(F.kv0), g.B, g.H, g.W, C, Q(L.dwpart), G(gr->dw_k), G(gr->db_k),
-                                      G(gr->dw_v), G(gr->db_v), s));
+  EDIT_LAUNCH(launch_dw_bwd_input<T>(Q(L.dkv), g.B, g.H, g.W, C, W(w->dw_k), W(w->dw_v), P(L.dk0v0), s));
+  // ... and with them the key / value Linears' bias gradients (sums of dk0, dv0 over tokens)
+  EDIT_LAUNCH(launch_dw_bwd_weight<T>(Q(L.dkv), FP(F.kv0), W(w->dw_k), W(w->dw_v), g.B, g.H, g.W, C, Q(L.dwpart),
+                                      G(gr->dw_k), G(gr->db_k), G(gr->dw_v), G(gr->db_v), G(gr->b_k), G(gr->b_v), s));
   // dXkv = [dk0 | dv0] [W_k; W_v] + dXq (the two input-gradient terms so far)
   if ((st = gemm(M, C, 2 * C, P(L.dk0v0), 2 * C, P(L.wkvT), 2 * C, P(L.dXkv), C, P(L.dXq))) != EDIT_OK) return st;
-  EDIT_LAUNCH(launch_transpose<T>(P(L.dk0v0), M, 2 * C, 2 * C, P(L.dkvT), Mp, s, Mp, 1, 0, 0, cs));
-  EDIT_LAUNCH(launch_colsum_finalize<T>(cs, 2 * C, nrt, G(gr->b_k), s, nullptr, G(gr->b_v), C));
+  EDIT_LAUNCH(launch_transpose<T>(P(L.dk0v0), M, 2 * C, 2 * C, P(L.dkvT), Mp, s, Mp));
   // dW_k and dW_v: one product over [dk0 | dv0]^T
   if ((st = wprod(2 * C, C, P(L.dkvT), P(L.xT))) != EDIT_OK) return st;
   if ((st = wsum2(2 * C, C, G(gr->w_k), G(gr->w_v), C)) != EDIT_OK) return st;
@@ -962,6 +962,19 @@ size_t edit_attn_backward_workspace_size(const edit_shape_t* shape) {
   Geometry g;
   if (check_shape(shape, 0, &g) != EDIT_OK) return 0;
   return make_bwd_layout(g).total;
+}
+
+edit_status_t edit_attn_backward_workspace_layout(const edit_shape_t* shape, edit_bwd_layout_t* out) {
+  Geometry g;
+  edit_status_t st = check_shape(shape, 0, &g);
+  if (st != EDIT_OK) return st;
+  if (!out) return fail(EDIT_ERR_ARG, "layout is NULL");
+  const BwdLayout L = make_bwd_layout(g);
+  out->dy = L.dy; out->dq_pre = L.dq_pre; out->dS = L.dS; out->dz = L.dz; out->dkv = L.dkv;
+  out->dk0v0 = L.dk0v0; out->dxq = L.dXq; out->dxkv = L.dXkv; out->dact = L.dact; out->dxc = L.dxc;
+  out->dxc_ld = (size_t)L.Crp;
+  out->total = L.total;
+  return EDIT_OK;
 }
 
 edit_status_t edit_attn_backward(const edit_shape_t* shape, const edit_weights_t* w, const void* x, const void* dy,

@@ -438,7 +438,11 @@ hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const floa
 // z = sum K'): per compressed token j and head,
 //   dK'_j = V'_j dS^T + dz, then the keys' ReLU (where K'_j > 0),
 //   dV'_j = K'_j dS.
-// Writes dkv [B][Nc][2C]: the keys' gradient before their ReLU | the values'.
+// Writes dkv [B][Nc][2C] in fp32: the keys' gradient before their ReLU | the
+// values'. It stays fp32 because its sums over tokens cancel: moving every K'
+// by one vector changes the outputs only through V'_j - y_i, a few percent of
+// V', so the bias gradients sum terms ~25 times larger than the result, and a
+// bf16 rounding of each term would leave errors of a few percent there.
 // On the matrix cores: dK'^T = dS V'^T (A operand dS) and dV'^T = dS^T K'^T
 // (A operand dS^T), 32 compressed tokens per wave.
 // ---------------------------------------------------------------------------
@@ -446,7 +450,7 @@ template <typename T, int KS>
 __global__ __launch_bounds__(256) void kv_bwd_kernel(const T* __restrict__ kc, const T* __restrict__ vc,
                                                      const float* __restrict__ dS, const float* __restrict__ dz,
                                                      int Nc, int heads, int d, int tiles_per_wave,
-                                                     T* __restrict__ dkv) {
+                                                     float* __restrict__ dkv) {
   using HM = HeadMat<T, KS>;
   using F = typename Frag<T>::type;
   __shared__ __attribute__((aligned(16))) T A1[HM::NC * HM::RT * 32 * HM::KP];   // dS
@@ -466,7 +470,7 @@ __global__ __launch_bounds__(256) void kv_bwd_kernel(const T* __restrict__ kc, c
     const int tok = tok0 + col;
     const bool valid = tok < Nc;
     const size_t row = ((size_t)b * Nc + (valid ? tok : 0)) * C + (size_t)h * d;
-    T* out = dkv + ((size_t)b * Nc + (valid ? tok : 0)) * 2 * C + (size_t)h * d;
+    float* out = dkv + ((size_t)b * Nc + (valid ? tok : 0)) * 2 * C + (size_t)h * d;
     // Every load of the tile (V', K' as operands, K' for the ReLU mask) is
     // issued before its first store: a load queued behind a store waits for it.
     F bv[KS], bk[KS];
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(256) void kv_bwd_kernel(const T* __restrict__ kc, c
 
 template <typename T>
 hipError_t launch_kv_bwd(const T* kc, const T* vc, const float* dS, const float* dz, int B, int Nc, int heads,
-                         int d, T* dkv, hipStream_t s) {
+                         int d, float* dkv, hipStream_t s) {
   if (d % 8 || d > 128 || Nc <= 0) return Nc <= 0 ? hipSuccess : hipErrorInvalidValue;
   const int tpw = head_tiles_per_wave(B, heads, Nc);
   dim3 grid(((Nc + 31) / 32 + 4 * tpw - 1) / (4 * tpw), heads, B);
@@ -546,7 +550,7 @@ hipError_t launch_kv_bwd(const T* kc, const T* vc, const float* dS, const float*
 // (taps visited in (ky, kx) order). One thread per pixel and 8 channels.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void dw_bwd_input_kernel(const T* __restrict__ dout, int B, int H, int W, int C,
+__global__ __launch_bounds__(256) void dw_bwd_input_kernel(const float* __restrict__ dout, int B, int H, int W, int C,
                                                            const T* __restrict__ dwk, const T* __restrict__ dwv,
                                                            T* __restrict__ din) {
   const int Hc = (H + 1) / 2, Wc = (W + 1) / 2;
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(256) void dw_bwd_input_kernel(const T* __restrict__
 }
 
 template <typename T>
-hipError_t launch_dw_bwd_input(const T* dout, int B, int H, int W, int C, const T* dwk, const T* dwv, T* din,
+hipError_t launch_dw_bwd_input(const float* dout, int B, int H, int W, int C, const T* dwk, const T* dwv, T* din,
                                hipStream_t s) {
   const long total = (long)B * H * W * (2 * C / 8);
   if (total <= 0) return hipSuccess;
@@ -604,15 +608,22 @@ hipError_t launch_dw_bwd_input(const T* dout, int B, int H, int W, int C, const 
 
 // Weight gradient of the depthwise convs: for tap t = (ky, kx) and channel c,
 //   dw[t][c] = sum_{b, y', x'} dout[y'][x'][c] in[2y'+ky-1][2x'+kx-1][c], db[c] = sum dout[y'][x'][c].
+// Also the sum over all input pixels of the input gradient (the preceding
+// Linear's bias gradient), from the fp32 dout rather than the rounded input
+// gradient: every output pixel's gradient reaches the input through its taps
+// that lie inside the image, so
+//   sum_pixels din[c] = (sum_t w[t][c]) db[c] - sum_{y', x'} dout[y'][x'][c] sum_{t outside} w[t][c],
+// where only border pixels have taps outside; the partials keep that last sum.
 // A block takes 32 channel chunks x 8 pixel lanes over kDwPix output pixels;
-// each thread keeps 10 x 8 sums, the 8 lanes are added through LDS, and the
-// chunk's partial goes to partial[chunk][10][2C]; the chunks are then added
+// each thread keeps 11 x 8 sums, the 8 lanes are added through LDS, and the
+// chunk's partial goes to partial[chunk][11][2C]; the chunks are then added
 // in order.
 constexpr int kDwPix = 32;    // output pixels per partial
 
 template <typename T>
-__global__ __launch_bounds__(256) void dw_bwd_weight_partial_kernel(const T* __restrict__ dout,
-                                                                    const T* __restrict__ in, int B, int H, int W,
+__global__ __launch_bounds__(256) void dw_bwd_weight_partial_kernel(const float* __restrict__ dout,
+                                                                    const T* __restrict__ in, const T* __restrict__ dwk,
+                                                                    const T* __restrict__ dwv, int B, int H, int W,
                                                                     int C, float* __restrict__ partial) {
   __shared__ float red[8][32 * 8 + 4];
   const int Hc = (H + 1) / 2, Wc = (W + 1) / 2, Pc = B * Hc * Wc;
@@ -621,9 +632,10 @@ __global__ __launch_bounds__(256) void dw_bwd_weight_partial_kernel(const T* __r
   const int cpp = (2 * C) / 8;
   const bool active = c8 < cpp;
   const int ch2 = 8 * c8;
-  float acc[10][8];
+  const T* wtap = ch2 < C ? dwk + ch2 : dwv + (ch2 - C);
+  float acc[11][8];
 #pragma unroll
-  for (int t = 0; t < 10; ++t)
+  for (int t = 0; t < 11; ++t)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[t][i] = 0.0f;
   const int p0 = chunk * kDwPix;
@@ -649,11 +661,26 @@ __global__ __launch_bounds__(256) void dw_bwd_weight_partial_kernel(const T* __r
           for (int i = 0; i < 8; ++i) acc[t][i] += g[i] * v[t][i];
         }
       }
+      // border pixels: dout times the taps that fall outside the image
+      if (yo == 0 || 2 * yo + 1 >= H || xo == 0 || 2 * xo + 1 >= W) {
+        float wo[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        for (int t = 0; t < 9; ++t) {
+          const int yy = 2 * yo + t / 3 - 1, xx = 2 * xo + t % 3 - 1;
+          if (yy < 0 || yy >= H || xx < 0 || xx >= W) {
+            float wt[8];
+            load8(wtap + t * C, wt);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wo[i] += wt[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[10][i] += g[i] * wo[i];
+      }
     }
   }
-  float* out = partial + (size_t)chunk * 10 * 2 * C;
+  float* out = partial + (size_t)chunk * 11 * 2 * C;
 #pragma unroll
-  for (int t = 0; t < 10; ++t) {
+  for (int t = 0; t < 11; ++t) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) red[pl][cl * 8 + i] = acc[t][i];
     __syncthreads();
@@ -671,21 +698,37 @@ __global__ __launch_bounds__(256) void dw_bwd_weight_partial_kernel(const T* __r
 }
 
 // Sum the pixel-chunk partials in order; write dw_k, db_k (channels < C) and
-// dw_v, db_v. Taps are stored [3][3][C] as the weights.
+// dw_v, db_v (taps stored [3][3][C] as the weights), and the input gradient's
+// sums over pixels bk (channels < C) and bv: (sum_t w[t][c]) db[c] minus the
+// border term, from the fp32 sums.
 template <typename T>
 __global__ __launch_bounds__(256) void dw_bwd_weight_finalize_kernel(const float* __restrict__ partial, int nchunks,
-                                                                     int C, T* __restrict__ dwk, T* __restrict__ dbk,
-                                                                     T* __restrict__ dwv, T* __restrict__ dbv) {
+                                                                     int C, const T* __restrict__ wk,
+                                                                     const T* __restrict__ wv, T* __restrict__ dwk,
+                                                                     T* __restrict__ dbk, T* __restrict__ dwv,
+                                                                     T* __restrict__ dbv, T* __restrict__ bk,
+                                                                     T* __restrict__ bv) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= 10 * 2 * C) return;
   const int t = i / (2 * C), c2 = i - t * 2 * C;
   float s = 0.0f;
 #pragma unroll 8
-  for (int ch = 0; ch < nchunks; ++ch) s += partial[(size_t)ch * 10 * 2 * C + i];
+  for (int ch = 0; ch < nchunks; ++ch) s += partial[(size_t)ch * 11 * 2 * C + (size_t)t * 2 * C + c2];
   const bool k = c2 < C;
   const int c = k ? c2 : c2 - C;
-  if (t < 9) (k ? dwk : dwv)[t * C + c] = from_f32<T>(s);
-  else (k ? dbk : dbv)[c] = from_f32<T>(s);
+  if (t < 9) {
+    (k ? dwk : dwv)[t * C + c] = from_f32<T>(s);
+    return;
+  }
+  (k ? dbk : dbv)[c] = from_f32<T>(s);
+  float border = 0.0f;
+#pragma unroll 8
+  for (int ch = 0; ch < nchunks; ++ch) border += partial[(size_t)ch * 11 * 2 * C + (size_t)10 * 2 * C + c2];
+  const T* w = k ? wk : wv;
+  float wsum = 0.0f;
+#pragma unroll
+  for (int tap = 0; tap < 9; ++tap) wsum += to_f32(w[tap * C + c]);
+  (k ? bk : bv)[c] = from_f32<T>(wsum * s - border);
 }
 
 int dw_bwd_chunks(int B, int H, int W) {
@@ -694,15 +737,16 @@ int dw_bwd_chunks(int B, int H, int W) {
 }
 
 template <typename T>
-hipError_t launch_dw_bwd_weight(const T* dout, const T* in, int B, int H, int W, int C, float* partial, T* dwk,
-                                T* dbk, T* dwv, T* dbv, hipStream_t s) {
+hipError_t launch_dw_bwd_weight(const float* dout, const T* in, const T* wk, const T* wv, int B, int H, int W, int C,
+                                float* partial, T* dwk, T* dbk, T* dwv, T* dbv, T* bk, T* bv, hipStream_t s) {
   const int nch = dw_bwd_chunks(B, H, W);
   dim3 grid(nch, (2 * C / 8 + 31) / 32);
-  hipLaunchKernelGGL((dw_bwd_weight_partial_kernel<T>), grid, dim3(256), 0, s, dout, in, B, H, W, C, partial);
+  hipLaunchKernelGGL((dw_bwd_weight_partial_kernel<T>), grid, dim3(256), 0, s, dout, in, wk, wv, B, H, W, C,
+                     partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dw_bwd_weight_finalize_kernel<T>), dim3((10 * 2 * C + 255) / 256), dim3(256), 0, s, partial,
-                     nch, C, dwk, dbk, dwv, dbv);
+                     nch, C, wk, wv, dwk, dbk, dwv, dbv, bk, bv);
   return hipGetLastError();
 }
 
@@ -995,11 +1039,11 @@ template hipError_t launch_splitk_reduce<float, bf16>(const float*, int, long lo
                                                  int, int, T*, int);                                              \
   template hipError_t launch_attn_bwd_q<T>(const T*, const T*, const float*, const float*, int, int, int, int,     \
                                            float, T*, float*, T*, hipStream_t);                                    \
-  template hipError_t launch_kv_bwd<T>(const T*, const T*, const float*, const float*, int, int, int, int, T*,     \
+  template hipError_t launch_kv_bwd<T>(const T*, const T*, const float*, const float*, int, int, int, int, float*, \
                                        hipStream_t);                                                               \
-  template hipError_t launch_dw_bwd_input<T>(const T*, int, int, int, int, const T*, const T*, T*, hipStream_t);   \
-  template hipError_t launch_dw_bwd_weight<T>(const T*, const T*, int, int, int, int, float*, T*, T*, T*, T*,      \
-                                              hipStream_t);                                                        \
+  template hipError_t launch_dw_bwd_input<T>(const float*, int, int, int, int, const T*, const T*, T*, hipStream_t); \
+  template hipError_t launch_dw_bwd_weight<T>(const float*, const T*, const T*, const T*, int, int, int, int, float*, \
+                                              T*, T*, T*, T*, T*, T*, hipStream_t);                                \
   template hipError_t launch_gn_bwd<T>(const T*, const T*, const T*, const float*, const T*, int, int, int, int,   \
                                        float*, float*, T*, T*, T*, int, hipStream_t);
 EDIT_INST(bf16)

@@ -148,18 +148,20 @@ hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int 
 template <typename T>
 hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const float* z, int B, int N, int heads, int d,
                              float eps, T* g, float* c, T* dq_pre, hipStream_t s);
-// dkv [B][Nc][2C] = [ (V' dS^T + dz) where K' > 0 | K' dS ].
+// dkv [B][Nc][2C] (fp32) = [ (V' dS^T + dz) where K' > 0 | K' dS ].
 template <typename T>
 hipError_t launch_kv_bwd(const T* kc, const T* vc, const float* dS, const float* dz, int B, int Nc, int heads,
-                         int d, T* dkv, hipStream_t s);
-// Depthwise 3x3 stride-2 backward over 2C channels: input gradient, and weight / bias gradients.
+                         int d, float* dkv, hipStream_t s);
+// Depthwise 3x3 stride-2 backward over 2C channels (dout fp32): input gradient, and weight / bias
+// gradients; bk / bv also receive the input gradient's sums over pixels (the key / value Linears'
+// bias gradients), formed from the fp32 dout.
 template <typename T>
-hipError_t launch_dw_bwd_input(const T* dout, int B, int H, int W, int C, const T* dwk, const T* dwv, T* din,
+hipError_t launch_dw_bwd_input(const float* dout, int B, int H, int W, int C, const T* dwk, const T* dwv, T* din,
                                hipStream_t s);
 int dw_bwd_chunks(int B, int H, int W);
 template <typename T>
-hipError_t launch_dw_bwd_weight(const T* dout, const T* in, int B, int H, int W, int C, float* partial, T* dwk,
-                                T* dbk, T* dwv, T* dbv, hipStream_t s);
+hipError_t launch_dw_bwd_weight(const float* dout, const T* in, const T* wk, const T* wv, int B, int H, int W, int C,
+                                float* partial, T* dwk, T* dbk, T* dwv, T* dbv, T* bk, T* bv, hipStream_t s);
 // GroupNorm + LeakyReLU backward: dgamma, dbeta and dxc from dact (partial: B x gn_bwd_chunks(N) x C x 2 floats).
 int gn_bwd_chunks(int N);
 template <typename T>

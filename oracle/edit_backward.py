@@ -169,7 +169,10 @@ PARAM_NAMES = ("w_cf1", "b_cf1", "gn_gamma", "gn_beta", "w_cf2", "b_cf2", "w_q",
                "w_v", "b_v", "dw_k", "db_k", "dw_v", "db_v", "w_o", "b_o")
 
 
-def edit_attn_backward(x, w, shape, dout, trace=None, masks=None):
+FORWARD_KEYS = ("xc", "cf_act", "q", "k0", "v0", "kc", "vc", "S", "z", "y")
+
+
+def edit_attn_backward(x, w, shape, dout, trace=None, forward=None):
     """Gradients of sum(dout * edit_attn_forward(x, w, shape)) with respect to
     x and every parameter, in the forward's composition (the restored stream
     xt is formed, as the page writes it). Returns (dx, {name: gradient}) with
@@ -177,21 +180,26 @@ def edit_attn_backward(x, w, shape, dout, trace=None, masks=None):
     intermediate gradients (dy, dq, dS, dz, dkc, dvc, dk0, dv0, dxt, dact,
     dxc).
 
-    ``masks`` (optional) fixes the side of each kink instead of reading it
-    from this function's own float64 forward (R28: the derivative of a kink
-    is decided by the sign of the forward value there). Keys, each a boolean
-    array in the shape of the forward tensor it decides:
-      "q"   [B, N, C]     the queries' ReLU passes (q > 0)
-      "kc"  [B, N', C]    the compressed keys' ReLU passes (K' > 0)
-      "act" [B, N, C/r]   the LeakyReLU after GroupNorm has slope 1 (act >= 0)
-    A pre-activation within rounding of zero may fall on different sides of
-    a kink in two computations of the same forward; given the other
-    computation's decisions, the chain rule here is the gradient of the same
-    piecewise-linear branch that computation took."""
+    ``forward`` (optional) supplies the forward tensors every step's backward
+    is evaluated at, instead of this function's own float64 forward: a dict
+    with the token-major arrays FORWARD_KEYS (xc, cf_act, q, k0, v0, kc, vc,
+    y as [B, tokens, channels]; S [B, h, d, d]; z [B, h, d]), e.g. those
+    another computation of the same forward stored. Each step's chain rule
+    then runs at that computation's values, kink decisions included (R28:
+    the derivative at a kink follows the sign of the forward value there),
+    and the restored stream is xt = x + cf_act W_cf2^T + b_cf2 from the given
+    cf_act. With the float64 forward's own tensors the result is unchanged."""
     H, W, heads, G = shape.H, shape.W, shape.heads, shape.gn_groups
     x = _f64(x)
     f = {}
-    O.edit_attn_forward(x, w, shape, f)
+    if forward is None:
+        O.edit_attn_forward(x, w, shape, f)
+    else:
+        missing = [k for k in FORWARD_KEYS if k not in forward]
+        if missing:
+            raise ValueError(f"forward lacks {missing}")
+        f = {k: _f64(forward[k]) for k in FORWARD_KEYS}
+        f["xt"] = x + O.linear(f["cf_act"], w["w_cf2"], w["b_cf2"])
     grid = lambda t: O.tokens_to_grid(t, H, W)
     tok = O.grid_to_tokens
 
@@ -201,9 +209,7 @@ def edit_attn_backward(x, w, shape, dout, trace=None, masks=None):
     dq, dS, dz = linear_attention_apply_backward(f["q"], f["S"], f["z"], heads, shape.eps, dy)
     dkc, dvc = kv_state_backward(f["kc"], f["vc"], dS, dz, heads)
     # Spatial Compressor: ReLU on the keys, depthwise stride-2 convs, Linears
-    masks = masks or {}
-    kc_on = masks["kc"] if "kc" in masks else f["kc"]
-    dkc_pre = relu_backward(kc_on, dkc)
+    dkc_pre = relu_backward(f["kc"], dkc)
     dk0, ddw_k, ddb_k = dwconv3x3_s2_backward(grid(f["k0"]), w["dw_k"], O.tokens_to_grid(
         dkc_pre, (H + 1) // 2, (W + 1) // 2))
     dv0, ddw_v, ddb_v = dwconv3x3_s2_backward(grid(f["v0"]), w["dw_v"], O.tokens_to_grid(
@@ -213,12 +219,10 @@ def edit_attn_backward(x, w, shape, dout, trace=None, masks=None):
     dx_v, dw_v, db_v = linear_backward(x, w["w_v"], dv0)
     # ConvFusion: outer ReLU, query Linear, residual + 1x1 restore,
     # LeakyReLU, GroupNorm, 3x3 conv
-    dq_pre = relu_backward(masks["q"] if "q" in masks else f["q"], dq)
+    dq_pre = relu_backward(f["q"], dq)
     dxt, dw_q, db_q = linear_backward(f["xt"], w["w_q"], dq_pre)
     dact, dw_cf2, db_cf2 = linear_backward(f["cf_act"], w["w_cf2"], dxt)
-    # a boolean "act" mask maps to +1 (slope 1) / -1 (the small slope) for the sign test
-    act_sign = np.where(masks["act"], 1.0, -1.0) if "act" in masks else f["cf_act"]
-    da0 = leaky_relu_backward(act_sign, dact)
+    da0 = leaky_relu_backward(f["cf_act"], dact)
     dxc, dgamma, dbeta = group_norm_backward(grid(f["xc"]), G, w["gn_gamma"], grid(da0))
     dx_c, dw_cf1, db_cf1 = conv3x3_backward(grid(x), w["w_cf1"], dxc)
     dx = dxt + tok(dx_c) + dx_k + dx_v

@@ -1,21 +1,25 @@
 """GPU parity of the layer backward (edit_attn_backward) against the
 float64 oracle backward, through the C ABI.
 
-A forward fills the workspace, the backward reads it; dx and all 18
-parameter gradients are compared with oracle.edit_backward on the same
-seeded inputs and upstream gradient. Outputs and scratch are NaN-filled
-first.
+A forward fills the workspace, the backward reads it; outputs and scratch are
+NaN-filled first. Two comparisons per case:
 
-The backward passes three kinks (the queries' ReLU, the keys' ReLU, the
-LeakyReLU after GroupNorm). Where a pre-activation lies within the GPU
-forward's rounding of zero, the GPU and a float64 forward can fall on
-opposite sides, and that gradient element then moves by a whole upstream
-value (about 2-6% normwise in bf16 for every gradient behind a kink). The
-oracle therefore takes its kink decisions from the GPU's own stored forward
-values (q > 0, K' > 0, act >= 0, read from the forward workspace): both sides
-then differentiate the same branch, and every tensor is gated max-relative,
-max |g - o| / max |o| <= 1e-4 (fp32) and <= 2e-2 (bf16). The normwise error
-against the oracle's own decisions is printed beside it as a diagnostic.
+- step by step (tests/_bwd_steps.py): every chain-rule step of the backward
+  -- the output Linear, the linear-attention apply, the per-head sums, the
+  depthwise convs, the key/value Linears, the query Linear and the 1x1
+  restore, LeakyReLU + GroupNorm, the 3x3 conv -- is the oracle's step
+  function fed the inputs that step had on the GPU (the forward tensors in
+  the forward workspace, the upstream gradient the previous GPU step left in
+  the backward workspace). Every intermediate gradient, dx and all 18
+  parameter gradients are gated max-relative, max |g - o| / max |o| <= 1e-4
+  (fp32) and <= 2e-2 (bf16). Fed the GPU's own inputs, no step inherits
+  another's rounding, and both sides take the same kink decisions (R28);
+- end to end: dx and the parameter gradients against the oracle's own
+  float64 forward and backward, normwise ||g - o|| / ||o|| <= 1e-3 (fp32) and
+  <= 1e-1 (bf16) (R29). In bf16 a pre-activation within rounding of zero can
+  take the other side of its kink, and the key gradients cancel ~25-fold
+  (dK' = V' dS^T + dz), so the bf16 forward's rounding alone moves some
+  gradients by a few percent there.
 """
 import numpy as np
 import pytest
@@ -25,6 +29,7 @@ from oracle import edit_backward as OB
 from seeded_inputs import CONFIGS, make_inputs, make_shape
 from seeded_inputs import round_to_bf16
 from tests._metrics import BF16_TOL, F32_TOL, max_rel_err, norm_rel_err
+from tests import _bwd_steps as BS
 
 pytestmark = pytest.mark.gpu
 
@@ -57,8 +62,8 @@ F32_PIXART1024 = make_shape(B=2, H=64, W=64, C=1152, heads=16, head_dim=72, redu
 
 
 def run_backward(s, inp, dout):
-    """GPU forward + backward; returns the gradients and the kink decisions
-    the GPU forward took (from its stored q, K' and act)."""
+    """GPU forward + backward; returns the gradients, the forward tensors the
+    GPU stored and the backward's intermediate gradients."""
     x = G.to_dev(inp["x"], s.dtype)
     w = G.dev_weights(inp["w"], s.dtype)
     y = torch.empty_like(x)
@@ -75,9 +80,11 @@ def run_backward(s, inp, dout):
     torch.cuda.synchronize()
     out = {"x": dx.float().cpu().numpy()}
     out.update({n: t.float().cpu().numpy() for n, t in grads.items()})
-    fwd = G.read_intermediates(s, fws)
-    masks = {"q": fwd["q"] > 0, "kc": fwd["kc"] > 0, "act": fwd["cf_act"] >= 0}
-    return out, masks
+    T = G.TORCH_DTYPE[s.dtype]
+    return out, BS.read_forward(lca, s, fws, torch, T), BS.read_backward(lca, s, ws, torch, T)
+
+
+END_TO_END_NORMWISE = {"f32": 1e-3, "bf16": 1e-1}
 
 
 def check_backward(s, seed=0):
@@ -87,31 +94,26 @@ def check_backward(s, seed=0):
     if s.dtype == "bf16":
         dout = round_to_bf16(dout)
     print(f"\n[gpu-case] backward {s} seed={seed}", flush=True)
-    got, masks = run_backward(s, inp, dout)
-    dx, grads = OB.edit_attn_backward(inp["x"], inp["w"], s, dout, masks=masks)
-    ref = {"x": dx, **grads}
-    # diagnostic only: the oracle's own kink decisions
-    tr = {}
-    dx0, grads0 = OB.edit_attn_backward(inp["x"], inp["w"], s, dout, trace=tr)
-    own = {"x": dx0, **grads0}
-    f = tr["forward"]
-    flips = {"q": int((masks["q"] != (f["q"] > 0)).sum()), "kc": int((masks["kc"] != (f["kc"] > 0)).sum()),
-             "act": int((masks["act"] != (f["cf_act"] >= 0)).sum())}
+    got, fwd, bwd = run_backward(s, inp, dout)
     tol = F32_TOL if s.dtype == "f32" else BF16_TOL
-    errs, bad = {}, {}
-    for k, r in ref.items():
-        g = got[k]
+    bad = {}
+    step = {}
+    for k, (g, r) in BS.step_pairs(s, inp["x"], inp["w"], dout, fwd, bwd, got).items():
         assert g.shape == r.shape, (k, g.shape, r.shape)
         assert np.isfinite(g).all(), f"{k}: non-finite elements (unwritten or overflow)"
-        e = max_rel_err(g, r)
-        errs[k] = (e, norm_rel_err(g, own[k]))
-        if not e <= tol:
-            bad[k] = e
-    print("kink decisions that differ from the float64 forward:", flips)
-    print("max-rel (GPU kink decisions) / normwise (float64 decisions):",
-          {k: f"{a:.2e}/{b:.2e}" for k, (a, b) in errs.items()}, flush=True)
-    assert not bad, f"over tolerance {tol}: {bad}"
-    return errs
+        step[k] = max_rel_err(g, r)
+        if not step[k] <= tol:
+            bad[k] = ("step max-rel", step[k])
+    dx0, grads0 = OB.edit_attn_backward(inp["x"], inp["w"], s, dout)
+    e2e = {}
+    for k, r in {"x": dx0, **grads0}.items():
+        e2e[k] = norm_rel_err(got[k], r)
+        if not e2e[k] <= END_TO_END_NORMWISE[s.dtype]:
+            bad[k] = ("end-to-end normwise", e2e[k])
+    print("step max-rel:", {k: f"{v:.2e}" for k, v in step.items()}, flush=True)
+    print("end-to-end normwise:", {k: f"{v:.2e}" for k, v in e2e.items()}, flush=True)
+    assert not bad, f"over tolerance: {bad}"
+    return step, e2e
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
@@ -123,8 +125,8 @@ def test_backward_deterministic():
     s = SHAPES["bf16_ragged_c384"]
     inp = make_inputs(s, seed=4)
     dout = np.random.default_rng(4).standard_normal((s.B, s.N, s.C)).astype(np.float32)
-    a, _ = run_backward(s, inp, dout)
-    b, _ = run_backward(s, inp, dout)
+    a = run_backward(s, inp, dout)[0]
+    b = run_backward(s, inp, dout)[0]
     for k in a:
         assert np.array_equal(a[k], b[k]), k
 
