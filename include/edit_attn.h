@@ -113,6 +113,28 @@ edit_status_t edit_attn_forward(const edit_shape_t* shape, const edit_weights_t*
                                 const void* x, void* y,
                                 void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* Bytes of the static scratch edit_attn_forward_noalloc works in (256 MiB: the
+ * workspace of up to about 22 000 tokens at C = 1152 in bf16, e.g. the
+ * 128 x 128 grid). */
+#define EDIT_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/* edit_attn_forward for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument, and the call allocates nothing. Its
+ * intermediates live in a static array of EDIT_NOALLOC_SCRATCH_BYTES bytes in
+ * the library's code object, one per device, held from the first such call
+ * on that device until the process ends (its address is looked up on that
+ * first call, with the device current). Shapes whose workspace
+ * (edit_attn_workspace_size) exceeds the array return EDIT_ERR_WORKSPACE
+ * before anything is launched. Every step runs in order on hip_stream (no
+ * second stream, no events); the result equals edit_attn_forward's bit for
+ * bit. All calls on one device share the array and its contents after the
+ * last call: calls that overlap in time on one device race, so the caller
+ * serialises them (e.g. one stream per device). No part of the array needs
+ * to start at zero. Other arguments, checks and errors as edit_attn_forward. */
+edit_status_t edit_attn_forward_noalloc(const edit_shape_t* shape, const edit_weights_t* w,
+                                        const void* x, void* y, void* hip_stream);
+
 /* Bytes of workspace mmedit_hybrid_forward needs; 0 if invalid. */
 size_t mmedit_hybrid_workspace_size(const edit_shape_t* shape, int n_text);
 

@@ -20,7 +20,7 @@ __all__ = [
     "lib_path", "header_symbols", "QUERY_MODES", "KV_MODES", "KEY_CONVFUSION_FIELDS",
     "edit_attn_variant_workspace_size", "edit_attn_variant_workspace_layout", "edit_attn_variant_forward",
     "edit_attn_backward_workspace_size", "edit_attn_backward", "edit_attn_backward_workspace_layout",
-    "BWD_LAYOUT_FIELDS",
+    "BWD_LAYOUT_FIELDS", "edit_attn_forward_noalloc", "EDIT_NOALLOC_SCRATCH_BYTES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -97,6 +97,9 @@ def _load():
     lib.edit_attn_forward.argtypes = [P(_Shape), P(_Weights), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_size_t, ctypes.c_void_p]
     lib.edit_attn_forward.restype = ctypes.c_int
+    lib.edit_attn_forward_noalloc.argtypes = [P(_Shape), P(_Weights), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]
+    lib.edit_attn_forward_noalloc.restype = ctypes.c_int
     lib.mmedit_hybrid_forward.argtypes = [P(_Shape), ctypes.c_int, P(_Weights), P(_TextWeights), ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p]
@@ -239,6 +242,18 @@ def edit_attn_forward(shape, weights, x, y, workspace, stream=None) -> None:
 def edit_attn_backward_workspace_size(shape) -> int:
     """Scratch bytes edit_attn_backward needs beyond the forward's workspace."""
     return int(_lib.edit_attn_backward_workspace_size(ctypes.byref(_shape(shape))))
+
+
+def edit_attn_forward_noalloc(shape, weights, x, y, stream=None) -> None:
+    """edit_attn_forward without a workspace: the library's static per-device
+    scratch (EDIT_NOALLOC_SCRATCH_BYTES) holds the intermediates and the call
+    allocates nothing; overlapping calls on one device race."""
+    sh = _shape(shape)
+    w = _weights(weights)
+    _check(_lib.edit_attn_forward_noalloc(ctypes.byref(sh), ctypes.byref(w), _ptr(x), _ptr(y), _stream(stream)))
+
+
+EDIT_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 def edit_attn_backward_workspace_layout(shape) -> dict:

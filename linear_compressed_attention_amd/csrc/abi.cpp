@@ -35,6 +35,12 @@
 
 using edit::bf16;
 
+// Scratch of edit_attn_forward_noalloc: one array per device, in the code object, so that the call
+// itself allocates nothing. On the host the array's name is a stand-in, not device memory: host code
+// uses only the address static_scratch() looks up. Every no-allocation call on a device shares the
+// array, so such calls that overlap in time on one device race.
+static __device__ __align__(256) unsigned char scratch[EDIT_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -303,9 +309,11 @@ edit_status_t check_device() {
   } while (0)
 
 // Records events[i] on the stream when per-step timing was asked for.
+// serial: every step on the caller's stream even without events (no second stream).
 struct Marks {
   void* const* ev;
   hipStream_t s;
+  bool serial = false;
   hipError_t mark(int i) const {
     return ev ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) : hipSuccess;
   }
@@ -439,6 +447,28 @@ edit_status_t side_stream(SideStream** out) {
   return EDIT_OK;
 }
 
+// The device address of the static scratch (above), looked up once per device (hipGetSymbolAddress
+// with that device current) and kept; host code passes only that address, never the array's name.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+edit_status_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= 64) return fail(EDIT_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(EDIT_ERR_HIP, "looking up the static scratch on device %d failed: %s", dev, hipGetErrorString(e));
+    if (misaligned(p, 256)) return fail(EDIT_ERR_HIP, "the static scratch is not 256-byte aligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return EDIT_OK;
+}
+
 // The image stream up to the linear-attention output y (steps 1-8 of the
 // layer; the ablation variants swap the query or the key/value processing).
 // The query branch (steps 1-4) and the key/value branch (steps 5-7) only
@@ -455,7 +485,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
   using namespace edit;
   auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  const bool fork = mk.ev == nullptr;
+  const bool fork = mk.ev == nullptr && !mk.serial;
 
   // 1-4. queries: q = ReLU((x + ConvFusion(x)) W_q^T + b_q), or ReLU(x W_q^T + b_q).
   // parts: which ConvFusion parts to queue; q_proj waits for `folded` on qs when it is given.
@@ -908,10 +938,12 @@ edit_status_t edit_attn_variant_workspace_layout(const edit_shape_t* shape, cons
   return EDIT_OK;
 }
 
+// workspace == nullptr with scratch_ws set: the static scratch (edit_attn_forward_noalloc), whose
+// device address is looked up only once the arguments have passed every check.
 static edit_status_t forward_impl(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
                                   void* workspace, size_t ws_bytes, void* hip_stream, void* const* events,
                                   const edit_variant_t* variant = nullptr,
-                                  const edit_convfusion_weights_t* kcf = nullptr) {
+                                  const edit_convfusion_weights_t* kcf = nullptr, bool scratch_ws = false) {
   Geometry g;
   edit_status_t st = check_shape(shape, 0, &g);
   if (st != EDIT_OK) return st;
@@ -920,19 +952,29 @@ static edit_status_t forward_impl(const edit_shape_t* shape, const edit_weights_
   if (g.kvmode == EDIT_KV_KEY_CONVFUSION && (st = check_convfusion_weights(kcf)) != EDIT_OK) return st;
   if ((st = check_ptr(x, "x")) != EDIT_OK) return st;
   if ((st = check_ptr(y, "y")) != EDIT_OK) return st;
-  if (!workspace) return fail(EDIT_ERR_ARG, "workspace is NULL");
-  if (misaligned(workspace, 256)) return fail(EDIT_ERR_ARG, "workspace is not 256-byte aligned");
   const Layout L = make_layout(g);
-  if (ws_bytes < L.total)
-    return fail(EDIT_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
   const size_t act = (size_t)g.M * g.C * g.es;
   if (overlap(y, act, x, act)) return fail(EDIT_ERR_ARG, "y overlaps x");
   if (overlaps_weight(y, act, w, g)) return fail(EDIT_ERR_ARG, "y overlaps a weight");
+  if (scratch_ws) {
+    if (L.total > EDIT_NOALLOC_SCRATCH_BYTES)
+      return fail(EDIT_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu", L.total,
+                  (size_t)EDIT_NOALLOC_SCRATCH_BYTES);
+    if ((st = check_device()) != EDIT_OK) return st;
+    if ((st = static_scratch(&workspace)) != EDIT_OK) return st;
+    ws_bytes = EDIT_NOALLOC_SCRATCH_BYTES;
+  } else {
+    if (!workspace) return fail(EDIT_ERR_ARG, "workspace is NULL");
+    if (misaligned(workspace, 256)) return fail(EDIT_ERR_ARG, "workspace is not 256-byte aligned");
+    if (ws_bytes < L.total)
+      return fail(EDIT_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+    if ((st = check_device()) != EDIT_OK) return st;
+  }
   if (overlap(y, act, workspace, ws_bytes)) return fail(EDIT_ERR_ARG, "y overlaps the workspace");
   if (overlap(x, act, workspace, ws_bytes)) return fail(EDIT_ERR_ARG, "x overlaps the workspace");
-  if ((st = check_device()) != EDIT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const Marks mk{events, s};
+  Marks mk{events, s};
+  mk.serial = scratch_ws;
   return g.dtype == EDIT_BF16 ? run_edit<bf16>(g, L, w, x, y, workspace, s, mk, kcf)
                               : run_edit<float>(g, L, w, x, y, workspace, s, mk, kcf);
 }
@@ -940,6 +982,11 @@ static edit_status_t forward_impl(const edit_shape_t* shape, const edit_weights_
 edit_status_t edit_attn_forward(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
                                 void* workspace, size_t ws_bytes, void* hip_stream) {
   return forward_impl(shape, w, x, y, workspace, ws_bytes, hip_stream, nullptr);
+}
+
+edit_status_t edit_attn_forward_noalloc(const edit_shape_t* shape, const edit_weights_t* w, const void* x, void* y,
+                                        void* hip_stream) {
+  return forward_impl(shape, w, x, y, nullptr, 0, hip_stream, nullptr, nullptr, nullptr, true);
 }
 
 edit_status_t edit_attn_variant_forward(const edit_shape_t* shape, const edit_variant_t* variant,

@@ -258,3 +258,34 @@ def test_forward_output_overlapping_a_weight_rejected():
     with pytest.raises(lca.EditError) as e:
         _call(y=_fake_weights()["w_q"])
     assert e.value.status == 1 and "weight" in e.value.detail
+
+
+def test_noalloc_rejects_a_shape_beyond_the_static_scratch():
+    """edit_attn_forward_noalloc checks the shape's workspace against its static scratch before it
+    touches a device (65536 tokens at C = 1152 need ~760 MB)."""
+    s = CONFIGS["pixart4096"]
+    assert lca.edit_attn_workspace_size(s) > lca.EDIT_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_forward_noalloc(s, _fake_weights(), 0x10000000000, 0x20000000000, stream=0)
+    assert e.value.status == 3 and "static scratch" in e.value.detail
+
+
+def test_noalloc_argument_errors_before_any_launch():
+    w = _fake_weights()
+    w["w_k"] = None
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_forward_noalloc(SHAPE, w, 0x9000000, 0xA000000, stream=0)
+    assert e.value.status == 1 and "w_k" in e.value.detail
+    with pytest.raises(lca.EditError) as e:
+        lca.edit_attn_forward_noalloc(SHAPE, _fake_weights(), 0x9000000, 0x9000000 + 64, stream=0)
+    assert e.value.status == 1 and "overlap" in e.value.detail
+
+
+def test_noalloc_scratch_bound_matches_the_header():
+    import os
+    import re
+    with open(os.path.join(os.path.dirname(os.path.dirname(lca.lib_path())), "include", "edit_attn.h")) as f:
+        m = re.search(r"#define EDIT_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == lca.EDIT_NOALLOC_SCRATCH_BYTES
+    # the 128 x 128, C = 1152 bf16 layer fits
+    assert lca.edit_attn_workspace_size(CONFIGS["pixart2048"]) <= lca.EDIT_NOALLOC_SCRATCH_BYTES
