@@ -40,8 +40,9 @@ STEP_KERNELS = {  # kernels launched per step at bf16 (rocprofv3 names start wit
     "gn_stats": "gn_finalize_channels_kernel",
     "cf_act": "gn_apply_kernel",
     "q_proj": "gemm_dma_kernel<128, 192, 2, 2, A_CAT2, E_BIAS_RELU>",
-    "kv_proj": "gemm_dma_kernel<128, 192, 2, 2, A_PLAIN, E_BIAS>", "sc_dwconv": "dwconv_s2_kernel",
-    "kv_state": "kv_state_partial_kernel + kv_state_finalize_kernel", "linattn_apply": "linattn_apply_kernel",
+    "kv_proj": "gemm_dma_kernel<128, 192, 2, 2, A_PLAIN, E_BIAS>",
+    "sc_dwconv": "dwconv_kv_state_kernel (the depthwise convs and the state partials)",
+    "kv_state": "kv_state_finalize_kernel", "linattn_apply": "linattn_apply_kernel",
     "out_proj": "gemm_dma_kernel<128, 192, 2, 2, A_PLAIN, E_BIAS>",
 }
 
@@ -81,6 +82,14 @@ def algorithmic_work(s):
         stats = (3.0 * tiles * Cr, 8 * tiles * Cr)
     else:
         act = (act[0] + fold[0], act[1] + fold[1])
+    dw = (2.0 * 9 * Mc * 2 * C, es * (2 * M * C + 2 * Mc * C + 2 * 10 * C))
+    state = (2.0 * Mc * C * (d + 1), es * 2 * Mc * C + st)
+    if s.dtype == "bf16":
+        # one pass makes K', V' and the state partials (K', V' are not read back); the kv_state step
+        # merges the per-(head, 256-token chunk) partials
+        parts = B * h * ((s.Nc + 255) // 256) * (16 * ((d + 16) // 16)) * (16 * ((d + 15) // 16)) * 4
+        dw = (dw[0] + state[0], dw[1] + st)
+        state = (float(parts) / 4, parts + st)
     return {
         "cf_conv3x3": conv,
         "gn_stats": stats,
@@ -89,8 +98,8 @@ def algorithmic_work(s):
         # ReLU([X | act] [W_q | W_q W_cf2]^T + b)
         "q_proj": (2.0 * M * C * (C + Cr), es * (M * C + M * Cr + M * C + C * (C + Cr) + C)),
         "kv_proj": (2.0 * M * 2 * C * C, es * (M * C + 2 * M * C + 2 * C * C + 2 * C)),
-        "sc_dwconv": (2.0 * 9 * Mc * 2 * C, es * (2 * M * C + 2 * Mc * C + 2 * 10 * C)),
-        "kv_state": (2.0 * Mc * C * (d + 1), es * 2 * Mc * C + st),
+        "sc_dwconv": dw,
+        "kv_state": state,
         "linattn_apply": (2.0 * M * C * (d + 1), es * 2 * M * C + st),
         "out_proj": (2.0 * M * C * C, es * (2 * M * C + C * C + C)),
     }

@@ -515,7 +515,18 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
       a.seg_rows = g.C; a.ldb = g.C; a.C = P(L.kv0); a.ldc = 2 * g.C; a.spread = fork;
       EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, ks));
       EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
-      // 6. compressed keys / values
+      // 6. compressed keys / values (bf16: with the state partials of step 7 in the same pass)
+      if constexpr (std::is_same<T, bf16>::value) {
+        EDIT_LAUNCH(launch_dwconv_kv_state<T>(P(L.kv0), g.B, g.H, g.W, g.C, g.heads, g.d,
+                                              static_cast<const T*>(w->dw_k), static_cast<const T*>(w->db_k),
+                                              static_cast<const T*>(w->dw_v), static_cast<const T*>(w->db_v),
+                                              P(L.kc), P(L.vc), F(L.kv_part), ks));
+        EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_STATE));
+        // 7. the per-head state: the chunk partials merged
+        EDIT_LAUNCH(launch_kv_state_finalize<T>(F(L.kv_part), g.B, g.heads, g.d, g.kv_chunks, F(L.S), F(L.z),
+                                                P(L.st), F(L.zp), ks));
+        return EDIT_OK;
+      }
       EDIT_LAUNCH(launch_dwconv_s2<T>(P(L.kv0), g.B, g.H, g.W, g.C, static_cast<const T*>(w->dw_k),
                                       static_cast<const T*>(w->db_k), static_cast<const T*>(w->dw_v),
                                       static_cast<const T*>(w->db_v), P(L.kc), P(L.vc), ks));

@@ -187,6 +187,161 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// The Spatial Compressor's depthwise 3x3 stride-2 convs and the state
+// partials in one kernel (sections "Spatial Compressor" and
+// "Linear-attention formula"): a block makes the compressed keys and values
+// of one head over one 256-token chunk, K' = ReLU(DW(k0) + b_k) and
+// V' = DW(v0) + b_v, writes them (kc, vc: the backward and the hybrid read
+// them), and, with the values still on chip, their chunk partial of
+// S^T = V'^T K' and z = sum K' on the matrix cores, the same partial
+// kv_state_partial_kernel writes from kc, vc (so kv_state_finalize_kernel
+// merges them unchanged). The compressed tensors are not read back.
+// Item e of a block: channel chunk c8 (fastest, so a token's head slice is
+// one contiguous run across lanes), token quad, K or V; an item convolves
+// four consecutive compressed tokens (each from its nine taps, loads at
+// clamped in-image positions, taps outside the image adding zero) and
+// writes them to LDS as one four-token word per channel, channel-major with
+// the kv_col swizzle, as kv_state_partial_kernel stages them.
+// ---------------------------------------------------------------------------
+constexpr int kDwStateThreads = 512;   // 8 waves: two per SIMD overlap one another's loads
+
+// Two tokens' values of one channel, written to LDS as one 4-byte word.
+__device__ __forceinline__ void store_pair(bf16* dst, bf16 a, bf16 b) {
+  bf16 v[2] = {a, b};
+  *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(v);
+}
+
+template <typename T, int DC>
+__global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
+    const T* __restrict__ kv0, int H, int W, int heads, int nchunks, const T* __restrict__ dwk,
+    const T* __restrict__ dbk, const T* __restrict__ dwv, const T* __restrict__ dbv, T* __restrict__ kc,
+    T* __restrict__ vc, float* __restrict__ partial) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  constexpr int NTH = kDwStateThreads;
+  constexpr int d = 8 * DC;
+  constexpr int DT = (d + 15) / 16, DR = (d + 16) / 16;
+  constexpr int SLAB = kKvChunk;
+  constexpr int PITCH = SLAB + 8;
+  constexpr int NT = DR * DT;
+  constexpr int NW = NTH / 64;
+  constexpr int TPW = (NT + NW - 1) / NW;
+  constexpr int PAIRS = SLAB / 2;
+  constexpr int ITEMS = 2 * PAIRS * DC;
+  static_assert(SLAB % 64 == 0, "kv_col swizzles within groups of 8 chunks of 8 columns");
+  __shared__ __attribute__((aligned(16))) T Kt[16 * DT * PITCH];
+  __shared__ __attribute__((aligned(16))) T At[16 * DR * PITCH];
+  const int Hc = (H + 1) / 2, Wc = (W + 1) / 2, Nc = Hc * Wc, C = heads * d;
+  const int lb = xcd_swizzle((int)blockIdx.x, (int)gridDim.x);
+  const int h = lb % heads, chunk = (lb / heads) % nchunks, b = lb / heads / nchunks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = chunk * kKvChunk, j1 = min(Nc, j0 + kKvChunk);
+  const T* img = kv0 + (size_t)b * H * W * 2 * C;
+
+  // rows that receive no token data: K' channels d .. 16 DT - 1, and the rows
+  // of A past V'^T and the two weight rows (ones, zeros: z = sum K')
+  {
+    const u32x4v zero = {0u, 0u, 0u, 0u};
+    constexpr int W16 = PITCH * (int)sizeof(T) / 16;
+    for (int i = tid; i < (16 * DT - d) * W16; i += NTH) reinterpret_cast<u32x4v*>(Kt + d * PITCH)[i] = zero;
+    for (int i = tid; i < (16 * DR - d - 2) * W16; i += NTH) reinterpret_cast<u32x4v*>(At + (d + 2) * PITCH)[i] = zero;
+    for (int t = tid; t < SLAB; t += NTH) {
+      At[d * PITCH + kv_col(d, t)] = from_f32<T>(j0 + t < j1 ? 1.0f : 0.0f);
+      At[(d + 1) * PITCH + kv_col(d + 1, t)] = from_f32<T>(0.0f);
+    }
+  }
+
+  for (int e = tid; e < ITEMS; e += NTH) {
+    const int c8 = (e % DC) * 8, rest = e / DC;
+    const int tp = rest % PAIRS, which = rest / PAIRS;   // which: 0 keys, 1 values
+    const int cin = which * C + h * d + c8;              // channel in kv0's [k0 | v0] row
+    const T* wt = (which ? dwv : dwk) + h * d + c8;
+    // Every load of the item (nine taps of two tokens, the taps' weights and
+    // the bias) is issued before any is used.
+    u32x4v raw[2][9];
+    int yo[2], xo[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = min(j0 + 2 * tp + u, j1 - 1);        // tokens past the chunk: recomputed, then zeroed
+      yo[u] = j / Wc;
+      xo[u] = j - yo[u] * Wc;
+#pragma unroll
+      for (int t = 0; t < 9; ++t) {
+        const int yc = min(max(2 * yo[u] + t / 3 - 1, 0), H - 1), xc = min(max(2 * xo[u] + t % 3 - 1, 0), W - 1);
+        raw[u][t] = *reinterpret_cast<const u32x4v*>(img + ((size_t)yc * W + xc) * 2 * C + cin);
+      }
+    }
+    float wv[9][8], o[2][8];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) load8(wt + t * C, wv[t]);
+    load8((which ? dbv : dbk) + h * d + c8, o[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[1][i] = o[0][i];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = j0 + 2 * tp + u;
+#pragma unroll
+      for (int t = 0; t < 9; ++t) {
+        const int yy = 2 * yo[u] + t / 3 - 1, xx = 2 * xo[u] + t % 3 - 1;
+        const bool in = yy >= 0 && yy < H && xx >= 0 && xx < W;
+        const T* v = reinterpret_cast<const T*>(&raw[u][t]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[u][i] += in ? wv[t][i] * to_f32(v[i]) : 0.0f;
+      }
+      if (!which) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[u][i] = o[u][i] > 0.0f ? o[u][i] : 0.0f;
+      }
+      if (j < j1) {
+        store8((which ? vc : kc) + ((size_t)b * Nc + j) * C + h * d + c8, o[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[u][i] = 0.0f;
+      }
+    }
+    // the state uses the values as stored
+    T* dst = which ? At : Kt;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = c8 + i;
+      store_pair(dst + row * PITCH + kv_col(row, 2 * tp), from_f32<T>(o[0][i]), from_f32<T>(o[1][i]));
+    }
+  }
+  __syncthreads();
+
+  typedef typename Frag<T>::type FragT;
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc_zero(acc[t]);
+#pragma unroll
+  for (int ks = 0; ks < SLAB / 32; ++ks) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int tile = wave + NW * t;
+      if (tile < NT) {
+        const int tr = tile / DT, tc = tile % DT;
+        FragT a, bb;
+        const int ra = tr * 16 + fr, rk = tc * 16 + fr;
+        frag_load(a, At + ra * PITCH + kv_col(ra, ks * 32 + fk));
+        frag_load(bb, Kt + rk * PITCH + kv_col(rk, ks * 32 + fk));
+        mma16(acc[t], a, bb);
+      }
+    }
+  }
+  float* out = partial + (((size_t)b * heads + h) * nchunks + chunk) * (16 * DR) * (16 * DT);
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int tile = wave + NW * t;
+    if (tile < NT) {
+      const int tr = tile / DT, tc = tile % DT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        out[(tr * 16 + (lane >> 4) * 4 + r) * (16 * DT) + tc * 16 + (lane & 15)] = acc[t][r];
+    }
+  }
+}
+
 // Sum the chunk partials in chunk order and emit S (f32, [d][d] as S[k][n]),
 // z (f32), the apply kernel's operand st[2][DP][DK] (rows n, K = k: S^T,
 // padded with zeros; bf16 keeps a hi and a lo part so hi + lo carries ~16
@@ -229,6 +384,17 @@ __global__ __launch_bounds__(256) void kv_state_finalize_kernel(const float* __r
 }
 
 template <typename T>
+hipError_t launch_kv_state_finalize(const float* partial, int B, int heads, int d, int nchunks, float* S, float* z,
+                                    T* st, float* zp, hipStream_t s) {
+  const int DT = (d + 15) / 16, DR = (d + 16) / 16;
+  const int DP = 16 * DT, DK = 32 * ((DT + 1) / 2);
+  dim3 fgrid((DP * DK + DK + 255) / 256, heads, B);
+  hipLaunchKernelGGL((kv_state_finalize_kernel<T>), fgrid, dim3(256), 0, s, partial, heads, d, DR, DT, nchunks, S,
+                     z, st, zp);
+  return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int heads, int d, float* partial,
                            int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s, const float* wrow) {
   const int DT = (d + 15) / 16, DR = (d + 16) / 16;
@@ -254,11 +420,34 @@ hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int DP = 16 * DT, DK = 32 * ((DT + 1) / 2);
-  dim3 fgrid((DP * DK + DK + 255) / 256, heads, B);
-  hipLaunchKernelGGL((kv_state_finalize_kernel<T>), fgrid, dim3(256), 0, s, partial, heads, d, DR, DT, nchunks, S,
-                     z, st, zp);
-  return hipGetLastError();
+  return launch_kv_state_finalize<T>(partial, B, heads, d, nchunks, S, z, st, zp, s);
+}
+
+template <typename T>
+hipError_t launch_dwconv_kv_state(const T* kv0, int B, int H, int W, int C, int heads, int d, const T* dwk,
+                                  const T* dbk, const T* dwv, const T* dbv, T* kc, T* vc, float* partial,
+                                  hipStream_t s) {
+  if constexpr (sizeof(T) != 2) {
+    return hipErrorNotSupported;   // fp32 keeps the two-kernel form (slabs of 64 tokens)
+  } else {
+    if (C != heads * d) return hipErrorInvalidValue;
+    const int Nc = ((H + 1) / 2) * ((W + 1) / 2), nchunks = kv_state_chunks(Nc);
+    if ((long long)nchunks * heads * B >= (1LL << 31)) return hipErrorInvalidValue;
+    dim3 grid(nchunks * heads * B);
+    switch (d / 8) {
+#define EDIT_DKV_CASE(DCV)                                                                                   \
+  case DCV:                                                                                                  \
+    hipLaunchKernelGGL((dwconv_kv_state_kernel<T, DCV>), grid, dim3(kDwStateThreads), 0, s, kv0, H, W, heads, \
+                       nchunks, dwk, dbk, dwv, dbv, kc, vc, partial);                                        \
+    break;
+      EDIT_DKV_CASE(1) EDIT_DKV_CASE(2) EDIT_DKV_CASE(3) EDIT_DKV_CASE(4) EDIT_DKV_CASE(5) EDIT_DKV_CASE(6)
+      EDIT_DKV_CASE(7) EDIT_DKV_CASE(8) EDIT_DKV_CASE(9) EDIT_DKV_CASE(10) EDIT_DKV_CASE(11) EDIT_DKV_CASE(12)
+      EDIT_DKV_CASE(13) EDIT_DKV_CASE(14) EDIT_DKV_CASE(15) EDIT_DKV_CASE(16)
+#undef EDIT_DKV_CASE
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -715,6 +904,10 @@ hipError_t launch_sdpa(const SdpaArgs<T>& a0, hipStream_t s) {
 #define EDIT_INST(T)                                                                                     \
   template hipError_t launch_kv_state<T>(const T*, const T*, int, int, int, int, int, float*, int, float*, \
                                          float*, T*, float*, hipStream_t, const float*);                              \
+  template hipError_t launch_dwconv_kv_state<T>(const T*, int, int, int, int, int, int, const T*, const T*,       \
+                                                const T*, const T*, T*, T*, float*, hipStream_t);                 \
+  template hipError_t launch_kv_state_finalize<T>(const float*, int, int, int, int, float*, float*, T*, float*,   \
+                                                  hipStream_t);                                                   \
   template hipError_t launch_linattn_apply<T>(const T*, int, const T*, const float*, int, int, int, int, \
                                               float, T*, int, float*, hipStream_t);                     \
   template hipError_t launch_sdpa<T>(const SdpaArgs<T>&, hipStream_t);

@@ -44,11 +44,18 @@ def test_conv_flops(work):
 
 
 def test_memory_bound_bytes(work):
-    assert work["sc_dwconv"][1] == BF * (M * 2 * C + 2 * NC * C) + BF * 2 * (9 * C + C)
+    # bf16: kv0 in, K' and V' out, the depthwise weights, the per-head state out (K', V' not read back)
+    st = S.B * S.heads * (S.head_dim ** 2 + S.head_dim) * 4
+    assert work["sc_dwconv"][1] == BF * (M * 2 * C + 2 * NC * C) + BF * 2 * (9 * C + C) + st
     # q in, y out; the per-head operand and z are a rounding error beside them
     assert work["linattn_apply"][1] == pytest.approx(BF * 2 * M * C, rel=0.01)
-    # K' and V' in, the per-head state out
-    assert work["kv_state"][1] == pytest.approx(BF * 2 * NC * C, rel=0.02)
+    # the merge of the 16 chunk partials (80 x 80 fp32 each) of the 16 heads, and the state out
+    assert work["kv_state"][1] == 16 * 16 * 80 * 80 * 4 + st
+    # fp32: the two passes of the design (K', V' written, then read by the state)
+    w32 = bench.algorithmic_work(CONFIGS["tiny"])
+    t = CONFIGS["tiny"]
+    nc = t.B * t.Nc
+    assert w32["kv_state"][1] == 4 * 2 * nc * t.C + t.B * t.heads * (t.head_dim ** 2 + t.head_dim) * 4
 
 
 def test_layer_floor():
