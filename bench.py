@@ -48,9 +48,13 @@ STEP_KERNELS = {  # kernels launched per step at bf16 (rocprofv3 names start wit
 
 
 def gn_tile_rows(s):
-    """Rows per statistics tile of the conv's epilogue: 256, or 128 where
-    256-row tiles would fill fewer than half of the 256 CUs (the library's
-    rule)."""
+    """Rows per statistics tile of the conv's epilogue (the library's rule):
+    256 where the conv runs on the kernel-row kernel (bf16, H*W a multiple of
+    256, W of 32..128 or a multiple of 256); else 256, or 128 where 256-row
+    tiles would fill fewer than half of the 256 CUs."""
+    if s.dtype == "bf16" and s.N % 256 == 0 and s.C % 64 == 0 and s.Cr % 96 == 0 and \
+            (s.W in (32, 64, 128) or s.W % 256 == 0):
+        return 256
     return 128 if (s.B * s.N // 256) * (s.Cr // 96) < 128 and s.N % 128 == 0 else 256
 
 

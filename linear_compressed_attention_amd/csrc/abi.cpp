@@ -140,9 +140,14 @@ edit_status_t apply_variant(const edit_variant_t* v, Geometry* g) {
 
 // The bf16 conv computes the GroupNorm partial statistics in its epilogue when its row tiles never
 // straddle two samples (H*W a multiple of the tile height) and it runs on the direct-load kernel (C a
-// multiple of 64, C/r of 96); otherwise a separate pass over xc does. Tiles are 256 rows, or 128 where
-// 256-row tiles (x C/r / 96 column tiles) would fill fewer than half of an MI355X's 256 CUs.
+// multiple of 64, C/r of 96); otherwise a separate pass over xc does. Tiles are 256 rows on the
+// kernel-row conv; on the tap-streaming conv 256, or 128 where 256-row tiles (x C/r / 96 column tiles)
+// would fill fewer than half of an MI355X's 256 CUs.
 int gn_tile_rows(const Geometry& g) {
+  // the kernel-row conv (conv_halo.hip) takes 256-row tiles of whole image rows or row segments
+  const bool rows_conv = g.es == 2 && g.N % 256 == 0 && g.C % 64 == 0 && g.Cr % 96 == 0 &&
+                         (g.W == 32 || g.W == 64 || g.W == 128 || g.W % 256 == 0);
+  if (rows_conv) return 256;
   const long tiles256 = (long)(g.M / 256) * (g.Cr / 96);
   return tiles256 < 128 && g.N % 128 == 0 ? 128 : 256;
 }

@@ -338,10 +338,6 @@ static hipError_t launch_tiles(const GemmArgs<T>& a, AMode am, EMode em, hipStre
   return hipErrorInvalidValue;
 }
 
-#ifndef EDIT_GEMM_FORCE
-#define EDIT_GEMM_FORCE 0
-#endif
-
 template <typename T>
 hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
@@ -373,13 +369,6 @@ hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s) 
   if constexpr (std::is_same<T, bf16>::value) {
     const hipError_t e = launch_gemm_dma(a, am, em, s);
     if (e != hipErrorNotSupported) return e;
-  }
-  switch (EDIT_GEMM_FORCE) {
-    case 1: return launch_tiles<T, 128, 96, 2, 2, 2, 1, 0, 16>(a, am, em, s);
-    case 2: return launch_tiles<T, 128, 96, 2, 2, 1, 1, 0, 16>(a, am, em, s);
-    case 3: return launch_tiles<T, 128, 144, 2, 1, 2, 1, 0, 16>(a, am, em, s);
-    case 4: return launch_tiles<T, 128, 128, 2, 2, 1, 1, 0, 16>(a, am, em, s);
-    default: break;
   }
   // Tile choice (measured on MI355X at the 16384-token shapes; the loop is
   // bound by LDS traffic and latency, not by the matrix cores, so the

@@ -66,6 +66,12 @@ struct GemmArgs {
 template <typename T>
 hipError_t launch_gemm(const GemmArgs<T>& a, AMode am, EMode em, hipStream_t s);
 
+// The bf16 3x3 conv (A_CONV3, E_BIAS or E_BIAS_GN with 256-row statistics
+// tiles) on the halo-staged implicit GEMM (conv_halo.hip): H*W a multiple of
+// 256, W in {32, 64, 128} or a multiple of 256, C a multiple of 16, N of 96.
+// Returns hipErrorNotSupported, launching nothing, for other shapes.
+hipError_t launch_conv3x3_halo(const GemmArgs<bf16>& a, EMode em, hipStream_t s);
+
 // The bf16 GEMM with direct global-to-LDS loads (plain or 3x3-conv A, bias or
 // bias + ReLU epilogue). Returns hipErrorNotSupported, launching nothing, for
 // shapes it does not cover.

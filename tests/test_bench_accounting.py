@@ -70,6 +70,6 @@ def test_layer_floor():
 def test_statistics_tile_rows():
     # 256-row statistics tiles unless they would fill fewer than half the CUs
     assert bench.gn_tile_rows(CONFIGS["pixart2048"]) == 256
-    assert bench.gn_tile_rows(CONFIGS["pixart1024"]) == 128
+    assert bench.gn_tile_rows(CONFIGS["pixart1024"]) == 256   # W = 64: the kernel-row conv
     assert bench.stats_in_conv(CONFIGS["pixart1024"]) and bench.stats_in_conv(CONFIGS["pixart2048"])
     assert not bench.stats_in_conv(CONFIGS["tiny"])   # fp32: the separate statistics pass

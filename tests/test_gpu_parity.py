@@ -79,6 +79,12 @@ SMALL = {
                                      dtype="bf16", x_std=1.0),
     "bf16_gnrestore_k288": make_shape(B=1, H=16, W=16, C=1152, heads=16, head_dim=72, reduction=4, gn_groups=32,
                                       dtype="bf16", x_std=1.0),
+    # the halo-staged conv: 256-pixel tiles of whole rows (W = 32: eight rows, W = 64: four), two
+    # samples, C/r = 96 (one column tile) and 288 (three)
+    "bf16_halo_w32": make_shape(B=2, H=8, W=32, C=384, heads=4, head_dim=96, reduction=4, gn_groups=8,
+                                dtype="bf16", x_std=1.0),
+    "bf16_halo_w64_c1152": make_shape(B=2, H=4, W=64, C=1152, heads=16, head_dim=72, reduction=4, gn_groups=32,
+                                      dtype="bf16", x_std=1.0),
     "f32_1x1": make_shape(B=2, H=1, W=1, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
                           dtype="f32", x_std=1.0),
     "f32_1x5": make_shape(B=1, H=1, W=5, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
