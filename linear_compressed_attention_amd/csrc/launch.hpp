@@ -224,6 +224,8 @@ template <typename T>
 hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s);
 // Key splits for Nq queries over Nkeys keys: enough blocks for the chip
 // (about 2048) with at least four 32-key slabs per split, at most 32.
-int sdpa_splits(int Nq, int Nkeys, int heads, int B);
+// bf16 (staged): one split per sdpa_staged_keys(d) keys (the keys a block stages at once).
+int sdpa_splits(int Nq, int Nkeys, int heads, int B, int d, bool staged);
+int sdpa_staged_keys(int d);
 
 }  // namespace edit
