@@ -11,7 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libedit_attn.so")
-SOURCES = ["gemm.hip", "gemm_dma.hip", "conv_halo.hip", "fold.hip", "norm_dwconv.hip", "attention.hip", "backward.hip", "abi.cpp"]
+SOURCES = ["gemm.hip", "gemm_dma.hip", "conv_halo.hip", "fold.hip", "norm_dwconv.hip", "attention.hip", "sdpa_staged.hip",
+           "backward.hip", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -22,10 +23,15 @@ FLAGS = [
 ]
 
 
+# Per-source flags. The staged softmax kernel's max reductions see no NaN operands (finite scores, -inf for
+# masked keys): without NaN semantics they fold into v_max3 with no operand canonicalisation.
+EXTRA = {"sdpa_staged.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src, obj_dir):
     obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -77,7 +77,7 @@ struct Geometry {
 struct Layout {
   size_t xc, gn_part, gn_stat, gn_scale, gn_shift, cf_act, q_fold_w, q_fold_b, q, kv0, kc, vc, kv_part, S, z, st,
       zp, y;
-  size_t qkv_t, y_img, y_txt, lin_den, sdpa_part;
+  size_t qkv_t, y_img, y_txt, lin_den, sdpa_part_img, sdpa_part_txt;
   size_t xc_k, gn_part_k, gn_stat_k, gn_scale_k, gn_shift_k, cf_act_k, k_fold_w, k_fold_b;   // key ConvFusion branch
   size_t total;
 };
@@ -203,13 +203,13 @@ Layout make_layout(const Geometry& g) {
     L.y_img = take(M * g.C * es);
     L.y_txt = take((size_t)g.B * g.nt * g.C * es);
     L.lin_den = take((size_t)g.B * g.N * g.heads * 4);
-    // the softmax blocks' key-split partials (image rows, then text rows, one buffer)
+    // the softmax blocks' key-split partials, image rows and text rows apart (bf16 runs both at once); none
+    // for a block that takes all its keys in one split
     const bool staged = g.es == 2;
-    const size_t pi = (size_t)edit::sdpa_splits(g.N, g.nt, g.heads, g.B, g.d, staged) * g.B * g.heads * g.N *
-                      (g.d + 2) * 4;
-    const size_t pt = (size_t)edit::sdpa_splits(g.nt, g.Nc + g.nt, g.heads, g.B, g.d, staged) * g.B * g.heads *
-                      g.nt * (g.d + 2) * 4;
-    L.sdpa_part = take(pi > pt ? pi : pt);
+    const int si = edit::sdpa_splits(g.N, g.nt, g.heads, g.B, g.d, staged);
+    const int st = edit::sdpa_splits(g.nt, g.Nc + g.nt, g.heads, g.B, g.d, staged);
+    L.sdpa_part_img = take(si > 1 ? (size_t)si * g.B * g.heads * g.N * (g.d + 2) * 4 : 0);
+    L.sdpa_part_txt = take(st > 1 ? (size_t)st * g.B * g.heads * g.nt * (g.d + 2) * 4 : 0);
   }
   L.total = off;
   return L;
@@ -653,8 +653,7 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   sa.out = P(L.y_img); sa.ldo = C;
   sa.blend_src = P(L.y); sa.ldbs = C; sa.alpha = eta; sa.beta = 1.0f - eta; sa.lin_den = lin_den;
   sa.splits = sdpa_splits(g.N, g.nt, g.heads, g.B, g.d, g.es == 2);
-  sa.part = reinterpret_cast<float*>(wsb + L.sdpa_part);
-  EDIT_LAUNCH(launch_sdpa<T>(sa, s));
+  sa.part = sa.splits > 1 ? reinterpret_cast<float*>(wsb + L.sdpa_part_img) : nullptr;
   // Text rows: softmax over [K'_I ; K_T] with values [V'_I ; V_T].
   SdpaArgs<T> ta{};
   ta.q = qkv; ta.ldq = 3 * C; ta.Nq = g.nt;
@@ -664,8 +663,9 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   ta.out = P(L.y_txt); ta.ldo = C;
   ta.blend_src = nullptr; ta.ldbs = 0; ta.alpha = 0.0f; ta.beta = 1.0f; ta.lin_den = nullptr;
   ta.splits = sdpa_splits(g.nt, g.Nc + g.nt, g.heads, g.B, g.d, g.es == 2);
-  ta.part = reinterpret_cast<float*>(wsb + L.sdpa_part);
-  EDIT_LAUNCH(launch_sdpa<T>(ta, s));
+  ta.part = ta.splits > 1 ? reinterpret_cast<float*>(wsb + L.sdpa_part_txt) : nullptr;
+  // text rows first: their key splits are the longer blocks of work, started before the image tiles
+  EDIT_LAUNCH(launch_sdpa_pair<T>(ta, sa, s));
 
   st = out_linear<T>(g.M, C, w->w_o, w->b_o, P(L.y_img), static_cast<T*>(y_img), s);
   if (st != EDIT_OK) return st;

@@ -830,33 +830,64 @@ __global__ __launch_bounds__(256) void sdpa_kernel(SdpaArgs<T> p) {
   }
 }
 
-// Merge of the key splits, one thread per output element: with M the largest
-// running max, the output is sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
-// then the same blend as the one-pass kernel (the exact eta's softmax mass is
-// 2^M times that denominator).
+// Merge of the key splits, one thread per four consecutive outputs of a row:
+// with M the largest running max, the output is
+// sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s, then the same blend as the
+// one-pass kernel (the exact eta's softmax mass is 2^M times that
+// denominator). Up to kCombineMax splits are read in one round trip (every
+// load issued before the first use); more take further passes of the loop.
+constexpr int kCombineMax = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void sdpa_combine_kernel(SdpaArgs<T> p) {
-  const int d = p.d;
-  const long long total = (long long)p.B * p.Nq * p.heads * d;
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= total) return;
-  const int n = (int)(idx % d);
-  long long r = idx / d;
-  const int h = (int)(r % p.heads);
-  r /= p.heads;
-  const int qi = (int)(r % p.Nq), b = (int)(r / p.Nq);
+  // grid: (Nq d / 4 / 256, heads, B); thread i of a (sample, head) takes query i / (d / 4), dims 4 (i % (d / 4))
+  const int d = p.d, d4 = d / 4, h = blockIdx.y, b = blockIdx.z;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= p.Nq * d4) return;
+  const int qi = i / d4, n = (i - qi * d4) * 4;
   const size_t sstride = (size_t)p.B * p.heads * p.Nq * (d + 2);
+  // rows of d + 2 floats (d a multiple of 8): the 4 outputs sit 8-byte aligned
   const float* base = p.part + (((size_t)b * p.heads + h) * p.Nq + qi) * (d + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, base[s * sstride + d]);
-  float L = 0.0f, O = 0.0f;
-  for (int s = 0; s < p.splits; ++s) {
-    const float* ps = base + s * sstride;
-    const float w = exp2f(ps[d] - M);
-    L += w * ps[d + 1];
-    O += w * ps[n];
+  float M = -INFINITY, L = 0.0f, O[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < p.splits; s0 += kCombineMax) {
+    float ms[kCombineMax], ls[kCombineMax];
+    float2 oa[kCombineMax], ob[kCombineMax];
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j) {
+      ms[j] = -INFINITY;
+      ls[j] = 0.0f;
+      oa[j] = ob[j] = make_float2(0.0f, 0.0f);
+      if (s0 + j < p.splits) {
+        const float* ps = base + (s0 + j) * sstride;
+        ms[j] = ps[d];
+        ls[j] = ps[d + 1];
+        oa[j] = *reinterpret_cast<const float2*>(ps + n);
+        ob[j] = *reinterpret_cast<const float2*>(ps + n + 2);
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j) Mn = fmaxf(Mn, ms[j]);
+    const float c = exp2f(M - Mn);   // 0 on the first pass (M = -inf)
+    L *= c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) O[k] *= c;
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j) {
+      if (s0 + j < p.splits) {
+        const float w = exp2f(ms[j] - Mn);
+        L += w * ls[j];
+        O[0] += w * oa[j].x;
+        O[1] += w * oa[j].y;
+        O[2] += w * ob[j].x;
+        O[3] += w * ob[j].y;
+      }
+    }
+    M = Mn;
   }
-  float o = O / L;
+  const float inv = 1.0f / L;
+  float o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = O[k] * inv;
   if (p.blend_src) {
     float alpha = p.alpha, beta = p.beta;
     if (p.lin_den) {
@@ -864,255 +895,12 @@ __global__ __launch_bounds__(256) void sdpa_combine_kernel(SdpaArgs<T> p) {
       alpha = lin / (lin + exp2f(M) * L);
       beta = 1.0f - alpha;
     }
-    o = alpha * to_f32(p.blend_src[((size_t)b * p.Nq + qi) * p.ldbs + h * d + n]) + beta * o;
+    const T* brow = p.blend_src + ((size_t)b * p.Nq + qi) * p.ldbs + h * d + n;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = alpha * to_f32(brow[k]) + beta * o[k];
   }
-  p.out[((size_t)b * p.Nq + qi) * p.ldo + h * d + n] = from_f32<T>(o);
+  store4(p.out + ((size_t)b * p.Nq + qi) * p.ldo + h * d + n, o);
 }
-
-// ---------------------------------------------------------------------------
-// Softmax attention with the key set staged once per block (bf16): the
-// hybrid's softmax blocks have few keys against many queries (image rows:
-// 4096 queries per head over the 333 text keys) or a few hundred keys per
-// split (text rows over [K'_I ; K_T]). A block stages one split of at most
-// KMAX keys of one (sample, head) -- K as [key][d], V^T as [d][key] -- and
-// its eight waves then walk 16-query tiles with no barrier: each wave keeps
-// the tile's whole row of scores S^T = K Q^T in registers (lane l: query
-// l % 16, four keys of each 16-key tile), takes the row maximum and the
-// exponentials in the exp2 domain, and multiplies O^T = V^T P^T with P^T as
-// the second matrix-core operand straight from those registers: within a
-// 32-key group lane group g holds keys 4g..4g+3 and 16+4g..16+4g+3, so V^T is
-// staged with the keys of each group in that order (one 16-byte read per
-// fragment). One split: the result is normalised and blended (eta, or the
-// exact per-row eta) and stored; several splits: fp32 partials (unnormalised
-// output, running max, sum) for sdpa_combine_kernel.
-// ---------------------------------------------------------------------------
-// keys per split: a multiple of the 96-key chunks, K and V^T within the LDS
-template <int DT> struct StagedKeys { static constexpr int n = DT <= 5 ? 384 : 288; };
-constexpr int kStagedThreads = 512;
-constexpr int kStagedQueries = 256;   // queries per block (16 tiles, two per wave)
-
-__device__ __forceinline__ int staged_pos(int k) {   // position of key k in its 32-key group of V^T
-  return (k & ~31) | (((k & 15) >> 2) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
-}
-
-template <int DT>
-__global__ __launch_bounds__(kStagedThreads) void sdpa_staged_kernel(SdpaArgs<bf16> p, int qpb) {
-  constexpr int KMAX = StagedKeys<DT>::n;
-  static_assert(KMAX % 96 == 0, "whole chunks");
-  constexpr int KS = (DT + 1) / 2, DK = 32 * KS;
-  constexpr int KP = DK + 8, VP = KMAX + 8;          // LDS row pitches (elements)
-  constexpr int NW = kStagedThreads / 64;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[KMAX * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[16 * DT * VP];
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int fr = lane & 15, g = lane >> 4;
-  const int d = p.d, dc = d / 8;
-  const int Ntot = p.N1 + p.N2;
-  const int nqb = (p.Nq + qpb - 1) / qpb;   // qpb: queries per block, a multiple of 16
-  const int sp = (int)blockIdx.x / nqb, qb = (int)blockIdx.x % nqb;
-  const int k0 = sp * KMAX, n = min(KMAX, Ntot - k0);   // this split's keys
-  const float sl2 = 1.4426950408889634f / sqrtf((float)d);   // log2(e) / sqrt(d)
-
-  // Stage K rows (zero past n and past d) and V^T (keys in fragment order, zero past n). Every
-  // load of a thread is issued before any LDS write (one memory round trip for the whole stage).
-  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  constexpr int KCH = KP / 8;                                  // 16-byte chunks per staged K row
-  constexpr int NKI = (KMAX * KCH + kStagedThreads - 1) / kStagedThreads;
-  constexpr int NVI = (KMAX * (16 * DT / 8) + kStagedThreads - 1) / kStagedThreads;
-  auto key_src = [&](int key, bool v) -> const bf16* {
-    const int kk = k0 + key;
-    const bool first = kk < p.N1;
-    const bf16* base = first ? (v ? p.v1 : p.k1) : (v ? p.v2 : p.k2);
-    return base + ((size_t)b * (first ? p.N1 : p.N2) + (first ? kk : kk - p.N1)) * (first ? p.ldkv1 : p.ldkv2) + h * d;
-  };
-  u32x4v kraw[NKI], vraw[NVI];
-#pragma unroll
-  for (int u = 0; u < NKI; ++u) {
-    const int e = tid + kStagedThreads * u, key = e / KCH, c8 = (e % KCH) * 8;
-    kraw[u] = u32x4v{0u, 0u, 0u, 0u};
-    if (key < n && c8 < d) kraw[u] = *reinterpret_cast<const u32x4v*>(key_src(key, false) + c8);
-  }
-  // V items run key-fastest (a wave covers 64 consecutive keys of one channel chunk), so each of the
-  // eight 2-byte stores below writes one contiguous 128-byte run of a V^T row (no bank conflicts).
-#pragma unroll
-  for (int u = 0; u < NVI; ++u) {
-    const int e = tid + kStagedThreads * u, key = e % KMAX, c8 = (e / KMAX) * 8;
-    vraw[u] = u32x4v{0u, 0u, 0u, 0u};
-    if (key < n && c8 < d) vraw[u] = *reinterpret_cast<const u32x4v*>(key_src(key, true) + c8);
-  }
-#pragma unroll
-  for (int u = 0; u < NKI; ++u) {
-    const int e = tid + kStagedThreads * u;
-    if (e < KMAX * KCH) *reinterpret_cast<u32x4v*>(Ks + (e / KCH) * KP + (e % KCH) * 8) = kraw[u];
-  }
-#pragma unroll
-  for (int u = 0; u < NVI; ++u) {
-    const int e = tid + kStagedThreads * u, key = e % KMAX, c8 = (e / KMAX) * 8;
-    if (c8 < d) {
-      const bf16* v = reinterpret_cast<const bf16*>(&vraw[u]);
-      const int pos = staged_pos(key);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) Vt[(c8 + i) * VP + pos] = v[i];
-    }
-  }
-  // V^T rows d .. 16 DT - 1 (head dims past d) are read by the last tile: zero them
-  for (int e = tid; e < (16 * DT - d) * VP; e += kStagedThreads) Vt[d * VP + e] = (bf16)0.0f;
-  __syncthreads();
-
-  const int q_lo = qb * qpb, q_hi = min(p.Nq, q_lo + qpb);
-  // the tile loop's pointers, formed once (fewer live scalars in the loop)
-  const bf16* qbase = p.q + (size_t)b * p.Nq * p.ldq + h * d;
-  const int ldq = p.ldq;
-  const bool split = p.splits > 1;
-  float* pbase = split ? p.part + (((size_t)sp * p.B + b) * p.heads + h) * (size_t)p.Nq * (d + 2) : nullptr;
-  bf16* obase = p.out + (size_t)b * p.Nq * p.ldo + h * d;
-  const int ldo = p.ldo;
-  const bf16* bbase = p.blend_src ? p.blend_src + (size_t)b * p.Nq * p.ldbs + h * d : nullptr;
-  const int ldbs = p.ldbs;
-  const float* lbase = p.lin_den ? p.lin_den + (size_t)b * p.Nq * p.heads + h : nullptr;
-  const int lstride = p.heads;
-  const float alpha0 = p.alpha, beta0 = p.beta;
-  // A wave's query tiles: the next tile's query fragments are requested while the current tile is
-  // computed, and the current tile's blend rows at its start (used at its end).
-  auto load_q = [&](bf16x8 (&dst)[KS], int qt) {
-    const int qi = qt + fr;
-    const bf16* qrow = qbase + (size_t)(qi < q_hi ? qi : q_lo) * ldq;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int k = s * 32 + g * 8;
-      if (k < d) dst[s] = *reinterpret_cast<const bf16x8*>(qrow + k);
-      else frag_zero(dst[s]);
-    }
-  };
-  bf16x8 bqn[KS];
-  if (q_lo + 16 * wave < q_hi) load_q(bqn, q_lo + 16 * wave);
-  for (int qt = q_lo + 16 * wave; qt < q_hi; qt += 16 * NW) {
-    const int qi = qt + fr;
-    const bool qv = qi < q_hi;
-    bf16x8 bq[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) bq[s] = bqn[s];
-    if (qt + 16 * NW < q_hi) load_q(bqn, qt + 16 * NW);
-    bf16x4 bb[DT];
-    float lin = 0.0f;
-    if (bbase && qv) {
-      const bf16* brow = bbase + (size_t)qi * ldbs;
-#pragma unroll
-      for (int tn = 0; tn < DT; ++tn) {
-        const int nn = tn * 16 + g * 4;
-        bb[tn] = nn < d ? *reinterpret_cast<const bf16x4*>(brow + nn) : bf16x4{};
-      }
-      if (lbase) lin = lbase[(size_t)qi * lstride];
-    }
-    // Online softmax over chunks of 96 keys (6 tiles of 16, 3 groups of 32): the chunk's raw scores of
-    // keys 16 t + 4 g + r for query fr, their maximum folded into the running one (the output and the
-    // sum rescaled by 2^((m_old - m_new) sl2)), then p = 2^(s sl2 - m sl2) and O^T += V^T P^T. Keys
-    // past n (zero rows of K, V) are set to -inf in the chunk that reaches past n.
-    float m = -INFINITY, l = 0.0f;
-    f32x4 acc[DT];
-#pragma unroll
-    for (int tn = 0; tn < DT; ++tn) acc_zero(acc[tn]);
-    const int nch = (n + 95) / 96;
-#pragma unroll 1
-    for (int ch = 0; ch < nch; ++ch) {
-      const int kb = 96 * ch;
-      f32x4 sc[6];
-      float cm = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 6; ++t) {
-        acc_zero(sc[t]);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          bf16x8 ak = *reinterpret_cast<const bf16x8*>(Ks + (kb + t * 16 + fr) * KP + s * 32 + g * 8);
-          mma16(sc[t], ak, bq[s]);
-        }
-      }
-      if (kb + 96 > n) {
-#pragma unroll
-        for (int t = 0; t < 6; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (kb + 16 * t + 4 * g + r >= n) sc[t][r] = -INFINITY;
-      }
-#pragma unroll
-      for (int t = 0; t < 6; ++t) cm = fmaxf(cm, fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])));
-      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-      const float mn = fmaxf(m, cm);
-      const float corr = __builtin_amdgcn_exp2f((m - mn) * sl2);   // 0 on the first chunk (m = -inf)
-      m = mn;
-      const float msl = mn * sl2;
-      l *= corr;
-#pragma unroll
-      for (int tn = 0; tn < DT; ++tn)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[tn][r] *= corr;
-#pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        float e[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * j][r], sl2, -msl));
-          e[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[2 * j + 1][r], sl2, -msl));
-        }
-        bf16x8 pf;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          l += e[r];
-          pf[r] = (bf16)e[r];
-        }
-#pragma unroll
-        for (int tn = 0; tn < DT; ++tn) {
-          bf16x8 av = *reinterpret_cast<const bf16x8*>(Vt + (tn * 16 + fr) * VP + kb + 32 * j + 8 * g);
-          mma16(acc[tn], av, pf);
-        }
-      }
-    }
-    const float msl = m * sl2;
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (!qv) continue;
-    if (split) {
-      // this split's partial: unnormalised output, max (log2 units), sum
-      float* prow = pbase + (size_t)qi * (d + 2);
-#pragma unroll
-      for (int tn = 0; tn < DT; ++tn) {
-        const int nn = tn * 16 + g * 4;
-        if (nn < d) *reinterpret_cast<f32x4*>(prow + nn) = acc[tn];
-      }
-      if (g == 0) {
-        prow[d] = msl;
-        prow[d + 1] = l;
-      }
-      continue;
-    }
-    const float inv = 1.0f / l;
-    bf16* orow = obase + (size_t)qi * ldo;
-    float alpha = alpha0, beta = beta0;
-    if (bbase && lbase) {
-      // exact eta: the linear block's mass q . z + eps against the softmax mass sum_t exp(s_t) = 2^msl l
-      alpha = lin / (lin + exp2f(msl) * l);
-      beta = 1.0f - alpha;
-    }
-#pragma unroll
-    for (int tn = 0; tn < DT; ++tn) {
-      const int nn = tn * 16 + g * 4;
-      if (nn < d) {
-        float o[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = acc[tn][r] * inv;
-        if (bbase) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = alpha * (float)bb[tn][r] + beta * o[r];
-        }
-        store4(orow + nn, o);
-      }
-    }
-  }
-}
-
-int sdpa_staged_keys(int d) { return (d + 15) / 16 <= 5 ? StagedKeys<5>::n : StagedKeys<8>::n; }
 
 int sdpa_splits(int Nq, int Nkeys, int heads, int B, int d, bool staged) {
   if (staged) return std::max(1, (Nkeys + sdpa_staged_keys(d) - 1) / sdpa_staged_keys(d));
@@ -1125,32 +913,23 @@ int sdpa_splits(int Nq, int Nkeys, int heads, int B, int d, bool staged) {
 }
 
 template <typename T>
+hipError_t launch_sdpa_combine(const SdpaArgs<T>& a, hipStream_t s) {
+  const long long per_head = (long long)a.Nq * (a.d / 4);
+  if (a.d % 8 || per_head >= (1LL << 31) - 256 || a.heads > 65535 || a.B > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((sdpa_combine_kernel<T>), dim3((unsigned)((per_head + 255) / 256), a.heads, a.B), dim3(256),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_sdpa(const SdpaArgs<T>& a0, hipStream_t s) {
   if (a0.Nq <= 0) return hipSuccess;
   SdpaArgs<T> a = a0;
   if constexpr (std::is_same<T, bf16>::value) {
     // the staged kernel: splits of at most sdpa_staged_keys(d) keys
-    const int need = sdpa_splits(a.Nq, a.N1 + a.N2, a.heads, a.B, a.d, true);
-    if (a.splits != need || (need > 1 && a.part == nullptr)) return hipErrorInvalidValue;
-    // queries per block: all of a small query set (its staged keys then serve every query tile), else
-    // 256 (two tiles per wave)
-    const int qpb = a.Nq <= 2 * kStagedQueries ? (a.Nq + 15) / 16 * 16 : kStagedQueries;
-    const long long gx = (long long)((a.Nq + qpb - 1) / qpb) * a.splits;
-    if (gx >= (1LL << 31)) return hipErrorInvalidValue;
-    dim3 grid((unsigned)gx, a.heads, a.B), block(kStagedThreads);
-    switch ((a.d + 15) / 16) {
-#define EDIT_STAGED_CASE(DTV) \
-  case DTV: hipLaunchKernelGGL((sdpa_staged_kernel<DTV>), grid, block, 0, s, a, qpb); break;
-      EDIT_STAGED_CASE(1) EDIT_STAGED_CASE(2) EDIT_STAGED_CASE(3) EDIT_STAGED_CASE(4)
-      EDIT_STAGED_CASE(5) EDIT_STAGED_CASE(6) EDIT_STAGED_CASE(7) EDIT_STAGED_CASE(8)
-#undef EDIT_STAGED_CASE
-      default: return hipErrorInvalidValue;
-    }
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_sdpa_staged(&a, 1, s);
     if (e != hipSuccess || a.splits == 1) return e;
-    const long long total = (long long)a.B * a.Nq * a.heads * a.d;
-    hipLaunchKernelGGL((sdpa_combine_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    return launch_sdpa_combine(a, s);
   }
   if (a.splits < 1 || a.part == nullptr) a.splits = 1;
   const long long gx = (long long)((a.Nq + 63) / 64) * a.splits;
@@ -1166,9 +945,25 @@ hipError_t launch_sdpa(const SdpaArgs<T>& a0, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  const long long total = (long long)a.B * a.Nq * a.heads * a.d;
-  hipLaunchKernelGGL((sdpa_combine_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_sdpa_combine(a, s);
+}
+
+template <typename T>
+hipError_t launch_sdpa_pair(const SdpaArgs<T>& a, const SdpaArgs<T>& b, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    // one staged launch over both problems, then the merge of each one's key splits
+    SdpaArgs<T> j[2] = {a, b};
+    int n = 0;
+    if (a.Nq > 0) j[n++] = a;
+    if (b.Nq > 0) j[n++] = b;
+    if (n == 0) return hipSuccess;
+    hipError_t e = launch_sdpa_staged(j, n, s);
+    for (int i = 0; i < n && e == hipSuccess; ++i)
+      if (j[i].splits > 1) e = launch_sdpa_combine(j[i], s);
+    return e;
+  }
+  hipError_t e = launch_sdpa<T>(a, s);
+  return e != hipSuccess ? e : launch_sdpa<T>(b, s);
 }
 
 #define EDIT_INST(T)                                                                                     \
@@ -1180,7 +975,8 @@ hipError_t launch_sdpa(const SdpaArgs<T>& a0, hipStream_t s) {
                                                   hipStream_t);                                                   \
   template hipError_t launch_linattn_apply<T>(const T*, int, const T*, const float*, int, int, int, int, \
                                               float, T*, int, float*, hipStream_t);                     \
-  template hipError_t launch_sdpa<T>(const SdpaArgs<T>&, hipStream_t);
+  template hipError_t launch_sdpa<T>(const SdpaArgs<T>&, hipStream_t);                                      \
+  template hipError_t launch_sdpa_pair<T>(const SdpaArgs<T>&, const SdpaArgs<T>&, hipStream_t);
 EDIT_INST(bf16)
 EDIT_INST(float)
 #undef EDIT_INST

@@ -227,5 +227,15 @@ hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s);
 // bf16 (staged): one split per sdpa_staged_keys(d) keys (the keys a block stages at once).
 int sdpa_splits(int Nq, int Nkeys, int heads, int B, int d, bool staged);
 int sdpa_staged_keys(int d);
+// Two softmax problems of one head geometry: bf16 runs both in one staged
+// launch (their blocks share the chip), then merges each one's key splits;
+// fp32 runs them one after the other. Each problem's partials need a buffer
+// of its own.
+template <typename T>
+hipError_t launch_sdpa_pair(const SdpaArgs<T>& a, const SdpaArgs<T>& b, hipStream_t s);
+// The bf16 softmax kernel with the keys staged in LDS (sdpa_staged.hip), over
+// one or two problems with the same d: one pass each, or with splits > 1 the
+// fp32 partials for sdpa_combine_kernel.
+hipError_t launch_sdpa_staged(const SdpaArgs<bf16>* jobs, int njobs, hipStream_t s);
 
 }  // namespace edit
