@@ -36,7 +36,9 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense matrix-core (f32: ve
 STEP_NAMES = ["cf_conv3x3", "gn_stats", "cf_act", "q_proj", "kv_proj", "sc_dwconv", "kv_state",
               "linattn_apply", "out_proj"]
 STEP_KERNELS = {  # kernels launched per step at bf16 (rocprofv3 names start with these)
-    "cf_conv3x3": "gemm_dma_kernel<256 or 128, 96, 4, 1, A_CONV3, E_BIAS_GN> (with the GroupNorm partials and the restore fold)",
+    # bf16, H*W a multiple of 256 and W of 32..128 or a multiple of 256: the kernel-row conv; otherwise the
+    # tap-by-tap implicit GEMM. Both carry the GroupNorm partials and the restore fold.
+    "cf_conv3x3": "conv3x3_rows_kernel<W, E_BIAS_GN> (else gemm_dma_kernel<256 or 128, 96, 4, 1, A_CONV3, E_BIAS_GN>)",
     "gn_stats": "gn_finalize_channels_kernel",
     "cf_act": "gn_apply_kernel",
     "q_proj": "gemm_dma_kernel<128, 192, 2, 2, A_CAT2, E_BIAS_RELU>",

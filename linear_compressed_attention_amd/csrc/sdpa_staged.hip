@@ -224,7 +224,8 @@ __global__ __launch_bounds__(kThreads) void sdpa_staged_kernel(const StagedJobs 
       } else {
         load_q(qf, qi);
       }
-      // the blend rows at this lane's output positions (dims 32 o + 8 j + 4 h .. + 3), read at the end
+      // the blend rows at this lane's output positions (dims 32 o + 8 j + 4 h .. + 3): requested here, used
+      // at the end of the tile (up to 64 head dims; wider heads read them at the end)
       bf16x4 bb[OT][4];
       float lin = 0.0f;
       auto load_blend = [&]() {
@@ -237,6 +238,7 @@ __global__ __launch_bounds__(kThreads) void sdpa_staged_kernel(const StagedJobs 
                                                    : bf16x4{};
         if (lbase) lin = lbase[(size_t)min(qrow, Nq - 1) * lstride];
       };
+      if (kPrefetch && bbase) load_blend();
 
       f32x16 acc[OT];
 #pragma unroll
@@ -302,17 +304,18 @@ __global__ __launch_bounds__(kThreads) void sdpa_staged_kernel(const StagedJobs 
       // the matrix cores work on them while the exponentials are taken.
       f32x16 sa, sb;
       scores(sa, 0);
+      int kt = 0;
 #pragma unroll 1
-      for (int kt = 0; kt < nkt; kt += 2) {
-        if (kt + 1 < nkt) scores(sb, kt + 1);
+      for (; kt + 1 < nkt; kt += 2) {
+        scores(sb, kt + 1);
         softmax_pv(sa, kt);
-        if (kt + 1 >= nkt) break;
         if (kt + 2 < nkt) scores(sa, kt + 2);
         softmax_pv(sb, kt + 1);
       }
+      if (kt < nkt) softmax_pv(sa, kt);   // an odd last tile
       l += other_half(l, upper);
       if (!qv) continue;
-      if (bbase) load_blend();
+      if (!kPrefetch && bbase) load_blend();
       if (split) {
         // this split's partial: unnormalised output, max (log2 units), sum
         float* prow = pbase + (size_t)qrow * (d + 2);
