@@ -182,11 +182,16 @@ def device_info():
 
 
 class HipEvents:
-    """hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+    """hipEvent_t handles from the process's HIP runtime (the one torch loaded). They only time: created
+    without the system-scope fence on recording (hipEventDisableSystemFence), so that the cache writeback
+    and invalidation a fenced event adds between two steps are not counted in either step; they are read
+    after a full device synchronisation."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence (hip_runtime_api.h)
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
@@ -194,9 +199,9 @@ class HipEvents:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
             if rc != 0:
-                raise RuntimeError(f"hipEventCreate failed ({rc})")
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
             out.append(e.value)
         return out
 
