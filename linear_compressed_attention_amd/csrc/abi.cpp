@@ -489,7 +489,7 @@ edit_status_t static_scratch(void** out) {
 template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
                         hipStream_t s, const Marks& mk, float* lin_den = nullptr,
-                        const edit_convfusion_weights_t* kcf = nullptr) {
+                        const edit_convfusion_weights_t* kcf = nullptr, bool apply = true) {
   using namespace edit;
   auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
@@ -587,9 +587,10 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     if (e2 != hipSuccess) return fail(EDIT_ERR_HIP, "joining the key/value stream failed: %s", hipGetErrorString(e2));
   }
   EDIT_LAUNCH(mk.mark(EDIT_STEP_APPLY));
-  // 8. y = q S / (q . z + eps)
-  EDIT_LAUNCH(launch_linattn_apply<T>(P(L.q), g.C, P(L.st), F(L.zp), g.B, g.N, g.heads, g.d, g.eps, P(L.y), g.C,
-                                      lin_den, s));
+  // 8. y = q S / (q . z + eps) (the hybrid may form it inside its image-row softmax instead)
+  if (apply)
+    EDIT_LAUNCH(launch_linattn_apply<T>(P(L.q), g.C, P(L.st), F(L.zp), g.B, g.N, g.heads, g.d, g.eps, P(L.y), g.C,
+                                        lin_den, s));
   return EDIT_OK;
 }
 
@@ -626,7 +627,12 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   char* wsb = static_cast<char*>(ws);
   auto P = [&](size_t off) { return reinterpret_cast<T*>(wsb + off); };
   float* lin_den = exact_eta && g.nt > 0 ? reinterpret_cast<float*>(wsb + L.lin_den) : nullptr;
-  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x_img), wsb, s, Marks{nullptr, s}, lin_den);
+  // bf16 with head dims up to 64 and the text keys in one split: the image rows' softmax kernel forms the
+  // linear part itself from the head's state (the apply step and y_lin's round trip through memory drop out)
+  const bool fuse = g.es == 2 && g.nt > 0 && edit::sdpa_staged_fuses_linear(g.d) &&
+                    edit::sdpa_splits(g.N, g.nt, g.heads, g.B, g.d, true) == 1;
+  edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x_img), wsb, s, Marks{nullptr, s},
+                                  fuse ? nullptr : lin_den, nullptr, !fuse);
   if (st != EDIT_OK) return st;
   if (g.nt == 0) return out_linear<T>(g.M, g.C, w->w_o, w->b_o, P(L.y), static_cast<T*>(y_img), s);
 
@@ -652,6 +658,13 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   sa.B = g.B; sa.heads = g.heads; sa.d = g.d;
   sa.out = P(L.y_img); sa.ldo = C;
   sa.blend_src = P(L.y); sa.ldbs = C; sa.alpha = eta; sa.beta = 1.0f - eta; sa.lin_den = lin_den;
+  if (fuse) {
+    // y_lin from the state in the kernel; the exact eta's q . z + eps is written to lin_den
+    sa.blend_src = nullptr; sa.ldbs = 0;
+    sa.lin_st = P(L.st); sa.lin_zp = reinterpret_cast<const float*>(wsb + L.zp); sa.lin_eps = g.eps;
+    sa.exact_eta = exact_eta ? 1 : 0;
+    sa.lin_den = nullptr; sa.lin_den_out = lin_den;
+  }
   sa.splits = sdpa_splits(g.N, g.nt, g.heads, g.B, g.d, g.es == 2);
   sa.part = sa.splits > 1 ? reinterpret_cast<float*>(wsb + L.sdpa_part_img) : nullptr;
   // Text rows: softmax over [K'_I ; K_T] with values [V'_I ; V_T].

@@ -213,6 +213,16 @@ struct SdpaArgs {
   // If set (with blend_src): alpha = L / (L + sum_t exp(s_t)) per query and
   // head, L = lin_den[b][query][head], beta = 1 - alpha.
   const float* lin_den;
+  // If set (bf16, staged kernel, d <= 64): the blend's linear part is formed
+  // in the kernel from the head's state instead of read from blend_src:
+  // lin_st[B][heads][2][DP][DK] (S^T as bf16 hi + lo, as the apply kernel
+  // reads it), lin_zp[B][heads][DK] (z), y_lin = q S / (q . z + lin_eps);
+  // with exact_eta, L = q . z + lin_eps in the formula above.
+  const T* lin_st;
+  const float* lin_zp;
+  float lin_eps;
+  int exact_eta;
+  float* lin_den_out;   // if set (with lin_st): q . z + lin_eps per [b][query][head]
   // Key splits (1: one pass over all keys). With splits > 1 each block takes
   // one split's slabs and writes fp32 partials [split][B][heads][Nq][d + 2]
   // (unnormalised output, running max, running sum) to part, and a second
@@ -227,6 +237,8 @@ hipError_t launch_sdpa(const SdpaArgs<T>& a, hipStream_t s);
 // bf16 (staged): one split per sdpa_staged_keys(d) keys (the keys a block stages at once).
 int sdpa_splits(int Nq, int Nkeys, int heads, int B, int d, bool staged);
 int sdpa_staged_keys(int d);
+// Whether the staged kernel forms the image rows' linear part itself (lin_st): bf16 with d <= 64.
+bool sdpa_staged_fuses_linear(int d);
 // Two softmax problems of one head geometry: bf16 runs both in one staged
 // launch (their blocks share the chip), then merges each one's key splits;
 // fp32 runs them one after the other. Each problem's partials need a buffer

@@ -49,13 +49,20 @@ struct StagedGeom {
   static constexpr int OT = DV / 32;               // output tiles
   static constexpr int KP = DK + 8, VP = KMAX + 8;  // LDS row pitches (elements): 16 bytes of padding
   static constexpr int VT_BYTES = DV * VP * 2;
-  static constexpr int BYTES = VT_BYTES + KMAX * KP * 2;
+  static constexpr int K_BYTES = KMAX * KP * 2;
+  // the fused linear part (head dims up to 64): S^T hi and lo, DV rows (zero past the operand's DP rows) of
+  // LK = the operand's DK columns plus 16 bytes of padding, and z
+  static constexpr bool LIN = DT <= 4;
+  static constexpr int LDP = 16 * DT, LK = 32 * ((DT + 1) / 2), LP = LK + 8;
+  static constexpr int LIN_BYTES = LIN ? 2 * DV * LP * 2 + LK * 4 : 0;
+  static constexpr int BYTES = VT_BYTES + K_BYTES + LIN_BYTES;
   static_assert(KMAX % 96 == 0, "whole chunks");
   static_assert(BYTES <= 160 * 1024, "LDS");
 };
 constexpr int kThreads = 512, kWaves = kThreads / 64;
 constexpr int kTileQ = 32;          // queries per wave tile
 constexpr float kLazyLog2 = 8.0f;   // headroom of the running maximum (log2 units)
+constexpr double kStageTiles = 3.0;  // a segment's staging, in a wave's 32-key tiles (schedule estimate)
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -88,10 +95,11 @@ __device__ __forceinline__ u32x4v load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 // their work units are concatenated, job 0's first.
 struct StagedJobs {
   SdpaArgs<bf16> job[2];
-  int nqt[2];   // query tiles per (split, sample, head) segment
-  int units0;   // job 0's units
-  int units;    // all units
-  int per;      // units per block
+  int nqt[2];     // query tiles per (split, sample, head) segment
+  int units0;     // job 0's units
+  int units;      // all units
+  int per[2];     // units per block of each job
+  int blocks0;    // blocks taking job 0 (the rest take job 1)
 };
 
 template <int DT>
@@ -101,6 +109,8 @@ __global__ __launch_bounds__(kThreads) void sdpa_staged_kernel(const StagedJobs 
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::BYTES];
   bf16* const Vt = reinterpret_cast<bf16*>(lds);
   bf16* const Ks = reinterpret_cast<bf16*>(lds + G::VT_BYTES);
+  bf16* const Ls = reinterpret_cast<bf16*>(lds + G::VT_BYTES + G::K_BYTES);   // S^T hi, then lo (fused linear)
+  float* const Lz = reinterpret_cast<float*>(lds + G::VT_BYTES + G::K_BYTES + (G::LIN ? 2 * DV * G::LP * 2 : 0));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fq = lane & 31, hh = lane >> 5;
   const bool upper = hh != 0;
@@ -109,7 +119,10 @@ __global__ __launch_bounds__(kThreads) void sdpa_staged_kernel(const StagedJobs 
   const bf16x2 ones2 = {(bf16)1.0f, (bf16)1.0f};
 
   const int blk = xcd_swizzle((int)blockIdx.x, (int)gridDim.x);
-  const int u0 = blk * J.per, u1 = min(J.units, u0 + J.per);
+  // this block's run of units: job 0's blocks first, then job 1's (a block takes one job's units only)
+  const bool j0 = blk < J.blocks0;
+  const int u0 = j0 ? blk * J.per[0] : J.units0 + (blk - J.blocks0) * J.per[1];
+  const int u1 = j0 ? min(J.units0, u0 + J.per[0]) : min(J.units, u0 + J.per[1]);
   for (int u = u0; u < u1;) {
     const int jb = u < J.units0 ? 0 : 1, ub = jb ? J.units0 : 0, nqt = J.nqt[jb];
     const SdpaArgs<bf16>& p = J.job[jb];
@@ -183,6 +196,20 @@ __global__ __launch_bounds__(kThreads) void sdpa_staged_kernel(const StagedJobs 
 #pragma unroll
         for (int j = 0; j < 8; ++j) Vt[(c8 + j) * VP + pos] = v[j];
       }
+    }
+    // the head's state operand for the fused linear part: S^T hi and lo (rows past the operand's LDP rows
+    // zero) and z
+    const bool linfuse = G::LIN && p.lin_st != nullptr;
+    if (linfuse) {
+      constexpr int LDP = G::LDP, LK = G::LK, LP = G::LP, LC = LK / 8;
+      const bf16* gst = p.lin_st + ((size_t)b * p.heads + h) * 2 * LDP * LK;
+      for (int e = tid; e < 2 * DV * LC; e += kThreads) {
+        const int part = e / (DV * LC), r = (e / LC) % DV, c8 = (e % LC) * 8;
+        u32x4v v = u32x4v{0u, 0u, 0u, 0u};
+        if (r < LDP) v = *reinterpret_cast<const u32x4v*>(gst + ((size_t)part * LDP + r) * LK + c8);
+        *reinterpret_cast<u32x4v*>(Ls + (part * DV + r) * LP + c8) = v;
+      }
+      for (int k = tid; k < LK; k += kThreads) Lz[k] = p.lin_zp[((size_t)b * p.heads + h) * LK + k];
     }
     __syncthreads();
 
@@ -314,6 +341,32 @@ __global__ __launch_bounds__(kThreads) void sdpa_staged_kernel(const StagedJobs 
       }
       if (kt < nkt) softmax_pv(sa, kt);   // an odd last tile
       l += other_half(l, upper);
+      // the fused linear part (every lane, before any leaves): y_lin^T = S^T q^T on the matrix cores (the lo
+      // part first, then hi, as the apply kernel adds them) and the normaliser q . z + eps, the lane's dims
+      // of its query then the other lane half's
+      f32x16 yl[G::LIN ? OT : 1];
+      float linv = 1.0f;
+      if constexpr (G::LIN) {
+        if (linfuse) {
+          float den = 0.0f;
+#pragma unroll
+          for (int s = 0; s < DT; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) den += (float)qf[s][i] * Lz[16 * s + 8 * hh + i];
+          den += other_half(den, upper);
+          linv = den + p.lin_eps;
+#pragma unroll
+          for (int o = 0; o < OT; ++o) {
+            acc_zero(yl[o]);
+#pragma unroll
+            for (int s = 0; s < DT; ++s) {
+              const bf16* ar = Ls + (o * 32 + fq) * G::LP + 16 * s + 8 * hh;
+              mma32(yl[o], *reinterpret_cast<const bf16x8*>(ar + DV * G::LP), qf[s]);
+              mma32(yl[o], *reinterpret_cast<const bf16x8*>(ar), qf[s]);
+            }
+          }
+        }
+      }
       if (!qv) continue;
       if (!kPrefetch && bbase) load_blend();
       if (split) {
@@ -336,11 +389,18 @@ __global__ __launch_bounds__(kThreads) void sdpa_staged_kernel(const StagedJobs 
       }
       const float inv = 1.0f / l;
       float alpha = p.alpha, beta = p.beta;
-      if (bbase && lbase) {
+      if (linfuse) {
         // exact eta: the linear block's mass q . z + eps against the softmax mass sum_t exp(s_t) = 2^(m sl2) l
+        if (p.exact_eta) {
+          alpha = linv / (linv + exp2f(m * sl2) * l);
+          beta = 1.0f - alpha;
+        }
+        if (p.lin_den_out && !upper) p.lin_den_out[((size_t)b * Nq + qrow) * p.heads + h] = linv;
+      } else if (bbase && lbase) {
         alpha = lin / (lin + exp2f(m * sl2) * l);
         beta = 1.0f - alpha;
       }
+      const float ilin = 1.0f / linv;
       bf16* orow = obase + (size_t)qrow * ldo + 4 * hh;
 #pragma unroll
       for (int o = 0; o < OT; ++o)
@@ -350,6 +410,12 @@ __global__ __launch_bounds__(kThreads) void sdpa_staged_kernel(const StagedJobs 
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[o][4 * j + r] * inv;
+            if constexpr (G::LIN) {
+              if (linfuse) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] = alpha * (yl[o][4 * j + r] * ilin) + beta * v[r];
+              }
+            }
             if (bbase) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) v[r] = alpha * (float)bb[o][j][r] + beta * v[r];
@@ -381,21 +447,42 @@ hipError_t launch_dt(const SdpaArgs<bf16>* a, int njobs, hipStream_t s) {
     if (dev < kMaxDev) g_slots[dev][DT].store(slots, std::memory_order_relaxed);
   }
   StagedJobs J{};
-  long long units = 0;
+  long long u[2] = {0, 0};
+  double kt[2] = {1.0, 1.0};   // 32-key tiles per unit, averaged over the splits
   for (int j = 0; j < 2; ++j) {
     const SdpaArgs<bf16>& x = a[j < njobs ? j : 0];
     J.job[j] = x;
     J.nqt[j] = std::max(1, (x.Nq + kTileQ - 1) / kTileQ);
     if (j < njobs) {
-      units += (long long)((x.Nq + kTileQ - 1) / kTileQ) * x.heads * x.B * x.splits;
-      if (j == 0) J.units0 = (int)std::min<long long>(units, 1LL << 30);
+      u[j] = (long long)((x.Nq + kTileQ - 1) / kTileQ) * x.heads * x.B * x.splits;
+      const int keys = x.N1 + x.N2, last = keys - (x.splits - 1) * StagedGeom<DT>::KMAX;
+      kt[j] = ((x.splits - 1) * (StagedGeom<DT>::KMAX / 32) + (last + 31) / 32) / (double)x.splits;
     }
   }
+  const long long units = u[0] + u[1];
   if (units <= 0) return hipSuccess;
   if (units >= (1LL << 30)) return hipErrorInvalidValue;
+  J.units0 = (int)u[0];
   J.units = (int)units;
-  J.per = (int)((units + slots - 1) / slots);
-  const long long blocks = (units + J.per - 1) / J.per;
+  // Blocks per job: the split that evens out the longest block, a block's time taken as its busiest wave's
+  // key tiles plus a staging (about kStageTiles key tiles) per segment it starts.
+  auto cost = [&](int j, long long per) {
+    const long long segs = (per - 1) / J.nqt[j] + 2;
+    return (double)((per + kWaves - 1) / kWaves) * kt[j] + (double)segs * kStageTiles;
+  };
+  long long b0 = u[0] > 0 ? slots : 0;
+  if (u[0] > 0 && u[1] > 0) {
+    double best = 1e300;
+    for (long long c = 1; c < slots; ++c) {
+      const long long p0 = (u[0] + c - 1) / c, p1 = (u[1] + (slots - c) - 1) / (slots - c);
+      const double t = std::max(cost(0, p0), cost(1, p1));
+      if (t < best) { best = t; b0 = c; }
+    }
+  }
+  J.per[0] = u[0] > 0 ? (int)((u[0] + b0 - 1) / b0) : 1;
+  J.per[1] = u[1] > 0 ? (int)((u[1] + (slots - b0) - 1) / std::max(1LL, slots - b0)) : 1;
+  J.blocks0 = u[0] > 0 ? (int)((u[0] + J.per[0] - 1) / J.per[0]) : 0;
+  const long long blocks = J.blocks0 + (u[1] > 0 ? (u[1] + J.per[1] - 1) / J.per[1] : 0);
   hipLaunchKernelGGL((sdpa_staged_kernel<DT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, J);
   return hipGetLastError();
 }
@@ -403,6 +490,8 @@ hipError_t launch_dt(const SdpaArgs<bf16>* a, int njobs, hipStream_t s) {
 }  // namespace
 
 int sdpa_staged_keys(int d) { return (d + 15) / 16 <= 5 ? StagedGeom<5>::KMAX : StagedGeom<8>::KMAX; }
+
+bool sdpa_staged_fuses_linear(int d) { return d > 0 && d <= 64 && d % 8 == 0; }
 
 hipError_t launch_sdpa_staged(const SdpaArgs<bf16>* a, int njobs, hipStream_t s) {
   if (a == nullptr || njobs < 1 || njobs > 2) return hipErrorInvalidValue;
@@ -417,6 +506,11 @@ hipError_t launch_sdpa_staged(const SdpaArgs<bf16>* a, int njobs, hipStream_t s)
     if (x.splits != need || (need > 1 && x.part == nullptr)) return hipErrorInvalidValue;
     // buffer offsets of a split's rows are 32-bit
     if (((long long)kmax * std::max(x.ldkv1, x.ldkv2) + d) * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+    // the fused linear part: head dims up to 64, one pass over the keys (the split merge blends from
+    // blend_src), and not beside blend_src
+    if (x.lin_st != nullptr &&
+        (!sdpa_staged_fuses_linear(d) || x.splits != 1 || x.lin_zp == nullptr || x.blend_src != nullptr))
+      return hipErrorInvalidValue;
   }
   switch ((d + 15) / 16) {
     case 1: return launch_dt<1>(a, njobs, s);

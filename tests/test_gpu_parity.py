@@ -123,7 +123,12 @@ def check_hybrid(s, n_text, seed=0, exact=False):
                                            eta="exact" if exact else "ratio")
     tol = _tol(s)
     pairs = {"out": (got["out"], out_i), "q": (got["q"], tr["q"]), "kc": (got["kc"], tr["kc"]),
-             "vc": (got["vc"], tr["vc"]), "y_lin": (got["y"], tr["y_lin"])}
+             "vc": (got["vc"], tr["vc"])}
+    # bf16 with head_dim <= 64 and the text keys in one split of 384: the image rows' softmax kernel forms the
+    # linear part itself and y_lin is never written (y_img and out carry it); otherwise it is compared
+    fused = s.dtype == "bf16" and s.head_dim <= 64 and 0 < n_text <= 384
+    if not fused:
+        pairs["y_lin"] = (got["y"], tr["y_lin"])
     if n_text:
         pairs.update({"out_txt": (got["out_txt"], out_t), "y_img": (got["y_img"], tr["y"]),
                       "y_txt": (got["y_txt"], tr["y_txt"]),
