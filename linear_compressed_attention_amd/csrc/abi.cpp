@@ -28,6 +28,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <mutex>
 
 #include "../../include/edit_attn.h"
@@ -489,7 +490,8 @@ edit_status_t static_scratch(void** out) {
 template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
                         hipStream_t s, const Marks& mk, float* lin_den = nullptr,
-                        const edit_convfusion_weights_t* kcf = nullptr, bool apply = true) {
+                        const edit_convfusion_weights_t* kcf = nullptr, bool apply = true,
+                        const std::function<edit_status_t(hipStream_t)>* side_first = nullptr) {
   using namespace edit;
   auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
@@ -568,6 +570,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     if (cf && (st = q_convfusion(s, CF_ALL)) != EDIT_OK) return st;
     if ((st = q_proj(s)) != EDIT_OK) return st;
     if ((st = kv_branch(s)) != EDIT_OK) return st;
+    if (side_first && (st = (*side_first)(s)) != EDIT_OK) return st;
   } else {
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream* side;
@@ -579,6 +582,9 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     // kernel queued ahead of the conv lets those blocks take every CU first.)
     st = cf ? q_convfusion(s, CF_ALL) : EDIT_OK;
     if (st == EDIT_OK) st = q_proj(s);
+    // work of the caller's that depends on neither branch (the hybrid's text Q|K|V) goes first on the side
+    // stream, beside the conv
+    if (st == EDIT_OK && side_first) st = (*side_first)(side->s);
     if (st == EDIT_OK) st = kv_branch(side->s);
     // Join even after a failed launch, so the caller's stream never runs ahead of queued side work.
     const hipError_t e1 = hipEventRecord(side->join, side->s);
@@ -631,21 +637,24 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
   // linear part itself from the head's state (the apply step and y_lin's round trip through memory drop out)
   const bool fuse = g.es == 2 && g.nt > 0 && edit::sdpa_staged_fuses_linear(g.d) &&
                     edit::sdpa_splits(g.N, g.nt, g.heads, g.B, g.d, true) == 1;
+  const int C = g.C, MT = g.B * g.nt;
+  // Text Q | K | V in one GEMM with three weight segments; it reads only x_txt, so it runs on the image
+  // path's side stream beside the conv (the image path joins that stream before it returns).
+  const std::function<edit_status_t(hipStream_t)> text_qkv = [&](hipStream_t ts) -> edit_status_t {
+    GemmArgs<T> a{};
+    a.M = MT; a.N = 3 * C; a.K = C; a.A = static_cast<const T*>(x_txt); a.lda = C;
+    a.Bseg[0] = static_cast<const T*>(wt->w_q); a.Bseg[1] = static_cast<const T*>(wt->w_k);
+    a.Bseg[2] = static_cast<const T*>(wt->w_v);
+    a.bias[0] = static_cast<const T*>(wt->b_q); a.bias[1] = static_cast<const T*>(wt->b_k);
+    a.bias[2] = static_cast<const T*>(wt->b_v);
+    a.seg_rows = C; a.ldb = C; a.C = P(L.qkv_t); a.ldc = 3 * C;
+    EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, ts));
+    return EDIT_OK;
+  };
   edit_status_t st = run_image<T>(g, L, w, static_cast<const T*>(x_img), wsb, s, Marks{nullptr, s},
-                                  fuse ? nullptr : lin_den, nullptr, !fuse);
+                                  fuse ? nullptr : lin_den, nullptr, !fuse, g.nt > 0 ? &text_qkv : nullptr);
   if (st != EDIT_OK) return st;
   if (g.nt == 0) return out_linear<T>(g.M, g.C, w->w_o, w->b_o, P(L.y), static_cast<T*>(y_img), s);
-
-  const int C = g.C, MT = g.B * g.nt;
-  // Text Q | K | V in one GEMM with three weight segments.
-  GemmArgs<T> a{};
-  a.M = MT; a.N = 3 * C; a.K = C; a.A = static_cast<const T*>(x_txt); a.lda = C;
-  a.Bseg[0] = static_cast<const T*>(wt->w_q); a.Bseg[1] = static_cast<const T*>(wt->w_k);
-  a.Bseg[2] = static_cast<const T*>(wt->w_v);
-  a.bias[0] = static_cast<const T*>(wt->b_q); a.bias[1] = static_cast<const T*>(wt->b_k);
-  a.bias[2] = static_cast<const T*>(wt->b_v);
-  a.seg_rows = C; a.ldb = C; a.C = P(L.qkv_t); a.ldc = 3 * C;
-  EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
 
   const T* qkv = P(L.qkv_t);
   const float eta = (float)((double)g.N / ((double)g.N + (double)g.nt));
