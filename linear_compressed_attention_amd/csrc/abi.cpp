@@ -75,10 +75,22 @@ struct Geometry {
   edit_dtype_t dtype;
 };
 
+// Output Linears with few 128-row tiles (the hybrid's text rows) leave most CUs idle: bf16 cuts K = C into
+// S slices (multiples of 64) whose fp32 partials a second kernel sums with the bias; S keeps the tiles of
+// all slices within one per CU. 1: no split.
+int out_splits(int M, int C, int es) {
+  if (es != 2 || C % 192 != 0) return 1;
+  const long tiles = (long)((M + 127) / 128) * (C / 192);
+  int S = 1;
+  for (int k = 2; k <= 8; ++k)
+    if ((C / 64) % k == 0 && tiles * k <= 256) S = k;
+  return S;
+}
+
 struct Layout {
   size_t xc, gn_part, gn_stat, gn_scale, gn_shift, cf_act, q_fold_w, q_fold_b, q, kv0, kc, vc, kv_part, S, z, st,
       zp, y;
-  size_t qkv_t, y_img, y_txt, lin_den, sdpa_part_img, sdpa_part_txt;
+  size_t qkv_t, y_img, y_txt, lin_den, sdpa_part_img, sdpa_part_txt, out_part_txt;
   size_t xc_k, gn_part_k, gn_stat_k, gn_scale_k, gn_shift_k, cf_act_k, k_fold_w, k_fold_b;   // key ConvFusion branch
   size_t total;
 };
@@ -211,6 +223,8 @@ Layout make_layout(const Geometry& g) {
     const int st = edit::sdpa_splits(g.nt, g.Nc + g.nt, g.heads, g.B, g.d, staged);
     L.sdpa_part_img = take(si > 1 ? (size_t)si * g.B * g.heads * g.N * (g.d + 2) * 4 : 0);
     L.sdpa_part_txt = take(st > 1 ? (size_t)st * g.B * g.heads * g.nt * (g.d + 2) * 4 : 0);
+    const int so = out_splits(g.B * g.nt, g.C, g.es);
+    L.out_part_txt = take(so > 1 ? (size_t)so * g.B * g.nt * g.C * 4 : 0);
   }
   L.total = off;
   return L;
@@ -601,13 +615,22 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
 }
 
 template <typename T>
-edit_status_t out_linear(int M, int C, const void* wo, const void* bo, const T* y, T* out, hipStream_t s) {
+edit_status_t out_linear(int M, int C, const void* wo, const void* bo, const T* y, T* out, hipStream_t s,
+                         float* part = nullptr, int S = 1) {
   using namespace edit;
   GemmArgs<T> a{};
   a.M = M; a.N = C; a.K = C; a.A = y; a.lda = C;
   a.Bseg[0] = a.Bseg[1] = a.Bseg[2] = static_cast<const T*>(wo);
   a.bias[0] = a.bias[1] = a.bias[2] = static_cast<const T*>(bo);
   a.seg_rows = C; a.ldb = C; a.C = out; a.ldc = C;
+  if (part != nullptr && S > 1) {
+    // S slices of K into fp32 partials [S][M][C], then their sum plus the bias
+    a.Cf = part; a.split_stride = (long long)M * C; a.kchunk = C / S;
+    EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_F32, s));
+    EDIT_LAUNCH(launch_splitk_reduce<T>(part, S, (long long)M * C, M, C, out, C, s, 0, 0, (T*)nullptr, 0,
+                                        static_cast<const T*>(bo)));
+    return EDIT_OK;
+  }
   EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, s));
   return EDIT_OK;
 }
@@ -691,7 +714,9 @@ edit_status_t run_hybrid(const Geometry& g, const Layout& L, const edit_weights_
 
   st = out_linear<T>(g.M, C, w->w_o, w->b_o, P(L.y_img), static_cast<T*>(y_img), s);
   if (st != EDIT_OK) return st;
-  return out_linear<T>(MT, C, wt->w_o, wt->b_o, P(L.y_txt), static_cast<T*>(y_txt), s);
+  const int so = out_splits(MT, C, g.es);
+  return out_linear<T>(MT, C, wt->w_o, wt->b_o, P(L.y_txt), static_cast<T*>(y_txt), s,
+                       so > 1 ? reinterpret_cast<float*>(wsb + L.out_part_txt) : nullptr, so);
 }
 
 // ---------------------------------------------------------------------------

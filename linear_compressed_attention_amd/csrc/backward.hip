@@ -179,12 +179,16 @@ template <typename O, typename O2>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S,
                                                             long long stride, int rows, int cols,
                                                             O* __restrict__ out, int ldo, int rpg, int gstride,
-                                                            O2* __restrict__ out2, int rsplit) {
+                                                            O2* __restrict__ out2, int rsplit,
+                                                            const O* __restrict__ bias) {
   const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= (long long)rows * cols) return;
   const int r = (int)(i / cols), c = (int)(i - (long long)r * cols);
   f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
   for (int s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4*>(part + (size_t)s * stride + i);
+  // the column bias of a split-K Linear, added once to the full sum
+  if (bias != nullptr)
+    for (int j = 0; j < 4; ++j) v[j] += (float)bias[c + j];
   const float o[4] = {v[0], v[1], v[2], v[3]};
   // rows from rsplit on go to the second output
   if (r < rsplit) store4(out + (size_t)(r % rpg) * ldo + (size_t)(r / rpg) * gstride + c, o);
@@ -193,14 +197,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 template <typename O, typename O2>
 hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int rows, int cols, O* out, int ldo,
-                                hipStream_t s, int rpg, int gstride, O2* out2, int rsplit) {
+                                hipStream_t s, int rpg, int gstride, O2* out2, int rsplit, const O* bias) {
   const long long n = (long long)rows * cols;
   if (n <= 0) return hipSuccess;
   if (out2 == nullptr || rsplit <= 0 || rsplit > rows) rsplit = rows;
   if (rpg <= 0) rpg = rsplit;
   if (cols % 4 || ldo % 4 || gstride % 4 || stride % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL((splitk_reduce_kernel<O, O2>), dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, part, S,
-                     stride, rows, cols, out, ldo, rpg, gstride, out2, rsplit);
+                     stride, rows, cols, out, ldo, rpg, gstride, out2, rsplit, bias);
   return hipGetLastError();
 }
 
@@ -1027,7 +1031,7 @@ hipError_t launch_small_nt(int M, int N, int K, const float* A, int lda, const T
 
 // fp32 rows to one output, bf16 rows to the other (one launch for two weight gradients)
 template hipError_t launch_splitk_reduce<float, bf16>(const float*, int, long long, int, int, float*, int, hipStream_t,
-                                                      int, int, bf16*, int);
+                                                      int, int, bf16*, int, const float*);
 
 #define EDIT_INST(T)                                                                                               \
   template hipError_t launch_transpose<T>(const T*, int, int, int, T*, int, hipStream_t, int, int, long, long,    \
@@ -1036,7 +1040,7 @@ template hipError_t launch_splitk_reduce<float, bf16>(const float*, int, long lo
   template hipError_t launch_colsum_finalize<T>(const float*, int, int, T*, hipStream_t, float*, T*, int);        \
   template hipError_t launch_zero<T>(T*, long, hipStream_t);                                                       \
   template hipError_t launch_splitk_reduce<T, T>(const float*, int, long long, int, int, T*, int, hipStream_t,   \
-                                                 int, int, T*, int);                                              \
+                                                 int, int, T*, int, const T*);                                    \
   template hipError_t launch_attn_bwd_q<T>(const T*, const T*, const float*, const float*, int, int, int, int,     \
                                            float, T*, float*, T*, hipStream_t);                                    \
   template hipError_t launch_kv_bwd<T>(const T*, const T*, const float*, const float*, int, int, int, int, float*, \

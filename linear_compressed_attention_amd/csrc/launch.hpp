@@ -158,10 +158,12 @@ hipError_t launch_colsum_finalize(const float* part, int rows, int n, T* out, hi
 template <typename T>
 hipError_t launch_zero(T* p, long n, hipStream_t s);
 // out[(r % rpg) * ldo + (r / rpg) * gstride + c] = sum_s part[s * stride + r * cols + c] (rpg 0: rows).
-// With out2, rows r >= rsplit go to out2 at row r - rsplit instead (rpg 0: rsplit).
+// With out2, rows r >= rsplit go to out2 at row r - rsplit instead (rpg 0: rsplit). With bias, bias[c] is
+// added to every row's sum.
 template <typename O, typename O2 = O>
 hipError_t launch_splitk_reduce(const float* part, int S, long long stride, int rows, int cols, O* out, int ldo,
-                                hipStream_t s, int rpg = 0, int gstride = 0, O2* out2 = nullptr, int rsplit = 0);
+                                hipStream_t s, int rpg = 0, int gstride = 0, O2* out2 = nullptr, int rsplit = 0,
+                                const O* bias = nullptr);
 // Linear-attention backward, query side: g = dy / den, c = -(dy . y) / den, dq_pre = (g S^T + c z) where q > 0.
 template <typename T>
 hipError_t launch_attn_bwd_q(const T* dy, const T* q, const float* S, const float* z, int B, int N, int heads, int d,
