@@ -12,16 +12,18 @@
 // V^T as [dim][key] -- then its eight waves walk the segment's tiles with no
 // barrier. A block restages only where its run crosses into the next segment.
 //
-// Tile. A wave holds the scores S^T = K Q^T of 96 keys x 32 queries in
-// registers (three 32x32x16 matrix-core products per 16 head dims): lane l
-// has query l % 32 and, of each 32-key group, keys 4h+r, 8+4h+r, 16+4h+r and
-// 24+4h+r (h = l / 32, r < 4). Online softmax in the exp2 domain: the chunk
-// maximum (the two lane halves exchanged by v_permlane32_swap), then
+// Tile. A wave takes a tile of 32 queries and walks the keys in 32-key
+// tiles, two score tiles in flight (the next one's products are issued
+// before this one's softmax): the scores S^T = K Q^T of a key tile (one
+// 32x32x16 matrix-core product per 16 head dims) sit in registers, lane l
+// holding query l % 32 and keys 4h+r, 8+4h+r, 16+4h+r and 24+4h+r (h = l /
+// 32, r < 4). Online softmax in the exp2 domain: the key tile's maximum (the
+// two lane halves exchanged by v_permlane32_swap), then
 // p = 2^((s - m) log2(e) / sqrt(d)) rounded to bf16, and O^T += V^T P^T with
 // P^T the second operand straight from those registers (V^T is staged in the
 // matching key order). The running maximum m is raised lazily: only when a
-// chunk's maximum exceeds it by more than 2^8 in the exponent, so p <= 256
-// and most chunks need no rescale of O and of the row sum. The row sum adds
+// key tile's maximum exceeds it by more than 2^8 in the exponent, so p <= 256
+// and most key tiles need no rescale of O and of the row sum. The row sum adds
 // the bf16-rounded p (v_dot2 with ones): the normaliser sums the same
 // weights the PV product used.
 //

@@ -152,6 +152,11 @@ HYB = {
                              x_std=1.0),
     "bf16_d72": make_shape(B=1, H=8, W=8, C=288, heads=4, head_dim=72, reduction=4, gn_groups=4, dtype="bf16",
                            x_std=1.0),
+    # narrower heads: the softmax blocks' two-query-tile waves at 2 and 3 head-dim steps of 16
+    "bf16_d32": make_shape(B=2, H=10, W=12, C=128, heads=4, head_dim=32, reduction=4, gn_groups=4, dtype="bf16",
+                           x_std=1.0),
+    "bf16_d48": make_shape(B=1, H=16, W=14, C=192, heads=4, head_dim=48, reduction=4, gn_groups=4, dtype="bf16",
+                           x_std=1.0),
     # enough keys that the softmax blocks split them (bf16: splits of 384 keys, so 300 text keys give the
     # text rows two splits over 256 + 300 keys, and 500 text keys split the image rows as well, both
     # problems writing partials in the one launch; fp32: the one-pass kernel's splits)
@@ -167,6 +172,7 @@ HYB = {
 
 @pytest.mark.parametrize("name,n_text", [("f32_small", 37), ("bf16_small", 77), ("bf16_d72", 5), ("f32_small", 1),
                                          ("bf16_many_keys", 300), ("bf16_many_keys", 500), ("bf16_d72", 420),
+                                         ("bf16_d32", 45), ("bf16_d48", 100), ("bf16_d48", 450),
                                          ("f32_many_keys", 300), ("f32_many_queries", 40)])
 def test_hybrid_small(name, n_text):
     check_hybrid(HYB[name], n_text, seed=2)
@@ -179,7 +185,7 @@ def test_hybrid_sd35m_full_size():
 
 @pytest.mark.parametrize("name,n_text", [("f32_small", 37), ("bf16_small", 77), ("bf16_d72", 5),
                                          ("bf16_many_keys", 300), ("bf16_many_keys", 500), ("bf16_d72", 420),
-                                         ("f32_many_keys", 300)])
+                                         ("bf16_d32", 45), ("f32_many_keys", 300)])
 def test_hybrid_exact_eta_small(name, n_text):
     check_hybrid(HYB[name], n_text, seed=6, exact=True)
 
