@@ -95,6 +95,13 @@ struct Layout {
   size_t total;
 };
 
+// State partials per (sample, head): the bf16 compressed path forms them in the depthwise kernel over 2-D
+// tiles of the compressed grid, every other path over runs of consecutive key/value tokens.
+int state_chunks(const Geometry& g) {
+  if (g.kvmode == EDIT_KV_COMPRESSED && g.es == 2) return edit::dw_state_chunks(g.Hc, g.Wc);
+  return edit::kv_state_chunks(g.Nkv);
+}
+
 edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
   if (!s) return fail(EDIT_ERR_ARG, "shape is NULL");
   if (s->B <= 0 || s->H <= 0 || s->W <= 0 || s->C <= 0 || s->heads <= 0 || s->head_dim <= 0 ||
@@ -127,10 +134,10 @@ edit_status_t check_shape(const edit_shape_t* s, int n_text, Geometry* g) {
   g->Hc = (s->H + 1) / 2; g->Wc = (s->W + 1) / 2; g->Nc = g->Hc * g->Wc; g->nt = n_text;
   g->qmode = EDIT_QUERY_CONVFUSION; g->kvmode = EDIT_KV_COMPRESSED; g->Nkv = g->Nc;
   g->gn_chunks = edit::groupnorm_chunks(g->N, Cr);
-  g->kv_chunks = edit::kv_state_chunks(g->Nkv);
   g->DT = (g->d + 15) / 16; g->DR = (g->d + 16) / 16;
   g->DP = edit::kv_state_dp(g->d); g->DK = edit::kv_state_dk(g->d);
   g->es = s->dtype == EDIT_BF16 ? 2 : 4;
+  g->kv_chunks = state_chunks(*g);
   g->eps = s->eps;
   g->dtype = s->dtype;
   return EDIT_OK;
@@ -147,7 +154,7 @@ edit_status_t apply_variant(const edit_variant_t* v, Geometry* g) {
   g->qmode = qm;
   g->kvmode = kvm;
   g->Nkv = kvm == EDIT_KV_COMPRESSED ? g->Nc : g->N;
-  g->kv_chunks = edit::kv_state_chunks(g->Nkv);
+  g->kv_chunks = state_chunks(*g);
   return EDIT_OK;
 }
 
@@ -544,7 +551,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
         EDIT_LAUNCH(launch_dwconv_kv_state<T>(P(L.kv0), g.B, g.H, g.W, g.C, g.heads, g.d,
                                               static_cast<const T*>(w->dw_k), static_cast<const T*>(w->db_k),
                                               static_cast<const T*>(w->dw_v), static_cast<const T*>(w->db_v),
-                                              P(L.kc), P(L.vc), F(L.kv_part), ks));
+                                              P(L.kc), P(L.vc), F(L.kv_part), g.kv_chunks, ks));
         EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_STATE));
         // 7. the per-head state: the chunk partials merged
         EDIT_LAUNCH(launch_kv_state_finalize<T>(F(L.kv_part), g.B, g.heads, g.d, g.kv_chunks, F(L.S), F(L.z),

@@ -23,6 +23,28 @@ namespace edit {
 constexpr int kKvChunk = 256;   // compressed tokens per state partial
 
 int kv_state_chunks(int Nc) { return (Nc + kKvChunk - 1) / kKvChunk; }
+
+// The fused depthwise + state kernel takes its chunks as tiles of the compressed grid, TH x TW = kKvChunk
+// tokens (both powers of two, TW even so that a token pair shares a row): 16 x 16 where the grid allows, so a
+// chunk reads (2 TH + 1) x (2 TW + 1) input pixels for 4 TH TW (the halo 6% instead of up to 50% for chunks
+// of whole compressed rows); shorter or narrower grids take wider or taller tiles.
+DwStateTile dw_state_tile(int Hc, int Wc) {
+  auto p2 = [](int v) { int p = 1; while (p < v) p <<= 1; return p; };
+  DwStateTile t;
+  t.th = std::min(16, p2(std::max(1, Hc)));
+  t.tw = kKvChunk / t.th;
+  if (t.tw > p2(std::max(2, Wc))) {
+    t.tw = p2(std::max(2, Wc));
+    t.th = kKvChunk / t.tw;
+  }
+  t.ncy = (Hc + t.th - 1) / t.th;
+  t.ncx = (Wc + t.tw - 1) / t.tw;
+  return t;
+}
+int dw_state_chunks(int Hc, int Wc) {
+  const DwStateTile t = dw_state_tile(Hc, Wc);
+  return t.ncy * t.ncx;
+}
 int kv_state_dp(int d) { return 16 * ((d + 15) / 16); }
 int kv_state_dk(int d) { return 32 * ((d + 31) / 32); }
 
@@ -191,18 +213,22 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
 // The Spatial Compressor's depthwise 3x3 stride-2 convs and the state
 // partials in one kernel (sections "Spatial Compressor" and
 // "Linear-attention formula"): a block makes the compressed keys and values
-// of one head over one 256-token chunk, K' = ReLU(DW(k0) + b_k) and
-// V' = DW(v0) + b_v, writes them (kc, vc: the backward and the hybrid read
-// them), and, with the values still on chip, their chunk partial of
-// S^T = V'^T K' and z = sum K' on the matrix cores, the same partial
-// kv_state_partial_kernel writes from kc, vc (so kv_state_finalize_kernel
-// merges them unchanged). The compressed tensors are not read back.
+// of one head over one chunk of 256 compressed tokens, K' = ReLU(DW(k0) +
+// b_k) and V' = DW(v0) + b_v, writes them (kc, vc: the backward and the
+// hybrid read them), and, with the values still on chip, their chunk
+// partial of S^T = V'^T K' and z = sum K' on the matrix cores, in the layout
+// kv_state_partial_kernel writes (so kv_state_finalize_kernel merges them
+// unchanged). A chunk is a th x tw tile of the compressed grid
+// (dw_state_tile: 16 x 16 where the grid allows), so that the input rows and
+// columns it shares with its neighbours (the taps' one-pixel border) are a
+// small part of what it reads. The compressed tensors are not read back.
 // Item e of a block: channel chunk c8 (fastest, so a token's head slice is
-// one contiguous run across lanes), token quad, K or V; an item convolves
-// four consecutive compressed tokens (each from its nine taps, loads at
-// clamped in-image positions, taps outside the image adding zero) and
-// writes them to LDS as one four-token word per channel, channel-major with
-// the kv_col swizzle, as kv_state_partial_kernel stages them.
+// one contiguous run across lanes), token pair (two neighbours in a tile
+// row), K or V; an item convolves its two tokens (each from its nine taps,
+// loads at clamped in-image positions, taps outside the image adding zero;
+// a token outside the grid is computed at a clamped position and zeroed)
+// and writes them to LDS as one two-token word per channel, channel-major
+// with the kv_col swizzle, the token's place in the tile as its column.
 // ---------------------------------------------------------------------------
 constexpr int kDwStateThreads = 512;   // 8 waves: two per SIMD overlap one another's loads
 
@@ -216,7 +242,7 @@ template <typename T, int DC>
 __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
     const T* __restrict__ kv0, int H, int W, int heads, int nchunks, const T* __restrict__ dwk,
     const T* __restrict__ dbk, const T* __restrict__ dwv, const T* __restrict__ dbv, T* __restrict__ kc,
-    T* __restrict__ vc, float* __restrict__ partial) {
+    T* __restrict__ vc, float* __restrict__ partial, int twl, int ncx) {
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   constexpr int NTH = kDwStateThreads;
   constexpr int d = 8 * DC;
@@ -235,7 +261,11 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
   const int lb = xcd_swizzle((int)blockIdx.x, (int)gridDim.x);
   const int h = lb % heads, chunk = (lb / heads) % nchunks, b = lb / heads / nchunks;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int j0 = chunk * kKvChunk, j1 = min(Nc, j0 + kKvChunk);
+  // the chunk's tile: compressed rows y0 .., columns x0 .. x0 + tw - 1 (tw = 2^twl); token t of the tile at
+  // (y0 + t / tw, x0 + t % tw)
+  const int tw = 1 << twl, cy = chunk / ncx;
+  const int y0 = cy * (SLAB >> twl), x0 = (chunk - cy * ncx) * tw;
+  auto in_grid = [&](int t) { return y0 + (t >> twl) < Hc && x0 + (t & (tw - 1)) < Wc; };
   const T* img = kv0 + (size_t)b * H * W * 2 * C;
 
   // rows that receive no token data: K' channels d .. 16 DT - 1, and the rows
@@ -246,7 +276,7 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
     for (int i = tid; i < (16 * DT - d) * W16; i += NTH) reinterpret_cast<u32x4v*>(Kt + d * PITCH)[i] = zero;
     for (int i = tid; i < (16 * DR - d - 2) * W16; i += NTH) reinterpret_cast<u32x4v*>(At + (d + 2) * PITCH)[i] = zero;
     for (int t = tid; t < SLAB; t += NTH) {
-      At[d * PITCH + kv_col(d, t)] = from_f32<T>(j0 + t < j1 ? 1.0f : 0.0f);
+      At[d * PITCH + kv_col(d, t)] = from_f32<T>(in_grid(t) ? 1.0f : 0.0f);
       At[(d + 1) * PITCH + kv_col(d + 1, t)] = from_f32<T>(0.0f);
     }
   }
@@ -260,11 +290,13 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
     // the bias) is issued before any is used.
     u32x4v raw[2][9];
     int yo[2], xo[2];
+    const int ty = y0 + ((2 * tp) >> twl), tx = x0 + ((2 * tp) & (tw - 1));
+    bool ok[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int j = min(j0 + 2 * tp + u, j1 - 1);        // tokens past the chunk: recomputed, then zeroed
-      yo[u] = j / Wc;
-      xo[u] = j - yo[u] * Wc;
+      ok[u] = ty < Hc && tx + u < Wc;                    // tokens outside the grid: clamped, then zeroed
+      yo[u] = min(ty, Hc - 1);
+      xo[u] = min(tx + u, Wc - 1);
 #pragma unroll
       for (int t = 0; t < 9; ++t) {
         const int yc = min(max(2 * yo[u] + t / 3 - 1, 0), H - 1), xc = min(max(2 * xo[u] + t % 3 - 1, 0), W - 1);
@@ -279,7 +311,6 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
     for (int i = 0; i < 8; ++i) o[1][i] = o[0][i];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int j = j0 + 2 * tp + u;
 #pragma unroll
       for (int t = 0; t < 9; ++t) {
         const int yy = 2 * yo[u] + t / 3 - 1, xx = 2 * xo[u] + t % 3 - 1;
@@ -292,8 +323,8 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[u][i] = o[u][i] > 0.0f ? o[u][i] : 0.0f;
       }
-      if (j < j1) {
-        store8((which ? vc : kc) + ((size_t)b * Nc + j) * C + h * d + c8, o[u]);
+      if (ok[u]) {
+        store8((which ? vc : kc) + ((size_t)b * Nc + (size_t)yo[u] * Wc + xo[u]) * C + h * d + c8, o[u]);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[u][i] = 0.0f;
@@ -426,19 +457,22 @@ hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int 
 template <typename T>
 hipError_t launch_dwconv_kv_state(const T* kv0, int B, int H, int W, int C, int heads, int d, const T* dwk,
                                   const T* dbk, const T* dwv, const T* dbv, T* kc, T* vc, float* partial,
-                                  hipStream_t s) {
+                                  int nchunks, hipStream_t s) {
   if constexpr (sizeof(T) != 2) {
     return hipErrorNotSupported;   // fp32 keeps the two-kernel form (slabs of 64 tokens)
   } else {
     if (C != heads * d) return hipErrorInvalidValue;
-    const int Nc = ((H + 1) / 2) * ((W + 1) / 2), nchunks = kv_state_chunks(Nc);
+    const DwStateTile tile = dw_state_tile((H + 1) / 2, (W + 1) / 2);
+    if (nchunks != tile.ncy * tile.ncx) return hipErrorInvalidValue;
     if ((long long)nchunks * heads * B >= (1LL << 31)) return hipErrorInvalidValue;
+    int twl = 0;
+    while ((1 << twl) < tile.tw) ++twl;
     dim3 grid(nchunks * heads * B);
     switch (d / 8) {
 #define EDIT_DKV_CASE(DCV)                                                                                   \
   case DCV:                                                                                                  \
     hipLaunchKernelGGL((dwconv_kv_state_kernel<T, DCV>), grid, dim3(kDwStateThreads), 0, s, kv0, H, W, heads, \
-                       nchunks, dwk, dbk, dwv, dbv, kc, vc, partial);                                        \
+                       nchunks, dwk, dbk, dwv, dbv, kc, vc, partial, twl, tile.ncx);                         \
     break;
       EDIT_DKV_CASE(1) EDIT_DKV_CASE(2) EDIT_DKV_CASE(3) EDIT_DKV_CASE(4) EDIT_DKV_CASE(5) EDIT_DKV_CASE(6)
       EDIT_DKV_CASE(7) EDIT_DKV_CASE(8) EDIT_DKV_CASE(9) EDIT_DKV_CASE(10) EDIT_DKV_CASE(11) EDIT_DKV_CASE(12)
@@ -970,7 +1004,7 @@ hipError_t launch_sdpa_pair(const SdpaArgs<T>& a, const SdpaArgs<T>& b, hipStrea
   template hipError_t launch_kv_state<T>(const T*, const T*, int, int, int, int, int, float*, int, float*, \
                                          float*, T*, float*, hipStream_t, const float*);                              \
   template hipError_t launch_dwconv_kv_state<T>(const T*, int, int, int, int, int, int, const T*, const T*,       \
-                                                const T*, const T*, T*, T*, float*, hipStream_t);                 \
+                                                const T*, const T*, T*, T*, float*, int, hipStream_t);            \
   template hipError_t launch_kv_state_finalize<T>(const float*, int, int, int, int, float*, float*, T*, float*,   \
                                                   hipStream_t);                                                   \
   template hipError_t launch_linattn_apply<T>(const T*, int, const T*, const float*, int, int, int, int, \

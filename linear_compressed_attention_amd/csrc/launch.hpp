@@ -120,14 +120,20 @@ hipError_t launch_kv_state(const T* kc, const T* vc, int ld, int B, int Nc, int 
                            int nchunks, float* S, float* z, T* st, float* zp, hipStream_t s,
                            const float* wrow = nullptr);
 int kv_state_chunks(int Nc);
-// The depthwise stride-2 convs (as launch_dwconv_s2) and the per-head state partials (as
-// launch_kv_state's first kernel over kc, vc) in one pass over kv0: kc, vc are written and the
-// partials [B][h][kv_state_chunks(Nc)][..] formed from the values on chip; launch_kv_state_finalize
-// then merges them. bf16 only (hipErrorNotSupported, nothing launched, for fp32).
+// Chunks of the fused depthwise + state kernel: th x tw compressed tokens (th * tw = 256), ncy x ncx of them
+// over an Hc x Wc grid.
+struct DwStateTile { int th, tw, ncy, ncx; };
+DwStateTile dw_state_tile(int Hc, int Wc);
+int dw_state_chunks(int Hc, int Wc);
+// The depthwise stride-2 convs (as launch_dwconv_s2) and the per-head state partials (one per chunk, as
+// launch_kv_state's first kernel forms them from kc, vc, but over dw_state_tile's 2-D chunks of the
+// compressed grid) in one pass over kv0: kc, vc are written and the partials [B][h][nchunks][..] formed from
+// the values on chip; launch_kv_state_finalize then merges them. nchunks must be dw_state_chunks(Hc, Wc)
+// (else hipErrorInvalidValue). bf16 only (hipErrorNotSupported, nothing launched, for fp32).
 template <typename T>
 hipError_t launch_dwconv_kv_state(const T* kv0, int B, int H, int W, int C, int heads, int d, const T* dwk,
                                   const T* dbk, const T* dwv, const T* dbv, T* kc, T* vc, float* partial,
-                                  hipStream_t s);
+                                  int nchunks, hipStream_t s);
 // S, z, st, zp of launch_kv_state from its chunk partials (summed in chunk order).
 template <typename T>
 hipError_t launch_kv_state_finalize(const float* partial, int B, int heads, int d, int nchunks, float* S, float* z,
