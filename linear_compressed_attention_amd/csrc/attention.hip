@@ -231,6 +231,14 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
 // with the kv_col swizzle, the token's place in the tile as its column.
 // ---------------------------------------------------------------------------
 constexpr int kDwStateThreads = 512;   // 8 waves: two per SIMD overlap one another's loads
+constexpr uint32_t kDwOob = 0x80000000u;   // past the sample's buffer resource: the load returns zeros
+
+typedef __bf16 dw_bf16x2 __attribute__((ext_vector_type(2)));
+
+// c + a.lo * b.lo + a.hi * b.hi for two bf16 pairs held in 32-bit words.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dw_bf16x2, a), __builtin_bit_cast(dw_bf16x2, b), c, false);
+}
 
 // Two tokens' values of one channel, written to LDS as one 4-byte word.
 __device__ __forceinline__ void store_pair(bf16* dst, bf16 a, bf16 b) {
@@ -267,6 +275,14 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
   const int y0 = cy * (SLAB >> twl), x0 = (chunk - cy * ncx) * tw;
   auto in_grid = [&](int t) { return y0 + (t >> twl) < Hc && x0 + (t & (tw - 1)) < Wc; };
   const T* img = kv0 + (size_t)b * H * W * 2 * C;
+  // the sample's [k0 | v0] rows as a buffer resource (the launch checks that its bytes stay below kDwOob)
+  const __amdgpu_buffer_rsrc_t rsI =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(img), (short)0, (int)((uint32_t)H * W * 4u * C), 0x00020000);
+  const uint32_t pixb = 4u * (uint32_t)C;   // bytes per pixel of kv0 (2C bf16)
+  // byte step of tap (ky, kx) from the top-left tap, uniform (held as scalars, added as they are)
+  uint32_t tapo[9];
+#pragma unroll
+  for (int t = 0; t < 9; ++t) tapo[t] = __builtin_amdgcn_readfirstlane((uint32_t)((t / 3) * W + t % 3) * pixb);
 
   // rows that receive no token data: K' channels d .. 16 DT - 1, and the rows
   // of A past V'^T and the two weight rows (ones, zeros: z = sum K')
@@ -286,9 +302,9 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
     const int tp = rest % PAIRS, which = rest / PAIRS;   // which: 0 keys, 1 values
     const int cin = which * C + h * d + c8;              // channel in kv0's [k0 | v0] row
     const T* wt = (which ? dwv : dwk) + h * d + c8;
-    // Every load of the item (nine taps of two tokens, the taps' weights and
-    // the bias) is issued before any is used.
-    u32x4v raw[2][9];
+    // Every load of the item (nine taps of two tokens, the taps' weights and the bias) is issued before any is
+    // used. A tap outside the image reads at an offset past the sample's resource, which returns zeros.
+    u32x4v raw[2][9], wr[9];
     int yo[2], xo[2];
     const int ty = y0 + ((2 * tp) >> twl), tx = x0 + ((2 * tp) & (tw - 1));
     bool ok[2];
@@ -297,27 +313,62 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
       ok[u] = ty < Hc && tx + u < Wc;                    // tokens outside the grid: clamped, then zeroed
       yo[u] = min(ty, Hc - 1);
       xo[u] = min(tx + u, Wc - 1);
+      // tap (ky, kx) reads pixel (2 yo + ky - 1, 2 xo + kx - 1): the top-left tap's byte offset (wrapping
+      // below zero for a border token, whose border taps are masked) plus the tap's fixed step; only the
+      // border rows and columns can fall outside the image
+      const uint32_t base = (uint32_t)((2 * yo[u] - 1) * W + 2 * xo[u] - 1) * pixb + 2u * (uint32_t)cin;
+      const bool top = yo[u] > 0, bot = 2 * yo[u] + 1 < H, lef = xo[u] > 0, rig = 2 * xo[u] + 1 < W;
 #pragma unroll
       for (int t = 0; t < 9; ++t) {
-        const int yc = min(max(2 * yo[u] + t / 3 - 1, 0), H - 1), xc = min(max(2 * xo[u] + t % 3 - 1, 0), W - 1);
-        raw[u][t] = *reinterpret_cast<const u32x4v*>(img + ((size_t)yc * W + xc) * 2 * C + cin);
+        const int ky = t / 3, kx = t % 3;
+        bool in = true;
+        if (ky == 0) in = in & top;
+        if (ky == 2) in = in & bot;
+        if (kx == 0) in = in & lef;
+        if (kx == 2) in = in & rig;
+        const uint32_t off = in ? base + tapo[t] : kDwOob;
+        raw[u][t] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rsI, (int)off, 0, 0));
       }
     }
-    float wv[9][8], o[2][8];
 #pragma unroll
-    for (int t = 0; t < 9; ++t) load8(wt + t * C, wv[t]);
+    for (int t = 0; t < 9; ++t) wr[t] = *reinterpret_cast<const u32x4v*>(wt + t * C);
+    float o[2][8];
     load8((which ? dbv : dbk) + h * d + c8, o[0]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[1][i] = o[0][i];
+    // Taps in pairs (0,1) (2,3) (4,5) (6,7) on v_dot2: word k of a tap holds channels 2k and 2k+1; the pair's
+    // lo halves (channel 2k of both taps) and hi halves (channel 2k+1) are regrouped into one word each, the
+    // weights once per item. Tap 8 alone, by fma.
+    uint32_t wp[4][4][2];
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a = wr[2 * pr][k], bw = wr[2 * pr + 1][k];
+        wp[pr][k][0] = (a & 0xFFFFu) | (bw << 16);
+        wp[pr][k][1] = (a >> 16) | (bw & 0xFFFF0000u);
+      }
+    float w8[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w8[2 * k] = __builtin_bit_cast(float, wr[8][k] << 16);
+      w8[2 * k + 1] = __builtin_bit_cast(float, wr[8][k] & 0xFFFF0000u);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int t = 0; t < 9; ++t) {
-        const int yy = 2 * yo[u] + t / 3 - 1, xx = 2 * xo[u] + t % 3 - 1;
-        const bool in = yy >= 0 && yy < H && xx >= 0 && xx < W;
-        const T* v = reinterpret_cast<const T*>(&raw[u][t]);
+      for (int pr = 0; pr < 4; ++pr)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[u][i] += in ? wv[t][i] * to_f32(v[i]) : 0.0f;
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t a = raw[u][2 * pr][k], bx = raw[u][2 * pr + 1][k];
+          o[u][2 * k] = dot2_bf16((a & 0xFFFFu) | (bx << 16), wp[pr][k][0], o[u][2 * k]);
+          o[u][2 * k + 1] = dot2_bf16((a >> 16) | (bx & 0xFFFF0000u), wp[pr][k][1], o[u][2 * k + 1]);
+        }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[u][2 * k] = __builtin_fmaf(w8[2 * k], __builtin_bit_cast(float, raw[u][8][k] << 16), o[u][2 * k]);
+        o[u][2 * k + 1] =
+            __builtin_fmaf(w8[2 * k + 1], __builtin_bit_cast(float, raw[u][8][k] & 0xFFFF0000u), o[u][2 * k + 1]);
       }
       if (!which) {
 #pragma unroll
@@ -464,6 +515,8 @@ hipError_t launch_dwconv_kv_state(const T* kv0, int B, int H, int W, int C, int 
     if (C != heads * d) return hipErrorInvalidValue;
     const DwStateTile tile = dw_state_tile((H + 1) / 2, (W + 1) / 2);
     if (nchunks != tile.ncy * tile.ncx) return hipErrorInvalidValue;
+    // a sample's rows are addressed by 32-bit offsets below the out-of-range marker
+    if ((size_t)H * W * 4 * C >= kDwOob) return hipErrorNotSupported;
     if ((long long)nchunks * heads * B >= (1LL << 31)) return hipErrorInvalidValue;
     int twl = 0;
     while ((1 << twl) < tile.tw) ++twl;
