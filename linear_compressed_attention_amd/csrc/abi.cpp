@@ -531,8 +531,24 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     if (cf) return cat_linear<T>(g, x, P(L.cf_act), P(L.q_fold_w), P(L.q_fold_b), P(L.q), g.C, fork, qs);
     return linear_cc<T>(g, x, w->w_q, w->b_q, P(L.q), g.C, true, fork, qs);
   };
-  // 5-7. keys, values and the per-head state S, z
-  auto kv_branch = [&](hipStream_t ks) -> edit_status_t {
+  // 6-7 at bf16 with compressed keys / values: the depthwise convs with the state partials in one pass, then
+  // their merge into S, z
+  auto dw_state = [&](hipStream_t ks) -> edit_status_t {
+    if constexpr (std::is_same<T, bf16>::value) {
+      EDIT_LAUNCH(launch_dwconv_kv_state<T>(P(L.kv0), g.B, g.H, g.W, g.C, g.heads, g.d,
+                                            static_cast<const T*>(w->dw_k), static_cast<const T*>(w->db_k),
+                                            static_cast<const T*>(w->dw_v), static_cast<const T*>(w->db_v),
+                                            P(L.kc), P(L.vc), F(L.kv_part), g.kv_chunks, ks));
+      EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_STATE));
+      EDIT_LAUNCH(launch_kv_state_finalize<T>(F(L.kv_part), g.B, g.heads, g.d, g.kv_chunks, F(L.S), F(L.z),
+                                              P(L.st), F(L.zp), ks));
+    }
+    return EDIT_OK;
+  };
+  const bool fused_dw = std::is_same<T, bf16>::value && g.kvmode == EDIT_KV_COMPRESSED;
+  // 5-7. keys, values and the per-head state S, z (with_dw false: the bf16 compressed path stops after the
+  // key/value GEMM and leaves dw_state to the caller)
+  auto kv_branch = [&](hipStream_t ks, bool with_dw) -> edit_status_t {
     edit_status_t st;
     EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_PROJ));
     const T *kk, *vv;
@@ -547,17 +563,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
       EDIT_LAUNCH(launch_gemm<T>(a, A_PLAIN, E_BIAS, ks));
       EDIT_LAUNCH(mk.mark(EDIT_STEP_SC_DWCONV));
       // 6. compressed keys / values (bf16: with the state partials of step 7 in the same pass)
-      if constexpr (std::is_same<T, bf16>::value) {
-        EDIT_LAUNCH(launch_dwconv_kv_state<T>(P(L.kv0), g.B, g.H, g.W, g.C, g.heads, g.d,
-                                              static_cast<const T*>(w->dw_k), static_cast<const T*>(w->db_k),
-                                              static_cast<const T*>(w->dw_v), static_cast<const T*>(w->db_v),
-                                              P(L.kc), P(L.vc), F(L.kv_part), g.kv_chunks, ks));
-        EDIT_LAUNCH(mk.mark(EDIT_STEP_KV_STATE));
-        // 7. the per-head state: the chunk partials merged
-        EDIT_LAUNCH(launch_kv_state_finalize<T>(F(L.kv_part), g.B, g.heads, g.d, g.kv_chunks, F(L.S), F(L.z),
-                                                P(L.st), F(L.zp), ks));
-        return EDIT_OK;
-      }
+      if (fused_dw) return with_dw ? dw_state(ks) : EDIT_OK;
       EDIT_LAUNCH(launch_dwconv_s2<T>(P(L.kv0), g.B, g.H, g.W, g.C, static_cast<const T*>(w->dw_k),
                                       static_cast<const T*>(w->db_k), static_cast<const T*>(w->dw_v),
                                       static_cast<const T*>(w->db_v), P(L.kc), P(L.vc), ks));
@@ -590,7 +596,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
   if (!fork) {
     if (cf && (st = q_convfusion(s, CF_ALL)) != EDIT_OK) return st;
     if ((st = q_proj(s)) != EDIT_OK) return st;
-    if ((st = kv_branch(s)) != EDIT_OK) return st;
+    if ((st = kv_branch(s, true)) != EDIT_OK) return st;
     if (side_first && (st = (*side_first)(s)) != EDIT_OK) return st;
   } else {
     std::lock_guard<std::mutex> lock(g_side_mu);
@@ -606,12 +612,17 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     // work of the caller's that depends on neither branch (the hybrid's text Q|K|V) goes first on the side
     // stream, beside the conv
     if (st == EDIT_OK && side_first) st = (*side_first)(side->s);
-    if (st == EDIT_OK) st = kv_branch(side->s);
+    // The bf16 compressed path joins after its key/value GEMM, which ends well before the query GEMM, so the
+    // caller's stream finds the join already satisfied; the depthwise + state pass then follows the query GEMM
+    // on the caller's stream with the whole chip (a join behind a still-running side stream leaves the chip
+    // idle ~11 us on MI355X).
+    if (st == EDIT_OK) st = kv_branch(side->s, !fused_dw);
     // Join even after a failed launch, so the caller's stream never runs ahead of queued side work.
     const hipError_t e1 = hipEventRecord(side->join, side->s);
     const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(s, side->join, 0) : e1;
     if (st != EDIT_OK) return st;
     if (e2 != hipSuccess) return fail(EDIT_ERR_HIP, "joining the key/value stream failed: %s", hipGetErrorString(e2));
+    if (fused_dw && (st = dw_state(s)) != EDIT_OK) return st;
   }
   EDIT_LAUNCH(mk.mark(EDIT_STEP_APPLY));
   // 8. y = q S / (q . z + eps) (the hybrid may form it inside its image-row softmax instead)
