@@ -544,8 +544,10 @@ hipError_t launch_dwconv_kv_state(const T* kv0, int B, int H, int W, int C, int 
 // walks 16-token tiles: Y^T = S^T Q^T with B = 16 queries read straight from
 // memory as 16-byte fragments (the next tile's are requested before the
 // current tile's matrix work). Lane l ends with 4 consecutive output channels
-// of token l % 16 (8-byte store). The denominator is a VALU dot of the lane's
-// query slice with z, summed over the four lanes that share a token.
+// of token l % 16 per 16-channel tile; at bf16 lanes l and l ^ 16 swap halves
+// of two tiles so that each stores 8 consecutive channels (16 bytes). The
+// denominator is a VALU dot of the lane's query slice with z, summed over the
+// four lanes that share a token.
 // ---------------------------------------------------------------------------
 constexpr int kApplyTokens = 512;   // tokens per block (32 tiles, 8 per wave)
 
@@ -647,16 +649,46 @@ __global__ __launch_bounds__(256) void linattn_apply_kernel(const T* __restrict_
         mma16(acc[tn], ahi[tn][s], bq[c][s]);
       }
     }
-    if (tok < N) {
-      T* yrow = y + ((size_t)b * N + tok) * ldy + h * d;
+    T* yrow = y + ((size_t)b * N + min(tok, N - 1)) * ldy + h * d;
+    if constexpr (SPLIT) {
+      // Lanes l and l ^ 16 (g and g ^ 1) hold channels 4g .. 4g+3 of each 16-channel tile. For the tiles tn,
+      // tb of a pair, even g keeps tn's four and takes its partner's four of tn, odd g keeps tb's and takes
+      // its partner's of tb: every lane then stores 8 consecutive channels (16 bytes; a lone last tile pairs
+      // with itself and only even g store).
+      uint32_t pk[DT][2];
 #pragma unroll
       for (int tn = 0; tn < DT; ++tn) {
-        const int n = tn * 16 + g * 4;
-        if (n < d) {
-          float o[4];
+        bf16x4 t4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = acc[tn][r] * inv;
-          store4(yrow + n, o);
+        for (int r = 0; r < 4; ++r) t4[r] = (bf16)(acc[tn][r] * inv);
+        pk[tn][0] = reinterpret_cast<const uint32_t*>(&t4)[0];
+        pk[tn][1] = reinterpret_cast<const uint32_t*>(&t4)[1];
+      }
+      const bool odd = (lane & 16) != 0;
+      auto from_partner = [&](uint32_t v) {
+        const auto pr = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return odd ? pr[0] : pr[1];
+      };
+#pragma unroll
+      for (int tn = 0; tn < DT; tn += 2) {
+        const int tb = tn + 1 < DT ? tn + 1 : tn;
+        const uint32_t r0 = from_partner(odd ? pk[tn][0] : pk[tb][0]);
+        const uint32_t r1 = from_partner(odd ? pk[tn][1] : pk[tb][1]);
+        const int n = odd ? tb * 16 + (g - 1) * 4 : tn * 16 + g * 4;
+        const uint4 w = odd ? make_uint4(r0, r1, pk[tb][0], pk[tb][1]) : make_uint4(pk[tn][0], pk[tn][1], r0, r1);
+        if (tok < N && n < d && !(odd && tb == tn)) *reinterpret_cast<uint4*>(yrow + n) = w;
+      }
+    } else {
+      if (tok < N) {
+#pragma unroll
+        for (int tn = 0; tn < DT; ++tn) {
+          const int n = tn * 16 + g * 4;
+          if (n < d) {
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = acc[tn][r] * inv;
+            store4(yrow + n, o);
+          }
         }
       }
     }
