@@ -85,6 +85,17 @@ SMALL = {
                                 dtype="bf16", x_std=1.0),
     "bf16_halo_w64_c1152": make_shape(B=2, H=4, W=64, C=1152, heads=16, head_dim=72, reduction=4, gn_groups=32,
                                       dtype="bf16", x_std=1.0),
+    # the bf16 depthwise + state kernel's chunks are tiles of the compressed grid: 16 x 16 (19 x 21 compressed:
+    # 2 x 2 chunks, three of them partial), one compressed row (64 x 4 and 1 x 256 tiles), one compressed
+    # column (128 x 2 tiles)
+    "bf16_tiles_19x21": make_shape(B=2, H=38, W=42, C=128, heads=2, head_dim=64, reduction=4, gn_groups=4,
+                                   dtype="bf16", x_std=1.0),
+    "bf16_1x5": make_shape(B=1, H=1, W=5, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
+                           dtype="bf16", x_std=1.0),
+    "bf16_2x600": make_shape(B=1, H=2, W=600, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
+                             dtype="bf16", x_std=1.0),
+    "bf16_600x2": make_shape(B=1, H=600, W=2, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
+                             dtype="bf16", x_std=1.0),
     "f32_1x1": make_shape(B=2, H=1, W=1, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
                           dtype="f32", x_std=1.0),
     "f32_1x5": make_shape(B=1, H=1, W=5, C=64, heads=2, head_dim=32, reduction=4, gn_groups=2,
