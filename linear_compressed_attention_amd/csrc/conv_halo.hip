@@ -286,10 +286,49 @@ __global__ __launch_bounds__(256, 1) void conv3x3_rows_kernel(GemmArgs<bf16> p, 
       EDIT_ROWS_DMA(S0, 0);
       if (nk > 1) EDIT_ROWS_DMA(S1, 1);
     }
+    // bias, then 16-byte stores: accumulator quad g of lane l holds channels 8g + 4(l >> 5) .. +3 of
+    // token l & 31; lanes l and l ^ 32 swap halves so that each stores 8 consecutive channels.
+#pragma unroll
+    for (int t = 0; t < TI; ++t) {
+      const int m = em0 + wave * 64 + t * 32 + fr;
+#pragma unroll
+      for (int c = 0; c < CJ; ++c) {
+        float f[4][4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) f[g][i] = acc[t][c][4 * g + i] + (float)bv[c][g][i];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int ge = 2 * j, go = 2 * j + 1;
+          const int n = en0 + c * 32 + 8 * (fh ? go : ge);
+          uint32_t pk[2][2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            bf16x4 b4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b4[i] = (bf16)f[hh ? go : ge][i];
+            pk[hh][0] = reinterpret_cast<const uint32_t*>(&b4)[0];
+            pk[hh][1] = reinterpret_cast<const uint32_t*>(&b4)[1];
+          }
+          const uint32_t s0 = fh ? pk[0][0] : pk[1][0];
+          const uint32_t s1 = fh ? pk[0][1] : pk[1][1];
+          const uint32_t r0 = other_half(s0, fh);
+          const uint32_t r1 = other_half(s1, fh);
+          uint32_t w[4];
+          w[0] = fh ? r0 : pk[0][0];
+          w[1] = fh ? r1 : pk[0][1];
+          w[2] = fh ? pk[1][0] : r0;
+          w[3] = fh ? pk[1][1] : r1;
+          *reinterpret_cast<uint4*>(p.C + (size_t)m * p.ldc + n) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+    }
     if (EM == E_BIAS_GN) {
-      // GroupNorm partial statistics of the tile as stored (bf16), per column over its 256 rows: the
-      // exact mean, then the sum of squared deviations from it (as gemm_dma.hip's statistics epilogue:
-      // lane sums, four row-local DPP levels, the 16-lane row swap, the waves through LDS).
+      // GroupNorm partial statistics of the tile as stored (bf16), per column over its 256 rows (after the
+      // stores are issued, so that they drain meanwhile): the exact mean, then the sum of squared deviations
+      // from it (as gemm_dma.hip's statistics epilogue: lane sums, four row-local DPP levels, the 16-lane row
+      // swap, the waves through LDS).
       auto stored = [&](int t, int c, int k) -> float {
         return (float)(bf16)(acc[t][c][k] + (float)bv[c][k >> 2][k & 3]);
       };
@@ -344,44 +383,6 @@ __global__ __launch_bounds__(256, 1) void conv3x3_rows_kernel(GemmArgs<bf16> p, 
           }
         }
         halo_barrier<63>();
-      }
-    }
-    // bias, then 16-byte stores: accumulator quad g of lane l holds channels 8g + 4(l >> 5) .. +3 of
-    // token l & 31; lanes l and l ^ 32 swap halves so that each stores 8 consecutive channels.
-#pragma unroll
-    for (int t = 0; t < TI; ++t) {
-      const int m = em0 + wave * 64 + t * 32 + fr;
-#pragma unroll
-      for (int c = 0; c < CJ; ++c) {
-        float f[4][4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) f[g][i] = acc[t][c][4 * g + i] + (float)bv[c][g][i];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int ge = 2 * j, go = 2 * j + 1;
-          const int n = en0 + c * 32 + 8 * (fh ? go : ge);
-          uint32_t pk[2][2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            bf16x4 b4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) b4[i] = (bf16)f[hh ? go : ge][i];
-            pk[hh][0] = reinterpret_cast<const uint32_t*>(&b4)[0];
-            pk[hh][1] = reinterpret_cast<const uint32_t*>(&b4)[1];
-          }
-          const uint32_t s0 = fh ? pk[0][0] : pk[1][0];
-          const uint32_t s1 = fh ? pk[0][1] : pk[1][1];
-          const uint32_t r0 = other_half(s0, fh);
-          const uint32_t r1 = other_half(s1, fh);
-          uint32_t w[4];
-          w[0] = fh ? r0 : pk[0][0];
-          w[1] = fh ? r1 : pk[0][1];
-          w[2] = fh ? pk[1][0] : r0;
-          w[3] = fh ? pk[1][1] : r1;
-          *reinterpret_cast<uint4*>(p.C + (size_t)m * p.ldc + n) = make_uint4(w[0], w[1], w[2], w[3]);
-        }
       }
     }
     if (next >= ntiles) break;
