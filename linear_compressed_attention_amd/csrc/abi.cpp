@@ -505,9 +505,11 @@ edit_status_t static_scratch(void** out) {
 // meet at step 8. Without per-step events the key/value branch runs on a
 // second stream, so its kernels take the CUs the query branch leaves idle
 // (the 3x3 conv has C/r / 96 x M / 256 tiles, 192 at 16384 tokens, fewer
-// than the CUs); with them every step runs in order on the caller's stream.
-// Each cross-stream event costs 5-10 us on MI355X, so there are only the
-// fork and the join.
+// than the CUs); at bf16 that stream carries only the key/value GEMM and the
+// depthwise + state pass follows the join on the caller's stream. With
+// per-step events every step runs in order on the caller's stream. Each
+// cross-stream event costs 5-10 us on MI355X, so there are only the fork
+// and the join.
 template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
                         hipStream_t s, const Marks& mk, float* lin_den = nullptr,
