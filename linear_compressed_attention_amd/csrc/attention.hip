@@ -231,7 +231,7 @@ __global__ __launch_bounds__(256) void kv_state_partial_kernel(const T* __restri
 // with the kv_col swizzle, the token's place in the tile as its column.
 // ---------------------------------------------------------------------------
 constexpr int kDwStateThreads = 512;   // 8 waves: two per SIMD overlap one another's loads
-constexpr uint32_t kDwOob = 0x80000000u;   // past the sample's buffer resource: the load returns zeros
+constexpr uint32_t kDwOob = 0x80000000u;   // past a block's buffer resource: the load returns zeros
 
 typedef __bf16 dw_bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -272,13 +272,16 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
   // the chunk's tile: compressed rows y0 .., columns x0 .. x0 + tw - 1 (tw = 2^twl); token t of the tile at
   // (y0 + t / tw, x0 + t % tw)
   const int tw = 1 << twl, cy = chunk / ncx;
-  const int y0 = cy * (SLAB >> twl), x0 = (chunk - cy * ncx) * tw;
+  const int y0 = cy * (SLAB >> twl), x0 = (chunk - cy * ncx) * tw;   // SLAB >> twl: the tile's rows
   auto in_grid = [&](int t) { return y0 + (t >> twl) < Hc && x0 + (t & (tw - 1)) < Wc; };
-  const T* img = kv0 + (size_t)b * H * W * 2 * C;
-  // the sample's [k0 | v0] rows as a buffer resource (the launch checks that its bytes stay below kDwOob)
-  const __amdgpu_buffer_rsrc_t rsI =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(img), (short)0, (int)((uint32_t)H * W * 4u * C), 0x00020000);
+  // the input rows the tile's taps reach, [r0, r1), as a buffer resource over the sample's [k0 | v0] rows
+  // (the launch checks that 2 th + 1 rows stay below kDwOob bytes)
+  const int th = SLAB >> twl;
+  const int r0 = max(2 * y0 - 1, 0), r1 = min(2 * (min(y0 + th, Hc) - 1) + 2, H);
+  const T* img = kv0 + ((size_t)b * H + r0) * W * 2 * C;
   const uint32_t pixb = 4u * (uint32_t)C;   // bytes per pixel of kv0 (2C bf16)
+  const __amdgpu_buffer_rsrc_t rsI = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(img), (short)0, (int)((uint32_t)(r1 - r0) * (uint32_t)W * pixb), 0x00020000);
   // byte step of tap (ky, kx) from the top-left tap, uniform (held as scalars, added as they are)
   uint32_t tapo[9];
 #pragma unroll
@@ -316,7 +319,7 @@ __global__ __launch_bounds__(kDwStateThreads) void dwconv_kv_state_kernel(
       // tap (ky, kx) reads pixel (2 yo + ky - 1, 2 xo + kx - 1): the top-left tap's byte offset (wrapping
       // below zero for a border token, whose border taps are masked) plus the tap's fixed step; only the
       // border rows and columns can fall outside the image
-      const uint32_t base = (uint32_t)((2 * yo[u] - 1) * W + 2 * xo[u] - 1) * pixb + 2u * (uint32_t)cin;
+      const uint32_t base = (uint32_t)((2 * yo[u] - 1 - r0) * W + 2 * xo[u] - 1) * pixb + 2u * (uint32_t)cin;
       const bool top = yo[u] > 0, bot = 2 * yo[u] + 1 < H, lef = xo[u] > 0, rig = 2 * xo[u] + 1 < W;
 #pragma unroll
       for (int t = 0; t < 9; ++t) {
@@ -515,8 +518,8 @@ hipError_t launch_dwconv_kv_state(const T* kv0, int B, int H, int W, int C, int 
     if (C != heads * d) return hipErrorInvalidValue;
     const DwStateTile tile = dw_state_tile((H + 1) / 2, (W + 1) / 2);
     if (nchunks != tile.ncy * tile.ncx) return hipErrorInvalidValue;
-    // a sample's rows are addressed by 32-bit offsets below the out-of-range marker
-    if ((size_t)H * W * 4 * C >= kDwOob) return hipErrorNotSupported;
+    // a block's input rows (at most 2 th + 1) are addressed by 32-bit offsets below the out-of-range marker
+    if ((size_t)(2 * tile.th + 1) * W * 4 * C >= kDwOob) return hipErrorNotSupported;
     if ((long long)nchunks * heads * B >= (1LL << 31)) return hipErrorInvalidValue;
     int twl = 0;
     while ((1 << twl) < tile.tw) ++twl;
