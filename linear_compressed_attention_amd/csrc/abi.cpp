@@ -758,21 +758,29 @@ struct SplitK {
   int S, kchunk;
 };
 
-// K slices for a [rows][cols] weight gradient over M tokens: about 512 blocks
-// (two per CU) in flight, slices a multiple of 64 tokens. The output tile is
-// the one the GEMM will pick: bf16 128 x 192 (cols a multiple of 192) or
-// 128 x 96 (of 96) on the DMA kernel, else 128 x 128.
+// K slices for a [rows][cols] weight gradient over M tokens, slices a multiple of 64 tokens. The output tile is
+// the one the GEMM will pick: bf16 128 x 192 (cols a multiple of 192) or 128 x 96 (of 96) on the DMA kernel, else
+// 128 x 128. The slice count minimises an estimate of the time in 64-token K steps: rounds of 512 blocks (two per
+// CU on 256 CUs) times the K steps of one slice, plus each slice's fp32 partial written and read back (~1 K step
+// per million output elements). A count just past a whole round (540 units on 512 slots) would leave a second
+// round of a few blocks running a whole slice on an almost idle chip.
 SplitK splitk(int rows, int cols, int M, bool bf) {
   const int bn = bf && cols % 192 == 0 ? 192 : (bf && cols % 96 == 0 ? 96 : 128);
   const long tiles = ((long)(rows + 127) / 128) * ((cols + bn - 1) / bn);
-  long S = (512 + tiles - 1) / tiles;
-  if (S > 32) S = 32;
-  if (S < 1) S = 1;
-  long kchunk = ((M + S - 1) / S + 63) / 64 * 64;
-  if (kchunk < 64) kchunk = 64;
+  const double slice_cost = (double)rows * cols * 1e-6;
+  long best_k = 64;
+  double best = 1e300;
+  for (long S = 1; S <= 32; ++S) {
+    long kchunk = ((M + S - 1) / S + 63) / 64 * 64;
+    if (kchunk < 64) kchunk = 64;
+    const long se = (M + kchunk - 1) / kchunk;
+    const long rounds = (tiles * se + 511) / 512;
+    const double t = (double)rounds * (double)(kchunk / 64) + (se > 1 ? (double)se * slice_cost : 0.0);
+    if (t < best) { best = t; best_k = kchunk; }
+  }
   SplitK r;
-  r.kchunk = (int)kchunk;
-  r.S = (int)((M + kchunk - 1) / kchunk);
+  r.kchunk = (int)best_k;
+  r.S = (int)((M + best_k - 1) / best_k);
   return r;
 }
 
