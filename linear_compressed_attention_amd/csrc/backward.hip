@@ -548,62 +548,71 @@ hipError_t launch_kv_bwd(const T* kc, const T* vc, const float* dS, const float*
 // ---------------------------------------------------------------------------
 // Depthwise 3x3 stride-2 backward (section "Spatial Compressor"), over the
 // keys and values side by side (2C channels; taps dwk for channels < C, dwv
-// above). Input gradient: input pixel (y, x) got tap (ky, kx) of output
-// (y', x') when y = 2y' + ky - 1 and x = 2x' + kx - 1, so
-//   d_in[y][x][c] = sum over those taps of dout[y'][x'][c] w[ky][kx][c]
-// (taps visited in (ky, kx) order). One thread per pixel and 8 channels.
+// above).
 // ---------------------------------------------------------------------------
+
+// Input gradient of the depthwise 3x3 stride-2 convs: din[y][x][c] = sum over the taps (ky, kx) with
+// y + 1 - ky and x + 1 - kx even of dout[(y + 1 - ky) / 2][(x + 1 - kx) / 2][c] w[ky][kx][c]. A thread takes
+// the 2x2 input pixels (2i + a, 2j + e) of one compressed position (i, j) and 8 channels: an even row uses tap
+// row 1 at output row i, an odd one tap row 0 at i + 1 and tap row 2 at i (columns alike), so the four pixels
+// read only dout at (i, j), (i + 1, j), (i, j + 1), (i + 1, j + 1) (zero past the grid), each once, with all
+// nine taps' weights. Taps are added in (ky, kx) order.
 template <typename T>
 __global__ __launch_bounds__(256) void dw_bwd_input_kernel(const float* __restrict__ dout, int B, int H, int W, int C,
                                                            const T* __restrict__ dwk, const T* __restrict__ dwv,
                                                            T* __restrict__ din) {
   const int Hc = (H + 1) / 2, Wc = (W + 1) / 2;
   const int cpp = (2 * C) / 8;
-  const long total = (long)B * H * W * cpp;
+  const long total = (long)B * Hc * Wc * cpp;
   const long idx = (long)xcd_swizzle(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   if (idx >= total) return;
   const int c8 = (int)(idx % cpp);
-  const long pix = idx / cpp;
-  const int x = (int)(pix % W), y = (int)((pix / W) % H), b = (int)(pix / ((long)W * H));
+  const long q = idx / cpp;
+  const int j = (int)(q % Wc), i = (int)((q / Wc) % Hc), b = (int)(q / ((long)Wc * Hc));
   const int ch2 = 8 * c8, ch = ch2 < C ? ch2 : ch2 - C;
   const T* w = ch2 < C ? dwk : dwv;
-  float acc[8];
+  // every load issued before any is used: the four output-gradient pixels (clamped, zeroed past the grid)
+  // and the nine taps
+  float g[2][2][8], wv[9][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  // yy = y + 1 - ky must be even: ky in {0, 2} for odd y, {1} for even y
-  // (likewise kx). The up to four taps' loads are all issued (at clamped
-  // addresses) before any is used; a tap that does not reach an output
-  // pixel adds nothing. Taps are still added in (ky, kx) order.
-  const int kys[2] = {(y & 1) ? 0 : 1, 2}, kxs[2] = {(x & 1) ? 0 : 1, 2};
-  float g[2][2][8], wv[2][2][8];
-  bool live[2][2];
+  for (int dy = 0; dy < 2; ++dy)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ky = kys[i], kx = kxs[j];
-      const int yy = y + 1 - ky, xx = x + 1 - kx;
-      live[i][j] = (i == 0 || (y & 1)) && (j == 0 || (x & 1)) && yy >= 0 && (yy >> 1) < Hc && xx >= 0 &&
-                   (xx >> 1) < Wc;
-      const int yc = min(max(yy >> 1, 0), Hc - 1), xc = min(max(xx >> 1, 0), Wc - 1);
-      load8(dout + (((size_t)b * Hc + yc) * Wc + xc) * 2 * C + ch2, g[i][j]);
-      load8(w + (ky * 3 + kx) * C + ch, wv[i][j]);
+    for (int dx = 0; dx < 2; ++dx) {
+      const int yo = min(i + dy, Hc - 1), xo = min(j + dx, Wc - 1);
+      load8(dout + (((size_t)b * Hc + yo) * Wc + xo) * 2 * C + ch2, g[dy][dx]);
     }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int t = 0; t < 9; ++t) load8(w + t * C + ch, wv[t]);
+  if (i + 1 >= Hc) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (live[i][j]) {
+    for (int k = 0; k < 8; ++k) g[1][0][k] = g[1][1][k] = 0.0f;
+  }
+  if (j + 1 >= Wc) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[k] += g[i][j][k] * wv[i][j][k];
-      }
-  store8(din + (size_t)pix * 2 * C + ch2, acc);
+    for (int k = 0; k < 8; ++k) g[0][1][k] = g[1][1][k] = 0.0f;
+  }
+  float o[2][2][8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    o[0][0][k] = 0.0f + g[0][0][k] * wv[4][k];                                   // (1,1) at (i, j)
+    o[0][1][k] = (0.0f + g[0][1][k] * wv[3][k]) + g[0][0][k] * wv[5][k];         // (1,0) at j+1, (1,2) at j
+    o[1][0][k] = (0.0f + g[1][0][k] * wv[1][k]) + g[0][0][k] * wv[7][k];         // (0,1) at i+1, (2,1) at i
+    o[1][1][k] = (((0.0f + g[1][1][k] * wv[0][k]) + g[1][0][k] * wv[2][k]) + g[0][1][k] * wv[6][k]) +
+                 g[0][0][k] * wv[8][k];                                           // (0,0) (0,2) (2,0) (2,2)
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int y = 2 * i + a, x = 2 * j + e;
+      if (y < H && x < W) store8(din + (((size_t)b * H + y) * W + x) * 2 * C + ch2, o[a][e]);
+    }
 }
 
 template <typename T>
 hipError_t launch_dw_bwd_input(const float* dout, int B, int H, int W, int C, const T* dwk, const T* dwv, T* din,
                                hipStream_t s) {
-  const long total = (long)B * H * W * (2 * C / 8);
+  const long total = (long)B * ((H + 1) / 2) * ((W + 1) / 2) * (2 * C / 8);
   if (total <= 0) return hipSuccess;
   hipLaunchKernelGGL((dw_bwd_input_kernel<T>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, dout, B, H, W,
                      C, dwk, dwv, din);
