@@ -958,11 +958,14 @@ hipError_t launch_gn_bwd(const T* dact, const T* act, const T* xc, const float* 
 // ---------------------------------------------------------------------------
 // Small fp32 product for the folded query weights' gradient:
 //   out[i][j] = add[i][j] + ru[i] rv[j] + sum_k A[i][k] B[j][k]
-// (A fp32 [M][lda], B [N][ldb], both K-contiguous). 64 x 64 output tiles,
-// 16 x 16 threads with 4 x 4 outputs each; K in chunks of 64 through LDS,
-// stored K-major so that a thread reads its 4 rows (columns) as one float4.
+// (A fp32 [M][lda], B [N][ldb], both K-contiguous), on the fp32 matrix cores
+// (32x32x2 steps). A block of four waves takes a 64 x 64 output tile, each
+// wave 32 x 32; K goes through LDS in chunks of 32 (B converted to fp32 as it
+// is staged), rows padded to 33 floats so that the 32 rows of a fragment read
+// fall in distinct banks. Lane l supplies row l % 32 of A and column l % 32
+// of B at the same k, so the product is the full fp32 sum over k.
 // ---------------------------------------------------------------------------
-constexpr int kSmKc = 64;
+constexpr int kSmKc = 32;
 
 template <typename TB, typename TO>
 __global__ __launch_bounds__(256) void small_nt_kernel(int M, int N, int K, const float* __restrict__ A, int lda,
@@ -970,60 +973,49 @@ __global__ __launch_bounds__(256) void small_nt_kernel(int M, int N, int K, cons
                                                        const float* __restrict__ add, int ldadd,
                                                        const float* __restrict__ ru, const TB* __restrict__ rv,
                                                        TO* __restrict__ out, int ldo) {
-  __shared__ __attribute__((aligned(16))) float As[kSmKc][64 + 4];
-  __shared__ __attribute__((aligned(16))) float Bs[kSmKc][64 + 4];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  __shared__ float As[64][kSmKc + 1];
+  __shared__ float Bs[64][kSmKc + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += kSmKc) {
-    // A: 64 rows x 16 float4 along K; B: 64 rows x 8 groups of 8 along K.
+  const int wr = (wave >> 1) * 32, wc = (wave & 1) * 32;
+  const int fr = lane & 31, fk = lane >> 5;
+  f32x16 acc;
 #pragma unroll
-    for (int e = tid; e < 64 * 16; e += 256) {
-      const int r = e >> 4, k = k0 + (e & 15) * 4;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += kSmKc) {
+    // A: 64 rows x 8 float4 along K; B: 64 rows x 4 groups of 8 along K (zero past M, N and K)
+#pragma unroll
+    for (int e = tid; e < 64 * 8; e += 256) {
+      const int r = e >> 3, k = k0 + (e & 7) * 4;
       f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
       if (i0 + r < M && k < K) v = *reinterpret_cast<const f32x4*>(A + (size_t)(i0 + r) * lda + k);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) As[(e & 15) * 4 + q][r] = v[q];
+      for (int q = 0; q < 4; ++q) As[r][(e & 7) * 4 + q] = v[q];
     }
-#pragma unroll
-    for (int e = tid; e < 64 * 8; e += 256) {
-      const int r = e >> 3, k = k0 + (e & 7) * 8;
+    {
+      const int r = tid >> 2, k = k0 + (tid & 3) * 8;
       float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (j0 + r < N && k < K) load8(Bm + (size_t)(j0 + r) * ldb + k, v);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) Bs[(e & 7) * 8 + q][r] = v[q];
+      for (int q = 0; q < 8; ++q) Bs[r][(tid & 3) * 8 + q] = v[q];
     }
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kSmKc; ++kk) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(&As[kk][ty * 4]);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bs[kk][tx * 4]);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] += av[a] * bv[c];
-    }
+    for (int kk = 0; kk < kSmKc; kk += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[wr + fr][kk + fk], Bs[wc + fr][kk + fk], acc, 0, 0, 0);
     __syncthreads();
   }
-  // Every load of the epilogue before its first store (a load queued behind
-  // a store waits for it).
+  // accumulator r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the wave's tile
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = i0 + ty * 4 + a, j = j0 + tx * 4 + c;
-      if (i < M && j < N) {
-        if (add) acc[a][c] += add[(size_t)i * ldadd + j];
-        if (ru) acc[a][c] += ru[i] * to_f32(rv[j]);
-      }
+  for (int r = 0; r < 16; ++r) {
+    const int i = i0 + wr + 8 * (r >> 2) + 4 * fk + (r & 3), j = j0 + wc + fr;
+    if (i < M && j < N) {
+      float v = acc[r];
+      if (add) v += add[(size_t)i * ldadd + j];
+      if (ru) v += ru[i] * to_f32(rv[j]);
+      out[(size_t)i * ldo + j] = from_f32<TO>(v);
     }
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = i0 + ty * 4 + a, j = j0 + tx * 4 + c;
-      if (i < M && j < N) out[(size_t)i * ldo + j] = from_f32<TO>(acc[a][c]);
-    }
+  }
 }
 
 template <typename TB, typename TO>
