@@ -982,24 +982,34 @@ __global__ __launch_bounds__(256) void small_nt_kernel(int M, int N, int K, cons
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  // A: 64 rows x 8 float4 along K (two per thread); B: 64 rows x 4 groups of 8 along K (one per thread); zero
+  // past M, N and K. A chunk's loads are issued before the previous chunk's products, so their latency overlaps.
+  f32x4 av[2];
+  float bv[8];
+  auto load_chunk = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = tid + 256 * h, r = e >> 3, k = k0 + (e & 7) * 4;
+      av[h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (i0 + r < M && k < K) av[h] = *reinterpret_cast<const f32x4*>(A + (size_t)(i0 + r) * lda + k);
+    }
+    const int r = tid >> 2, k = k0 + (tid & 3) * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) bv[q] = 0.0f;
+    if (j0 + r < N && k < K) load8(Bm + (size_t)(j0 + r) * ldb + k, bv);
+  };
+  load_chunk(0);
   for (int k0 = 0; k0 < K; k0 += kSmKc) {
-    // A: 64 rows x 8 float4 along K; B: 64 rows x 4 groups of 8 along K (zero past M, N and K)
 #pragma unroll
-    for (int e = tid; e < 64 * 8; e += 256) {
-      const int r = e >> 3, k = k0 + (e & 7) * 4;
-      f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (i0 + r < M && k < K) v = *reinterpret_cast<const f32x4*>(A + (size_t)(i0 + r) * lda + k);
+    for (int h = 0; h < 2; ++h) {
+      const int e = tid + 256 * h;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) As[r][(e & 7) * 4 + q] = v[q];
+      for (int q = 0; q < 4; ++q) As[e >> 3][(e & 7) * 4 + q] = av[h][q];
     }
-    {
-      const int r = tid >> 2, k = k0 + (tid & 3) * 8;
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (j0 + r < N && k < K) load8(Bm + (size_t)(j0 + r) * ldb + k, v);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) Bs[r][(tid & 3) * 8 + q] = v[q];
-    }
+    for (int q = 0; q < 8; ++q) Bs[tid >> 2][(tid & 3) * 8 + q] = bv[q];
     __syncthreads();
+    if (k0 + kSmKc < K) load_chunk(k0 + kSmKc);
 #pragma unroll
     for (int kk = 0; kk < kSmKc; kk += 2)
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[wr + fr][kk + fk], Bs[wc + fr][kk + fk], acc, 0, 0, 0);
