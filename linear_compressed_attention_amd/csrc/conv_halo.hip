@@ -280,6 +280,19 @@ __global__ __launch_bounds__(256, 1) void conv3x3_rows_kernel(GemmArgs<bf16> p, 
 
     // The stages are free: queue the next tile's first two steps, then write this tile.
     const int em0 = m0, en0 = n0;
+    // E_RES: the residual rows at this lane's store positions (as the exchanged stores below: token l & 31,
+    // 8 channels from 32 c + 16 j + 8 (l >> 5)), requested before the next tile's loads
+    uint4 rres[EM == E_RES ? TI : 1][EM == E_RES ? CJ : 1][2];
+    if constexpr (EM == E_RES) {
+#pragma unroll
+      for (int t = 0; t < TI; ++t)
+#pragma unroll
+        for (int c = 0; c < CJ; ++c)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            rres[t][c][j] = *reinterpret_cast<const uint4*>(p.R + (size_t)(em0 + wave * 64 + t * 32 + fr) * p.ldr +
+                                                            en0 + c * 32 + 16 * j + 8 * fh);
+    }
     const int next = tl + nblk;
     if (next < ntiles) {
       EDIT_ROWS_TILE(next);
@@ -302,6 +315,24 @@ __global__ __launch_bounds__(256, 1) void conv3x3_rows_kernel(GemmArgs<bf16> p, 
         for (int j = 0; j < 2; ++j) {
           const int ge = 2 * j, go = 2 * j + 1;
           const int n = en0 + c * 32 + 8 * (fh ? go : ge);
+          if constexpr (EM == E_RES) {
+            // fp32 halves exchanged, the residual added, one rounding: lane half 0 holds channels n .. n + 3 of
+            // its own and n + 4 .. n + 7 of its partner's, half 1 the partner's n .. n + 3 and its own
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float sv = fh ? f[ge][i] : f[go][i];
+              const float rv = __builtin_bit_cast(float, other_half(__builtin_bit_cast(uint32_t, sv), fh));
+              v[fh ? i : 4 + i] = rv;
+              v[fh ? 4 + i : i] = fh ? f[go][i] : f[ge][i];
+            }
+            const bf16* rb = reinterpret_cast<const bf16*>(&rres[t][c][j]);
+            bf16x8 o8;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o8[k] = (bf16)(v[k] + (float)rb[k]);
+            *reinterpret_cast<bf16x8*>(p.C + (size_t)m * p.ldc + n) = o8;
+            continue;
+          }
           uint32_t pk[2][2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
@@ -424,9 +455,11 @@ hipError_t launch_rows_tiles(const GemmArgs<bf16>& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_conv3x3_halo(const GemmArgs<bf16>& a, EMode em, hipStream_t s) {
-  if (em != E_BIAS && em != E_BIAS_GN) return hipErrorNotSupported;
-  if (a.R != nullptr || a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin || a.ldb != 9 * a.Cin)
+  if (em != E_BIAS && em != E_BIAS_GN && em != E_RES) return hipErrorNotSupported;
+  if ((em == E_RES) != (a.R != nullptr) || a.Cin % 64 != 0 || a.lda != a.Cin || a.K != 9 * a.Cin ||
+      a.ldb != 9 * a.Cin)
     return hipErrorNotSupported;
+  if (em == E_RES && (a.ldr % 8 != 0 || a.fold.W != nullptr)) return hipErrorNotSupported;
   if (a.N % 96 != 0 || a.seg_rows != a.N || a.ldc % 8 != 0 || a.ldc < a.N) return hipErrorNotSupported;
   const long hw = (long)a.H * a.W;
   if (hw % 256 != 0 || a.M % hw != 0) return hipErrorNotSupported;
@@ -436,7 +469,9 @@ hipError_t launch_conv3x3_halo(const GemmArgs<bf16>& a, EMode em, hipStream_t s)
   const int L = a.W <= 256 ? a.W : 256;
   if (a.W > 256 && a.W % 256 != 0) return hipErrorNotSupported;
 #define EDIT_HALO_CASE(LV)                                                                       \
-  if (L == LV) return em == E_BIAS_GN ? launch_rows_tiles<LV, E_BIAS_GN>(a, s) : launch_rows_tiles<LV, E_BIAS>(a, s);
+  if (L == LV)                                                                                    \
+    return em == E_BIAS_GN ? launch_rows_tiles<LV, E_BIAS_GN>(a, s)                               \
+                           : (em == E_RES ? launch_rows_tiles<LV, E_RES>(a, s) : launch_rows_tiles<LV, E_BIAS>(a, s));
   EDIT_HALO_CASE(32)
   EDIT_HALO_CASE(64)
   EDIT_HALO_CASE(128)

@@ -636,7 +636,7 @@ hipError_t launch_gemm_dma(const GemmArgs<bf16>& a, AMode am, EMode em, hipStrea
   //  - the 3x3 conv (162 K steps): 119 us against 227 us for the register-staged kernel;
   //  - plain-A projections with 128 x 192 tiles, two stages, two blocks per CU: 46 us at
   //    16384 x 1152 x 1152 and 91 us at 16384 x 2304 x 1152 against 63 and 105 us register-staged.
-  if (am == A_CONV3 && (em == E_BIAS || em == E_BIAS_GN)) {
+  if (am == A_CONV3 && (em == E_BIAS || em == E_BIAS_GN || em == E_RES)) {
     // the halo-staged kernel where it covers the shape
     const hipError_t e = launch_conv3x3_halo(a, em, s);
     if (e != hipErrorNotSupported) return e;
