@@ -710,10 +710,12 @@ __global__ __launch_bounds__(256) void dw_bwd_weight_partial_kernel(const float*
   }
 }
 
-// Sum the pixel-chunk partials in order; write dw_k, db_k (channels < C) and
+// Sum the pixel-chunk partials; write dw_k, db_k (channels < C) and
 // dw_v, db_v (taps stored [3][3][C] as the weights), and the input gradient's
 // sums over pixels bk (channels < C) and bv: (sum_t w[t][c]) db[c] minus the
-// border term, from the fp32 sums.
+// border term, from the fp32 sums. A block takes 32 outputs; lane q of the 8
+// lanes per output sums chunks q, q + 8, .. in order, then lane 0 adds the 8
+// lane sums in order (a fixed order: the result is reproducible bit for bit).
 template <typename T>
 __global__ __launch_bounds__(256) void dw_bwd_weight_finalize_kernel(const float* __restrict__ partial, int nchunks,
                                                                      int C, const T* __restrict__ wk,
@@ -721,12 +723,31 @@ __global__ __launch_bounds__(256) void dw_bwd_weight_finalize_kernel(const float
                                                                      T* __restrict__ dbk, T* __restrict__ dwv,
                                                                      T* __restrict__ dbv, T* __restrict__ bk,
                                                                      T* __restrict__ bv) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= 10 * 2 * C) return;
-  const int t = i / (2 * C), c2 = i - t * 2 * C;
-  float s = 0.0f;
-#pragma unroll 8
-  for (int ch = 0; ch < nchunks; ++ch) s += partial[(size_t)ch * 11 * 2 * C + (size_t)t * 2 * C + c2];
+  __shared__ float red[2][8][33];
+  const int o = threadIdx.x & 31, q = threadIdx.x >> 5;
+  const int i = blockIdx.x * 32 + o;
+  const bool live = i < 10 * 2 * C;
+  const int t = live ? i / (2 * C) : 0, c2 = live ? i - t * 2 * C : 0;
+  float s = 0.0f, border = 0.0f;
+  if (live) {
+#pragma unroll 4
+    for (int ch = q; ch < nchunks; ch += 8) {
+      const float* pp = partial + (size_t)ch * 11 * 2 * C + c2;
+      s += pp[(size_t)t * 2 * C];
+      if (t == 9) border += pp[(size_t)10 * 2 * C];
+    }
+  }
+  red[0][q][o] = s;
+  red[1][q][o] = border;
+  __syncthreads();
+  if (q != 0 || !live) return;
+  s = 0.0f;
+  border = 0.0f;
+#pragma unroll
+  for (int l = 0; l < 8; ++l) {
+    s += red[0][l][o];
+    border += red[1][l][o];
+  }
   const bool k = c2 < C;
   const int c = k ? c2 : c2 - C;
   if (t < 9) {
@@ -734,9 +755,6 @@ __global__ __launch_bounds__(256) void dw_bwd_weight_finalize_kernel(const float
     return;
   }
   (k ? dbk : dbv)[c] = from_f32<T>(s);
-  float border = 0.0f;
-#pragma unroll 8
-  for (int ch = 0; ch < nchunks; ++ch) border += partial[(size_t)ch * 11 * 2 * C + (size_t)10 * 2 * C + c2];
   const T* w = k ? wk : wv;
   float wsum = 0.0f;
 #pragma unroll
@@ -758,7 +776,7 @@ hipError_t launch_dw_bwd_weight(const float* dout, const T* in, const T* wk, con
                      partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dw_bwd_weight_finalize_kernel<T>), dim3((10 * 2 * C + 255) / 256), dim3(256), 0, s, partial,
+  hipLaunchKernelGGL((dw_bwd_weight_finalize_kernel<T>), dim3((10 * 2 * C + 31) / 32), dim3(256), 0, s, partial,
                      nch, C, wk, wv, dwk, dbk, dwv, dbv, bk, bv);
   return hipGetLastError();
 }
