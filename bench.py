@@ -8,8 +8,8 @@ workload's synthetic input, which is resident in HBM before timing starts.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload pixart2048]
 
 Prints one JSON line. `value` is image tokens/s over the K timed steps
-(HIP events on the stream the library launches on, bracketed by device
-synchronisation). `roofline` covers the step with the longest average
+(timing-only HIP events, recorded without a system-scope fence, on the stream
+the library launches on, bracketed by device synchronisation). `roofline` covers the step with the longest average
 duration: its algorithmic work per launch over its average duration, timed
 live with events the library records between its steps, against MI355X's
 published peak. `cpu_baseline` times the float64 CPU oracle on a bounded
@@ -194,6 +194,7 @@ class HipEvents:
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -205,6 +206,12 @@ class HipEvents:
             out.append(e.value)
         return out
 
+    def record(self, e, stream):
+        """Record e on a torch stream."""
+        rc = self.hip.hipEventRecord(e, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
         rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
@@ -215,6 +222,34 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(e)
+
+
+def timed_steps(step, K, stream):
+    """K calls of step() back to back between two timing-only events, bracketed by device synchronisation:
+    (milliseconds on the GPU, wall seconds, per-call milliseconds). The per-call durations come from a second
+    pass of K calls with an event between each two; every event recorded on the stream costs the chip a few
+    microseconds, so they run slightly longer than the first pass's mean and serve only as its spread."""
+    import torch
+    tev = HipEvents()
+    e = tev.create(2)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    tev.record(e[0], stream)
+    for _ in range(K):
+        step()
+    tev.record(e[1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = tev.elapsed_ms(e[0], e[1])
+    ev = tev.create(K + 1)
+    tev.record(ev[0], stream)
+    for i in range(K):
+        step()
+        tev.record(ev[i + 1], stream)
+    torch.cuda.synchronize()
+    per_iter = [tev.elapsed_ms(ev[i], ev[i + 1]) for i in range(K)]
+    tev.destroy(e + ev)
+    return ms, wall, per_iter
 
 
 def cpu_baseline(shape, inp, min_runs, budget_s, eta="ratio", query="convfusion", kv="compressed"):
@@ -290,16 +325,7 @@ def bench_backward(args, s, inp):
         step()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    wall0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(K):
-        step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = ev[0].elapsed_time(ev[K])
-    per_iter = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]
+    ms, wall, per_iter = timed_steps(step, K, stream)
     assert torch.isfinite(dx).all().item(), "non-finite dx"
     flops = backward_work(s)
     ach = flops / (ms / K * 1e-3) / 1e12
@@ -429,19 +455,10 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K forwards, an event before each and after the last.
+    # Timed region: K forwards back to back, as the layers of a model run, between two timing-only events
+    # (no system-scope fence on recording; read after the device synchronisation).
     K = args.steps
-    evk = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    evk[0].record(stream)
-    for i in range(K):
-        step()
-        evk[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = evk[0].elapsed_time(evk[K])
-    per_iter = [evk[i].elapsed_time(evk[i + 1]) for i in range(K)]
+    ms, wall, per_iter = timed_steps(step, K, stream)
     ms_per_step = ms / K
     value = s.B * s.N * K / (ms / 1e3)
     assert torch.isfinite(y).all().item(), "non-finite output"

@@ -514,7 +514,7 @@ template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
                         hipStream_t s, const Marks& mk, float* lin_den = nullptr,
                         const edit_convfusion_weights_t* kcf = nullptr, bool apply = true,
-                        const std::function<edit_status_t(hipStream_t)>* side_first = nullptr) {
+                        const std::function<edit_status_t(hipStream_t)>* side_work = nullptr) {
   using namespace edit;
   auto P = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
@@ -599,7 +599,7 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     if (cf && (st = q_convfusion(s, CF_ALL)) != EDIT_OK) return st;
     if ((st = q_proj(s)) != EDIT_OK) return st;
     if ((st = kv_branch(s, true)) != EDIT_OK) return st;
-    if (side_first && (st = (*side_first)(s)) != EDIT_OK) return st;
+    if (side_work && (st = (*side_work)(s)) != EDIT_OK) return st;
   } else {
     std::lock_guard<std::mutex> lock(g_side_mu);
     SideStream* side;
@@ -612,8 +612,9 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     st = cf ? q_convfusion(s, CF_ALL) : EDIT_OK;
     if (st == EDIT_OK) st = q_proj(s);
     // work of the caller's that depends on neither branch (the hybrid's text Q|K|V) goes first on the side
-    // stream, beside the conv
-    if (st == EDIT_OK && side_first) st = (*side_first)(side->s);
+    // stream, beside the conv (measured at SD3.5M: queued after the key/value GEMM instead, that GEMM starts
+    // ~60 us earlier but the text GEMM then runs beside the query GEMM, and the join comes ~20 us later)
+    if (st == EDIT_OK && side_work) st = (*side_work)(side->s);
     // The bf16 compressed path joins after its key/value GEMM, which ends well before the query GEMM, so the
     // caller's stream finds the join already satisfied; the depthwise + state pass then follows the query GEMM
     // on the caller's stream with the whole chip (a join behind a still-running side stream leaves the chip
