@@ -29,10 +29,8 @@
  *            accumulator are fp32); EDIT_F32 is fp32 throughout.
  *   Memory   every pointer is a device pointer owned by the caller; the
  *            library allocates no memory and keeps no data between calls
- *            (on first use on a device it creates one more stream and one
- *            event there, kept for the life of the process; the forwards
- *            also order the two streams through an 8-byte flag held in the
- *            library's code object).
+ *            (on first use on a device it creates one more stream and two
+ *            events there, kept for the life of the process).
  *            Tensor pointers must be 16-byte aligned, the workspace
  *            256-byte aligned. Outputs must not overlap inputs or the
  *            workspace.

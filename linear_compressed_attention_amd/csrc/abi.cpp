@@ -440,23 +440,14 @@ edit_status_t linear_cc(const Geometry& g, const T* a_in, const void* w, const v
   return EDIT_OK;
 }
 
-// A second stream per device for the key/value branch. It is forked from the caller's stream by an event
-// and joined back through a flag: the side stream writes generation g to the flag after its work, and the
-// caller's stream waits for it (hipStreamWriteValue64 / hipStreamWaitValue64, carried out by the command
-// processor once the producing kernels have ended and released their writes). On MI355X a wait on an event
-// already recorded leaves the caller's stream idle ~6 us, the flag ~1 us. The fork stays an event: its
-// ~10 us of latency is what lets the caller's conv take the CUs before the key/value GEMM's blocks (forked
-// through a flag, the GEMM started first and the conv took 199 us instead of 116). The stream and the event
-// are created on first use and kept for the life of the process; the flag is a static word of the library's
-// code object (zero when it loads; each device holds its own copy). g_side_mu serialises the enqueue of a
-// fork .. join section, so that the event records and the generations stay in order per device.
-static __device__ __align__(64) unsigned long long side_join_flag[1];
-
+// A second stream per device for the key/value branch, and the events that
+// fork it from the caller's stream and join it back. Created on first use,
+// kept for the life of the process; g_side_mu serialises the enqueue of a
+// fork .. join section, so that concurrent callers do not interleave records
+// of the shared events.
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr;
-  unsigned long long* join = nullptr;    // this device's side_join_flag
-  unsigned long long gen = 0;            // the last generation written
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 std::mutex g_side_mu;
 SideStream g_side[64];
@@ -467,15 +458,16 @@ edit_status_t side_stream(SideStream** out) {
   if (e != hipSuccess || dev < 0 || dev >= 64) return fail(EDIT_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
   SideStream& ss = g_side[dev];
   if (!ss.s) {
-    // Both streams run on this device: a device-scope release is enough. Everything is set up before any of
-    // it is kept, so a failure leaves the slot empty for the next call to retry.
-    void* p = nullptr;
-    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(side_join_flag))) != hipSuccess || p == nullptr)
-      return fail(EDIT_ERR_HIP, "looking up the join flag failed: %s", hipGetErrorString(e));
+    // Both streams run on this device: a device-scope release is enough. All
+    // three objects are created before any is kept, so a failure leaves the
+    // slot empty for the next call to retry.
+    const unsigned fl = hipEventDisableTiming | hipEventReleaseToDevice;
     SideStream n;
-    n.join = static_cast<unsigned long long*>(p);
     if ((e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming | hipEventReleaseToDevice)) != hipSuccess) {
+        (e = hipEventCreateWithFlags(&n.fork, fl)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&n.join, fl)) != hipSuccess) {
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
       if (n.s) (void)hipStreamDestroy(n.s);
       return fail(EDIT_ERR_HIP, "creating the key/value stream failed: %s", hipGetErrorString(e));
     }
@@ -515,9 +507,9 @@ edit_status_t static_scratch(void** out) {
 // (the 3x3 conv has C/r / 96 x M / 256 tiles, 192 at 16384 tokens, fewer
 // than the CUs); at bf16 that stream carries only the key/value GEMM and the
 // depthwise + state pass follows the join on the caller's stream. With
-// per-step events every step runs in order on the caller's stream. There
-// are only the fork and the join: each cross-stream dependency costs the
-// consumer several microseconds on MI355X.
+// per-step events every step runs in order on the caller's stream. Each
+// cross-stream event costs 5-10 us on MI355X, so there are only the fork
+// and the join.
 template <typename T>
 edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t* w, const T* x, char* ws,
                         hipStream_t s, const Marks& mk, float* lin_den = nullptr,
@@ -628,11 +620,9 @@ edit_status_t run_image(const Geometry& g, const Layout& L, const edit_weights_t
     // on the caller's stream with the whole chip (a join behind a still-running side stream leaves the chip
     // idle ~11 us on MI355X).
     if (st == EDIT_OK) st = kv_branch(side->s, !fused_dw);
-    // Join even after a failed launch, so the caller's stream never runs ahead of queued side work (and
-    // waits only for a flag the side stream has been given to write).
-    const unsigned long long gen = ++side->gen;
-    const hipError_t e1 = hipStreamWriteValue64(side->s, side->join, gen, 0);
-    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitValue64(s, side->join, gen, hipStreamWaitValueGte, ~0ull) : e1;
+    // Join even after a failed launch, so the caller's stream never runs ahead of queued side work.
+    const hipError_t e1 = hipEventRecord(side->join, side->s);
+    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(s, side->join, 0) : e1;
     if (st != EDIT_OK) return st;
     if (e2 != hipSuccess) return fail(EDIT_ERR_HIP, "joining the key/value stream failed: %s", hipGetErrorString(e2));
     if (fused_dw && (st = dw_state(s)) != EDIT_OK) return st;
