@@ -372,7 +372,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed forwards first; about 100 bring the chip to the steady rate of back-to-back layers")
     ap.add_argument("--workload", default="pixart2048")
     ap.add_argument("--cpu-runs", type=int, default=3, help="minimum oracle runs for cpu_baseline (0 = skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
